@@ -1,0 +1,233 @@
+"""Decode-step benchmark of the packed K6/V4 KV cache on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+
+A step is one pass of the hot path for one layer: quantise-and-append the
+new token of every sequence (lkv_quant_append), then split-K decode
+attention of one query per sequence over the whole packed cache
+(lkv_decode_split + lkv_decode_combine, i.e. lkv_decode_attn).  Steps rotate
+over several layer caches so that consecutive steps stream from HBM, not
+from the 256 MB last-level cache.  Every step re-appends the row of the last
+position and attends over all N positions, the same work as the step that
+brings the context to N tokens.
+
+Prints one JSON line.  `value` is packed-KV GB/s: counted bytes per step
+(packed codes + fp32 scales + uint8 zero points of every live token and KV
+head, plus Q and O, plus the appended rows) over the measured step time.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, 8 TB/s
+METRIC = "packed-KV decode attention GB/s (% of HBM peak); decode tokens/s at 32K ctx"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", type=int, default=2, choices=[2, 4])
+    p.add_argument("--layers", type=int, default=4, help="layer caches rotated over (HBM, not cache)")
+    p.add_argument("--split-tokens", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seqs", type=int, default=8, help="sequences in the oracle's timed sample")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="also run a plain 1 GiB device copy (counter scaling reference)")
+    p.add_argument("--fp16-layer", action="store_true", help="time the fp16 sensitive-layer format")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("decode.hip", "decode_mfma.hip"):
+        path = os.path.join(ROOT, "quantized_kv_cache_token_amd", "csrc", name)
+        if os.path.exists(path):
+            h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the kernel runs on one GPU's share; see the sharding notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from quantized_kv_cache_token_amd import inputs, lkv, workloads
+
+    wl = workloads.BY_INDEX[args.workload]
+    if args.fp16_layer:
+        kb, vb = 16, 16
+    else:
+        kb, vb = wl.k_bits, wl.v_bits
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    B, Hq, Hkv, D, N = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.n_ctx
+    nblk = (N + 63) // 64
+    bt = torch.arange(B * nblk, dtype=torch.int32, device=dev).view(B, nblk)
+    lens = torch.full((B,), N, dtype=torch.int32, device=dev)
+    outl = inputs.outlier_channels(wl.seed, Hkv, D) if wl.outliers else None
+
+    # ---- layer caches, filled by the append kernel (prefill, untimed)
+    caches = []
+    for layer in range(args.layers):
+        c = lkv.Cache(D, wl.group_size, kb, vb, Hkv, B * nblk, device=dev)
+        for b in range(B):
+            k, v = inputs.kv_rows(wl.seed, b, N - 1, Hkv, D, dtype=wl.dtype, outliers=outl, layer=layer,
+                                  device=dev)
+            cu = torch.tensor([0, N - 1], dtype=torch.int32, device=dev)
+            lkv.quant_append(c, k, v, cu, torch.zeros(1, dtype=torch.int32, device=dev), bt[b:b + 1], N - 1)
+            del k, v
+        caches.append(c)
+    torch.cuda.synchronize()
+    chunk = caches[0].chunk_bytes
+    view = lkv.View(bt, lens, N)
+
+    # ---- per-step inputs: the new token's K/V and the query, per layer
+    new_k, new_v, qs = [], [], []
+    for layer in range(args.layers):
+        k, v = inputs.kv_rows(wl.seed, 1000, B, Hkv, D, dtype=wl.dtype, outliers=outl, layer=layer, step=1,
+                              device=dev)
+        new_k.append(k.contiguous())
+        new_v.append(v.contiguous())
+        qs.append(inputs.queries(wl.seed, B, Hq, D, dtype=wl.dtype, layer=layer, device=dev))
+    cu1 = torch.arange(B + 1, dtype=torch.int32, device=dev)
+    last = torch.full((B,), N - 1, dtype=torch.int32, device=dev)
+    sm = float(np.float32(1.0 / np.sqrt(D)))
+    split = args.split_tokens or lkv.decode_plan([caches[0]], [view], B, Hq)
+    ws = lkv.decode_workspace([caches[0]], [view], B, Hq, split, dev)
+    out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
+
+    def step(i, ev=None):
+        c = caches[i % args.layers]
+        lkv.quant_append(c, new_k[i % args.layers], new_v[i % args.layers], cu1, last, bt, 1)
+        if ev is not None:
+            ev[0].record()
+        lkv.decode_split([c], [view], qs[i % args.layers], sm, 0.0, split, ws)
+        if ev is not None:
+            ev[1].record()
+        lkv.decode_combine([c], [view], B, Hq, split, out, ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    step_s = (t1 - t0) / args.steps
+    split_ms = [a.elapsed_time(b) for a, b in evs]
+    split_s = float(np.mean(split_ms)) / 1e3
+
+    per_token_head = chunk // 64
+    q_bytes = 2 if wl.dtype == "bf16" else 4
+    kv_bytes = B * Hkv * N * per_token_head
+    decode_bytes = kv_bytes + B * Hq * D * q_bytes + B * Hq * D * 4
+    append_bytes = B * Hkv * (2 * D * q_bytes + per_token_head)
+    step_bytes = decode_bytes + append_bytes
+    value = step_bytes / step_s / 1e9
+    split_alg = kv_bytes + B * Hq * D * q_bytes
+    achieved = split_alg / split_s / 1e9
+    kname = "decode_split"
+    wname = wl.name if not args.fp16_layer else wl.name.replace("k6v4", "fp16")
+    traffic = measured_traffic(kname, wname)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wname, "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
+                   "ctx_tokens": N, "group_size": wl.group_size, "k_bits": kb, "v_bits": vb,
+                   "q_dtype": wl.dtype, "split_tokens": split, "layers_rotated": args.layers},
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s": round(B / step_s, 1),
+        "bytes_per_step": step_bytes,
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "alg_bytes_per_launch": split_alg,
+                     "avg_launch_us": round(split_s * 1e6, 2)},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(wl, kb, vb, min(args.cpu_seqs, B), per_token_head, q_bytes)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(wl, kb, vb, nseq, per_token_head, q_bytes):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    `nseq` sequences, all their query heads, one step (append one row, decode
+    over N tokens), on this host's cores.  GB/s over the same counted bytes."""
+    import numpy as np
+
+    from oracle import oracle as O
+    from quantized_kv_cache_token_amd import inputs
+
+    B, Hq, Hkv, D, N = nseq, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.n_ctx
+    nblk = (N + 63) // 64
+    outl = inputs.outlier_channels(wl.seed, Hkv, D) if wl.outliers else None
+    cache = O.Cache(D, wl.group_size, kb, vb, Hkv, B * nblk)
+    bt = np.arange(B * nblk, dtype=np.int32).reshape(B, nblk)
+    for b in range(B):
+        k, v = inputs.kv_rows(wl.seed, b, N - 1, Hkv, D, dtype=wl.dtype, outliers=outl)
+        O.append(cache, k.float().numpy(), v.float().numpy(), [0, N - 1], [0], bt[b:b + 1])
+    k, v = inputs.kv_rows(wl.seed, 1000, B, Hkv, D, dtype=wl.dtype, outliers=outl, step=1)
+    q = inputs.queries(wl.seed, B, Hq, D, dtype=wl.dtype).float().numpy()
+    sm = float(np.float32(1.0 / np.sqrt(D)))
+    t0 = time.perf_counter()
+    O.append(cache, k.float().numpy(), v.float().numpy(), np.arange(B + 1), np.full(B, N - 1), bt)
+    O.decode([cache], [bt], [np.full(B, N, np.int32)], q, sm, 0.0, 0)
+    dt = time.perf_counter() - t0
+    nbytes = B * Hkv * N * per_token_head + B * Hq * D * (q_bytes + 4) + B * Hkv * (2 * D * q_bytes + per_token_head)
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{B} of {wl.batch} sequences, all {Hq} query heads, one step (append 1 row + fp64 "
+                      f"decode over {N} tokens); {dt:.2f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,197 @@
+/*
+ * lkv.h -- C ABI of the MI355X (gfx950) quantised KV-cache decode library.
+ *
+ * The three calls follow the pages' statement of the problem:
+ *   lkv_quant_append  quantise new K/V rows and bit-pack them into the cache
+ *   lkv_decode_attn   attention of the current decode queries against the
+ *                     packed cache (split over the token axis, then merged)
+ *   lkv_tier_update   attention-aware tiers: HIGH keeps 6-bit V, MID gets
+ *                     4-bit V, LOW is evicted
+ * Sources of each operation are cited at its declaration.
+ *
+ * Conventions for every call:
+ *  - Pointers are device pointers unless marked (host).  The caller owns every
+ *    buffer (pools, tables, lengths, Q, K, V, scores, outputs, workspaces);
+ *    the library allocates nothing and holds no global state besides its
+ *    loaded kernels.
+ *  - `stream` is a hipStream_t (0 = the null stream).  Work is queued on it and
+ *    never synchronised by the library; device faults surface at the caller's
+ *    next synchronisation.
+ *  - Host-side argument checks run before any launch: a call that fails them
+ *    returns LKV_EINVAL or LKV_EUNSUPPORTED and queues nothing.  A launch
+ *    failure reported by the HIP runtime returns LKV_EHIP.
+ *  - Calls are thread-safe as long as concurrent calls write distinct buffers.
+ *
+ * Cache format (one layout for every call).  Tokens are grouped in blocks of
+ * 64.  A pool is [num_blocks][num_kv_heads][chunk_bytes]; one chunk holds one
+ * block of one KV head in six sections, each padded to a multiple of 128 B:
+ *   K codes   64 token rows, each the head_dim channel codes as a k_bits-bit
+ *             bitstream
+ *   V codes   head_dim channel rows, each the 64 slot codes as a v_bits-bit
+ *             bitstream
+ *   K scales  fp32 [head_dim/group_size][64]
+ *   V scales  fp32 [head_dim/group_size][64]
+ *   K zeros   uint8 [head_dim/group_size][64]
+ *   V zeros   uint8 [head_dim/group_size][64]
+ * A bitstream holds field i in bits [i*b, i*b+b), LSB first, in little-endian
+ * 32-bit words.  Element x of channel d in group d/group_size is stored as the
+ * code q with scale s and zero point z such that x ~ (q - z) * s.  With
+ * k_bits = v_bits = 16 (precision-sensitive layers) the fields are fp16 bit
+ * patterns (round to nearest even) and the metadata sections are empty.
+ * Logical block i of sequence b lives in pool block block_table[b][i]; a
+ * contiguous cache is the identity table.
+ */
+#ifndef LKV_H
+#define LKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LKV_BLOCK_TOKENS 64
+
+typedef enum {
+    LKV_OK = 0,
+    LKV_EINVAL = -1,       /* null pointer, bad size or inconsistent arguments */
+    LKV_EUNSUPPORTED = -2, /* a format or shape this build has no kernel for */
+    LKV_EHIP = -3          /* the HIP runtime refused a launch */
+} lkv_status;
+
+typedef enum { LKV_F32 = 0, LKV_BF16 = 1, LKV_F16 = 2 } lkv_dtype;
+
+/* One cache.  head_dim 64 or 128; group_size 16, 32 or 64 dividing head_dim;
+ * (k_bits, v_bits) in {4, 6} x {4, 6}, or (16, 16); block_tokens 64.  pool is
+ * 256-byte aligned and holds num_blocks * num_kv_heads * chunk bytes. */
+typedef struct lkv_cache {
+    int32_t head_dim;
+    int32_t group_size;
+    int32_t k_bits;
+    int32_t v_bits;
+    int32_t num_kv_heads;
+    int32_t block_tokens;
+    int64_t num_blocks;
+    void* pool;
+} lkv_cache;
+
+/* What a batch reads from one cache. */
+typedef struct lkv_view {
+    const int32_t* block_table; /* [batch][max_blocks] int32 */
+    const int32_t* seq_lens;    /* [batch] int32, live tokens per sequence */
+    int32_t max_blocks;
+    int32_t max_len;            /* (host) upper bound of seq_lens, sizes the grid */
+} lkv_view;
+
+/* Human-readable name of a status. */
+const char* lkv_status_string(int status);
+
+/* Byte offsets of the six sections of a chunk and, in off[6], the chunk size
+ * (the memory layout reorganised for the quantised format: LeanKV page,
+ * implementation details).  Returns LKV_OK or LKV_EUNSUPPORTED. */
+int lkv_chunk_layout(int32_t head_dim, int32_t group_size, int32_t k_bits, int32_t v_bits,
+                     int64_t off[7]);
+
+/* Quantise and append new rows.
+ * Group-wise asymmetric integer quantisation with an fp32 scale and an integer
+ * zero point per group of group_size channels along head_dim (TurboQuant
+ * page, core innovation), at 6 bits for K and 4 bits for V, or fp16 for
+ * precision-sensitive layers (Super KV Compression page, first layer).  Per
+ * group, in fp32 with no contraction and correctly rounded division:
+ *   constant group c: (s, z, q) = (c, 0, 1), (-c, 1, 0) or (0, 0, 0);
+ *   otherwise lo = min(min x, 0), hi = max(max x, 0), s = (hi - lo) / qmax,
+ *   z = clamp(rint(-lo / s)), q = clamp(rint(x / s) + z), qmax = 2^bits - 1,
+ *   rint rounding half to even.
+ * k, v       [total_new][num_kv_heads][head_dim] in `dtype` (LKV_F32/BF16/F16)
+ * cu_new     [batch+1] int32, rows of sequence b are cu_new[b] .. cu_new[b+1]-1
+ * start_pos  [batch] int32, cache position of the first new row of b
+ * block_table[batch][max_blocks]; every block the rows land in must be mapped
+ * max_new    (host) upper bound of cu_new[b+1]-cu_new[b]; sizes the grid
+ * Writes the rows' codes, scales and zeros and nothing else in the pool.
+ * Sequence lengths are not updated: the caller advances its seq_lens. */
+int lkv_quant_append(const lkv_cache* cache, const void* k, const void* v, int32_t dtype,
+                     const int32_t* cu_new, const int32_t* start_pos,
+                     const int32_t* block_table, int32_t max_blocks,
+                     int32_t batch, int32_t max_new, void* stream);
+
+/* Split plan of lkv_decode_attn: a multiple of 64 tokens per split, chosen
+ * from the shapes alone (deterministic).  (host) */
+int lkv_decode_plan(const lkv_cache* segs, const lkv_view* views, int32_t nseg,
+                    int32_t batch, int32_t num_q_heads, int32_t* split_tokens);
+
+/* Bytes of workspace lkv_decode_attn needs for a split size (host):
+ * fp32 partials [batch][num_q_heads][total_splits][head_dim + 2]. */
+int64_t lkv_decode_workspace_bytes(const lkv_cache* segs, const lkv_view* views, int32_t nseg,
+                                   int32_t batch, int32_t num_q_heads, int32_t split_tokens);
+
+/* Decode attention over the packed cache.
+ * For each sequence b and query head h (KV head h / (num_q_heads /
+ * num_kv_heads)), softmax(sm_scale * q . k_hat) over every live token of
+ * every segment (segments in order; nseg 1, or 2 for a tiered cache {HIGH,
+ * MID}), weighted sum of v_hat, where k_hat, v_hat = (q - z) * s.  Tokens are
+ * processed per split of split_tokens (0 = lkv_decode_plan's choice),
+ * counted from the start of each segment, and per 64-token block inside a
+ * split.  Sparse-V skip (Super KV Compression page, third layer): after a
+ * block's scores are folded into the split's running maximum m and sum L,
+ * the V term of token j for head h is skipped when
+ *   exp(s_j - m) < tau_low * L;
+ * skipped tokens stay in the softmax denominator.  tau_low <= 0 skips
+ * nothing.  Partial results of the splits are merged by a second kernel.
+ * q          [batch][num_q_heads][head_dim] in q_dtype (LKV_F32 or LKV_BF16)
+ * out        [batch][num_q_heads][head_dim] fp32
+ * workspace  lkv_decode_workspace_bytes() bytes, 256-byte aligned
+ * The cache is only read. */
+int lkv_decode_attn(const lkv_cache* segs, const lkv_view* views, int32_t nseg,
+                    const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+                    float sm_scale, float tau_low, int32_t split_tokens,
+                    float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The two stages of lkv_decode_attn, for callers that schedule them apart
+ * (lkv_decode_attn is exactly lkv_decode_split followed by
+ * lkv_decode_combine on the same stream).  split_tokens must be the
+ * resolved (non-zero) split size. */
+int lkv_decode_split(const lkv_cache* segs, const lkv_view* views, int32_t nseg,
+                     const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+                     float sm_scale, float tau_low, int32_t split_tokens,
+                     void* workspace, size_t workspace_bytes, void* stream);
+int lkv_decode_combine(const lkv_cache* segs, const lkv_view* views, int32_t nseg,
+                       int32_t batch, int32_t num_q_heads, int32_t split_tokens,
+                       float* out, const void* workspace, size_t workspace_bytes, void* stream);
+
+/* Thresholds from the quantisation error bound (Super KV Compression page,
+ * second layer), for n live tokens (host):
+ *   tau_low = eps4 / n,  tau_high = (eps4 / eps6) / n,  eps_b = 1/(2(2^b - 1)).
+ * Evicting every token of weight < tau_low moves an output by at most
+ * eps4 * max|v|, the 4-bit half-step relative to a group's range. */
+void lkv_default_thresholds(int32_t n_tokens, float* tau_low, float* tau_high);
+
+/* Workspace bytes of lkv_tier_update (host). */
+int64_t lkv_tier_workspace_bytes(int32_t batch, int32_t scores_stride);
+
+/* Attention-aware tier update (Super KV Compression page, second layer).
+ * src is a K6/V6 cache.  For token j < seq_len[b] with score s = scores[b][j]:
+ *   s >= tau_high             HIGH: K6 row and V6 row copied bit for bit into
+ *                             dst_h (K6/V6)
+ *   tau_low <= s < tau_high   MID: K6 row copied, V dequantised in fp32
+ *                             ((q - z) * s) and requantised at 4 bits into
+ *                             dst_m (K6/V4)
+ *   s < tau_low               LOW: evicted
+ * Survivors are written from position 0 of their destination in increasing
+ * token order (block tables h_block_table, m_block_table).  tiers[b][j]
+ * receives 2, 1 or 0 for j < seq_len[b]; n_high[b], n_mid[b] the counts.  If
+ * a destination has fewer than the count's slots (max_blocks * 64), the
+ * count is returned negated and nothing is written to either destination for
+ * that sequence.  scores, tiers: [batch][scores_stride]; workspace:
+ * lkv_tier_workspace_bytes() bytes.  src is only read. */
+int lkv_tier_update(const lkv_cache* src, const lkv_view* src_view,
+                    const float* scores, int32_t scores_stride, float tau_low, float tau_high,
+                    const lkv_cache* dst_h, const int32_t* h_block_table, int32_t h_max_blocks,
+                    const lkv_cache* dst_m, const int32_t* m_block_table, int32_t m_max_blocks,
+                    int32_t* n_high, int32_t* n_mid, uint8_t* tiers, int32_t batch,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LKV_H */

@@ -1,0 +1,70 @@
+"""Build the HIP library liblkv.so for gfx950 with hipcc (in-tree).
+
+    python -m quantized_kv_cache_token_amd.build
+
+Kernels that compute quantisation codes (append, tier update) are compiled
+with -ffp-contract=off so that their fp32 arithmetic is exactly the stated
+sequence of IEEE operations.  Packed-fp32 instructions are disabled for all
+device code.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "liblkv.so")
+
+ARCH = "gfx950"
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall"]
+SOURCES = [
+    ("append.hip", ["-ffp-contract=off"]),
+    ("tier.hip", ["-ffp-contract=off"]),
+    ("decode.hip", []),
+    ("decode_mfma.hip", []),
+    ("api.cpp", ["-x", "hip"]),
+]
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    cc = hipcc()
+    objs = []
+    for src, extra in SOURCES:
+        path = os.path.join(CSRC, src)
+        if not os.path.exists(path):
+            continue
+        obj = os.path.join(BUILD, src.replace(".", "_") + ".o")
+        cmd = [cc, *COMMON, *extra, "-c", path, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError(f"hipcc failed on {src}")
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("link failed")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,274 @@
+// api.cpp -- the C ABI of include/lkv.h: host-side validation, split plans
+// and kernel launches.  No allocation, no synchronisation, no global state.
+#include <stdint.h>
+#include <string.h>
+
+#include <cmath>
+
+#include "lkv_internal.h"
+
+namespace lkv {
+
+static int64_t pad128(int64_t x) { return (x + 127) / 128 * 128; }
+
+int make_fmt(const lkv_cache* c, Fmt* f)
+{
+    if (!c) return LKV_EINVAL;
+    int64_t off[7];
+    const int st = lkv_chunk_layout(c->head_dim, c->group_size, c->k_bits, c->v_bits, off);
+    if (st != LKV_OK) return st;
+    if (c->block_tokens != BT) return LKV_EUNSUPPORTED;
+    if (c->num_kv_heads < 1 || c->num_blocks < 1 || !c->pool) return LKV_EINVAL;
+    if ((uintptr_t)c->pool % 256 != 0) return LKV_EINVAL;
+    f->D = c->head_dim;
+    f->g = c->group_size;
+    f->kb = c->k_bits;
+    f->vb = c->v_bits;
+    f->H = c->num_kv_heads;
+    f->fp16 = c->k_bits == 16;
+    f->ngroups = f->fp16 ? 0 : c->head_dim / c->group_size;
+    f->off_kc = (int32_t)off[0];
+    f->off_vc = (int32_t)off[1];
+    f->off_ks = (int32_t)off[2];
+    f->off_vs = (int32_t)off[3];
+    f->off_kz = (int32_t)off[4];
+    f->off_vz = (int32_t)off[5];
+    f->chunk = off[6];
+    f->krow = c->head_dim * c->k_bits / 8;
+    f->vrow = BT * c->v_bits / 8;
+    return LKV_OK;
+}
+
+static bool g_supported(int G) { return G == 1 || G == 2 || G == 4 || G == 8 || G == 16; }
+
+// Checks shared by the decode entry points; fills one Fmt per segment.
+static int check_decode(const lkv_cache* segs, const lkv_view* views, int32_t nseg, int32_t batch,
+                        int32_t num_q_heads, Fmt* f)
+{
+    if (!segs || !views || nseg < 1 || nseg > 2 || batch < 0 || num_q_heads < 1) return LKV_EINVAL;
+    for (int s = 0; s < nseg; s++) {
+        const int st = make_fmt(&segs[s], &f[s]);
+        if (st != LKV_OK) return st;
+        if (f[s].D != f[0].D || f[s].H != f[0].H) return LKV_EINVAL;
+        const lkv_view& v = views[s];
+        if (v.max_blocks < 1 || v.max_len < 0 || (int64_t)v.max_len > (int64_t)v.max_blocks * BT)
+            return LKV_EINVAL;
+        if (batch > 0 && (!v.block_table || !v.seq_lens)) return LKV_EINVAL;
+    }
+    if (num_q_heads % f[0].H != 0) return LKV_EINVAL;
+    if (!g_supported(num_q_heads / f[0].H)) return LKV_EUNSUPPORTED;
+    return LKV_OK;
+}
+
+static int32_t splits_of(int32_t max_len, int32_t split_tokens)
+{
+    return (max_len + split_tokens - 1) / split_tokens;
+}
+
+static int64_t total_splits(const lkv_view* views, int32_t nseg, int32_t split_tokens)
+{
+    int64_t n = 0;
+    for (int s = 0; s < nseg; s++) n += splits_of(views[s].max_len, split_tokens);
+    return n;
+}
+
+}  // namespace lkv
+
+using namespace lkv;
+
+extern "C" {
+
+const char* lkv_status_string(int status)
+{
+    switch (status) {
+    case LKV_OK: return "ok";
+    case LKV_EINVAL: return "invalid argument";
+    case LKV_EUNSUPPORTED: return "unsupported format or shape";
+    case LKV_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+int lkv_chunk_layout(int32_t head_dim, int32_t group_size, int32_t k_bits, int32_t v_bits, int64_t off[7])
+{
+    if (!off) return LKV_EINVAL;
+    if (head_dim != 64 && head_dim != 128) return LKV_EUNSUPPORTED;
+    const bool fp16 = k_bits == 16 && v_bits == 16;
+    const bool q_ok = (k_bits == 4 || k_bits == 6) && (v_bits == 4 || v_bits == 6);
+    if (!fp16 && !q_ok) return LKV_EUNSUPPORTED;
+    if (!fp16 && !(group_size == 16 || group_size == 32 || group_size == 64)) return LKV_EUNSUPPORTED;
+    if (!fp16 && head_dim % group_size != 0) return LKV_EUNSUPPORTED;
+    const int64_t ng = fp16 ? 0 : head_dim / group_size;
+    const int64_t sz[6] = {(int64_t)BT * head_dim * k_bits / 8, (int64_t)head_dim * BT * v_bits / 8,
+                           ng * BT * 4, ng * BT * 4, ng * BT, ng * BT};
+    int64_t at = 0;
+    for (int i = 0; i < 6; i++) {
+        off[i] = at;
+        at += pad128(sz[i]);
+    }
+    off[6] = at;
+    return LKV_OK;
+}
+
+int lkv_quant_append(const lkv_cache* cache, const void* k, const void* v, int32_t dtype,
+                     const int32_t* cu_new, const int32_t* start_pos, const int32_t* block_table,
+                     int32_t max_blocks, int32_t batch, int32_t max_new, void* stream)
+{
+    Fmt f;
+    const int st = make_fmt(cache, &f);
+    if (st != LKV_OK) return st;
+    if (batch < 0 || max_new < 0 || max_blocks < 1) return LKV_EINVAL;
+    if (dtype != LKV_F32 && dtype != LKV_BF16 && dtype != LKV_F16) return LKV_EINVAL;
+    if (batch == 0 || max_new == 0) return LKV_OK;
+    if (!k || !v || !cu_new || !start_pos || !block_table) return LKV_EINVAL;
+    const hipError_t e = launch_append(f, (uint8_t*)cache->pool, k, v, dtype, cu_new, start_pos, block_table,
+                                       max_blocks, batch, max_new, (hipStream_t)stream);
+    return e == hipSuccess ? LKV_OK : LKV_EHIP;
+}
+
+int lkv_decode_plan(const lkv_cache* segs, const lkv_view* views, int32_t nseg, int32_t batch,
+                    int32_t num_q_heads, int32_t* split_tokens)
+{
+    Fmt f[2];
+    if (!split_tokens) return LKV_EINVAL;
+    const int st = check_decode(segs, views, nseg, batch, num_q_heads, f);
+    if (st != LKV_OK) return st;
+    // Aim at about 2048 single-wave work items (8 per compute unit on a
+    // 256-CU part), never fewer than one 64-token block nor more than 64
+    // blocks per split.
+    int64_t blocks = 0;
+    for (int s = 0; s < nseg; s++) blocks += (int64_t)batch * f[0].H * ((views[s].max_len + BT - 1) / BT);
+    int64_t per = (blocks + 2047) / 2048;
+    if (per < 1) per = 1;
+    if (per > 64) per = 64;
+    *split_tokens = (int32_t)(per * BT);
+    return LKV_OK;
+}
+
+int64_t lkv_decode_workspace_bytes(const lkv_cache* segs, const lkv_view* views, int32_t nseg, int32_t batch,
+                                   int32_t num_q_heads, int32_t split_tokens)
+{
+    Fmt f[2];
+    const int st = check_decode(segs, views, nseg, batch, num_q_heads, f);
+    if (st != LKV_OK) return st;
+    if (split_tokens <= 0 || split_tokens % BT != 0) return LKV_EINVAL;
+    return (int64_t)batch * num_q_heads * total_splits(views, nseg, split_tokens) * (f[0].D + 2) * 4;
+}
+
+int lkv_decode_split(const lkv_cache* segs, const lkv_view* views, int32_t nseg, const void* q, int32_t q_dtype,
+                     int32_t batch, int32_t num_q_heads, float sm_scale, float tau_low, int32_t split_tokens,
+                     void* workspace, size_t workspace_bytes, void* stream)
+{
+    Fmt f[2];
+    const int st = check_decode(segs, views, nseg, batch, num_q_heads, f);
+    if (st != LKV_OK) return st;
+    if (q_dtype != LKV_F32 && q_dtype != LKV_BF16) return LKV_EINVAL;
+    if (split_tokens <= 0 || split_tokens % BT != 0) return LKV_EINVAL;
+    if (!std::isfinite(sm_scale) || std::isnan(tau_low)) return LKV_EINVAL;
+    const int64_t need = (int64_t)batch * num_q_heads * total_splits(views, nseg, split_tokens) * (f[0].D + 2) * 4;
+    if ((int64_t)workspace_bytes < need) return LKV_EINVAL;
+    if (batch == 0) return LKV_OK;
+    if (!q || (need > 0 && !workspace) || (uintptr_t)workspace % 16 != 0) return LKV_EINVAL;
+    const int32_t tot = (int32_t)total_splits(views, nseg, split_tokens);
+    int32_t base = 0;
+    for (int s = 0; s < nseg; s++) {
+        SegArgs a;
+        a.f = f[s];
+        a.pool = (const uint8_t*)segs[s].pool;
+        a.block_table = views[s].block_table;
+        a.seq_lens = views[s].seq_lens;
+        a.max_blocks = views[s].max_blocks;
+        a.n_splits = splits_of(views[s].max_len, split_tokens);
+        a.split_base = base;
+        base += a.n_splits;
+        const hipError_t e = launch_decode_split(a, q, q_dtype, batch, num_q_heads, sm_scale, tau_low, split_tokens,
+                                                 tot, (float*)workspace, (hipStream_t)stream);
+        if (e != hipSuccess) return LKV_EHIP;
+    }
+    return LKV_OK;
+}
+
+int lkv_decode_combine(const lkv_cache* segs, const lkv_view* views, int32_t nseg, int32_t batch,
+                       int32_t num_q_heads, int32_t split_tokens, float* out, const void* workspace,
+                       size_t workspace_bytes, void* stream)
+{
+    Fmt f[2];
+    const int st = check_decode(segs, views, nseg, batch, num_q_heads, f);
+    if (st != LKV_OK) return st;
+    if (split_tokens <= 0 || split_tokens % BT != 0) return LKV_EINVAL;
+    const int64_t tot = total_splits(views, nseg, split_tokens);
+    const int64_t need = (int64_t)batch * num_q_heads * tot * (f[0].D + 2) * 4;
+    if ((int64_t)workspace_bytes < need) return LKV_EINVAL;
+    if (batch == 0) return LKV_OK;
+    if (!out || (need > 0 && !workspace)) return LKV_EINVAL;
+    const hipError_t e = launch_decode_combine(batch, num_q_heads, f[0].D, (int32_t)tot, (const float*)workspace,
+                                               out, (hipStream_t)stream);
+    return e == hipSuccess ? LKV_OK : LKV_EHIP;
+}
+
+int lkv_decode_attn(const lkv_cache* segs, const lkv_view* views, int32_t nseg, const void* q, int32_t q_dtype,
+                    int32_t batch, int32_t num_q_heads, float sm_scale, float tau_low, int32_t split_tokens,
+                    float* out, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (split_tokens == 0) {
+        const int st = lkv_decode_plan(segs, views, nseg, batch, num_q_heads, &split_tokens);
+        if (st != LKV_OK) return st;
+    }
+    if (batch > 0 && !out) return LKV_EINVAL;
+    int st = lkv_decode_split(segs, views, nseg, q, q_dtype, batch, num_q_heads, sm_scale, tau_low, split_tokens,
+                              workspace, workspace_bytes, stream);
+    if (st != LKV_OK) return st;
+    return lkv_decode_combine(segs, views, nseg, batch, num_q_heads, split_tokens, out, workspace, workspace_bytes,
+                              stream);
+}
+
+void lkv_default_thresholds(int32_t n_tokens, float* tau_low, float* tau_high)
+{
+    const double eps4 = 1.0 / (2.0 * 15.0);  // half a 4-bit step over the group range
+    const double eps6 = 1.0 / (2.0 * 63.0);  // half a 6-bit step
+    const double n = n_tokens > 0 ? (double)n_tokens : 1.0;
+    if (tau_low) *tau_low = (float)(eps4 / n);
+    if (tau_high) *tau_high = (float)((eps4 / eps6) / n);
+}
+
+int64_t lkv_tier_workspace_bytes(int32_t batch, int32_t scores_stride)
+{
+    if (batch < 0 || scores_stride < 0) return LKV_EINVAL;
+    return 2 * (int64_t)batch * scores_stride * 4;
+}
+
+int lkv_tier_update(const lkv_cache* src, const lkv_view* src_view, const float* scores, int32_t scores_stride,
+                    float tau_low, float tau_high, const lkv_cache* dst_h, const int32_t* h_block_table,
+                    int32_t h_max_blocks, const lkv_cache* dst_m, const int32_t* m_block_table,
+                    int32_t m_max_blocks, int32_t* n_high, int32_t* n_mid, uint8_t* tiers, int32_t batch,
+                    void* workspace, size_t workspace_bytes, void* stream)
+{
+    Fmt fs, fh, fm;
+    int st = make_fmt(src, &fs);
+    if (st != LKV_OK) return st;
+    if ((st = make_fmt(dst_h, &fh)) != LKV_OK) return st;
+    if ((st = make_fmt(dst_m, &fm)) != LKV_OK) return st;
+    if (fs.fp16 || fs.vb != 6) return LKV_EUNSUPPORTED;
+    if (fh.D != fs.D || fh.g != fs.g || fh.H != fs.H || fh.kb != fs.kb || fh.vb != 6) return LKV_EINVAL;
+    if (fm.D != fs.D || fm.g != fs.g || fm.H != fs.H || fm.kb != fs.kb || fm.vb != 4) return LKV_EINVAL;
+    if (!src_view || batch < 0 || scores_stride < 0 || h_max_blocks < 1 || m_max_blocks < 1) return LKV_EINVAL;
+    if (src_view->max_blocks < 1 || src_view->max_len < 0 || src_view->max_len > scores_stride ||
+        (int64_t)src_view->max_len > (int64_t)src_view->max_blocks * BT)
+        return LKV_EINVAL;
+    if (std::isnan(tau_low) || std::isnan(tau_high)) return LKV_EINVAL;
+    if ((int64_t)workspace_bytes < lkv_tier_workspace_bytes(batch, scores_stride)) return LKV_EINVAL;
+    if (batch == 0) return LKV_OK;
+    if (!src_view->block_table || !src_view->seq_lens || !scores || !h_block_table || !m_block_table || !n_high ||
+        !n_mid || !tiers || (scores_stride > 0 && !workspace))
+        return LKV_EINVAL;
+    int32_t* h_src = (int32_t*)workspace;
+    int32_t* m_src = h_src + (int64_t)batch * scores_stride;
+    const hipError_t e = launch_tier_update(
+        fs, (const uint8_t*)src->pool, src_view->block_table, src_view->seq_lens, src_view->max_blocks,
+        src_view->max_len, scores, scores_stride, tau_low, tau_high, fh, (uint8_t*)dst_h->pool, h_block_table,
+        h_max_blocks, fm, (uint8_t*)dst_m->pool, m_block_table, m_max_blocks, n_high, n_mid, tiers, batch, h_src,
+        m_src, (hipStream_t)stream);
+    return e == hipSuccess ? LKV_OK : LKV_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,210 @@
+// decode.hip -- split-K decode attention over the packed cache (generic
+// vector-ALU kernel, every format and query dtype) and the merge of split
+// partials.
+//
+// Work unit: one wave per (split, KV head, sequence).  A split walks its
+// 64-token blocks in order; lane j holds token j of the block for the scores,
+// and channels lane + 64 i for the V accumulation.  Per block and query head
+// the running maximum m and sum L are updated (online softmax), the sparse-V
+// rule of the Super KV Compression page (third layer) drops the V term of a
+// token whose exp(s - m) < tau_low * L, and the accumulators are rescaled.
+// The partial (o[D], m, L) of every split is written to the workspace; the
+// combine kernel merges them.
+#include <hip/hip_fp16.h>
+
+#include "lkv_internal.h"
+#include "quant_device.h"
+
+namespace lkv {
+
+struct SplitArgs {
+    SegArgs seg;
+    const void* q;
+    int32_t q_dtype;
+    int32_t num_q_heads;
+    int32_t split_tokens;
+    int32_t total_splits;
+    float sm_scale;
+    float tau_low;
+    float* partials;
+};
+
+__device__ __forceinline__ float wave_max(float x)
+{
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+    return x;
+}
+__device__ __forceinline__ float wave_sum(float x)
+{
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+// Dequantised K element (token slot j, channel d) and V element.
+__device__ __forceinline__ float deq_k(const uint8_t* ch, const Fmt& f, int j, int d)
+{
+    const uint32_t c = get_field((const uint32_t*)(ch + f.off_kc + j * f.krow), d, f.kb);
+    if (f.fp16) return __half2float(__ushort_as_half((uint16_t)c));
+    const int gi = d / f.g;
+    const float s = ((const float*)(ch + f.off_ks))[gi * BT + j];
+    const int z = ch[f.off_kz + gi * BT + j];
+    return (float)((int)c - z) * s;
+}
+__device__ __forceinline__ float deq_v(const uint8_t* ch, const Fmt& f, int j, int d)
+{
+    const uint32_t c = get_field((const uint32_t*)(ch + f.off_vc + d * f.vrow), j, f.vb);
+    if (f.fp16) return __half2float(__ushort_as_half((uint16_t)c));
+    const int gi = d / f.g;
+    const float s = ((const float*)(ch + f.off_vs))[gi * BT + j];
+    const int z = ch[f.off_vz + gi * BT + j];
+    return (float)((int)c - z) * s;
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(64) void split_valu_kernel(SplitArgs a)
+{
+    constexpr int VPL = D / 64;
+    const SegArgs& sg = a.seg;
+    const Fmt& f = sg.f;
+    const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x;
+    const int len = max(0, min(sg.seq_lens[b], sg.max_blocks * BT));  // out-of-contract lengths are clamped
+    const int t0 = sp * a.split_tokens;
+    const int t1 = min(t0 + a.split_tokens, len);
+
+    __shared__ float qs[G][D];
+    __shared__ float ps[G][BT];
+    for (int i = lane; i < G * D; i += 64) {
+        const int h = i / D, d = i % D;
+        qs[h][d] = load_as_float(a.q, ((int64_t)b * a.num_q_heads + kvh * G + h) * D + d, a.q_dtype);
+    }
+    __syncthreads();
+
+    float m[G], L[G], o[G][VPL];
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        m[h] = -INFINITY;
+        L[h] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < VPL; i++) o[h][i] = 0.0f;
+    }
+
+    for (int bs = t0; bs < t1; bs += BT) {
+        const int64_t blk = sg.block_table[(int64_t)b * sg.max_blocks + bs / BT];
+        const uint8_t* ch = sg.pool + (blk * f.H + kvh) * f.chunk;
+        const int nlive = min(BT, t1 - bs);
+        const bool live = lane < nlive;
+        float s[G];
+#pragma unroll
+        for (int h = 0; h < G; h++) s[h] = 0.0f;
+        if (live) {
+            for (int d = 0; d < D; d++) {
+                const float kh = deq_k(ch, f, lane, d);
+#pragma unroll
+                for (int h = 0; h < G; h++) s[h] += qs[h][d] * kh;
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+            const float sc = live ? s[h] * a.sm_scale : -INFINITY;
+            const float m_new = fmaxf(m[h], wave_max(sc));
+            const float e = live ? __expf(sc - m_new) : 0.0f;
+            const float alpha = __expf(m[h] - m_new);
+            L[h] = L[h] * alpha + wave_sum(e);
+            m[h] = m_new;
+            const bool skip = a.tau_low > 0.0f && e < a.tau_low * L[h];
+            ps[h][lane] = skip ? 0.0f : e;
+#pragma unroll
+            for (int i = 0; i < VPL; i++) o[h][i] *= alpha;
+        }
+        __syncthreads();
+        for (int j = 0; j < nlive; j++) {
+#pragma unroll
+            for (int i = 0; i < VPL; i++) {
+                const float vh = deq_v(ch, f, j, lane + 64 * i);
+#pragma unroll
+                for (int h = 0; h < G; h++) o[h][i] += ps[h][j] * vh;
+            }
+        }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        float* p = a.partials +
+                   (((int64_t)b * a.num_q_heads + kvh * G + h) * a.total_splits + sg.split_base + sp) * (D + 2);
+#pragma unroll
+        for (int i = 0; i < VPL; i++) p[lane + 64 * i] = o[h][i];
+        if (lane == 0) {
+            p[D] = m[h];
+            p[D + 1] = L[h];
+        }
+    }
+}
+
+template <int D>
+static hipError_t launch_valu_d(const SplitArgs& a, int G, dim3 grid, hipStream_t st)
+{
+    switch (G) {
+    case 1: hipLaunchKernelGGL((split_valu_kernel<D, 1>), grid, dim3(64), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((split_valu_kernel<D, 2>), grid, dim3(64), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((split_valu_kernel<D, 4>), grid, dim3(64), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((split_valu_kernel<D, 8>), grid, dim3(64), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((split_valu_kernel<D, 16>), grid, dim3(64), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_split(const SegArgs& s, const void* q, int q_dtype, int32_t batch,
+                               int32_t num_q_heads, float sm_scale, float tau_low,
+                               int32_t split_tokens, int32_t total_splits, float* partials,
+                               hipStream_t stream)
+{
+    if (batch == 0 || s.n_splits == 0) return hipSuccess;
+    SplitArgs a;
+    a.seg = s;
+    a.q = q;
+    a.q_dtype = q_dtype;
+    a.num_q_heads = num_q_heads;
+    a.split_tokens = split_tokens;
+    a.total_splits = total_splits;
+    a.sm_scale = sm_scale;
+    a.tau_low = tau_low;
+    a.partials = partials;
+    const int G = num_q_heads / s.f.H;
+    dim3 grid((unsigned)s.n_splits, (unsigned)s.f.H, (unsigned)batch);
+    return s.f.D == 64 ? launch_valu_d<64>(a, G, grid, stream) : launch_valu_d<128>(a, G, grid, stream);
+}
+
+// Merge of the split partials of one (sequence, query head):
+//   M = max_i m_i,  O = sum_i o_i e^(m_i - M) / sum_i L_i e^(m_i - M).
+__global__ void combine_kernel(int32_t num_q_heads, int32_t D, int32_t total_splits,
+                               const float* __restrict__ part, float* __restrict__ out)
+{
+    const int64_t bh = blockIdx.x;
+    const int d = threadIdx.x;
+    const float* p = part + bh * total_splits * (D + 2);
+    float M = -INFINITY;
+    for (int i = 0; i < total_splits; i++) M = fmaxf(M, p[i * (D + 2) + D]);
+    float L = 0.0f, acc = 0.0f;
+    for (int i = 0; i < total_splits; i++) {
+        const float mi = p[i * (D + 2) + D];
+        if (mi == -INFINITY) continue;
+        const float w = __expf(mi - M);
+        L += p[i * (D + 2) + D + 1] * w;
+        acc += p[i * (D + 2) + d] * w;
+    }
+    out[bh * D + d] = L > 0.0f ? acc / L : 0.0f;
+}
+
+hipError_t launch_decode_combine(int32_t batch, int32_t num_q_heads, int32_t D, int32_t total_splits,
+                                 const float* partials, float* out, hipStream_t stream)
+{
+    if (batch == 0) return hipSuccess;
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(batch * num_q_heads)), dim3((unsigned)D), 0, stream,
+                       num_q_heads, D, total_splits, partials, out);
+    return hipGetLastError();
+}
+
+}  // namespace lkv

@@ -1,0 +1,59 @@
+// lkv_internal.h -- shared declarations of the HIP library (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lkv.h"
+
+namespace lkv {
+
+constexpr int BT = LKV_BLOCK_TOKENS;  // tokens per block / chunk
+
+// Resolved cache format: byte offsets of the six chunk sections.
+struct Fmt {
+    int32_t D, g, kb, vb, H, ngroups;
+    int32_t fp16;                                     // k_bits == v_bits == 16
+    int32_t off_kc, off_vc, off_ks, off_vs, off_kz, off_vz;
+    int32_t krow;                                     // bytes of one K token row
+    int32_t vrow;                                     // bytes of one V channel row
+    int64_t chunk;                                    // bytes of one chunk
+};
+
+// Fills f from a cache descriptor; returns LKV_OK, LKV_EINVAL or
+// LKV_EUNSUPPORTED.
+int make_fmt(const lkv_cache* c, Fmt* f);
+
+// One segment of a decode call, as the split kernel sees it.
+struct SegArgs {
+    Fmt f;
+    const uint8_t* pool;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    int32_t max_blocks;
+    int32_t n_splits;      // splits of this segment in the grid
+    int32_t split_base;    // index of its first split in the partials
+};
+
+hipError_t launch_append(const Fmt& f, uint8_t* pool, const void* k, const void* v, int dtype,
+                         const int32_t* cu_new, const int32_t* start_pos, const int32_t* block_table,
+                         int32_t max_blocks, int32_t batch, int32_t max_new, hipStream_t stream);
+
+// Partials: fp32 [batch][Hq][total_splits][D + 2] = (o[D], m, L).
+hipError_t launch_decode_split(const SegArgs& s, const void* q, int q_dtype, int32_t batch,
+                               int32_t num_q_heads, float sm_scale, float tau_low,
+                               int32_t split_tokens, int32_t total_splits, float* partials,
+                               hipStream_t stream);
+
+hipError_t launch_decode_combine(int32_t batch, int32_t num_q_heads, int32_t D, int32_t total_splits,
+                                 const float* partials, float* out, hipStream_t stream);
+
+hipError_t launch_tier_update(const Fmt& fs, const uint8_t* src_pool, const int32_t* src_bt,
+                              const int32_t* src_lens, int32_t src_max_blocks, int32_t max_len,
+                              const float* scores, int32_t stride, float tau_low, float tau_high,
+                              const Fmt& fh, uint8_t* h_pool, const int32_t* h_bt, int32_t h_max_blocks,
+                              const Fmt& fm, uint8_t* m_pool, const int32_t* m_bt, int32_t m_max_blocks,
+                              int32_t* n_high, int32_t* n_mid, uint8_t* tiers, int32_t batch,
+                              int32_t* h_src, int32_t* m_src, hipStream_t stream);
+
+}  // namespace lkv

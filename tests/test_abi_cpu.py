@@ -1,0 +1,131 @@
+"""The C ABI without a GPU: the library loads, exports every function
+include/lkv.h declares, and rejects bad arguments on the host before any
+launch.  No call here reaches a kernel."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+from quantized_kv_cache_token_amd import lkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "lkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lkv_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = lkv.lib()
+    names = _declared()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(lkv.EXPORTS) == names
+
+
+def test_chunk_layout_matches_the_oracle():
+    for fmt in [(128, 64, 6, 4), (64, 32, 6, 4), (128, 64, 6, 6), (128, 64, 4, 4), (128, 64, 16, 16),
+                (64, 16, 6, 6), (128, 32, 4, 6)]:
+        assert lkv.chunk_layout(*fmt) == O.chunk_layout(*fmt)
+    for bad in [(96, 32, 6, 4), (128, 48, 6, 4), (128, 64, 5, 4), (128, 64, 16, 4), (128, 128, 6, 4)]:
+        with pytest.raises(lkv.LkvError):
+            lkv.chunk_layout(*bad)
+
+
+def test_default_thresholds_bit_exact_with_the_oracle():
+    for n in [1, 7, 256, 3277, 13107, 32768, 131072]:
+        assert lkv.default_thresholds(n) == O.default_thresholds(n)
+
+
+def _cache(pool=0x10000, **kw):
+    d = dict(head_dim=128, group_size=64, k_bits=6, v_bits=4, num_kv_heads=8, block_tokens=64,
+             num_blocks=16, pool=pool)
+    d.update(kw)
+    return lkv._Cache(**d)
+
+
+def _view(max_len=1024, max_blocks=16):
+    return lkv._View(0x20000, 0x30000, max_blocks, max_len)
+
+
+def test_append_rejects_bad_arguments():
+    L = lkv.lib()
+    k = C.c_void_p(0x40000)
+    args = lambda c, dt=1, bt=C.c_void_p(0x50000), mb=16, b=2, mn=4: L.lkv_quant_append(
+        C.byref(c), k, k, dt, k, k, bt, mb, b, mn, None)
+    assert args(_cache(head_dim=96)) == lkv.EUNSUPPORTED
+    assert args(_cache(k_bits=5)) == lkv.EUNSUPPORTED
+    assert args(_cache(block_tokens=32)) == lkv.EUNSUPPORTED
+    assert args(_cache(pool=0)) == lkv.EINVAL
+    assert args(_cache(pool=0x10010)) == lkv.EINVAL          # not 256-byte aligned
+    assert args(_cache(num_kv_heads=0)) == lkv.EINVAL
+    assert args(_cache(), dt=7) == lkv.EINVAL
+    assert args(_cache(), bt=None) == lkv.EINVAL
+    assert args(_cache(), mb=0) == lkv.EINVAL
+    assert args(_cache(), b=-1) == lkv.EINVAL
+    assert args(_cache(), b=0) == lkv.OK                      # nothing to do, nothing queued
+    assert args(_cache(), mn=0) == lkv.OK
+
+
+def test_decode_rejects_bad_arguments_and_plans_deterministically():
+    L = lkv.lib()
+    q = C.c_void_p(0x60000)
+
+    def call(segs, views, n=1, Hq=32, dt=1, split=1024, ws=1 << 30, b=8, sm=0.088, tau=0.0):
+        cs = (lkv._Cache * len(segs))(*segs)
+        vs = (lkv._View * len(views))(*views)
+        return L.lkv_decode_attn(cs, vs, n, q, dt, b, Hq, sm, tau, split, C.c_void_p(0x70000),
+                                 C.c_void_p(0x80000), ws, None)
+
+    assert call([_cache()], [_view()], n=0) == lkv.EINVAL
+    assert call([_cache()] * 3, [_view()] * 3, n=3) == lkv.EINVAL
+    assert call([_cache()], [_view()], Hq=12) == lkv.EINVAL            # not a multiple of Hkv
+    assert call([_cache()], [_view()], Hq=8 * 3) == lkv.EUNSUPPORTED   # G = 3
+    assert call([_cache()], [_view()], dt=2) == lkv.EINVAL             # fp16 queries
+    assert call([_cache()], [_view()], split=100) == lkv.EINVAL
+    assert call([_cache()], [_view(max_len=2000, max_blocks=16)]) == lkv.EINVAL
+    assert call([_cache()], [_view()], ws=16) == lkv.EINVAL            # workspace too small
+    assert call([_cache()], [_view()], sm=float("inf")) == lkv.EINVAL
+    assert call([_cache(), _cache(head_dim=64, group_size=32)], [_view(), _view()], n=2) == lkv.EINVAL
+    assert call([_cache()], [_view()], b=0) == lkv.OK
+
+    cs = (lkv._Cache * 1)(_cache())
+    vs = (lkv._View * 1)(_view(max_len=32768, max_blocks=512))
+    out = C.c_int32()
+    assert L.lkv_decode_plan(cs, vs, 1, 8, 32, C.byref(out)) == lkv.OK
+    assert out.value == 1024               # 8 x 8 x 512 blocks / 2048 work items = 16 blocks
+    ws = L.lkv_decode_workspace_bytes(cs, vs, 1, 8, 32, 1024)
+    assert ws == 8 * 32 * 32 * 130 * 4
+    vs1 = (lkv._View * 1)(_view(max_len=256, max_blocks=4))
+    cs1 = (lkv._Cache * 1)(_cache(head_dim=64, group_size=32, num_kv_heads=1))
+    assert L.lkv_decode_plan(cs1, vs1, 1, 1, 1, C.byref(out)) == lkv.OK and out.value == 64
+
+
+def test_tier_update_rejects_bad_formats():
+    L = lkv.lib()
+    p = C.c_void_p(0x90000)
+    src, h, m = _cache(v_bits=6), _cache(v_bits=6), _cache(v_bits=4)
+    v = _view(max_len=1024)
+
+    def call(src=src, h=h, m=m, stride=1024, ws=1 << 20):
+        return L.lkv_tier_update(C.byref(src), C.byref(v), p, stride, 1e-6, 1e-4, C.byref(h), p, 16,
+                                 C.byref(m), p, 16, p, p, p, 8, p, ws, None)
+
+    assert call(src=_cache(v_bits=4)) == lkv.EUNSUPPORTED     # the source must hold V6
+    assert call(h=_cache(v_bits=4)) == lkv.EINVAL
+    assert call(m=_cache(v_bits=6)) == lkv.EINVAL
+    assert call(m=_cache(v_bits=4, group_size=32)) == lkv.EINVAL
+    assert call(stride=512) == lkv.EINVAL                      # scores shorter than max_len
+    assert call(ws=100) == lkv.EINVAL
+    assert L.lkv_tier_workspace_bytes(8, 32768) == 2 * 8 * 32768 * 4
+
+
+def test_status_strings():
+    assert lkv.status_string(lkv.OK) == "ok"
+    assert "invalid" in lkv.status_string(lkv.EINVAL)

@@ -1,0 +1,220 @@
+"""GPU parity of the three calls against the oracle on small seeded cases
+that still span several blocks and a ragged tail.  Codes, scales, zeros,
+tiers and counts bit-exact; attention within max|d| <= 1e-3 max|v_hat| and
+relative L2 <= 1e-4."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from quantized_kv_cache_token_amd import inputs, lkv
+from tests.gpu_common import Pair, assert_attention_close, max_abs_vhat, say, sm_scale, to_f32_host
+from tests.oracle_cases import block_tables
+
+pytestmark = pytest.mark.gpu
+
+FORMATS = [(64, 32, 6, 4), (128, 64, 6, 4), (128, 64, 6, 6), (128, 64, 4, 4), (128, 32, 4, 6),
+           (64, 16, 6, 6), (128, 64, 16, 16), (64, 32, 16, 16)]
+
+
+def _fmt_id(f):
+    return "D{}g{}k{}v{}".format(*f)
+
+
+def _prefill(pair: Pair, lens, Hkv, D, dtype, seed, bt, outliers=False):
+    """Append every sequence's rows in one call, and return the inputs."""
+    K, V = [], []
+    out = inputs.outlier_channels(seed, Hkv, D) if outliers else None
+    for b, n in enumerate(lens):
+        k, v = inputs.kv_rows(seed, b, int(n), Hkv, D, dtype=dtype, outliers=out)
+        K.append(k)
+        V.append(v)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    pair.append(torch.cat(K), torch.cat(V), cu, np.zeros(len(lens), np.int32), bt)
+    return K, V
+
+
+@pytest.mark.parametrize("fmt", FORMATS, ids=_fmt_id)
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_append_pool_bit_exact(fmt, dtype):
+    D, g, kb, vb = fmt
+    rng = np.random.default_rng(1)
+    lens = [1, 63, 64, 65, 300]
+    Hkv = 2
+    bt, nblk = block_tables([n + 70 for n in lens], rng)
+    pair = Pair(D, g, kb, vb, Hkv, nblk)
+    say("append prefill", fmt, dtype)
+    _prefill(pair, lens, Hkv, D, dtype, 7, bt, outliers=True)
+    assert pair.pool_equal(), pair.first_pool_mismatch()
+    # then appends of 1 and of 5 rows at ragged positions into partial blocks
+    for step, t in enumerate([1, 5, 1]):
+        say("append step", step, t)
+        k, v = inputs.kv_rows(7, 99, len(lens) * t, Hkv, D, dtype=dtype, step=step + 1)
+        cu = np.arange(len(lens) + 1, dtype=np.int32) * t
+        pair.append(k, v, cu, np.array(lens, np.int32), bt)
+        lens = [n + t for n in lens]
+        assert pair.pool_equal(), pair.first_pool_mismatch()
+
+
+def test_append_special_groups_bit_exact():
+    """Constant, one-sided, tie and zero groups (fp32 inputs)."""
+    D, g = 128, 64
+    rows = []
+    consts = [0.0, -0.0, 1e-30, -1e-30, 1.0, -1.0, np.pi, 1e30, -1e30, 3.3895313892515355e38]
+    for c in consts:
+        rows.append(np.full(D, c, np.float32))
+    rng = np.random.default_rng(3)
+    rows.append(rng.uniform(0.5, 2.0, D).astype(np.float32))
+    rows.append(-rng.uniform(0.5, 2.0, D).astype(np.float32))
+    tie = np.zeros(D, np.float32)
+    tie[:11] = [-7.75, 8.0, 0.125, 0.375, 0.625, 0.875, 1.0, -1.0, 0.0, -0.125, -0.375]
+    tie[64:75] = tie[:11]
+    rows.append(tie)
+    rows.append((1.0 + 1e-6 * rng.standard_normal(D)).astype(np.float32))
+    x = torch.tensor(np.stack(rows))[:, None, :]
+    n = x.shape[0]
+    for kb, vb in [(6, 4), (4, 6), (16, 16)]:
+        pair = Pair(D, g, kb, vb, 1, 2)
+        say("append special groups", kb, vb)
+        pair.append(x, -x, [0, n], [0], np.array([[0, 1]], np.int32))
+        assert pair.pool_equal(), pair.first_pool_mismatch()
+
+
+def _decode_case(fmt, G, qdtype, lens, tau, split, seed=5, Hkv=2, nseg=1):
+    D, g, kb, vb = fmt
+    rng = np.random.default_rng(seed)
+    pairs, views, ref_views = [], [], []
+    for s in range(nseg):
+        seg_lens = [max(0, n - 37 * s) for n in lens]
+        bt, nblk = block_tables([max(n, 1) for n in seg_lens], rng)
+        pair = Pair(D, g, kb, vb, Hkv, nblk)
+        _prefill(pair, seg_lens, Hkv, D, "bf16", seed + s, bt, outliers=True)
+        pairs.append(pair)
+        lt = torch.tensor(seg_lens, dtype=torch.int32)
+        views.append(lkv.View(torch.tensor(bt).cuda(), lt.cuda(), max(seg_lens)))
+        ref_views.append((bt, np.array(seg_lens, np.int32)))
+    q = inputs.queries(seed, len(lens), Hkv * G, D, dtype=qdtype)
+    sm = sm_scale(D)
+    say("decode", fmt, "G", G, qdtype, "lens", lens, "tau", tau, "split", split, "nseg", nseg)
+    out = lkv.decode_attn([p.gpu for p in pairs], views, q.cuda(), sm, tau, split)
+    torch.cuda.synchronize()
+    want = O.decode([p.ref for p in pairs], [v[0] for v in ref_views], [v[1] for v in ref_views],
+                    to_f32_host(q), sm, tau, split)
+    vmax = max(max_abs_vhat(p.ref) for p in pairs)
+    return out.cpu().numpy(), want, vmax
+
+
+@pytest.mark.parametrize("fmt", FORMATS, ids=_fmt_id)
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_decode_parity_formats(fmt, G):
+    got, want, vmax = _decode_case(fmt, G, "bf16", [1, 64, 200, 777], 0.0, 128)
+    assert_attention_close(got, want, vmax, f"{fmt} G{G}")
+
+
+@pytest.mark.parametrize("qdtype", ["f32", "bf16"])
+@pytest.mark.parametrize("split", [64, 256, 1024])
+@pytest.mark.parametrize("tau", [0.0, 1e-5, 2e-4])
+def test_decode_parity_splits_and_skip(qdtype, split, tau):
+    got, want, vmax = _decode_case((128, 64, 6, 4), 4, qdtype, [5, 700, 1500, 2048], tau, split)
+    assert_attention_close(got, want, vmax, f"split {split} tau {tau}")
+
+
+def test_decode_skip_changes_the_result_as_the_oracle_does():
+    """With a large tau the skip moves the output well beyond the tolerance;
+    the GPU follows the oracle with skip, not the oracle without."""
+    fmt = (128, 64, 6, 4)
+    got, want, vmax = _decode_case(fmt, 4, "bf16", [3000, 2500], 2e-4, 512, seed=9)
+    assert_attention_close(got, want, vmax, "skip on")
+    _, want0, _ = _decode_case(fmt, 4, "bf16", [3000, 2500], 0.0, 512, seed=9)
+    assert np.linalg.norm(want - want0) / np.linalg.norm(want0) > 1e-3
+
+
+@pytest.mark.parametrize("fmt", [(128, 64, 6, 6), (128, 64, 6, 4)], ids=_fmt_id)
+def test_decode_two_segments(fmt):
+    got, want, vmax = _decode_case(fmt, 4, "bf16", [40, 300, 129], 1e-5, 64, nseg=2)
+    assert_attention_close(got, want, vmax, "two segments")
+
+
+def test_decode_empty_and_degenerate():
+    """Zero-length sequences give 0; a single token gives its v_hat."""
+    fmt = (128, 64, 6, 4)
+    got, want, vmax = _decode_case(fmt, 4, "bf16", [0, 1, 0, 65], 0.0, 64)
+    assert np.all(got[0] == 0) and np.all(got[2] == 0)
+    assert_attention_close(got, want, vmax, "empty")
+
+
+def test_decode_leaves_the_pool_unchanged():
+    D, g, kb, vb = 128, 64, 6, 4
+    rng = np.random.default_rng(2)
+    bt, nblk = block_tables([500, 300], rng)
+    pair = Pair(D, g, kb, vb, 2, nblk)
+    _prefill(pair, [500, 300], 2, D, "bf16", 3, bt)
+    before = pair.gpu.pool.clone()
+    view = lkv.View(torch.tensor(bt).cuda(), torch.tensor([500, 300], dtype=torch.int32).cuda(), 500)
+    q = inputs.queries(3, 2, 8, D).cuda()
+    say("decode pool unchanged")
+    lkv.decode_attn([pair.gpu], [view], q, sm_scale(D), 1e-4, 128)
+    torch.cuda.synchronize()
+    assert torch.equal(before, pair.gpu.pool)
+
+
+def test_decode_is_deterministic():
+    fmt = (128, 64, 6, 4)
+    a, _, _ = _decode_case(fmt, 8, "bf16", [900, 1300], 1e-5, 256)
+    b, _, _ = _decode_case(fmt, 8, "bf16", [900, 1300], 1e-5, 256)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("lens", [[300, 65, 1, 0], [2000, 1500]])
+def test_tier_update_bit_exact(lens):
+    D, g, Hkv = 128, 64, 2
+    rng = np.random.default_rng(4)
+    stride = max(lens) + 13
+    bt, nblk = block_tables([max(n, 1) for n in lens], rng)
+    src = Pair(D, g, 6, 6, Hkv, nblk)
+    _prefill(src, lens, Hkv, D, "bf16", 11, bt, outliers=True)
+    tl, th = O.default_thresholds(stride)
+    scores = torch.zeros(len(lens), stride)
+    for b, n in enumerate(lens):
+        scores[b, :n] = inputs.tier_scores(11, b, n, tl, th)
+    if lens[0] >= 2:
+        scores[0, 0], scores[0, 1] = tl, th   # exact boundaries
+    hbt, hn = block_tables([max(n, 1) for n in lens], rng)
+    mbt, mn = block_tables([max(n, 1) for n in lens], rng)
+    h, m = Pair(D, g, 6, 6, Hkv, hn), Pair(D, g, 6, 4, Hkv, mn)
+    tiers = torch.full((len(lens), stride), 255, dtype=torch.uint8, device="cuda")
+    nh = torch.zeros(len(lens), dtype=torch.int32, device="cuda")
+    nm = torch.zeros_like(nh)
+    view = lkv.View(torch.tensor(bt).cuda(), torch.tensor(lens, dtype=torch.int32).cuda(), max(lens))
+    say("tier update", lens)
+    lkv.tier_update(src.gpu, view, scores.cuda(), tl, th, h.gpu, torch.tensor(hbt).cuda(), m.gpu,
+                    torch.tensor(mbt).cuda(), nh, nm, tiers)
+    torch.cuda.synchronize()
+    t_ref, nh_ref, nm_ref = O.tier_update(src.ref, bt, np.array(lens, np.int32), scores.numpy(), tl, th,
+                                          h.ref, hbt, m.ref, mbt)
+    assert np.array_equal(nh.cpu().numpy(), nh_ref) and np.array_equal(nm.cpu().numpy(), nm_ref)
+    assert np.array_equal(tiers.cpu().numpy(), t_ref)
+    assert h.pool_equal(), h.first_pool_mismatch()
+    assert m.pool_equal(), m.first_pool_mismatch()
+
+
+def test_tier_update_without_room_writes_nothing():
+    D, g, Hkv = 128, 64, 1
+    lens = [400]
+    bt, nblk = block_tables(lens)
+    src = Pair(D, g, 6, 6, Hkv, nblk)
+    _prefill(src, lens, Hkv, D, "bf16", 12, bt)
+    tl, th = O.default_thresholds(400)
+    scores = torch.full((1, 400), th)             # every token HIGH: 400 > 64 slots
+    h, m = Pair(D, g, 6, 6, Hkv, 1), Pair(D, g, 6, 4, Hkv, 1)
+    tiers = torch.zeros((1, 400), dtype=torch.uint8, device="cuda")
+    nh = torch.zeros(1, dtype=torch.int32, device="cuda")
+    nm = torch.zeros_like(nh)
+    view = lkv.View(torch.tensor(bt).cuda(), torch.tensor(lens, dtype=torch.int32).cuda(), 400)
+    one = torch.zeros((1, 1), dtype=torch.int32, device="cuda")
+    say("tier update without room")
+    lkv.tier_update(src.gpu, view, scores.cuda(), tl, th, h.gpu, one, m.gpu, one, nh, nm, tiers)
+    torch.cuda.synchronize()
+    assert nh.item() == -400 and nm.item() == 0
+    assert int(h.gpu.pool.abs().sum()) == 0 and int(m.gpu.pool.abs().sum()) == 0
+    assert bool((tiers == 2).all())
