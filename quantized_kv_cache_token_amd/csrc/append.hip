@@ -90,14 +90,14 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
         const uint32_t word = pack_word(w, f.kb, 0, D, [&](int c) { return (uint32_t)kc[slot][c]; });
         ((uint32_t*)(ch + f.off_kc + slot * f.krow))[w] = word;
     }
-    // V rows: channel-major; words shared with slots not written by this call
-    // keep their other bits.
-    const int wv = BT * f.vb / 32;
+    // V rows: channel-major; only the words that hold bits of slots [s0, s1)
+    // are touched, and their bits of other slots are kept.
+    const int w0 = (f.vb * s0) / 32, w1 = (f.vb * s1 - 1) / 32;
+    const int wv = w1 - w0 + 1;
     for (int idx = threadIdx.x; idx < D * wv; idx += blockDim.x) {
         const int d = idx / wv;
-        const int w = idx % wv;
+        const int w = w0 + idx % wv;
         const uint32_t mask = field_mask(w, f.vb, s0, s1);
-        if (mask == 0) continue;
         uint32_t word = pack_word(w, f.vb, s0, s1, [&](int s) { return (uint32_t)vc[s][d]; });
         uint32_t* dst = (uint32_t*)(ch + f.off_vc + d * f.vrow) + w;
         if (mask != 0xFFFFFFFFu) word = (*dst & ~mask) | (word & mask);

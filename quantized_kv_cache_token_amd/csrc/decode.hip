@@ -24,7 +24,7 @@ struct SplitArgs {
     int32_t num_q_heads;
     int32_t split_tokens;
     int32_t total_splits;
-    float sm_scale;
+    float score_scale;  // sm_scale * log2(e): scores are kept in base 2
     float tau_low;
     float* partials;
 };
@@ -106,10 +106,10 @@ __global__ __launch_bounds__(64) void split_valu_kernel(SplitArgs a)
         }
 #pragma unroll
         for (int h = 0; h < G; h++) {
-            const float sc = live ? s[h] * a.sm_scale : -INFINITY;
+            const float sc = live ? s[h] * a.score_scale : -INFINITY;
             const float m_new = fmaxf(m[h], wave_max(sc));
-            const float e = live ? __expf(sc - m_new) : 0.0f;
-            const float alpha = __expf(m[h] - m_new);
+            const float e = live ? exp2f(sc - m_new) : 0.0f;
+            const float alpha = exp2f(m[h] - m_new);
             L[h] = L[h] * alpha + wave_sum(e);
             m[h] = m_new;
             const bool skip = a.tau_low > 0.0f && e < a.tau_low * L[h];
@@ -162,6 +162,10 @@ hipError_t launch_decode_split(const SegArgs& s, const void* q, int q_dtype, int
                                hipStream_t stream)
 {
     if (batch == 0 || s.n_splits == 0) return hipSuccess;
+    hipError_t err;
+    if (launch_decode_split_mfma(s, q, q_dtype, batch, num_q_heads, sm_scale, tau_low, split_tokens, total_splits,
+                                 partials, stream, &err))
+        return err;
     SplitArgs a;
     a.seg = s;
     a.q = q;
@@ -169,7 +173,7 @@ hipError_t launch_decode_split(const SegArgs& s, const void* q, int q_dtype, int
     a.num_q_heads = num_q_heads;
     a.split_tokens = split_tokens;
     a.total_splits = total_splits;
-    a.sm_scale = sm_scale;
+    a.score_scale = sm_scale * 1.4426950408889634f;
     a.tau_low = tau_low;
     a.partials = partials;
     const int G = num_q_heads / s.f.H;
@@ -177,33 +181,51 @@ hipError_t launch_decode_split(const SegArgs& s, const void* q, int q_dtype, int
     return s.f.D == 64 ? launch_valu_d<64>(a, G, grid, stream) : launch_valu_d<128>(a, G, grid, stream);
 }
 
-// Merge of the split partials of one (sequence, query head):
-//   M = max_i m_i,  O = sum_i o_i e^(m_i - M) / sum_i L_i e^(m_i - M).
-__global__ void combine_kernel(int32_t num_q_heads, int32_t D, int32_t total_splits,
-                               const float* __restrict__ part, float* __restrict__ out)
+// Merge of the split partials of one (sequence, query head), m in base 2:
+//   M = max_i m_i,  O = sum_i o_i 2^(m_i - M) / sum_i L_i 2^(m_i - M).
+// One wave per (sequence, query head): the split maxima and sums are reduced
+// across lanes, then every lane accumulates its channels over the splits
+// with coalesced loads of whole partial rows.
+template <int D>
+__global__ __launch_bounds__(64) void combine_kernel(int32_t total_splits, const float* __restrict__ part,
+                                                     float* __restrict__ out)
 {
+    constexpr int VPL = D / 64;
     const int64_t bh = blockIdx.x;
-    const int d = threadIdx.x;
+    const int lane = threadIdx.x;
     const float* p = part + bh * total_splits * (D + 2);
     float M = -INFINITY;
-    for (int i = 0; i < total_splits; i++) M = fmaxf(M, p[i * (D + 2) + D]);
-    float L = 0.0f, acc = 0.0f;
-    for (int i = 0; i < total_splits; i++) {
-        const float mi = p[i * (D + 2) + D];
-        if (mi == -INFINITY) continue;
-        const float w = __expf(mi - M);
-        L += p[i * (D + 2) + D + 1] * w;
-        acc += p[i * (D + 2) + d] * w;
+    for (int i = lane; i < total_splits; i += 64) M = fmaxf(M, p[(int64_t)i * (D + 2) + D]);
+    M = wave_max(M);
+    float L = 0.0f;
+    for (int i = lane; i < total_splits; i += 64) {
+        const float mi = p[(int64_t)i * (D + 2) + D];
+        if (mi != -INFINITY) L += p[(int64_t)i * (D + 2) + D + 1] * exp2f(mi - M);
     }
-    out[bh * D + d] = L > 0.0f ? acc / L : 0.0f;
+    L = wave_sum(L);
+    float acc[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; j++) acc[j] = 0.0f;
+#pragma unroll 8
+    for (int i = 0; i < total_splits; i++) {
+        const float* pi = p + (int64_t)i * (D + 2);
+        const float mi = pi[D];
+        const float w = mi == -INFINITY ? 0.0f : exp2f(mi - M);
+#pragma unroll
+        for (int j = 0; j < VPL; j++) acc[j] += pi[lane + 64 * j] * w;
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+#pragma unroll
+    for (int j = 0; j < VPL; j++) out[bh * D + lane + 64 * j] = acc[j] * inv;
 }
 
 hipError_t launch_decode_combine(int32_t batch, int32_t num_q_heads, int32_t D, int32_t total_splits,
                                  const float* partials, float* out, hipStream_t stream)
 {
     if (batch == 0) return hipSuccess;
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(batch * num_q_heads)), dim3((unsigned)D), 0, stream,
-                       num_q_heads, D, total_splits, partials, out);
+    const dim3 grid((unsigned)(batch * num_q_heads));
+    if (D == 64) hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(64), 0, stream, total_splits, partials, out);
+    else hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(64), 0, stream, total_splits, partials, out);
     return hipGetLastError();
 }
 

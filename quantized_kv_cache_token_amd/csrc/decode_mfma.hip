@@ -1,0 +1,582 @@
+// decode_mfma.hip -- split-K decode attention with matrix cores (gfx950).
+//
+// For bf16 queries over a K6 cache (V4 or V6), head_dim 128, group 64, and 4
+// or 8 query heads per KV head.  One wave owns one (split, KV head,
+// sequence); a split walks its 64-token blocks in order, 16-token tiles at a
+// time.
+//
+// Q.K (v_mfma_f32_16x16x32_bf16): rows are tokens, columns are (query head,
+// channel group) pairs, so one MFMA produces the per-group dot products
+//   dot'(t, h, g) = sum_{d in g} q_hd * (128 + c_td)
+// where the bf16 A operand is built from the 6-bit code c by placing it in
+// the mantissa of 128.0 (exact); Q is the B operand, masked to the group.
+// The score of a token is then
+//   s(t, h) = sm * sum_g s_g(t) * (dot'(t, h, g) - (128 + z_g(t)) * qsum(h, g))
+// with qsum(h, g) the sum of q over the group, i.e. the dequantised dot
+// product sum_d q_hd (c_td - z) s.  Scores are kept in base-2 units.
+//
+// P.V (v_mfma_f32_16x16x32_bf16, 32 tokens): rows are (query head, hi/lo part),
+// the K dimension is tokens, columns are channels.  The A operand carries
+// p'(t) = p(t) * s_v(t) split into a bf16 high part and the bf16 rounding
+// of the remainder (16 significant bits together); the B operand carries
+// OFF + c (OFF = 16 for 4-bit codes, 128 for 6-bit codes, both exact in
+// bf16).  sum_t p'(t) (OFF + z(t)) is accumulated beside it and subtracted
+// at the end, giving sum_t p(t) s_v(t) (c_t - z(t)) = sum_t p(t) v_hat(t).
+//
+// The QK result registers of a lane are exactly the P.V A-operand registers
+// it needs (rows of the QK output = K index of the P.V input), so no data
+// moves between the two products.  Token order inside a block is permuted
+// (the same permutation on both sides) so that the V bytes a lane loads
+// unpack with one shift and one mask per pair of 4-bit codes.
+//
+// Online softmax per head, the sparse-V skip of the Super KV Compression
+// page (third layer: after a block is folded into the running maximum m and
+// sum L, exp(s - m) < tau_low * L drops the token's V term) and the partial
+// (o[128], m, L) per split follow the generic kernel exactly.
+#include <hip/hip_fp16.h>
+
+#include "lkv_internal.h"
+
+namespace lkv {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+struct MfmaArgs {
+    SegArgs seg;
+    const uint16_t* q;   // bf16 [B][Hq][128]
+    int32_t num_q_heads;
+    int32_t split_tokens;
+    int32_t total_splits;
+    float score_scale;   // sm_scale * log2(e)
+    float tau_low;
+    float* partials;
+};
+
+__device__ __forceinline__ f32x4_t mfma_16x16x32(const uint32_t (&a)[4], const uint32_t (&b)[4], f32x4_t c)
+{
+    bf16x8_t av, bv;
+    __builtin_memcpy(&av, a, 16);
+    __builtin_memcpy(&bv, b, 16);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, c, 0, 0, 0);
+}
+
+// x | (x << 10): one VALU instruction.
+__device__ __forceinline__ uint32_t lshl10_or(uint32_t x)
+{
+    uint32_t y;
+    asm("v_lshl_or_b32 %0, %1, 10, %1" : "=v"(y) : "v"(x));
+    return y;
+}
+
+// (x & m) | c in one instruction; m and c live in VGPRs (a VOP3 instruction
+// of this family reads at most one scalar operand).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c)
+{
+    uint32_t y;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(y) : "v"(x), "v"(m), "v"(c));
+    return y;
+}
+
+// Constants of the code-to-bf16 conversions, kept in registers.
+struct Magic {
+    uint32_t m6, c6;   // 0x003F003F, 0x43004300: 6-bit code -> 128 + c
+    uint32_t m4, c4;   // 0x00780078, 0x41804180: 4-bit code (at bit 3) -> 16 + c
+};
+
+__device__ __forceinline__ Magic make_magic()
+{
+    Magic k;
+    // opaque moves so that the constants are materialised once in VGPRs
+    asm volatile("v_mov_b32 %0, 0x003F003F" : "=v"(k.m6));
+    asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(k.c6));
+    asm volatile("v_mov_b32 %0, 0x00780078" : "=v"(k.m4));
+    asm volatile("v_mov_b32 %0, 0x41804180" : "=v"(k.c4));
+    return k;
+}
+
+// Two adjacent 6-bit codes at bit BIT of an N-word bitstream, as a pair of
+// bf16 values 128 + c (low half: the first code).
+template <int BIT, int N>
+__device__ __forceinline__ uint32_t pair6(const uint32_t (&w)[N], const Magic& k)
+{
+    constexpr int wi = BIT >> 5, sh = BIT & 31;
+    uint32_t x;
+    if constexpr (sh <= 20) {
+        x = __builtin_amdgcn_ubfe(w[wi], sh, 12);
+    } else {
+        x = __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & 0xFFFu;
+    }
+    return and_or(lshl10_or(x), k.m6, k.c6);  // code a at bits 0..5, code b at 16..21
+}
+
+// Nibbles K and K+4 of w as a pair of bf16 values 16 + c.
+template <int K>
+__device__ __forceinline__ uint32_t pair4(uint32_t w, const Magic& k)
+{
+    uint32_t y;
+    if constexpr (K == 0) y = w << 3;
+    else y = w >> (4 * K - 3);
+    return and_or(y, k.m4, k.c4);
+}
+
+// Token (0..15 of the lane group's 16) of row r of QK tile t.  4-bit V: the
+// rows of tiles 2u, 2u+1 are nibbles (0,4,1,5 | 2,6,3,7) of one V word, so
+// the P.V K index j of tile pair u is nibble {0,4,1,5,2,6,3,7}[j]; 6-bit V:
+// natural order.
+template <int VB>
+__device__ __forceinline__ constexpr int tok_of(int t, int r)
+{
+    if constexpr (VB == 4) {
+        // nibble {0,4,1,5}[r] of word t>>1 for even t, {2,6,3,7}[r] for odd t
+        return 8 * (t >> 1) + 2 * (t & 1) + (r >> 1) + 4 * (r & 1);
+    } else {
+        return 4 * t + r;
+    }
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to nearest-even bf16, packed low/high.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
+{
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Value of the neighbouring lane (lane ^ 1) -- DPP quad permutation.
+__device__ __forceinline__ float xor1(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+
+// Reductions over the four 16-lane rows (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float rows_max(float v)
+{
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float v)
+{
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ uint32_t byte_of(const uint32_t (&w)[4], int x) { return (w[x >> 2] >> (8 * (x & 3))) & 0xFFu; }
+
+// Raw bytes of one block held by one lane: codes in registers, the block's
+// scales and zero points (1280 contiguous bytes: K scales, V scales, K zeros,
+// V zeros) through a per-wave LDS buffer.
+template <int VB>
+struct BlockRegs {
+    uint32_t kr[4][6];                  // K: tile t -> 32 channels of one token
+    uint32_t vr[8][VB == 4 ? 2 : 3];    // V: channel tile T -> 16 tokens of one channel
+    uint4 meta[2];                      // this lane's 16 B slices of the metadata
+};
+
+constexpr int META_BYTES = 1280;        // D 128, group 64: 2 groups x 64 slots x (4 + 4 + 1 + 1)
+constexpr int META_VS = 512, META_KZ = 1024, META_VZ = 1152;
+
+template <int VB>
+__device__ __forceinline__ void load_k(BlockRegs<VB>& R, const uint8_t* ch, uint32_t off_kc, int c, int q)
+{
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+        const uint32_t tok = 16 * (c >> 2) + tok_of<VB>(t, c & 3);
+        const uint2* p = (const uint2*)(ch + (off_kc + tok * 96 + 24 * q));
+        const uint2 x0 = p[0], x1 = p[1], x2 = p[2];
+        R.kr[t][0] = x0.x; R.kr[t][1] = x0.y; R.kr[t][2] = x1.x;
+        R.kr[t][3] = x1.y; R.kr[t][4] = x2.x; R.kr[t][5] = x2.y;
+    }
+}
+
+template <int VB>
+__device__ __forceinline__ void load_v(BlockRegs<VB>& R, const uint8_t* ch, uint32_t off_vc, int c, int q)
+{
+#pragma unroll
+    for (int T = 0; T < 8; T++) {
+        if constexpr (VB == 4) {
+            const uint2 x = *(const uint2*)(ch + (off_vc + (16 * T + c) * 32 + 8 * q));
+            R.vr[T][0] = x.x;
+            R.vr[T][1] = x.y;
+        } else {
+            const uint32_t* p = (const uint32_t*)(ch + (off_vc + (16 * T + c) * 48 + 12 * q));
+            R.vr[T][0] = p[0];
+            R.vr[T][1] = p[1];
+            R.vr[T][2] = p[2];
+        }
+    }
+}
+
+template <int VB>
+__device__ __forceinline__ void load_meta(BlockRegs<VB>& R, const uint8_t* ch, uint32_t off_ks, int lane)
+{
+    const uint4* m = (const uint4*)(ch + off_ks);
+    R.meta[0] = m[lane];
+    R.meta[1] = m[64 + min(lane, (META_BYTES - 1024) / 16 - 1)];  // every lane loads: no branch
+}
+
+__device__ __forceinline__ void stage_meta(const uint4 (&meta)[2], uint4* lds, int lane)
+{
+    lds[lane] = meta[0];
+    // lanes past the last slice rewrite it with the same bytes: no branch
+    lds[64 + min(lane, (META_BYTES - 1024) / 16 - 1)] = meta[1];
+}
+
+__device__ __forceinline__ void read16f(const uint8_t* lds, float (&v)[16])
+{
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const float4 x = ((const float4*)lds)[i];
+        v[4 * i] = x.x; v[4 * i + 1] = x.y; v[4 * i + 2] = x.z; v[4 * i + 3] = x.w;
+    }
+}
+
+__device__ __forceinline__ void read16b(const uint8_t* lds, uint32_t (&w)[4])
+{
+    const uint4 x = *(const uint4*)lds;
+    w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+}
+
+// Running state of one lane.
+struct SplitState {
+    float m_run, l_run;
+    f32x4_t acc[8];
+};
+
+// One 64-token block in three phases (the kernel issues the next block's
+// loads between them): Q.K, scores + online softmax + sparse-V skip, P.V.
+template <int VB>
+__device__ __forceinline__ void block_qk(const BlockRegs<VB>& R, const uint32_t (&qb)[4][4], float q128,
+                                         const Magic& mk, f32x4_t (&dot)[4])
+{
+    // ---- Q.K: 4 tiles x 4 K-steps of 32 channels
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+        uint32_t ka[4][4];
+        ka[0][0] = pair6<0>(R.kr[t], mk);   ka[0][1] = pair6<12>(R.kr[t], mk);
+        ka[0][2] = pair6<24>(R.kr[t], mk);  ka[0][3] = pair6<36>(R.kr[t], mk);
+        ka[1][0] = pair6<48>(R.kr[t], mk);  ka[1][1] = pair6<60>(R.kr[t], mk);
+        ka[1][2] = pair6<72>(R.kr[t], mk);  ka[1][3] = pair6<84>(R.kr[t], mk);
+        ka[2][0] = pair6<96>(R.kr[t], mk);  ka[2][1] = pair6<108>(R.kr[t], mk);
+        ka[2][2] = pair6<120>(R.kr[t], mk); ka[2][3] = pair6<132>(R.kr[t], mk);
+        ka[3][0] = pair6<144>(R.kr[t], mk); ka[3][1] = pair6<156>(R.kr[t], mk);
+        ka[3][2] = pair6<168>(R.kr[t], mk); ka[3][3] = pair6<180>(R.kr[t], mk);
+        f32x4_t d4 = {-q128, -q128, -q128, -q128};  // removes the 128 offset of the codes
+#pragma unroll
+        for (int s = 0; s < 4; s++) d4 = mfma_16x16x32(ka[s], qb[s], d4);
+        dot[t] = d4;
+    }
+
+}
+
+// Scores of the lane's 16 tokens from the block's dot products, folded into
+// the running (m, L); fills the weights p (0 for dead or skipped tokens) and
+// returns the rescale factor of this lane's head.
+template <int VB, int G>
+__device__ __forceinline__ float block_softmax(const f32x4_t (&dot)[4], const uint8_t* lds, SplitState& S, float qsum,
+                                               float score_scale, float tau_low, int nlive, int q, int c,
+                                               float (&p)[16])
+{
+    const int gc = c & 1;
+    float sk[16];
+    uint32_t zk[4];
+    read16f(lds + gc * 256 + 64 * q, sk);
+    read16b(lds + META_KZ + gc * 64 + 16 * q, zk);
+    float sc[16];
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int x = tok_of<VB>(t, r);
+            // this lane's group share: s_g * sum_{d in g} q_d (c_d - z_g)
+            const float pg = sk[x] * (dot[t][r] - (float)byte_of(zk, x) * qsum);
+            float s2 = (pg + xor1(pg)) * score_scale;  // both groups, base 2
+            if (nlive < BT) s2 = 16 * q + x < nlive ? s2 : -INFINITY;
+            sc[4 * t + r] = s2;
+            bmax = fmaxf(bmax, s2);
+        }
+    }
+    bmax = rows_max(bmax);
+    const float m_new = fmaxf(S.m_run, bmax);
+    const float alpha = __builtin_amdgcn_exp2f(S.m_run - m_new);
+    float bsum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        p[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
+        bsum += p[i];
+    }
+    S.l_run = S.l_run * alpha + rows_sum(bsum);
+    S.m_run = m_new;
+    if (tau_low > 0.0f) {  // sparse-V skip against the running bound
+        const float thr = tau_low * S.l_run;
+#pragma unroll
+        for (int i = 0; i < 16; i++) p[i] = p[i] < thr ? 0.0f : p[i];
+    }
+    return alpha;
+}
+
+// bf16 pair of -(OFF + z) for two zero-point bytes a (low half) and b.
+template <int VB>
+__device__ __forceinline__ uint32_t neg_off_pair(uint32_t a, uint32_t b)
+{
+    if constexpr (VB == 4) return 0xC180C180u | (a << 3) | (b << 19);   // -(16 + z)
+    else return 0xC300C300u | a | (b << 16);                          // -(128 + z)
+}
+
+template <int VB, int G>
+__device__ __forceinline__ void block_pv(const BlockRegs<VB>& R, const uint8_t* lds, SplitState& S,
+                                         const float (&p)[16], float alpha, bool dead, bool skip, int q, int c,
+                                         int hA, const Magic& mk)
+{
+    constexpr int NG = G == 8 ? 2 : 1;
+    const int part = c & 1;
+
+    // rescale the accumulators when a running maximum moved
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+        const float alA = __shfl(alpha, 2 * hA, 64), alB = __shfl(alpha, 2 * hA + 2, 64);
+#pragma unroll
+        for (int T = 0; T < 8; T++) {
+            S.acc[T][0] *= alA;
+            S.acc[T][1] *= alA;
+            S.acc[T][2] *= alB;
+            S.acc[T][3] *= alB;
+        }
+    }
+
+    float sv[NG][16];
+#pragma unroll
+    for (int g = 0; g < NG; g++) read16f(lds + META_VS + (G == 8 ? g : (c >> 3)) * 256 + 64 * q, sv[g]);
+    uint32_t zv[2][4];
+#pragma unroll
+    for (int g = 0; g < 2; g++) read16b(lds + META_VZ + g * 64 + 16 * q, zv[g]);
+
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+        // A operand: p * s_v split into bf16 high part and bf16 remainder
+        uint32_t pa[NG][4];
+        bool any = false;
+#pragma unroll
+        for (int g = 0; g < NG; g++) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const int t = 2 * u + (j >> 2), r = j & 3;
+                const int x = tok_of<VB>(t, r);
+                const float pj = p[4 * t + r];
+                float pp = pj * sv[g][x];
+                if (dead) pp = pj > 0.0f ? pp : 0.0f;  // dead token: its scale bytes may be stale
+                any |= pp > 0.0f;
+                const float hi = __uint_as_float(__float_as_uint(pp) & 0xFFFF0000u);
+                v[j] = part ? pp - hi : hi;
+            }
+#pragma unroll
+            for (int k = 0; k < 4; k++) pa[g][k] = pack_bf16(v[2 * k], v[2 * k + 1]);
+        }
+        if (skip && !__builtin_amdgcn_ballot_w64(any)) continue;  // every V term of the 32 tokens skipped
+        // correction operand: -(OFF + z) of each token, the same for every column
+        uint32_t bz[2][4];
+#pragma unroll
+        for (int g = 0; g < 2; g++) {
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                const int xa = tok_of<VB>(2 * u + ((2 * k) >> 2), (2 * k) & 3);
+                const int xb = tok_of<VB>(2 * u + ((2 * k + 1) >> 2), (2 * k + 1) & 3);
+                bz[g][k] = neg_off_pair<VB>(byte_of(zv[g], xa), byte_of(zv[g], xb));
+            }
+        }
+#pragma unroll
+        for (int T = 0; T < 8; T++) {
+            uint32_t bv[4];
+            if constexpr (VB == 4) {
+                const uint32_t w = R.vr[T][u];
+                bv[0] = pair4<0>(w, mk);
+                bv[1] = pair4<1>(w, mk);
+                bv[2] = pair4<2>(w, mk);
+                bv[3] = pair4<3>(w, mk);
+            } else if (u == 0) {
+                bv[0] = pair6<0>(R.vr[T], mk);
+                bv[1] = pair6<12>(R.vr[T], mk);
+                bv[2] = pair6<24>(R.vr[T], mk);
+                bv[3] = pair6<36>(R.vr[T], mk);
+            } else {
+                bv[0] = pair6<48>(R.vr[T], mk);
+                bv[1] = pair6<60>(R.vr[T], mk);
+                bv[2] = pair6<72>(R.vr[T], mk);
+                bv[3] = pair6<84>(R.vr[T], mk);
+            }
+            const int gT = T >> 2;
+            const int ga = G == 8 ? gT : 0;
+            // sum_t p'(t) (-(OFF + z(t))), then + sum_t p'(t) (OFF + c(t)): the
+            // offset never accumulates beyond 32 tokens
+            S.acc[T] = mfma_16x16x32(pa[ga], bz[gT], S.acc[T]);
+            S.acc[T] = mfma_16x16x32(pa[ga], bv, S.acc[T]);
+        }
+    }
+}
+
+template <int VB, int G>
+__global__ __launch_bounds__(64) void split_mfma_kernel(MfmaArgs a)
+{
+    static_assert(G == 4 || G == 8, "4 or 8 query heads per KV head");
+    constexpr int D = 128;
+    const SegArgs& sg = a.seg;
+    const Fmt& f = sg.f;
+    const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x;
+    const int c = lane & 15, q = lane >> 4;
+    const int len = max(0, min(sg.seq_lens[b], sg.max_blocks * BT));
+    const int t0 = sp * a.split_tokens;
+    const int t1 = max(t0, min(t0 + a.split_tokens, len));  // empty split: t1 == t0
+
+    // ---- roles of this lane
+    // QK column c -> (head hc, group gc); P.V row c -> (head hc, part c&1,
+    // and for G = 4 the group c>>3, the two groups sharing one A operand).
+    const int hc = G == 8 ? (c >> 1) : ((c & 7) >> 1);
+    const int gc = c & 1;
+    const int part = c & 1;
+    const int head = kvh * G + hc;
+    // heads of the P.V output rows held by this lane (rows 4q .. 4q+3)
+    const int hA = G == 8 ? 2 * q : 2 * (q & 1);
+
+    // ---- Q as the QK B operand: this lane group (q) holds channels
+    // [32q, 32q + 32), in group q >> 1; zero unless that is the column's group.
+    uint32_t qb[4][4];
+    float qpart = 0.0f;
+    {
+        const uint4* src = (const uint4*)(a.q + ((int64_t)b * a.num_q_heads + head) * D + 32 * q);
+        const bool live = (q >> 1) == gc;
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+            const uint4 v = src[s];
+            qb[s][0] = live ? v.x : 0u;
+            qb[s][1] = live ? v.y : 0u;
+            qb[s][2] = live ? v.z : 0u;
+            qb[s][3] = live ? v.w : 0u;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const uint32_t u = qb[s][j];
+                qpart += __uint_as_float(u << 16) + __uint_as_float(u & 0xFFFF0000u);
+            }
+        }
+    }
+    const float qsum = rows_sum(qpart);
+    const float q128 = 128.0f * qsum;
+
+    const Magic mk = make_magic();
+    SplitState S;
+    S.m_run = -INFINITY;
+    S.l_run = 0.0f;
+#pragma unroll
+    for (int T = 0; T < 8; T++) S.acc[T] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    __shared__ uint4 meta_lds[META_BYTES / 16];
+    const uint8_t* lds = (const uint8_t*)meta_lds;
+    const bool skip = a.tau_low > 0.0f;
+
+    // the split's block-table entries (at most 64), one per lane, so that
+    // every chunk address is a register read instead of a memory round trip
+    const int nblk = (t1 - t0 + BT - 1) / BT;
+    const int32_t* bt = sg.block_table + (int64_t)b * sg.max_blocks + t0 / BT;
+    // (an empty split reads nothing: its first-block loads below go to pool
+    // block 0, which every cache has)
+    const int bt_lane = lane < nblk ? bt[lane] : 0;
+    // format fields as plain values (kept in scalar registers)
+    const uint8_t* const pool = sg.pool;
+    const int64_t chunk = f.chunk;
+    const int H = f.H;
+    const uint32_t off_kc = (uint32_t)f.off_kc, off_vc = (uint32_t)f.off_vc, off_ks = (uint32_t)f.off_ks;
+    auto chunk_of = [=](int k) {
+        const int blk = __builtin_amdgcn_readlane(bt_lane, k);
+        return pool + ((int64_t)blk * H + kvh) * chunk;
+    };
+
+    // Blocks in order.  The next block's metadata, K codes and V codes are
+    // loaded as soon as this block no longer needs the registers they go to,
+    // so they stream in while this block computes.  (After the last block
+    // the loads repeat it, from L2.)
+    BlockRegs<VB> R;
+    {
+        // the same issue order as inside the loop: metadata, K, V
+        const uint8_t* c0 = chunk_of(0);
+        load_meta<VB>(R, c0, off_ks, lane);
+        asm volatile("" ::: "memory");
+        load_k<VB>(R, c0, off_kc, c, q);
+        asm volatile("" ::: "memory");
+        load_v<VB>(R, c0, off_vc, c, q);
+        asm volatile("" ::: "memory");
+    }
+    // (the empty asm statements keep the compiler from moving the loads to
+    // their first use)
+    for (int k = 0; k < nblk; k++) {
+        const uint8_t* cn = chunk_of(min(k + 1, nblk - 1));
+        stage_meta(R.meta, meta_lds, lane);
+        load_meta<VB>(R, cn, off_ks, lane);
+        asm volatile("" ::: "memory");
+        f32x4_t dot[4];
+        block_qk<VB>(R, qb, q128, mk, dot);
+        load_k<VB>(R, cn, off_kc, c, q);
+        asm volatile("" ::: "memory");
+        const int nlive = min(BT, t1 - t0 - k * BT);
+        float p[16];
+        const float alpha = block_softmax<VB, G>(dot, lds, S, qsum, a.score_scale, a.tau_low, nlive, q, c, p);
+        block_pv<VB, G>(R, lds, S, p, alpha, nlive < BT, skip, q, c, hA, mk);
+        load_v<VB>(R, cn, off_vc, c, q);
+        asm volatile("" ::: "memory");
+    }
+
+    // ---- write the partial (o, m, L) of every head of the group
+    // P.V output: lane (column c, row group q) holds rows 4q .. 4q+3 of each
+    // channel tile T; rows 4q, 4q+1 are head hA (hi, lo), 4q+2, 4q+3 head hA+1.
+    float* base = a.partials + ((int64_t)b * a.num_q_heads + kvh * G) * a.total_splits * (D + 2);
+    const int64_t hstride = (int64_t)a.total_splits * (D + 2);
+    const int64_t soff = (int64_t)(sg.split_base + sp) * (D + 2);
+#pragma unroll
+    for (int T = 0; T < 8; T++) {
+        // G = 8: both groups valid in every lane; G = 4: rows of group q >> 1
+        if (G == 4 && (q >> 1) != (T >> 2)) continue;
+        base[hA * hstride + soff + 16 * T + c] = S.acc[T][0] + S.acc[T][1];
+        base[(hA + 1) * hstride + soff + 16 * T + c] = S.acc[T][2] + S.acc[T][3];
+    }
+    if (q == 0 && part == 0 && (G == 8 || c < 8)) {
+        base[hc * hstride + soff + D] = S.m_run;
+        base[hc * hstride + soff + D + 1] = S.l_run;
+    }
+}
+
+// Returns true and launches when the format and shape have a matrix-core
+// kernel; false leaves the call to the generic kernel.
+bool launch_decode_split_mfma(const SegArgs& s, const void* q, int q_dtype, int32_t batch, int32_t num_q_heads,
+                              float sm_scale, float tau_low, int32_t split_tokens, int32_t total_splits,
+                              float* partials, hipStream_t stream, hipError_t* err)
+{
+    const Fmt& f = s.f;
+    const int G = num_q_heads / f.H;
+    if (q_dtype != LKV_BF16 || f.D != 128 || f.g != 64 || f.fp16 || f.kb != 6 || (f.vb != 4 && f.vb != 6) ||
+        (G != 4 && G != 8))
+        return false;
+    MfmaArgs a;
+    a.seg = s;
+    a.q = (const uint16_t*)q;
+    a.num_q_heads = num_q_heads;
+    a.split_tokens = split_tokens;
+    a.total_splits = total_splits;
+    a.score_scale = sm_scale * 1.4426950408889634f;
+    a.tau_low = tau_low;
+    a.partials = partials;
+    dim3 grid((unsigned)s.n_splits, (unsigned)f.H, (unsigned)batch);
+    if (f.vb == 4 && G == 4) hipLaunchKernelGGL((split_mfma_kernel<4, 4>), grid, dim3(64), 0, stream, a);
+    else if (f.vb == 4) hipLaunchKernelGGL((split_mfma_kernel<4, 8>), grid, dim3(64), 0, stream, a);
+    else if (G == 4) hipLaunchKernelGGL((split_mfma_kernel<6, 4>), grid, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL((split_mfma_kernel<6, 8>), grid, dim3(64), 0, stream, a);
+    *err = hipGetLastError();
+    return true;
+}
+
+}  // namespace lkv

@@ -45,6 +45,12 @@ hipError_t launch_decode_split(const SegArgs& s, const void* q, int q_dtype, int
                                int32_t split_tokens, int32_t total_splits, float* partials,
                                hipStream_t stream);
 
+// Matrix-core split kernel: launches and returns true when the format and
+// shape have one (bf16 Q, D 128, g 64, K6, V4 or V6, G 4 or 8).
+bool launch_decode_split_mfma(const SegArgs& s, const void* q, int q_dtype, int32_t batch, int32_t num_q_heads,
+                              float sm_scale, float tau_low, int32_t split_tokens, int32_t total_splits,
+                              float* partials, hipStream_t stream, hipError_t* err);
+
 hipError_t launch_decode_combine(int32_t batch, int32_t num_q_heads, int32_t D, int32_t total_splits,
                                  const float* partials, float* out, hipStream_t stream);
 

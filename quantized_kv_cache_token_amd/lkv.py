@@ -238,3 +238,40 @@ def tier_update(src: Cache, src_view: View, scores: torch.Tensor, tau_low: float
         h_block_table.shape[1], C.byref(cm), _ptr(m_block_table), m_block_table.shape[1], _ptr(n_high),
         _ptr(n_mid), _ptr(tiers), B, _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+
+
+class Prepared:
+    """Pre-marshalled calls for a fixed set of tensors, for loops that issue
+    the same call many times (the ctypes structures are built once).  The
+    tensors must stay alive and keep their storage while it is used."""
+
+    def __init__(self, fn: str, *args):
+        self._fn = getattr(lib(), fn)
+        self._name = fn
+        self._args = args
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != OK:
+            raise LkvError(self._name, st)
+
+
+def prepare_append(cache: Cache, k, v, cu_new, start_pos, block_table, max_new: int, stream=None) -> Prepared:
+    cc = cache.c()
+    return Prepared("lkv_quant_append", C.byref(cc), _ptr(k), _ptr(v), _DTYPE[k.dtype], _ptr(cu_new),
+                    _ptr(start_pos), _ptr(block_table), block_table.shape[1], start_pos.shape[0], int(max_new),
+                    _stream(stream))
+
+
+def prepare_decode(caches, views, q, sm_scale: float, tau_low: float, split_tokens: int, out, workspace,
+                   stream=None) -> tuple[Prepared, Prepared]:
+    """(split, combine) stages of lkv_decode_attn as prepared calls."""
+    B, Hq, _ = q.shape
+    cs, vs, n = _segs(caches, views)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = _stream(stream)
+    split = Prepared("lkv_decode_split", cs, vs, n, _ptr(q), _DTYPE[q.dtype], B, Hq, sm_scale, tau_low,
+                     split_tokens, _ptr(workspace), nbytes, st)
+    comb = Prepared("lkv_decode_combine", cs, vs, n, B, Hq, split_tokens, _ptr(out), _ptr(workspace), nbytes, st)
+    split._keep = comb._keep = (cs, vs)
+    return split, comb
