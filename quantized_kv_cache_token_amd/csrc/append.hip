@@ -5,7 +5,12 @@
 // are merged and written without atomics.  Each wave quantises whole rows
 // (one token's K or V): the group min / max is a wavefront reduction over the
 // lanes holding the group, the codes go to LDS, and the workgroup then packs
-// 32-bit words and writes them with coalesced stores.
+// 32-bit words and writes them.
+//
+// Decode appends one row per sequence, so the kernel is laid out for
+// latency: the index loads are issued together, the V words that must be
+// merged are loaded as soon as the chunk address is known, and nothing waits
+// on memory between those loads and the stores.
 #include <hip/hip_fp16.h>
 
 #include "lkv_internal.h"
@@ -23,10 +28,20 @@ struct AppendArgs {
     const int32_t* block_table;
     int32_t max_blocks;
     int32_t nblk;    // logical blocks a sequence's new rows can touch
-    int32_t dtype;
 };
 
-template <int D>
+template <int DT>
+__device__ __forceinline__ float load_in(const void* p, int64_t i)
+{
+    if constexpr (DT == LKV_F32) return ((const float*)p)[i];
+    const uint16_t u = ((const uint16_t*)p)[i];
+    if constexpr (DT == LKV_BF16) return __uint_as_float((uint32_t)u << 16);
+    return __half2float(__ushort_as_half(u));
+}
+
+constexpr int MAXW = 16;  // V words per thread: D * 64 slots * 16 bits / 32 / 256 threads at most
+
+template <int D, int DT>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
 {
     constexpr int VPL = D / 64;  // values per lane: channels lane + 64 * i
@@ -34,40 +49,60 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
     const int b = blockIdx.x / a.nblk;
     const int i = blockIdx.x % a.nblk;
     const int kvh = blockIdx.y;
+    // the three index loads are independent: issue them together
     const int row0 = a.cu_new[b];
-    const int n = a.cu_new[b + 1] - row0;
-    if (n <= 0) return;
+    const int row1 = a.cu_new[b + 1];
     const int sp = a.start_pos[b];
+    const int n = row1 - row0;
     const int lb = sp / BT + i;
     const int p0 = max(sp, lb * BT);
     const int p1 = min(sp + n, lb * BT + BT);
-    if (p0 >= p1) return;
+    if (n <= 0 || p0 >= p1) return;
     const int s0 = p0 - lb * BT, s1 = p1 - lb * BT;  // slots written by this call
     const int64_t blk = a.block_table[(int64_t)b * a.max_blocks + lb];
     uint8_t* ch = a.pool + (blk * f.H + kvh) * f.chunk;
 
-    __shared__ uint16_t kc[BT][D];
-    __shared__ uint16_t vc[BT][D];
-
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    for (int r = wave; r < 2 * (s1 - s0); r += 4) {
+    const int nrows = 2 * (s1 - s0);
+
+    // V words of this chunk that hold bits of slots [s0, s1): load the old
+    // contents of the partially covered ones now, to merge later
+    const int w0 = (f.vb * s0) / 32, w1 = (f.vb * s1 - 1) / 32;
+    const int wv = w1 - w0 + 1;
+    const int nw = D * wv;
+    uint32_t old[MAXW];
+#pragma unroll
+    for (int j = 0; j < MAXW; j++) {
+        const int idx = threadIdx.x + 256 * j;
+        old[j] = 0u;
+        if (idx < nw) {
+            const int d = idx / wv, w = w0 + idx % wv;
+            if (field_mask(w, f.vb, s0, s1) != 0xFFFFFFFFu)
+                old[j] = ((const uint32_t*)(ch + f.off_vc + d * f.vrow))[w];
+        }
+    }
+
+    __shared__ uint16_t kc[BT][D];
+    __shared__ uint16_t vc[BT][D];
+    for (int r = wave; r < nrows; r += 4) {
         const int slot = s0 + (r >> 1);
         const bool is_v = r & 1;
         const int64_t in_row = (int64_t)(row0 + (lb * BT + slot - sp)) * f.H + kvh;
-        const void* src = is_v ? a.v : a.k;
+        float x[VPL];
+#pragma unroll
+        for (int j = 0; j < VPL; j++) x[j] = load_in<DT>(is_v ? a.v : a.k, in_row * D + lane + 64 * j);
         const int bits = is_v ? f.vb : f.kb;
 #pragma unroll
         for (int j = 0; j < VPL; j++) {
             const int d = lane + 64 * j;
-            const float x = load_as_float(src, in_row * D + d, a.dtype);
             uint32_t code;
             if (f.fp16) {
-                code = f16_bits(x);
+                code = f16_bits(x[j]);
             } else {
                 float s;
                 int z;
-                code = (uint32_t)quantize_lane(x, f.g, bits, &s, &z);
+                code = (uint32_t)quantize_lane(x[j], f.g, bits, &s, &z);
                 if ((d % f.g) == 0) {
                     const int gi = d / f.g;
                     float* sc = (float*)(ch + (is_v ? f.off_vs : f.off_ks));
@@ -91,18 +126,26 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
         ((uint32_t*)(ch + f.off_kc + slot * f.krow))[w] = word;
     }
     // V rows: channel-major; only the words that hold bits of slots [s0, s1)
-    // are touched, and their bits of other slots are kept.
-    const int w0 = (f.vb * s0) / 32, w1 = (f.vb * s1 - 1) / 32;
-    const int wv = w1 - w0 + 1;
-    for (int idx = threadIdx.x; idx < D * wv; idx += blockDim.x) {
-        const int d = idx / wv;
-        const int w = w0 + idx % wv;
-        const uint32_t mask = field_mask(w, f.vb, s0, s1);
-        uint32_t word = pack_word(w, f.vb, s0, s1, [&](int s) { return (uint32_t)vc[s][d]; });
-        uint32_t* dst = (uint32_t*)(ch + f.off_vc + d * f.vrow) + w;
-        if (mask != 0xFFFFFFFFu) word = (*dst & ~mask) | (word & mask);
-        *dst = word;
+    // are written, and their bits of other slots are kept.
+#pragma unroll
+    for (int j = 0; j < MAXW; j++) {
+        const int idx = threadIdx.x + 256 * j;
+        if (idx < nw) {
+            const int d = idx / wv, w = w0 + idx % wv;
+            const uint32_t mask = field_mask(w, f.vb, s0, s1);
+            uint32_t word = pack_word(w, f.vb, s0, s1, [&](int s) { return (uint32_t)vc[s][d]; });
+            if (mask != 0xFFFFFFFFu) word = (old[j] & ~mask) | (word & mask);
+            ((uint32_t*)(ch + f.off_vc + d * f.vrow))[w] = word;
+        }
     }
+}
+
+template <int D>
+static void launch_d(const AppendArgs& a, int dtype, dim3 grid, hipStream_t stream)
+{
+    if (dtype == LKV_F32) hipLaunchKernelGGL((append_kernel<D, LKV_F32>), grid, dim3(256), 0, stream, a);
+    else if (dtype == LKV_BF16) hipLaunchKernelGGL((append_kernel<D, LKV_BF16>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((append_kernel<D, LKV_F16>), grid, dim3(256), 0, stream, a);
 }
 
 hipError_t launch_append(const Fmt& f, uint8_t* pool, const void* k, const void* v, int dtype,
@@ -120,10 +163,9 @@ hipError_t launch_append(const Fmt& f, uint8_t* pool, const void* k, const void*
     a.block_table = block_table;
     a.max_blocks = max_blocks;
     a.nblk = (max_new + BT - 1) / BT + 1;
-    a.dtype = dtype;
     dim3 grid((unsigned)batch * (unsigned)a.nblk, (unsigned)f.H);
-    if (f.D == 64) hipLaunchKernelGGL(append_kernel<64>, grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(append_kernel<128>, grid, dim3(256), 0, stream, a);
+    if (f.D == 64) launch_d<64>(a, dtype, grid, stream);
+    else launch_d<128>(a, dtype, grid, stream);
     return hipGetLastError();
 }
 

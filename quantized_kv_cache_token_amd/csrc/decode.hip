@@ -183,36 +183,46 @@ hipError_t launch_decode_split(const SegArgs& s, const void* q, int q_dtype, int
 
 // Merge of the split partials of one (sequence, query head), m in base 2:
 //   M = max_i m_i,  O = sum_i o_i 2^(m_i - M) / sum_i L_i 2^(m_i - M).
-// One wave per (sequence, query head): the split maxima and sums are reduced
-// across lanes, then every lane accumulates its channels over the splits
-// with coalesced loads of whole partial rows.
+// One wave per (sequence, query head).  The partial rows of up to 32 splits,
+// their maxima and their sums are loaded together (one memory latency); the
+// weights are computed in the lane that holds each split and broadcast.
 template <int D>
 __global__ __launch_bounds__(64) void combine_kernel(int32_t total_splits, const float* __restrict__ part,
                                                      float* __restrict__ out)
 {
     constexpr int VPL = D / 64;
+    constexpr int CH = 32;
     const int64_t bh = blockIdx.x;
     const int lane = threadIdx.x;
     const float* p = part + bh * total_splits * (D + 2);
-    float M = -INFINITY;
-    for (int i = lane; i < total_splits; i += 64) M = fmaxf(M, p[(int64_t)i * (D + 2) + D]);
-    M = wave_max(M);
-    float L = 0.0f;
-    for (int i = lane; i < total_splits; i += 64) {
-        const float mi = p[(int64_t)i * (D + 2) + D];
-        if (mi != -INFINITY) L += p[(int64_t)i * (D + 2) + D + 1] * exp2f(mi - M);
-    }
-    L = wave_sum(L);
     float acc[VPL];
 #pragma unroll
     for (int j = 0; j < VPL; j++) acc[j] = 0.0f;
-#pragma unroll 8
-    for (int i = 0; i < total_splits; i++) {
-        const float* pi = p + (int64_t)i * (D + 2);
-        const float mi = pi[D];
-        const float w = mi == -INFINITY ? 0.0f : exp2f(mi - M);
+    float M = -INFINITY, L = 0.0f;
+    for (int i0 = 0; i0 < total_splits; i0 += CH) {
+        const int n = min(CH, total_splits - i0);
+        float ov[CH][VPL];
 #pragma unroll
-        for (int j = 0; j < VPL; j++) acc[j] += pi[lane + 64 * j] * w;
+        for (int i = 0; i < CH; i++) {
+#pragma unroll
+            for (int j = 0; j < VPL; j++) ov[i][j] = i < n ? p[(int64_t)(i0 + i) * (D + 2) + lane + 64 * j] : 0.0f;
+        }
+        const float mi = lane < n ? p[(int64_t)(i0 + lane) * (D + 2) + D] : -INFINITY;
+        const float li = lane < n ? p[(int64_t)(i0 + lane) * (D + 2) + D + 1] : 0.0f;
+        const float m_new = fmaxf(M, wave_max(mi));
+        if (m_new == -INFINITY) continue;  // no token so far
+        const float alpha = exp2f(M - m_new);
+        const float wi = mi == -INFINITY ? 0.0f : exp2f(mi - m_new);
+        L = L * alpha + wave_sum(li * wi);
+#pragma unroll
+        for (int j = 0; j < VPL; j++) acc[j] *= alpha;
+#pragma unroll
+        for (int i = 0; i < CH; i++) {
+            const float w = __shfl(wi, i, 64);
+#pragma unroll
+            for (int j = 0; j < VPL; j++) acc[j] += ov[i][j] * w;
+        }
+        M = m_new;
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
 #pragma unroll
