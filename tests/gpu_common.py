@@ -21,24 +21,29 @@ def say(*a):
     sys.stdout.flush()
 
 
-def max_abs_vhat(cache: O.Cache) -> float:
-    """max |v_hat| over every slot of a host pool (unwritten slots are 0)."""
+def max_abs_vhat(cache: O.Cache, batch: int = 256) -> float:
+    """max |v_hat| over every slot of a host pool (unwritten slots are 0),
+    taken over batches of chunks so that large pools stay cheap."""
     D, g, vb = cache.head_dim, cache.group_size, cache.v_bits
     off = cache.layout
-    ch = cache.pool.reshape(-1, cache.chunk_bytes)
+    ch_all = cache.pool.reshape(-1, cache.chunk_bytes)
     vbytes = D * BT * vb // 8
-    bits = np.unpackbits(ch[:, off[1]:off[1] + vbytes], axis=1, bitorder="little")
-    bits = bits.reshape(ch.shape[0], D * BT, vb).astype(np.uint32)
-    codes = (bits << np.arange(vb, dtype=np.uint32)).sum(-1).reshape(ch.shape[0], D, BT)
-    if vb == 16:
-        vals = codes.astype(np.uint16).view(np.float16).astype(np.float64)
-        return float(np.abs(vals).max())
     ng = D // g
-    s = ch[:, off[3]:off[3] + ng * BT * 4].copy().view(np.float32).reshape(-1, ng, BT).astype(np.float64)
-    z = ch[:, off[5]:off[5] + ng * BT].reshape(-1, ng, BT).astype(np.float64)
     gi = np.arange(D) // g
-    vals = (codes - z[:, gi, :]) * s[:, gi, :]
-    return float(np.abs(vals).max())
+    best = 0.0
+    for c0 in range(0, ch_all.shape[0], batch):
+        ch = ch_all[c0:c0 + batch]
+        bits = np.unpackbits(ch[:, off[1]:off[1] + vbytes], axis=1, bitorder="little")
+        bits = bits.reshape(ch.shape[0], D * BT, vb).astype(np.uint32)
+        codes = (bits << np.arange(vb, dtype=np.uint32)).sum(-1).reshape(ch.shape[0], D, BT)
+        if vb == 16:
+            vals = codes.astype(np.uint16).view(np.float16).astype(np.float64)
+        else:
+            s = ch[:, off[3]:off[3] + ng * BT * 4].copy().view(np.float32).reshape(-1, ng, BT).astype(np.float64)
+            z = ch[:, off[5]:off[5] + ng * BT].reshape(-1, ng, BT).astype(np.float64)
+            vals = (codes - z[:, gi, :]) * s[:, gi, :]
+        best = max(best, float(np.abs(vals).max()))
+    return best
 
 
 def assert_attention_close(got: np.ndarray, want: np.ndarray, vmax: float, what: str = ""):
