@@ -18,7 +18,6 @@ head, plus Q and O, plus the appended rows) over the measured step time.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -36,26 +35,18 @@ PROFILES = os.path.join(ROOT, "profiles")
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=400)
+    p.add_argument("--warmup", type=int, default=40)
     p.add_argument("--workload", type=int, default=2, choices=[2, 4])
     p.add_argument("--layers", type=int, default=4, help="layer caches rotated over (HBM, not cache)")
     p.add_argument("--split-tokens", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seqs", type=int, default=8, help="sequences in the oracle's timed sample")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="least oracle time in the CPU baseline")
     p.add_argument("--copy-probe", action="store_true",
-                   help="also run a plain 1 GiB device copy (counter scaling reference)")
+                   help="after the timed steps, stream 1 GiB in and 1 GiB out (counter scaling reference)")
     p.add_argument("--fp16-layer", action="store_true", help="time the fp16 sensitive-layer format")
     return p.parse_args()
-
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for name in ("decode.hip", "decode_mfma.hip"):
-        path = os.path.join(ROOT, "quantized_kv_cache_token_amd", "csrc", name)
-        if os.path.exists(path):
-            h.update(open(path, "rb").read())
-    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel: str, workload: str):
@@ -65,6 +56,8 @@ def measured_traffic(kernel: str, workload: str):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
+    from quantized_kv_cache_token_amd.profsum import kernel_source_hash
+
     if rec.get("source_hash") != kernel_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
@@ -156,11 +149,13 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     if args.copy_probe:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        # a plain streaming kernel of known traffic: reads 1 GiB, writes 1 GiB
+        src = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
+        del src, dst
 
     step_s = (t1 - t0) / args.steps
     split_ms = [a.elapsed_time(b) for a, b in evs.values()]
@@ -204,14 +199,16 @@ def main():
                      "avg_launch_us": round(split_s * 1e6, 2)},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(wl, kb, vb, min(args.cpu_seqs, B), per_token_head, q_bytes)
+        rec["cpu_baseline"] = cpu_baseline(wl, kb, vb, min(args.cpu_seqs, B), per_token_head, q_bytes,
+                                           args.cpu_seconds)
     print(json.dumps(rec), flush=True)
 
 
-def cpu_baseline(wl, kb, vb, nseq, per_token_head, q_bytes):
+def cpu_baseline(wl, kb, vb, nseq, per_token_head, q_bytes, min_seconds):
     """The oracle, as it stands, on a bounded sample of the same workload:
-    `nseq` sequences, all their query heads, one step (append one row, decode
-    over N tokens), on this host's cores.  GB/s over the same counted bytes."""
+    `nseq` sequences with all their query heads; one step appends one row per
+    sequence and decodes over N tokens.  Steps repeat until `min_seconds` have
+    passed.  GB/s over the same counted bytes as the GPU line."""
     import numpy as np
 
     from oracle import oracle as O
@@ -226,17 +223,24 @@ def cpu_baseline(wl, kb, vb, nseq, per_token_head, q_bytes):
         k, v = inputs.kv_rows(wl.seed, b, N - 1, Hkv, D, dtype=wl.dtype, outliers=outl)
         O.append(cache, k.float().numpy(), v.float().numpy(), [0, N - 1], [0], bt[b:b + 1])
     k, v = inputs.kv_rows(wl.seed, 1000, B, Hkv, D, dtype=wl.dtype, outliers=outl, step=1)
+    k, v = k.float().numpy(), v.float().numpy()
     q = inputs.queries(wl.seed, B, Hq, D, dtype=wl.dtype).float().numpy()
     sm = float(np.float32(1.0 / np.sqrt(D)))
+    cu, last, lens = np.arange(B + 1), np.full(B, N - 1), np.full(B, N, np.int32)
+    steps = 0
     t0 = time.perf_counter()
-    O.append(cache, k.float().numpy(), v.float().numpy(), np.arange(B + 1), np.full(B, N - 1), bt)
-    O.decode([cache], [bt], [np.full(B, N, np.int32)], q, sm, 0.0, 0)
-    dt = time.perf_counter() - t0
+    while True:
+        O.append(cache, k, v, cu, last, bt)
+        O.decode([cache], [bt], [lens], q, sm, 0.0, 0)
+        steps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
     nbytes = B * Hkv * N * per_token_head + B * Hq * D * (q_bytes + 4) + B * Hkv * (2 * D * q_bytes + per_token_head)
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{B} of {wl.batch} sequences, all {Hq} query heads, one step (append 1 row + fp64 "
-                      f"decode over {N} tokens); {dt:.2f} s"}
+    return {"value": round(steps * nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": O.num_threads(),
+            "kind": "oracle",
+            "sample": f"{B} of {wl.batch} sequences, all {Hq} query heads; {steps} steps of (append 1 row per "
+                      f"sequence + fp64 decode over {N} tokens) in {dt:.2f} s"}
 
 
 if __name__ == "__main__":

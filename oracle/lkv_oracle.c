@@ -30,6 +30,9 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define BT ORC_BLOCK_TOKENS
 
@@ -572,4 +575,13 @@ void orc_default_thresholds(int32_t n_tokens, float* tau_low, float* tau_high)
     const double n = n_tokens > 0 ? (double)n_tokens : 1.0;
     *tau_low = (float)(eps4 / n);
     *tau_high = (float)((eps4 / eps6) / n);
+}
+
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }

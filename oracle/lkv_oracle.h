@@ -104,6 +104,10 @@ int orc_tier_update(const orc_cache* src, const orc_view* src_view,
  * tokens: tau_low = eps4/n, tau_high = (eps4/eps6)/n, eps_b = 1/(2(2^b-1)). */
 void orc_default_thresholds(int32_t n_tokens, float* tau_low, float* tau_high);
 
+/* Threads an OpenMP parallel region of the oracle runs with (1 when built
+ * without OpenMP): the core count a timing of the oracle states. */
+int orc_num_threads(void);
+
 #ifdef __cplusplus
 }
 #endif

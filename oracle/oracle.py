@@ -74,6 +74,8 @@ def lib():
         L.orc_tier_update.restype = C.c_int
         L.orc_default_thresholds.argtypes = [C.c_int32, C.POINTER(C.c_float), C.POINTER(C.c_float)]
         L.orc_default_thresholds.restype = None
+        L.orc_num_threads.argtypes = []
+        L.orc_num_threads.restype = C.c_int
         _lib = L
     return _lib
 
@@ -125,6 +127,11 @@ def default_thresholds(n_tokens: int) -> tuple[float, float]:
     lo, hi = C.c_float(), C.c_float()
     lib().orc_default_thresholds(n_tokens, C.byref(lo), C.byref(hi))
     return float(lo.value), float(hi.value)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().orc_num_threads())
 
 
 # ------------------------------------------------------------------ caches
