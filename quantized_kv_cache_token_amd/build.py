@@ -28,6 +28,7 @@ SOURCES = [
     ("tier.hip", ["-ffp-contract=off"]),
     ("decode.hip", []),
     ("decode_mfma.hip", []),
+    ("decode_f16.hip", []),
     ("api.cpp", ["-x", "hip"]),
 ]
 

@@ -166,6 +166,9 @@ hipError_t launch_decode_split(const SegArgs& s, const void* q, int q_dtype, int
     if (launch_decode_split_mfma(s, q, q_dtype, batch, num_q_heads, sm_scale, tau_low, split_tokens, total_splits,
                                  partials, stream, &err))
         return err;
+    if (launch_decode_split_f16(s, q, q_dtype, batch, num_q_heads, sm_scale, tau_low, split_tokens, total_splits,
+                                partials, stream, &err))
+        return err;
     SplitArgs a;
     a.seg = s;
     a.q = q;

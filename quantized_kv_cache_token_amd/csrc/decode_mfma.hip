@@ -36,12 +36,9 @@
 #include <hip/hip_fp16.h>
 
 #include "lkv_internal.h"
+#include "wave_util.h"
 
 namespace lkv {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short short4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 struct MfmaArgs {
     SegArgs seg;
@@ -53,14 +50,6 @@ struct MfmaArgs {
     float tau_low;
     float* partials;
 };
-
-__device__ __forceinline__ f32x4_t mfma_16x16x32(const uint32_t (&a)[4], const uint32_t (&b)[4], f32x4_t c)
-{
-    bf16x8_t av, bv;
-    __builtin_memcpy(&av, a, 16);
-    __builtin_memcpy(&bv, b, 16);
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, c, 0, 0, 0);
-}
 
 // x | (x << 10): one VALU instruction.
 __device__ __forceinline__ uint32_t lshl10_or(uint32_t x)
@@ -182,28 +171,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
 {
     const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
     return __builtin_bit_cast(uint32_t, v);
-}
-
-// Value of the neighbouring lane (lane ^ 1) -- DPP quad permutation.
-__device__ __forceinline__ float xor1(float v)
-{
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
-}
-
-// Reductions over the four 16-lane rows (lanes l, l^16, l^32, l^48).
-__device__ __forceinline__ float rows_max(float v)
-{
-    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float rows_sum(float v)
-{
-    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ uint32_t byte_of(const uint32_t (&w)[4], int x) { return (w[x >> 2] >> (8 * (x & 3))) & 0xFFu; }
@@ -627,8 +594,9 @@ bool launch_decode_split_mfma(const SegArgs& s, const void* q, int q_dtype, int3
     const Fmt& f = s.f;
     const int G = num_q_heads / f.H;
     if (q_dtype != LKV_BF16 || f.D != 128 || f.g != 64 || f.fp16 || f.kb != 6 || (f.vb != 4 && f.vb != 6) ||
-        (G != 4 && G != 8))
+        (G != 4 && G != 8) || ((uintptr_t)q & 15) != 0)  // Q is read 16 bytes at a time
         return false;
+    if (split_tokens > 64 * BT) return false;  // a split's block-table entries are held one per lane
     MfmaArgs a;
     a.seg = s;
     a.q = (const uint16_t*)q;

@@ -51,6 +51,12 @@ bool launch_decode_split_mfma(const SegArgs& s, const void* q, int q_dtype, int3
                               float sm_scale, float tau_low, int32_t split_tokens, int32_t total_splits,
                               float* partials, hipStream_t stream, hipError_t* err);
 
+// Matrix-core split kernel of the fp16 format: launches and returns true for
+// D 128, bf16 or fp32 Q, G 4 or 8.
+bool launch_decode_split_f16(const SegArgs& s, const void* q, int q_dtype, int32_t batch, int32_t num_q_heads,
+                             float sm_scale, float tau_low, int32_t split_tokens, int32_t total_splits,
+                             float* partials, hipStream_t stream, hipError_t* err);
+
 hipError_t launch_decode_combine(int32_t batch, int32_t num_q_heads, int32_t D, int32_t total_splits,
                                  const float* partials, float* out, hipStream_t stream);
 

@@ -34,7 +34,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 PROBE_BYTES = 1 << 30          # the streaming probe reads and writes 1 GiB
 PROBE_REGEX = r"neg_kernel"    # its kernel: an elementwise negation over fp32
-DECODE_SOURCES = ("decode.hip", "decode_mfma.hip")
+DECODE_SOURCES = ("decode.hip", "decode_mfma.hip", "decode_f16.hip", "wave_util.h")
 
 
 def kernel_source_hash() -> str:

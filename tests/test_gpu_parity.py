@@ -119,6 +119,65 @@ def test_decode_parity_splits_and_skip(qdtype, split, tau):
     assert_attention_close(got, want, vmax, f"split {split} tau {tau}")
 
 
+@pytest.mark.parametrize("G", [4, 8])
+@pytest.mark.parametrize("qdtype", ["f32", "bf16"])
+@pytest.mark.parametrize("split,tau", [(64, 0.0), (1024, 0.0), (256, 1e-5), (1024, 2e-4)])
+def test_decode_parity_fp16_layer(G, qdtype, split, tau):
+    """The fp16 sensitive-layer format on its matrix-core kernel."""
+    got, want, vmax = _decode_case((128, 64, 16, 16), G, qdtype, [5, 700, 1500, 2048], tau, split)
+    assert_attention_close(got, want, vmax, f"fp16 G{G} {qdtype} split {split} tau {tau}")
+
+
+@pytest.mark.parametrize("fmt", [(128, 64, 6, 4), (128, 64, 6, 6), (128, 64, 16, 16), (64, 32, 6, 4)], ids=_fmt_id)
+def test_decode_ignores_stale_bytes_past_the_end(fmt):
+    """Slots past a sequence's end may hold any bytes (here all 0xFF: NaN
+    scales, NaN fp16 values); they must not reach the output."""
+    D, g, kb, vb = fmt
+    lens = [1, 65, 200, 777]
+    rng = np.random.default_rng(21)
+    bt, nblk = block_tables(lens, rng)
+    pair = Pair(D, g, kb, vb, 2, nblk)
+    pair.gpu.pool.fill_(0xFF)
+    pair.ref.pool[:] = 0xFF
+    _prefill(pair, lens, 2, D, "bf16", 21, bt, outliers=True)
+    for G in (4, 8):
+        q = inputs.queries(21, len(lens), 2 * G, D)
+        view = lkv.View(torch.tensor(bt).cuda(), torch.tensor(lens, dtype=torch.int32).cuda(), max(lens))
+        say("decode stale bytes", fmt, "G", G)
+        got = lkv.decode_attn([pair.gpu], [view], q.cuda(), sm_scale(D), 0.0, 128).cpu().numpy()
+        want = O.decode([pair.ref], [bt], [np.array(lens, np.int32)], to_f32_host(q), sm_scale(D), 0.0, 128)
+        # v_hat over the live slots only (the stale ones decode to NaN)
+        live = Pair(D, g, kb, vb, 2, nblk)
+        _prefill(live, lens, 2, D, "bf16", 21, bt, outliers=True)
+        assert_attention_close(got, want, max_abs_vhat(live.ref), f"stale bytes {fmt} G{G}")
+
+
+@pytest.mark.parametrize("fmt", [(128, 64, 6, 4), (128, 64, 16, 16)], ids=_fmt_id)
+def test_decode_split_longer_than_4096_tokens(fmt):
+    got, want, vmax = _decode_case(fmt, 4, "bf16", [9000, 5000, 4097], 1e-5, 8192)
+    assert_attention_close(got, want, vmax, f"split 8192 {fmt}")
+
+
+@pytest.mark.parametrize("fmt", [(128, 64, 6, 4), (128, 64, 16, 16)], ids=_fmt_id)
+def test_decode_query_not_16_byte_aligned(fmt):
+    D, g, kb, vb = fmt
+    lens = [300, 129]
+    rng = np.random.default_rng(8)
+    bt, nblk = block_tables(lens, rng)
+    pair = Pair(D, g, kb, vb, 2, nblk)
+    _prefill(pair, lens, 2, D, "bf16", 8, bt)
+    q = inputs.queries(8, 2, 8, D)
+    buf = torch.empty(q.numel() + 1, dtype=q.dtype, device="cuda")
+    qv = buf[1:].view(q.shape)
+    qv.copy_(q.cuda())
+    assert qv.data_ptr() % 16 != 0
+    view = lkv.View(torch.tensor(bt).cuda(), torch.tensor(lens, dtype=torch.int32).cuda(), max(lens))
+    say("decode unaligned q", fmt)
+    got = lkv.decode_attn([pair.gpu], [view], qv, sm_scale(D), 0.0, 64).cpu().numpy()
+    want = O.decode([pair.ref], [bt], [np.array(lens, np.int32)], to_f32_host(q), sm_scale(D), 0.0, 64)
+    assert_attention_close(got, want, max_abs_vhat(pair.ref), f"unaligned q {fmt}")
+
+
 def test_decode_skip_changes_the_result_as_the_oracle_does():
     """With a large tau the skip moves the output well beyond the tolerance;
     the GPU follows the oracle with skip, not the oracle without."""
