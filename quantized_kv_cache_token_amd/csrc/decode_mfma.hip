@@ -35,6 +35,8 @@
 // (o[128], m, L) per split follow the generic kernel exactly.
 #include <hip/hip_fp16.h>
 
+#include <type_traits>
+
 #include "lkv_internal.h"
 #include "wave_util.h"
 
@@ -173,6 +175,13 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// a * b rounded to fp32 on its own: never fused into a later addition.
+__device__ __forceinline__ float mul_rounded(float a, float b)
+{
+#pragma clang fp contract(off)
+    return a * b;
+}
+
 __device__ __forceinline__ uint32_t byte_of(const uint32_t (&w)[4], int x) { return (w[x >> 2] >> (8 * (x & 3))) & 0xFFu; }
 
 // Raw bytes of one block held by one lane: codes in registers, the block's
@@ -287,7 +296,10 @@ __device__ __forceinline__ void block_qk(const BlockRegs<VB>& R, const uint32_t 
 // the running (m, L); fills the weights p (0 for dead or skipped tokens) and
 // returns the rescale factor of this lane's head.  keep: bit u set unless
 // every V term of tile pair u (32 tokens) is skipped for every head.
-template <int VB, int G>
+// PARTIAL: the block has dead slots past the end (nlive < 64), masked here;
+// full blocks skip that work.  score_scale > 0 is applied after the maximum
+// (the maximum of scaled scores is the scaled maximum), inside the exponent.
+template <int VB, int G, bool PARTIAL>
 __device__ __forceinline__ float block_softmax(const f32x4_t (&dot)[4], const uint8_t* lds, SplitState& S, float qsum,
                                                float score_scale, float tau_low, int nlive, int q, int c,
                                                float (&p)[16], uint32_t& keep)
@@ -304,15 +316,18 @@ __device__ __forceinline__ float block_softmax(const f32x4_t (&dot)[4], const ui
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             const int x = tok_of<VB>(t, r);
-            // this lane's group share: s_g * sum_{d in g} q_d (c_d - z_g)
-            const float pg = sk[x] * (dot[t][r] - (float)byte_of(zk, x) * qsum);
-            float s2 = (pg + xor1(pg)) * score_scale;  // both groups, base 2
-            if (nlive < BT) s2 = 16 * q + x < nlive ? s2 : -INFINITY;
+            // this lane's group share: s_g * sum_{d in g} q_d (c_d - z_g),
+            // rounded before the exchange so that the two lanes of a head
+            // add the same two numbers and hold bit-identical scores (their
+            // running maxima must never differ)
+            const float pg = mul_rounded(sk[x], dot[t][r] - (float)byte_of(zk, x) * qsum);
+            float s2 = pg + xor1(pg);  // both groups, natural units
+            if constexpr (PARTIAL) s2 = 16 * q + x < nlive ? s2 : -INFINITY;
             sc[4 * t + r] = s2;
             bmax = fmaxf(bmax, s2);
         }
     }
-    bmax = rows_max(bmax);
+    bmax = rows_max(bmax) * score_scale;  // base 2
     // The reference maximum only moves when a block exceeds it by more than
     // 2^8: weights stay <= 256 (no overflow anywhere), the accumulators are
     // rarely rescaled, and p / L -- all that the output and the skip rule
@@ -322,7 +337,7 @@ __device__ __forceinline__ float block_softmax(const f32x4_t (&dot)[4], const ui
     float bsum = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-        p[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
+        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], score_scale, -m_new));
         bsum += p[i];
     }
     S.l_run = S.l_run * alpha + rows_sum(bsum);
@@ -364,9 +379,9 @@ __device__ __forceinline__ void neg_off_pairs(const uint32_t (&z)[4], int u, uin
     }
 }
 
-template <int VB, int G>
+template <int VB, int G, bool PARTIAL>
 __device__ __forceinline__ void block_pv(const BlockRegs<VB>& R, const uint8_t* lds, SplitState& S,
-                                         const float (&p)[16], float alpha, bool dead, uint32_t keep, int q, int c,
+                                         const float (&p)[16], float alpha, uint32_t keep, int q, int c,
                                          int hA, const Magic& mk)
 {
     constexpr int NG = G == 8 ? 2 : 1;
@@ -405,7 +420,7 @@ __device__ __forceinline__ void block_pv(const BlockRegs<VB>& R, const uint8_t* 
                 const int x = tok_of<VB>(t, r);
                 const float pj = p[4 * t + r];
                 float pp = pj * sv[g][x];
-                if (dead) pp = pj > 0.0f ? pp : 0.0f;  // dead token: its scale bytes may be stale
+                if constexpr (PARTIAL) pp = pj > 0.0f ? pp : 0.0f;  // dead token: its scale bytes may be stale
                 const float hi = __uint_as_float(__float_as_uint(pp) & 0xFFFF0000u);
                 v[j] = part ? pp - hi : hi;
             }
@@ -447,7 +462,7 @@ __device__ __forceinline__ void block_pv(const BlockRegs<VB>& R, const uint8_t* 
 }
 
 template <int VB, int G>
-__global__ __launch_bounds__(64) void split_mfma_kernel(MfmaArgs a)
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void split_mfma_kernel(MfmaArgs a)
 {
     static_assert(G == 4 || G == 8, "4 or 8 query heads per KV head");
     constexpr int D = 128;
@@ -548,7 +563,8 @@ __global__ __launch_bounds__(64) void split_mfma_kernel(MfmaArgs a)
     }
     // (the empty asm statements keep the compiler from moving the loads to
     // their first use)
-    for (int k = 0; k < nblk; k++) {
+    auto block = [&](int k, auto partial) {
+        constexpr bool PARTIAL = decltype(partial)::value;
         const uint8_t* cn = chunk_of(min(k + 1, nblk - 1));
         stage_meta(R.meta, meta_lds, lane);
         load_meta<VB>(R, cn, off_ks, lane);
@@ -560,11 +576,16 @@ __global__ __launch_bounds__(64) void split_mfma_kernel(MfmaArgs a)
         const int nlive = min(BT, t1 - t0 - k * BT);
         float p[16];
         uint32_t keep;
-        const float alpha = block_softmax<VB, G>(dot, lds, S, qsum, a.score_scale, a.tau_low, nlive, q, c, p, keep);
-        block_pv<VB, G>(R, lds, S, p, alpha, nlive < BT, keep, q, c, hA, mk);
+        const float alpha =
+            block_softmax<VB, G, PARTIAL>(dot, lds, S, qsum, a.score_scale, a.tau_low, nlive, q, c, p, keep);
+        block_pv<VB, G, PARTIAL>(R, lds, S, p, alpha, keep, q, c, hA, mk);
         load_v<VB>(R, cn, off_vc, c, q);
         asm volatile("" ::: "memory");
-    }
+    };
+    // full blocks, then the split's last block if it has dead slots
+    const int nfull = (t1 - t0) / BT;
+    for (int k = 0; k < nfull; k++) block(k, std::false_type{});
+    if (nfull < nblk) block(nfull, std::true_type{});
 
     // ---- write the partial (o, m, L) of every head of the group
     // P.V output: lane (column c, row group q) holds rows 4q .. 4q+3 of each
@@ -594,7 +615,8 @@ bool launch_decode_split_mfma(const SegArgs& s, const void* q, int q_dtype, int3
     const Fmt& f = s.f;
     const int G = num_q_heads / f.H;
     if (q_dtype != LKV_BF16 || f.D != 128 || f.g != 64 || f.fp16 || f.kb != 6 || (f.vb != 4 && f.vb != 6) ||
-        (G != 4 && G != 8) || ((uintptr_t)q & 15) != 0)  // Q is read 16 bytes at a time
+        (G != 4 && G != 8) || ((uintptr_t)q & 15) != 0 ||  // Q is read 16 bytes at a time
+        !(sm_scale > 0.0f))  // the scale is applied after the block maximum
         return false;
     if (split_tokens > 64 * BT) return false;  // a split's block-table entries are held one per lane
     MfmaArgs a;
