@@ -46,6 +46,7 @@ def parse():
     p.add_argument("--copy-probe", action="store_true",
                    help="after the timed steps, stream 1 GiB in and 1 GiB out (counter scaling reference)")
     p.add_argument("--fp16-layer", action="store_true", help="time the fp16 sensitive-layer format")
+    p.add_argument("--no-tier", action="store_true", help="skip the tier-update secondary figure")
     return p.parse_args()
 
 
@@ -88,18 +89,26 @@ def main():
     lens = torch.full((B,), N, dtype=torch.int32, device=dev)
     outl = inputs.outlier_channels(wl.seed, Hkv, D) if wl.outliers else None
 
-    # ---- layer caches, filled by the append kernel (prefill, untimed)
+    # ---- layer caches, filled by the append kernel (prefill; each call timed
+    # with events for the secondary figures, outside the timed steps)
     caches = []
+    prefill_ms = []
     for layer in range(args.layers):
         c = lkv.Cache(D, wl.group_size, kb, vb, Hkv, B * nblk, device=dev)
         for b in range(B):
             k, v = inputs.kv_rows(wl.seed, b, N - 1, Hkv, D, dtype=wl.dtype, outliers=outl, layer=layer,
                                   device=dev)
             cu = torch.tensor([0, N - 1], dtype=torch.int32, device=dev)
-            lkv.quant_append(c, k, v, cu, torch.zeros(1, dtype=torch.int32, device=dev), bt[b:b + 1], N - 1)
+            sp0 = torch.zeros(1, dtype=torch.int32, device=dev)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            lkv.quant_append(c, k, v, cu, sp0, bt[b:b + 1], N - 1)
+            e1.record()
+            prefill_ms.append((e0, e1))
             del k, v
         caches.append(c)
     torch.cuda.synchronize()
+    prefill_ms = [a.elapsed_time(b) for a, b in prefill_ms]
     chunk = caches[0].chunk_bytes
     view = lkv.View(bt, lens, N)
 
@@ -198,10 +207,64 @@ def main():
                      "traffic": traffic, "alg_bytes_per_launch": split_alg,
                      "avg_launch_us": round(split_s * 1e6, 2)},
     }
+    in_bytes = 2 if wl.dtype in ("bf16", "f16") else 4
+    pre_bytes = (N - 1) * Hkv * (2 * D * in_bytes + per_token_head)
+    pre_s = float(np.median(prefill_ms)) / 1e3
+    rec["secondary"] = {
+        "append_prefill": {"GB/s": round(pre_bytes / pre_s / 1e9, 1), "us_per_call": round(pre_s * 1e6, 1),
+                           "rows_per_call": N - 1, "counted": "bf16 K/V rows in + packed rows out"},
+    }
+    if not args.fp16_layer and not args.no_tier:
+        del caches, calls
+        torch.cuda.empty_cache()
+        rec["secondary"]["tier_update"] = tier_figure(wl, dev)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, kb, vb, min(args.cpu_seqs, B), per_token_head, q_bytes,
                                            args.cpu_seconds)
     print(json.dumps(rec), flush=True)
+
+
+def tier_figure(wl, dev):
+    """One lkv_tier_update at the tiered workload's shape (the batch and
+    context of `wl`, K6V6 source, scores with 10% high / 30% mid / 60% low),
+    timed with events after one untimed call.  Counted bytes: source rows and
+    scores read, survivors' rows, tiers and counts written."""
+    import numpy as np
+    import torch
+
+    from quantized_kv_cache_token_amd import inputs, lkv
+
+    B, Hkv, D, N = wl.batch, wl.num_kv_heads, wl.head_dim, wl.n_ctx
+    nblk = (N + 63) // 64
+    bt = torch.arange(B * nblk, dtype=torch.int32, device=dev).view(B, nblk)
+    src = lkv.Cache(D, wl.group_size, 6, 6, Hkv, B * nblk, device=dev)
+    outl = inputs.outlier_channels(wl.seed, Hkv, D) if wl.outliers else None
+    for b in range(B):
+        k, v = inputs.kv_rows(wl.seed, b, N, Hkv, D, dtype=wl.dtype, outliers=outl, device=dev)
+        lkv.quant_append(src, k, v, torch.tensor([0, N], dtype=torch.int32, device=dev),
+                         torch.zeros(1, dtype=torch.int32, device=dev), bt[b:b + 1], N)
+        del k, v
+    tl, th = lkv.default_thresholds(N)
+    scores = torch.stack([inputs.tier_scores(wl.seed, b, N, tl, th) for b in range(B)]).to(dev)
+    hdst = lkv.Cache(D, wl.group_size, 6, 6, Hkv, B * nblk, device=dev)
+    mdst = lkv.Cache(D, wl.group_size, 6, 4, Hkv, B * nblk, device=dev)
+    tiers = torch.zeros((B, N), dtype=torch.uint8, device=dev)
+    nh = torch.zeros(B, dtype=torch.int32, device=dev)
+    nm = torch.zeros_like(nh)
+    view = lkv.View(bt, torch.full((B,), N, dtype=torch.int32, device=dev), N)
+    ws = torch.empty(lkv.tier_workspace_bytes(B, N), dtype=torch.uint8, device=dev)
+    call = lambda: lkv.tier_update(src, view, scores, tl, th, hdst, bt, mdst, bt, nh, nm, tiers, ws)
+    call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    call()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3
+    n_h, n_m = int(nh.sum()), int(nm.sum())
+    nbytes = B * N * Hkv * 212 + B * N * 4 + (n_h * 212 + n_m * 180) * Hkv + B * N + 8 * B
+    return {"GB/s": round(nbytes / t / 1e9, 1), "us_per_call": round(t * 1e6, 1), "high": n_h, "mid": n_m,
+            "evicted": B * N - n_h - n_m, "counted": "K6V6 rows and scores in, HIGH/MID rows and tiers out"}
 
 
 def cpu_baseline(wl, kb, vb, nseq, per_token_head, q_bytes, min_seconds):

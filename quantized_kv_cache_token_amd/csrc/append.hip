@@ -7,10 +7,11 @@
 // lanes holding the group, the codes go to LDS, and the workgroup then packs
 // 32-bit words and writes them.
 //
-// Decode appends one row per sequence, so the kernel is laid out for
-// latency: the index loads are issued together, the V words that must be
-// merged are loaded as soon as the chunk address is known, and nothing waits
-// on memory between those loads and the stores.
+// Latency: every input load of a wave is issued before it quantises its
+// first row, and the V words that other slots share are merged in memory
+// with atomic AND/OR (no load of the old word), so a one-row decode append
+// waits for two memory round trips: the indices, then the rows and the block
+// table entry.
 #include <hip/hip_fp16.h>
 
 #include "lkv_internal.h"
@@ -30,16 +31,24 @@ struct AppendArgs {
     int32_t nblk;    // logical blocks a sequence's new rows can touch
 };
 
+// Raw bits of input element i (fp32, or a 16-bit pattern), and their value.
 template <int DT>
-__device__ __forceinline__ float load_in(const void* p, int64_t i)
+__device__ __forceinline__ uint32_t load_raw(const void* p, int64_t i)
 {
-    if constexpr (DT == LKV_F32) return ((const float*)p)[i];
-    const uint16_t u = ((const uint16_t*)p)[i];
-    if constexpr (DT == LKV_BF16) return __uint_as_float((uint32_t)u << 16);
-    return __half2float(__ushort_as_half(u));
+    if constexpr (DT == LKV_F32) return ((const uint32_t*)p)[i];
+    return ((const uint16_t*)p)[i];
+}
+template <int DT>
+__device__ __forceinline__ float raw_value(uint32_t u)
+{
+    if constexpr (DT == LKV_F32) return __uint_as_float(u);
+    if constexpr (DT == LKV_BF16) return __uint_as_float(u << 16);
+    return __half2float(__ushort_as_half((uint16_t)u));
 }
 
 constexpr int MAXW = 16;  // V words per thread: D * 64 slots * 16 bits / 32 / 256 threads at most
+constexpr int MAXR = 32;  // rows per wave: 64 slots x (K, V) / 4 waves
+constexpr int CH = 8;     // rows whose loads are issued together
 
 template <int D, int DT>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
@@ -63,56 +72,54 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
     uint8_t* ch = a.pool + (blk * f.H + kvh) * f.chunk;
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int nrows = 2 * (s1 - s0);
-
-    // V words of this chunk that hold bits of slots [s0, s1): load the old
-    // contents of the partially covered ones now, to merge later
-    const int w0 = (f.vb * s0) / 32, w1 = (f.vb * s1 - 1) / 32;
-    const int wv = w1 - w0 + 1;
-    const int nw = D * wv;
-    uint32_t old[MAXW];
-#pragma unroll
-    for (int j = 0; j < MAXW; j++) {
-        const int idx = threadIdx.x + 256 * j;
-        old[j] = 0u;
-        if (idx < nw) {
-            const int d = idx / wv, w = w0 + idx % wv;
-            if (field_mask(w, f.vb, s0, s1) != 0xFFFFFFFFu)
-                old[j] = ((const uint32_t*)(ch + f.off_vc + d * f.vrow))[w];
-        }
-    }
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
+    const int nrows = 2 * (s1 - s0);  // row r: slot s0 + r / 2, K (r even) or V (r odd)
 
     __shared__ uint16_t kc[BT][D];
     __shared__ uint16_t vc[BT][D];
-    for (int r = wave; r < nrows; r += 4) {
-        const int slot = s0 + (r >> 1);
-        const bool is_v = r & 1;
-        const int64_t in_row = (int64_t)(row0 + (lb * BT + slot - sp)) * f.H + kvh;
-        float x[VPL];
+    // Rows go in chunks of CH per wave.  A chunk's input values are all
+    // requested before any is used; rows past the end reload the last valid
+    // row (in bounds, no branch), so the chunk waits for memory once.
+#pragma unroll 1
+    for (int k0 = 0; k0 < MAXR; k0 += CH) {
+        if (wave + 4 * k0 >= nrows) break;
+        uint32_t x[CH][VPL];  // raw bits: converted where used
 #pragma unroll
-        for (int j = 0; j < VPL; j++) x[j] = load_in<DT>(is_v ? a.v : a.k, in_row * D + lane + 64 * j);
-        const int bits = is_v ? f.vb : f.kb;
+        for (int k = 0; k < CH; k++) {
+            const int r = min(wave + 4 * (k0 + k), nrows - 1);
+            const int slot = s0 + (r >> 1);
+            const int64_t in_row = (int64_t)(row0 + (lb * BT + slot - sp)) * f.H + kvh;
 #pragma unroll
-        for (int j = 0; j < VPL; j++) {
-            const int d = lane + 64 * j;
-            uint32_t code;
-            if (f.fp16) {
-                code = f16_bits(x[j]);
-            } else {
-                float s;
-                int z;
-                code = (uint32_t)quantize_lane(x[j], f.g, bits, &s, &z);
-                if ((d % f.g) == 0) {
-                    const int gi = d / f.g;
-                    float* sc = (float*)(ch + (is_v ? f.off_vs : f.off_ks));
-                    uint8_t* zc = ch + (is_v ? f.off_vz : f.off_kz);
-                    sc[gi * BT + slot] = s;
-                    zc[gi * BT + slot] = (uint8_t)z;
+            for (int j = 0; j < VPL; j++) x[k][j] = load_raw<DT>((r & 1) ? a.v : a.k, in_row * D + lane + 64 * j);
+        }
+#pragma unroll
+        for (int k = 0; k < CH; k++) {
+            const int r = wave + 4 * (k0 + k);
+            if (r >= nrows) break;
+            const int slot = s0 + (r >> 1);
+            const bool is_v = r & 1;
+            const int bits = is_v ? f.vb : f.kb;
+#pragma unroll
+            for (int j = 0; j < VPL; j++) {
+                const int d = lane + 64 * j;
+                uint32_t code;
+                if (f.fp16) {
+                    code = f16_bits(raw_value<DT>(x[k][j]));
+                } else {
+                    float sc;
+                    int z;
+                    code = (uint32_t)quantize_lane(raw_value<DT>(x[k][j]), f.g, bits, &sc, &z);
+                    if ((d % f.g) == 0) {
+                        const int gi = d / f.g;
+                        float* scales = (float*)(ch + (is_v ? f.off_vs : f.off_ks));
+                        uint8_t* zeros = ch + (is_v ? f.off_vz : f.off_kz);
+                        scales[gi * BT + slot] = sc;
+                        zeros[gi * BT + slot] = (uint8_t)z;
+                    }
                 }
+                if (is_v) vc[slot][d] = (uint16_t)code;
+                else kc[slot][d] = (uint16_t)code;
             }
-            if (is_v) vc[slot][d] = (uint16_t)code;
-            else kc[slot][d] = (uint16_t)code;
         }
     }
     __syncthreads();
@@ -126,16 +133,26 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
         ((uint32_t*)(ch + f.off_kc + slot * f.krow))[w] = word;
     }
     // V rows: channel-major; only the words that hold bits of slots [s0, s1)
-    // are written, and their bits of other slots are kept.
+    // are written.  A word shared with other slots keeps their bits: its
+    // field bits are cleared, then set, by two atomics (in program order to
+    // the same address, so the second sees the first).
+    const int w0 = (f.vb * s0) / 32, w1 = (f.vb * s1 - 1) / 32;
+    const int wv = w1 - w0 + 1;
+    const int nw = D * wv;
 #pragma unroll
     for (int j = 0; j < MAXW; j++) {
         const int idx = threadIdx.x + 256 * j;
         if (idx < nw) {
             const int d = idx / wv, w = w0 + idx % wv;
             const uint32_t mask = field_mask(w, f.vb, s0, s1);
-            uint32_t word = pack_word(w, f.vb, s0, s1, [&](int s) { return (uint32_t)vc[s][d]; });
-            if (mask != 0xFFFFFFFFu) word = (old[j] & ~mask) | (word & mask);
-            ((uint32_t*)(ch + f.off_vc + d * f.vrow))[w] = word;
+            const uint32_t word = pack_word(w, f.vb, s0, s1, [&](int s) { return (uint32_t)vc[s][d]; });
+            uint32_t* dst = (uint32_t*)(ch + f.off_vc + d * f.vrow) + w;
+            if (mask == 0xFFFFFFFFu) {
+                *dst = word;
+            } else {
+                atomicAnd(dst, ~mask);
+                atomicOr(dst, word & mask);
+            }
         }
     }
 }
