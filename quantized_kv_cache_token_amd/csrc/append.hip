@@ -92,10 +92,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
 #pragma unroll
             for (int j = 0; j < VPL; j++) x[k][j] = load_raw<DT>((r & 1) ? a.v : a.k, in_row * D + lane + 64 * j);
         }
-#pragma unroll
-        for (int k = 0; k < CH; k++) {
+        auto process = [&](int k) {
             const int r = wave + 4 * (k0 + k);
-            if (r >= nrows) break;
             const int slot = s0 + (r >> 1);
             const bool is_v = r & 1;
             const int bits = is_v ? f.vb : f.kb;
@@ -119,6 +117,18 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
                 }
                 if (is_v) vc[slot][d] = (uint16_t)code;
                 else kc[slot][d] = (uint16_t)code;
+            }
+        };
+        if (wave + 4 * (k0 + CH - 1) < nrows) {
+            // a full chunk: no branch between rows, so their independent
+            // reductions and divisions interleave
+#pragma unroll
+            for (int k = 0; k < CH; k++) process(k);
+        } else {
+#pragma unroll
+            for (int k = 0; k < CH; k++) {
+                if (wave + 4 * (k0 + k) >= nrows) break;
+                process(k);
             }
         }
     }

@@ -13,17 +13,36 @@
 
 namespace lkv {
 
-// min / max over aligned segments of `seg` lanes (seg a power of two <= 64).
-__device__ __forceinline__ float seg_min(float x, int seg)
+// min / max over aligned segments of `seg` lanes (seg 16, 32 or 64), with
+// lane exchanges that stay in the vector ALU: quad permutations (lane ^ 1,
+// lane ^ 2), mirrors within 8 and 16 lanes (after the smaller steps every
+// lane of the half holds its half's extreme), then swaps of 16-lane rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v)
 {
-    for (int o = seg >> 1; o > 0; o >>= 1) x = fminf(x, __shfl_xor(x, o, 64));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <bool MAX>
+__device__ __forceinline__ float seg_extreme(float x, int seg)
+{
+    auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : fminf(a, b); };
+    x = op(x, dpp_mov<0xB1>(x));   // quad_perm [1,0,3,2]
+    x = op(x, dpp_mov<0x4E>(x));   // quad_perm [2,3,0,1]
+    x = op(x, dpp_mov<0x141>(x));  // row_half_mirror
+    x = op(x, dpp_mov<0x140>(x));  // row_mirror
+    if (seg >= 32) {
+        const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    }
+    if (seg >= 64) {
+        const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    }
     return x;
 }
-__device__ __forceinline__ float seg_max(float x, int seg)
-{
-    for (int o = seg >> 1; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-    return x;
-}
+__device__ __forceinline__ float seg_min(float x, int seg) { return seg_extreme<false>(x, seg); }
+__device__ __forceinline__ float seg_max(float x, int seg) { return seg_extreme<true>(x, seg); }
 
 // Quantise the value x held by this lane; the group is the aligned segment of
 // g lanes that holds it.  Returns the code; *s, *z receive the group's scale
