@@ -166,7 +166,10 @@ int lkv_decode_combine(const lkv_cache* segs, const lkv_view* views, int32_t nse
  * eps4 * max|v|, the 4-bit half-step relative to a group's range. */
 void lkv_default_thresholds(int32_t n_tokens, float* tau_low, float* tau_high);
 
-/* Workspace bytes of lkv_tier_update (host). */
+/* Workspace bytes of lkv_tier_update (host): two int32 maps [batch]
+ * [scores_stride] (source token of each HIGH / MID destination position),
+ * then (HIGH, MID) int32 counts per 2048-token scan chunk of each sequence.
+ * The workspace must be 8-byte aligned; its contents need no initialisation. */
 int64_t lkv_tier_workspace_bytes(int32_t batch, int32_t scores_stride);
 
 /* Attention-aware tier update (Super KV Compression page, second layer).

@@ -234,7 +234,9 @@ void lkv_default_thresholds(int32_t n_tokens, float* tau_low, float* tau_high)
 int64_t lkv_tier_workspace_bytes(int32_t batch, int32_t scores_stride)
 {
     if (batch < 0 || scores_stride < 0) return LKV_EINVAL;
-    return 2 * (int64_t)batch * scores_stride * 4;
+    // source token of every HIGH and MID destination position, then the
+    // (HIGH, MID) counts of every 2048-token scan chunk
+    return 2 * (int64_t)batch * scores_stride * 4 + (int64_t)batch * tier_chunks(scores_stride) * 8;
 }
 
 int lkv_tier_update(const lkv_cache* src, const lkv_view* src_view, const float* scores, int32_t scores_stride,
@@ -259,15 +261,16 @@ int lkv_tier_update(const lkv_cache* src, const lkv_view* src_view, const float*
     if ((int64_t)workspace_bytes < lkv_tier_workspace_bytes(batch, scores_stride)) return LKV_EINVAL;
     if (batch == 0) return LKV_OK;
     if (!src_view->block_table || !src_view->seq_lens || !scores || !h_block_table || !m_block_table || !n_high ||
-        !n_mid || !tiers || (scores_stride > 0 && !workspace))
+        !n_mid || !tiers || !workspace || (uintptr_t)workspace % 8 != 0)
         return LKV_EINVAL;
     int32_t* h_src = (int32_t*)workspace;
     int32_t* m_src = h_src + (int64_t)batch * scores_stride;
+    int32_t* counts = m_src + (int64_t)batch * scores_stride;
     const hipError_t e = launch_tier_update(
         fs, (const uint8_t*)src->pool, src_view->block_table, src_view->seq_lens, src_view->max_blocks,
         src_view->max_len, scores, scores_stride, tau_low, tau_high, fh, (uint8_t*)dst_h->pool, h_block_table,
         h_max_blocks, fm, (uint8_t*)dst_m->pool, m_block_table, m_max_blocks, n_high, n_mid, tiers, batch, h_src,
-        m_src, (hipStream_t)stream);
+        m_src, counts, (hipStream_t)stream);
     return e == hipSuccess ? LKV_OK : LKV_EHIP;
 }
 

@@ -66,6 +66,9 @@ hipError_t launch_tier_update(const Fmt& fs, const uint8_t* src_pool, const int3
                               const Fmt& fh, uint8_t* h_pool, const int32_t* h_bt, int32_t h_max_blocks,
                               const Fmt& fm, uint8_t* m_pool, const int32_t* m_bt, int32_t m_max_blocks,
                               int32_t* n_high, int32_t* n_mid, uint8_t* tiers, int32_t batch,
-                              int32_t* h_src, int32_t* m_src, hipStream_t stream);
+                              int32_t* h_src, int32_t* m_src, int32_t* counts, hipStream_t stream);
+
+// Scan chunks of a scores row of `stride` tokens (2048 tokens each, at least one).
+inline int32_t tier_chunks(int32_t stride) { return stride > 0 ? (stride + 2047) / 2048 : 1; }
 
 }  // namespace lkv

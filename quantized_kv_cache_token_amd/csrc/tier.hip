@@ -1,10 +1,13 @@
 // tier.hip -- attention-aware tier update (Super KV Compression page, second
 // layer), built with -ffp-contract=off.
 //
-//  classify_scan: one workgroup per sequence.  Tier of each token from its
-//    score (HIGH >= tau_high, MID >= tau_low, LOW otherwise), block-wide
-//    exclusive scans of the HIGH and MID flags (stable order), the source
-//    token index of every destination position, and the two counts.
+//  tier_count: one workgroup per (2048-token chunk, sequence) counts the
+//    chunk's HIGH (score >= tau_high) and MID (tau_low <= score < tau_high)
+//    tokens.
+//  tier_write: the same grid.  Each chunk adds up the counts of the chunks
+//    before it (stable order), scans its own tokens, and writes their tiers
+//    and the source token of every destination position.  The first chunk
+//    writes the two counts (negative when a destination has no room).
 //  compact: one workgroup per (sequence, destination block, KV head,
 //    segment).  It gathers its 64 destination rows: K rows, scales and zeros
 //    copied bit for bit; V6 codes copied (HIGH) or dequantised in fp32 and
@@ -16,54 +19,131 @@
 
 namespace lkv {
 
-__global__ __launch_bounds__(1024) void classify_scan_kernel(
-    const float* __restrict__ scores, int32_t stride, int32_t len_cap, const int32_t* __restrict__ lens,
-    float tau_low, float tau_high, int32_t h_cap, int32_t m_cap, uint8_t* __restrict__ tiers,
-    int32_t* __restrict__ h_src, int32_t* __restrict__ m_src, int32_t* __restrict__ n_high,
-    int32_t* __restrict__ n_mid)
+constexpr int TIER_CHUNK = 2048;  // tokens per scan workgroup: 256 threads x 8
+constexpr int TIER_PER = 8;
+
+__device__ __forceinline__ int tier_of(float s, float tau_low, float tau_high)
 {
-    const int b = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int len = max(0, min(lens[b], len_cap));  // out-of-contract lengths are clamped
-    const int per = (len + 1023) / 1024;
-    const int j0 = min(tid * per, len), j1 = min(j0 + per, len);
-    const float* sc = scores + (int64_t)b * stride;
-    int ch = 0, cm = 0;
-    for (int j = j0; j < j1; j++) {
-        const float s = sc[j];
-        ch += s >= tau_high;
-        cm += (s >= tau_low) & (s < tau_high);
+    return s >= tau_high ? 2 : (s >= tau_low ? 1 : 0);
+}
+
+struct TierScanArgs {
+    const float* scores;
+    int32_t stride;
+    int32_t len_cap;
+    const int32_t* lens;
+    float tau_low, tau_high;
+    int32_t h_cap, m_cap;
+    uint8_t* tiers;
+    int32_t* h_src;
+    int32_t* m_src;
+    int32_t* n_high;
+    int32_t* n_mid;
+    int2* counts;      // [batch][nchunks] (HIGH, MID)
+    int32_t nchunks;
+};
+
+// Tiers of this thread's 8 tokens (3 = past the end), their loads issued
+// together.
+__device__ __forceinline__ void thread_tiers(const TierScanArgs& a, int b, int len, int j0, int (&t)[TIER_PER])
+{
+    const float* sc = a.scores + (int64_t)b * a.stride;
+    float v[TIER_PER];
+#pragma unroll
+    for (int i = 0; i < TIER_PER; i++) v[i] = j0 + i < len ? sc[j0 + i] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < TIER_PER; i++) t[i] = j0 + i < len ? tier_of(v[i], a.tau_low, a.tau_high) : 3;
+}
+
+// Sum over the 256-thread workgroup of (h, m), every thread gets the total.
+__device__ __forceinline__ int2 block_sum2(int h, int m, int2* red)
+{
+    for (int o = 32; o > 0; o >>= 1) {
+        h += __shfl_xor(h, o, 64);
+        m += __shfl_xor(m, o, 64);
     }
-    // exclusive scan of (ch, cm) over the 1024 threads
-    __shared__ int wsum_h[16], wsum_m[16];
-    const int lane = tid & 63, wave = tid >> 6;
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[wave] = make_int2(h, m);
+    __syncthreads();
+    int2 r = make_int2(0, 0);
+#pragma unroll
+    for (int w = 0; w < 4; w++) { r.x += red[w].x; r.y += red[w].y; }
+    return r;
+}
+
+__global__ __launch_bounds__(256) void tier_count_kernel(TierScanArgs a)
+{
+    const int c = blockIdx.x, b = blockIdx.y;
+    const int len = max(0, min(a.lens[b], a.len_cap));  // out-of-contract lengths are clamped
+    const int j0 = c * TIER_CHUNK + TIER_PER * threadIdx.x;
+    int t[TIER_PER];
+    thread_tiers(a, b, len, j0, t);
+    int h = 0, m = 0;
+#pragma unroll
+    for (int i = 0; i < TIER_PER; i++) {
+        h += t[i] == 2;
+        m += t[i] == 1;
+    }
+    __shared__ int2 red[4];
+    const int2 r = block_sum2(h, m, red);
+    if (threadIdx.x == 0) a.counts[(int64_t)b * a.nchunks + c] = r;
+}
+
+__global__ __launch_bounds__(256) void tier_write_kernel(TierScanArgs a)
+{
+    const int c = blockIdx.x, b = blockIdx.y;
+    const int len = max(0, min(a.lens[b], a.len_cap));
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // totals, and the counts of the chunks before this one
+    int th = 0, tm = 0, bh = 0, bm = 0;
+    for (int i = lane; i < a.nchunks; i += 64) {
+        const int2 v = a.counts[(int64_t)b * a.nchunks + i];
+        th += v.x;
+        tm += v.y;
+        if (i < c) { bh += v.x; bm += v.y; }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+        th += __shfl_xor(th, o, 64);
+        tm += __shfl_xor(tm, o, 64);
+        bh += __shfl_xor(bh, o, 64);
+        bm += __shfl_xor(bm, o, 64);
+    }
+    const bool fits = th <= a.h_cap && tm <= a.m_cap;
+    if (c == 0 && tid == 0) {
+        a.n_high[b] = fits ? th : -th;
+        a.n_mid[b] = fits ? tm : -tm;
+    }
+    const int j0 = c * TIER_CHUNK + TIER_PER * tid;
+    int t[TIER_PER];
+    thread_tiers(a, b, len, j0, t);
+    uint8_t* tr = a.tiers + (int64_t)b * a.stride;
+#pragma unroll
+    for (int i = 0; i < TIER_PER; i++)
+        if (t[i] < 3) tr[j0 + i] = (uint8_t)t[i];
+    if (!fits) return;
+    int ch = 0, cm = 0;
+#pragma unroll
+    for (int i = 0; i < TIER_PER; i++) {
+        ch += t[i] == 2;
+        cm += t[i] == 1;
+    }
+    // exclusive scan of (ch, cm) over the workgroup
     int ih = ch, im = cm;
     for (int o = 1; o < 64; o <<= 1) {
-        const int th = __shfl_up(ih, o, 64), tm = __shfl_up(im, o, 64);
-        if (lane >= o) { ih += th; im += tm; }
+        const int uh = __shfl_up(ih, o, 64), um = __shfl_up(im, o, 64);
+        if (lane >= o) { ih += uh; im += um; }
     }
-    if (lane == 63) { wsum_h[wave] = ih; wsum_m[wave] = im; }
+    __shared__ int2 wsum[4];
+    if (lane == 63) wsum[wave] = make_int2(ih, im);
     __syncthreads();
-    int base_h = 0, base_m = 0, tot_h = 0, tot_m = 0;
-    for (int w = 0; w < 16; w++) {
-        if (w < wave) { base_h += wsum_h[w]; base_m += wsum_m[w]; }
-        tot_h += wsum_h[w];
-        tot_m += wsum_m[w];
-    }
-    int ph = base_h + ih - ch, pm = base_m + im - cm;
-    const bool fits = tot_h <= h_cap && tot_m <= m_cap;
-    uint8_t* t = tiers + (int64_t)b * stride;
-    for (int j = j0; j < j1; j++) {
-        const float s = sc[j];
-        const int tier = s >= tau_high ? 2 : (s >= tau_low ? 1 : 0);
-        t[j] = (uint8_t)tier;
-        if (!fits) continue;
-        if (tier == 2) h_src[(int64_t)b * stride + ph++] = j;
-        else if (tier == 1) m_src[(int64_t)b * stride + pm++] = j;
-    }
-    if (tid == 0) {
-        n_high[b] = fits ? tot_h : -tot_h;
-        n_mid[b] = fits ? tot_m : -tot_m;
+    int ph = bh + ih - ch, pm = bm + im - cm;
+    for (int w = 0; w < wave; w++) { ph += wsum[w].x; pm += wsum[w].y; }
+    int32_t* hs = a.h_src + (int64_t)b * a.stride;
+    int32_t* ms = a.m_src + (int64_t)b * a.stride;
+#pragma unroll
+    for (int i = 0; i < TIER_PER; i++) {
+        if (t[i] == 2) hs[ph++] = j0 + i;
+        else if (t[i] == 1) ms[pm++] = j0 + i;
     }
 }
 
@@ -86,6 +166,8 @@ struct CompactArgs {
     int32_t nblk;
 };
 
+constexpr int CU = 4;  // slots a wave keeps in flight
+
 template <int D>
 __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a)
 {
@@ -106,47 +188,82 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a)
     uint8_t* dpool = seg == 0 ? a.h_pool : a.m_pool;
     uint8_t* dch = dpool + ((int64_t)dbt[(int64_t)b * dmax + lb] * fd.H + kvh) * fd.chunk;
 
+    // every slot's source chunk and slot, resolved at once
+    __shared__ const uint8_t* src_ch[BT];
+    __shared__ int src_slot[BT];
+    if (threadIdx.x < cnt) {
+        const int j = idx[threadIdx.x];
+        src_slot[threadIdx.x] = j % BT;
+        src_ch[threadIdx.x] =
+            a.src_pool + ((int64_t)a.src_bt[(int64_t)b * a.src_max_blocks + j / BT] * fs.H + kvh) * fs.chunk;
+    }
+    __syncthreads();
+
     __shared__ uint8_t vc[BT][D];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int s = wave; s < cnt; s += 4) {
-        const int j = idx[s];
-        const int sslot = j % BT;
-        const uint8_t* sch =
-            a.src_pool + ((int64_t)a.src_bt[(int64_t)b * a.src_max_blocks + j / BT] * fs.H + kvh) * fs.chunk;
-        // K row, K scales, K zeros: bit for bit
-        const uint32_t* krow_s = (const uint32_t*)(sch + fs.off_kc + sslot * fs.krow);
-        uint32_t* krow_d = (uint32_t*)(dch + fd.off_kc + s * fd.krow);
-        for (int w = lane; w < fs.krow / 4; w += 64) krow_d[w] = krow_s[w];
-        if (lane < fs.ngroups) {
-            ((float*)(dch + fd.off_ks))[lane * BT + s] = ((const float*)(sch + fs.off_ks))[lane * BT + sslot];
-            dch[fd.off_kz + lane * BT + s] = sch[fs.off_kz + lane * BT + sslot];
-        }
-        if (seg == 0) {
+    const int kw = fs.krow / 4;  // K words per row (<= 64)
+    for (int s0 = wave; s0 < cnt; s0 += 4 * CU) {
+        // loads of CU slots (s0, s0 + 4, ...; past the end: the last slot again)
+        uint32_t kword[CU], vlo[CU][VPL], vhi[CU][VPL];
+        float ks[CU], vs[CU][VPL];
+        uint32_t kz[CU], vz[CU][VPL];
 #pragma unroll
-            for (int i = 0; i < VPL; i++) {
-                const int d = lane + 64 * i;
-                vc[s][d] = (uint8_t)get_field((const uint32_t*)(sch + fs.off_vc + d * fs.vrow), sslot, fs.vb);
-            }
-            if (lane < fs.ngroups) {
-                ((float*)(dch + fd.off_vs))[lane * BT + s] = ((const float*)(sch + fs.off_vs))[lane * BT + sslot];
-                dch[fd.off_vz + lane * BT + s] = sch[fs.off_vz + lane * BT + sslot];
-            }
-        } else {
+        for (int u = 0; u < CU; u++) {
+            const int s = min(s0 + 4 * u, cnt - 1);
+            const uint8_t* sch = src_ch[s];
+            const int sslot = src_slot[s];
+            kword[u] = lane < kw ? ((const uint32_t*)(sch + fs.off_kc + sslot * fs.krow))[lane] : 0u;
+            const int gl = min(lane, fs.ngroups - 1);
+            ks[u] = ((const float*)(sch + fs.off_ks))[gl * BT + sslot];
+            kz[u] = sch[fs.off_kz + gl * BT + sslot];
+            const int bit = sslot * fs.vb;
 #pragma unroll
             for (int i = 0; i < VPL; i++) {
                 const int d = lane + 64 * i;
                 const int gi = d / fs.g;
-                const uint32_t c6 = get_field((const uint32_t*)(sch + fs.off_vc + d * fs.vrow), sslot, fs.vb);
-                const float s6 = ((const float*)(sch + fs.off_vs))[gi * BT + sslot];
-                const int z6 = sch[fs.off_vz + gi * BT + sslot];
-                const float x = (float)((int)c6 - z6) * s6;  // one fp32 rounding
-                float s4;
-                int z4;
-                const int c4 = quantize_lane(x, fd.g, fd.vb, &s4, &z4);
-                vc[s][d] = (uint8_t)c4;
-                if ((d % fd.g) == 0) {
-                    ((float*)(dch + fd.off_vs))[gi * BT + s] = s4;
-                    dch[fd.off_vz + gi * BT + s] = (uint8_t)z4;
+                // the two words that can hold the field (the second may be
+                // the next row's first word: still inside the chunk)
+                const uint32_t* w = (const uint32_t*)(sch + fs.off_vc + d * fs.vrow) + (bit >> 5);
+                vlo[u][i] = w[0];
+                vhi[u][i] = w[1];
+                vs[u][i] = ((const float*)(sch + fs.off_vs))[gi * BT + sslot];
+                vz[u][i] = sch[fs.off_vz + gi * BT + sslot];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < CU; u++) {
+            const int s = s0 + 4 * u;
+            if (s >= cnt) break;
+            const int sslot = src_slot[s];
+            // K row, K scales, K zeros: bit for bit
+            if (lane < kw) ((uint32_t*)(dch + fd.off_kc + s * fd.krow))[lane] = kword[u];
+            if (lane < fs.ngroups) {
+                ((float*)(dch + fd.off_ks))[lane * BT + s] = ks[u];
+                dch[fd.off_kz + lane * BT + s] = (uint8_t)kz[u];
+            }
+            const int sh = (sslot * fs.vb) & 31;
+#pragma unroll
+            for (int i = 0; i < VPL; i++) {
+                const int d = lane + 64 * i;
+                const int gi = d / fs.g;
+                const uint64_t x64 = ((uint64_t)vhi[u][i] << 32) | vlo[u][i];
+                const uint32_t c6 = (uint32_t)(x64 >> sh) & ((1u << fs.vb) - 1u);
+                if (seg == 0) {
+                    vc[s][d] = (uint8_t)c6;
+                    if ((d % fs.g) == 0) {
+                        ((float*)(dch + fd.off_vs))[gi * BT + s] = vs[u][i];
+                        dch[fd.off_vz + gi * BT + s] = (uint8_t)vz[u][i];
+                    }
+                } else {
+                    const float x = (float)((int)c6 - (int)vz[u][i]) * vs[u][i];  // one fp32 rounding
+                    float s4;
+                    int z4;
+                    const int c4 = quantize_lane(x, fd.g, fd.vb, &s4, &z4);
+                    vc[s][d] = (uint8_t)c4;
+                    if ((d % fd.g) == 0) {
+                        ((float*)(dch + fd.off_vs))[gi * BT + s] = s4;
+                        dch[fd.off_vz + gi * BT + s] = (uint8_t)z4;
+                    }
                 }
             }
         }
@@ -166,12 +283,28 @@ hipError_t launch_tier_update(const Fmt& fs, const uint8_t* src_pool, const int3
                               const Fmt& fh, uint8_t* h_pool, const int32_t* h_bt, int32_t h_max_blocks,
                               const Fmt& fm, uint8_t* m_pool, const int32_t* m_bt, int32_t m_max_blocks,
                               int32_t* n_high, int32_t* n_mid, uint8_t* tiers, int32_t batch,
-                              int32_t* h_src, int32_t* m_src, hipStream_t stream)
+                              int32_t* h_src, int32_t* m_src, int32_t* counts, hipStream_t stream)
 {
     if (batch == 0) return hipSuccess;
-    hipLaunchKernelGGL(classify_scan_kernel, dim3((unsigned)batch), dim3(1024), 0, stream, scores, stride,
-                       min(stride, src_max_blocks * BT), src_lens, tau_low, tau_high, h_max_blocks * BT, m_max_blocks * BT, tiers, h_src, m_src,
-                       n_high, n_mid);
+    TierScanArgs t;
+    t.scores = scores;
+    t.stride = stride;
+    t.len_cap = min(stride, src_max_blocks * BT);
+    t.lens = src_lens;
+    t.tau_low = tau_low;
+    t.tau_high = tau_high;
+    t.h_cap = h_max_blocks * BT;
+    t.m_cap = m_max_blocks * BT;
+    t.tiers = tiers;
+    t.h_src = h_src;
+    t.m_src = m_src;
+    t.n_high = n_high;
+    t.n_mid = n_mid;
+    t.counts = (int2*)counts;
+    t.nchunks = tier_chunks(stride);
+    const dim3 sgrid((unsigned)t.nchunks, (unsigned)batch);
+    hipLaunchKernelGGL(tier_count_kernel, sgrid, dim3(256), 0, stream, t);
+    hipLaunchKernelGGL(tier_write_kernel, sgrid, dim3(256), 0, stream, t);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || max_len == 0) return e;
     CompactArgs a;

@@ -123,7 +123,9 @@ def test_tier_update_rejects_bad_formats():
     assert call(m=_cache(v_bits=4, group_size=32)) == lkv.EINVAL
     assert call(stride=512) == lkv.EINVAL                      # scores shorter than max_len
     assert call(ws=100) == lkv.EINVAL
-    assert L.lkv_tier_workspace_bytes(8, 32768) == 2 * 8 * 32768 * 4
+    # two int32 source maps [B][stride], then (HIGH, MID) int32 counts per 2048-token scan chunk
+    assert L.lkv_tier_workspace_bytes(8, 32768) == 2 * 8 * 32768 * 4 + 8 * 16 * 8
+    assert L.lkv_tier_workspace_bytes(2, 300) == 2 * 2 * 300 * 4 + 2 * 1 * 8
 
 
 def test_status_strings():
