@@ -82,6 +82,9 @@ typedef struct lkv_view {
     const int32_t* seq_lens;    /* [batch] int32, live tokens per sequence */
     int32_t max_blocks;
     int32_t max_len;            /* (host) upper bound of seq_lens, sizes the grid */
+    int64_t sum_len;            /* (host) hint: total of seq_lens over the batch,
+                                   or 0 if unknown; only lkv_decode_plan reads it,
+                                   to size splits for ragged batches */
 } lkv_view;
 
 /* Human-readable name of a status. */
@@ -116,7 +119,9 @@ int lkv_quant_append(const lkv_cache* cache, const void* k, const void* v, int32
                      int32_t batch, int32_t max_new, void* stream);
 
 /* Split plan of lkv_decode_attn: a multiple of 64 tokens per split, chosen
- * from the shapes alone (deterministic).  (host) */
+ * from the shapes alone (deterministic).  It aims at about 2048 splits with
+ * work: a sequence is counted at max_len tokens, or, when views carry a
+ * sum_len hint, the batch at sum_len tokens.  (host) */
 int lkv_decode_plan(const lkv_cache* segs, const lkv_view* views, int32_t nseg,
                     int32_t batch, int32_t num_q_heads, int32_t* split_tokens);
 
@@ -150,7 +155,10 @@ int lkv_decode_attn(const lkv_cache* segs, const lkv_view* views, int32_t nseg,
 /* The two stages of lkv_decode_attn, for callers that schedule them apart
  * (lkv_decode_attn is exactly lkv_decode_split followed by
  * lkv_decode_combine on the same stream).  split_tokens must be the
- * resolved (non-zero) split size. */
+ * resolved (non-zero) split size.  lkv_decode_split writes the partial
+ * (o[head_dim], m, L) of every split; a split past its sequence's end writes
+ * only m = -inf and L = 0, and lkv_decode_combine gives it weight 0 without
+ * reading its o row, so the workspace needs no initialisation. */
 int lkv_decode_split(const lkv_cache* segs, const lkv_view* views, int32_t nseg,
                      const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
                      float sm_scale, float tau_low, int32_t split_tokens,

@@ -3,6 +3,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "lkv_internal.h"
@@ -134,11 +135,32 @@ int lkv_decode_plan(const lkv_cache* segs, const lkv_view* views, int32_t nseg, 
     const int st = check_decode(segs, views, nseg, batch, num_q_heads, f);
     if (st != LKV_OK) return st;
     // Aim at about 2048 single-wave work items (8 per compute unit on a
-    // 256-CU part), never fewer than one 64-token block nor more than 64
-    // blocks per split.
-    int64_t blocks = 0;
-    for (int s = 0; s < nseg; s++) blocks += (int64_t)batch * f[0].H * ((views[s].max_len + BT - 1) / BT);
-    int64_t per = (blocks + 2047) / 2048;
+    // 256-CU part, two resident waves per SIMD), never fewer than one
+    // 64-token block nor more than 64 blocks per split.
+    constexpr int64_t ITEMS = 2048;
+    bool hinted = false;
+    for (int s = 0; s < nseg; s++) hinted |= views[s].sum_len > 0;
+    int64_t per = 1;
+    if (!hinted) {
+        // every sequence counted at max_len: equal splits fill the items
+        int64_t blocks = 0;
+        for (int s = 0; s < nseg; s++) blocks += (int64_t)batch * f[0].H * ((views[s].max_len + BT - 1) / BT);
+        per = (blocks + ITEMS - 1) / ITEMS;
+    } else {
+        // a ragged batch: each sequence's last split is partial, so a split
+        // size p gives at most H * (total blocks / p + batch) splits with
+        // work; take the smallest p whose count fits in one round of items
+        for (per = 1; per < 64; per++) {
+            int64_t items = 0;
+            for (int s = 0; s < nseg; s++) {
+                const int64_t dense = (int64_t)batch * ((views[s].max_len + BT - 1) / BT);
+                const int64_t blocks =
+                    views[s].sum_len > 0 ? std::min(dense, (views[s].sum_len + BT - 1) / BT) : dense;
+                items += (int64_t)f[0].H * ((blocks + per - 1) / per + batch);
+            }
+            if (items <= ITEMS) break;
+        }
+    }
     if (per < 1) per = 1;
     if (per > 64) per = 64;
     *split_tokens = (int32_t)(per * BT);
@@ -170,19 +192,25 @@ int lkv_decode_split(const lkv_cache* segs, const lkv_view* views, int32_t nseg,
     if (batch == 0) return LKV_OK;
     if (!q || (need > 0 && !workspace) || (uintptr_t)workspace % 16 != 0) return LKV_EINVAL;
     const int32_t tot = (int32_t)total_splits(views, nseg, split_tokens);
+    SegArgs a[2];
     int32_t base = 0;
     for (int s = 0; s < nseg; s++) {
-        SegArgs a;
-        a.f = f[s];
-        a.pool = (const uint8_t*)segs[s].pool;
-        a.block_table = views[s].block_table;
-        a.seq_lens = views[s].seq_lens;
-        a.max_blocks = views[s].max_blocks;
-        a.n_splits = splits_of(views[s].max_len, split_tokens);
-        a.split_base = base;
-        base += a.n_splits;
-        const hipError_t e = launch_decode_split(a, q, q_dtype, batch, num_q_heads, sm_scale, tau_low, split_tokens,
-                                                 tot, (float*)workspace, (hipStream_t)stream);
+        a[s].f = f[s];
+        a[s].pool = (const uint8_t*)segs[s].pool;
+        a[s].block_table = views[s].block_table;
+        a[s].seq_lens = views[s].seq_lens;
+        a[s].max_blocks = views[s].max_blocks;
+        a[s].n_splits = splits_of(views[s].max_len, split_tokens);
+        a[s].split_base = base;
+        base += a[s].n_splits;
+    }
+    hipError_t e;
+    if (nseg == 2 && launch_decode_split_mfma_tiered(a[0], a[1], q, q_dtype, batch, num_q_heads, sm_scale, tau_low,
+                                                     split_tokens, tot, (float*)workspace, (hipStream_t)stream, &e))
+        return e == hipSuccess ? LKV_OK : LKV_EHIP;
+    for (int s = 0; s < nseg; s++) {
+        e = launch_decode_split(a[s], q, q_dtype, batch, num_q_heads, sm_scale, tau_low, split_tokens, tot,
+                                (float*)workspace, (hipStream_t)stream);
         if (e != hipSuccess) return LKV_EHIP;
     }
     return LKV_OK;
@@ -201,8 +229,12 @@ int lkv_decode_combine(const lkv_cache* segs, const lkv_view* views, int32_t nse
     if ((int64_t)workspace_bytes < need) return LKV_EINVAL;
     if (batch == 0) return LKV_OK;
     if (!out || (need > 0 && !workspace)) return LKV_EINVAL;
-    const hipError_t e = launch_decode_combine(batch, num_q_heads, f[0].D, (int32_t)tot, (const float*)workspace,
-                                               out, (hipStream_t)stream);
+    CombineArgs ca;
+    ca.part = (const float*)workspace;
+    ca.out = out;
+    ca.num_q_heads = num_q_heads;
+    ca.total_splits = (int32_t)tot;
+    const hipError_t e = launch_decode_combine(ca, batch, f[0].D, (hipStream_t)stream);
     return e == hipSuccess ? LKV_OK : LKV_EHIP;
 }
 

@@ -71,6 +71,15 @@ __global__ __launch_bounds__(64) void split_valu_kernel(SplitArgs a)
     const int len = max(0, min(sg.seq_lens[b], sg.max_blocks * BT));  // out-of-contract lengths are clamped
     const int t0 = sp * a.split_tokens;
     const int t1 = min(t0 + a.split_tokens, len);
+    if (t1 <= t0) {  // a split past the end: only (m, L) = (-inf, 0), its o row is never read
+        if (lane < G) {
+            float* p = a.partials +
+                       (((int64_t)b * a.num_q_heads + kvh * G + lane) * a.total_splits + sg.split_base + sp) * (D + 2);
+            p[D] = -INFINITY;
+            p[D + 1] = 0.0f;
+        }
+        return;
+    }
 
     __shared__ float qs[G][D];
     __shared__ float ps[G][BT];
@@ -186,24 +195,26 @@ hipError_t launch_decode_split(const SegArgs& s, const void* q, int q_dtype, int
 
 // Merge of the split partials of one (sequence, query head), m in base 2:
 //   M = max_i m_i,  O = sum_i o_i 2^(m_i - M) / sum_i L_i 2^(m_i - M).
-// One wave per (sequence, query head).  The partial rows of up to 32 splits,
-// their maxima and their sums are loaded together (one memory latency); the
-// weights are computed in the lane that holds each split and broadcast.
+// A split without tokens has m = -inf and an o row that was never written:
+// its weight is 0 and its row is left out by a select (a stale NaN must not
+// reach the sum).  One wave per (sequence, query head).  The partial rows of
+// up to 32 splits, their maxima and their sums are loaded together (one
+// memory latency); the weights are computed in the lane that holds each
+// split and broadcast.
 template <int D>
-__global__ __launch_bounds__(64) void combine_kernel(int32_t total_splits, const float* __restrict__ part,
-                                                     float* __restrict__ out)
+__global__ __launch_bounds__(64) void combine_kernel(CombineArgs a)
 {
     constexpr int VPL = D / 64;
     constexpr int CH = 32;
     const int64_t bh = blockIdx.x;
     const int lane = threadIdx.x;
-    const float* p = part + bh * total_splits * (D + 2);
+    const float* p = a.part + bh * a.total_splits * (D + 2);
     float acc[VPL];
 #pragma unroll
     for (int j = 0; j < VPL; j++) acc[j] = 0.0f;
     float M = -INFINITY, L = 0.0f;
-    for (int i0 = 0; i0 < total_splits; i0 += CH) {
-        const int n = min(CH, total_splits - i0);
+    for (int i0 = 0; i0 < a.total_splits; i0 += CH) {
+        const int n = min(CH, a.total_splits - i0);
         float ov[CH][VPL];
 #pragma unroll
         for (int i = 0; i < CH; i++) {
@@ -223,22 +234,21 @@ __global__ __launch_bounds__(64) void combine_kernel(int32_t total_splits, const
         for (int i = 0; i < CH; i++) {
             const float w = __shfl(wi, i, 64);
 #pragma unroll
-            for (int j = 0; j < VPL; j++) acc[j] += ov[i][j] * w;
+            for (int j = 0; j < VPL; j++) acc[j] += w != 0.0f ? ov[i][j] * w : 0.0f;
         }
         M = m_new;
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
 #pragma unroll
-    for (int j = 0; j < VPL; j++) out[bh * D + lane + 64 * j] = acc[j] * inv;
+    for (int j = 0; j < VPL; j++) a.out[bh * D + lane + 64 * j] = acc[j] * inv;
 }
 
-hipError_t launch_decode_combine(int32_t batch, int32_t num_q_heads, int32_t D, int32_t total_splits,
-                                 const float* partials, float* out, hipStream_t stream)
+hipError_t launch_decode_combine(const CombineArgs& a, int32_t batch, int32_t D, hipStream_t stream)
 {
     if (batch == 0) return hipSuccess;
-    const dim3 grid((unsigned)(batch * num_q_heads));
-    if (D == 64) hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(64), 0, stream, total_splits, partials, out);
-    else hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(64), 0, stream, total_splits, partials, out);
+    const dim3 grid((unsigned)(batch * a.num_q_heads));
+    if (D == 64) hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(64), 0, stream, a);
     return hipGetLastError();
 }
 

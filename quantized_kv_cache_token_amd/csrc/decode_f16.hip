@@ -118,7 +118,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
     const int c = lane & 15, q = lane >> 4;
     const int len = max(0, min(sg.seq_lens[b], sg.max_blocks * BT));
     const int t0 = sp * a.split_tokens;
-    const int t1 = max(t0, min(t0 + a.split_tokens, len));  // empty split: t1 == t0
+    const int t1 = min(t0 + a.split_tokens, len);
+    if (t1 <= t0) {  // a split past the end: only (m, L) = (-inf, 0), its o row is never read
+        if (threadIdx.x < G) {
+            float* p = a.partials + (((int64_t)b * a.num_q_heads + kvh * G + threadIdx.x) * a.total_splits +
+                                     sg.split_base + sp) * (D + 2);
+            p[D] = -INFINITY;
+            p[D + 1] = 0.0f;
+        }
+        return;
+    }
 
     // QK column / P.V row c -> (head hc, part c & 1); with G = 4, columns
     // and rows 8..15 repeat 0..7.
@@ -183,8 +192,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
 
     const int nblk = (t1 - t0 + BT - 1) / BT;
     const int32_t* bt = sg.block_table + (int64_t)b * sg.max_blocks + t0 / BT;
-    // (an empty split reads nothing: its first-block loads go to pool block
-    // 0, which every cache has)
     const int bt_lane = lane < nblk ? bt[lane] : 0;
     const uint8_t* const pool = sg.pool;
     const int64_t chunk = f.chunk;

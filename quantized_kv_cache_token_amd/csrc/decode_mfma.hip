@@ -461,19 +461,29 @@ __device__ __forceinline__ void block_pv(const BlockRegs<VB>& R, const uint8_t* 
     }
 }
 
+// One wave's split: split sp of KV head blockIdx.y of sequence blockIdx.z.
 template <int VB, int G>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void split_mfma_kernel(MfmaArgs a)
+__device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint4* meta_lds)
 {
     static_assert(G == 4 || G == 8, "4 or 8 query heads per KV head");
     constexpr int D = 128;
     const SegArgs& sg = a.seg;
     const Fmt& f = sg.f;
-    const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int kvh = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x;
     const int c = lane & 15, q = lane >> 4;
     const int len = max(0, min(sg.seq_lens[b], sg.max_blocks * BT));
     const int t0 = sp * a.split_tokens;
-    const int t1 = max(t0, min(t0 + a.split_tokens, len));  // empty split: t1 == t0
+    const int t1 = min(t0 + a.split_tokens, len);
+    if (t1 <= t0) {  // a split past the end: only (m, L) = (-inf, 0), its o row is never read
+        if (threadIdx.x < G) {
+            float* p = a.partials + (((int64_t)b * a.num_q_heads + kvh * G + threadIdx.x) * a.total_splits +
+                                     sg.split_base + sp) * (D + 2);
+            p[D] = -INFINITY;
+            p[D + 1] = 0.0f;
+        }
+        return;
+    }
 
     // ---- roles of this lane
     // QK column c -> (head hc, group gc); P.V row c -> (head hc, part c&1,
@@ -526,15 +536,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
 #pragma unroll
     for (int T = 0; T < 8; T++) S.acc[T] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    __shared__ uint4 meta_lds[META_BYTES / 16];
     const uint8_t* lds = (const uint8_t*)meta_lds;
 
     // the split's block-table entries (at most 64), one per lane, so that
     // every chunk address is a register read instead of a memory round trip
     const int nblk = (t1 - t0 + BT - 1) / BT;
     const int32_t* bt = sg.block_table + (int64_t)b * sg.max_blocks + t0 / BT;
-    // (an empty split reads nothing: its first-block loads below go to pool
-    // block 0, which every cache has)
     const int bt_lane = lane < nblk ? bt[lane] : 0;
     // format fields as plain values (kept in scalar registers)
     const uint8_t* const pool = sg.pool;
@@ -606,19 +613,41 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
     }
 }
 
-// Returns true and launches when the format and shape have a matrix-core
-// kernel; false leaves the call to the generic kernel.
-bool launch_decode_split_mfma(const SegArgs& s, const void* q, int q_dtype, int32_t batch, int32_t num_q_heads,
-                              float sm_scale, float tau_low, int32_t split_tokens, int32_t total_splits,
-                              float* partials, hipStream_t stream, hipError_t* err)
+template <int VB, int G>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void split_mfma_kernel(MfmaArgs a)
+{
+    __shared__ uint4 meta_lds[META_BYTES / 16];
+    split_body<VB, G>(a, blockIdx.x, meta_lds);
+}
+
+// Both segments of a tiered cache in one launch: workgroups [0, n0) run the
+// HIGH (V6) segment's splits, the rest the MID (V4) segment's, so the two
+// share the machine instead of running one after the other.
+template <int G>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void split_mfma_tiered_kernel(MfmaArgs a0,
+                                                                                                       MfmaArgs a1)
+{
+    __shared__ uint4 meta_lds[META_BYTES / 16];
+    const int sp = blockIdx.x;
+    if (sp < a0.seg.n_splits) split_body<6, G>(a0, sp, meta_lds);
+    else split_body<4, G>(a1, sp - a0.seg.n_splits, meta_lds);
+}
+
+// Whether a segment has a matrix-core kernel.
+static bool mfma_ok(const SegArgs& s, const void* q, int q_dtype, int32_t num_q_heads, float sm_scale,
+                    int32_t split_tokens)
 {
     const Fmt& f = s.f;
     const int G = num_q_heads / f.H;
-    if (q_dtype != LKV_BF16 || f.D != 128 || f.g != 64 || f.fp16 || f.kb != 6 || (f.vb != 4 && f.vb != 6) ||
-        (G != 4 && G != 8) || ((uintptr_t)q & 15) != 0 ||  // Q is read 16 bytes at a time
-        !(sm_scale > 0.0f))  // the scale is applied after the block maximum
-        return false;
-    if (split_tokens > 64 * BT) return false;  // a split's block-table entries are held one per lane
+    return q_dtype == LKV_BF16 && f.D == 128 && f.g == 64 && !f.fp16 && f.kb == 6 && (f.vb == 4 || f.vb == 6) &&
+           (G == 4 || G == 8) && ((uintptr_t)q & 15) == 0 &&  // Q is read 16 bytes at a time
+           sm_scale > 0.0f &&                                   // the scale is applied after the block maximum
+           split_tokens <= 64 * BT;  // a split's block-table entries are held one per lane
+}
+
+static MfmaArgs mfma_args(const SegArgs& s, const void* q, int32_t num_q_heads, float sm_scale, float tau_low,
+                          int32_t split_tokens, int32_t total_splits, float* partials)
+{
     MfmaArgs a;
     a.seg = s;
     a.q = (const uint16_t*)q;
@@ -628,6 +657,40 @@ bool launch_decode_split_mfma(const SegArgs& s, const void* q, int q_dtype, int3
     a.score_scale = sm_scale * 1.4426950408889634f;
     a.tau_low = tau_low;
     a.partials = partials;
+    return a;
+}
+
+bool launch_decode_split_mfma_tiered(const SegArgs& high, const SegArgs& mid, const void* q, int q_dtype,
+                                     int32_t batch, int32_t num_q_heads, float sm_scale, float tau_low,
+                                     int32_t split_tokens, int32_t total_splits, float* partials,
+                                     hipStream_t stream, hipError_t* err)
+{
+    if (high.f.vb != 6 || mid.f.vb != 4 || high.f.H != mid.f.H ||
+        !mfma_ok(high, q, q_dtype, num_q_heads, sm_scale, split_tokens) ||
+        !mfma_ok(mid, q, q_dtype, num_q_heads, sm_scale, split_tokens))
+        return false;
+    *err = hipSuccess;
+    if (batch == 0 || high.n_splits + mid.n_splits == 0) return true;  // nothing to launch
+    const MfmaArgs a0 = mfma_args(high, q, num_q_heads, sm_scale, tau_low, split_tokens, total_splits, partials);
+    const MfmaArgs a1 = mfma_args(mid, q, num_q_heads, sm_scale, tau_low, split_tokens, total_splits, partials);
+    const int G = num_q_heads / high.f.H;
+    dim3 grid((unsigned)(high.n_splits + mid.n_splits), (unsigned)high.f.H, (unsigned)batch);
+    if (G == 4) hipLaunchKernelGGL(split_mfma_tiered_kernel<4>, grid, dim3(64), 0, stream, a0, a1);
+    else hipLaunchKernelGGL(split_mfma_tiered_kernel<8>, grid, dim3(64), 0, stream, a0, a1);
+    *err = hipGetLastError();
+    return true;
+}
+
+// Returns true and launches when the format and shape have a matrix-core
+// kernel; false leaves the call to the generic kernel.
+bool launch_decode_split_mfma(const SegArgs& s, const void* q, int q_dtype, int32_t batch, int32_t num_q_heads,
+                              float sm_scale, float tau_low, int32_t split_tokens, int32_t total_splits,
+                              float* partials, hipStream_t stream, hipError_t* err)
+{
+    if (!mfma_ok(s, q, q_dtype, num_q_heads, sm_scale, split_tokens)) return false;
+    const Fmt& f = s.f;
+    const int G = num_q_heads / f.H;
+    const MfmaArgs a = mfma_args(s, q, num_q_heads, sm_scale, tau_low, split_tokens, total_splits, partials);
     dim3 grid((unsigned)s.n_splits, (unsigned)f.H, (unsigned)batch);
     if (f.vb == 4 && G == 4) hipLaunchKernelGGL((split_mfma_kernel<4, 4>), grid, dim3(64), 0, stream, a);
     else if (f.vb == 4) hipLaunchKernelGGL((split_mfma_kernel<4, 8>), grid, dim3(64), 0, stream, a);

@@ -51,14 +51,29 @@ bool launch_decode_split_mfma(const SegArgs& s, const void* q, int q_dtype, int3
                               float sm_scale, float tau_low, int32_t split_tokens, int32_t total_splits,
                               float* partials, hipStream_t stream, hipError_t* err);
 
+// Both segments of a tiered cache ({HIGH K6V6, MID K6V4}) in one matrix-core
+// launch; false when either segment has no matrix-core kernel.
+bool launch_decode_split_mfma_tiered(const SegArgs& high, const SegArgs& mid, const void* q, int q_dtype,
+                                     int32_t batch, int32_t num_q_heads, float sm_scale, float tau_low,
+                                     int32_t split_tokens, int32_t total_splits, float* partials,
+                                     hipStream_t stream, hipError_t* err);
+
 // Matrix-core split kernel of the fp16 format: launches and returns true for
 // D 128, bf16 or fp32 Q, G 4 or 8.
 bool launch_decode_split_f16(const SegArgs& s, const void* q, int q_dtype, int32_t batch, int32_t num_q_heads,
                              float sm_scale, float tau_low, int32_t split_tokens, int32_t total_splits,
                              float* partials, hipStream_t stream, hipError_t* err);
 
-hipError_t launch_decode_combine(int32_t batch, int32_t num_q_heads, int32_t D, int32_t total_splits,
-                                 const float* partials, float* out, hipStream_t stream);
+// What the merge reads and writes: partials [B][Hq][total_splits][D + 2]
+// (splits without tokens hold only m = -inf, L = 0), out [B][Hq][D].
+struct CombineArgs {
+    const float* part;
+    float* out;
+    int32_t num_q_heads;
+    int32_t total_splits;
+};
+
+hipError_t launch_decode_combine(const CombineArgs& a, int32_t batch, int32_t D, hipStream_t stream);
 
 hipError_t launch_tier_update(const Fmt& fs, const uint8_t* src_pool, const int32_t* src_bt,
                               const int32_t* src_lens, int32_t src_max_blocks, int32_t max_len,

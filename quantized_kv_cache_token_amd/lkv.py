@@ -36,7 +36,7 @@ class _Cache(C.Structure):
 
 class _View(C.Structure):
     _fields_ = [("block_table", C.c_void_p), ("seq_lens", C.c_void_p), ("max_blocks", C.c_int32),
-                ("max_len", C.c_int32)]
+                ("max_len", C.c_int32), ("sum_len", C.c_int64)]
 
 
 _lib = None
@@ -132,12 +132,13 @@ class View:
     block_table: torch.Tensor   # int32 [B][max_blocks], device
     seq_lens: torch.Tensor      # int32 [B], device
     max_len: int                # host upper bound of seq_lens
+    sum_len: int = 0            # host hint: total of seq_lens (0 = unknown), read by the split plan only
 
     def c(self) -> _View:
         assert self.block_table.dtype == torch.int32 and self.seq_lens.dtype == torch.int32
         assert self.block_table.is_contiguous() and self.seq_lens.is_contiguous()
         return _View(self.block_table.data_ptr(), self.seq_lens.data_ptr(), self.block_table.shape[1],
-                     int(self.max_len))
+                     int(self.max_len), int(self.sum_len))
 
 
 def quant_append(cache: Cache, k: torch.Tensor, v: torch.Tensor, cu_new: torch.Tensor, start_pos: torch.Tensor,

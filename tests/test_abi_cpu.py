@@ -50,8 +50,8 @@ def _cache(pool=0x10000, **kw):
     return lkv._Cache(**d)
 
 
-def _view(max_len=1024, max_blocks=16):
-    return lkv._View(0x20000, 0x30000, max_blocks, max_len)
+def _view(max_len=1024, max_blocks=16, sum_len=0):
+    return lkv._View(0x20000, 0x30000, max_blocks, max_len, sum_len)
 
 
 def test_append_rejects_bad_arguments():
@@ -105,6 +105,22 @@ def test_decode_rejects_bad_arguments_and_plans_deterministically():
     vs1 = (lkv._View * 1)(_view(max_len=256, max_blocks=4))
     cs1 = (lkv._Cache * 1)(_cache(head_dim=64, group_size=32, num_kv_heads=1))
     assert L.lkv_decode_plan(cs1, vs1, 1, 1, 1, C.byref(out)) == lkv.OK and out.value == 64
+
+
+def test_plan_uses_the_total_length_hint_of_a_ragged_batch():
+    """64 ragged sequences, 2 KV heads, max_len 16512: counted at max_len
+    they make 64 x 258 x 2 = 33024 blocks, 17 per work item.  With the
+    batch's total length 557056 (8704 blocks), p blocks per split give at most
+    2 x (ceil(8704 / p) + 64) splits with work; p = 10 is the smallest with at
+    most 2048 (1870).  A hint above the dense count is capped by it: then
+    2 x (ceil(16512 / p) + 64) <= 2048 needs p = 18."""
+    L = lkv.lib()
+    out = C.c_int32()
+    cs = (lkv._Cache * 1)(_cache(num_kv_heads=2, num_blocks=10000))
+    for hint, want in [(0, 17 * 64), (557056, 10 * 64), (10**9, 18 * 64)]:
+        vs = (lkv._View * 1)(_view(max_len=16512, max_blocks=258, sum_len=hint))
+        assert L.lkv_decode_plan(cs, vs, 1, 64, 16, C.byref(out)) == lkv.OK
+        assert out.value == want, (hint, out.value)
 
 
 def test_tier_update_rejects_bad_formats():

@@ -194,6 +194,34 @@ def test_decode_two_segments(fmt):
     assert_attention_close(got, want, vmax, "two segments")
 
 
+@pytest.mark.parametrize("G", [4, 8])
+@pytest.mark.parametrize("tau", [0.0, 1e-5])
+def test_decode_tiered_segments_one_launch(G, tau):
+    """A HIGH (K6V6) and a MID (K6V4) segment, decoded in one matrix-core
+    launch: ragged lengths, a sequence whose HIGH segment is empty, and one
+    whose MID segment is a single token."""
+    D, g, Hkv = 128, 64, 2
+    rng = np.random.default_rng(31)
+    lens_h = [0, 130, 700, 64]
+    lens_m = [900, 1, 2100, 65]
+    pairs, views, ref = [], [], []
+    for fmt_v, lens, seed in ((6, lens_h, 40), (4, lens_m, 41)):
+        bt, nblk = block_tables([max(n, 1) for n in lens], rng)
+        pair = Pair(D, g, 6, fmt_v, Hkv, nblk)
+        _prefill(pair, lens, Hkv, D, "bf16", seed, bt, outliers=True)
+        pairs.append(pair)
+        views.append(lkv.View(torch.tensor(bt).cuda(), torch.tensor(lens, dtype=torch.int32).cuda(), max(lens)))
+        ref.append((bt, np.array(lens, np.int32)))
+    q = inputs.queries(42, len(lens_h), Hkv * G, D)
+    sm = sm_scale(D)
+    split = 256
+    say("decode tiered one launch G", G, "tau", tau)
+    got = lkv.decode_attn([p.gpu for p in pairs], views, q.cuda(), sm, tau, split).cpu().numpy()
+    want = O.decode([p.ref for p in pairs], [r[0] for r in ref], [r[1] for r in ref], to_f32_host(q), sm, tau, split)
+    vmax = max(max_abs_vhat(p.ref) for p in pairs)
+    assert_attention_close(got, want, vmax, f"tiered G{G} tau {tau}")
+
+
 def test_decode_empty_and_degenerate():
     """Zero-length sequences give 0; a single token gives its v_hat."""
     fmt = (128, 64, 6, 4)
