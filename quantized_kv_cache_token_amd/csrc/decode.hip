@@ -197,23 +197,23 @@ hipError_t launch_decode_split(const SegArgs& s, const void* q, int q_dtype, int
 //   M = max_i m_i,  O = sum_i o_i 2^(m_i - M) / sum_i L_i 2^(m_i - M).
 // A split without tokens has m = -inf and an o row that was never written:
 // its weight is 0 and its row is left out by a select (a stale NaN must not
-// reach the sum).  One wave per (sequence, query head).  The partial rows of
-// up to 32 splits, their maxima and their sums are loaded together (one
-// memory latency); the weights are computed in the lane that holds each
-// split and broadcast.
-template <int D>
-__global__ __launch_bounds__(64) void combine_kernel(CombineArgs a)
+// reach the sum).  One workgroup of NW waves per (sequence, query head): wave
+// w merges splits [32 w, 32 w + 32), then [32 (w + NW), ...), loading each
+// chunk's rows, maxima and sums together (one memory latency per chunk); with
+// NW > 1 the running states are then merged through LDS.
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void combine_kernel(CombineArgs a)
 {
     constexpr int VPL = D / 64;
     constexpr int CH = 32;
     const int64_t bh = blockIdx.x;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const float* p = a.part + bh * a.total_splits * (D + 2);
     float acc[VPL];
 #pragma unroll
     for (int j = 0; j < VPL; j++) acc[j] = 0.0f;
     float M = -INFINITY, L = 0.0f;
-    for (int i0 = 0; i0 < a.total_splits; i0 += CH) {
+    for (int i0 = CH * wave; i0 < a.total_splits; i0 += CH * NW) {
         const int n = min(CH, a.total_splits - i0);
         float ov[CH][VPL];
 #pragma unroll
@@ -238,17 +238,54 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a)
         }
         M = m_new;
     }
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    if constexpr (NW == 1) {
+        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
 #pragma unroll
-    for (int j = 0; j < VPL; j++) a.out[bh * D + lane + 64 * j] = acc[j] * inv;
+        for (int j = 0; j < VPL; j++) a.out[bh * D + lane + 64 * j] = acc[j] * inv;
+        return;
+    }
+    // merge the waves' (M, L, acc)
+    __shared__ float sm_m[NW], sm_l[NW];
+    __shared__ float sm_o[NW][D];
+    if (lane == 0) {
+        sm_m[wave] = M;
+        sm_l[wave] = L;
+    }
+#pragma unroll
+    for (int j = 0; j < VPL; j++) sm_o[wave][lane + 64 * j] = acc[j];
+    __syncthreads();
+    if (wave != 0) return;
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; w++) Mt = fmaxf(Mt, sm_m[w]);
+    float Lt = 0.0f, o[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; j++) o[j] = 0.0f;
+    if (Mt != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < NW; w++) {
+            const float ww = sm_m[w] == -INFINITY ? 0.0f : exp2f(sm_m[w] - Mt);
+            Lt += sm_l[w] * ww;
+#pragma unroll
+            for (int j = 0; j < VPL; j++) o[j] += sm_o[w][lane + 64 * j] * ww;
+        }
+    }
+    const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
+#pragma unroll
+    for (int j = 0; j < VPL; j++) a.out[bh * D + lane + 64 * j] = o[j] * inv;
 }
 
 hipError_t launch_decode_combine(const CombineArgs& a, int32_t batch, int32_t D, hipStream_t stream)
 {
     if (batch == 0) return hipSuccess;
     const dim3 grid((unsigned)(batch * a.num_q_heads));
-    if (D == 64) hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(64), 0, stream, a);
+    // one wave takes up to 32 splits in one memory latency; more splits are
+    // spread over four waves
+    const bool one = a.total_splits <= 32;
+    if (D == 64 && one) hipLaunchKernelGGL((combine_kernel<64, 1>), grid, dim3(64), 0, stream, a);
+    else if (D == 64) hipLaunchKernelGGL((combine_kernel<64, 4>), grid, dim3(256), 0, stream, a);
+    else if (one) hipLaunchKernelGGL((combine_kernel<128, 1>), grid, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL((combine_kernel<128, 4>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

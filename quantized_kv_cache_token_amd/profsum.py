@@ -34,11 +34,13 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 PROBE_BYTES = 1 << 30          # the streaming probe reads and writes 1 GiB
 PROBE_REGEX = r"neg_kernel"    # its kernel: an elementwise negation over fp32
-DECODE_SOURCES = ("decode.hip", "decode_mfma.hip", "decode_f16.hip", "wave_util.h")
+# the sources of the split kernel the traffic record describes
+DECODE_SOURCES = ("decode_mfma.hip", "wave_util.h", "lkv_internal.h")
 
 
 def kernel_source_hash() -> str:
-    """Hash of the decode kernel sources (ties a counter summary to them)."""
+    """Hash of the matrix-core split kernel's sources (ties a counter summary
+    to them)."""
     h = hashlib.sha256()
     for name in DECODE_SOURCES:
         path = os.path.join(HERE, "csrc", name)
