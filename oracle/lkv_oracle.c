@@ -358,11 +358,18 @@ static double deq_v(const uint8_t* ch, const fmt_t* f, int slot, int d)
  *     exp(s_j - m) < tau_low * L.
  * Since the final weight of j is at most exp(s_j - m) / L, only tokens whose
  * true softmax weight is under tau_low are skipped.  Skipped tokens stay in
- * the softmax denominator; only their V contribution is dropped. */
+ * the softmax denominator; only their V contribution is dropped.
+ *
+ * Accumulated attention scores (the signal of the attention-aware tiers,
+ * Super KV Compression page, second layer): when score_acc is given, the
+ * softmax weight a_jh = exp(s_jh - M_h) / L_h of every live token j of
+ * segment s, summed over the query heads h of the sequence, is added to
+ * score_acc[s][b][j].  Skipped tokens keep their weight (they stay in the
+ * softmax); the sum over heads runs in head order. */
 int orc_decode(const orc_cache* segs, const orc_view* views, int32_t nseg,
                const float* q, int32_t batch, int32_t num_q_heads,
                float sm_scale, float tau_low, int32_t split_tokens,
-               double* out, uint8_t* skip)
+               double* out, uint8_t* skip, double* score_acc, int32_t acc_stride)
 {
     if (nseg < 1 || nseg > 8 || batch < 0 || num_q_heads <= 0) return -1;
     if (split_tokens < 0 || split_tokens % BT != 0) return -1;
@@ -387,6 +394,17 @@ int orc_decode(const orc_cache* segs, const orc_view* views, int32_t nseg,
                 if (blk < 0 || blk >= segs[s].num_blocks) return -1;
             }
         }
+    }
+    if (score_acc) {
+        for (int s = 0; s < nseg; s++)
+            for (int b = 0; b < batch; b++)
+                if (views[s].seq_lens[b] > acc_stride) return -1;
+    }
+    /* the weights of every (b, h), summed over h after the parallel loop */
+    double* wts = NULL;
+    if (score_acc && batch > 0 && total_cap > 0) {
+        wts = (double*)malloc(sizeof(double) * (size_t)batch * (size_t)num_q_heads * (size_t)total_cap);
+        if (!wts) return -1;
     }
     int fail = 0;
 #pragma omp parallel
@@ -462,12 +480,34 @@ int orc_decode(const orc_cache* segs, const orc_view* views, int32_t nseg,
                 }
                 if (n > 0)
                     for (int d = 0; d < D; d++) o[d] /= L;
+                if (wts) {
+                    double* w = wts + ((int64_t)b * num_q_heads + h) * total_cap;
+                    for (int64_t j = 0; j < n; j++) w[j] = exp(sc[j] - M) / L;
+                }
             }
         }
         free(sc);
         free(kept);
         free(qd);
     }
+    if (wts && !fail) {
+#pragma omp parallel for schedule(dynamic)
+        for (int b = 0; b < batch; b++) {
+            int64_t base = 0;
+            for (int s = 0; s < nseg; s++) {
+                const int32_t len = views[s].seq_lens[b];
+                double* acc = score_acc + ((int64_t)s * batch + b) * acc_stride;
+                for (int32_t j = 0; j < len; j++) {
+                    double sum = 0.0;
+                    for (int h = 0; h < num_q_heads; h++)
+                        sum += wts[((int64_t)b * num_q_heads + h) * total_cap + base + j];
+                    acc[j] += sum;
+                }
+                base += len;
+            }
+        }
+    }
+    free(wts);
     return fail ? -1 : 0;
 }
 

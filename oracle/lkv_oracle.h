@@ -82,11 +82,14 @@ int orc_append(const orc_cache* c, const float* k, const float* v,
  * tau_low <= 0 disables the sparse-V skip.  out: fp64 [batch][Hq][D].
  * skip (optional, may be NULL): uint8 [batch][Hq][nseg][max_tok] where
  * max_tok = max over segments of max_blocks*64; 1 = V term skipped.
+ * score_acc (optional, may be NULL): fp64 [nseg][batch][acc_stride]; the
+ * softmax weight of every live token, summed over the query heads, is added
+ * to it (acc_stride >= every seq_len).
  * Returns 0 or -1 on bad arguments. */
 int orc_decode(const orc_cache* segs, const orc_view* views, int32_t nseg,
                const float* q, int32_t batch, int32_t num_q_heads,
                float sm_scale, float tau_low, int32_t split_tokens,
-               double* out, uint8_t* skip);
+               double* out, uint8_t* skip, double* score_acc, int32_t acc_stride);
 
 /* Tier update.  src: K6V6 cache + view.  scores fp32 [batch][scores_stride].
  * Writes tiers uint8 [batch][scores_stride] (0 low, 1 mid, 2 high; entries

@@ -64,7 +64,7 @@ def lib():
         L.orc_append.restype = C.c_int
         L.orc_decode.argtypes = [C.POINTER(_Cache), C.POINTER(_View), C.c_int32, C.c_void_p,
                                  C.c_int32, C.c_int32, C.c_float, C.c_float, C.c_int32,
-                                 C.c_void_p, C.c_void_p]
+                                 C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32]
         L.orc_decode.restype = C.c_int
         L.orc_tier_update.argtypes = [C.POINTER(_Cache), C.POINTER(_View), C.c_void_p, C.c_int32,
                                       C.c_float, C.c_float,
@@ -183,11 +183,14 @@ def append(cache: Cache, k: np.ndarray, v: np.ndarray, cu_new, start_pos, block_
 
 
 def decode(caches, block_tables, seq_lens, q: np.ndarray, sm_scale: float,
-           tau_low: float = 0.0, split_tokens: int = 0, want_skip: bool = False):
+           tau_low: float = 0.0, split_tokens: int = 0, want_skip: bool = False,
+           score_acc: np.ndarray | None = None):
     """fp64 attention of q (fp32 [B][Hq][D]) over one or more segments.
 
     Returns out (fp64 [B][Hq][D]) and, if want_skip, the skip flags
-    (uint8 [B][Hq][nseg][max_tok])."""
+    (uint8 [B][Hq][nseg][max_tok]).  score_acc (fp64 [nseg][B][stride],
+    C-contiguous) receives, added in place, every live token's softmax weight
+    summed over the query heads."""
     q = np.ascontiguousarray(q, dtype=np.float32)
     B, Hq, D = q.shape
     nseg = len(caches)
@@ -200,8 +203,13 @@ def decode(caches, block_tables, seq_lens, q: np.ndarray, sm_scale: float,
     if want_skip:
         max_tok = max(bt.shape[1] for bt in bts) * BLOCK_TOKENS
         skip = np.zeros((B, Hq, nseg, max_tok), np.uint8)
+    if score_acc is not None:
+        assert score_acc.dtype == np.float64 and score_acc.flags.c_contiguous
+        assert score_acc.ndim == 3 and score_acc.shape[:2] == (nseg, B)
     rc = lib().orc_decode(ccs, views, nseg, _p(q), B, Hq, sm_scale, tau_low, split_tokens,
-                          _p(out), _p(skip) if skip is not None else None)
+                          _p(out), _p(skip) if skip is not None else None,
+                          _p(score_acc) if score_acc is not None else None,
+                          score_acc.shape[2] if score_acc is not None else 0)
     if rc != 0:
         raise ValueError("oracle decode rejected its arguments")
     return (out, skip) if want_skip else out
