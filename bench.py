@@ -147,6 +147,8 @@ def setup_uniform(args, wl, dev) -> Setup:
         S.calls.append((app, spl, comb))
         S.keep += [k, v, q]
     S.keep += [caches, bt, lens, view, cu1, last, ws, out]
+    if not args.fp16_layer:
+        S.secondary["decode_with_scores"] = scores_figure(caches, view, S.keep, B, Hq, Hkv, D, N, sm, split, dev)
     ptk = caches[0].chunk_bytes // 64
     qb = 2 if wl.dtype == "bf16" else 4
     kv = B * Hkv * N * ptk
@@ -164,6 +166,44 @@ def setup_uniform(args, wl, dev) -> Setup:
                                      "us_per_call": round(pre_s * 1e6, 1), "rows_per_call": N - 1,
                                      "counted": "bf16 K/V rows in + packed rows out"}
     return S
+
+
+def scores_figure(caches, view, keep, B, Hq, Hkv, D, N, sm, split, dev):
+    """lkv_decode_attn_scores against lkv_decode_attn over the same layer
+    caches: 32 calls of each, back to back, between one event pair."""
+    import torch
+
+    from quantized_kv_cache_token_amd import lkv
+
+    acc = torch.zeros((1, B, N), dtype=torch.float32, device=dev)
+    out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
+    ws_s = lkv.decode_scores_workspace([caches[0]], [view], B, Hq, split, dev)
+    ws = lkv.decode_workspace([caches[0]], [view], B, Hq, split, dev)
+    qs = [torch.randn(B, Hq, D, device=dev).to(torch.bfloat16) for _ in caches]
+    with_s = [lkv.prepare_decode_scores([c], [view], q, sm, 0.0, split, out, acc, ws_s) for c, q in zip(caches, qs)]
+    plain = []
+    for c, q in zip(caches, qs):
+        spl, comb = lkv.prepare_decode([c], [view], q, sm, 0.0, split, out, ws)
+        plain.append((spl, comb))
+
+    def run(fn):
+        for i in range(8):
+            fn(i)
+        e0, e1 = _event(), _event()
+        e0.record()
+        for i in range(32):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 32 * 1e3
+
+    t_s = run(lambda i: with_s[i % len(with_s)]())
+    t_p = run(lambda i: [f() for f in plain[i % len(plain)]])
+    keep += [acc, out, ws_s, ws, qs, with_s, plain]
+    extra = B * Hq * N * 4 * 2 + B * N * 4 * 2
+    return {"us_per_call": round(t_s, 1), "plain_us_per_call": round(t_p, 1),
+            "extra_bytes_per_call": extra,
+            "counted": "score rows written and read (B x Hq x N fp32) plus the accumulator read and written"}
 
 
 def setup_tiered(args, wl, dev) -> Setup:

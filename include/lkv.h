@@ -167,6 +167,30 @@ int lkv_decode_combine(const lkv_cache* segs, const lkv_view* views, int32_t nse
                        int32_t batch, int32_t num_q_heads, int32_t split_tokens,
                        float* out, const void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes of lkv_decode_attn_scores (host): the decode partials,
+ * then fp32 score rows [batch][num_q_heads][sum over segments of max_len
+ * rounded up to 64], then (M, 1/L) fp32 pairs [batch][num_q_heads], each part
+ * 256-byte aligned. */
+int64_t lkv_decode_scores_workspace_bytes(const lkv_cache* segs, const lkv_view* views, int32_t nseg,
+                                          int32_t batch, int32_t num_q_heads, int32_t split_tokens);
+
+/* lkv_decode_attn that also accumulates attention scores: the per-token
+ * signal of the attention-aware tiers (Super KV Compression page, second
+ * layer).  For every live token j of segment s of sequence b it adds
+ *   score_acc[s][b][j] += sum over query heads h of a_bhj,
+ * a_bhj = exp(s_bhj - M_bh) / L_bh, the token's softmax weight for head h
+ * over all live tokens of all segments (the weights of skipped tokens
+ * included: the skip drops only their V term).  out is exactly what
+ * lkv_decode_attn writes.  score_acc: fp32 [nseg][batch][acc_stride],
+ * acc_stride >= every view's max_len; entries past a sequence's length are
+ * left untouched.  workspace: lkv_decode_scores_workspace_bytes() bytes,
+ * 256-byte aligned.  The cache is only read. */
+int lkv_decode_attn_scores(const lkv_cache* segs, const lkv_view* views, int32_t nseg,
+                           const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+                           float sm_scale, float tau_low, int32_t split_tokens, float* out,
+                           float* score_acc, int32_t acc_stride, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 /* Thresholds from the quantisation error bound (Super KV Compression page,
  * second layer), for n live tokens (host):
  *   tau_low = eps4 / n,  tau_high = (eps4 / eps6) / n,  eps_b = 1/(2(2^b - 1)).

@@ -73,6 +73,26 @@ static int64_t total_splits(const lkv_view* views, int32_t nseg, int32_t split_t
     return n;
 }
 
+static int64_t align256(int64_t n) { return (n + 255) / 256 * 256; }
+
+// Columns of the score rows: every segment's max_len rounded up to 64.
+static int32_t score_cols(const lkv_view* views, int32_t nseg)
+{
+    int32_t n = 0;
+    for (int s = 0; s < nseg; s++) n += (views[s].max_len + BT - 1) / BT * BT;
+    return n;
+}
+
+// Split stage; scores (optional) receives the base-2 score rows.
+static int split_impl(const lkv_cache* segs, const lkv_view* views, int32_t nseg, const void* q, int32_t q_dtype,
+                      int32_t batch, int32_t num_q_heads, float sm_scale, float tau_low, int32_t split_tokens,
+                      void* workspace, size_t workspace_bytes, void* stream, float* scores, int32_t score_stride);
+
+// Merge stage; ml (optional) receives (M, 1 / L) per (sequence, head).
+static int combine_impl(const lkv_cache* segs, const lkv_view* views, int32_t nseg, int32_t batch,
+                        int32_t num_q_heads, int32_t split_tokens, float* out, const void* workspace,
+                        size_t workspace_bytes, void* stream, float* ml);
+
 }  // namespace lkv
 
 using namespace lkv;
@@ -177,9 +197,13 @@ int64_t lkv_decode_workspace_bytes(const lkv_cache* segs, const lkv_view* views,
     return (int64_t)batch * num_q_heads * total_splits(views, nseg, split_tokens) * (f[0].D + 2) * 4;
 }
 
-int lkv_decode_split(const lkv_cache* segs, const lkv_view* views, int32_t nseg, const void* q, int32_t q_dtype,
-                     int32_t batch, int32_t num_q_heads, float sm_scale, float tau_low, int32_t split_tokens,
-                     void* workspace, size_t workspace_bytes, void* stream)
+}  // extern "C"
+
+namespace lkv {
+
+static int split_impl(const lkv_cache* segs, const lkv_view* views, int32_t nseg, const void* q, int32_t q_dtype,
+                      int32_t batch, int32_t num_q_heads, float sm_scale, float tau_low, int32_t split_tokens,
+                      void* workspace, size_t workspace_bytes, void* stream, float* scores, int32_t score_stride)
 {
     Fmt f[2];
     const int st = check_decode(segs, views, nseg, batch, num_q_heads, f);
@@ -203,6 +227,9 @@ int lkv_decode_split(const lkv_cache* segs, const lkv_view* views, int32_t nseg,
         a[s].n_splits = splits_of(views[s].max_len, split_tokens);
         a[s].split_base = base;
         base += a[s].n_splits;
+        a[s].scores = scores;
+        a[s].score_stride = score_stride;
+        a[s].tok_base = s == 0 ? 0 : (views[0].max_len + BT - 1) / BT * BT;
     }
     hipError_t e;
     if (nseg == 2 && launch_decode_split_mfma_tiered(a[0], a[1], q, q_dtype, batch, num_q_heads, sm_scale, tau_low,
@@ -216,9 +243,9 @@ int lkv_decode_split(const lkv_cache* segs, const lkv_view* views, int32_t nseg,
     return LKV_OK;
 }
 
-int lkv_decode_combine(const lkv_cache* segs, const lkv_view* views, int32_t nseg, int32_t batch,
-                       int32_t num_q_heads, int32_t split_tokens, float* out, const void* workspace,
-                       size_t workspace_bytes, void* stream)
+static int combine_impl(const lkv_cache* segs, const lkv_view* views, int32_t nseg, int32_t batch,
+                        int32_t num_q_heads, int32_t split_tokens, float* out, const void* workspace,
+                        size_t workspace_bytes, void* stream, float* ml)
 {
     Fmt f[2];
     const int st = check_decode(segs, views, nseg, batch, num_q_heads, f);
@@ -234,8 +261,81 @@ int lkv_decode_combine(const lkv_cache* segs, const lkv_view* views, int32_t nse
     ca.out = out;
     ca.num_q_heads = num_q_heads;
     ca.total_splits = (int32_t)tot;
+    ca.ml = ml;
     const hipError_t e = launch_decode_combine(ca, batch, f[0].D, (hipStream_t)stream);
     return e == hipSuccess ? LKV_OK : LKV_EHIP;
+}
+
+}  // namespace lkv
+
+extern "C" {
+
+int lkv_decode_split(const lkv_cache* segs, const lkv_view* views, int32_t nseg, const void* q, int32_t q_dtype,
+                     int32_t batch, int32_t num_q_heads, float sm_scale, float tau_low, int32_t split_tokens,
+                     void* workspace, size_t workspace_bytes, void* stream)
+{
+    return split_impl(segs, views, nseg, q, q_dtype, batch, num_q_heads, sm_scale, tau_low, split_tokens, workspace,
+                      workspace_bytes, stream, nullptr, 0);
+}
+
+int lkv_decode_combine(const lkv_cache* segs, const lkv_view* views, int32_t nseg, int32_t batch,
+                       int32_t num_q_heads, int32_t split_tokens, float* out, const void* workspace,
+                       size_t workspace_bytes, void* stream)
+{
+    return combine_impl(segs, views, nseg, batch, num_q_heads, split_tokens, out, workspace, workspace_bytes, stream,
+                        nullptr);
+}
+
+int64_t lkv_decode_scores_workspace_bytes(const lkv_cache* segs, const lkv_view* views, int32_t nseg,
+                                          int32_t batch, int32_t num_q_heads, int32_t split_tokens)
+{
+    const int64_t part = lkv_decode_workspace_bytes(segs, views, nseg, batch, num_q_heads, split_tokens);
+    if (part < 0) return part;
+    return align256(part) + align256((int64_t)batch * num_q_heads * score_cols(views, nseg) * 4) +
+           (int64_t)batch * num_q_heads * 8;
+}
+
+int lkv_decode_attn_scores(const lkv_cache* segs, const lkv_view* views, int32_t nseg, const void* q,
+                           int32_t q_dtype, int32_t batch, int32_t num_q_heads, float sm_scale, float tau_low,
+                           int32_t split_tokens, float* out, float* score_acc, int32_t acc_stride, void* workspace,
+                           size_t workspace_bytes, void* stream)
+{
+    if (split_tokens == 0) {
+        const int st = lkv_decode_plan(segs, views, nseg, batch, num_q_heads, &split_tokens);
+        if (st != LKV_OK) return st;
+    }
+    const int64_t need = lkv_decode_scores_workspace_bytes(segs, views, nseg, batch, num_q_heads, split_tokens);
+    if (need < 0) return (int)need;
+    if ((int64_t)workspace_bytes < need) return LKV_EINVAL;
+    for (int s = 0; s < nseg; s++)
+        if (acc_stride < views[s].max_len) return LKV_EINVAL;
+    if (batch == 0) return LKV_OK;
+    if (!out || !score_acc || !workspace || (uintptr_t)workspace % 256 != 0) return LKV_EINVAL;
+    const int64_t part = align256(lkv_decode_workspace_bytes(segs, views, nseg, batch, num_q_heads, split_tokens));
+    const int32_t cols = score_cols(views, nseg);
+    float* scores = (float*)((uint8_t*)workspace + part);
+    float* ml = (float*)((uint8_t*)workspace + part + align256((int64_t)batch * num_q_heads * cols * 4));
+    int st = split_impl(segs, views, nseg, q, q_dtype, batch, num_q_heads, sm_scale, tau_low, split_tokens,
+                        workspace, (size_t)part, stream, scores, cols);
+    if (st != LKV_OK) return st;
+    st = combine_impl(segs, views, nseg, batch, num_q_heads, split_tokens, out, workspace, (size_t)part, stream, ml);
+    if (st != LKV_OK) return st;
+    ScoreAccArgs sa;
+    sa.scores = scores;
+    sa.score_stride = cols;
+    sa.ml = ml;
+    sa.num_q_heads = num_q_heads;
+    sa.batch = batch;
+    sa.nseg = nseg;
+    for (int s = 0; s < 2; s++) {
+        const bool on = s < nseg;
+        sa.lens[s] = on ? views[s].seq_lens : nullptr;
+        sa.len_cap[s] = on ? views[s].max_blocks * BT : 0;
+        sa.tok_base[s] = s == 0 ? 0 : (views[0].max_len + BT - 1) / BT * BT;
+    }
+    sa.acc = score_acc;
+    sa.acc_stride = acc_stride;
+    return launch_score_accumulate(sa, (hipStream_t)stream) == hipSuccess ? LKV_OK : LKV_EHIP;
 }
 
 int lkv_decode_attn(const lkv_cache* segs, const lkv_view* views, int32_t nseg, const void* q, int32_t q_dtype,

@@ -116,6 +116,8 @@ __global__ __launch_bounds__(64) void split_valu_kernel(SplitArgs a)
 #pragma unroll
         for (int h = 0; h < G; h++) {
             const float sc = live ? s[h] * a.score_scale : -INFINITY;
+            if (sg.scores != nullptr && live)
+                sg.scores[((int64_t)b * a.num_q_heads + kvh * G + h) * sg.score_stride + sg.tok_base + bs + lane] = sc;
             const float m_new = fmaxf(m[h], wave_max(sc));
             const float e = live ? exp2f(sc - m_new) : 0.0f;
             const float alpha = exp2f(m[h] - m_new);
@@ -242,6 +244,10 @@ __global__ __launch_bounds__(64 * NW) void combine_kernel(CombineArgs a)
         const float inv = L > 0.0f ? 1.0f / L : 0.0f;
 #pragma unroll
         for (int j = 0; j < VPL; j++) a.out[bh * D + lane + 64 * j] = acc[j] * inv;
+        if (a.ml != nullptr && lane == 0) {
+            a.ml[2 * bh] = M;
+            a.ml[2 * bh + 1] = inv;
+        }
         return;
     }
     // merge the waves' (M, L, acc)
@@ -273,6 +279,10 @@ __global__ __launch_bounds__(64 * NW) void combine_kernel(CombineArgs a)
     const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
 #pragma unroll
     for (int j = 0; j < VPL; j++) a.out[bh * D + lane + 64 * j] = o[j] * inv;
+    if (a.ml != nullptr && lane == 0) {
+        a.ml[2 * bh] = Mt;
+        a.ml[2 * bh + 1] = inv;
+    }
 }
 
 hipError_t launch_decode_combine(const CombineArgs& a, int32_t batch, int32_t D, hipStream_t stream)
@@ -286,6 +296,44 @@ hipError_t launch_decode_combine(const CombineArgs& a, int32_t batch, int32_t D,
     else if (D == 64) hipLaunchKernelGGL((combine_kernel<64, 4>), grid, dim3(256), 0, stream, a);
     else if (one) hipLaunchKernelGGL((combine_kernel<128, 1>), grid, dim3(64), 0, stream, a);
     else hipLaunchKernelGGL((combine_kernel<128, 4>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+// Accumulated attention scores: one thread per column of the score rows
+// (a token of one segment) adds that token's softmax weight summed over the
+// query heads, 2^(s - M) / L per head with the merged (M, 1 / L) of the head,
+// to acc[segment][b][token].  Columns past a sequence's end were never
+// written and are skipped.
+__global__ __launch_bounds__(256) void score_accumulate_kernel(ScoreAccArgs a)
+{
+    const int b = blockIdx.y;
+    const int col = blockIdx.x * 256 + threadIdx.x;
+    if (col >= a.score_stride) return;
+    const int seg = a.nseg > 1 && col >= a.tok_base[1] ? 1 : 0;
+    const int j = col - a.tok_base[seg];
+    const int len = max(0, min(a.lens[seg][b], a.len_cap[seg]));
+    if (j >= len) return;
+    const float* srow = a.scores + (int64_t)b * a.num_q_heads * a.score_stride + col;
+    const float* ml = a.ml + (int64_t)b * a.num_q_heads * 2;
+    // heads in groups of 4 whose loads are issued together
+    float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    int h = 0;
+    for (; h + 4 <= a.num_q_heads; h += 4) {
+        float x[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) x[u] = srow[(int64_t)(h + u) * a.score_stride];
+#pragma unroll
+        for (int u = 0; u < 4; u++) part[u] += exp2f(x[u] - ml[2 * (h + u)]) * ml[2 * (h + u) + 1];
+    }
+    for (; h < a.num_q_heads; h++) part[0] += exp2f(srow[(int64_t)h * a.score_stride] - ml[2 * h]) * ml[2 * h + 1];
+    a.acc[((int64_t)seg * a.batch + b) * a.acc_stride + j] += (part[0] + part[1]) + (part[2] + part[3]);
+}
+
+hipError_t launch_score_accumulate(const ScoreAccArgs& a, hipStream_t stream)
+{
+    if (a.batch == 0 || a.score_stride == 0) return hipSuccess;
+    const dim3 grid((unsigned)((a.score_stride + 255) / 256), (unsigned)a.batch);
+    hipLaunchKernelGGL(score_accumulate_kernel, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -136,6 +136,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
     const int head = kvh * G + hc;
     // heads of the P.V output rows this lane holds (rows 4q .. 4q+3)
     const int hA = G == 8 ? 2 * q : 2 * (q & 1);
+    // this lane's head's score row, at the split's first token; the part-0
+    // lane of each head stores the scores when the call asks for them
+    float* const srow = sg.scores != nullptr && part == 0 && c < 2 * G
+                            ? sg.scores + ((int64_t)b * a.num_q_heads + head) * sg.score_stride + sg.tok_base + t0
+                            : nullptr;
 
     // ---- Q as the QK B operand: K-step s, K index 8q + i <-> channel 32s + 8q + i
     float x[4][8];
@@ -244,6 +249,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
                 if (nlive < BT) s2 = f16_tok(t, 4 * q + r) < nlive ? s2 : -INFINITY;
                 p[4 * t + r] = s2;
                 bmax = fmaxf(bmax, s2);
+            }
+        }
+        if (srow != nullptr) {
+            // tokens f16_tok(t, 4q) .. + 3 of tile t are consecutive
+            float* dst = srow + (int64_t)k * BT;
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                const int x = f16_tok(t, 4 * q);
+                if (nlive == BT) {
+                    *(float4*)(dst + x) = make_float4(p[4 * t], p[4 * t + 1], p[4 * t + 2], p[4 * t + 3]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; r++)
+                        if (x + r < nlive) dst[x + r] = p[4 * t + r];
+                }
             }
         }
         bmax = rows_max(bmax);

@@ -299,10 +299,13 @@ __device__ __forceinline__ void block_qk(const BlockRegs<VB>& R, const uint32_t 
 // PARTIAL: the block has dead slots past the end (nlive < 64), masked here;
 // full blocks skip that work.  score_scale > 0 is applied after the maximum
 // (the maximum of scaled scores is the scaled maximum), inside the exponent.
+// srow: when non-null, the block's column of this lane's head in the score
+// rows; the lane that owns the head (part 0) stores its 16 tokens' base-2
+// scores there.
 template <int VB, int G, bool PARTIAL>
 __device__ __forceinline__ float block_softmax(const f32x4_t (&dot)[4], const uint8_t* lds, SplitState& S, float qsum,
                                                float score_scale, float tau_low, int nlive, int q, int c,
-                                               float (&p)[16], uint32_t& keep)
+                                               float (&p)[16], uint32_t& keep, float* srow)
 {
     const int gc = c & 1;
     float sk[16];
@@ -325,6 +328,23 @@ __device__ __forceinline__ float block_softmax(const f32x4_t (&dot)[4], const ui
             if constexpr (PARTIAL) s2 = 16 * q + x < nlive ? s2 : -INFINITY;
             sc[4 * t + r] = s2;
             bmax = fmaxf(bmax, s2);
+        }
+    }
+    if (srow != nullptr && (c & 1) == 0 && (G == 8 || c < 8)) {
+        float v[16];  // token 16 q + i of the block
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+#pragma unroll
+            for (int r = 0; r < 4; r++) v[tok_of<VB>(t, r)] = sc[4 * t + r] * score_scale;
+        }
+        float* dst = srow + 16 * q;
+        if constexpr (PARTIAL) {
+#pragma unroll
+            for (int i = 0; i < 16; i++)
+                if (16 * q + i < nlive) dst[i] = v[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; i++) ((float4*)dst)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
         }
     }
     bmax = rows_max(bmax) * score_scale;  // base 2
@@ -494,6 +514,8 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
     const int head = kvh * G + hc;
     // heads of the P.V output rows held by this lane (rows 4q .. 4q+3)
     const int hA = G == 8 ? 2 * q : 2 * (q & 1);
+    // this lane's head's score row, at the split's first token
+    const int64_t srow0 = ((int64_t)b * a.num_q_heads + head) * sg.score_stride + sg.tok_base + t0;
 
     // ---- Q as the QK B operand: this lane group (q) holds channels
     // [32q, 32q + 32), in group q >> 1; zero unless that is the column's group.
@@ -583,8 +605,9 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
         const int nlive = min(BT, t1 - t0 - k * BT);
         float p[16];
         uint32_t keep;
+        float* srow = sg.scores != nullptr ? sg.scores + srow0 + (int64_t)k * BT : nullptr;
         const float alpha =
-            block_softmax<VB, G, PARTIAL>(dot, lds, S, qsum, a.score_scale, a.tau_low, nlive, q, c, p, keep);
+            block_softmax<VB, G, PARTIAL>(dot, lds, S, qsum, a.score_scale, a.tau_low, nlive, q, c, p, keep, srow);
         block_pv<VB, G, PARTIAL>(R, lds, S, p, alpha, keep, q, c, hA, mk);
         load_v<VB>(R, cn, off_vc, c, q);
         asm volatile("" ::: "memory");

@@ -33,6 +33,12 @@ struct SegArgs {
     int32_t max_blocks;
     int32_t n_splits;      // splits of this segment in the grid
     int32_t split_base;    // index of its first split in the partials
+    // optional: every live token's base-2 score per query head, into rows
+    // scores[b * num_q_heads + h][score_stride] from column tok_base
+    // (multiples of 64); null when the call wants no scores
+    float* scores;
+    int32_t score_stride;
+    int32_t tok_base;
 };
 
 hipError_t launch_append(const Fmt& f, uint8_t* pool, const void* k, const void* v, int dtype,
@@ -71,7 +77,26 @@ struct CombineArgs {
     float* out;
     int32_t num_q_heads;
     int32_t total_splits;
+    float* ml;             // optional: (M, 1 / L) of every (sequence, head), base 2
 };
+
+// Accumulated attention scores: for every live token j of segment s of
+// sequence b, acc[s][b][j] += sum_h 2^(score[b][h][tok_base_s + j] - M_bh) / L_bh.
+struct ScoreAccArgs {
+    const float* scores;
+    int32_t score_stride;
+    const float* ml;
+    int32_t num_q_heads;
+    int32_t batch;
+    int32_t nseg;
+    const int32_t* lens[2];
+    int32_t len_cap[2];
+    int32_t tok_base[2];
+    float* acc;
+    int32_t acc_stride;
+};
+
+hipError_t launch_score_accumulate(const ScoreAccArgs& a, hipStream_t stream);
 
 hipError_t launch_decode_combine(const CombineArgs& a, int32_t batch, int32_t D, hipStream_t stream);
 

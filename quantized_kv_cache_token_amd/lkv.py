@@ -43,6 +43,7 @@ _lib = None
 
 EXPORTS = ["lkv_status_string", "lkv_chunk_layout", "lkv_quant_append", "lkv_decode_plan",
            "lkv_decode_workspace_bytes", "lkv_decode_attn", "lkv_decode_split", "lkv_decode_combine",
+           "lkv_decode_scores_workspace_bytes", "lkv_decode_attn_scores",
            "lkv_default_thresholds", "lkv_tier_workspace_bytes", "lkv_tier_update"]
 
 
@@ -65,6 +66,9 @@ def lib():
         "lkv_decode_attn": ([PC, PV, I32, P, I32, I32, I32, F, F, I32, P, P, C.c_size_t, V], C.c_int),
         "lkv_decode_split": ([PC, PV, I32, P, I32, I32, I32, F, F, I32, P, C.c_size_t, V], C.c_int),
         "lkv_decode_combine": ([PC, PV, I32, I32, I32, I32, P, P, C.c_size_t, V], C.c_int),
+        "lkv_decode_scores_workspace_bytes": ([PC, PV, I32, I32, I32, I32], I64),
+        "lkv_decode_attn_scores": ([PC, PV, I32, P, I32, I32, I32, F, F, I32, P, P, I32, P, C.c_size_t, V],
+                                   C.c_int),
         "lkv_default_thresholds": ([I32, C.POINTER(F), C.POINTER(F)], None),
         "lkv_tier_workspace_bytes": ([I32, I32], I64),
         "lkv_tier_update": ([PC, PV, P, I32, F, F, PC, P, I32, PC, P, I32, P, P, P, I32, P, C.c_size_t, V],
@@ -196,6 +200,36 @@ def decode_attn(caches, views, q: torch.Tensor, sm_scale: float, tau_low: float 
     return out
 
 
+def decode_scores_workspace(caches, views, batch, num_q_heads, split_tokens, device="cuda") -> torch.Tensor:
+    cs, vs, n = _segs(caches, views)
+    r = lib().lkv_decode_scores_workspace_bytes(cs, vs, n, batch, num_q_heads, split_tokens)
+    if r < 0:
+        raise LkvError("lkv_decode_scores_workspace_bytes", r)
+    return torch.empty(max(r, 4), dtype=torch.uint8, device=device)
+
+
+def decode_attn_scores(caches, views, q: torch.Tensor, score_acc: torch.Tensor, sm_scale: float,
+                       tau_low: float = 0.0, split_tokens: int = 0, out: torch.Tensor | None = None,
+                       workspace: torch.Tensor | None = None, stream=None):
+    """lkv_decode_attn_scores: decode as decode_attn, and add each live
+    token's softmax weight summed over the query heads to score_acc
+    (fp32 [nseg][B][stride])."""
+    B, Hq, D = q.shape
+    assert q.is_contiguous() and score_acc.is_contiguous() and score_acc.dtype == torch.float32
+    assert score_acc.dim() == 3 and score_acc.shape[:2] == (len(caches), B)
+    if split_tokens == 0:
+        split_tokens = decode_plan(caches, views, B, Hq)
+    if workspace is None:
+        workspace = decode_scores_workspace(caches, views, B, Hq, split_tokens, q.device)
+    if out is None:
+        out = torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
+    cs, vs, n = _segs(caches, views)
+    _check("lkv_decode_attn_scores", lib().lkv_decode_attn_scores(
+        cs, vs, n, _ptr(q), _DTYPE[q.dtype], B, Hq, sm_scale, tau_low, split_tokens, _ptr(out), _ptr(score_acc),
+        score_acc.shape[2], _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
 def decode_split(caches, views, q, sm_scale, tau_low, split_tokens, workspace, stream=None) -> None:
     B, Hq, _ = q.shape
     cs, vs, n = _segs(caches, views)
@@ -262,6 +296,18 @@ def prepare_append(cache: Cache, k, v, cu_new, start_pos, block_table, max_new: 
     return Prepared("lkv_quant_append", C.byref(cc), _ptr(k), _ptr(v), _DTYPE[k.dtype], _ptr(cu_new),
                     _ptr(start_pos), _ptr(block_table), block_table.shape[1], start_pos.shape[0], int(max_new),
                     _stream(stream))
+
+
+def prepare_decode_scores(caches, views, q, sm_scale: float, tau_low: float, split_tokens: int, out, score_acc,
+                          workspace, stream=None) -> Prepared:
+    """lkv_decode_attn_scores as a prepared call."""
+    B, Hq, _ = q.shape
+    cs, vs, n = _segs(caches, views)
+    call = Prepared("lkv_decode_attn_scores", cs, vs, n, _ptr(q), _DTYPE[q.dtype], B, Hq, sm_scale, tau_low,
+                    split_tokens, _ptr(out), _ptr(score_acc), score_acc.shape[2], _ptr(workspace),
+                    workspace.numel() * workspace.element_size(), _stream(stream))
+    call._keep = (cs, vs)
+    return call
 
 
 def prepare_decode(caches, views, q, sm_scale: float, tau_low: float, split_tokens: int, out, workspace,
