@@ -114,3 +114,57 @@ def test_scores_reject_a_short_stride():
     acc = torch.zeros((1, 1, 299), dtype=torch.float32, device="cuda")
     with pytest.raises(lkv.LkvError):
         lkv.decode_attn_scores([pair.gpu], [view], q, acc, sm_scale(D), 0.0, 64)
+
+
+def test_scores_drive_the_tier_update():
+    """The loop the tiers are for: decode with scores for three steps, tier
+    the K6V6 cache on the accumulated scores, decode HIGH + MID.  The oracle
+    tiers from the same fp32 scores: tiers, counts and pools bit-exact, then
+    attention within tolerance."""
+    from tests.gpu_common import assert_attention_close, max_abs_vhat
+
+    D, g, Hkv, G = 128, 64, 2, 4
+    lens = [700, 1300, 64]
+    rng = np.random.default_rng(80)
+    bt, nblk = block_tables(lens, rng)
+    src = Pair(D, g, 6, 6, Hkv, nblk)
+    _prefill(src, lens, Hkv, D, 81, bt)
+    stride = 1408
+    view = lkv.View(torch.tensor(bt).cuda(), torch.tensor(lens, dtype=torch.int32).cuda(), max(lens))
+    acc = torch.zeros((1, len(lens), stride), dtype=torch.float32, device="cuda")
+    want_acc = np.zeros((1, len(lens), stride))
+    say("decode scores, three steps")
+    for step in range(3):
+        q = inputs.queries(82, len(lens), Hkv * G, D, step=step)
+        lkv.decode_attn_scores([src.gpu], [view], q.cuda(), acc, sm_scale(D), 0.0, 256)
+        O.decode([src.ref], [bt], [np.array(lens, np.int32)], to_f32_host(q), sm_scale(D), 0.0, 256,
+                 score_acc=want_acc)
+    torch.cuda.synchronize()
+    assert_scores_close(acc.cpu().numpy(), want_acc, "three steps")
+    # the thresholds bound one head's weight at one step: tier on the mean
+    # weight per head and step (both sides read these same fp32 values)
+    scores = (acc[0] / (3 * Hkv * G)).contiguous()
+    tl, th = lkv.default_thresholds(max(lens))
+    hbt, hn = block_tables(lens, rng)
+    mbt, mn = block_tables(lens, rng)
+    h, m = Pair(D, g, 6, 6, Hkv, hn), Pair(D, g, 6, 4, Hkv, mn)
+    tiers = torch.full((len(lens), stride), 255, dtype=torch.uint8, device="cuda")
+    nh = torch.zeros(len(lens), dtype=torch.int32, device="cuda")
+    nm = torch.zeros_like(nh)
+    say("tier update on decode scores")
+    lkv.tier_update(src.gpu, view, scores, tl, th, h.gpu, torch.tensor(hbt).cuda(), m.gpu, torch.tensor(mbt).cuda(),
+                    nh, nm, tiers)
+    torch.cuda.synchronize()
+    t_ref, nh_ref, nm_ref = O.tier_update(src.ref, bt, np.array(lens, np.int32), scores.cpu().numpy(), tl, th,
+                                          h.ref, hbt, m.ref, mbt)
+    assert np.array_equal(tiers.cpu().numpy(), t_ref)
+    assert np.array_equal(nh.cpu().numpy(), nh_ref) and np.array_equal(nm.cpu().numpy(), nm_ref)
+    assert 0 < int(nh_ref.sum()) < int(nm_ref.sum())  # HIGH and MID both occur
+    assert h.pool_equal() and m.pool_equal()
+    q = inputs.queries(83, len(lens), Hkv * G, D)
+    views = [lkv.View(torch.tensor(hbt).cuda(), nh, int(nh_ref.max())),
+             lkv.View(torch.tensor(mbt).cuda(), nm, int(nm_ref.max()))]
+    say("decode the tiered segments")
+    got = lkv.decode_attn([h.gpu, m.gpu], views, q.cuda(), sm_scale(D), tl, 128).cpu().numpy()
+    want = O.decode([h.ref, m.ref], [hbt, mbt], [nh_ref, nm_ref], to_f32_host(q), sm_scale(D), tl, 128)
+    assert_attention_close(got, want, max(max_abs_vhat(h.ref), max_abs_vhat(m.ref)), "tiered after scores")
