@@ -116,8 +116,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
     const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x;
     const int c = lane & 15, q = lane >> 4;
-    const int len = max(0, min(sg.seq_lens[b], sg.max_blocks * BT));
     const int t0 = sp * a.split_tokens;
+    // the split's block-table entries (at most 64, one per lane) do not
+    // depend on the length: they are requested together with it
+    const int32_t* bt = sg.block_table + (int64_t)b * sg.max_blocks + t0 / BT;
+    const int bt_lane = lane < min(64, sg.max_blocks - t0 / BT) ? bt[lane] : 0;
+    const int len = max(0, min(sg.seq_lens[b], sg.max_blocks * BT));
+    asm volatile("" ::: "memory");  // both loads are issued before either is waited for
     const int t1 = min(t0 + a.split_tokens, len);
     if (t1 <= t0) {  // a split past the end: only (m, L) = (-inf, 0), its o row is never read
         if (threadIdx.x < G) {
@@ -196,8 +201,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
     for (int T = 0; T < 8; T++) acc[T] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     const int nblk = (t1 - t0 + BT - 1) / BT;
-    const int32_t* bt = sg.block_table + (int64_t)b * sg.max_blocks + t0 / BT;
-    const int bt_lane = lane < nblk ? bt[lane] : 0;
     const uint8_t* const pool = sg.pool;
     const int64_t chunk = f.chunk;
     const int H = f.H;

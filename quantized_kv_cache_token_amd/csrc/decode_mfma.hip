@@ -492,8 +492,13 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
     const int kvh = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x;
     const int c = lane & 15, q = lane >> 4;
-    const int len = max(0, min(sg.seq_lens[b], sg.max_blocks * BT));
     const int t0 = sp * a.split_tokens;
+    // the split's block-table entries (at most 64, one per lane) do not
+    // depend on the length: they are requested together with it
+    const int32_t* bt = sg.block_table + (int64_t)b * sg.max_blocks + t0 / BT;
+    const int bt_lane = lane < min(64, sg.max_blocks - t0 / BT) ? bt[lane] : 0;
+    const int len = max(0, min(sg.seq_lens[b], sg.max_blocks * BT));
+    asm volatile("" ::: "memory");  // both loads are issued before either is waited for
     const int t1 = min(t0 + a.split_tokens, len);
     if (t1 <= t0) {  // a split past the end: only (m, L) = (-inf, 0), its o row is never read
         if (threadIdx.x < G) {
@@ -563,8 +568,6 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
     // the split's block-table entries (at most 64), one per lane, so that
     // every chunk address is a register read instead of a memory round trip
     const int nblk = (t1 - t0 + BT - 1) / BT;
-    const int32_t* bt = sg.block_table + (int64_t)b * sg.max_blocks + t0 / BT;
-    const int bt_lane = lane < nblk ? bt[lane] : 0;
     // format fields as plain values (kept in scalar registers)
     const uint8_t* const pool = sg.pool;
     const int64_t chunk = f.chunk;
