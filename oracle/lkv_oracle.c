@@ -608,6 +608,122 @@ int orc_tier_update(const orc_cache* src, const orc_view* src_view,
     return 0;
 }
 
+/* One token of one KV head from a source chunk to a destination chunk: the
+ * K row, K scales and K zeros bit for bit; the V row bit for bit when the
+ * formats match, else (V6 -> V4) dequantised in fp32 and quantised at 4
+ * bits, as the tier update does for MID tokens. */
+static void move_token(const uint8_t* sch, const fmt_t* fs, int sslot, uint8_t* dch, const fmt_t* fd, int dslot)
+{
+    for (int d = 0; d < fs->D; d++) put_k(dch, fd, dslot, d, get_k(sch, fs, sslot, d));
+    for (int gi = 0; gi < fs->ngroups; gi++) {
+        set_scale(dch, fd, 2, gi, dslot, get_scale(sch, fs, 2, gi, sslot));
+        set_zero(dch, fd, 4, gi, dslot, get_zero(sch, fs, 4, gi, sslot));
+    }
+    if (fs->vb == fd->vb) {
+        for (int d = 0; d < fs->D; d++) put_v(dch, fd, dslot, d, get_v(sch, fs, sslot, d));
+        for (int gi = 0; gi < fs->ngroups; gi++) {
+            set_scale(dch, fd, 3, gi, dslot, get_scale(sch, fs, 3, gi, sslot));
+            set_zero(dch, fd, 5, gi, dslot, get_zero(sch, fs, 5, gi, sslot));
+        }
+    } else {
+        float row[1024];
+        for (int d = 0; d < fs->D; d++) {
+            int gi = d / fs->g;
+            row[d] = (float)((int)get_v(sch, fs, sslot, d) - get_zero(sch, fs, 5, gi, sslot)) *
+                     get_scale(sch, fs, 3, gi, sslot);
+        }
+        store_row(dch, fd, dslot, row, 1);
+    }
+}
+
+static int blocks_valid(const orc_view* v, const orc_cache* c, int b, int32_t n)
+{
+    for (int lb = 0; lb < (n + BT - 1) / BT; lb++) {
+        int32_t blk = v->block_table[(int64_t)b * v->max_blocks + lb];
+        if (blk < 0 || blk >= c->num_blocks) return 0;
+    }
+    return 1;
+}
+
+/* Re-tiering of a tiered cache with fresh scores (the periodic form of the
+ * attention-aware tiers, Super KV Compression page, second layer).  The
+ * HIGH segment (K6V6) and the MID segment (K6V4) are rebuilt into new ones:
+ *   HIGH token, score >= tau_high           stays HIGH (copied)
+ *   HIGH token, tau_low <= score < tau_high demoted to MID (V requantised)
+ *   MID token,  score >= tau_low            stays MID (copied; its 6-bit
+ *                                           values are gone, so it is never
+ *                                           promoted)
+ *   any token,  score < tau_low             evicted
+ * New HIGH: HIGH-kept tokens in order.  New MID: MID-kept tokens in order,
+ * then demoted tokens in order.  h_tiers / m_tiers receive the new tier of
+ * every token of each source (2, 1 or 0). */
+int orc_retier(const orc_cache* h, const orc_view* h_view, const float* h_scores, int32_t h_stride,
+               const orc_cache* m, const orc_view* m_view, const float* m_scores, int32_t m_stride,
+               float tau_low, float tau_high,
+               const orc_cache* dst_h, const int32_t* dh_bt, int32_t dh_max_blocks,
+               const orc_cache* dst_m, const int32_t* dm_bt, int32_t dm_max_blocks,
+               int32_t* n_high, int32_t* n_mid, uint8_t* h_tiers, uint8_t* m_tiers, int32_t batch)
+{
+    fmt_t fh, fm, fdh, fdm;
+    if (make_fmt(h, &fh) || make_fmt(m, &fm) || make_fmt(dst_h, &fdh) || make_fmt(dst_m, &fdm)) return -1;
+    if (fh.fp16 || fh.vb != 6 || fm.vb != 4 || fdh.vb != 6 || fdm.vb != 4) return -1;
+    const fmt_t* all[3] = {&fm, &fdh, &fdm};
+    for (int i = 0; i < 3; i++)
+        if (all[i]->D != fh.D || all[i]->g != fh.g || all[i]->H != fh.H || all[i]->kb != fh.kb) return -1;
+    if (batch < 0 || h_stride < 0 || m_stride < 0) return -1;
+    for (int b = 0; b < batch; b++) {
+        const int32_t lh = h_view->seq_lens[b], lm = m_view->seq_lens[b];
+        if (lh < 0 || lh > h_stride || lh > (int64_t)h_view->max_blocks * BT) return -1;
+        if (lm < 0 || lm > m_stride || lm > (int64_t)m_view->max_blocks * BT) return -1;
+        int32_t nh = 0, nm = 0;
+        for (int32_t j = 0; j < lh; j++) {
+            const float sc = h_scores[(int64_t)b * h_stride + j];
+            nh += sc >= tau_high;
+            nm += sc >= tau_low && sc < tau_high;
+        }
+        for (int32_t j = 0; j < lm; j++) nm += m_scores[(int64_t)b * m_stride + j] >= tau_low;
+        if (nh > (int64_t)dh_max_blocks * BT || nm > (int64_t)dm_max_blocks * BT) return -1;
+        const orc_view dh_view = {dh_bt, NULL, dh_max_blocks}, dm_view = {dm_bt, NULL, dm_max_blocks};
+        if (!blocks_valid(h_view, h, b, lh) || !blocks_valid(m_view, m, b, lm) ||
+            !blocks_valid(&dh_view, dst_h, b, nh) || !blocks_valid(&dm_view, dst_m, b, nm))
+            return -1;
+    }
+#pragma omp parallel for schedule(dynamic)
+    for (int b = 0; b < batch; b++) {
+        const int32_t lh = h_view->seq_lens[b], lm = m_view->seq_lens[b];
+        int32_t nh = 0, nm = 0;
+        /* MID-kept tokens first, then the demoted ones */
+        for (int pass = 0; pass < 3; pass++) {
+            const int from_m = pass == 0;
+            const int32_t len = from_m ? lm : lh;
+            for (int32_t j = 0; j < len; j++) {
+                const float sc = from_m ? m_scores[(int64_t)b * m_stride + j] : h_scores[(int64_t)b * h_stride + j];
+                const int tier = from_m ? (sc >= tau_low ? 1 : 0) : (sc >= tau_high ? 2 : (sc >= tau_low ? 1 : 0));
+                if (pass == 0) m_tiers[(int64_t)b * m_stride + j] = (uint8_t)tier;
+                if (pass == 1) h_tiers[(int64_t)b * h_stride + j] = (uint8_t)tier;
+                /* pass 1 places demoted tokens, pass 2 HIGH-kept ones */
+                const int place = pass == 0 ? tier == 1 : (pass == 1 ? tier == 1 : tier == 2);
+                if (!place) continue;
+                const orc_cache* sc_c = from_m ? m : h;
+                const fmt_t* fs = from_m ? &fm : &fh;
+                const orc_view* sv = from_m ? m_view : h_view;
+                const int32_t sblk = sv->block_table[(int64_t)b * sv->max_blocks + j / BT];
+                const int to_h = pass == 2;
+                const int32_t dpos = to_h ? nh++ : nm++;
+                const int32_t dblk = to_h ? dh_bt[(int64_t)b * dh_max_blocks + dpos / BT]
+                                          : dm_bt[(int64_t)b * dm_max_blocks + dpos / BT];
+                for (int kvh = 0; kvh < fh.H; kvh++)
+                    move_token(chunk_ptr(sc_c, fs, sblk, kvh), fs, j % BT,
+                               chunk_ptr(to_h ? dst_h : dst_m, to_h ? &fdh : &fdm, dblk, kvh), to_h ? &fdh : &fdm,
+                               dpos % BT);
+            }
+        }
+        n_high[b] = nh;
+        n_mid[b] = nm;
+    }
+    return 0;
+}
+
 void orc_default_thresholds(int32_t n_tokens, float* tau_low, float* tau_high)
 {
     const double eps4 = 1.0 / (2.0 * 15.0); /* half a 4-bit step, relative to the range */

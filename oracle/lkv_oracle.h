@@ -103,6 +103,22 @@ int orc_tier_update(const orc_cache* src, const orc_view* src_view,
                     const orc_cache* dst_m, const int32_t* m_block_table, int32_t m_max_blocks,
                     int32_t* n_high, int32_t* n_mid, uint8_t* tiers, int32_t batch);
 
+/* Re-tiering of a tiered cache {h: K6V6, m: K6V4} with fresh scores
+ * ([batch][h_stride], [batch][m_stride]) into new segments dst_h (K6V6) and
+ * dst_m (K6V4): HIGH tokens of h with score >= tau_high stay HIGH; tokens of
+ * h with tau_low <= score < tau_high are demoted to MID (V requantised);
+ * tokens of m with score >= tau_low stay MID (never promoted); tokens with
+ * score < tau_low are evicted.  dst_m holds the kept MID tokens first, then
+ * the demoted ones, each in token order.  h_tiers, m_tiers receive the new
+ * tier of every source token; n_high, n_mid the new counts.  Returns 0, or
+ * -1 on bad arguments (including a destination without room). */
+int orc_retier(const orc_cache* h, const orc_view* h_view, const float* h_scores, int32_t h_stride,
+               const orc_cache* m, const orc_view* m_view, const float* m_scores, int32_t m_stride,
+               float tau_low, float tau_high,
+               const orc_cache* dst_h, const int32_t* dh_bt, int32_t dh_max_blocks,
+               const orc_cache* dst_m, const int32_t* dm_bt, int32_t dm_max_blocks,
+               int32_t* n_high, int32_t* n_mid, uint8_t* h_tiers, uint8_t* m_tiers, int32_t batch);
+
 /* Thresholds from the 4-bit and 6-bit quantisation error bounds for n live
  * tokens: tau_low = eps4/n, tau_high = (eps4/eps6)/n, eps_b = 1/(2(2^b-1)). */
 void orc_default_thresholds(int32_t n_tokens, float* tau_low, float* tau_high);

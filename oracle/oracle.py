@@ -72,6 +72,11 @@ def lib():
                                       C.POINTER(_Cache), C.c_void_p, C.c_int32,
                                       C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32]
         L.orc_tier_update.restype = C.c_int
+        L.orc_retier.argtypes = [C.POINTER(_Cache), C.POINTER(_View), C.c_void_p, C.c_int32,
+                                 C.POINTER(_Cache), C.POINTER(_View), C.c_void_p, C.c_int32, C.c_float, C.c_float,
+                                 C.POINTER(_Cache), C.c_void_p, C.c_int32, C.POINTER(_Cache), C.c_void_p, C.c_int32,
+                                 C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32]
+        L.orc_retier.restype = C.c_int
         L.orc_default_thresholds.argtypes = [C.c_int32, C.POINTER(C.c_float), C.POINTER(C.c_float)]
         L.orc_default_thresholds.restype = None
         L.orc_num_threads.argtypes = []
@@ -235,3 +240,28 @@ def tier_update(src: Cache, src_bt, src_lens, scores: np.ndarray, tau_low: float
     if rc != 0:
         raise ValueError("oracle tier update rejected its arguments")
     return tiers, nh, nm
+
+
+def retier(h: Cache, h_bt, h_lens, h_scores: np.ndarray, m: Cache, m_bt, m_lens, m_scores: np.ndarray,
+           tau_low: float, tau_high: float, dst_h: Cache, dh_bt, dst_m: Cache, dm_bt):
+    """Re-tiering of a tiered cache {h: K6V6, m: K6V4} with fresh scores.
+    Returns (h_tiers uint8 [B][h_stride], m_tiers uint8 [B][m_stride],
+    n_high int32 [B], n_mid int32 [B])."""
+    hb, hl, mb, ml = _i32(h_bt), _i32(h_lens), _i32(m_bt), _i32(m_lens)
+    dhb, dmb = _i32(dh_bt), _i32(dm_bt)
+    hs = np.ascontiguousarray(h_scores, dtype=np.float32)
+    ms = np.ascontiguousarray(m_scores, dtype=np.float32)
+    B = hs.shape[0]
+    ht = np.full(hs.shape, 255, np.uint8)
+    mt = np.full(ms.shape, 255, np.uint8)
+    nh = np.zeros(B, np.int32)
+    nm = np.zeros(B, np.int32)
+    ch, cm, cdh, cdm = h.c(), m.c(), dst_h.c(), dst_m.c()
+    hv = _View(hb.ctypes.data, hl.ctypes.data, hb.shape[1])
+    mv = _View(mb.ctypes.data, ml.ctypes.data, mb.shape[1])
+    rc = lib().orc_retier(C.byref(ch), C.byref(hv), _p(hs), hs.shape[1], C.byref(cm), C.byref(mv), _p(ms),
+                          ms.shape[1], tau_low, tau_high, C.byref(cdh), _p(dhb), dhb.shape[1], C.byref(cdm), _p(dmb),
+                          dmb.shape[1], _p(nh), _p(nm), _p(ht), _p(mt), B)
+    if rc != 0:
+        raise ValueError("oracle retier rejected its arguments")
+    return ht, mt, nh, nm
