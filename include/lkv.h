@@ -7,6 +7,8 @@
  *                     packed cache (split over the token axis, then merged)
  *   lkv_tier_update   attention-aware tiers: HIGH keeps 6-bit V, MID gets
  *                     4-bit V, LOW is evicted
+ *   lkv_retier        the same tiers applied again to a tiered cache as its
+ *                     scores change
  * Sources of each operation are cited at its declaration.
  *
  * Conventions for every call:
@@ -225,6 +227,40 @@ int lkv_tier_update(const lkv_cache* src, const lkv_view* src_view,
                     const lkv_cache* dst_m, const int32_t* m_block_table, int32_t m_max_blocks,
                     int32_t* n_high, int32_t* n_mid, uint8_t* tiers, int32_t batch,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of lkv_retier (host): two int32 maps [batch]
+ * [h_stride + m_stride], the (HIGH, MID) int32 counts of every 2048-token
+ * scan chunk of both segments, and two int32 totals per sequence.  8-byte
+ * aligned; its contents need no initialisation. */
+int64_t lkv_retier_workspace_bytes(int32_t batch, int32_t h_stride, int32_t m_stride);
+
+/* Re-tiering of a tiered cache with fresh scores (the attention-aware tiers
+ * applied again as the scores change, Super KV Compression page, second
+ * layer).  h is the HIGH segment (K6/V6 or K4/V6), m the MID segment (same K,
+ * V4), each with its view and its scores ([batch][h_stride],
+ * [batch][m_stride], fp32).  For a HIGH token with score s:
+ *   s >= tau_high             stays HIGH: copied bit for bit into dst_h
+ *   tau_low <= s < tau_high   demoted to MID: K copied, V dequantised in fp32
+ *                             and requantised at 4 bits into dst_m
+ *   s < tau_low               evicted
+ * and for a MID token: s >= tau_low stays MID (copied bit for bit into dst_m;
+ * its 6-bit V is gone, so a MID token is never promoted), else evicted.
+ * dst_h receives the kept HIGH tokens in token order; dst_m the kept MID
+ * tokens in token order, then the demoted tokens in token order, each from
+ * position 0 (block tables dh_block_table, dm_block_table).  h_tiers[b][j]
+ * and m_tiers[b][j] receive each live token's new tier (2, 1 or 0); n_high
+ * and n_mid the new lengths.  If a destination has fewer than the count's
+ * slots, both counts are returned negated and nothing is written to either
+ * destination for that sequence.  The destination blocks must not be blocks
+ * that the sources use (the pools may be the same), and n_high, n_mid must
+ * not be the sources' seq_lens.  Workspace: lkv_retier_workspace_bytes(). */
+int lkv_retier(const lkv_cache* h, const lkv_view* h_view, const float* h_scores, int32_t h_stride,
+               const lkv_cache* m, const lkv_view* m_view, const float* m_scores, int32_t m_stride,
+               float tau_low, float tau_high,
+               const lkv_cache* dst_h, const int32_t* dh_block_table, int32_t dh_max_blocks,
+               const lkv_cache* dst_m, const int32_t* dm_block_table, int32_t dm_max_blocks,
+               int32_t* n_high, int32_t* n_mid, uint8_t* h_tiers, uint8_t* m_tiers, int32_t batch,
+               void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

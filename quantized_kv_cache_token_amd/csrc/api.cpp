@@ -366,10 +366,59 @@ void lkv_default_thresholds(int32_t n_tokens, float* tau_low, float* tau_high)
 int64_t lkv_tier_workspace_bytes(int32_t batch, int32_t scores_stride)
 {
     if (batch < 0 || scores_stride < 0) return LKV_EINVAL;
-    // source token of every HIGH and MID destination position, then the
-    // (HIGH, MID) counts of every 2048-token scan chunk
-    return 2 * (int64_t)batch * scores_stride * 4 + (int64_t)batch * tier_chunks(scores_stride) * 8;
+    return tiering_workspace_bytes(batch, &scores_stride, 1);
 }
+
+int64_t lkv_retier_workspace_bytes(int32_t batch, int32_t h_stride, int32_t m_stride)
+{
+    if (batch < 0 || h_stride < 0 || m_stride < 0) return LKV_EINVAL;
+    const int32_t strides[2] = {m_stride, h_stride};
+    return tiering_workspace_bytes(batch, strides, 2);
+}
+
+}  // extern "C"
+
+namespace {
+
+// A source segment of the tiers: quantised K, vb-bit V, and the shape
+// (D, g, H, K bits) of ref when ref is given.
+int tier_source(const lkv_cache* c, const lkv_view* v, const float* scores, int32_t stride, uint8_t* tiers,
+                int vb, int max_tier, const Fmt* ref, TierSource* out)
+{
+    Fmt f;
+    int st = make_fmt(c, &f);
+    if (st != LKV_OK) return st;
+    if (f.fp16 || f.vb != vb) return ref ? LKV_EINVAL : LKV_EUNSUPPORTED;
+    if (ref && (f.D != ref->D || f.g != ref->g || f.H != ref->H || f.kb != ref->kb)) return LKV_EINVAL;
+    if (!v || stride < 0 || v->max_blocks < 1 || v->max_len < 0 || v->max_len > stride ||
+        (int64_t)v->max_len > (int64_t)v->max_blocks * BT)
+        return LKV_EINVAL;
+    *out = TierSource{f, (const uint8_t*)c->pool, v->block_table, v->seq_lens, v->max_blocks, v->max_len,
+                      scores, stride, tiers, max_tier};
+    return LKV_OK;
+}
+
+int tier_dest(const lkv_cache* c, const int32_t* bt, int32_t max_blocks, int vb, const Fmt& ref, TierDest* out)
+{
+    Fmt f;
+    int st = make_fmt(c, &f);
+    if (st != LKV_OK) return st;
+    if (f.D != ref.D || f.g != ref.g || f.H != ref.H || f.kb != ref.kb || f.vb != vb || max_blocks < 1)
+        return LKV_EINVAL;
+    *out = TierDest{f, (uint8_t*)c->pool, bt, max_blocks};
+    return LKV_OK;
+}
+
+bool sources_ready(const TierSource* s, int n)
+{
+    for (int i = 0; i < n; i++)
+        if (!s[i].block_table || !s[i].view_lens || !s[i].scores || !s[i].tiers) return false;
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
 
 int lkv_tier_update(const lkv_cache* src, const lkv_view* src_view, const float* scores, int32_t scores_stride,
                     float tau_low, float tau_high, const lkv_cache* dst_h, const int32_t* h_block_table,
@@ -377,32 +426,46 @@ int lkv_tier_update(const lkv_cache* src, const lkv_view* src_view, const float*
                     int32_t m_max_blocks, int32_t* n_high, int32_t* n_mid, uint8_t* tiers, int32_t batch,
                     void* workspace, size_t workspace_bytes, void* stream)
 {
-    Fmt fs, fh, fm;
-    int st = make_fmt(src, &fs);
+    TierSource s;
+    TierDest h, m;
+    int st = tier_source(src, src_view, scores, scores_stride, tiers, 6, 2, nullptr, &s);
     if (st != LKV_OK) return st;
-    if ((st = make_fmt(dst_h, &fh)) != LKV_OK) return st;
-    if ((st = make_fmt(dst_m, &fm)) != LKV_OK) return st;
-    if (fs.fp16 || fs.vb != 6) return LKV_EUNSUPPORTED;
-    if (fh.D != fs.D || fh.g != fs.g || fh.H != fs.H || fh.kb != fs.kb || fh.vb != 6) return LKV_EINVAL;
-    if (fm.D != fs.D || fm.g != fs.g || fm.H != fs.H || fm.kb != fs.kb || fm.vb != 4) return LKV_EINVAL;
-    if (!src_view || batch < 0 || scores_stride < 0 || h_max_blocks < 1 || m_max_blocks < 1) return LKV_EINVAL;
-    if (src_view->max_blocks < 1 || src_view->max_len < 0 || src_view->max_len > scores_stride ||
-        (int64_t)src_view->max_len > (int64_t)src_view->max_blocks * BT)
-        return LKV_EINVAL;
-    if (std::isnan(tau_low) || std::isnan(tau_high)) return LKV_EINVAL;
+    if ((st = tier_dest(dst_h, h_block_table, h_max_blocks, 6, s.f, &h)) != LKV_OK) return st;
+    if ((st = tier_dest(dst_m, m_block_table, m_max_blocks, 4, s.f, &m)) != LKV_OK) return st;
+    if (batch < 0 || std::isnan(tau_low) || std::isnan(tau_high)) return LKV_EINVAL;
     if ((int64_t)workspace_bytes < lkv_tier_workspace_bytes(batch, scores_stride)) return LKV_EINVAL;
     if (batch == 0) return LKV_OK;
-    if (!src_view->block_table || !src_view->seq_lens || !scores || !h_block_table || !m_block_table || !n_high ||
-        !n_mid || !tiers || !workspace || (uintptr_t)workspace % 8 != 0)
+    if (!sources_ready(&s, 1) || !h_block_table || !m_block_table || !n_high || !n_mid || !workspace ||
+        (uintptr_t)workspace % 8 != 0)
         return LKV_EINVAL;
-    int32_t* h_src = (int32_t*)workspace;
-    int32_t* m_src = h_src + (int64_t)batch * scores_stride;
-    int32_t* counts = m_src + (int64_t)batch * scores_stride;
-    const hipError_t e = launch_tier_update(
-        fs, (const uint8_t*)src->pool, src_view->block_table, src_view->seq_lens, src_view->max_blocks,
-        src_view->max_len, scores, scores_stride, tau_low, tau_high, fh, (uint8_t*)dst_h->pool, h_block_table,
-        h_max_blocks, fm, (uint8_t*)dst_m->pool, m_block_table, m_max_blocks, n_high, n_mid, tiers, batch, h_src,
-        m_src, counts, (hipStream_t)stream);
+    const hipError_t e = launch_tiering(&s, 1, tau_low, tau_high, h, m, n_high, n_mid, batch, workspace,
+                                        (hipStream_t)stream);
+    return e == hipSuccess ? LKV_OK : LKV_EHIP;
+}
+
+int lkv_retier(const lkv_cache* h, const lkv_view* h_view, const float* h_scores, int32_t h_stride,
+               const lkv_cache* m, const lkv_view* m_view, const float* m_scores, int32_t m_stride,
+               float tau_low, float tau_high, const lkv_cache* dst_h, const int32_t* dh_block_table,
+               int32_t dh_max_blocks, const lkv_cache* dst_m, const int32_t* dm_block_table, int32_t dm_max_blocks,
+               int32_t* n_high, int32_t* n_mid, uint8_t* h_tiers, uint8_t* m_tiers, int32_t batch,
+               void* workspace, size_t workspace_bytes, void* stream)
+{
+    TierSource s[2];  // destination order: the kept MID tokens first
+    TierDest dh, dm;
+    int st = tier_source(h, h_view, h_scores, h_stride, h_tiers, 6, 2, nullptr, &s[1]);
+    if (st != LKV_OK) return st;
+    if ((st = tier_source(m, m_view, m_scores, m_stride, m_tiers, 4, 1, &s[1].f, &s[0])) != LKV_OK) return st;
+    if ((st = tier_dest(dst_h, dh_block_table, dh_max_blocks, 6, s[1].f, &dh)) != LKV_OK) return st;
+    if ((st = tier_dest(dst_m, dm_block_table, dm_max_blocks, 4, s[1].f, &dm)) != LKV_OK) return st;
+    if (batch < 0 || std::isnan(tau_low) || std::isnan(tau_high)) return LKV_EINVAL;
+    const int64_t need = lkv_retier_workspace_bytes(batch, h_stride, m_stride);
+    if (need < 0 || (int64_t)workspace_bytes < need) return LKV_EINVAL;
+    if (batch == 0) return LKV_OK;
+    if (!sources_ready(s, 2) || !dh_block_table || !dm_block_table || !n_high || !n_mid || !workspace ||
+        (uintptr_t)workspace % 8 != 0)
+        return LKV_EINVAL;
+    const hipError_t e = launch_tiering(s, 2, tau_low, tau_high, dh, dm, n_high, n_mid, batch, workspace,
+                                        (hipStream_t)stream);
     return e == hipSuccess ? LKV_OK : LKV_EHIP;
 }
 

@@ -100,15 +100,45 @@ hipError_t launch_score_accumulate(const ScoreAccArgs& a, hipStream_t stream);
 
 hipError_t launch_decode_combine(const CombineArgs& a, int32_t batch, int32_t D, hipStream_t stream);
 
-hipError_t launch_tier_update(const Fmt& fs, const uint8_t* src_pool, const int32_t* src_bt,
-                              const int32_t* src_lens, int32_t src_max_blocks, int32_t max_len,
-                              const float* scores, int32_t stride, float tau_low, float tau_high,
-                              const Fmt& fh, uint8_t* h_pool, const int32_t* h_bt, int32_t h_max_blocks,
-                              const Fmt& fm, uint8_t* m_pool, const int32_t* m_bt, int32_t m_max_blocks,
-                              int32_t* n_high, int32_t* n_mid, uint8_t* tiers, int32_t batch,
-                              int32_t* h_src, int32_t* m_src, int32_t* counts, hipStream_t stream);
+// A source segment of a tier scan and a destination segment.
+struct TierSource {
+    Fmt f;
+    const uint8_t* pool;
+    const int32_t* block_table;
+    const int32_t* view_lens;
+    int32_t max_blocks;
+    int32_t max_len;
+    const float* scores;   // [batch][stride]
+    int32_t stride;
+    uint8_t* tiers;        // [batch][stride]
+    int32_t max_tier;      // 2, or 1 for a MID source (never promoted)
+};
+struct TierDest {
+    Fmt f;
+    uint8_t* pool;
+    const int32_t* block_table;
+    int32_t max_blocks;
+};
+
+// Tier update (one K6V6 source) or re-tiering (sources {MID, HIGH}, in that
+// order).  workspace: tiering_workspace_bytes(), 8-byte aligned.
+hipError_t launch_tiering(const TierSource* src, int nsrc, float tau_low, float tau_high, const TierDest& h,
+                          const TierDest& m, int32_t* n_high, int32_t* n_mid, int32_t batch, void* workspace,
+                          hipStream_t stream);
 
 // Scan chunks of a scores row of `stride` tokens (2048 tokens each, at least one).
 inline int32_t tier_chunks(int32_t stride) { return stride > 0 ? (stride + 2047) / 2048 : 1; }
+
+// Two int32 maps [batch][sum of strides], the (HIGH, MID) counts of every
+// scan chunk of every source, and with two sources source 0's totals.
+inline int64_t tiering_workspace_bytes(int32_t batch, const int32_t* strides, int nsrc)
+{
+    int64_t map = 0, chunks = 0;
+    for (int i = 0; i < nsrc; i++) {
+        map += strides[i];
+        chunks += tier_chunks(strides[i]);
+    }
+    return 2 * (int64_t)batch * map * 4 + (int64_t)batch * chunks * 8 + (nsrc == 2 ? (int64_t)batch * 8 : 0);
+}
 
 }  // namespace lkv

@@ -44,7 +44,8 @@ _lib = None
 EXPORTS = ["lkv_status_string", "lkv_chunk_layout", "lkv_quant_append", "lkv_decode_plan",
            "lkv_decode_workspace_bytes", "lkv_decode_attn", "lkv_decode_split", "lkv_decode_combine",
            "lkv_decode_scores_workspace_bytes", "lkv_decode_attn_scores",
-           "lkv_default_thresholds", "lkv_tier_workspace_bytes", "lkv_tier_update"]
+           "lkv_default_thresholds", "lkv_tier_workspace_bytes", "lkv_tier_update",
+           "lkv_retier_workspace_bytes", "lkv_retier"]
 
 
 def lib():
@@ -73,6 +74,9 @@ def lib():
         "lkv_tier_workspace_bytes": ([I32, I32], I64),
         "lkv_tier_update": ([PC, PV, P, I32, F, F, PC, P, I32, PC, P, I32, P, P, P, I32, P, C.c_size_t, V],
                             C.c_int),
+        "lkv_retier_workspace_bytes": ([I32, I32, I32], I64),
+        "lkv_retier": ([PC, PV, P, I32, PC, PV, P, I32, F, F, PC, P, I32, PC, P, I32, P, P, P, P, I32, P,
+                        C.c_size_t, V], C.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -273,6 +277,35 @@ def tier_update(src: Cache, src_view: View, scores: torch.Tensor, tau_low: float
         h_block_table.shape[1], C.byref(cm), _ptr(m_block_table), m_block_table.shape[1], _ptr(n_high),
         _ptr(n_mid), _ptr(tiers), B, _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+
+
+def retier_workspace_bytes(batch: int, h_stride: int, m_stride: int) -> int:
+    r = lib().lkv_retier_workspace_bytes(batch, h_stride, m_stride)
+    if r < 0:
+        raise LkvError("lkv_retier_workspace_bytes", r)
+    return r
+
+
+def retier(h: Cache, h_view: View, h_scores: torch.Tensor, m: Cache, m_view: View, m_scores: torch.Tensor,
+           tau_low: float, tau_high: float, dst_h: Cache, dh_block_table: torch.Tensor, dst_m: Cache,
+           dm_block_table: torch.Tensor, n_high: torch.Tensor, n_mid: torch.Tensor, h_tiers: torch.Tensor,
+           m_tiers: torch.Tensor, workspace: torch.Tensor | None = None, stream=None) -> None:
+    """lkv_retier: scores fp32 [B][stride] per segment; tiers uint8 of the
+    same shapes."""
+    B, hs = h_scores.shape
+    ms = m_scores.shape[1]
+    assert m_scores.shape[0] == B and h_scores.dtype == torch.float32 and m_scores.dtype == torch.float32
+    assert h_tiers.dtype == torch.uint8 and h_tiers.shape == h_scores.shape
+    assert m_tiers.dtype == torch.uint8 and m_tiers.shape == m_scores.shape
+    if workspace is None:
+        workspace = torch.empty(max(retier_workspace_bytes(B, hs, ms), 8), dtype=torch.uint8,
+                                device=h_scores.device)
+    ch, cm, cdh, cdm, hv, mv = h.c(), m.c(), dst_h.c(), dst_m.c(), h_view.c(), m_view.c()
+    _check("lkv_retier", lib().lkv_retier(
+        C.byref(ch), C.byref(hv), _ptr(h_scores), hs, C.byref(cm), C.byref(mv), _ptr(m_scores), ms, tau_low,
+        tau_high, C.byref(cdh), _ptr(dh_block_table), dh_block_table.shape[1], C.byref(cdm),
+        _ptr(dm_block_table), dm_block_table.shape[1], _ptr(n_high), _ptr(n_mid), _ptr(h_tiers), _ptr(m_tiers), B,
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 class Prepared:

@@ -144,6 +144,30 @@ def test_tier_update_rejects_bad_formats():
     assert L.lkv_tier_workspace_bytes(2, 300) == 2 * 2 * 300 * 4 + 2 * 1 * 8
 
 
+def test_retier_rejects_bad_formats():
+    L = lkv.lib()
+    p = C.c_void_p(0x90000)
+    h, m = _cache(v_bits=6), _cache(v_bits=4)
+    v = _view(max_len=1024)
+
+    def call(h=h, m=m, dh=h, dm=m, hs=1024, ms=1024, ws=1 << 22):
+        return L.lkv_retier(C.byref(h), C.byref(v), p, hs, C.byref(m), C.byref(v), p, ms, 1e-6, 1e-4,
+                            C.byref(dh), p, 16, C.byref(dm), p, 16, p, p, p, p, 8, p, ws, None)
+
+    assert call(h=_cache(v_bits=4)) == lkv.EUNSUPPORTED        # HIGH holds V6
+    assert call(m=_cache(v_bits=6)) == lkv.EINVAL               # MID holds V4
+    assert call(m=_cache(v_bits=4, k_bits=4)) == lkv.EINVAL     # the same K in every segment
+    assert call(dh=_cache(v_bits=4)) == lkv.EINVAL
+    assert call(dm=_cache(v_bits=4, num_kv_heads=2)) == lkv.EINVAL
+    assert call(ms=512) == lkv.EINVAL                           # MID scores shorter than max_len
+    assert call(ws=100) == lkv.EINVAL
+    # two int32 maps [B][h + m strides], (HIGH, MID) counts per 2048-token
+    # chunk of each segment, then two int32 totals per sequence
+    assert L.lkv_retier_workspace_bytes(8, 32768, 4096) == 2 * 8 * 36864 * 4 + 8 * (16 + 2) * 8 + 8 * 8
+    assert L.lkv_retier_workspace_bytes(2, 300, 0) == 2 * 2 * 300 * 4 + 2 * (1 + 1) * 8 + 2 * 8
+    assert L.lkv_retier_workspace_bytes(-1, 1, 1) == lkv.EINVAL
+
+
 def test_status_strings():
     assert lkv.status_string(lkv.OK) == "ok"
     assert "invalid" in lkv.status_string(lkv.EINVAL)

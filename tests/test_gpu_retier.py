@@ -1,0 +1,156 @@
+"""GPU re-tiering of a tiered cache (lkv_retier) against the oracle: tiers,
+counts and destination pools bit-exact, then attention over the new
+segments within max|d| <= 1e-3 max|v_hat| and relative L2 <= 1e-4."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from quantized_kv_cache_token_amd import inputs, lkv
+from tests.gpu_common import Pair, assert_attention_close, max_abs_vhat, say, sm_scale, to_f32_host
+from tests.oracle_cases import block_tables
+
+pytestmark = pytest.mark.gpu
+
+D, g = 128, 64
+
+
+def _dev(a, dtype=torch.int32):
+    return torch.tensor(np.asarray(a), dtype=dtype).cuda()
+
+
+def _segment_scores(base, lens, stride, tl, th, frac_high, frac_mid):
+    s = torch.zeros(len(lens), stride)
+    for b, n in enumerate(lens):
+        s[b, :n] = inputs.tier_scores(base, b, int(n), tl, th, frac_high=frac_high, frac_mid=frac_mid)
+    return s
+
+
+def _tiered(lens, Hkv, seed, rng):
+    """A K6V6 cache tiered once, on the GPU and in the oracle (bit-exact)."""
+    bt, nblk = block_tables([max(n, 1) for n in lens], rng)
+    src = Pair(D, g, 6, 6, Hkv, nblk)
+    K, V = [], []
+    for b, n in enumerate(lens):
+        k, v = inputs.kv_rows(seed, b, int(n), Hkv, D, dtype="bf16")
+        K.append(k)
+        V.append(v)
+    src.append(torch.cat(K), torch.cat(V), np.concatenate([[0], np.cumsum(lens)]).astype(np.int32),
+               np.zeros(len(lens), np.int32), bt)
+    stride = max(lens) + 5
+    tl, th = O.default_thresholds(max(lens))
+    scores = _segment_scores(seed, lens, stride, tl, th, 0.3, 0.4)
+    hbt, hn = block_tables([max(n, 1) for n in lens], rng)
+    mbt, mn = block_tables([max(n, 1) for n in lens], rng)
+    h, m = Pair(D, g, 6, 6, Hkv, hn), Pair(D, g, 6, 4, Hkv, mn)
+    nh = torch.zeros(len(lens), dtype=torch.int32, device="cuda")
+    nm = torch.zeros_like(nh)
+    tiers = torch.zeros((len(lens), stride), dtype=torch.uint8, device="cuda")
+    view = lkv.View(_dev(bt), _dev(lens), max(lens))
+    lkv.tier_update(src.gpu, view, scores.cuda(), tl, th, h.gpu, _dev(hbt), m.gpu, _dev(mbt), nh, nm, tiers)
+    _, nh_ref, nm_ref = O.tier_update(src.ref, bt, np.array(lens, np.int32), scores.numpy(), tl, th, h.ref, hbt,
+                                      m.ref, mbt)
+    assert np.array_equal(nh.cpu().numpy(), nh_ref) and np.array_equal(nm.cpu().numpy(), nm_ref)
+    assert h.pool_equal() and m.pool_equal()
+    return h, hbt, nh_ref, m, mbt, nm_ref, tl, th
+
+
+def _retier_both(h, hbt, nh, m, mbt, nm, tl, th, seed, rng, frac=(0.3, 0.4), boundaries=True, room=None):
+    """Fresh scores per segment, then lkv_retier and the oracle's retier
+    into new destinations.  Returns everything the checks need."""
+    B, Hkv = len(nh), h.gpu.num_kv_heads
+    hs_stride, ms_stride = int(max(nh.max(), 1)) + 3, int(max(nm.max(), 1)) + 7
+    hs = _segment_scores(seed, nh, hs_stride, tl, th, *frac)
+    ms = _segment_scores(seed + 1, nm, ms_stride, tl, th, *frac)
+    if boundaries:  # exact threshold values: equal to tau_low keeps, equal to tau_high is HIGH
+        b = int(np.argmax(nh))
+        if nh[b] >= 2:
+            hs[b, 0], hs[b, 1] = tl, th
+        b = int(np.argmax(nm))
+        if nm[b] >= 2:
+            ms[b, 0], ms[b, 1] = tl, th
+    cap = [max(int(a + c), 1) for a, c in zip(nh, nm)] if room is None else room
+    dhb, dhn = block_tables(cap, rng)
+    dmb, dmn = block_tables(cap, rng)
+    dh, dm = Pair(D, g, 6, 6, Hkv, dhn), Pair(D, g, 6, 4, Hkv, dmn)
+    n_high = torch.zeros(B, dtype=torch.int32, device="cuda")
+    n_mid = torch.zeros_like(n_high)
+    ht = torch.full((B, hs_stride), 255, dtype=torch.uint8, device="cuda")
+    mt = torch.full((B, ms_stride), 255, dtype=torch.uint8, device="cuda")
+    hv = lkv.View(_dev(hbt), _dev(nh), int(nh.max()))
+    mv = lkv.View(_dev(mbt), _dev(nm), int(nm.max()))
+    lkv.retier(h.gpu, hv, hs.cuda(), m.gpu, mv, ms.cuda(), tl, th, dh.gpu, _dev(dhb), dm.gpu, _dev(dmb), n_high,
+               n_mid, ht, mt)
+    torch.cuda.synchronize()
+    ref = O.retier(h.ref, hbt, nh, hs.numpy(), m.ref, mbt, nm, ms.numpy(), tl, th, dh.ref, dhb, dm.ref, dmb) \
+        if room is None else None
+    return dict(hs=hs, ms=ms, dh=dh, dhb=dhb, dm=dm, dmb=dmb, nh=n_high.cpu().numpy(), nm=n_mid.cpu().numpy(),
+                ht=ht.cpu().numpy(), mt=mt.cpu().numpy(), ref=ref)
+
+
+def _check_bit_exact(r):
+    ht, mt, nh, nm = r["ref"]
+    assert np.array_equal(r["nh"], nh) and np.array_equal(r["nm"], nm)
+    assert np.array_equal(r["ht"], ht) and np.array_equal(r["mt"], mt)
+    assert r["dh"].pool_equal(), r["dh"].first_pool_mismatch()
+    assert r["dm"].pool_equal(), r["dm"].first_pool_mismatch()
+
+
+@pytest.mark.parametrize("lens", [[300, 65, 1, 0, 130], [5000, 2600], [64, 2049]], ids=str)
+def test_retier_bit_exact_then_decode(lens):
+    """Tier once, re-tier twice (the second time from the first's output),
+    bit-exact each time; then decode the final segments."""
+    Hkv, G = 2, 4
+    rng = np.random.default_rng(90)
+    say("retier: first tiering", lens)
+    h, hbt, nh, m, mbt, nm, tl, th = _tiered(lens, Hkv, 91, rng)
+    for it in range(2):
+        say("retier", it, "counts", nh.tolist(), nm.tolist())
+        r = _retier_both(h, hbt, nh, m, mbt, nm, tl, th, 92 + 10 * it, rng)
+        _check_bit_exact(r)
+        h, hbt, nh, m, mbt, nm = r["dh"], r["dhb"], r["nh"], r["dm"], r["dmb"], r["nm"]
+    q = inputs.queries(95, len(lens), Hkv * G, D)
+    views = [lkv.View(_dev(hbt), _dev(nh), int(max(nh.max(), 0))), lkv.View(_dev(mbt), _dev(nm), int(nm.max()))]
+    say("decode the re-tiered segments")
+    got = lkv.decode_attn([h.gpu, m.gpu], views, q.cuda(), sm_scale(D), tl, 128).cpu().numpy()
+    want = O.decode([h.ref, m.ref], [hbt, mbt], [nh, nm], to_f32_host(q), sm_scale(D), tl, 128)
+    assert_attention_close(got, want, max(max_abs_vhat(h.ref), max_abs_vhat(m.ref)), f"retiered {lens}")
+
+
+def test_retier_all_evicted_and_all_kept():
+    """Every token evicted gives empty segments; every token above tau_high
+    keeps HIGH as HIGH and MID as MID (no promotion)."""
+    Hkv = 1
+    rng = np.random.default_rng(96)
+    h, hbt, nh, m, mbt, nm, tl, th = _tiered([700, 200], Hkv, 97, rng)
+    say("retier all evicted")
+    r = _retier_both(h, hbt, nh, m, mbt, nm, tl, th, 98, rng, frac=(0.0, 0.0), boundaries=False)
+    _check_bit_exact(r)
+    assert np.all(r["nh"] == 0) and np.all(r["nm"] == 0)
+    say("retier all kept")
+    r = _retier_both(h, hbt, nh, m, mbt, nm, tl, th, 99, rng, frac=(1.0, 0.0), boundaries=False)
+    _check_bit_exact(r)
+    assert np.array_equal(r["nh"], nh) and np.array_equal(r["nm"], nm)
+
+
+def test_retier_without_room_writes_nothing():
+    Hkv = 1
+    rng = np.random.default_rng(100)
+    h, hbt, nh, m, mbt, nm, tl, th = _tiered([600, 60], Hkv, 101, rng)
+    say("retier without room")
+    # one destination block per sequence: the longer sequence keeps more
+    # than 64 MID tokens, the shorter one fits
+    r = _retier_both(h, hbt, nh, m, mbt, nm, tl, th, 102, rng, frac=(0.0, 0.5), boundaries=False,
+                     room=[64, 64])
+    hs, ms = r["hs"].numpy(), r["ms"].numpy()
+    want_h = [(hs[b, :nh[b]] >= th).sum() for b in range(2)]
+    want_m = [(ms[b, :nm[b]] >= tl).sum() + ((hs[b, :nh[b]] >= tl) & (hs[b, :nh[b]] < th)).sum() for b in range(2)]
+    for b in range(2):
+        fits = want_h[b] <= 64 and want_m[b] <= 64
+        sign = 1 if fits else -1
+        assert r["nh"][b] == sign * want_h[b] and r["nm"][b] == sign * want_m[b], (b, want_h, want_m)
+    assert r["nm"][0] < 0 and r["nm"][1] > 0
+    # nothing written for sequence 0: its destination blocks are still zero
+    for pair, bt in ((r["dh"], r["dhb"]), (r["dm"], r["dmb"])):
+        pool = pair.gpu.pool.cpu().numpy().reshape(-1, Hkv * pair.ref.chunk_bytes)
+        assert not pool[int(bt[0, 0])].any()

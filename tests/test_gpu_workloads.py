@@ -100,7 +100,8 @@ def test_workload2_llama8b_32k_sampled():
 @pytest.mark.timeout(900)
 def test_workload3_tiered_sampled():
     """K6V6 cache, tier update with the error-bound thresholds, decode over
-    the HIGH (K6V6) and MID (K6V4) segments with the sparse-V skip."""
+    the HIGH (K6V6) and MID (K6V4) segments with the sparse-V skip, then a
+    re-tiering of those segments with fresh scores."""
     wl = workloads.LLAMA8B_32K_TIERED
     B, Hq, Hkv, D, N = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.n_ctx
     nb = N // BT
@@ -128,6 +129,22 @@ def test_workload3_tiered_sampled():
     out = lkv.decode_attn([hdst, mdst], views, q.cuda(), sm_scale(D), tl, split).cpu().numpy()
     torch.cuda.synchronize()
     t_all = tiers.cpu().numpy()
+    # re-tiering with fresh scores into new segments
+    hs = torch.zeros(B, N)
+    ms = torch.zeros(B, N)
+    for b in range(B):
+        hs[b, :nh_h[b]] = inputs.tier_scores(wl.seed + 1, b, int(nh_h[b]), tl, th)
+        ms[b, :nm_h[b]] = inputs.tier_scores(wl.seed + 2, b, int(nm_h[b]), tl, th)
+    h2 = lkv.Cache(D, wl.group_size, 6, 6, Hkv, B * nb)
+    m2 = lkv.Cache(D, wl.group_size, 6, 4, Hkv, B * nb)
+    nh2, nm2 = torch.zeros_like(nh), torch.zeros_like(nh)
+    ht2 = torch.zeros((B, N), dtype=torch.uint8, device="cuda")
+    mt2 = torch.zeros((B, N), dtype=torch.uint8, device="cuda")
+    say("workload 3 retier")
+    lkv.retier(hdst, views[0], hs.cuda(), mdst, views[1], ms.cuda(), tl, th, h2, hbt.cuda(), m2, hbt.cuda(), nh2, nm2,
+               ht2, mt2)
+    torch.cuda.synchronize()
+    nh2_h, nm2_h, ht2_h, mt2_h = nh2.cpu().numpy(), nm2.cpu().numpy(), ht2.cpu().numpy(), mt2.cpu().numpy()
     for b in (1, 6):
         say("workload 3 oracle, sequence", b)
         ref = O.Cache(D, wl.group_size, 6, 6, Hkv, nb)
@@ -142,6 +159,14 @@ def test_workload3_tiered_sampled():
         _chunks_equal(mdst.pool, hbt[b].numpy(), rm, rbt[0], int(nm_h[b]), Hkv)
         want = O.decode([rh, rm], [rbt, rbt], [nh_ref, nm_ref], q[b:b + 1].float().numpy(), sm_scale(D), tl, split)
         assert_attention_close(out[b:b + 1], want, max(max_abs_vhat(rh), max_abs_vhat(rm)), f"workload 3 seq {b}")
+        say("workload 3 oracle retier, sequence", b)
+        rh2, rm2 = O.Cache(D, wl.group_size, 6, 6, Hkv, nb), O.Cache(D, wl.group_size, 6, 4, Hkv, nb)
+        ht_ref, mt_ref, nh2_ref, nm2_ref = O.retier(rh, rbt, nh_ref, hs[b:b + 1, :nh_ref[0]].numpy(), rm, rbt, nm_ref,
+                                                    ms[b:b + 1, :nm_ref[0]].numpy(), tl, th, rh2, rbt, rm2, rbt)
+        assert nh2_h[b] == nh2_ref[0] and nm2_h[b] == nm2_ref[0]
+        assert np.array_equal(ht2_h[b, :nh_ref[0]], ht_ref[0]) and np.array_equal(mt2_h[b, :nm_ref[0]], mt_ref[0])
+        _chunks_equal(h2.pool, hbt[b].numpy(), rh2, rbt[0], int(nh2_h[b]), Hkv)
+        _chunks_equal(m2.pool, hbt[b].numpy(), rm2, rbt[0], int(nm2_h[b]), Hkv)
 
 
 @pytest.mark.timeout(900)
