@@ -200,10 +200,12 @@ int lkv_decode_attn_scores(const lkv_cache* segs, const lkv_view* views, int32_t
  * eps4 * max|v|, the 4-bit half-step relative to a group's range. */
 void lkv_default_thresholds(int32_t n_tokens, float* tau_low, float* tau_high);
 
-/* Workspace bytes of lkv_tier_update (host): two int32 maps [batch]
- * [scores_stride] (source token of each HIGH / MID destination position),
- * then (HIGH, MID) int32 counts per 2048-token scan chunk of each sequence.
- * The workspace must be 8-byte aligned; its contents need no initialisation. */
+/* Workspace bytes of lkv_tier_update (host): (HIGH, MID) int32 counts per
+ * 2048-token scan chunk of each sequence, then the (HIGH, MID) destination
+ * positions of every 64-token block of each sequence:
+ * batch * (ceil(scores_stride / 2048) + ceil(scores_stride / 64)) * 8 bytes
+ * (each ceil at least 1).  The workspace must be 8-byte aligned; its contents
+ * need no initialisation. */
 int64_t lkv_tier_workspace_bytes(int32_t batch, int32_t scores_stride);
 
 /* Attention-aware tier update (Super KV Compression page, second layer).
@@ -228,10 +230,12 @@ int lkv_tier_update(const lkv_cache* src, const lkv_view* src_view,
                     int32_t* n_high, int32_t* n_mid, uint8_t* tiers, int32_t batch,
                     void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes of lkv_retier (host): two int32 maps [batch]
- * [h_stride + m_stride], the (HIGH, MID) int32 counts of every 2048-token
- * scan chunk of both segments, and two int32 totals per sequence.  8-byte
- * aligned; its contents need no initialisation. */
+/* Workspace bytes of lkv_retier (host): the (HIGH, MID) int32 counts of
+ * every 2048-token scan chunk and the (HIGH, MID) destination positions of
+ * every 64-token block, of both segments:
+ * batch * (ceil(h_stride / 2048) + ceil(m_stride / 2048) + ceil(h_stride / 64)
+ * + ceil(m_stride / 64)) * 8 bytes (each ceil at least 1).  8-byte aligned;
+ * its contents need no initialisation. */
 int64_t lkv_retier_workspace_bytes(int32_t batch, int32_t h_stride, int32_t m_stride);
 
 /* Re-tiering of a tiered cache with fresh scores (the attention-aware tiers

@@ -129,16 +129,20 @@ hipError_t launch_tiering(const TierSource* src, int nsrc, float tau_low, float 
 // Scan chunks of a scores row of `stride` tokens (2048 tokens each, at least one).
 inline int32_t tier_chunks(int32_t stride) { return stride > 0 ? (stride + 2047) / 2048 : 1; }
 
-// Two int32 maps [batch][sum of strides], the (HIGH, MID) counts of every
-// scan chunk of every source, and with two sources source 0's totals.
+// 64-token blocks of a scores row (at least one).
+inline int32_t tier_blocks(int32_t stride) { return stride > 0 ? (stride + BT - 1) / BT : 1; }
+
+// The (HIGH, MID) int32 counts of every scan chunk of every source, then
+// the (HIGH, MID) destination positions of every 64-token block of every
+// source.
 inline int64_t tiering_workspace_bytes(int32_t batch, const int32_t* strides, int nsrc)
 {
-    int64_t map = 0, chunks = 0;
+    int64_t chunks = 0, blocks = 0;
     for (int i = 0; i < nsrc; i++) {
-        map += strides[i];
         chunks += tier_chunks(strides[i]);
+        blocks += tier_blocks(strides[i]);
     }
-    return 2 * (int64_t)batch * map * 4 + (int64_t)batch * chunks * 8 + (nsrc == 2 ? (int64_t)batch * 8 : 0);
+    return (int64_t)batch * (chunks + blocks) * 8;
 }
 
 }  // namespace lkv

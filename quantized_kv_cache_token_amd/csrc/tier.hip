@@ -9,14 +9,18 @@
 //    below tau_high or from a source that is MID already) tokens.
 //  tier_write: the same grid.  Each chunk adds up the counts that come
 //    before it in destination order (stable), scans its own tokens, and
-//    writes their tiers and the source token of every destination position.
-//    The first chunk writes the two counts (negative when a destination has
-//    no room) and source 0's totals.
-//  compact: one workgroup per (sequence, destination block, KV head,
-//    destination).  It gathers its 64 destination rows: K rows, scales and
-//    zeros copied bit for bit; V codes copied when the source holds the
-//    destination's width, else (V6 -> V4) dequantised in fp32 and
-//    requantised at 4 bits; then packs the channel-major V rows.
+//    writes their tiers and the destination positions of every 64-token
+//    block's first HIGH and MID survivor.  The first chunk writes the two
+//    counts (negative when a destination has no room).
+//  tier_move: one workgroup per (8 consecutive source chunks, KV head,
+//    sequence, source).  Each source chunk is read once, whole and
+//    coalesced; its survivors go to consecutive destination positions.  K
+//    rows, scales and zeros are stored straight from the loaded pieces; V
+//    codes are copied (same width) or dequantised in fp32 and requantised
+//    at 4 bits (V6 -> V4) into an LDS block of destination codes, which is
+//    packed into the channel-major rows when it fills or the workgroup ends.
+//    Only the words a neighbouring workgroup also writes are merged with
+//    atomics.
 #include <hip/hip_fp16.h>
 
 #include "lkv_internal.h"
@@ -38,6 +42,8 @@ struct TierSrc {
     int32_t max_tier;  // 2; 1 for a source whose tokens can no longer be HIGH
     int32_t nchunks;
     int32_t chunk0;    // its first chunk in a sequence's row of counts
+    int2* blk_base;    // [batch][base_stride]: (HIGH, MID) destination position of
+    int32_t base_stride;  // each 64-token block's first survivor
 };
 
 struct TierScanArgs {
@@ -45,14 +51,10 @@ struct TierScanArgs {
     int32_t nsrc;
     float tau_low, tau_high;
     int32_t h_cap, m_cap;
-    int32_t* h_map;  // [batch][map_stride]: source token of each destination position
-    int32_t* m_map;
-    int32_t map_stride;
     int32_t* n_high;
     int32_t* n_mid;
     int2* counts;    // [batch][count_stride] (HIGH, MID): source 0's chunks, then source 1's
     int32_t count_stride;
-    int2* bounds;    // [batch] (HIGH, MID) totals of source 0; null with one source
 };
 
 __device__ __forceinline__ int tier_of(float s, float tau_low, float tau_high, int max_tier)
@@ -95,7 +97,7 @@ __device__ __forceinline__ int2 block_sum2(int h, int m, int2* red)
 __global__ __launch_bounds__(256) void tier_count_kernel(TierScanArgs a)
 {
     const int c = blockIdx.x, b = blockIdx.y;
-    const TierSrc& src = a.src[blockIdx.z];
+    const TierSrc& src = blockIdx.z == 0 ? a.src[0] : a.src[1];
     if (c >= src.nchunks) return;
     const int len = max(0, min(src.lens[b], src.len_cap));  // out-of-contract lengths are clamped
     const int j0 = c * TIER_CHUNK + TIER_PER * threadIdx.x;
@@ -115,35 +117,30 @@ __global__ __launch_bounds__(256) void tier_count_kernel(TierScanArgs a)
 __global__ __launch_bounds__(256) void tier_write_kernel(TierScanArgs a)
 {
     const int c = blockIdx.x, b = blockIdx.y, z = blockIdx.z;
-    const TierSrc& src = a.src[z];
+    const TierSrc& src = z == 0 ? a.src[0] : a.src[1];
     if (c >= src.nchunks) return;
     const int len = max(0, min(src.lens[b], src.len_cap));
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // totals over every source, the counts that come before this chunk in
-    // destination order (earlier sources, then earlier chunks), and the
-    // totals of source 0
-    const int self = src.chunk0 + c, n0 = a.src[0].nchunks;
-    int th = 0, tm = 0, bh = 0, bm = 0, h0 = 0, m0 = 0;
+    // totals over every source, and the counts that come before this chunk
+    // in destination order (earlier sources, then earlier chunks)
+    const int self = src.chunk0 + c;
+    int th = 0, tm = 0, bh = 0, bm = 0;
     for (int i = lane; i < a.count_stride; i += 64) {
         const int2 v = a.counts[(int64_t)b * a.count_stride + i];
         th += v.x;
         tm += v.y;
         if (i < self) { bh += v.x; bm += v.y; }
-        if (i < n0) { h0 += v.x; m0 += v.y; }
     }
     for (int o = 32; o > 0; o >>= 1) {
         th += __shfl_xor(th, o, 64);
         tm += __shfl_xor(tm, o, 64);
         bh += __shfl_xor(bh, o, 64);
         bm += __shfl_xor(bm, o, 64);
-        h0 += __shfl_xor(h0, o, 64);
-        m0 += __shfl_xor(m0, o, 64);
     }
     const bool fits = th <= a.h_cap && tm <= a.m_cap;
     if (z == 0 && c == 0 && tid == 0) {
         a.n_high[b] = fits ? th : -th;
         a.n_mid[b] = fits ? tm : -tm;
-        if (a.bounds) a.bounds[b] = make_int2(h0, m0);
     }
     const int j0 = c * TIER_CHUNK + TIER_PER * tid;
     int t[TIER_PER];
@@ -170,156 +167,283 @@ __global__ __launch_bounds__(256) void tier_write_kernel(TierScanArgs a)
     __syncthreads();
     int ph = bh + ih - ch, pm = bm + im - cm;
     for (int w = 0; w < wave; w++) { ph += wsum[w].x; pm += wsum[w].y; }
-    int32_t* hs = a.h_map + (int64_t)b * a.map_stride;
-    int32_t* ms = a.m_map + (int64_t)b * a.map_stride;
-#pragma unroll
-    for (int i = 0; i < TIER_PER; i++) {
-        if (t[i] == 2) hs[ph++] = j0 + i;
-        else if (t[i] == 1) ms[pm++] = j0 + i;
+    // eight threads hold one 64-token block: the first writes its base
+    static_assert(8 * TIER_PER == BT, "a block is eight scan threads");
+    if ((tid & 7) == 0 && j0 < len) src.blk_base[(int64_t)b * src.base_stride + j0 / BT] = make_int2(ph, pm);
+}
+
+constexpr int MOVE_CHUNKS = 8;   // source chunks per workgroup, in token order
+constexpr int MOVE_PIECES = 5;   // 16-byte pieces per thread of one chunk (chunks up to 20 KiB)
+constexpr int MOVE_META = 5120;  // bytes of the scale and zero sections (D / g = 8 groups)
+
+struct MoveSrc {
+    Fmt f;
+    const uint8_t* pool;
+    const int32_t* bt;
+    int32_t max_blocks;
+    const int32_t* lens;
+    int32_t len_cap;
+    const uint8_t* tiers;
+    int32_t tier_stride;
+    const int2* blk_base;
+    int32_t base_stride;
+};
+
+struct MoveDst {
+    Fmt f;
+    uint8_t* pool;
+    const int32_t* bt;
+    int32_t max_blocks;
+};
+
+struct MoveArgs {
+    MoveSrc src[2];
+    MoveDst dst[2];  // 0: HIGH, 1: MID
+    const int32_t* n_high;
+    const int32_t* n_mid;
+    int32_t nsrc;
+};
+
+__device__ __forceinline__ uint8_t* dst_chunk(const MoveDst& d, int b, int pos, int kvh)
+{
+    return d.pool + ((int64_t)d.bt[(int64_t)b * d.max_blocks + pos / BT] * d.f.H + kvh) * d.f.chunk;
+}
+
+// Packs destination slots [slo, shi) of every channel row from the staged
+// codes into chunk dch; words shared with slots outside the range are
+// merged with atomics.
+template <int D>
+__device__ __forceinline__ void flush_block(const Fmt& fd, uint8_t* dch, const uint8_t (*st)[D], int slo, int shi)
+{
+    const int vb = fd.vb;
+    const int w0 = slo * vb / 32, w1 = (shi * vb - 1) / 32 + 1, nw = w1 - w0;
+    for (int i = threadIdx.x; i < D * nw; i += blockDim.x) {
+        const int d = i / nw, w = w0 + i % nw;
+        const uint32_t mask = field_mask(w, vb, slo, shi);
+        const uint32_t word = pack_word(w, vb, slo, shi, [&](int s) { return (uint32_t)st[s][d]; });
+        uint32_t* dst = (uint32_t*)(dch + fd.off_vc + d * fd.vrow) + w;
+        if (mask == 0xFFFFFFFFu) {
+            *dst = word;
+        } else {
+            atomicAnd(dst, ~mask);
+            atomicOr(dst, word & mask);
+        }
     }
 }
 
-struct CompactArgs {
-    Fmt fs0, fs1;                 // source formats (the second only with two sources)
-    const uint8_t* src_pool[2];
-    const int32_t* src_bt[2];
-    int32_t src_max_blocks[2];
-    Fmt fh, fm;
-    uint8_t* h_pool;
-    const int32_t* h_bt;
-    int32_t h_max_blocks;
-    uint8_t* m_pool;
-    const int32_t* m_bt;
-    int32_t m_max_blocks;
-    const int32_t* n_high;
-    const int32_t* n_mid;
-    const int32_t* h_map;
-    const int32_t* m_map;
-    int32_t map_stride;
-    const int2* bounds;           // null with one source
-    int32_t nblk;
-};
+// Where slot s of a source chunk goes: its segment (0 HIGH, 1 MID, -1
+// evicted), destination chunk and slot.  The survivors of segment i (mask
+// mk_i) take consecutive positions from pos_i in slot order; a chunk's
+// survivors span at most two destination blocks (dA_i: pos_i's block, dB_i:
+// the next one).
+__device__ __forceinline__ int slot_dest(int s, uint64_t mk0, uint64_t mk1, int pos0, int pos1, uint8_t* dA0,
+                                         uint8_t* dB0, uint8_t* dA1, uint8_t* dB1, uint8_t** dch, int* ds)
+{
+    const uint64_t bit = 1ull << s, lt = bit - 1ull;
+    if (mk0 & bit) {
+        const int P = pos0 + __popcll(mk0 & lt);
+        *dch = P / BT == pos0 / BT ? dA0 : dB0;
+        *ds = P % BT;
+        return 0;
+    }
+    if (mk1 & bit) {
+        const int P = pos1 + __popcll(mk1 & lt);
+        *dch = P / BT == pos1 / BT ? dA1 : dB1;
+        *ds = P % BT;
+        return 1;
+    }
+    return -1;
+}
 
-constexpr int CU = 4;  // slots a wave keeps in flight
-
-// One workgroup per (sequence, destination block, KV head, destination).
-// Destination position p of a sequence comes from source 0 below that
-// source's total for the destination (bounds), else from source 1.
+// V codes of survivor ranks [r0, r1) of one segment, copied at the source
+// width into staged slots r + sh.
 template <int D>
-__global__ __launch_bounds__(256) void compact_kernel(CompactArgs a)
+__device__ __forceinline__ void copy_codes(uint8_t (*st)[D], const uint8_t* src_of, const uint32_t* vsrc, int vrow_w,
+                                           int vb, int r0, int r1, int sh)
+{
+    const int cnt = (r1 - r0) * D;
+    for (int i = threadIdx.x; i < cnt; i += 256) {
+        const int r = r0 + i / D, d = i % D;
+        st[r + sh][d] = (uint8_t)get_field(vsrc + d * vrow_w, src_of[r], vb);
+    }
+}
+
+// MID survivor ranks [r0, r1) from 6-bit V: dequantised in fp32 and
+// requantised at the destination width, one token per wave; codes into
+// staged slots r + sh, scales and zeros straight to the destination.
+template <int D>
+__device__ __forceinline__ void requant_codes(uint8_t (*st)[D], const uint8_t* src_of, const uint32_t* vsrc,
+                                              int vrow_w, const Fmt& fs, const Fmt& fm, const float* m_vs,
+                                              const uint8_t* m_vz, int pos, uint8_t* dA, uint8_t* dB, int r0, int r1,
+                                              int sh)
 {
     constexpr int VPL = D / 64;
-    const int seg = blockIdx.z;  // 0: HIGH -> h, 1: MID -> m
-    const int b = blockIdx.x / a.nblk, lb = blockIdx.x % a.nblk, kvh = blockIdx.y;
-    const int nh = a.n_high[b], nm = a.n_mid[b];
-    if (nh < 0 || nm < 0) return;  // no room: nothing is written
-    const int n = seg == 0 ? nh : nm;
-    const int p0 = lb * BT;
-    if (p0 >= n) return;
-    const int cnt = min(BT, n - p0);
-    const Fmt& fd = seg == 0 ? a.fh : a.fm;
-    const int32_t* idx = (seg == 0 ? a.h_map : a.m_map) + (int64_t)b * a.map_stride + p0;
-    const int32_t* dbt = seg == 0 ? a.h_bt : a.m_bt;
-    const int32_t dmax = seg == 0 ? a.h_max_blocks : a.m_max_blocks;
-    uint8_t* dpool = seg == 0 ? a.h_pool : a.m_pool;
-    uint8_t* dch = dpool + ((int64_t)dbt[(int64_t)b * dmax + lb] * fd.H + kvh) * fd.chunk;
-    const int bound = a.bounds ? (seg == 0 ? a.bounds[b].x : a.bounds[b].y) : 0x7FFFFFFF;
-
-    // every slot's source, chunk and slot, resolved at once
-    __shared__ const uint8_t* src_ch[BT];
-    __shared__ int src_slot[BT];
-    __shared__ int src_id[BT];
-    if (threadIdx.x < cnt) {
-        const int j = idx[threadIdx.x];
-        const int sid = p0 + (int)threadIdx.x >= bound;
-        const int64_t chunk = sid ? a.fs1.chunk : a.fs0.chunk;
-        src_id[threadIdx.x] = sid;
-        src_slot[threadIdx.x] = j % BT;
-        src_ch[threadIdx.x] =
-            a.src_pool[sid] + ((int64_t)a.src_bt[sid][(int64_t)b * a.src_max_blocks[sid] + j / BT] * fd.H + kvh) *
-                                  chunk;
-    }
-    __syncthreads();
-
-    __shared__ uint8_t vc[BT][D];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int kw = fd.krow / 4;  // K words per row (<= 64), equal in every format here
-    for (int s0 = wave; s0 < cnt; s0 += 4 * CU) {
-        // loads of CU slots (s0, s0 + 4, ...; past the end: the last slot again)
-        uint32_t kword[CU], vlo[CU][VPL], vhi[CU][VPL];
-        float ks[CU], vs[CU][VPL];
-        uint32_t kz[CU], vz[CU][VPL];
+    for (int r = r0 + wave; r < r1; r += 4) {
+        const int s = src_of[r];
+        const int P = pos + r;
+        uint8_t* dch = P / BT == pos / BT ? dA : dB;
 #pragma unroll
-        for (int u = 0; u < CU; u++) {
-            const int s = min(s0 + 4 * u, cnt - 1);
-            const Fmt& fs = __builtin_amdgcn_readfirstlane(src_id[s]) ? a.fs1 : a.fs0;
-            const uint8_t* sch = src_ch[s];
-            const int sslot = src_slot[s];
-            kword[u] = lane < kw ? ((const uint32_t*)(sch + fs.off_kc + sslot * fs.krow))[lane] : 0u;
-            const int gl = min(lane, fs.ngroups - 1);
-            ks[u] = ((const float*)(sch + fs.off_ks))[gl * BT + sslot];
-            kz[u] = sch[fs.off_kz + gl * BT + sslot];
-            const int bit = sslot * fs.vb;
-#pragma unroll
-            for (int i = 0; i < VPL; i++) {
-                const int d = lane + 64 * i;
-                const int gi = d / fs.g;
-                // the two words that can hold the field (the second may be
-                // the next row's first word, or the first metadata word:
-                // still inside the chunk)
-                const uint32_t* w = (const uint32_t*)(sch + fs.off_vc + d * fs.vrow) + (bit >> 5);
-                vlo[u][i] = w[0];
-                vhi[u][i] = w[1];
-                vs[u][i] = ((const float*)(sch + fs.off_vs))[gi * BT + sslot];
-                vz[u][i] = sch[fs.off_vz + gi * BT + sslot];
+        for (int i = 0; i < VPL; i++) {
+            const int d = lane + 64 * i;
+            const int gi = d / fs.g;
+            const uint32_t code = get_field(vsrc + d * vrow_w, s, fs.vb);
+            const float x = (float)((int)code - (int)m_vz[gi * BT + s]) * m_vs[gi * BT + s];
+            float s4;
+            int z4;
+            const int c4 = quantize_lane(x, fm.g, fm.vb, &s4, &z4);
+            st[r + sh][d] = (uint8_t)c4;
+            if (d % fm.g == 0) {
+                ((float*)(dch + fm.off_vs))[gi * BT + P % BT] = s4;
+                dch[fm.off_vz + gi * BT + P % BT] = (uint8_t)z4;
             }
         }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void tier_move_kernel(MoveArgs a)
+{
+    __shared__ uint32_t vsrc[D * 12 + 4];        // the V section (up to 6-bit), plus slack for straddling reads
+    __shared__ uint32_t meta[MOVE_META / 4];     // K scales, V scales, K zeros, V zeros
+    __shared__ uint8_t stage[2][BT][D];          // destination codes of the current HIGH / MID block
+    __shared__ uint8_t src_of[4][2][BT];         // per wave: source slot of each survivor rank
+
+    const int si = blockIdx.z % a.nsrc, b = blockIdx.z / a.nsrc, kvh = blockIdx.y;
+    if (a.n_high[b] < 0 || a.n_mid[b] < 0) return;  // no room: nothing is written
+    const MoveSrc& S = si == 0 ? a.src[0] : a.src[1];
+    const Fmt& fs = S.f;
+    const int len = max(0, min(S.lens[b], S.len_cap));
+    const int nblocks = (len + BT - 1) / BT;
+    const int c0 = blockIdx.x * MOVE_CHUNKS;
+    if (c0 >= nblocks) return;
+    const int c1 = min(nblocks, c0 + MOVE_CHUNKS);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int2 base = S.blk_base[(int64_t)b * S.base_stride + c0];
+    // next destination position of each segment, and the first position this
+    // workgroup staged in the segment's current block
+    int pos0 = base.x, pos1 = base.y, lo0 = base.x, lo1 = base.y;
+    const int krows = BT * fs.krow, vbytes = D * fs.vrow;
+    const int npieces = (int)(fs.chunk / 16);
+    const int vrow_w = fs.vrow / 4;
+    const float* m_ks = (const float*)meta;
+    const float* m_vs = (const float*)((const uint8_t*)meta + (fs.off_vs - fs.off_ks));
+    const uint8_t* m_kz = (const uint8_t*)meta + (fs.off_kz - fs.off_ks);
+    const uint8_t* m_vz = (const uint8_t*)meta + (fs.off_vz - fs.off_ks);
+    // destination layouts: both hold the source's K format, so K rows sit at
+    // the same offsets; the scale and zero sections differ with the V width
+    const Fmt& fh = a.dst[0].f;
+    const Fmt& fm = a.dst[1].f;
+    const bool copy_m = fm.vb == fs.vb;  // MID survivors keep their V codes (a MID source)
+
+    for (int c = c0; c < c1; c++) {
+        // tiers of the chunk's 64 slots; every wave derives the same masks
+        const int nvalid = min(BT, len - c * BT);
+        const int t = lane < nvalid ? S.tiers[(int64_t)b * S.tier_stride + c * BT + lane] : 0;
+        const uint64_t mk0 = __ballot(t == 2), mk1 = __ballot(t == 1);
+        const uint64_t below = (1ull << lane) - 1ull;
+        if (t == 2) src_of[wave][0][__popcll(mk0 & below)] = (uint8_t)lane;
+        else if (t == 1) src_of[wave][1][__popcll(mk1 & below)] = (uint8_t)lane;
+        const int n0 = __popcll(mk0), n1 = __popcll(mk1);
+        if (n0 + n1 == 0) continue;
+
+        const uint8_t* sch = S.pool + ((int64_t)S.bt[(int64_t)b * S.max_blocks + c] * fs.H + kvh) * fs.chunk;
+        uint4 pc[MOVE_PIECES];
 #pragma unroll
-        for (int u = 0; u < CU; u++) {
-            const int s = s0 + 4 * u;
-            if (s >= cnt) break;
-            const Fmt& fs = __builtin_amdgcn_readfirstlane(src_id[s]) ? a.fs1 : a.fs0;
-            const int sslot = src_slot[s];
-            // K row, K scales, K zeros: bit for bit
-            if (lane < kw) ((uint32_t*)(dch + fd.off_kc + s * fd.krow))[lane] = kword[u];
-            if (lane < fs.ngroups) {
-                ((float*)(dch + fd.off_ks))[lane * BT + s] = ks[u];
-                dch[fd.off_kz + lane * BT + s] = (uint8_t)kz[u];
+        for (int k = 0; k < MOVE_PIECES; k++) {
+            const int p = tid + 256 * k;
+            pc[k] = p < npieces ? ((const uint4*)sch)[p] : make_uint4(0u, 0u, 0u, 0u);
+        }
+        // destination chunks: the block of each segment's next position and
+        // the one after it
+        uint8_t *dA0 = nullptr, *dB0 = nullptr, *dA1 = nullptr, *dB1 = nullptr;
+        if (n0) {
+            dA0 = dst_chunk(a.dst[0], b, pos0, kvh);
+            dB0 = pos0 % BT + n0 > BT ? dst_chunk(a.dst[0], b, pos0 + BT, kvh) : dA0;
+        }
+        if (n1) {
+            dA1 = dst_chunk(a.dst[1], b, pos1, kvh);
+            dB1 = pos1 % BT + n1 > BT ? dst_chunk(a.dst[1], b, pos1 + BT, kvh) : dA1;
+        }
+        __syncthreads();  // the previous chunk's readers of vsrc and meta are done
+#pragma unroll
+        for (int k = 0; k < MOVE_PIECES; k++) {
+            const int off = 16 * (tid + 256 * k);
+            if (off >= 16 * npieces) continue;
+            if (off >= fs.off_ks) {
+                *(uint4*)((uint8_t*)meta + (off - fs.off_ks)) = pc[k];
+            } else if (off >= fs.off_vc) {
+                if (off < fs.off_vc + vbytes) *(uint4*)((uint8_t*)vsrc + (off - fs.off_vc)) = pc[k];
+            } else if (off < krows) {  // a K row piece: stored straight to its survivor's row
+                uint8_t* dch;
+                int ds;
+                if (slot_dest(off / fs.krow, mk0, mk1, pos0, pos1, dA0, dB0, dA1, dB1, &dch, &ds) >= 0)
+                    *(uint4*)(dch + fh.off_kc + ds * fh.krow + off % fs.krow) = pc[k];
             }
-            const int sh = (sslot * fs.vb) & 31;
-            const bool same = fs.vb == fd.vb;
-#pragma unroll
-            for (int i = 0; i < VPL; i++) {
-                const int d = lane + 64 * i;
-                const int gi = d / fs.g;
-                const uint64_t x64 = ((uint64_t)vhi[u][i] << 32) | vlo[u][i];
-                const uint32_t code = (uint32_t)(x64 >> sh) & ((1u << fs.vb) - 1u);
-                if (same) {  // V codes, scale and zero copied
-                    vc[s][d] = (uint8_t)code;
-                    if ((d % fs.g) == 0) {
-                        ((float*)(dch + fd.off_vs))[gi * BT + s] = vs[u][i];
-                        dch[fd.off_vz + gi * BT + s] = (uint8_t)vz[u][i];
-                    }
-                } else {  // 6 -> 4 bits: dequantised, one fp32 rounding, requantised
-                    const float x = (float)((int)code - (int)vz[u][i]) * vs[u][i];
-                    float s4;
-                    int z4;
-                    const int c4 = quantize_lane(x, fd.g, fd.vb, &s4, &z4);
-                    vc[s][d] = (uint8_t)c4;
-                    if ((d % fd.g) == 0) {
-                        ((float*)(dch + fd.off_vs))[gi * BT + s] = s4;
-                        dch[fd.off_vz + gi * BT + s] = (uint8_t)z4;
-                    }
+        }
+        __syncthreads();
+        // K scales and zeros of every survivor; V scales and zeros where V is copied
+        for (int i = tid; i < fs.ngroups * BT; i += 256) {
+            uint8_t* dch;
+            int ds;
+            const int seg = slot_dest(i % BT, mk0, mk1, pos0, pos1, dA0, dB0, dA1, dB1, &dch, &ds);
+            if (seg < 0) continue;
+            ds += i / BT * BT;
+            ((float*)(dch + (seg == 0 ? fh.off_ks : fm.off_ks)))[ds] = m_ks[i];
+            dch[(seg == 0 ? fh.off_kz : fm.off_kz) + ds] = m_kz[i];
+            if (seg == 0 || copy_m) {
+                ((float*)(dch + (seg == 0 ? fh.off_vs : fm.off_vs)))[ds] = m_vs[i];
+                dch[(seg == 0 ? fh.off_vz : fm.off_vz) + ds] = m_vz[i];
+            }
+        }
+        // V codes of each segment into its staged block; a block that fills
+        // is packed out and the rest of the chunk's survivors start the next
+        // one.  HIGH codes are always copied (6-bit to 6-bit).
+        if (n0) {
+            const int first = min(n0, BT - pos0 % BT);
+            copy_codes<D>(stage[0], src_of[wave][0], vsrc, vrow_w, fs.vb, 0, first, pos0 % BT);
+            if (pos0 % BT + n0 >= BT) {  // the block is complete
+                __syncthreads();
+                flush_block<D>(fh, dA0, stage[0], lo0 - pos0 / BT * BT, BT);
+                __syncthreads();
+                lo0 = (pos0 / BT + 1) * BT;
+                if (first < n0) copy_codes<D>(stage[0], src_of[wave][0], vsrc, vrow_w, fs.vb, first, n0, -first);
+            }
+            pos0 += n0;
+        }
+        if (n1) {
+            const int first = min(n1, BT - pos1 % BT);
+            if (copy_m)
+                copy_codes<D>(stage[1], src_of[wave][1], vsrc, vrow_w, fs.vb, 0, first, pos1 % BT);
+            else
+                requant_codes<D>(stage[1], src_of[wave][1], vsrc, vrow_w, fs, fm, m_vs, m_vz, pos1, dA1, dB1,
+                                 0, first, pos1 % BT);
+            if (pos1 % BT + n1 >= BT) {
+                __syncthreads();
+                flush_block<D>(fm, dA1, stage[1], lo1 - pos1 / BT * BT, BT);
+                __syncthreads();
+                lo1 = (pos1 / BT + 1) * BT;
+                if (first < n1) {
+                    if (copy_m)
+                        copy_codes<D>(stage[1], src_of[wave][1], vsrc, vrow_w, fs.vb, first, n1, -first);
+                    else
+                        requant_codes<D>(stage[1], src_of[wave][1], vsrc, vrow_w, fs, fm, m_vs, m_vz, pos1, dA1,
+                                         dB1, first, n1, -first);
                 }
             }
+            pos1 += n1;
         }
     }
-    __syncthreads();
-    const int wv = BT * fd.vb / 32;
-    for (int i = threadIdx.x; i < D * wv; i += blockDim.x) {
-        const int d = i / wv, w = i % wv;
-        const uint32_t word = pack_word(w, fd.vb, 0, cnt, [&](int s) { return (uint32_t)vc[s][d]; });
-        ((uint32_t*)(dch + fd.off_vc + d * fd.vrow))[w] = word;
+    // the partly filled last block of each segment
+    if (pos0 > lo0) {
+        __syncthreads();
+        const int blk0 = lo0 / BT * BT;
+        flush_block<D>(fh, dst_chunk(a.dst[0], b, lo0, kvh), stage[0], lo0 - blk0, pos0 - blk0);
+    }
+    if (pos1 > lo1) {
+        __syncthreads();
+        const int blk0 = lo1 / BT * BT;
+        flush_block<D>(fm, dst_chunk(a.dst[1], b, lo1, kvh), stage[1], lo1 - blk0, pos1 - blk0);
     }
 }
 
@@ -328,8 +452,18 @@ hipError_t launch_tiering(const TierSource* src, int nsrc, float tau_low, float 
                           hipStream_t stream)
 {
     if (batch == 0) return hipSuccess;
+    for (int i = 0; i < nsrc; i++)  // every quantised format fits the move kernel's staging
+        if (src[i].f.chunk > 16 * 256 * MOVE_PIECES || src[i].f.chunk - src[i].f.off_ks > MOVE_META ||
+            src[i].f.vb > 6 || src[i].f.D != h.f.D)
+            return hipErrorInvalidValue;
     TierScanArgs t = {};
-    int32_t max_chunks = 0, map_stride = 0, max_len = 0;
+    int2* counts = (int2*)workspace;
+    int32_t count_stride = 0, base_total = 0, max_chunks = 0, max_blocks = 0;
+    for (int i = 0; i < nsrc; i++) {
+        count_stride += tier_chunks(src[i].stride);
+        max_blocks = max(max_blocks, (src[i].max_len + BT - 1) / BT);
+    }
+    int2* bases = counts + (int64_t)batch * count_stride;
     for (int i = 0; i < nsrc; i++) {
         TierSrc& s = t.src[i];
         s.scores = src[i].scores;
@@ -340,55 +474,48 @@ hipError_t launch_tiering(const TierSource* src, int nsrc, float tau_low, float 
         s.max_tier = src[i].max_tier;
         s.nchunks = tier_chunks(src[i].stride);
         s.chunk0 = t.count_stride;
+        s.base_stride = tier_blocks(src[i].stride);
+        s.blk_base = bases + (int64_t)batch * base_total;
+        base_total += s.base_stride;
         t.count_stride += s.nchunks;
         max_chunks = max(max_chunks, s.nchunks);
-        map_stride += src[i].stride;
-        max_len += src[i].max_len;
     }
     t.nsrc = nsrc;
     t.tau_low = tau_low;
     t.tau_high = tau_high;
     t.h_cap = h.max_blocks * BT;
     t.m_cap = m.max_blocks * BT;
-    t.map_stride = map_stride;
-    t.h_map = (int32_t*)workspace;
-    t.m_map = t.h_map + (int64_t)batch * map_stride;
-    t.counts = (int2*)(t.m_map + (int64_t)batch * map_stride);
-    t.bounds = nsrc == 2 ? t.counts + (int64_t)batch * t.count_stride : nullptr;
+    t.counts = counts;
     t.n_high = n_high;
     t.n_mid = n_mid;
     const dim3 sgrid((unsigned)max_chunks, (unsigned)batch, (unsigned)nsrc);
     hipLaunchKernelGGL(tier_count_kernel, sgrid, dim3(256), 0, stream, t);
     hipLaunchKernelGGL(tier_write_kernel, sgrid, dim3(256), 0, stream, t);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || max_len == 0) return e;
-    CompactArgs a = {};
-    a.fs0 = src[0].f;
-    a.fs1 = nsrc == 2 ? src[1].f : src[0].f;
+    if (e != hipSuccess || max_blocks == 0) return e;
+    MoveArgs a = {};
     for (int i = 0; i < nsrc; i++) {
-        a.src_pool[i] = src[i].pool;
-        a.src_bt[i] = src[i].block_table;
-        a.src_max_blocks[i] = src[i].max_blocks;
+        MoveSrc& s = a.src[i];
+        s.f = src[i].f;
+        s.pool = src[i].pool;
+        s.bt = src[i].block_table;
+        s.max_blocks = src[i].max_blocks;
+        s.lens = src[i].view_lens;
+        s.len_cap = t.src[i].len_cap;
+        s.tiers = src[i].tiers;
+        s.tier_stride = src[i].stride;
+        s.blk_base = t.src[i].blk_base;
+        s.base_stride = t.src[i].base_stride;
     }
-    a.fh = h.f;
-    a.fm = m.f;
-    a.h_pool = h.pool;
-    a.h_bt = h.block_table;
-    a.h_max_blocks = h.max_blocks;
-    a.m_pool = m.pool;
-    a.m_bt = m.block_table;
-    a.m_max_blocks = m.max_blocks;
+    a.dst[0] = MoveDst{h.f, h.pool, h.block_table, h.max_blocks};
+    a.dst[1] = MoveDst{m.f, m.pool, m.block_table, m.max_blocks};
     a.n_high = n_high;
     a.n_mid = n_mid;
-    a.h_map = t.h_map;
-    a.m_map = t.m_map;
-    a.map_stride = map_stride;
-    a.bounds = t.bounds;
-    // destination blocks that can hold a survivor
-    a.nblk = min((max_len + BT - 1) / BT, max(h.max_blocks, m.max_blocks));
-    dim3 grid((unsigned)(batch * a.nblk), (unsigned)h.f.H, 2);
-    if (h.f.D == 64) hipLaunchKernelGGL(compact_kernel<64>, grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(compact_kernel<128>, grid, dim3(256), 0, stream, a);
+    a.nsrc = nsrc;
+    const dim3 grid((unsigned)((max_blocks + MOVE_CHUNKS - 1) / MOVE_CHUNKS), (unsigned)h.f.H,
+                    (unsigned)(batch * nsrc));
+    if (h.f.D == 64) hipLaunchKernelGGL(tier_move_kernel<64>, grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(tier_move_kernel<128>, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -139,9 +139,11 @@ def test_tier_update_rejects_bad_formats():
     assert call(m=_cache(v_bits=4, group_size=32)) == lkv.EINVAL
     assert call(stride=512) == lkv.EINVAL                      # scores shorter than max_len
     assert call(ws=100) == lkv.EINVAL
-    # two int32 source maps [B][stride], then (HIGH, MID) int32 counts per 2048-token scan chunk
-    assert L.lkv_tier_workspace_bytes(8, 32768) == 2 * 8 * 32768 * 4 + 8 * 16 * 8
-    assert L.lkv_tier_workspace_bytes(2, 300) == 2 * 2 * 300 * 4 + 2 * 1 * 8
+    # (HIGH, MID) int32 counts per 2048-token scan chunk, then (HIGH, MID)
+    # destination positions per 64-token block
+    assert L.lkv_tier_workspace_bytes(8, 32768) == 8 * (16 + 512) * 8
+    assert L.lkv_tier_workspace_bytes(2, 300) == 2 * (1 + 5) * 8
+    assert L.lkv_tier_workspace_bytes(1, 0) == 1 * (1 + 1) * 8
 
 
 def test_retier_rejects_bad_formats():
@@ -161,10 +163,10 @@ def test_retier_rejects_bad_formats():
     assert call(dm=_cache(v_bits=4, num_kv_heads=2)) == lkv.EINVAL
     assert call(ms=512) == lkv.EINVAL                           # MID scores shorter than max_len
     assert call(ws=100) == lkv.EINVAL
-    # two int32 maps [B][h + m strides], (HIGH, MID) counts per 2048-token
-    # chunk of each segment, then two int32 totals per sequence
-    assert L.lkv_retier_workspace_bytes(8, 32768, 4096) == 2 * 8 * 36864 * 4 + 8 * (16 + 2) * 8 + 8 * 8
-    assert L.lkv_retier_workspace_bytes(2, 300, 0) == 2 * 2 * 300 * 4 + 2 * (1 + 1) * 8 + 2 * 8
+    # (HIGH, MID) counts per 2048-token chunk and destination positions per
+    # 64-token block, of each segment
+    assert L.lkv_retier_workspace_bytes(8, 32768, 4096) == 8 * (16 + 2 + 512 + 64) * 8
+    assert L.lkv_retier_workspace_bytes(2, 300, 0) == 2 * (1 + 1 + 5 + 1) * 8
     assert L.lkv_retier_workspace_bytes(-1, 1, 1) == lkv.EINVAL
 
 

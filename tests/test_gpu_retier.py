@@ -154,3 +154,64 @@ def test_retier_without_room_writes_nothing():
     for pair, bt in ((r["dh"], r["dhb"]), (r["dm"], r["dmb"])):
         pool = pair.gpu.pool.cpu().numpy().reshape(-1, Hkv * pair.ref.chunk_bytes)
         assert not pool[int(bt[0, 0])].any()
+
+
+def _stale(pair: Pair, seed: int):
+    """Fill both pools of a pair with the same random bytes."""
+    junk = np.random.default_rng(seed).integers(0, 256, pair.ref.pool.size, dtype=np.uint8)
+    pair.ref.pool[:] = junk
+    pair.gpu.pool.copy_(torch.from_numpy(junk).cuda())
+
+
+def test_tier_and_retier_into_stale_pools():
+    """Destinations full of stale bytes: only the survivors' fields change,
+    exactly as in the oracle (whole pools compared)."""
+    Hkv, lens = 2, [900, 70, 1300]
+    rng = np.random.default_rng(110)
+    bt, nblk = block_tables(lens, rng)
+    src = Pair(D, g, 6, 6, Hkv, nblk)
+    K, V = zip(*[inputs.kv_rows(111, b, n, Hkv, D, dtype="bf16") for b, n in enumerate(lens)])
+    src.append(torch.cat(K), torch.cat(V), np.concatenate([[0], np.cumsum(lens)]).astype(np.int32),
+               np.zeros(len(lens), np.int32), bt)
+    stride = max(lens)
+    tl, th = O.default_thresholds(stride)
+    scores = _segment_scores(112, lens, stride, tl, th, 0.2, 0.3)
+    hbt, hn = block_tables(lens, rng)
+    mbt, mn = block_tables(lens, rng)
+    h, m = Pair(D, g, 6, 6, Hkv, hn), Pair(D, g, 6, 4, Hkv, mn)
+    _stale(h, 113)
+    _stale(m, 114)
+    nh = torch.zeros(len(lens), dtype=torch.int32, device="cuda")
+    nm = torch.zeros_like(nh)
+    tiers = torch.zeros((len(lens), stride), dtype=torch.uint8, device="cuda")
+    say("tier update into stale pools")
+    lkv.tier_update(src.gpu, lkv.View(_dev(bt), _dev(lens), stride), scores.cuda(), tl, th, h.gpu, _dev(hbt), m.gpu,
+                    _dev(mbt), nh, nm, tiers)
+    torch.cuda.synchronize()
+    _, nh_ref, nm_ref = O.tier_update(src.ref, bt, np.array(lens, np.int32), scores.numpy(), tl, th, h.ref, hbt,
+                                      m.ref, mbt)
+    assert np.array_equal(nh.cpu().numpy(), nh_ref) and np.array_equal(nm.cpu().numpy(), nm_ref)
+    assert h.pool_equal(), h.first_pool_mismatch()
+    assert m.pool_equal(), m.first_pool_mismatch()
+    say("retier into stale pools")
+    hs_stride, ms_stride = int(nh_ref.max()), int(nm_ref.max())
+    hs = _segment_scores(115, nh_ref, hs_stride, tl, th, 0.3, 0.4)
+    ms = _segment_scores(116, nm_ref, ms_stride, tl, th, 0.3, 0.4)
+    cap = [int(a + c) for a, c in zip(nh_ref, nm_ref)]
+    dhb, dhn = block_tables(cap, rng)
+    dmb, dmn = block_tables(cap, rng)
+    dh, dm = Pair(D, g, 6, 6, Hkv, dhn), Pair(D, g, 6, 4, Hkv, dmn)
+    _stale(dh, 117)
+    _stale(dm, 118)
+    n_high, n_mid = torch.zeros_like(nh), torch.zeros_like(nh)
+    ht = torch.full((len(lens), hs_stride), 255, dtype=torch.uint8, device="cuda")  # as the oracle's
+    mt = torch.full((len(lens), ms_stride), 255, dtype=torch.uint8, device="cuda")
+    lkv.retier(h.gpu, lkv.View(_dev(hbt), nh, hs_stride), hs.cuda(), m.gpu, lkv.View(_dev(mbt), nm, ms_stride),
+               ms.cuda(), tl, th, dh.gpu, _dev(dhb), dm.gpu, _dev(dmb), n_high, n_mid, ht, mt)
+    torch.cuda.synchronize()
+    ht_ref, mt_ref, nh2, nm2 = O.retier(h.ref, hbt, nh_ref, hs.numpy(), m.ref, mbt, nm_ref, ms.numpy(), tl, th,
+                                        dh.ref, dhb, dm.ref, dmb)
+    assert np.array_equal(n_high.cpu().numpy(), nh2) and np.array_equal(n_mid.cpu().numpy(), nm2)
+    assert np.array_equal(ht.cpu().numpy(), ht_ref) and np.array_equal(mt.cpu().numpy(), mt_ref)
+    assert dh.pool_equal(), dh.first_pool_mismatch()
+    assert dm.pool_equal(), dm.first_pool_mismatch()
