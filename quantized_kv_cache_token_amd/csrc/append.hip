@@ -1,5 +1,8 @@
 // append.hip -- quantise-and-pack append (built with -ffp-contract=off).
 //
+// append_quant_kernel serves the quantised formats; append_kernel the fp16
+// format and inputs not aligned to two elements.
+//
 // One workgroup owns one (sequence, logical block, KV head) chunk for the
 // call, so the channel-major V rows, whose 32-bit words hold several tokens,
 // are merged and written without atomics.  Each wave quantises whole rows
@@ -167,12 +170,197 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
     }
 }
 
+// ---- quantised formats (K and V at 4 or 6 bits) ----
+//
+// The same placement as append_kernel, with each lane holding P = D / 64
+// consecutive channels (one 4- or 8-byte load per lane and row), the faster
+// quantiser, and word packing in whole groups of fields.  K codes are
+// staged per slot (a lane's P codes in one 16-bit value), V codes channel-
+// major with a row pitch of 68 bytes (the transposed stores of a wave hit
+// distinct banks).
+constexpr int VPITCH = 68;
+
+template <int DT, int P>
+__device__ __forceinline__ void load_vals(const void* p, int64_t i, uint32_t (&u)[P])
+{
+    if constexpr (DT == LKV_F32) {
+        if constexpr (P == 2) {
+            const uint2 t = *(const uint2*)((const uint32_t*)p + i);
+            u[0] = t.x;
+            u[1] = t.y;
+        } else {
+            u[0] = ((const uint32_t*)p)[i];
+        }
+    } else {
+        if constexpr (P == 2) {
+            const uint32_t t = *(const uint32_t*)((const uint16_t*)p + i);
+            u[0] = t & 0xFFFFu;
+            u[1] = t >> 16;
+        } else {
+            u[0] = ((const uint16_t*)p)[i];
+        }
+    }
+}
+
+// K words of one slot: group m of NV lane values (NB bits each) -> NW words.
+template <int NB, int NV, int NW>
+__device__ __forceinline__ void pack_k_group(const uint16_t* row, int m, uint32_t* dst)
+{
+    uint32_t v[NV], w[NW];
+#pragma unroll
+    for (int i = 0; i < NV; i++) v[i] = row[m * NV + i];
+    pack_values<NB, NV, NW>(v, w);
+#pragma unroll
+    for (int i = 0; i < NW; i++) dst[m * NW + i] = w[i];
+}
+
+template <int NB, int NV, int NW>
+__device__ __forceinline__ void pack_k_rows(const uint16_t (*kq)[64], uint8_t* ch, const Fmt& f, int s0, int s1)
+{
+    constexpr int G = 64 / NV;  // groups per slot
+    for (int idx = threadIdx.x; idx < (s1 - s0) * G; idx += blockDim.x) {
+        const int slot = s0 + idx / G;
+        pack_k_group<NB, NV, NW>(kq[slot], idx % G, (uint32_t*)(ch + f.off_kc + slot * f.krow));
+    }
+}
+
+// V words of channel rows: group m of NV slots -> NW words; only the words
+// holding bits of slots [s0, s1) are written, shared words merged with
+// atomics.
+template <int NB, int NV, int NW, int D>
+__device__ __forceinline__ void pack_v_rows(const uint8_t (*vt)[VPITCH], uint8_t* ch, const Fmt& f, int s0, int s1)
+{
+    const int m0 = s0 / NV, m1 = (s1 - 1) / NV;
+    const int ng = m1 - m0 + 1;
+    for (int idx = threadIdx.x; idx < D * ng; idx += blockDim.x) {
+        const int d = idx / ng, m = m0 + idx % ng;
+        uint32_t v[NV], w[NW];
+        const uint32_t* src = (const uint32_t*)(vt[d] + m * NV);
+#pragma unroll
+        for (int i = 0; i < NV / 4; i++) {
+            const uint32_t t = src[i];
+            v[4 * i] = t & 0xFFu;
+            v[4 * i + 1] = (t >> 8) & 0xFFu;
+            v[4 * i + 2] = (t >> 16) & 0xFFu;
+            v[4 * i + 3] = t >> 24;
+        }
+        pack_values<NB, NV, NW>(v, w);
+        uint32_t* row = (uint32_t*)(ch + f.off_vc + d * f.vrow) + m * NW;
+#pragma unroll
+        for (int i = 0; i < NW; i++) {
+            const uint32_t mask = field_mask(m * NW + i, NB, s0, s1);
+            if (mask == 0xFFFFFFFFu) {
+                row[i] = w[i];
+            } else if (mask != 0u) {
+                atomicAnd(row + i, ~mask);
+                atomicOr(row + i, w[i] & mask);
+            }
+        }
+    }
+}
+
+template <int D, int DT>
+__global__ __launch_bounds__(256) void append_quant_kernel(AppendArgs a)
+{
+    constexpr int P = D / 64;  // channels P * lane + p
+    const Fmt& f = a.f;
+    const int b = blockIdx.x / a.nblk;
+    const int i = blockIdx.x % a.nblk;
+    const int kvh = blockIdx.y;
+    const int row0 = a.cu_new[b];
+    const int row1 = a.cu_new[b + 1];
+    const int sp = a.start_pos[b];
+    const int n = row1 - row0;
+    const int lb = sp / BT + i;
+    const int p0 = max(sp, lb * BT);
+    const int p1 = min(sp + n, lb * BT + BT);
+    if (n <= 0 || p0 >= p1) return;
+    const int s0 = p0 - lb * BT, s1 = p1 - lb * BT;  // slots written by this call
+    const int64_t blk = a.block_table[(int64_t)b * a.max_blocks + lb];
+    uint8_t* ch = a.pool + (blk * f.H + kvh) * f.chunk;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nrows = 2 * (s1 - s0);  // row r: slot s0 + r / 2, K (r even) or V (r odd)
+
+    __shared__ uint16_t kq[BT][64];
+    __shared__ uint8_t vt[D][VPITCH];
+#pragma unroll 1
+    for (int k0 = 0; k0 < MAXR; k0 += CH) {
+        if (wave + 4 * k0 >= nrows) break;
+        uint32_t u[CH][P];
+#pragma unroll
+        for (int k = 0; k < CH; k++) {
+            const int r = min(wave + 4 * (k0 + k), nrows - 1);
+            const int slot = s0 + (r >> 1);
+            const int64_t in_row = (int64_t)(row0 + (lb * BT + slot - sp)) * f.H + kvh;
+            load_vals<DT, P>((r & 1) ? a.v : a.k, in_row * D + P * lane, u[k]);
+        }
+        QRow<P> q[CH];
+#pragma unroll
+        for (int k = 0; k < CH; k++) {
+            const int r = wave + 4 * (k0 + k);
+            float x[P];
+#pragma unroll
+            for (int p = 0; p < P; p++) x[p] = raw_value<DT>(u[k][p]);
+            quantize_fast<P>(x, f.g, (r & 1) ? f.vb : f.kb, q[k]);
+        }
+        // lanes whose quotient sat too close to a half-integer
+#pragma unroll
+        for (int k = 0; k < CH; k++) {
+            if (q[k].slow) {
+                const int r = wave + 4 * (k0 + k);
+                float x[P];
+#pragma unroll
+                for (int p = 0; p < P; p++) x[p] = raw_value<DT>(u[k][p]);
+                quantize_exact<P>(x, (r & 1) ? f.vb : f.kb, q[k]);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < CH; k++) {
+            const int r = wave + 4 * (k0 + k);
+            if (r >= nrows) break;
+            const int slot = s0 + (r >> 1);
+            const bool is_v = r & 1;
+            if (is_v) {
+#pragma unroll
+                for (int p = 0; p < P; p++) vt[P * lane + p][slot] = (uint8_t)q[k].q[p];
+            } else {
+                kq[slot][lane] = (uint16_t)(P == 2 ? (q[k].q[0] | (q[k].q[1] << f.kb)) : q[k].q[0]);
+            }
+            if ((P * lane) % f.g == 0) {
+                const int gi = P * lane / f.g;
+                ((float*)(ch + (is_v ? f.off_vs : f.off_ks)))[gi * BT + slot] = q[k].s;
+                ch[(is_v ? f.off_vz : f.off_kz) + gi * BT + slot] = (uint8_t)q[k].z;
+            }
+        }
+    }
+    __syncthreads();
+    const int knb = P * f.kb;  // bits of one lane's K value
+    if (knb == 12) pack_k_rows<12, 8, 3>(kq, ch, f, s0, s1);
+    else if (knb == 8) pack_k_rows<8, 4, 1>(kq, ch, f, s0, s1);
+    else if (knb == 6) pack_k_rows<6, 16, 3>(kq, ch, f, s0, s1);
+    else pack_k_rows<4, 8, 1>(kq, ch, f, s0, s1);
+    if (f.vb == 6) pack_v_rows<6, 16, 3, D>(vt, ch, f, s0, s1);
+    else pack_v_rows<4, 8, 1, D>(vt, ch, f, s0, s1);
+}
+
 template <int D>
 static void launch_d(const AppendArgs& a, int dtype, dim3 grid, hipStream_t stream)
 {
-    if (dtype == LKV_F32) hipLaunchKernelGGL((append_kernel<D, LKV_F32>), grid, dim3(256), 0, stream, a);
-    else if (dtype == LKV_BF16) hipLaunchKernelGGL((append_kernel<D, LKV_BF16>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((append_kernel<D, LKV_F16>), grid, dim3(256), 0, stream, a);
+    // the quantised kernel loads P = D / 64 elements per lane at once: it needs
+    // K and V aligned to P elements
+    const uintptr_t need = (uintptr_t)(D / 64) * (dtype == LKV_F32 ? 4 : 2);
+    const bool aligned = (uintptr_t)a.k % need == 0 && (uintptr_t)a.v % need == 0;
+    if (a.f.fp16 || !aligned) {
+        if (dtype == LKV_F32) hipLaunchKernelGGL((append_kernel<D, LKV_F32>), grid, dim3(256), 0, stream, a);
+        else if (dtype == LKV_BF16) hipLaunchKernelGGL((append_kernel<D, LKV_BF16>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((append_kernel<D, LKV_F16>), grid, dim3(256), 0, stream, a);
+        return;
+    }
+    if (dtype == LKV_F32) hipLaunchKernelGGL((append_quant_kernel<D, LKV_F32>), grid, dim3(256), 0, stream, a);
+    else if (dtype == LKV_BF16) hipLaunchKernelGGL((append_quant_kernel<D, LKV_BF16>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((append_quant_kernel<D, LKV_F16>), grid, dim3(256), 0, stream, a);
 }
 
 hipError_t launch_append(const Fmt& f, uint8_t* pool, const void* k, const void* v, int dtype,

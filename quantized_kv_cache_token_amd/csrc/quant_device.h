@@ -75,6 +75,148 @@ __device__ __forceinline__ int quantize_lane(float x, int g, int bits, float* s_
     return q;
 }
 
+// ---- faster quantiser for rows held P consecutive channels per lane ----
+//
+// The same codes, scale and zero point as quantize_lane (finite inputs), with
+// fewer operations:
+//  - min / max by compares (no NaN handling) over the lane's P values, then
+//    over the g / P lanes of the group;
+//  - s = RN(r / qmax) as r * RN(1 / qmax) plus one fma correction, which is
+//    the correctly rounded quotient for every finite r >= 0 when qmax is 15
+//    or 63 (checked exhaustively over all fp32 values);
+//  - rint(RN(x / s)) from an approximate reciprocal and one fma correction,
+//    which gives the quotient to within an ulp: rint can differ only when
+//    that quotient lies within a few ulps of a half-integer.  Such lanes
+//    (and any scale that is not a finite normal number) are flagged and
+//    recomputed with correctly rounded division (quantize_exact).
+
+template <bool MAX>
+__device__ __forceinline__ float pick(float a, float b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); }
+
+// Extreme over aligned segments of `lanes` lanes (8, 16, 32 or 64).
+template <bool MAX>
+__device__ __forceinline__ float lanes_extreme(float x, int lanes)
+{
+    x = pick<MAX>(x, dpp_mov<0xB1>(x));   // quad_perm [1,0,3,2]
+    x = pick<MAX>(x, dpp_mov<0x4E>(x));   // quad_perm [2,3,0,1]
+    x = pick<MAX>(x, dpp_mov<0x141>(x));  // row_half_mirror
+    if (lanes >= 16) x = pick<MAX>(x, dpp_mov<0x140>(x));  // row_mirror
+    if (lanes >= 32) {
+        const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = pick<MAX>(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    }
+    if (lanes >= 64) {
+        const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = pick<MAX>(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    }
+    return x;
+}
+
+// rint(RN(x / s)) for a finite normal s > 0 and |x / s| < 128, from rc
+// within two ulps of 1 / s; sets `slow` when the result is not certain.
+__device__ __forceinline__ float rint_quot(float x, float s, float rc, bool& slow)
+{
+    const float q0 = x * rc;
+    const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, s, x), rc, q0);
+    const float r = rintf(q1);
+    slow = slow || !(__builtin_fabsf(q1 - r) <= 0.5f - 0x1p-16f);
+    return r;
+}
+
+// Group state of one row: the group's min / max and the lane's codes.
+template <int P>
+struct QRow {
+    float mn, mx, s;
+    int z;
+    int q[P];
+    bool slow;
+};
+
+// Quantise the lane's P values x (channels P * lane + p); the group is the
+// aligned segment of g / P lanes.  bits is 4 or 6.
+template <int P>
+__device__ __forceinline__ void quantize_fast(const float (&x)[P], int g, int bits, QRow<P>& o)
+{
+    const int qmax = (1 << bits) - 1;
+    const float fq = (float)qmax;
+    const float C = bits == 6 ? 0x1.041042p-6f : 0x1.111112p-4f;  // RN(1/63), RN(1/15)
+    float mn = x[0], mx = x[0];
+#pragma unroll
+    for (int p = 1; p < P; p++) {
+        mn = pick<false>(mn, x[p]);
+        mx = pick<true>(mx, x[p]);
+    }
+    mn = lanes_extreme<false>(mn, g / P);
+    mx = lanes_extreme<true>(mx, g / P);
+    const float lo = mn < 0.0f ? mn : 0.0f;
+    const float hi = mx > 0.0f ? mx : 0.0f;
+    const float r = hi - lo;
+    const float s0 = r * C;
+    const float s = __builtin_fmaf(__builtin_fmaf(-s0, fq, r), C, s0);
+    const float rc = __builtin_amdgcn_rcpf(s);
+    bool slow = !(s >= 0x1p-126f && s <= 0x1.fffffep127f);
+    const float zf = rint_quot(-lo, s, rc, slow);
+    int z = (int)zf;
+    z = z < 0 ? 0 : (z > qmax ? qmax : z);
+#pragma unroll
+    for (int p = 0; p < P; p++) {
+        int q = (int)rint_quot(x[p], s, rc, slow) + z;
+        o.q[p] = q < 0 ? 0 : (q > qmax ? qmax : q);
+    }
+    o.mn = mn;
+    o.mx = mx;
+    o.s = s;
+    o.z = z;
+    o.slow = slow;
+    if (mn == mx) {  // a constant group c: (c, 0, 1) | (-c, 1, 0) | (0, 0, 0)
+        o.slow = false;
+        o.s = mn > 0.0f ? mn : (mn < 0.0f ? -mn : 0.0f);
+        o.z = mn < 0.0f ? 1 : 0;
+#pragma unroll
+        for (int p = 0; p < P; p++) o.q[p] = mn > 0.0f ? 1 : 0;
+    }
+}
+
+// The same with correctly rounded division throughout, for flagged lanes.
+template <int P>
+__device__ __forceinline__ void quantize_exact(const float (&x)[P], int bits, QRow<P>& o)
+{
+    const int qmax = (1 << bits) - 1;
+    const float lo = o.mn < 0.0f ? o.mn : 0.0f;
+    const float hi = o.mx > 0.0f ? o.mx : 0.0f;
+    const float s = (hi - lo) / (float)qmax;
+    int z = (int)rintf(-lo / s);
+    z = z < 0 ? 0 : (z > qmax ? qmax : z);
+#pragma unroll
+    for (int p = 0; p < P; p++) {
+        int q = (int)rintf(x[p] / s) + z;
+        o.q[p] = q < 0 ? 0 : (q > qmax ? qmax : q);
+    }
+    o.s = s;
+    o.z = z;
+    o.slow = false;
+}
+
+// NV values of NB bits (low bits of v, higher bits ignored) as NW words,
+// LSB first.
+template <int NB, int NV, int NW>
+__device__ __forceinline__ void pack_values(const uint32_t (&v)[NV], uint32_t (&w)[NW])
+{
+    static_assert(NB * NV == 32 * NW, "whole words");
+    uint64_t acc = 0;
+    int nacc = 0, o = 0;
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+        acc |= (uint64_t)(v[i] & ((1u << NB) - 1u)) << nacc;
+        nacc += NB;
+        if (nacc >= 32) {
+            w[o++] = (uint32_t)acc;
+            acc >>= 32;
+            nacc -= 32;
+        }
+    }
+}
+
 // Word w of a bitstream of `bits`-bit fields, field i read by get(i) for
 // i in [0, n); fields outside [lo, hi) count as zero.
 template <typename Get>

@@ -80,6 +80,68 @@ def test_append_special_groups_bit_exact():
         assert pair.pool_equal(), pair.first_pool_mismatch()
 
 
+def _tie_rows(D, g, bits, rng):
+    """fp32 rows whose groups have power-of-two scales, so that -lo / s and
+    x / s land exactly on half-integers (and a few ulps away from them),
+    plus groups of subnormal values and groups whose range overflows."""
+    qmax = (1 << bits) - 1
+    rows = []
+    for e in (-3, 0, 5):
+        s = 2.0 ** e
+        row = np.zeros(D, np.float32)
+        for g0 in range(0, D, g):
+            k = rng.integers(-qmax // 2, qmax // 2, g).astype(np.float64) + 0.5
+            vals = (k * s).astype(np.float32)
+            vals[0], vals[1] = -(qmax / 2) * s, (qmax / 2) * s  # range qmax * s: the scale is s, -lo / s a tie
+            near = rng.random(g) < 0.3
+            vals[2:][near[2:]] = np.nextafter(vals[2:][near[2:]], np.float32(np.inf) * rng.choice([-1, 1], near[2:].sum()))
+            row[g0:g0 + g] = vals
+        rows.append(row)
+    rows.append((rng.standard_normal(D) * 1e-40).astype(np.float32))      # subnormal scales
+    big = rng.uniform(-3.3e38, 3.3e38, D).astype(np.float32)
+    big[::g] = -3.3e38
+    big[1::g] = 3.3e38                                                     # hi - lo overflows
+    rows.append(big)
+    return rows
+
+
+@pytest.mark.parametrize("D,g", [(128, 64), (128, 32), (128, 16), (64, 32), (64, 16)])
+def test_append_quotient_ties_bit_exact(D, g):
+    """Half-integer quotients (exact ties and their neighbours), subnormal
+    scales and overflowing ranges: the lanes the fast quantiser defers to
+    correctly rounded division."""
+    rng = np.random.default_rng(31)
+    for kb, vb in [(6, 4), (4, 6), (6, 6)]:
+        rows = _tie_rows(D, g, kb, rng) + _tie_rows(D, g, vb, rng)
+        x = torch.tensor(np.stack(rows))[:, None, :]
+        n = x.shape[0]
+        pair = Pair(D, g, kb, vb, 1, 1)
+        say("append quotient ties", D, g, kb, vb)
+        pair.append(x, -x, [0, n], [0], np.array([[0]], np.int32))
+        assert pair.pool_equal(), pair.first_pool_mismatch()
+
+
+def test_append_unaligned_inputs_bit_exact():
+    """K and V views one element off their allocation's alignment."""
+    D, g, Hkv = 128, 64, 2
+    lens = [70, 3]
+    rng = np.random.default_rng(32)
+    bt, nblk = block_tables([n + 64 for n in lens], rng)
+    for dtype in ("bf16", "f32"):
+        pair = Pair(D, g, 6, 4, Hkv, nblk)
+        k, v = inputs.kv_rows(33, 0, sum(lens), Hkv, D, dtype=dtype)
+        kk = torch.empty(k.numel() + 1, dtype=k.dtype, device="cuda")[1:].view(k.shape)
+        vv = torch.empty(v.numel() + 1, dtype=v.dtype, device="cuda")[1:].view(v.shape)
+        kk.copy_(k.cuda())
+        vv.copy_(v.cuda())
+        cu = np.array([0, lens[0], sum(lens)], np.int32)
+        say("append unaligned", dtype)
+        lkv.quant_append(pair.gpu, kk, vv, torch.tensor(cu).cuda(), torch.zeros(2, dtype=torch.int32).cuda(),
+                         torch.tensor(bt).cuda(), max(lens))
+        O.append(pair.ref, to_f32_host(k), to_f32_host(v), cu, np.zeros(2, np.int32), bt)
+        assert pair.pool_equal(), pair.first_pool_mismatch()
+
+
 def _decode_case(fmt, G, qdtype, lens, tau, split, seed=5, Hkv=2, nseg=1):
     D, g, kb, vb = fmt
     rng = np.random.default_rng(seed)
