@@ -178,8 +178,6 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
 // staged per slot (a lane's P codes in one 16-bit value), V codes channel-
 // major with a row pitch of 68 bytes (the transposed stores of a wave hit
 // distinct banks).
-constexpr int VPITCH = 68;
-
 template <int DT, int P>
 __device__ __forceinline__ void load_vals(const void* p, int64_t i, uint32_t (&u)[P])
 {
@@ -221,41 +219,6 @@ __device__ __forceinline__ void pack_k_rows(const uint16_t (*kq)[64], uint8_t* c
     for (int idx = threadIdx.x; idx < (s1 - s0) * G; idx += blockDim.x) {
         const int slot = s0 + idx / G;
         pack_k_group<NB, NV, NW>(kq[slot], idx % G, (uint32_t*)(ch + f.off_kc + slot * f.krow));
-    }
-}
-
-// V words of channel rows: group m of NV slots -> NW words; only the words
-// holding bits of slots [s0, s1) are written, shared words merged with
-// atomics.
-template <int NB, int NV, int NW, int D>
-__device__ __forceinline__ void pack_v_rows(const uint8_t (*vt)[VPITCH], uint8_t* ch, const Fmt& f, int s0, int s1)
-{
-    const int m0 = s0 / NV, m1 = (s1 - 1) / NV;
-    const int ng = m1 - m0 + 1;
-    for (int idx = threadIdx.x; idx < D * ng; idx += blockDim.x) {
-        const int d = idx / ng, m = m0 + idx % ng;
-        uint32_t v[NV], w[NW];
-        const uint32_t* src = (const uint32_t*)(vt[d] + m * NV);
-#pragma unroll
-        for (int i = 0; i < NV / 4; i++) {
-            const uint32_t t = src[i];
-            v[4 * i] = t & 0xFFu;
-            v[4 * i + 1] = (t >> 8) & 0xFFu;
-            v[4 * i + 2] = (t >> 16) & 0xFFu;
-            v[4 * i + 3] = t >> 24;
-        }
-        pack_values<NB, NV, NW>(v, w);
-        uint32_t* row = (uint32_t*)(ch + f.off_vc + d * f.vrow) + m * NW;
-#pragma unroll
-        for (int i = 0; i < NW; i++) {
-            const uint32_t mask = field_mask(m * NW + i, NB, s0, s1);
-            if (mask == 0xFFFFFFFFu) {
-                row[i] = w[i];
-            } else if (mask != 0u) {
-                atomicAnd(row + i, ~mask);
-                atomicOr(row + i, w[i] & mask);
-            }
-        }
     }
 }
 
@@ -341,8 +304,8 @@ __global__ __launch_bounds__(256) void append_quant_kernel(AppendArgs a)
     else if (knb == 8) pack_k_rows<8, 4, 1>(kq, ch, f, s0, s1);
     else if (knb == 6) pack_k_rows<6, 16, 3>(kq, ch, f, s0, s1);
     else pack_k_rows<4, 8, 1>(kq, ch, f, s0, s1);
-    if (f.vb == 6) pack_v_rows<6, 16, 3, D>(vt, ch, f, s0, s1);
-    else pack_v_rows<4, 8, 1, D>(vt, ch, f, s0, s1);
+    if (f.vb == 6) pack_v_rows<6, 16, 3, D>(vt, ch, f.off_vc, f.vrow, s0, s1);
+    else pack_v_rows<4, 8, 1, D>(vt, ch, f.off_vc, f.vrow, s0, s1);
 }
 
 template <int D>

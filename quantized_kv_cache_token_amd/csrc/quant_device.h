@@ -246,6 +246,47 @@ __device__ __forceinline__ uint32_t field_mask(int w, int bits, int lo, int hi)
     return (uint32_t)m;
 }
 
+// Channel-major staging of V codes: one byte per (channel, slot), rows 68
+// bytes apart, so that a wave storing one slot of 64 consecutive channels
+// hits distinct banks.
+constexpr int VPITCH = 68;
+
+// V words of channel rows: group m of NV slots -> NW words; only the words
+// holding bits of slots [s0, s1) are written, shared words merged with
+// atomics.
+template <int NB, int NV, int NW, int D>
+__device__ __forceinline__ void pack_v_rows(const uint8_t (*vt)[VPITCH], uint8_t* ch, int off_vc, int vrow, int s0,
+                                            int s1)
+{
+    const int m0 = s0 / NV, m1 = (s1 - 1) / NV;
+    const int ng = m1 - m0 + 1;
+    for (int idx = threadIdx.x; idx < D * ng; idx += blockDim.x) {
+        const int d = idx / ng, m = m0 + idx % ng;
+        uint32_t v[NV], w[NW];
+        const uint32_t* src = (const uint32_t*)(vt[d] + m * NV);
+#pragma unroll
+        for (int i = 0; i < NV / 4; i++) {
+            const uint32_t t = src[i];
+            v[4 * i] = t & 0xFFu;
+            v[4 * i + 1] = (t >> 8) & 0xFFu;
+            v[4 * i + 2] = (t >> 16) & 0xFFu;
+            v[4 * i + 3] = t >> 24;
+        }
+        pack_values<NB, NV, NW>(v, w);
+        uint32_t* row = (uint32_t*)(ch + off_vc + d * vrow) + m * NW;
+#pragma unroll
+        for (int i = 0; i < NW; i++) {
+            const uint32_t mask = field_mask(m * NW + i, NB, s0, s1);
+            if (mask == 0xFFFFFFFFu) {
+                row[i] = w[i];
+            } else if (mask != 0u) {
+                atomicAnd(row + i, ~mask);
+                atomicOr(row + i, w[i] & mask);
+            }
+        }
+    }
+}
+
 // Field i of a bitstream held in global or shared memory (32-bit words).
 __device__ __forceinline__ uint32_t get_field(const uint32_t* words, int i, int bits)
 {

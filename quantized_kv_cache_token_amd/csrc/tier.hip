@@ -213,22 +213,10 @@ __device__ __forceinline__ uint8_t* dst_chunk(const MoveDst& d, int b, int pos, 
 // codes into chunk dch; words shared with slots outside the range are
 // merged with atomics.
 template <int D>
-__device__ __forceinline__ void flush_block(const Fmt& fd, uint8_t* dch, const uint8_t (*st)[D], int slo, int shi)
+__device__ __forceinline__ void flush_block(const Fmt& fd, uint8_t* dch, const uint8_t (*st)[VPITCH], int slo, int shi)
 {
-    const int vb = fd.vb;
-    const int w0 = slo * vb / 32, w1 = (shi * vb - 1) / 32 + 1, nw = w1 - w0;
-    for (int i = threadIdx.x; i < D * nw; i += blockDim.x) {
-        const int d = i / nw, w = w0 + i % nw;
-        const uint32_t mask = field_mask(w, vb, slo, shi);
-        const uint32_t word = pack_word(w, vb, slo, shi, [&](int s) { return (uint32_t)st[s][d]; });
-        uint32_t* dst = (uint32_t*)(dch + fd.off_vc + d * fd.vrow) + w;
-        if (mask == 0xFFFFFFFFu) {
-            *dst = word;
-        } else {
-            atomicAnd(dst, ~mask);
-            atomicOr(dst, word & mask);
-        }
-    }
+    if (fd.vb == 6) pack_v_rows<6, 16, 3, D>(st, dch, fd.off_vc, fd.vrow, slo, shi);
+    else pack_v_rows<4, 8, 1, D>(st, dch, fd.off_vc, fd.vrow, slo, shi);
 }
 
 // Where slot s of a source chunk goes: its segment (0 HIGH, 1 MID, -1
@@ -256,46 +244,60 @@ __device__ __forceinline__ int slot_dest(int s, uint64_t mk0, uint64_t mk1, int 
 }
 
 // V codes of survivor ranks [r0, r1) of one segment, copied at the source
-// width into staged slots r + sh.
+// width into staged slots r + sh of the channel-major stage.
 template <int D>
-__device__ __forceinline__ void copy_codes(uint8_t (*st)[D], const uint8_t* src_of, const uint32_t* vsrc, int vrow_w,
-                                           int vb, int r0, int r1, int sh)
+__device__ __forceinline__ void copy_codes(uint8_t (*st)[VPITCH], const uint8_t* src_of, const uint32_t* vsrc,
+                                           int vrow_w, int vb, int r0, int r1, int sh)
 {
     const int cnt = (r1 - r0) * D;
     for (int i = threadIdx.x; i < cnt; i += 256) {
         const int r = r0 + i / D, d = i % D;
-        st[r + sh][d] = (uint8_t)get_field(vsrc + d * vrow_w, src_of[r], vb);
+        st[d][r + sh] = (uint8_t)get_field(vsrc + d * vrow_w, src_of[r], vb);
     }
 }
 
 // MID survivor ranks [r0, r1) from 6-bit V: dequantised in fp32 and
-// requantised at the destination width, one token per wave; codes into
-// staged slots r + sh, scales and zeros straight to the destination.
+// requantised at the destination width, four tokens per wave at a time
+// (lane: channels P * lane + p); codes into staged slots r + sh, scales and
+// zeros straight to the destination.
 template <int D>
-__device__ __forceinline__ void requant_codes(uint8_t (*st)[D], const uint8_t* src_of, const uint32_t* vsrc,
+__device__ __forceinline__ void requant_codes(uint8_t (*st)[VPITCH], const uint8_t* src_of, const uint32_t* vsrc,
                                               int vrow_w, const Fmt& fs, const Fmt& fm, const float* m_vs,
                                               const uint8_t* m_vz, int pos, uint8_t* dA, uint8_t* dB, int r0, int r1,
                                               int sh)
 {
-    constexpr int VPL = D / 64;
+    constexpr int P = D / 64, T = 4;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int r = r0 + wave; r < r1; r += 4) {
-        const int s = src_of[r];
-        const int P = pos + r;
-        uint8_t* dch = P / BT == pos / BT ? dA : dB;
+    for (int rb = r0 + T * wave; rb < r1; rb += 4 * T) {
+        float x[T][P];
+        QRow<P> q[T];
 #pragma unroll
-        for (int i = 0; i < VPL; i++) {
-            const int d = lane + 64 * i;
-            const int gi = d / fs.g;
-            const uint32_t code = get_field(vsrc + d * vrow_w, s, fs.vb);
-            const float x = (float)((int)code - (int)m_vz[gi * BT + s]) * m_vs[gi * BT + s];
-            float s4;
-            int z4;
-            const int c4 = quantize_lane(x, fm.g, fm.vb, &s4, &z4);
-            st[r + sh][d] = (uint8_t)c4;
-            if (d % fm.g == 0) {
-                ((float*)(dch + fm.off_vs))[gi * BT + P % BT] = s4;
-                dch[fm.off_vz + gi * BT + P % BT] = (uint8_t)z4;
+        for (int t = 0; t < T; t++) {
+            const int s = src_of[min(rb + t, r1 - 1)];
+#pragma unroll
+            for (int p = 0; p < P; p++) {
+                const int d = P * lane + p, gi = d / fs.g;
+                const uint32_t code = get_field(vsrc + d * vrow_w, s, fs.vb);
+                x[t][p] = (float)((int)code - (int)m_vz[gi * BT + s]) * m_vs[gi * BT + s];  // one fp32 rounding
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < T; t++) quantize_fast<P>(x[t], fm.g, fm.vb, q[t]);
+#pragma unroll
+        for (int t = 0; t < T; t++)
+            if (q[t].slow) quantize_exact<P>(x[t], fm.vb, q[t]);
+#pragma unroll
+        for (int t = 0; t < T; t++) {
+            const int r = rb + t;
+            if (r >= r1) break;
+            const int P_ = pos + r;
+            uint8_t* dch = P_ / BT == pos / BT ? dA : dB;
+#pragma unroll
+            for (int p = 0; p < P; p++) st[P * lane + p][r + sh] = (uint8_t)q[t].q[p];
+            if ((P * lane) % fm.g == 0) {
+                const int gi = P * lane / fm.g;
+                ((float*)(dch + fm.off_vs))[gi * BT + P_ % BT] = q[t].s;
+                dch[fm.off_vz + gi * BT + P_ % BT] = (uint8_t)q[t].z;
             }
         }
     }
@@ -306,7 +308,7 @@ __global__ __launch_bounds__(256) void tier_move_kernel(MoveArgs a)
 {
     __shared__ uint32_t vsrc[D * 12 + 4];        // the V section (up to 6-bit), plus slack for straddling reads
     __shared__ uint32_t meta[MOVE_META / 4];     // K scales, V scales, K zeros, V zeros
-    __shared__ uint8_t stage[2][BT][D];          // destination codes of the current HIGH / MID block
+    __shared__ uint8_t stage[2][D][VPITCH];      // destination codes of the current HIGH / MID block
     __shared__ uint8_t src_of[4][2][BT];         // per wave: source slot of each survivor rank
 
     const int si = blockIdx.z % a.nsrc, b = blockIdx.z / a.nsrc, kvh = blockIdx.y;
