@@ -222,6 +222,64 @@ __device__ __forceinline__ void pack_k_rows(const uint16_t (*kq)[64], uint8_t* c
     }
 }
 
+// Rows wave + 4 * (k0 + k), k < CHN, of one chunk: their loads are issued
+// together, then they are quantised with their reductions interleaved (rows
+// past the end reload the last row and are not stored).
+template <int D, int DT, int CHN>
+__device__ __forceinline__ void quant_rows(const AppendArgs& a, int k0, int wave, int lane, int nrows, int s0,
+                                           int row0, int lb, int sp, int kvh, uint8_t* ch, uint16_t (*kq)[64],
+                                           uint8_t (*vt)[VPITCH])
+{
+    constexpr int P = D / 64;
+    const Fmt& f = a.f;
+    uint32_t u[CHN][P];
+#pragma unroll
+    for (int k = 0; k < CHN; k++) {
+        const int r = min(wave + 4 * (k0 + k), nrows - 1);
+        const int slot = s0 + (r >> 1);
+        const int64_t in_row = (int64_t)(row0 + (lb * BT + slot - sp)) * f.H + kvh;
+        load_vals<DT, P>((r & 1) ? a.v : a.k, in_row * D + P * lane, u[k]);
+    }
+    QRow<P> q[CHN];
+#pragma unroll
+    for (int k = 0; k < CHN; k++) {
+        const int r = wave + 4 * (k0 + k);
+        float x[P];
+#pragma unroll
+        for (int p = 0; p < P; p++) x[p] = raw_value<DT>(u[k][p]);
+        quantize_fast<P>(x, f.g, (r & 1) ? f.vb : f.kb, q[k]);
+    }
+    // lanes whose quotient sat too close to a half-integer
+#pragma unroll
+    for (int k = 0; k < CHN; k++) {
+        if (q[k].slow) {
+            const int r = wave + 4 * (k0 + k);
+            float x[P];
+#pragma unroll
+            for (int p = 0; p < P; p++) x[p] = raw_value<DT>(u[k][p]);
+            quantize_exact<P>(x, (r & 1) ? f.vb : f.kb, q[k]);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < CHN; k++) {
+        const int r = wave + 4 * (k0 + k);
+        if (r >= nrows) break;
+        const int slot = s0 + (r >> 1);
+        const bool is_v = r & 1;
+        if (is_v) {
+#pragma unroll
+            for (int p = 0; p < P; p++) vt[P * lane + p][slot] = (uint8_t)q[k].q[p];
+        } else {
+            kq[slot][lane] = (uint16_t)(P == 2 ? (q[k].q[0] | (q[k].q[1] << f.kb)) : q[k].q[0]);
+        }
+        if ((P * lane) % f.g == 0) {
+            const int gi = P * lane / f.g;
+            ((float*)(ch + (is_v ? f.off_vs : f.off_ks)))[gi * BT + slot] = q[k].s;
+            ch[(is_v ? f.off_vz : f.off_kz) + gi * BT + slot] = (uint8_t)q[k].z;
+        }
+    }
+}
+
 template <int D, int DT>
 __global__ __launch_bounds__(256) void append_quant_kernel(AppendArgs a)
 {
@@ -248,54 +306,13 @@ __global__ __launch_bounds__(256) void append_quant_kernel(AppendArgs a)
 
     __shared__ uint16_t kq[BT][64];
     __shared__ uint8_t vt[D][VPITCH];
+    if (nrows <= 4) {  // at most one row per wave (a decode step): no batch of duplicates
+        if (wave < nrows) quant_rows<D, DT, 1>(a, 0, wave, lane, nrows, s0, row0, lb, sp, kvh, ch, kq, vt);
+    } else {
 #pragma unroll 1
-    for (int k0 = 0; k0 < MAXR; k0 += CH) {
-        if (wave + 4 * k0 >= nrows) break;
-        uint32_t u[CH][P];
-#pragma unroll
-        for (int k = 0; k < CH; k++) {
-            const int r = min(wave + 4 * (k0 + k), nrows - 1);
-            const int slot = s0 + (r >> 1);
-            const int64_t in_row = (int64_t)(row0 + (lb * BT + slot - sp)) * f.H + kvh;
-            load_vals<DT, P>((r & 1) ? a.v : a.k, in_row * D + P * lane, u[k]);
-        }
-        QRow<P> q[CH];
-#pragma unroll
-        for (int k = 0; k < CH; k++) {
-            const int r = wave + 4 * (k0 + k);
-            float x[P];
-#pragma unroll
-            for (int p = 0; p < P; p++) x[p] = raw_value<DT>(u[k][p]);
-            quantize_fast<P>(x, f.g, (r & 1) ? f.vb : f.kb, q[k]);
-        }
-        // lanes whose quotient sat too close to a half-integer
-#pragma unroll
-        for (int k = 0; k < CH; k++) {
-            if (q[k].slow) {
-                const int r = wave + 4 * (k0 + k);
-                float x[P];
-#pragma unroll
-                for (int p = 0; p < P; p++) x[p] = raw_value<DT>(u[k][p]);
-                quantize_exact<P>(x, (r & 1) ? f.vb : f.kb, q[k]);
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < CH; k++) {
-            const int r = wave + 4 * (k0 + k);
-            if (r >= nrows) break;
-            const int slot = s0 + (r >> 1);
-            const bool is_v = r & 1;
-            if (is_v) {
-#pragma unroll
-                for (int p = 0; p < P; p++) vt[P * lane + p][slot] = (uint8_t)q[k].q[p];
-            } else {
-                kq[slot][lane] = (uint16_t)(P == 2 ? (q[k].q[0] | (q[k].q[1] << f.kb)) : q[k].q[0]);
-            }
-            if ((P * lane) % f.g == 0) {
-                const int gi = P * lane / f.g;
-                ((float*)(ch + (is_v ? f.off_vs : f.off_ks)))[gi * BT + slot] = q[k].s;
-                ch[(is_v ? f.off_vz : f.off_kz) + gi * BT + slot] = (uint8_t)q[k].z;
-            }
+        for (int k0 = 0; k0 < MAXR; k0 += CH) {
+            if (wave + 4 * k0 >= nrows) break;
+            quant_rows<D, DT, CH>(a, k0, wave, lane, nrows, s0, row0, lb, sp, kvh, ch, kq, vt);
         }
     }
     __syncthreads();
