@@ -220,6 +220,31 @@ def decode(caches, block_tables, seq_lens, q: np.ndarray, sm_scale: float,
     return (out, skip) if want_skip else out
 
 
+def decode_multi(caches, block_tables, seq_lens, q: np.ndarray, sm_scale: float,
+                 tau_low: float = 0.0, split_tokens: int = 0):
+    """Attention of T query tokens per sequence over the packed cache, with a
+    causal mask (the queries of a chunked prefill, or tokens to verify).
+
+    q: fp32 [B][T][Hq][D]; seq_lens count every cached token including the T
+    new ones, which are the last T tokens of the first segment.  Query token
+    i of sequence b sits at position L - T + i of that segment and attends to
+    every token of the other segments and to the first segment's tokens
+    0 .. L - T + i.  Each query token is therefore one decode query (decode
+    above) over that causal prefix, with the same split size and sparse-V
+    rule.  Returns fp64 [B][T][Hq][D]."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    B, T, Hq, D = q.shape
+    bts = [_i32(t) for t in block_tables]
+    lens = [_i32(n) for n in seq_lens]
+    if T < 1 or np.any(lens[0] < T):
+        raise ValueError("every sequence must hold its T query tokens")
+    ebts = [np.repeat(bt, T, axis=0) for bt in bts]                  # entry (b, i): sequence b's table
+    elens = [np.repeat(ln, T) for ln in lens]
+    elens[0] = elens[0] - (T - 1) + np.tile(np.arange(T, dtype=np.int32), B)  # causal prefix in segment 0
+    out = decode(caches, ebts, elens, q.reshape(B * T, Hq, D), sm_scale, tau_low, split_tokens)
+    return out.reshape(B, T, Hq, D)
+
+
 def tier_update(src: Cache, src_bt, src_lens, scores: np.ndarray, tau_low: float, tau_high: float,
                 dst_h: Cache, h_bt, dst_m: Cache, m_bt):
     """Returns (tiers uint8 [B][stride], n_high int32 [B], n_mid int32 [B])."""
