@@ -5,6 +5,8 @@
  *   lkv_quant_append  quantise new K/V rows and bit-pack them into the cache
  *   lkv_decode_attn   attention of the current decode queries against the
  *                     packed cache (split over the token axis, then merged)
+ *   lkv_decode_attn_multi  the same for several query tokens per sequence,
+ *                     with a causal mask
  *   lkv_tier_update   attention-aware tiers: HIGH keeps 6-bit V, MID gets
  *                     4-bit V, LOW is evicted
  *   lkv_retier        the same tiers applied again to a tiered cache as its
@@ -153,6 +155,27 @@ int lkv_decode_attn(const lkv_cache* segs, const lkv_view* views, int32_t nseg,
                     const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
                     float sm_scale, float tau_low, int32_t split_tokens,
                     float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Attention of several query tokens per sequence over the packed cache,
+ * with a causal mask: the queries of a chunked prefill, or draft tokens to
+ * verify.  The TurboQuant page states that the quantised cache stacks with
+ * FlashAttention-style attention; this is that computation over it.
+ * q_per_seq = T query tokens per sequence; their K and V rows are already
+ * appended and are the last T tokens of the first segment (seq_lens count
+ * them).  Query token i of sequence b attends to that segment's tokens
+ * 0 .. L_b - T + i and to every token of the other segments: each query
+ * token is one lkv_decode_attn query over its causal prefix, with the same
+ * split size and sparse-V rule.
+ * q          [batch][T][num_q_heads][head_dim] in q_dtype
+ * out        [batch][T][num_q_heads][head_dim] fp32
+ * split_tokens  0 = lkv_decode_plan(..., batch * T, ...)
+ * workspace  lkv_decode_workspace_bytes(..., batch * T, ...) bytes
+ * views[0].max_len must be at least T; a sequence shorter than T gives
+ * zero rows for the queries that see no token.  T = 1 is lkv_decode_attn. */
+int lkv_decode_attn_multi(const lkv_cache* segs, const lkv_view* views, int32_t nseg, const void* q,
+                          int32_t q_dtype, int32_t batch, int32_t q_per_seq, int32_t num_q_heads, float sm_scale,
+                          float tau_low, int32_t split_tokens, float* out, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /* The two stages of lkv_decode_attn, for callers that schedule them apart
  * (lkv_decode_attn is exactly lkv_decode_split followed by

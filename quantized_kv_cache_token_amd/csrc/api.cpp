@@ -83,10 +83,12 @@ static int32_t score_cols(const lkv_view* views, int32_t nseg)
     return n;
 }
 
-// Split stage; scores (optional) receives the base-2 score rows.
+// Split stage; scores (optional) receives the base-2 score rows.  batch
+// counts grid entries: sequences times q_per_seq query tokens.
 static int split_impl(const lkv_cache* segs, const lkv_view* views, int32_t nseg, const void* q, int32_t q_dtype,
                       int32_t batch, int32_t num_q_heads, float sm_scale, float tau_low, int32_t split_tokens,
-                      void* workspace, size_t workspace_bytes, void* stream, float* scores, int32_t score_stride);
+                      void* workspace, size_t workspace_bytes, void* stream, float* scores, int32_t score_stride,
+                      int32_t q_per_seq = 1);
 
 // Merge stage; ml (optional) receives (M, 1 / L) per (sequence, head).
 static int combine_impl(const lkv_cache* segs, const lkv_view* views, int32_t nseg, int32_t batch,
@@ -203,7 +205,8 @@ namespace lkv {
 
 static int split_impl(const lkv_cache* segs, const lkv_view* views, int32_t nseg, const void* q, int32_t q_dtype,
                       int32_t batch, int32_t num_q_heads, float sm_scale, float tau_low, int32_t split_tokens,
-                      void* workspace, size_t workspace_bytes, void* stream, float* scores, int32_t score_stride)
+                      void* workspace, size_t workspace_bytes, void* stream, float* scores, int32_t score_stride,
+                      int32_t q_per_seq)
 {
     Fmt f[2];
     const int st = check_decode(segs, views, nseg, batch, num_q_heads, f);
@@ -230,6 +233,8 @@ static int split_impl(const lkv_cache* segs, const lkv_view* views, int32_t nseg
         a[s].scores = scores;
         a[s].score_stride = score_stride;
         a[s].tok_base = s == 0 ? 0 : (views[0].max_len + BT - 1) / BT * BT;
+        a[s].q_per_seq = q_per_seq;
+        a[s].causal = q_per_seq > 1 && s == 0;  // the new tokens are the first segment's tail
     }
     hipError_t e;
     if (nseg == 2 && launch_decode_split_mfma_tiered(a[0], a[1], q, q_dtype, batch, num_q_heads, sm_scale, tau_low,
@@ -351,6 +356,27 @@ int lkv_decode_attn(const lkv_cache* segs, const lkv_view* views, int32_t nseg, 
                               workspace, workspace_bytes, stream);
     if (st != LKV_OK) return st;
     return lkv_decode_combine(segs, views, nseg, batch, num_q_heads, split_tokens, out, workspace, workspace_bytes,
+                              stream);
+}
+
+int lkv_decode_attn_multi(const lkv_cache* segs, const lkv_view* views, int32_t nseg, const void* q,
+                          int32_t q_dtype, int32_t batch, int32_t q_per_seq, int32_t num_q_heads, float sm_scale,
+                          float tau_low, int32_t split_tokens, float* out, void* workspace, size_t workspace_bytes,
+                          void* stream)
+{
+    if (q_per_seq < 1 || (int64_t)batch * q_per_seq > INT32_MAX) return LKV_EINVAL;
+    const int32_t entries = batch * q_per_seq;
+    for (int s = 0; s < nseg && views; s++)
+        if (views[s].max_len < (s == 0 ? q_per_seq : 0) && batch > 0) return LKV_EINVAL;
+    if (split_tokens == 0) {
+        const int st = lkv_decode_plan(segs, views, nseg, entries, num_q_heads, &split_tokens);
+        if (st != LKV_OK) return st;
+    }
+    if (batch > 0 && !out) return LKV_EINVAL;
+    const int st = split_impl(segs, views, nseg, q, q_dtype, entries, num_q_heads, sm_scale, tau_low, split_tokens,
+                              workspace, workspace_bytes, stream, nullptr, 0, q_per_seq);
+    if (st != LKV_OK) return st;
+    return lkv_decode_combine(segs, views, nseg, entries, num_q_heads, split_tokens, out, workspace, workspace_bytes,
                               stream);
 }
 

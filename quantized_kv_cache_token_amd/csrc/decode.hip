@@ -68,7 +68,7 @@ __global__ __launch_bounds__(64) void split_valu_kernel(SplitArgs a)
     const Fmt& f = sg.f;
     const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x;
-    const int len = max(0, min(sg.seq_lens[b], sg.max_blocks * BT));  // out-of-contract lengths are clamped
+    const int len = max(0, min(entry_len(sg, b), sg.max_blocks * BT));  // out-of-contract lengths are clamped
     const int t0 = sp * a.split_tokens;
     const int t1 = min(t0 + a.split_tokens, len);
     if (t1 <= t0) {  // a split past the end: only (m, L) = (-inf, 0), its o row is never read
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(64) void split_valu_kernel(SplitArgs a)
     }
 
     for (int bs = t0; bs < t1; bs += BT) {
-        const int64_t blk = sg.block_table[(int64_t)b * sg.max_blocks + bs / BT];
+        const int64_t blk = sg.block_table[(int64_t)entry_seq(sg, b) * sg.max_blocks + bs / BT];
         const uint8_t* ch = sg.pool + (blk * f.H + kvh) * f.chunk;
         const int nlive = min(BT, t1 - bs);
         const bool live = lane < nlive;

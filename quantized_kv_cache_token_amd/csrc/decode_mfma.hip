@@ -495,9 +495,12 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
     const int t0 = sp * a.split_tokens;
     // the split's block-table entries (at most 64, one per lane) do not
     // depend on the length: they are requested together with it
-    const int32_t* bt = sg.block_table + (int64_t)b * sg.max_blocks + t0 / BT;
+    // (the sequence and length are uniform: computed before the lane-dependent
+    // load, so that they stay in scalar registers)
+    const int seq = entry_seq(sg, b);
+    const int len = max(0, min(entry_len(sg, b), sg.max_blocks * BT));
+    const int32_t* bt = sg.block_table + (int64_t)seq * sg.max_blocks + t0 / BT;
     const int bt_lane = lane < min(64, sg.max_blocks - t0 / BT) ? bt[lane] : 0;
-    const int len = max(0, min(sg.seq_lens[b], sg.max_blocks * BT));
     asm volatile("" ::: "memory");  // both loads are issued before either is waited for
     const int t1 = min(t0 + a.split_tokens, len);
     if (t1 <= t0) {  // a split past the end: only (m, L) = (-inf, 0), its o row is never read

@@ -39,7 +39,22 @@ struct SegArgs {
     float* scores;
     int32_t score_stride;
     int32_t tok_base;
+    // query tokens per sequence: grid entry e is query token e % q_per_seq of
+    // sequence e / q_per_seq; when causal (the segment holding the new
+    // tokens) that entry reads all but the q_per_seq - 1 - e % q_per_seq
+    // newest tokens
+    int32_t q_per_seq;
+    int32_t causal;
 };
+
+// Block-table row and length that grid entry e reads in segment s (the
+// length before clamping to the table).
+__device__ __forceinline__ int entry_seq(const SegArgs& s, int e) { return e / s.q_per_seq; }
+__device__ __forceinline__ int entry_len(const SegArgs& s, int e)
+{
+    const int len = s.seq_lens[e / s.q_per_seq];
+    return s.causal ? len - (s.q_per_seq - 1 - e % s.q_per_seq) : len;
+}
 
 hipError_t launch_append(const Fmt& f, uint8_t* pool, const void* k, const void* v, int dtype,
                          const int32_t* cu_new, const int32_t* start_pos, const int32_t* block_table,

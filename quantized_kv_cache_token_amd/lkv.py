@@ -45,7 +45,7 @@ EXPORTS = ["lkv_status_string", "lkv_chunk_layout", "lkv_quant_append", "lkv_dec
            "lkv_decode_workspace_bytes", "lkv_decode_attn", "lkv_decode_split", "lkv_decode_combine",
            "lkv_decode_scores_workspace_bytes", "lkv_decode_attn_scores",
            "lkv_default_thresholds", "lkv_tier_workspace_bytes", "lkv_tier_update",
-           "lkv_retier_workspace_bytes", "lkv_retier"]
+           "lkv_retier_workspace_bytes", "lkv_retier", "lkv_decode_attn_multi"]
 
 
 def lib():
@@ -75,6 +75,7 @@ def lib():
         "lkv_tier_update": ([PC, PV, P, I32, F, F, PC, P, I32, PC, P, I32, P, P, P, I32, P, C.c_size_t, V],
                             C.c_int),
         "lkv_retier_workspace_bytes": ([I32, I32, I32], I64),
+        "lkv_decode_attn_multi": ([PC, PV, I32, P, I32, I32, I32, I32, F, F, I32, P, P, C.c_size_t, V], C.c_int),
         "lkv_retier": ([PC, PV, P, I32, PC, PV, P, I32, F, F, PC, P, I32, PC, P, I32, P, P, P, P, I32, P,
                         C.c_size_t, V], C.c_int),
     }
@@ -200,6 +201,26 @@ def decode_attn(caches, views, q: torch.Tensor, sm_scale: float, tau_low: float 
     cs, vs, n = _segs(caches, views)
     _check("lkv_decode_attn", lib().lkv_decode_attn(
         cs, vs, n, _ptr(q), _DTYPE[q.dtype], B, Hq, sm_scale, tau_low, split_tokens, _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def decode_attn_multi(caches, views, q: torch.Tensor, sm_scale: float, tau_low: float = 0.0,
+                      split_tokens: int = 0, out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                      stream=None):
+    """lkv_decode_attn_multi: q [B][T][Hq][D] (fp32 or bf16), the last T
+    tokens of the first segment -> out fp32 [B][T][Hq][D], causal."""
+    B, T, Hq, D = q.shape
+    assert q.is_contiguous()
+    if split_tokens == 0:
+        split_tokens = decode_plan(caches, views, B * T, Hq)
+    if workspace is None:
+        workspace = decode_workspace(caches, views, B * T, Hq, split_tokens, q.device)
+    if out is None:
+        out = torch.empty(B, T, Hq, D, dtype=torch.float32, device=q.device)
+    cs, vs, n = _segs(caches, views)
+    _check("lkv_decode_attn_multi", lib().lkv_decode_attn_multi(
+        cs, vs, n, _ptr(q), _DTYPE[q.dtype], B, T, Hq, sm_scale, tau_low, split_tokens, _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 

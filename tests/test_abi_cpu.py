@@ -170,6 +170,24 @@ def test_retier_rejects_bad_formats():
     assert L.lkv_retier_workspace_bytes(-1, 1, 1) == lkv.EINVAL
 
 
+def test_decode_multi_rejects_bad_arguments():
+    L = lkv.lib()
+    p = C.c_void_p(0x90000)
+    cs = (lkv._Cache * 1)(_cache())
+    vs = (lkv._View * 1)(_view(max_len=1024))
+
+    def call(T=4, max_len=1024, q_dtype=lkv.BF16, ws=1 << 30):
+        v = (lkv._View * 1)(_view(max_len=max_len))
+        return L.lkv_decode_attn_multi(cs, v, 1, p, q_dtype, 8, T, 32, 0.088, 0.0, 256, p, p, ws, None)
+
+    assert call(T=0) == lkv.EINVAL
+    assert call(max_len=3) == lkv.EINVAL       # every sequence holds its T query tokens
+    assert call(q_dtype=7) == lkv.EINVAL
+    assert call(ws=100) == lkv.EINVAL          # partials for batch * T entries
+    # the workspace is lkv_decode_workspace_bytes for batch * T entries
+    assert L.lkv_decode_workspace_bytes(cs, vs, 1, 8 * 4, 32, 256) == 8 * 4 * 32 * 4 * 130 * 4
+
+
 def test_status_strings():
     assert lkv.status_string(lkv.OK) == "ok"
     assert "invalid" in lkv.status_string(lkv.EINVAL)

@@ -284,6 +284,16 @@ def test_decode_tiered_segments_one_launch(G, tau):
     assert_attention_close(got, want, vmax, f"tiered G{G} tau {tau}")
 
 
+@pytest.mark.parametrize("fmt", [(128, 64, 6, 4), (128, 64, 6, 6)], ids=_fmt_id)
+@pytest.mark.parametrize("G", [4, 8])
+def test_decode_one_token_past_a_full_block(fmt, G):
+    """65 tokens in one 256-token split (a full block, then one live slot):
+    the matrix-core kernels once gave non-finite rows here for K6V6, G 4,
+    when the sequence length was held in vector registers."""
+    got, want, vmax = _decode_case(fmt, G, "bf16", [65], 0.0, 256, seed=40)
+    assert_attention_close(got, want, vmax, f"65 tokens {fmt} G{G}")
+
+
 def test_decode_empty_and_degenerate():
     """Zero-length sequences give 0; a single token gives its v_hat."""
     fmt = (128, 64, 6, 4)
