@@ -147,9 +147,10 @@ def setup_uniform(args, wl, dev) -> Setup:
         S.calls.append((app, spl, comb))
         S.keep += [k, v, q]
     S.keep += [caches, bt, lens, view, cu1, last, ws, out]
+    ptk = caches[0].chunk_bytes // 64
     if not args.fp16_layer:
         S.secondary["decode_with_scores"] = scores_figure(caches, view, S.keep, B, Hq, Hkv, D, N, sm, split, dev)
-    ptk = caches[0].chunk_bytes // 64
+        S.secondary["multi_token"] = multi_figure(caches, view, S.keep, B, Hq, Hkv, D, N, sm, ptk, dev)
     qb = 2 if wl.dtype == "bf16" else 4
     kv = B * Hkv * N * ptk
     S.per_token_head, S.q_bytes = ptk, qb
@@ -204,6 +205,43 @@ def scores_figure(caches, view, keep, B, Hq, Hkv, D, N, sm, split, dev):
     return {"us_per_call": round(t_s, 1), "plain_us_per_call": round(t_p, 1),
             "extra_bytes_per_call": extra,
             "counted": "score rows written and read (B x Hq x N fp32) plus the accumulator read and written"}
+
+
+def multi_figure(caches, view, keep, B, Hq, Hkv, D, N, sm, ptk, dev):
+    """lkv_decode_attn_multi over the same layer caches: T query tokens per
+    sequence (the last T of the N cached ones, causal), T = 4 and 16, with
+    the library's split plan; 32 calls rotated over the layers between one
+    event pair after 8 untimed ones.  Counted bytes: the cache once, Q and
+    the fp32 output."""
+    import torch
+
+    from quantized_kv_cache_token_amd import lkv
+
+    fig = {}
+    for T in (4, 16):
+        split = lkv.decode_plan([caches[0]], [view], B * T, Hq)
+        ws = lkv.decode_workspace([caches[0]], [view], B * T, Hq, split, dev)
+        out = torch.empty(B, T, Hq, D, dtype=torch.float32, device=dev)
+        qs = [torch.randn(B, T, Hq, D, device=dev).to(torch.bfloat16) for _ in caches]
+
+        def call(i):
+            lkv.decode_attn_multi([caches[i % len(caches)]], [view], qs[i % len(caches)], sm, 0.0, split, out, ws)
+
+        for i in range(8):
+            call(i)
+        e0, e1 = _event(), _event()
+        e0.record()
+        for i in range(32):
+            call(i)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 32 / 1e3
+        nbytes = B * Hkv * N * ptk + B * T * Hq * D * (2 + 4)
+        fig[f"T{T}"] = {"us_per_call": round(t * 1e6, 1), "GB/s": round(nbytes / t / 1e9, 1),
+                        "query_tokens_per_s": round(B * T / t, 1), "split_tokens": split}
+        keep += [ws, out, qs]
+    fig["counted"] = "the layer's packed cache once, bf16 Q and fp32 output"
+    return fig
 
 
 def setup_tiered(args, wl, dev) -> Setup:
