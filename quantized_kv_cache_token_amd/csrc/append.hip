@@ -225,7 +225,7 @@ __device__ __forceinline__ void pack_k_rows(const uint16_t (*kq)[64], uint8_t* c
 // Rows wave + 4 * (k0 + k), k < CHN, of one chunk: their loads are issued
 // together, then they are quantised with their reductions interleaved (rows
 // past the end reload the last row and are not stored).
-template <int D, int DT, int CHN>
+template <int D, int DT, int CHN, int GS>
 __device__ __forceinline__ void quant_rows(const AppendArgs& a, int k0, int wave, int lane, int nrows, int s0,
                                            int row0, int lb, int sp, int kvh, uint8_t* ch, uint16_t (*kq)[64],
                                            uint8_t (*vt)[VPITCH])
@@ -247,7 +247,7 @@ __device__ __forceinline__ void quant_rows(const AppendArgs& a, int k0, int wave
         float x[P];
 #pragma unroll
         for (int p = 0; p < P; p++) x[p] = raw_value<DT>(u[k][p]);
-        quantize_fast<P>(x, f.g, (r & 1) ? f.vb : f.kb, q[k]);
+        quantize_fast<P, GS>(x, (r & 1) ? f.vb : f.kb, q[k]);
     }
     // lanes whose quotient sat too close to a half-integer
 #pragma unroll
@@ -272,15 +272,15 @@ __device__ __forceinline__ void quant_rows(const AppendArgs& a, int k0, int wave
         } else {
             kq[slot][lane] = (uint16_t)(P == 2 ? (q[k].q[0] | (q[k].q[1] << f.kb)) : q[k].q[0]);
         }
-        if ((P * lane) % f.g == 0) {
-            const int gi = P * lane / f.g;
+        if ((P * lane) % GS == 0) {
+            const int gi = P * lane / GS;
             ((float*)(ch + (is_v ? f.off_vs : f.off_ks)))[gi * BT + slot] = q[k].s;
             ch[(is_v ? f.off_vz : f.off_kz) + gi * BT + slot] = (uint8_t)q[k].z;
         }
     }
 }
 
-template <int D, int DT>
+template <int D, int DT, int GS>
 __global__ __launch_bounds__(256) void append_quant_kernel(AppendArgs a)
 {
     constexpr int P = D / 64;  // channels P * lane + p
@@ -307,12 +307,12 @@ __global__ __launch_bounds__(256) void append_quant_kernel(AppendArgs a)
     __shared__ uint16_t kq[BT][64];
     __shared__ uint8_t vt[D][VPITCH];
     if (nrows <= 4) {  // at most one row per wave (a decode step): no batch of duplicates
-        if (wave < nrows) quant_rows<D, DT, 1>(a, 0, wave, lane, nrows, s0, row0, lb, sp, kvh, ch, kq, vt);
+        if (wave < nrows) quant_rows<D, DT, 1, GS>(a, 0, wave, lane, nrows, s0, row0, lb, sp, kvh, ch, kq, vt);
     } else {
 #pragma unroll 1
         for (int k0 = 0; k0 < MAXR; k0 += CH) {
             if (wave + 4 * k0 >= nrows) break;
-            quant_rows<D, DT, CH>(a, k0, wave, lane, nrows, s0, row0, lb, sp, kvh, ch, kq, vt);
+            quant_rows<D, DT, CH, GS>(a, k0, wave, lane, nrows, s0, row0, lb, sp, kvh, ch, kq, vt);
         }
     }
     __syncthreads();
@@ -323,6 +323,17 @@ __global__ __launch_bounds__(256) void append_quant_kernel(AppendArgs a)
     else pack_k_rows<4, 8, 1>(kq, ch, f, s0, s1);
     if (f.vb == 6) pack_v_rows<6, 16, 3, D>(vt, ch, f.off_vc, f.vrow, s0, s1);
     else pack_v_rows<4, 8, 1, D>(vt, ch, f.off_vc, f.vrow, s0, s1);
+}
+
+template <int D, int GS>
+static void launch_quant(const AppendArgs& a, int dtype, dim3 grid, hipStream_t stream)
+{
+    if constexpr (GS <= D) {
+        if (dtype == LKV_F32) hipLaunchKernelGGL((append_quant_kernel<D, LKV_F32, GS>), grid, dim3(256), 0, stream, a);
+        else if (dtype == LKV_BF16)
+            hipLaunchKernelGGL((append_quant_kernel<D, LKV_BF16, GS>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((append_quant_kernel<D, LKV_F16, GS>), grid, dim3(256), 0, stream, a);
+    }
 }
 
 template <int D>
@@ -338,9 +349,9 @@ static void launch_d(const AppendArgs& a, int dtype, dim3 grid, hipStream_t stre
         else hipLaunchKernelGGL((append_kernel<D, LKV_F16>), grid, dim3(256), 0, stream, a);
         return;
     }
-    if (dtype == LKV_F32) hipLaunchKernelGGL((append_quant_kernel<D, LKV_F32>), grid, dim3(256), 0, stream, a);
-    else if (dtype == LKV_BF16) hipLaunchKernelGGL((append_quant_kernel<D, LKV_BF16>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((append_quant_kernel<D, LKV_F16>), grid, dim3(256), 0, stream, a);
+    if (a.f.g == 64) launch_quant<D, 64>(a, dtype, grid, stream);
+    else if (a.f.g == 32) launch_quant<D, 32>(a, dtype, grid, stream);
+    else launch_quant<D, 16>(a, dtype, grid, stream);
 }
 
 hipError_t launch_append(const Fmt& f, uint8_t* pool, const void* k, const void* v, int dtype,

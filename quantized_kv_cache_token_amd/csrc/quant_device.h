@@ -90,26 +90,37 @@ __device__ __forceinline__ int quantize_lane(float x, int g, int bits, float* s_
 //    (and any scale that is not a finite normal number) are flagged and
 //    recomputed with correctly rounded division (quantize_exact).
 
-template <bool MAX>
-__device__ __forceinline__ float pick(float a, float b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); }
-
-// Extreme over aligned segments of `lanes` lanes (8, 16, 32 or 64).
-template <bool MAX>
-__device__ __forceinline__ float lanes_extreme(float x, int lanes)
+// Order-preserving integer key of a finite float (the map is its own
+// inverse): min / max of keys are single integer instructions, with no NaN
+// handling.  -0 orders below +0; the quantiser treats both alike.
+__device__ __forceinline__ int fkey(float x)
 {
-    x = pick<MAX>(x, dpp_mov<0xB1>(x));   // quad_perm [1,0,3,2]
-    x = pick<MAX>(x, dpp_mov<0x4E>(x));   // quad_perm [2,3,0,1]
-    x = pick<MAX>(x, dpp_mov<0x141>(x));  // row_half_mirror
-    if (lanes >= 16) x = pick<MAX>(x, dpp_mov<0x140>(x));  // row_mirror
-    if (lanes >= 32) {
-        const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-        x = pick<MAX>(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const int i = __float_as_int(x);
+    return i ^ ((i >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float fkey_value(int k) { return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF)); }
+
+template <bool MAX>
+__device__ __forceinline__ int pick(int a, int b) { return MAX ? max(a, b) : min(a, b); }
+
+// Extreme of keys over aligned segments of LANES lanes (8, 16, 32 or 64).
+template <bool MAX, int LANES>
+__device__ __forceinline__ int lanes_extreme(int k)
+{
+    static_assert(LANES == 8 || LANES == 16 || LANES == 32 || LANES == 64, "segment of 8 to 64 lanes");
+    k = pick<MAX>(k, __builtin_amdgcn_update_dpp(0, k, 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
+    k = pick<MAX>(k, __builtin_amdgcn_update_dpp(0, k, 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
+    k = pick<MAX>(k, __builtin_amdgcn_update_dpp(0, k, 0x141, 0xF, 0xF, true));  // row_half_mirror
+    if constexpr (LANES >= 16) k = pick<MAX>(k, __builtin_amdgcn_update_dpp(0, k, 0x140, 0xF, 0xF, true));  // row_mirror
+    if constexpr (LANES >= 32) {
+        const auto a = __builtin_amdgcn_permlane16_swap((uint32_t)k, (uint32_t)k, false, false);
+        k = pick<MAX>((int)a[0], (int)a[1]);
     }
-    if (lanes >= 64) {
-        const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-        x = pick<MAX>(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    if constexpr (LANES >= 64) {
+        const auto a = __builtin_amdgcn_permlane32_swap((uint32_t)k, (uint32_t)k, false, false);
+        k = pick<MAX>((int)a[0], (int)a[1]);
     }
-    return x;
+    return k;
 }
 
 // rint(RN(x / s)) for a finite normal s > 0 and |x / s| < 128, from rc
@@ -132,22 +143,23 @@ struct QRow {
     bool slow;
 };
 
-// Quantise the lane's P values x (channels P * lane + p); the group is the
-// aligned segment of g / P lanes.  bits is 4 or 6.
-template <int P>
-__device__ __forceinline__ void quantize_fast(const float (&x)[P], int g, int bits, QRow<P>& o)
+// Quantise the lane's P values x (channels P * lane + p); the group of GS
+// channels is the aligned segment of GS / P lanes.  bits is 4 or 6.  No
+// branch: the rows a wave quantises together interleave.
+template <int P, int GS>
+__device__ __forceinline__ void quantize_fast(const float (&x)[P], int bits, QRow<P>& o)
 {
     const int qmax = (1 << bits) - 1;
     const float fq = (float)qmax;
     const float C = bits == 6 ? 0x1.041042p-6f : 0x1.111112p-4f;  // RN(1/63), RN(1/15)
-    float mn = x[0], mx = x[0];
+    int kn = fkey(x[0]), kx = kn;
 #pragma unroll
     for (int p = 1; p < P; p++) {
-        mn = pick<false>(mn, x[p]);
-        mx = pick<true>(mx, x[p]);
+        kn = pick<false>(kn, fkey(x[p]));
+        kx = pick<true>(kx, fkey(x[p]));
     }
-    mn = lanes_extreme<false>(mn, g / P);
-    mx = lanes_extreme<true>(mx, g / P);
+    const float mn = fkey_value(lanes_extreme<false, GS / P>(kn));
+    const float mx = fkey_value(lanes_extreme<true, GS / P>(kx));
     const float lo = mn < 0.0f ? mn : 0.0f;
     const float hi = mx > 0.0f ? mx : 0.0f;
     const float r = hi - lo;

@@ -260,8 +260,8 @@ __device__ __forceinline__ void copy_codes(uint8_t (*st)[VPITCH], const uint8_t*
 // requantised at the destination width, four tokens per wave at a time
 // (lane: channels P * lane + p); codes into staged slots r + sh, scales and
 // zeros straight to the destination.
-template <int D>
-__device__ __forceinline__ void requant_codes(uint8_t (*st)[VPITCH], const uint8_t* src_of, const uint32_t* vsrc,
+template <int D, int GS>
+__device__ __forceinline__ void requant_codes_g(uint8_t (*st)[VPITCH], const uint8_t* src_of, const uint32_t* vsrc,
                                               int vrow_w, const Fmt& fs, const Fmt& fm, const float* m_vs,
                                               const uint8_t* m_vz, int pos, uint8_t* dA, uint8_t* dB, int r0, int r1,
                                               int sh)
@@ -282,7 +282,7 @@ __device__ __forceinline__ void requant_codes(uint8_t (*st)[VPITCH], const uint8
             }
         }
 #pragma unroll
-        for (int t = 0; t < T; t++) quantize_fast<P>(x[t], fm.g, fm.vb, q[t]);
+        for (int t = 0; t < T; t++) quantize_fast<P, GS>(x[t], fm.vb, q[t]);
 #pragma unroll
         for (int t = 0; t < T; t++)
             if (q[t].slow) quantize_exact<P>(x[t], fm.vb, q[t]);
@@ -294,13 +294,24 @@ __device__ __forceinline__ void requant_codes(uint8_t (*st)[VPITCH], const uint8
             uint8_t* dch = P_ / BT == pos / BT ? dA : dB;
 #pragma unroll
             for (int p = 0; p < P; p++) st[P * lane + p][r + sh] = (uint8_t)q[t].q[p];
-            if ((P * lane) % fm.g == 0) {
-                const int gi = P * lane / fm.g;
+            if ((P * lane) % GS == 0) {
+                const int gi = P * lane / GS;
                 ((float*)(dch + fm.off_vs))[gi * BT + P_ % BT] = q[t].s;
                 dch[fm.off_vz + gi * BT + P_ % BT] = (uint8_t)q[t].z;
             }
         }
     }
+}
+
+template <int D>
+__device__ __forceinline__ void requant_codes(uint8_t (*st)[VPITCH], const uint8_t* src_of, const uint32_t* vsrc,
+                                              int vrow_w, const Fmt& fs, const Fmt& fm, const float* m_vs,
+                                              const uint8_t* m_vz, int pos, uint8_t* dA, uint8_t* dB, int r0, int r1,
+                                              int sh)
+{
+    if (fm.g == 64) requant_codes_g<D, 64>(st, src_of, vsrc, vrow_w, fs, fm, m_vs, m_vz, pos, dA, dB, r0, r1, sh);
+    else if (fm.g == 32) requant_codes_g<D, 32>(st, src_of, vsrc, vrow_w, fs, fm, m_vs, m_vz, pos, dA, dB, r0, r1, sh);
+    else requant_codes_g<D, 16>(st, src_of, vsrc, vrow_w, fs, fm, m_vs, m_vz, pos, dA, dB, r0, r1, sh);
 }
 
 template <int D>
@@ -338,24 +349,33 @@ __global__ __launch_bounds__(256) void tier_move_kernel(MoveArgs a)
     const Fmt& fm = a.dst[1].f;
     const bool copy_m = fm.vb == fs.vb;  // MID survivors keep their V codes (a MID source)
 
+    // a chunk's tiers and its pieces are requested together (the tiers and
+    // block of the next chunk one iteration ahead)
+    auto tiers_of = [&](int c) __attribute__((always_inline)) {
+        return lane < min(BT, len - c * BT) ? (int)S.tiers[(int64_t)b * S.tier_stride + c * BT + lane] : 0;
+    };
+    int t_next = tiers_of(c0);
+    int blk_next = S.bt[(int64_t)b * S.max_blocks + c0];
     for (int c = c0; c < c1; c++) {
-        // tiers of the chunk's 64 slots; every wave derives the same masks
-        const int nvalid = min(BT, len - c * BT);
-        const int t = lane < nvalid ? S.tiers[(int64_t)b * S.tier_stride + c * BT + lane] : 0;
-        const uint64_t mk0 = __ballot(t == 2), mk1 = __ballot(t == 1);
-        const uint64_t below = (1ull << lane) - 1ull;
-        if (t == 2) src_of[wave][0][__popcll(mk0 & below)] = (uint8_t)lane;
-        else if (t == 1) src_of[wave][1][__popcll(mk1 & below)] = (uint8_t)lane;
-        const int n0 = __popcll(mk0), n1 = __popcll(mk1);
-        if (n0 + n1 == 0) continue;
-
-        const uint8_t* sch = S.pool + ((int64_t)S.bt[(int64_t)b * S.max_blocks + c] * fs.H + kvh) * fs.chunk;
+        const uint8_t* sch = S.pool + ((int64_t)blk_next * fs.H + kvh) * fs.chunk;
         uint4 pc[MOVE_PIECES];
 #pragma unroll
         for (int k = 0; k < MOVE_PIECES; k++) {
             const int p = tid + 256 * k;
             pc[k] = p < npieces ? ((const uint4*)sch)[p] : make_uint4(0u, 0u, 0u, 0u);
         }
+        // tiers of the chunk's 64 slots; every wave derives the same masks
+        const int t = t_next;
+        if (c + 1 < c1) {
+            t_next = tiers_of(c + 1);
+            blk_next = S.bt[(int64_t)b * S.max_blocks + c + 1];
+        }
+        const uint64_t mk0 = __ballot(t == 2), mk1 = __ballot(t == 1);
+        const uint64_t below = (1ull << lane) - 1ull;
+        if (t == 2) src_of[wave][0][__popcll(mk0 & below)] = (uint8_t)lane;
+        else if (t == 1) src_of[wave][1][__popcll(mk1 & below)] = (uint8_t)lane;
+        const int n0 = __popcll(mk0), n1 = __popcll(mk1);
+        if (n0 + n1 == 0) continue;
         // destination chunks: the block of each segment's next position and
         // the one after it
         uint8_t *dA0 = nullptr, *dB0 = nullptr, *dA1 = nullptr, *dB1 = nullptr;
