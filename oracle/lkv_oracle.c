@@ -193,7 +193,9 @@ void orc_quantize_group(const float* x, int n, int bits,
 
 typedef struct {
     int D, g, kb, vb, H, fp16, ngroups;
-    int64_t off[7];
+    int knorm;      /* direction-preserving K: factor section at off_kn */
+    int64_t off_kn;
+    int64_t off[7]; /* [6]: chunk bytes, the factor section included */
     int64_t krow; /* bytes per K token row */
     int64_t vrow; /* bytes per V channel row */
 } fmt_t;
@@ -213,7 +215,20 @@ static int make_fmt(const orc_cache* c, fmt_t* f)
     f->ngroups = f->fp16 ? 0 : c->head_dim / c->group_size;
     f->krow = (int64_t)f->D * f->kb / 8;
     f->vrow = (int64_t)BT * f->vb / 8;
+    f->knorm = c->k_norm != 0;
+    f->off_kn = f->off[6];
+    if (f->knorm) {
+        if (f->fp16) return -1;
+        f->off[6] += BT * 4; /* one fp32 factor per slot (256 B, a multiple of 128) */
+    }
     return 0;
+}
+
+static float get_knorm(const uint8_t* ch, const fmt_t* f, int slot)
+{
+    float r;
+    memcpy(&r, ch + f->off_kn + (int64_t)slot * 4, 4);
+    return r;
 }
 
 static uint8_t* chunk_ptr(const orc_cache* c, const fmt_t* f, int64_t blk, int kvh)
@@ -287,6 +302,24 @@ static void store_row(uint8_t* ch, const fmt_t* f, int slot, const float* x, int
         set_scale(ch, f, is_v ? 3 : 2, gi, slot, s);
         set_zero(ch, f, is_v ? 5 : 4, gi, slot, z);
     }
+    if (!is_v && f->knorm) {
+        /* Direction-preserving K (norm-direction page, insight of the method):
+         * the group codes carry the key's direction (group quantisation is
+         * invariant to scaling the whole key); the factor r = |k| / |k_hat|
+         * restores the norm, so that the key read back is r * k_hat, with
+         * the direction of the codes and the norm of k.  Norms in fp64, r
+         * rounded once to fp32; a zero k_hat takes r = 1. */
+        double nx = 0.0, nk = 0.0;
+        for (int d = 0; d < f->D; d++) {
+            const int gi = d / f->g;
+            const double kh = (double)((int)get_k(ch, f, slot, d) - (int)get_zero(ch, f, 4, gi, slot)) *
+                              (double)get_scale(ch, f, 2, gi, slot);
+            nx += (double)x[d] * (double)x[d];
+            nk += kh * kh;
+        }
+        const float r = nk > 0.0 ? (float)sqrt(nx / nk) : 1.0f;
+        memcpy(ch + f->off_kn + (int64_t)slot * 4, &r, 4);
+    }
 }
 
 /* ------------------------------------------------------------- append */
@@ -338,7 +371,8 @@ static double deq_k(const uint8_t* ch, const fmt_t* f, int slot, int d)
     uint32_t code = get_k(ch, f, slot, d);
     if (f->fp16) return orc_f16_to_f64((uint16_t)code);
     int gi = d / f->g;
-    return (double)((int)code - (int)get_zero(ch, f, 4, gi, slot)) * (double)get_scale(ch, f, 2, gi, slot);
+    const double kh = (double)((int)code - (int)get_zero(ch, f, 4, gi, slot)) * (double)get_scale(ch, f, 2, gi, slot);
+    return f->knorm ? kh * (double)get_knorm(ch, f, slot) : kh;
 }
 static double deq_v(const uint8_t* ch, const fmt_t* f, int slot, int d)
 {
@@ -528,6 +562,7 @@ int orc_tier_update(const orc_cache* src, const orc_view* src_view,
     fmt_t fs, fh, fm;
     if (make_fmt(src, &fs) || make_fmt(dst_h, &fh) || make_fmt(dst_m, &fm)) return -1;
     if (fs.fp16 || fs.vb != 6) return -1;
+    if (fs.knorm || fh.knorm || fm.knorm) return -1; /* tiers hold the plain K codec */
     if (fh.D != fs.D || fh.g != fs.g || fh.H != fs.H || fh.kb != fs.kb || fh.vb != 6) return -1;
     if (fm.D != fs.D || fm.g != fs.g || fm.H != fs.H || fm.kb != fs.kb || fm.vb != 4) return -1;
     if (batch < 0 || scores_stride < 0) return -1;
@@ -667,6 +702,7 @@ int orc_retier(const orc_cache* h, const orc_view* h_view, const float* h_scores
     fmt_t fh, fm, fdh, fdm;
     if (make_fmt(h, &fh) || make_fmt(m, &fm) || make_fmt(dst_h, &fdh) || make_fmt(dst_m, &fdm)) return -1;
     if (fh.fp16 || fh.vb != 6 || fm.vb != 4 || fdh.vb != 6 || fdm.vb != 4) return -1;
+    if (fh.knorm || fm.knorm || fdh.knorm || fdm.knorm) return -1; /* tiers hold the plain K codec */
     const fmt_t* all[3] = {&fm, &fdh, &fdm};
     for (int i = 0; i < 3; i++)
         if (all[i]->D != fh.D || all[i]->g != fh.g || all[i]->H != fh.H || all[i]->kb != fh.kb) return -1;

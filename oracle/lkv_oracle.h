@@ -44,6 +44,8 @@ typedef struct orc_cache {
     int32_t num_kv_heads;  /* Hkv */
     int64_t num_blocks;
     uint8_t* pool;
+    int32_t k_norm;        /* 1: direction-preserving K (a per-token norm factor
+                              after the six sections); quantised formats only */
 } orc_cache;
 
 /* Which blocks of a cache a batch reads: host block table and lengths. */

@@ -25,7 +25,7 @@ class _Cache(C.Structure):
     _fields_ = [("head_dim", C.c_int32), ("group_size", C.c_int32),
                 ("k_bits", C.c_int32), ("v_bits", C.c_int32),
                 ("num_kv_heads", C.c_int32), ("num_blocks", C.c_int64),
-                ("pool", C.c_void_p)]
+                ("pool", C.c_void_p), ("k_norm", C.c_int32)]
 
 
 class _View(C.Structure):
@@ -151,16 +151,18 @@ class Cache:
     num_kv_heads: int
     num_blocks: int
     pool: np.ndarray = None
+    k_norm: int = 0  # 1: direction-preserving K, one fp32 norm factor per slot after the six sections
 
     def __post_init__(self):
         self.layout = chunk_layout(self.head_dim, self.group_size, self.k_bits, self.v_bits)
-        self.chunk_bytes = self.layout[6]
+        self.knorm_offset = self.layout[6]
+        self.chunk_bytes = self.layout[6] + (BLOCK_TOKENS * 4 if self.k_norm else 0)
         if self.pool is None:
             self.pool = np.zeros(self.num_blocks * self.num_kv_heads * self.chunk_bytes, np.uint8)
 
     def c(self) -> _Cache:
         return _Cache(self.head_dim, self.group_size, self.k_bits, self.v_bits,
-                      self.num_kv_heads, self.num_blocks, self.pool.ctypes.data)
+                      self.num_kv_heads, self.num_blocks, self.pool.ctypes.data, self.k_norm)
 
     def chunk(self, blk: int, kvh: int) -> np.ndarray:
         o = (blk * self.num_kv_heads + kvh) * self.chunk_bytes

@@ -55,8 +55,10 @@ def dequant_chunk(chunk: np.ndarray, D: int, g: int, kb: int, vb: int):
 
 
 def dequant_sequence(pool: np.ndarray, chunk_bytes: int, Hkv: int, D: int, g: int, kb: int, vb: int,
-                     block_row: np.ndarray, n: int):
-    """K_hat, V_hat float64 [Hkv][n][D] of one sequence."""
+                     block_row: np.ndarray, n: int, knorm_offset: int | None = None):
+    """K_hat, V_hat float64 [Hkv][n][D] of one sequence.  knorm_offset: the
+    byte offset of the per-slot fp32 norm factors of a direction-preserving
+    K cache, which scale each K row."""
     K = np.zeros((Hkv, n, D))
     V = np.zeros((Hkv, n, D))
     for lb in range(-(-n // BT)):
@@ -64,6 +66,9 @@ def dequant_sequence(pool: np.ndarray, chunk_bytes: int, Hkv: int, D: int, g: in
         for h in range(Hkv):
             o = (blk * Hkv + h) * chunk_bytes
             kh, vh, _ = dequant_chunk(pool[o:o + chunk_bytes], D, g, kb, vb)
+            if knorm_offset is not None:
+                r = pool[o + knorm_offset:o + knorm_offset + 4 * BT].view(np.float32).astype(np.float64)
+                kh = kh * r[:, None]
             m = min(BT, n - lb * BT)
             K[h, lb * BT:lb * BT + m] = kh[:m]
             V[h, lb * BT:lb * BT + m] = vh[:m]

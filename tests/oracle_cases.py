@@ -23,14 +23,14 @@ def block_tables(lens, rng=None, extra_blocks=0):
     return bt, total
 
 
-def build_cache(K, V, D, g, kb, vb, rng=None, lens=None):
+def build_cache(K, V, D, g, kb, vb, rng=None, lens=None, k_norm=0):
     """Append per-sequence rows K[b], V[b] (fp32 [n_b][Hkv][D]) into a fresh
     oracle cache.  Returns (cache, block_table, lens)."""
     B = len(K)
     Hkv = K[0].shape[1]
     lens = np.array([k.shape[0] for k in K], np.int32) if lens is None else np.asarray(lens, np.int32)
     bt, total = block_tables(lens, rng)
-    cache = O.Cache(D, g, kb, vb, Hkv, total)
+    cache = O.Cache(D, g, kb, vb, Hkv, total, k_norm=k_norm)
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     O.append(cache, np.concatenate(K), np.concatenate(V), cu, np.zeros(B, np.int32), bt)
     return cache, bt, lens
