@@ -44,6 +44,16 @@
  * patterns (round to nearest even) and the metadata sections are empty.
  * Logical block i of sequence b lives in pool block block_table[b][i]; a
  * contiguous cache is the identity table.
+ *
+ * Direction-preserving K (k_norm = 1; the norm-direction page's insight that
+ * a key's direction matters more to attention than its norm): quantised
+ * formats only.  A seventh section, fp32 [64] (256 B) after the six, holds
+ * one factor per slot, r = |k| / |k_hat| (norms in fp64, r rounded to fp32;
+ * 1 for a zero k_hat), and every call reads the key as r * k_hat: the
+ * direction of the group codes with the norm of the original key.  The
+ * codes, scales and zeros are those of the plain format.  lkv_quant_append
+ * needs K and V aligned to head_dim / 64 elements for it; decode runs the
+ * generic kernel; the tier calls return LKV_EUNSUPPORTED.
  */
 #ifndef LKV_H
 #define LKV_H
@@ -68,7 +78,8 @@ typedef enum { LKV_F32 = 0, LKV_BF16 = 1, LKV_F16 = 2 } lkv_dtype;
 
 /* One cache.  head_dim 64 or 128; group_size 16, 32 or 64 dividing head_dim;
  * (k_bits, v_bits) in {4, 6} x {4, 6}, or (16, 16); block_tokens 64.  pool is
- * 256-byte aligned and holds num_blocks * num_kv_heads * chunk bytes. */
+ * 256-byte aligned and holds num_blocks * num_kv_heads * chunk bytes, where
+ * chunk is lkv_chunk_layout's off[6], plus 256 when k_norm is 1. */
 typedef struct lkv_cache {
     int32_t head_dim;
     int32_t group_size;
@@ -78,6 +89,7 @@ typedef struct lkv_cache {
     int32_t block_tokens;
     int64_t num_blocks;
     void* pool;
+    int32_t k_norm;  /* 1: direction-preserving K (see below); 0: plain */
 } lkv_cache;
 
 /* What a batch reads from one cache. */
@@ -96,7 +108,8 @@ const char* lkv_status_string(int status);
 
 /* Byte offsets of the six sections of a chunk and, in off[6], the chunk size
  * (the memory layout reorganised for the quantised format: LeanKV page,
- * implementation details).  Returns LKV_OK or LKV_EUNSUPPORTED. */
+ * implementation details); with k_norm = 1 the factor section starts at
+ * off[6] and adds 256 bytes.  Returns LKV_OK or LKV_EUNSUPPORTED. */
 int lkv_chunk_layout(int32_t head_dim, int32_t group_size, int32_t k_bits, int32_t v_bits,
                      int64_t off[7]);
 

@@ -37,6 +37,12 @@ int make_fmt(const lkv_cache* c, Fmt* f)
     f->chunk = off[6];
     f->krow = c->head_dim * c->k_bits / 8;
     f->vrow = BT * c->v_bits / 8;
+    f->k_norm = c->k_norm != 0;
+    f->off_kn = (int32_t)off[6];
+    if (f->k_norm) {
+        if (f->fp16) return LKV_EUNSUPPORTED;
+        f->chunk += BT * 4;  // one fp32 factor per slot
+    }
     return LKV_OK;
 }
 
@@ -144,6 +150,10 @@ int lkv_quant_append(const lkv_cache* cache, const void* k, const void* v, int32
     if (dtype != LKV_F32 && dtype != LKV_BF16 && dtype != LKV_F16) return LKV_EINVAL;
     if (batch == 0 || max_new == 0) return LKV_OK;
     if (!k || !v || !cu_new || !start_pos || !block_table) return LKV_EINVAL;
+    if (f.k_norm) {  // the norm factors come from the quantised kernel, which needs P-element alignment
+        const uintptr_t need = (uintptr_t)(f.D / 64) * (dtype == LKV_F32 ? 4 : 2);
+        if ((uintptr_t)k % need != 0 || (uintptr_t)v % need != 0) return LKV_EUNSUPPORTED;
+    }
     const hipError_t e = launch_append(f, (uint8_t*)cache->pool, k, v, dtype, cu_new, start_pos, block_table,
                                        max_blocks, batch, max_new, (hipStream_t)stream);
     return e == hipSuccess ? LKV_OK : LKV_EHIP;
@@ -415,6 +425,7 @@ int tier_source(const lkv_cache* c, const lkv_view* v, const float* scores, int3
     int st = make_fmt(c, &f);
     if (st != LKV_OK) return st;
     if (f.fp16 || f.vb != vb) return ref ? LKV_EINVAL : LKV_EUNSUPPORTED;
+    if (f.k_norm) return LKV_EUNSUPPORTED;  // tiers hold the plain K codec
     if (ref && (f.D != ref->D || f.g != ref->g || f.H != ref->H || f.kb != ref->kb)) return LKV_EINVAL;
     if (!v || stride < 0 || v->max_blocks < 1 || v->max_len < 0 || v->max_len > stride ||
         (int64_t)v->max_len > (int64_t)v->max_blocks * BT)
@@ -431,6 +442,7 @@ int tier_dest(const lkv_cache* c, const int32_t* bt, int32_t max_blocks, int vb,
     if (st != LKV_OK) return st;
     if (f.D != ref.D || f.g != ref.g || f.H != ref.H || f.kb != ref.kb || f.vb != vb || max_blocks < 1)
         return LKV_EINVAL;
+    if (f.k_norm) return LKV_EUNSUPPORTED;
     *out = TierDest{f, (uint8_t*)c->pool, bt, max_blocks};
     return LKV_OK;
 }

@@ -260,6 +260,27 @@ __device__ __forceinline__ void quant_rows(const AppendArgs& a, int k0, int wave
             quantize_exact<P>(x, (r & 1) ? f.vb : f.kb, q[k]);
         }
     }
+    // direction-preserving K: the factor |k| / |k_hat| of each K row (rows of
+    // waves 0 and 2), norms summed in fp64
+    float rn[CHN];
+    if (f.k_norm && (wave & 1) == 0) {
+#pragma unroll
+        for (int k = 0; k < CHN; k++) {
+            double nx = 0.0, nk = 0.0;
+#pragma unroll
+            for (int p = 0; p < P; p++) {
+                const double x = (double)raw_value<DT>(u[k][p]);
+                const double kh = (double)(q[k].q[p] - q[k].z) * (double)q[k].s;
+                nx += x * x;
+                nk += kh * kh;
+            }
+            for (int o = 32; o > 0; o >>= 1) {
+                nx += __shfl_xor(nx, o, 64);
+                nk += __shfl_xor(nk, o, 64);
+            }
+            rn[k] = nk > 0.0 ? (float)sqrt(nx / nk) : 1.0f;
+        }
+    }
 #pragma unroll
     for (int k = 0; k < CHN; k++) {
         const int r = wave + 4 * (k0 + k);
@@ -271,6 +292,7 @@ __device__ __forceinline__ void quant_rows(const AppendArgs& a, int k0, int wave
             for (int p = 0; p < P; p++) vt[P * lane + p][slot] = (uint8_t)q[k].q[p];
         } else {
             kq[slot][lane] = (uint16_t)(P == 2 ? (q[k].q[0] | (q[k].q[1] << f.kb)) : q[k].q[0]);
+            if (f.k_norm && lane == 0) ((float*)(ch + f.off_kn))[slot] = rn[k];
         }
         if ((P * lane) % GS == 0) {
             const int gi = P * lane / GS;

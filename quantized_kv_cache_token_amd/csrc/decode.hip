@@ -112,6 +112,11 @@ __global__ __launch_bounds__(64) void split_valu_kernel(SplitArgs a)
 #pragma unroll
                 for (int h = 0; h < G; h++) s[h] += qs[h][d] * kh;
             }
+            if (f.k_norm) {  // direction-preserving K: the key is r * k_hat
+                const float r = ((const float*)(ch + f.off_kn))[lane];
+#pragma unroll
+                for (int h = 0; h < G; h++) s[h] *= r;
+            }
         }
 #pragma unroll
         for (int h = 0; h < G; h++) {

@@ -668,7 +668,8 @@ static bool mfma_ok(const SegArgs& s, const void* q, int q_dtype, int32_t num_q_
 {
     const Fmt& f = s.f;
     const int G = num_q_heads / f.H;
-    return q_dtype == LKV_BF16 && f.D == 128 && f.g == 64 && !f.fp16 && f.kb == 6 && (f.vb == 4 || f.vb == 6) &&
+    return q_dtype == LKV_BF16 && f.D == 128 && f.g == 64 && !f.fp16 && !f.k_norm && f.kb == 6 &&
+           (f.vb == 4 || f.vb == 6) &&
            (G == 4 || G == 8) && ((uintptr_t)q & 15) == 0 &&  // Q is read 16 bytes at a time
            sm_scale > 0.0f &&                                   // the scale is applied after the block maximum
            split_tokens <= 64 * BT;  // a split's block-table entries are held one per lane

@@ -18,6 +18,8 @@ struct Fmt {
     int32_t krow;                                     // bytes of one K token row
     int32_t vrow;                                     // bytes of one V channel row
     int64_t chunk;                                    // bytes of one chunk
+    int32_t k_norm;                                   // direction-preserving K: factors at off_kn
+    int32_t off_kn;                                   // fp32 [64] norm factors, after the six sections
 };
 
 // Fills f from a cache descriptor; returns LKV_OK, LKV_EINVAL or

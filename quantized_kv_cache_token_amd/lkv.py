@@ -31,7 +31,7 @@ class LkvError(RuntimeError):
 class _Cache(C.Structure):
     _fields_ = [("head_dim", C.c_int32), ("group_size", C.c_int32), ("k_bits", C.c_int32),
                 ("v_bits", C.c_int32), ("num_kv_heads", C.c_int32), ("block_tokens", C.c_int32),
-                ("num_blocks", C.c_int64), ("pool", C.c_void_p)]
+                ("num_blocks", C.c_int64), ("pool", C.c_void_p), ("k_norm", C.c_int32)]
 
 
 class _View(C.Structure):
@@ -122,9 +122,11 @@ class Cache:
     num_blocks: int
     pool: torch.Tensor = None
     device: str = "cuda"
+    k_norm: int = 0  # 1: direction-preserving K, one fp32 norm factor per slot after the six sections
 
     def __post_init__(self):
-        self.chunk_bytes = chunk_layout(self.head_dim, self.group_size, self.k_bits, self.v_bits)[6]
+        self.knorm_offset = chunk_layout(self.head_dim, self.group_size, self.k_bits, self.v_bits)[6]
+        self.chunk_bytes = self.knorm_offset + (BLOCK_TOKENS * 4 if self.k_norm else 0)
         nbytes = self.num_blocks * self.num_kv_heads * self.chunk_bytes
         if self.pool is None:
             self.pool = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
@@ -132,7 +134,7 @@ class Cache:
 
     def c(self) -> _Cache:
         return _Cache(self.head_dim, self.group_size, self.k_bits, self.v_bits, self.num_kv_heads,
-                      BLOCK_TOKENS, self.num_blocks, self.pool.data_ptr())
+                      BLOCK_TOKENS, self.num_blocks, self.pool.data_ptr(), self.k_norm)
 
 
 @dataclass

@@ -1,0 +1,94 @@
+"""The direction-preserving K codec on the GPU against the oracle: codes,
+scales and zeros bit-exact, the per-slot norm factors within one fp32 ulp
+(both sum the norms in fp64, in different orders), decode within max|d| <=
+1e-3 max|v_hat| and relative L2 <= 1e-4."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from quantized_kv_cache_token_amd import inputs, lkv
+from tests.gpu_common import assert_attention_close, say, sm_scale, to_f32_host
+from tests.oracle_cases import block_tables
+
+pytestmark = pytest.mark.gpu
+
+
+class NormPair:
+    def __init__(self, D, g, kb, vb, Hkv, nblk):
+        self.gpu = lkv.Cache(D, g, kb, vb, Hkv, nblk, k_norm=1)
+        self.ref = O.Cache(D, g, kb, vb, Hkv, nblk, k_norm=1)
+        assert self.gpu.chunk_bytes == self.ref.chunk_bytes and self.gpu.knorm_offset == self.ref.knorm_offset
+
+    def compare(self):
+        torch.cuda.synchronize()
+        cb, ko = self.ref.chunk_bytes, self.ref.knorm_offset
+        got = self.gpu.pool.cpu().numpy().reshape(-1, cb)
+        want = self.ref.pool.reshape(-1, cb)
+        assert np.array_equal(got[:, :ko], want[:, :ko]), "codes, scales or zeros differ"
+        rg = got[:, ko:].copy().view(np.float32)
+        rw = want[:, ko:].copy().view(np.float32)
+        ulp = np.spacing(np.abs(rw).astype(np.float32))
+        bad = np.abs(rg - rw) > ulp
+        assert not bad.any(), f"{bad.sum()} norm factors beyond one ulp, e.g. {rg[bad][:3]} vs {rw[bad][:3]}"
+
+
+def _append(pair, lens, Hkv, D, seed, bt, dtype="bf16"):
+    out = inputs.outlier_channels(seed, Hkv, D)
+    K, V = zip(*[inputs.kv_rows(seed, b, n, Hkv, D, dtype=dtype, outliers=out) for b, n in enumerate(lens)])
+    k, v = torch.cat(K), torch.cat(V)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    lkv.quant_append(pair.gpu, k.cuda(), v.cuda(), torch.tensor(cu).cuda(), torch.zeros(len(lens), dtype=torch.int32).cuda(),
+                     torch.tensor(bt).cuda(), max(lens))
+    O.append(pair.ref, to_f32_host(k), to_f32_host(v), cu, np.zeros(len(lens), np.int32), bt)
+
+
+@pytest.mark.parametrize("fmt", [(128, 64, 6, 4), (128, 32, 4, 6), (64, 16, 6, 6)], ids=lambda f: "D{}g{}k{}v{}".format(*f))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_knorm_append_then_decode(fmt, dtype):
+    D, g, kb, vb = fmt
+    Hkv, G = 2, 4
+    lens = [1, 65, 300]
+    rng = np.random.default_rng(120)
+    bt, nblk = block_tables([n + 2 for n in lens], rng)
+    pair = NormPair(D, g, kb, vb, Hkv, nblk)
+    say("knorm append", fmt, dtype)
+    _append(pair, lens, Hkv, D, 121, bt, dtype)
+    pair.compare()
+    # a decode step: one more row per sequence, then attention with the skip
+    k1, v1 = inputs.kv_rows(122, 0, len(lens), Hkv, D, dtype=dtype)
+    cu = np.arange(len(lens) + 1, dtype=np.int32)
+    lkv.quant_append(pair.gpu, k1.cuda(), v1.cuda(), torch.tensor(cu).cuda(), torch.tensor(lens, dtype=torch.int32).cuda(),
+                     torch.tensor(bt).cuda(), 1)
+    O.append(pair.ref, to_f32_host(k1), to_f32_host(v1), cu, np.array(lens, np.int32), bt)
+    pair.compare()
+    lens = [n + 1 for n in lens]
+    q = inputs.queries(123, len(lens), Hkv * G, D)
+    view = lkv.View(torch.tensor(bt).cuda(), torch.tensor(lens, dtype=torch.int32).cuda(), max(lens))
+    for tau in (0.0, 1e-4):
+        say("knorm decode", fmt, "tau", tau)
+        got = lkv.decode_attn([pair.gpu], [view], q.cuda(), sm_scale(D), tau, 128).cpu().numpy()
+        want = O.decode([pair.ref], [bt], [np.array(lens, np.int32)], to_f32_host(q), sm_scale(D), tau, 128)
+        vmax = 0.0
+        for b, n in enumerate(lens):
+            from tests import np_reference as R
+            _, Vh = R.dequant_sequence(pair.ref.pool, pair.ref.chunk_bytes, Hkv, D, g, kb, vb, bt[b], n)
+            vmax = max(vmax, float(np.abs(Vh).max()))
+        assert_attention_close(got, want, vmax, f"knorm {fmt} tau {tau}")
+
+
+def test_knorm_rejects_unaligned_inputs_and_tiers():
+    D, g, Hkv = 128, 64, 1
+    bt, nblk = block_tables([64])
+    c = lkv.Cache(D, g, 6, 6, Hkv, nblk, k_norm=1)
+    k = torch.zeros(64 * D + 1, dtype=torch.bfloat16, device="cuda")[1:].view(64, 1, D)
+    with pytest.raises(lkv.LkvError):
+        lkv.quant_append(c, k, k, torch.tensor([0, 64], dtype=torch.int32).cuda(), torch.zeros(1, dtype=torch.int32).cuda(),
+                         torch.tensor(bt).cuda(), 64)
+    h, m = lkv.Cache(D, g, 6, 6, Hkv, nblk), lkv.Cache(D, g, 6, 4, Hkv, nblk)
+    view = lkv.View(torch.tensor(bt).cuda(), torch.tensor([64], dtype=torch.int32).cuda(), 64)
+    with pytest.raises(lkv.LkvError):
+        lkv.tier_update(c, view, torch.ones(1, 64, device="cuda"), 0.1, 0.5, h, torch.tensor(bt).cuda(), m,
+                        torch.tensor(bt).cuda(), torch.zeros(1, dtype=torch.int32, device="cuda"),
+                        torch.zeros(1, dtype=torch.int32, device="cuda"),
+                        torch.zeros(1, 64, dtype=torch.uint8, device="cuda"))
