@@ -195,6 +195,10 @@ struct BlockRegs {
 };
 
 constexpr int META_BYTES = 1280;        // D 128, group 64: 2 groups x 64 slots x (4 + 4 + 1 + 1)
+// With direction-preserving K the 64 fp32 norm factors follow at once
+// (every section is a multiple of 128 B): 1536 contiguous bytes.
+constexpr int META_KN_BYTES = META_BYTES + 256;
+template <bool KN> constexpr int meta_bytes() { return KN ? META_KN_BYTES : META_BYTES; }
 constexpr int META_VS = 512, META_KZ = 1024, META_VZ = 1152;
 
 template <int VB>
@@ -228,19 +232,20 @@ __device__ __forceinline__ void load_v(BlockRegs<VB>& R, const uint8_t* ch, uint
     }
 }
 
-template <int VB>
+template <int VB, bool KN>
 __device__ __forceinline__ void load_meta(BlockRegs<VB>& R, const uint8_t* ch, uint32_t off_ks, int lane)
 {
     const uint4* m = (const uint4*)(ch + off_ks);
     R.meta[0] = m[lane];
-    R.meta[1] = m[64 + min(lane, (META_BYTES - 1024) / 16 - 1)];  // every lane loads: no branch
+    R.meta[1] = m[64 + min(lane, (meta_bytes<KN>() - 1024) / 16 - 1)];  // every lane loads: no branch
 }
 
+template <bool KN>
 __device__ __forceinline__ void stage_meta(const uint4 (&meta)[2], uint4* lds, int lane)
 {
     lds[lane] = meta[0];
     // lanes past the last slice rewrite it with the same bytes: no branch
-    lds[64 + min(lane, (META_BYTES - 1024) / 16 - 1)] = meta[1];
+    lds[64 + min(lane, (meta_bytes<KN>() - 1024) / 16 - 1)] = meta[1];
 }
 
 __device__ __forceinline__ void read16f(const uint8_t* lds, float (&v)[16])
@@ -302,7 +307,7 @@ __device__ __forceinline__ void block_qk(const BlockRegs<VB>& R, const uint32_t 
 // srow: when non-null, the block's column of this lane's head in the score
 // rows; the lane that owns the head (part 0) stores its 16 tokens' base-2
 // scores there.
-template <int VB, int G, bool PARTIAL>
+template <int VB, int G, bool PARTIAL, bool KN>
 __device__ __forceinline__ float block_softmax(const f32x4_t (&dot)[4], const uint8_t* lds, SplitState& S, float qsum,
                                                float score_scale, float tau_low, int nlive, int q, int c,
                                                float (&p)[16], uint32_t& keep, float* srow)
@@ -313,6 +318,8 @@ __device__ __forceinline__ float block_softmax(const f32x4_t (&dot)[4], const ui
     read16f(lds + gc * 256 + 64 * q, sk);
     read16b(lds + META_KZ + gc * 64 + 16 * q, zk);
     float sc[16];
+    float rk[16];  // direction-preserving K: the norm factors of the lane's 16 tokens
+    if constexpr (KN) read16f(lds + META_BYTES + 64 * q, rk);
     float bmax = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 4; t++) {
@@ -325,6 +332,7 @@ __device__ __forceinline__ float block_softmax(const f32x4_t (&dot)[4], const ui
             // running maxima must never differ)
             const float pg = mul_rounded(sk[x], dot[t][r] - (float)byte_of(zk, x) * qsum);
             float s2 = pg + xor1(pg);  // both groups, natural units
+            if constexpr (KN) s2 *= rk[x];  // the key is r * k_hat (the same product on both lanes)
             if constexpr (PARTIAL) s2 = 16 * q + x < nlive ? s2 : -INFINITY;
             sc[4 * t + r] = s2;
             bmax = fmaxf(bmax, s2);
@@ -482,7 +490,7 @@ __device__ __forceinline__ void block_pv(const BlockRegs<VB>& R, const uint8_t* 
 }
 
 // One wave's split: split sp of KV head blockIdx.y of sequence blockIdx.z.
-template <int VB, int G>
+template <int VB, int G, bool KN>
 __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint4* meta_lds)
 {
     static_assert(G == 4 || G == 8, "4 or 8 query heads per KV head");
@@ -589,7 +597,7 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
     {
         // the same issue order as inside the loop: metadata, K, V
         const uint8_t* c0 = chunk_of(0);
-        load_meta<VB>(R, c0, off_ks, lane);
+        load_meta<VB, KN>(R, c0, off_ks, lane);
         asm volatile("" ::: "memory");
         load_k<VB>(R, c0, off_kc, c, q);
         asm volatile("" ::: "memory");
@@ -601,8 +609,8 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
     auto block = [&](int k, auto partial) {
         constexpr bool PARTIAL = decltype(partial)::value;
         const uint8_t* cn = chunk_of(min(k + 1, nblk - 1));
-        stage_meta(R.meta, meta_lds, lane);
-        load_meta<VB>(R, cn, off_ks, lane);
+        stage_meta<KN>(R.meta, meta_lds, lane);
+        load_meta<VB, KN>(R, cn, off_ks, lane);
         asm volatile("" ::: "memory");
         f32x4_t dot[4];
         block_qk<VB>(R, qb, q128, mk, dot);
@@ -613,7 +621,7 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
         uint32_t keep;
         float* srow = sg.scores != nullptr ? sg.scores + srow0 + (int64_t)k * BT : nullptr;
         const float alpha =
-            block_softmax<VB, G, PARTIAL>(dot, lds, S, qsum, a.score_scale, a.tau_low, nlive, q, c, p, keep, srow);
+            block_softmax<VB, G, PARTIAL, KN>(dot, lds, S, qsum, a.score_scale, a.tau_low, nlive, q, c, p, keep, srow);
         block_pv<VB, G, PARTIAL>(R, lds, S, p, alpha, keep, q, c, hA, mk);
         load_v<VB>(R, cn, off_vc, c, q);
         asm volatile("" ::: "memory");
@@ -642,11 +650,11 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
     }
 }
 
-template <int VB, int G>
+template <int VB, int G, bool KN>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void split_mfma_kernel(MfmaArgs a)
 {
-    __shared__ uint4 meta_lds[META_BYTES / 16];
-    split_body<VB, G>(a, blockIdx.x, meta_lds);
+    __shared__ uint4 meta_lds[meta_bytes<KN>() / 16];
+    split_body<VB, G, KN>(a, blockIdx.x, meta_lds);
 }
 
 // Both segments of a tiered cache in one launch: workgroups [0, n0) run the
@@ -658,8 +666,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
 {
     __shared__ uint4 meta_lds[META_BYTES / 16];
     const int sp = blockIdx.x;
-    if (sp < a0.seg.n_splits) split_body<6, G>(a0, sp, meta_lds);
-    else split_body<4, G>(a1, sp - a0.seg.n_splits, meta_lds);
+    if (sp < a0.seg.n_splits) split_body<6, G, false>(a0, sp, meta_lds);
+    else split_body<4, G, false>(a1, sp - a0.seg.n_splits, meta_lds);
 }
 
 // Whether a segment has a matrix-core kernel.
@@ -668,8 +676,8 @@ static bool mfma_ok(const SegArgs& s, const void* q, int q_dtype, int32_t num_q_
 {
     const Fmt& f = s.f;
     const int G = num_q_heads / f.H;
-    return q_dtype == LKV_BF16 && f.D == 128 && f.g == 64 && !f.fp16 && !f.k_norm && f.kb == 6 &&
-           (f.vb == 4 || f.vb == 6) &&
+    return q_dtype == LKV_BF16 && f.D == 128 && f.g == 64 && !f.fp16 && f.kb == 6 && (f.vb == 4 || f.vb == 6) &&
+           (!f.k_norm || f.off_kn == f.off_ks + META_BYTES) &&  // the factors follow the metadata
            (G == 4 || G == 8) && ((uintptr_t)q & 15) == 0 &&  // Q is read 16 bytes at a time
            sm_scale > 0.0f &&                                   // the scale is applied after the block maximum
            split_tokens <= 64 * BT;  // a split's block-table entries are held one per lane
@@ -695,7 +703,7 @@ bool launch_decode_split_mfma_tiered(const SegArgs& high, const SegArgs& mid, co
                                      int32_t split_tokens, int32_t total_splits, float* partials,
                                      hipStream_t stream, hipError_t* err)
 {
-    if (high.f.vb != 6 || mid.f.vb != 4 || high.f.H != mid.f.H ||
+    if (high.f.vb != 6 || mid.f.vb != 4 || high.f.H != mid.f.H || high.f.k_norm || mid.f.k_norm ||
         !mfma_ok(high, q, q_dtype, num_q_heads, sm_scale, split_tokens) ||
         !mfma_ok(mid, q, q_dtype, num_q_heads, sm_scale, split_tokens))
         return false;
@@ -722,10 +730,15 @@ bool launch_decode_split_mfma(const SegArgs& s, const void* q, int q_dtype, int3
     const int G = num_q_heads / f.H;
     const MfmaArgs a = mfma_args(s, q, num_q_heads, sm_scale, tau_low, split_tokens, total_splits, partials);
     dim3 grid((unsigned)s.n_splits, (unsigned)f.H, (unsigned)batch);
-    if (f.vb == 4 && G == 4) hipLaunchKernelGGL((split_mfma_kernel<4, 4>), grid, dim3(64), 0, stream, a);
-    else if (f.vb == 4) hipLaunchKernelGGL((split_mfma_kernel<4, 8>), grid, dim3(64), 0, stream, a);
-    else if (G == 4) hipLaunchKernelGGL((split_mfma_kernel<6, 4>), grid, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL((split_mfma_kernel<6, 8>), grid, dim3(64), 0, stream, a);
+    if (f.k_norm) {  // direction-preserving K
+        if (f.vb == 4 && G == 4) hipLaunchKernelGGL((split_mfma_kernel<4, 4, true>), grid, dim3(64), 0, stream, a);
+        else if (f.vb == 4) hipLaunchKernelGGL((split_mfma_kernel<4, 8, true>), grid, dim3(64), 0, stream, a);
+        else if (G == 4) hipLaunchKernelGGL((split_mfma_kernel<6, 4, true>), grid, dim3(64), 0, stream, a);
+        else hipLaunchKernelGGL((split_mfma_kernel<6, 8, true>), grid, dim3(64), 0, stream, a);
+    } else if (f.vb == 4 && G == 4) hipLaunchKernelGGL((split_mfma_kernel<4, 4, false>), grid, dim3(64), 0, stream, a);
+    else if (f.vb == 4) hipLaunchKernelGGL((split_mfma_kernel<4, 8, false>), grid, dim3(64), 0, stream, a);
+    else if (G == 4) hipLaunchKernelGGL((split_mfma_kernel<6, 4, false>), grid, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL((split_mfma_kernel<6, 8, false>), grid, dim3(64), 0, stream, a);
     *err = hipGetLastError();
     return true;
 }
