@@ -151,6 +151,7 @@ def setup_uniform(args, wl, dev) -> Setup:
     if not args.fp16_layer:
         S.secondary["decode_with_scores"] = scores_figure(caches, view, S.keep, B, Hq, Hkv, D, N, sm, split, dev)
         S.secondary["multi_token"] = multi_figure(caches, view, S.keep, B, Hq, Hkv, D, N, sm, ptk, dev)
+        S.secondary["k_norm"] = knorm_figure(args, wl, bt, view, S.keep, sm, dev)
     qb = 2 if wl.dtype == "bf16" else 4
     kv = B * Hkv * N * ptk
     S.per_token_head, S.q_bytes = ptk, qb
@@ -242,6 +243,59 @@ def multi_figure(caches, view, keep, B, Hq, Hkv, D, N, sm, ptk, dev):
         keep += [ws, out, qs]
     fig["counted"] = "the layer's packed cache once, bf16 Q and fp32 output"
     return fig
+
+
+def knorm_figure(args, wl, bt, view, keep, sm, dev):
+    """The direction-preserving K codec at the same shape: layer caches
+    appended with k_norm = 1 (each prefill timed with events), then 32
+    decode calls rotated over them between one event pair after 8 untimed
+    ones.  Counted bytes per token-head: the plain format's plus the 4-byte
+    norm factor."""
+    import numpy as np
+    import torch
+
+    from quantized_kv_cache_token_amd import inputs, lkv
+
+    B, Hq, Hkv, D, N = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.n_ctx
+    outl = inputs.outlier_channels(wl.seed, Hkv, D) if wl.outliers else None
+    caches, pre = [], []
+    for layer in range(args.layers):
+        c = lkv.Cache(D, wl.group_size, wl.k_bits, wl.v_bits, Hkv, bt.numel(), device=dev, k_norm=1)
+        for b in range(B):
+            k, v = inputs.kv_rows(wl.seed, b, N, Hkv, D, dtype=wl.dtype, outliers=outl, layer=layer, device=dev)
+            e0, e1 = _event(), _event()
+            e0.record()
+            lkv.quant_append(c, k, v, torch.tensor([0, N], dtype=torch.int32, device=dev),
+                             torch.zeros(1, dtype=torch.int32, device=dev), bt[b:b + 1], N)
+            e1.record()
+            pre.append((e0, e1))
+            del k, v
+        caches.append(c)
+    split = lkv.decode_plan([caches[0]], [view], B, Hq)
+    ws = lkv.decode_workspace([caches[0]], [view], B, Hq, split, dev)
+    out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
+    qs = [inputs.queries(wl.seed, B, Hq, D, dtype=wl.dtype, layer=layer, device=dev) for layer in range(args.layers)]
+    calls = [lkv.prepare_decode([c], [view], q, sm, 0.0, split, out, ws) for c, q in zip(caches, qs)]
+    for i in range(8):
+        for f in calls[i % len(calls)]:
+            f()
+    e0, e1 = _event(), _event()
+    e0.record()
+    for i in range(32):
+        for f in calls[i % len(calls)]:
+            f()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 32 / 1e3
+    ptk = caches[0].chunk_bytes // 64
+    nbytes = B * Hkv * N * ptk + B * Hq * D * (2 + 4)
+    pre_s = float(np.median([a.elapsed_time(b) for a, b in pre])) / 1e3
+    pre_bytes = N * Hkv * (2 * D * 2 + ptk)
+    keep += [caches, ws, out, qs, calls]
+    return {"decode_us_per_call": round(t * 1e6, 1), "decode_GB/s": round(nbytes / t / 1e9, 1),
+            "bytes_per_token_head": ptk, "append_prefill_us": round(pre_s * 1e6, 1),
+            "append_prefill_GB/s": round(pre_bytes / pre_s / 1e9, 1),
+            "counted": "codes, scales, zeros and norm factors once, bf16 Q and fp32 output"}
 
 
 def setup_tiered(args, wl, dev) -> Setup:
