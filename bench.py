@@ -58,6 +58,8 @@ def parse():
                    help="after the timed steps, stream 1 GiB in and 1 GiB out (counter scaling reference)")
     p.add_argument("--fp16-layer", action="store_true", help="time the fp16 sensitive-layer format")
     p.add_argument("--no-tier", action="store_true", help="skip the tier-update and re-tiering secondary figures")
+    p.add_argument("--no-secondary", action="store_true",
+                   help="skip every secondary figure but the prefill append (counter passes: only the step's kernels run)")
     return p.parse_args()
 
 
@@ -148,7 +150,7 @@ def setup_uniform(args, wl, dev) -> Setup:
         S.keep += [k, v, q]
     S.keep += [caches, bt, lens, view, cu1, last, ws, out]
     ptk = caches[0].chunk_bytes // 64
-    if not args.fp16_layer:
+    if not args.fp16_layer and not args.no_secondary:
         S.secondary["decode_with_scores"] = scores_figure(caches, view, S.keep, B, Hq, Hkv, D, N, sm, split, dev)
         S.secondary["multi_token"] = multi_figure(caches, view, S.keep, B, Hq, Hkv, D, N, sm, ptk, dev)
         S.secondary["k_norm"] = knorm_figure(args, wl, bt, view, S.keep, sm, dev)
@@ -537,7 +539,7 @@ def main():
     secondary = dict(S.secondary)
     ptk, qb = S.per_token_head, S.q_bytes
     kb, vb = S.config.get("k_bits"), S.config.get("v_bits")
-    if args.workload == 2 and not args.fp16_layer and not args.no_tier:
+    if args.workload == 2 and not args.fp16_layer and not args.no_tier and not args.no_secondary:
         del S
         torch.cuda.empty_cache()
         secondary["tier_update"], secondary["retier"] = tier_figure(workloads.BY_INDEX[3], dev)
