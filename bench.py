@@ -222,7 +222,7 @@ def multi_figure(caches, view, keep, B, Hq, Hkv, D, N, sm, ptk, dev):
 
     fig = {}
     for T in (4, 16):
-        split = lkv.decode_plan([caches[0]], [view], B * T, Hq)
+        split = lkv.decode_plan_multi([caches[0]], [view], B, T, Hq)
         ws = lkv.decode_workspace([caches[0]], [view], B * T, Hq, split, dev)
         out = torch.empty(B, T, Hq, D, dtype=torch.float32, device=dev)
         qs = [torch.randn(B, T, Hq, D, device=dev).to(torch.bfloat16) for _ in caches]

@@ -369,6 +369,18 @@ int lkv_decode_attn(const lkv_cache* segs, const lkv_view* views, int32_t nseg, 
                               stream);
 }
 
+int lkv_decode_plan_multi(const lkv_cache* segs, const lkv_view* views, int32_t nseg, int32_t batch,
+                          int32_t q_per_seq, int32_t num_q_heads, int32_t* split_tokens)
+{
+    if (q_per_seq < 1 || (int64_t)batch * q_per_seq > INT32_MAX) return LKV_EINVAL;
+    // at 4 query heads per KV head the matrix-core kernel runs the query
+    // tokens in pairs: plan for the work items it launches
+    int32_t items = batch * q_per_seq;
+    if (segs && nseg >= 1 && segs[0].num_kv_heads > 0 && num_q_heads == 4 * segs[0].num_kv_heads)
+        items = batch * ((q_per_seq + 1) / 2);
+    return lkv_decode_plan(segs, views, nseg, items, num_q_heads, split_tokens);
+}
+
 int lkv_decode_attn_multi(const lkv_cache* segs, const lkv_view* views, int32_t nseg, const void* q,
                           int32_t q_dtype, int32_t batch, int32_t q_per_seq, int32_t num_q_heads, float sm_scale,
                           float tau_low, int32_t split_tokens, float* out, void* workspace, size_t workspace_bytes,
@@ -379,7 +391,7 @@ int lkv_decode_attn_multi(const lkv_cache* segs, const lkv_view* views, int32_t 
     for (int s = 0; s < nseg && views; s++)
         if (views[s].max_len < (s == 0 ? q_per_seq : 0) && batch > 0) return LKV_EINVAL;
     if (split_tokens == 0) {
-        const int st = lkv_decode_plan(segs, views, nseg, entries, num_q_heads, &split_tokens);
+        const int st = lkv_decode_plan_multi(segs, views, nseg, batch, q_per_seq, num_q_heads, &split_tokens);
         if (st != LKV_OK) return st;
     }
     if (batch > 0 && !out) return LKV_EINVAL;

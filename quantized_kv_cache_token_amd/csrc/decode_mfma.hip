@@ -361,11 +361,14 @@ __device__ __forceinline__ float block_softmax(const f32x4_t (&dot)[4], const ui
     // rarely rescaled, and p / L -- all that the output and the skip rule
     // depend on -- does not change.
     const float m_new = bmax > S.m_run + 8.0f ? bmax : S.m_run;
-    const float alpha = __builtin_amdgcn_exp2f(S.m_run - m_new);
+    // a masked block can leave a column with no live token so far (the
+    // earlier token of a query pair): its weights are 0, not exp2(NaN)
+    const float m_ref = PARTIAL && m_new == -INFINITY ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(S.m_run - m_ref);
     float bsum = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], score_scale, -m_new));
+        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], score_scale, -m_ref));
         bsum += p[i];
     }
     S.l_run = S.l_run * alpha + rows_sum(bsum);
@@ -489,11 +492,19 @@ __device__ __forceinline__ void block_pv(const BlockRegs<VB>& R, const uint8_t* 
     }
 }
 
-// One wave's split: split sp of KV head blockIdx.y of sequence blockIdx.z.
-template <int VB, int G, bool KN>
+// One wave's split: split sp of KV head blockIdx.y of grid entry blockIdx.z.
+// PAIR (the 8-head layout over 4 query heads per KV head): grid entry
+// blockIdx.z is a pair of consecutive query tokens (2i, 2i + 1) of one
+// sequence of a multi-token call; the layout's heads 0-3 are token 2i's
+// four heads and heads 4-7 token 2i + 1's, so every block is unpacked once
+// for both.  The earlier token's causal prefix is one token shorter: its
+// columns are masked in the split's last blocks.  An odd T's last token is
+// paired with itself and its second copy is not written.
+template <int VB, int G, bool KN, bool PAIR = false>
 __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint4* meta_lds)
 {
     static_assert(G == 4 || G == 8, "4 or 8 query heads per KV head");
+    static_assert(!PAIR || G == 8, "a pair fills the 8-head layout");
     constexpr int D = 128;
     const SegArgs& sg = a.seg;
     const Fmt& f = sg.f;
@@ -505,14 +516,37 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
     // depend on the length: they are requested together with it
     // (the sequence and length are uniform: computed before the lane-dependent
     // load, so that they stay in scalar registers)
-    const int seq = entry_seq(sg, b);
-    const int len = max(0, min(entry_len(sg, b), sg.max_blocks * BT));
+    int seq, len, e0 = b, e1 = b, len0 = 0;  // PAIR: the tokens' entries and the earlier one's length
+    if constexpr (PAIR) {
+        const int T = sg.q_per_seq, np = (T + 1) >> 1;
+        const int tk = 2 * (b % np);
+        e0 = b / np * T + tk;
+        e1 = tk + 1 < T ? e0 + 1 : e0;
+        seq = entry_seq(sg, e0);
+        len0 = max(0, min(entry_len(sg, e0), sg.max_blocks * BT));
+        len = max(0, min(entry_len(sg, e1), sg.max_blocks * BT));
+    } else {
+        seq = entry_seq(sg, b);
+        len = max(0, min(entry_len(sg, b), sg.max_blocks * BT));
+    }
+    // partial row (entry, query head) of layout head hh, and whether it is written
+    auto prow = [&](int hh) -> int64_t {
+        if constexpr (PAIR) return (int64_t)(hh >= 4 ? e1 : e0) * a.num_q_heads + kvh * 4 + (hh & 3);
+        else return (int64_t)b * a.num_q_heads + kvh * G + hh;
+    };
+    auto pwrite = [&](int hh) { return !PAIR || hh < 4 || e1 != e0; };
     const int32_t* bt = sg.block_table + (int64_t)seq * sg.max_blocks + t0 / BT;
     const int bt_lane = lane < min(64, sg.max_blocks - t0 / BT) ? bt[lane] : 0;
     asm volatile("" ::: "memory");  // both loads are issued before either is waited for
     const int t1 = min(t0 + a.split_tokens, len);
     if (t1 <= t0) {  // a split past the end: only (m, L) = (-inf, 0), its o row is never read
-        if (threadIdx.x < G) {
+        if constexpr (PAIR) {
+            if (lane < G && pwrite(lane)) {
+                float* p = a.partials + (prow(lane) * a.total_splits + sg.split_base + sp) * (D + 2);
+                p[D] = -INFINITY;
+                p[D + 1] = 0.0f;
+            }
+        } else if (threadIdx.x < G) {
             float* p = a.partials + (((int64_t)b * a.num_q_heads + kvh * G + threadIdx.x) * a.total_splits +
                                      sg.split_base + sp) * (D + 2);
             p[D] = -INFINITY;
@@ -538,7 +572,7 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
     uint32_t qb[4][4];
     float qpart = 0.0f;
     {
-        const uint4* src = (const uint4*)(a.q + ((int64_t)b * a.num_q_heads + head) * D + 32 * q);
+        const uint4* src = (const uint4*)(a.q + (PAIR ? prow(hc) : (int64_t)b * a.num_q_heads + head) * D + 32 * q);
         const bool live = (q >> 1) == gc;
         uint32_t qw[16];  // channels 2i, 2i+1 of this lane group's 32
 #pragma unroll
@@ -579,6 +613,11 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
     // the split's block-table entries (at most 64), one per lane, so that
     // every chunk address is a register read instead of a memory round trip
     const int nblk = (t1 - t0 + BT - 1) / BT;
+    // end of this lane's column's tokens in the split, and of the tokens
+    // every column has (they differ only for a pair: t1 belongs to the later
+    // token, the earlier one ends a token sooner)
+    const int tl0 = PAIR ? max(t0, min(t0 + a.split_tokens, len0)) : t1;
+    const int tl = PAIR && c < 8 ? tl0 : t1;
     // format fields as plain values (kept in scalar registers)
     const uint8_t* const pool = sg.pool;
     const int64_t chunk = f.chunk;
@@ -616,24 +655,47 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
         block_qk<VB>(R, qb, q128, mk, dot);
         load_k<VB>(R, cn, off_kc, c, q);
         asm volatile("" ::: "memory");
-        const int nlive = min(BT, t1 - t0 - k * BT);
+        const int nlive = min(BT, tl - t0 - k * BT);  // PAIR: this lane's column's (may be <= 0)
         float p[16];
         uint32_t keep;
-        float* srow = sg.scores != nullptr ? sg.scores + srow0 + (int64_t)k * BT : nullptr;
+        float* srow = !PAIR && sg.scores != nullptr ? sg.scores + srow0 + (int64_t)k * BT : nullptr;
         const float alpha =
             block_softmax<VB, G, PARTIAL, KN>(dot, lds, S, qsum, a.score_scale, a.tau_low, nlive, q, c, p, keep, srow);
         block_pv<VB, G, PARTIAL>(R, lds, S, p, alpha, keep, q, c, hA, mk);
         load_v<VB>(R, cn, off_vc, c, q);
         asm volatile("" ::: "memory");
     };
-    // full blocks, then the split's last block if it has dead slots
-    const int nfull = (t1 - t0) / BT;
+    // full blocks, then the split's last block if it has dead slots (PAIR:
+    // blocks full for both tokens, then the rest, at most two, masked per
+    // column)
+    const int nfull = (tl0 - t0) / BT;
     for (int k = 0; k < nfull; k++) block(k, std::false_type{});
-    if (nfull < nblk) block(nfull, std::true_type{});
+    if constexpr (PAIR) {
+        for (int k = nfull; k < nblk; k++) block(k, std::true_type{});
+    } else if (nfull < nblk) block(nfull, std::true_type{});
 
     // ---- write the partial (o, m, L) of every head of the group
     // P.V output: lane (column c, row group q) holds rows 4q .. 4q+3 of each
     // channel tile T; rows 4q, 4q+1 are head hA (hi, lo), 4q+2, 4q+3 head hA+1.
+    if constexpr (PAIR) {
+        // rows hA, hA + 1 belong to one token (hA even)
+        const int64_t soff = (int64_t)(sg.split_base + sp) * (D + 2);
+        float* pa = a.partials + prow(hA) * a.total_splits * (D + 2) + soff;
+        float* pb = a.partials + prow(hA + 1) * a.total_splits * (D + 2) + soff;
+        if (pwrite(hA)) {
+#pragma unroll
+            for (int T = 0; T < 8; T++) {
+                pa[16 * T + c] = S.acc[T][0] + S.acc[T][1];
+                pb[16 * T + c] = S.acc[T][2] + S.acc[T][3];
+            }
+        }
+        if (q == 0 && part == 0 && pwrite(hc)) {
+            float* pm = a.partials + prow(hc) * a.total_splits * (D + 2) + soff;
+            pm[D] = S.m_run;
+            pm[D + 1] = S.l_run;
+        }
+        return;
+    }
     float* base = a.partials + ((int64_t)b * a.num_q_heads + kvh * G) * a.total_splits * (D + 2);
     const int64_t hstride = (int64_t)a.total_splits * (D + 2);
     const int64_t soff = (int64_t)(sg.split_base + sp) * (D + 2);
@@ -655,6 +717,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
 {
     __shared__ uint4 meta_lds[meta_bytes<KN>() / 16];
     split_body<VB, G, KN>(a, blockIdx.x, meta_lds);
+}
+
+// Query-token pairs of a multi-token call with 4 query heads per KV head
+// (split_body's PAIR): grid z = sequence x ceil(T / 2) pairs.
+template <int VB, bool KN>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void split_mfma_pair_kernel(MfmaArgs a)
+{
+    __shared__ uint4 meta_lds[meta_bytes<KN>() / 16];
+    split_body<VB, 8, KN, true>(a, blockIdx.x, meta_lds);
 }
 
 // Both segments of a tiered cache in one launch: workgroups [0, n0) run the
@@ -729,6 +800,16 @@ bool launch_decode_split_mfma(const SegArgs& s, const void* q, int q_dtype, int3
     const Fmt& f = s.f;
     const int G = num_q_heads / f.H;
     const MfmaArgs a = mfma_args(s, q, num_q_heads, sm_scale, tau_low, split_tokens, total_splits, partials);
+    const int T = s.q_per_seq;
+    if (T > 1 && G == 4) {  // batch counts B * T entries: B * ceil(T / 2) pairs
+        dim3 grid((unsigned)s.n_splits, (unsigned)f.H, (unsigned)(batch / T * ((T + 1) / 2)));
+        if (f.vb == 4 && f.k_norm) hipLaunchKernelGGL((split_mfma_pair_kernel<4, true>), grid, dim3(64), 0, stream, a);
+        else if (f.vb == 4) hipLaunchKernelGGL((split_mfma_pair_kernel<4, false>), grid, dim3(64), 0, stream, a);
+        else if (f.k_norm) hipLaunchKernelGGL((split_mfma_pair_kernel<6, true>), grid, dim3(64), 0, stream, a);
+        else hipLaunchKernelGGL((split_mfma_pair_kernel<6, false>), grid, dim3(64), 0, stream, a);
+        *err = hipGetLastError();
+        return true;
+    }
     dim3 grid((unsigned)s.n_splits, (unsigned)f.H, (unsigned)batch);
     if (f.k_norm) {  // direction-preserving K
         if (f.vb == 4 && G == 4) hipLaunchKernelGGL((split_mfma_kernel<4, 4, true>), grid, dim3(64), 0, stream, a);

@@ -45,7 +45,7 @@ EXPORTS = ["lkv_status_string", "lkv_chunk_layout", "lkv_quant_append", "lkv_dec
            "lkv_decode_workspace_bytes", "lkv_decode_attn", "lkv_decode_split", "lkv_decode_combine",
            "lkv_decode_scores_workspace_bytes", "lkv_decode_attn_scores",
            "lkv_default_thresholds", "lkv_tier_workspace_bytes", "lkv_tier_update",
-           "lkv_retier_workspace_bytes", "lkv_retier", "lkv_decode_attn_multi"]
+           "lkv_retier_workspace_bytes", "lkv_retier", "lkv_decode_attn_multi", "lkv_decode_plan_multi"]
 
 
 def lib():
@@ -76,6 +76,7 @@ def lib():
                             C.c_int),
         "lkv_retier_workspace_bytes": ([I32, I32, I32], I64),
         "lkv_decode_attn_multi": ([PC, PV, I32, P, I32, I32, I32, I32, F, F, I32, P, P, C.c_size_t, V], C.c_int),
+        "lkv_decode_plan_multi": ([PC, PV, I32, I32, I32, I32, C.POINTER(I32)], C.c_int),
         "lkv_retier": ([PC, PV, P, I32, PC, PV, P, I32, F, F, PC, P, I32, PC, P, I32, P, P, P, P, I32, P,
                         C.c_size_t, V], C.c_int),
     }
@@ -176,6 +177,15 @@ def decode_plan(caches, views, batch: int, num_q_heads: int) -> int:
     return out.value
 
 
+def decode_plan_multi(caches, views, batch: int, q_per_seq: int, num_q_heads: int) -> int:
+    """lkv_decode_plan_multi: the split size decode_attn_multi plans."""
+    cs, vs, n = _segs(caches, views)
+    out = C.c_int32()
+    _check("lkv_decode_plan_multi", lib().lkv_decode_plan_multi(cs, vs, n, batch, q_per_seq, num_q_heads,
+                                                                C.byref(out)))
+    return out.value
+
+
 def decode_workspace_bytes(caches, views, batch: int, num_q_heads: int, split_tokens: int) -> int:
     cs, vs, n = _segs(caches, views)
     r = lib().lkv_decode_workspace_bytes(cs, vs, n, batch, num_q_heads, split_tokens)
@@ -215,7 +225,7 @@ def decode_attn_multi(caches, views, q: torch.Tensor, sm_scale: float, tau_low: 
     B, T, Hq, D = q.shape
     assert q.is_contiguous()
     if split_tokens == 0:
-        split_tokens = decode_plan(caches, views, B * T, Hq)
+        split_tokens = decode_plan_multi(caches, views, B, T, Hq)
     if workspace is None:
         workspace = decode_workspace(caches, views, B * T, Hq, split_tokens, q.device)
     if out is None:

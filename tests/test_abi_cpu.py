@@ -188,6 +188,25 @@ def test_decode_multi_rejects_bad_arguments():
     assert L.lkv_decode_workspace_bytes(cs, vs, 1, 8 * 4, 32, 256) == 8 * 4 * 32 * 4 * 130 * 4
 
 
+def test_multi_token_plan_counts_query_pairs_at_four_heads_per_kv_head():
+    L = lkv.lib()
+    out = C.c_int32()
+    vs = (lkv._View * 1)(_view(max_len=32768, max_blocks=512))
+
+    def plan(B, T, Hq, Hkv=8):
+        cs = (lkv._Cache * 1)(_cache(num_kv_heads=Hkv))
+        st = L.lkv_decode_plan_multi(cs, vs, 1, B, T, Hq, C.byref(out))
+        return out.value if st == lkv.OK else st
+
+    # G = 4: B * ceil(T / 2) pairs; G = 8: B * T query tokens (2048 work items)
+    assert plan(8, 4, 32) == 2048      # 8 x 2 pairs x 8 heads x 512 blocks / 2048 = 32 blocks
+    assert plan(8, 3, 32) == 2048      # ceil(3 / 2) = 2 pairs
+    assert plan(8, 4, 64) == 4096      # 8 x 4 tokens x 8 heads x 512 / 2048 = 64 blocks
+    assert plan(8, 1, 32) == 1024      # one token: the plain decode plan
+    assert plan(8, 0, 32) == lkv.EINVAL
+    assert plan(1 << 20, 1 << 12, 32) == lkv.EINVAL
+
+
 def test_status_strings():
     assert lkv.status_string(lkv.OK) == "ok"
     assert "invalid" in lkv.status_string(lkv.EINVAL)

@@ -70,12 +70,28 @@ def test_multi_causal_prefix_and_plan():
     lens = [40, 513, 2000]
     got, want, vmax, (pair, view, q, bt) = _multi_case(fmt, G, "bf16", lens, T, 0.0, 0)
     assert_attention_close(got.reshape(-1, *got.shape[2:]), want.reshape(-1, *want.shape[2:]), vmax, "planned")
-    split = lkv.decode_plan([pair.gpu], [view], len(lens) * T, 2 * G)
+    split = lkv.decode_plan_multi([pair.gpu], [view], len(lens), T, 2 * G)
     for i in (0, T - 1):
         pre = torch.tensor([n - T + i + 1 for n in lens], dtype=torch.int32).cuda()
         dec = lkv.decode_attn([pair.gpu], [lkv.View(view.block_table, pre, max(lens))], q[:, i].contiguous().cuda(),
                               sm_scale(128), 0.0, split)
         assert np.array_equal(got[:, i], dec.cpu().numpy())
+
+
+@pytest.mark.parametrize("vb", [4, 6])
+@pytest.mark.parametrize("T", [2, 3, 5, 8])
+@pytest.mark.parametrize("split", [64, 128])
+def test_query_pairs_at_block_edges(vb, T, split):
+    """4 query heads per KV head: query tokens run in pairs through the
+    8-head matrix-core layout.  Prefixes that end on a block edge give the
+    earlier token of a pair no live token in the split's last block (or in a
+    whole split); an odd T pairs its last token with itself."""
+    fmt = (128, 64, 6, vb)
+    lens = [T, 64 + T - 1, 64 + T, 128 + T - 1, 129 + T, 300, 1100]
+    got, want, vmax, (pair, view, q, bt) = _multi_case(fmt, 4, "bf16", lens, T, 1e-4, split, seed=45)
+    assert np.all(np.isfinite(got))
+    assert_attention_close(got.reshape(-1, *got.shape[2:]), want.reshape(-1, *want.shape[2:]), vmax,
+                           f"pairs v{vb} T {T} split {split}")
 
 
 @pytest.mark.parametrize("G", [4, 8])
