@@ -53,22 +53,17 @@ struct MfmaArgs {
     float* partials;
 };
 
-// x | (x << 10): one VALU instruction.
-__device__ __forceinline__ uint32_t lshl10_or(uint32_t x)
-{
-    uint32_t y;
-    asm("v_lshl_or_b32 %0, %1, 10, %1" : "=v"(y) : "v"(x));
-    return y;
-}
+// The bit manipulations below are plain C, never inline asm: a matrix-core
+// instruction that reads a VGPR just written by a vector instruction needs
+// wait states, which the compiler inserts only for instructions it can see.
+// (An asm block feeding an MFMA operand one instruction later gave wrong
+// products under some schedules.)
 
-// (x & m) | c in one instruction; m and c live in VGPRs (a VOP3 instruction
-// of this family reads at most one scalar operand).
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c)
-{
-    uint32_t y;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(y) : "v"(x), "v"(m), "v"(c));
-    return y;
-}
+// x | (x << 10) (v_lshl_or_b32).
+__device__ __forceinline__ uint32_t lshl10_or(uint32_t x) { return (x << 10) | x; }
+
+// (x & m) | c (v_and_or_b32).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) { return (x & m) | c; }
 
 // Constants of the code-to-bf16 conversions, kept in registers.
 struct Magic {
@@ -76,15 +71,19 @@ struct Magic {
     uint32_t m4, c4;   // 0x00780078, 0x41804180: 4-bit code (at bit 3) -> 16 + c
 };
 
+// v in a VGPR, its value hidden from the optimiser so that the constants
+// stay in registers and (x & m) | c is one v_and_or_b32 rather than two
+// instructions with literals.  The asm holds no instruction: the v_mov that
+// sets the register is the compiler's own.
+__device__ __forceinline__ uint32_t opaque(uint32_t v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
 __device__ __forceinline__ Magic make_magic()
 {
-    Magic k;
-    // opaque moves so that the constants are materialised once in VGPRs
-    asm volatile("v_mov_b32 %0, 0x003F003F" : "=v"(k.m6));
-    asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(k.c6));
-    asm volatile("v_mov_b32 %0, 0x00780078" : "=v"(k.m4));
-    asm volatile("v_mov_b32 %0, 0x41804180" : "=v"(k.c4));
-    return k;
+    return Magic{opaque(0x003F003Fu), opaque(0x43004300u), opaque(0x00780078u), opaque(0x41804180u)};
 }
 
 // Two adjacent 6-bit codes at bit BIT of an N-word bitstream, as a pair of
@@ -109,11 +108,13 @@ __device__ __forceinline__ uint32_t pair6(const uint32_t (&w)[N], const Magic& k
 // packed 16-bit shift and one and_or; the four that straddle a half pair up
 // as (2, 13) and (5, 10).  Pair j of group n covers channels
 //   KPAIR[j] = {(0,3), (1,4), (6,8), (7,9), (11,14), (12,15), (2,13), (5,10)}.
+// Both 16-bit halves of w shifted right by the matching half of sh (each
+// below 16) (v_pk_lshrrev_b16).
+typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pk_shr(uint32_t w, uint32_t sh)
 {
-    uint32_t y;
-    asm("v_pk_lshrrev_b16 %0, %1, %2" : "=v"(y) : "s"(sh), "v"(w));
-    return y;
+    const u16x2_t r = __builtin_bit_cast(u16x2_t, w) >> __builtin_bit_cast(u16x2_t, sh);
+    return __builtin_bit_cast(uint32_t, r);
 }
 
 __device__ __forceinline__ void k16_pairs(uint32_t w0, uint32_t w1, uint32_t w2, const Magic& k, uint32_t (&o)[8])
