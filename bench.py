@@ -448,8 +448,8 @@ def setup_ragged(args, wl, dev) -> Setup:
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the kernel runs on one GPU's share; see the sharding notes).", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path; its kernels run on one "
+              "GPU's share of a cache sharded by KV head.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -70,7 +70,7 @@ extern "C" {
 typedef enum {
     LKV_OK = 0,
     LKV_EINVAL = -1,       /* null pointer, bad size or inconsistent arguments */
-    LKV_EUNSUPPORTED = -2, /* a format or shape this build has no kernel for */
+    LKV_EUNSUPPORTED = -2, /* a format or shape the library has no kernel for */
     LKV_EHIP = -3          /* the HIP runtime refused a launch */
 } lkv_status;
 
