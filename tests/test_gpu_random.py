@@ -1,15 +1,23 @@
-"""Seeded random decode and multi-token cases against the oracle: every
-format, G, one or two segments, ragged lengths drawn half from block and
-split edges, split sizes, skip thresholds and query dtypes.  Attention
-within max|d| <= 1e-3 max|v_hat| and rel L2 <= 1e-4.  The cases are fixed
-by the seed; a wider run of the same generator (7800 cases) found no
+"""Seeded random cases against the oracle.
+
+Decode and multi-token queries: every format, G, one or two segments,
+ragged lengths drawn half from block and split edges, split sizes, skip
+thresholds and query dtypes; attention within max|d| <= 1e-3 max|v_hat|
+and rel L2 <= 1e-4.  Appends (a prefill, then more rows into partly filled
+blocks) and tier updates followed by two re-tierings: bit-exact pools,
+tiers and counts.  The cases are fixed by the seeds; wider runs of the same
+generators (7800 decode cases, 23900 append and tier cases) found no
 failure."""
 import numpy as np
 import pytest
+import torch
 
-from tests.gpu_common import assert_attention_close
+from quantized_kv_cache_token_amd import inputs
+from tests import test_gpu_retier as TR
+from tests.gpu_common import Pair, assert_attention_close, say
+from tests.oracle_cases import block_tables
 from tests.test_gpu_multi import _multi_case
-from tests.test_gpu_parity import FORMATS, _decode_case
+from tests.test_gpu_parity import FORMATS, _decode_case, _prefill
 
 pytestmark = pytest.mark.gpu
 
@@ -45,3 +53,50 @@ def test_seeded_random_cases():
         else:
             got, want, vmax = _decode_case(fmt, G, qd, lens, tau, split, seed=seed, Hkv=Hkv, nseg=nseg)
         assert_attention_close(got, want, vmax, what)
+
+
+N_BITEXACT = 120
+APPEND_EDGE = [1, 2, 63, 64, 65, 127, 128, 129]
+TIER_EDGE = APPEND_EDGE + [2047, 2048, 2049]
+
+
+def test_seeded_random_appends_and_tiers_bit_exact():
+    rng = np.random.default_rng(11)
+    for i in range(N_BITEXACT):
+        if rng.random() < 0.5:
+            fmt = FORMATS[rng.integers(len(FORMATS))]
+            D, g, kb, vb = fmt
+            dtype = str(rng.choice(["f32", "bf16", "f16"]))
+            Hkv = int(rng.choice([1, 2, 3]))
+            B = int(rng.integers(1, 5))
+            lens = [int(rng.choice(APPEND_EDGE)) if rng.random() < 0.5 else int(rng.integers(0, 700))
+                    for _ in range(B)]
+            extra = [int(rng.integers(0, 70)) for _ in range(B)]
+            bt, nblk = block_tables([n + e + 1 for n, e in zip(lens, extra)], rng)
+            pair = Pair(D, g, kb, vb, Hkv, nblk)
+            seed = int(rng.integers(1, 10**6))
+            say("case", i, "append", fmt, dtype, "Hkv", Hkv, "lens", lens, "extra", extra, "seed", seed)
+            _prefill(pair, lens, Hkv, D, dtype, seed, bt, outliers=bool(rng.random() < 0.5))
+            assert pair.pool_equal(), pair.first_pool_mismatch()
+            K, V = [], []
+            for b, e in enumerate(extra):
+                k, v = inputs.kv_rows(seed + 1, b, e, Hkv, D, dtype=dtype)
+                K.append(k)
+                V.append(v)
+            cu = np.concatenate([[0], np.cumsum(extra)]).astype(np.int32)
+            pair.append(torch.cat(K), torch.cat(V), cu, np.array(lens, np.int32), bt)
+            assert pair.pool_equal(), pair.first_pool_mismatch()
+        else:
+            Hkv = int(rng.choice([1, 2]))
+            B = int(rng.integers(1, 4))
+            lens = [int(rng.choice(TIER_EDGE)) if rng.random() < 0.4 else int(rng.integers(1, 3000))
+                    for _ in range(B)]
+            seed = int(rng.integers(1, 10**6))
+            say("case", i, "tier", "Hkv", Hkv, "lens", lens, "seed", seed)
+            h, hbt, nh, m, mbt, nm, tl, th = TR._tiered(lens, Hkv, seed, rng)
+            for it in range(2):
+                frac = (float(rng.uniform(0, 0.5)), float(rng.uniform(0, 0.5)))
+                r = TR._retier_both(h, hbt, nh, m, mbt, nm, tl, th, seed + 7 * it + 1, rng, frac=frac,
+                                    boundaries=bool(rng.random() < 0.5))
+                TR._check_bit_exact(r)
+                h, hbt, nh, m, mbt, nm = r["dh"], r["dhb"], r["nh"], r["dm"], r["dmb"], r["nm"]
