@@ -169,6 +169,13 @@ int lkv_decode_attn(const lkv_cache* segs, const lkv_view* views, int32_t nseg,
                     float sm_scale, float tau_low, int32_t split_tokens,
                     float* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Split size for lkv_decode_attn_multi (host): lkv_decode_plan over the
+ * work items the call launches, batch * T query tokens, or batch * ceil(T/2)
+ * query-token pairs at 4 query heads per KV head (the matrix-core kernel
+ * then runs two tokens of a sequence through one pass over its blocks). */
+int lkv_decode_plan_multi(const lkv_cache* segs, const lkv_view* views, int32_t nseg,
+                          int32_t batch, int32_t q_per_seq, int32_t num_q_heads, int32_t* split_tokens);
+
 /* Attention of several query tokens per sequence over the packed cache,
  * with a causal mask: the queries of a chunked prefill, or draft tokens to
  * verify.  The TurboQuant page states that the quantised cache stacks with
@@ -185,13 +192,6 @@ int lkv_decode_attn(const lkv_cache* segs, const lkv_view* views, int32_t nseg,
  * workspace  lkv_decode_workspace_bytes(..., batch * T, ...) bytes
  * views[0].max_len must be at least T; a sequence shorter than T gives
  * zero rows for the queries that see no token.  T = 1 is lkv_decode_attn. */
-/* Split size for lkv_decode_attn_multi (host): lkv_decode_plan over the
- * work items the call launches, batch * T query tokens, or batch * ceil(T/2)
- * query-token pairs at 4 query heads per KV head (the matrix-core kernel
- * then runs two tokens of a sequence through one pass over its blocks). */
-int lkv_decode_plan_multi(const lkv_cache* segs, const lkv_view* views, int32_t nseg,
-                          int32_t batch, int32_t q_per_seq, int32_t num_q_heads, int32_t* split_tokens);
-
 int lkv_decode_attn_multi(const lkv_cache* segs, const lkv_view* views, int32_t nseg, const void* q,
                           int32_t q_dtype, int32_t batch, int32_t q_per_seq, int32_t num_q_heads, float sm_scale,
                           float tau_low, int32_t split_tokens, float* out, void* workspace, size_t workspace_bytes,
