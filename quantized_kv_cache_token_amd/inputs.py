@@ -95,6 +95,8 @@ def tier_scores(base: int, seq: int, n_tokens: int, tau_low: float, tau_high: fl
     n_h = int(round(frac_high * n_tokens))
     n_m = int(round(frac_mid * n_tokens))
     n_l = n_tokens - n_h - n_m
+    if n_l < 0:
+        raise ValueError("frac_high + frac_mid must not exceed 1")
     u = torch.rand(n_tokens, generator=g, dtype=torch.float32)
     lo = torch.empty(n_tokens, dtype=torch.float32)
     width = torch.empty(n_tokens, dtype=torch.float32)
@@ -105,7 +107,6 @@ def tier_scores(base: int, seq: int, n_tokens: int, tau_low: float, tau_high: fl
     perm = torch.randperm(n_tokens, generator=g)
     out = torch.empty(n_tokens, dtype=torch.float32)
     out[perm] = vals
-    assert n_l >= 0
     return out
 
 

@@ -97,6 +97,12 @@ def _check(fn: str, status: int) -> None:
         raise LkvError(fn, status)
 
 
+def _require(cond: bool, what: str) -> None:
+    """Argument check of the binding; unlike assert it is kept under -O."""
+    if not cond:
+        raise ValueError(what)
+
+
 def _stream(stream=None):
     s = stream if stream is not None else torch.cuda.current_stream()
     return C.c_void_p(s.cuda_stream)
@@ -131,7 +137,8 @@ class Cache:
         nbytes = self.num_blocks * self.num_kv_heads * self.chunk_bytes
         if self.pool is None:
             self.pool = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
-        assert self.pool.numel() == nbytes and self.pool.dtype == torch.uint8
+        _require(self.pool.numel() == nbytes and self.pool.dtype == torch.uint8,
+                 f"pool must be {nbytes} uint8 bytes")
 
     def c(self) -> _Cache:
         return _Cache(self.head_dim, self.group_size, self.k_bits, self.v_bits, self.num_kv_heads,
@@ -147,8 +154,10 @@ class View:
     sum_len: int = 0            # host hint: total of seq_lens (0 = unknown), read by the split plan only
 
     def c(self) -> _View:
-        assert self.block_table.dtype == torch.int32 and self.seq_lens.dtype == torch.int32
-        assert self.block_table.is_contiguous() and self.seq_lens.is_contiguous()
+        _require(self.block_table.dtype == torch.int32 and self.seq_lens.dtype == torch.int32,
+                 "block_table and seq_lens must be int32")
+        _require(self.block_table.is_contiguous() and self.seq_lens.is_contiguous(),
+                 "block_table and seq_lens must be contiguous")
         return _View(self.block_table.data_ptr(), self.seq_lens.data_ptr(), self.block_table.shape[1],
                      int(self.max_len), int(self.sum_len))
 
@@ -156,8 +165,9 @@ class View:
 def quant_append(cache: Cache, k: torch.Tensor, v: torch.Tensor, cu_new: torch.Tensor, start_pos: torch.Tensor,
                  block_table: torch.Tensor, max_new: int, stream=None) -> None:
     """lkv_quant_append: k, v [total_new][Hkv][D] (fp32, bf16 or fp16)."""
-    assert k.dtype == v.dtype and k.is_contiguous() and v.is_contiguous()
-    assert k.shape == v.shape and k.shape[1:] == (cache.num_kv_heads, cache.head_dim)
+    _require(k.dtype == v.dtype and k.is_contiguous() and v.is_contiguous(), "k and v: one dtype, contiguous")
+    _require(k.shape == v.shape and k.shape[1:] == (cache.num_kv_heads, cache.head_dim),
+             "k and v must be [total_new][Hkv][D] of the cache")
     cc = cache.c()
     _check("lkv_quant_append", lib().lkv_quant_append(
         C.byref(cc), _ptr(k), _ptr(v), _DTYPE[k.dtype], _ptr(cu_new), _ptr(start_pos), _ptr(block_table),
@@ -166,7 +176,7 @@ def quant_append(cache: Cache, k: torch.Tensor, v: torch.Tensor, cu_new: torch.T
 
 def _segs(caches, views):
     n = len(caches)
-    assert n == len(views)
+    _require(n == len(views), "one view per cache")
     return (_Cache * n)(*[c.c() for c in caches]), (_View * n)(*[v.c() for v in views]), n
 
 
@@ -203,7 +213,7 @@ def decode_attn(caches, views, q: torch.Tensor, sm_scale: float, tau_low: float 
                 out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
     """lkv_decode_attn: q [B][Hq][D] (fp32 or bf16) -> out fp32 [B][Hq][D]."""
     B, Hq, D = q.shape
-    assert q.is_contiguous()
+    _require(q.is_contiguous(), "q must be contiguous")
     if split_tokens == 0:
         split_tokens = decode_plan(caches, views, B, Hq)
     if workspace is None:
@@ -223,7 +233,7 @@ def decode_attn_multi(caches, views, q: torch.Tensor, sm_scale: float, tau_low: 
     """lkv_decode_attn_multi: q [B][T][Hq][D] (fp32 or bf16), the last T
     tokens of the first segment -> out fp32 [B][T][Hq][D], causal."""
     B, T, Hq, D = q.shape
-    assert q.is_contiguous()
+    _require(q.is_contiguous(), "q must be contiguous")
     if split_tokens == 0:
         split_tokens = decode_plan_multi(caches, views, B, T, Hq)
     if workspace is None:
@@ -252,8 +262,9 @@ def decode_attn_scores(caches, views, q: torch.Tensor, score_acc: torch.Tensor, 
     token's softmax weight summed over the query heads to score_acc
     (fp32 [nseg][B][stride])."""
     B, Hq, D = q.shape
-    assert q.is_contiguous() and score_acc.is_contiguous() and score_acc.dtype == torch.float32
-    assert score_acc.dim() == 3 and score_acc.shape[:2] == (len(caches), B)
+    _require(q.is_contiguous() and score_acc.is_contiguous() and score_acc.dtype == torch.float32,
+             "q and score_acc contiguous, score_acc fp32")
+    _require(score_acc.dim() == 3 and score_acc.shape[:2] == (len(caches), B), "score_acc must be [nseg][B][stride]")
     if split_tokens == 0:
         split_tokens = decode_plan(caches, views, B, Hq)
     if workspace is None:
@@ -301,7 +312,8 @@ def tier_update(src: Cache, src_view: View, scores: torch.Tensor, tau_low: float
                 workspace: torch.Tensor | None = None, stream=None) -> None:
     """lkv_tier_update: scores fp32 [B][stride]; tiers uint8 [B][stride]."""
     B, stride = scores.shape
-    assert scores.dtype == torch.float32 and tiers.dtype == torch.uint8 and tiers.shape == scores.shape
+    _require(scores.dtype == torch.float32 and tiers.dtype == torch.uint8 and tiers.shape == scores.shape,
+             "scores fp32 and tiers uint8, both [B][stride]")
     if workspace is None:
         workspace = torch.empty(max(tier_workspace_bytes(B, stride), 4), dtype=torch.uint8, device=scores.device)
     cs, ch, cm, sv = src.c(), dst_h.c(), dst_m.c(), src_view.c()
@@ -327,9 +339,10 @@ def retier(h: Cache, h_view: View, h_scores: torch.Tensor, m: Cache, m_view: Vie
     same shapes."""
     B, hs = h_scores.shape
     ms = m_scores.shape[1]
-    assert m_scores.shape[0] == B and h_scores.dtype == torch.float32 and m_scores.dtype == torch.float32
-    assert h_tiers.dtype == torch.uint8 and h_tiers.shape == h_scores.shape
-    assert m_tiers.dtype == torch.uint8 and m_tiers.shape == m_scores.shape
+    _require(m_scores.shape[0] == B and h_scores.dtype == torch.float32 and m_scores.dtype == torch.float32,
+             "scores fp32 [B][stride] per segment")
+    _require(h_tiers.dtype == torch.uint8 and h_tiers.shape == h_scores.shape, "h_tiers uint8, shape of h_scores")
+    _require(m_tiers.dtype == torch.uint8 and m_tiers.shape == m_scores.shape, "m_tiers uint8, shape of m_scores")
     if workspace is None:
         workspace = torch.empty(max(retier_workspace_bytes(B, hs, ms), 8), dtype=torch.uint8,
                                 device=h_scores.device)
