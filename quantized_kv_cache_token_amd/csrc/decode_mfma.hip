@@ -10,6 +10,10 @@
 //   dot'(t, h, g) = sum_{d in g} q_hd * (128 + c_td)
 // where the bf16 A operand is built from the 6-bit code c by placing it in
 // the mantissa of 128.0 (exact); Q is the B operand, masked to the group.
+// With 4 query heads per KV head (one query token) the K dimension of each
+// product carries two 16-token sets instead, and the columns are (set, head,
+// group): every column is used and a lane scores 8 tokens of a block, not 16
+// (the two-set layout below).
 // The score of a token is then
 //   s(t, h) = sm * sum_g s_g(t) * (dot'(t, h, g) - (128 + z_g(t)) * qsum(h, g))
 // with qsum(h, g) the sum of q over the group, i.e. the dequantised dot
@@ -19,8 +23,8 @@
 // the K dimension is tokens, columns are channels.  The A operand carries
 // p'(t) = p(t) * s_v(t) split into a bf16 high part and the bf16 rounding
 // of the remainder (16 significant bits together); the B operand carries
-// OFF + c (OFF = 16 for 4-bit codes, 128 for 6-bit codes, both exact in
-// bf16).  sum_t p'(t) (OFF + z(t)) is accumulated beside it and subtracted
+// OFF + c (OFF = 128 for 6-bit codes and for the first nibble pair of a
+// 4-bit word, 16 for its other pairs; all exact in bf16).  sum_t p'(t) (OFF + z(t)) is accumulated beside it and subtracted
 // at the end, giving sum_t p(t) s_v(t) (c_t - z(t)) = sum_t p(t) v_hat(t).
 //
 // The QK result registers of a lane are exactly the P.V A-operand registers
@@ -69,6 +73,7 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
 struct Magic {
     uint32_t m6, c6;   // 0x003F003F, 0x43004300: 6-bit code -> 128 + c
     uint32_t m4, c4;   // 0x00780078, 0x41804180: 4-bit code (at bit 3) -> 16 + c
+    uint32_t m4lo;     // 0x000F000F: 4-bit code at bit 0 -> 128 + c (with c6)
 };
 
 // v in a VGPR, its value hidden from the optimiser so that the constants
@@ -83,7 +88,8 @@ __device__ __forceinline__ uint32_t opaque(uint32_t v)
 
 __device__ __forceinline__ Magic make_magic()
 {
-    return Magic{opaque(0x003F003Fu), opaque(0x43004300u), opaque(0x00780078u), opaque(0x41804180u)};
+    return Magic{opaque(0x003F003Fu), opaque(0x43004300u), opaque(0x00780078u), opaque(0x41804180u),
+                 opaque(0x000F000Fu)};
 }
 
 // Two adjacent 6-bit codes at bit BIT of an N-word bitstream, as a pair of
@@ -142,14 +148,14 @@ __device__ __forceinline__ constexpr int kpair_ch(int j, int e)
     return e == 0 ? a[j] : b[j];
 }
 
-// Nibbles K and K+4 of w as a pair of bf16 values 16 + c.
+// Nibbles K and K+4 of w as a pair of bf16 values: OFF4<K> + c.  Nibbles 0
+// and 4 already sit in the low mantissa bits of the two halves and become
+// 128 + c with no shift; the others are shifted to bit 3 and become 16 + c.
 template <int K>
 __device__ __forceinline__ uint32_t pair4(uint32_t w, const Magic& k)
 {
-    uint32_t y;
-    if constexpr (K == 0) y = w << 3;
-    else y = w >> (4 * K - 3);
-    return and_or(y, k.m4, k.c4);
+    if constexpr (K == 0) return and_or(w, k.m4lo, k.c6);
+    else return and_or(w >> (4 * K - 3), k.m4, k.c4);
 }
 
 // Token (0..15 of the lane group's 16) of row r of QK tile t.  4-bit V: the
@@ -320,7 +326,8 @@ __device__ __forceinline__ void block_qk(const BlockRegs<VB>& R, const uint32_t 
 
 }
 
-// Scores of the lane's 16 tokens from the block's dot products, folded into
+// 8-head layout (8 heads of one token, or 4 heads of each of a query-token
+// pair): scores of the lane's 16 tokens from the block's dot products, folded into
 // the running (m, L); fills the weights p (0 for dead or skipped tokens) and
 // returns the rescale factor of this lane's head.  keep: bit u set unless
 // every V term of tile pair u (32 tokens) is skipped for every head.
@@ -330,7 +337,7 @@ __device__ __forceinline__ void block_qk(const BlockRegs<VB>& R, const uint32_t 
 // srow: when non-null, the block's column of this lane's head in the score
 // rows; the lane that owns the head (part 0) stores its 16 tokens' base-2
 // scores there.
-template <int VB, int G, bool PARTIAL, bool KN>
+template <int VB, bool PARTIAL, bool KN>
 __device__ __forceinline__ float block_softmax(const f32x4_t (&dot)[4], const uint8_t* lds, SplitState& S, float qsum,
                                                float score_scale, float tau_low, int nlive, int q, int c,
                                                float (&p)[16], uint32_t& keep, float* srow)
@@ -361,7 +368,7 @@ __device__ __forceinline__ float block_softmax(const f32x4_t (&dot)[4], const ui
             bmax = fmaxf(bmax, s2);
         }
     }
-    if (srow != nullptr && (c & 1) == 0 && (G == 8 || c < 8)) {
+    if (srow != nullptr && (c & 1) == 0) {
         float v[16];  // token 16 q + i of the block
 #pragma unroll
         for (int t = 0; t < 4; t++) {
@@ -422,7 +429,7 @@ __device__ __forceinline__ void neg_off_pairs(const uint32_t (&z)[4], int u, uin
         if constexpr (VB == 4) {
             // K index 2k, 2k+1 are tokens 8u + k, 8u + k + 4: byte k of lo and of hi
             const uint32_t x = __builtin_amdgcn_perm(hi, lo, 0x0C000C00u | (uint32_t)k | ((uint32_t)(4 + k) << 16));
-            o[k] = (x << 3) | 0xC180C180u;  // -(16 + z)
+            o[k] = k == 0 ? x | 0xC300C300u : (x << 3) | 0xC180C180u;  // -(OFF4<k> + z): 128 for k = 0, else 16
         } else {
             // K index 2k, 2k+1 are tokens 8u + 2k, 8u + 2k + 1
             const uint32_t w = k < 2 ? lo : hi;
@@ -433,12 +440,14 @@ __device__ __forceinline__ void neg_off_pairs(const uint32_t (&z)[4], int u, uin
     }
 }
 
-template <int VB, int G, bool PARTIAL>
+// 8-head layout: P.V of the block, rows (head, part); each V group has an
+// A operand of its own.
+template <int VB, bool PARTIAL>
 __device__ __forceinline__ void block_pv(const BlockRegs<VB>& R, const uint8_t* lds, SplitState& S,
                                          const float (&p)[16], float alpha, uint32_t keep, int q, int c,
                                          int hA, const Magic& mk)
 {
-    constexpr int NG = G == 8 ? 2 : 1;
+    constexpr int NG = 2;
     const int part = c & 1;
 
     // rescale the accumulators when a running maximum moved
@@ -455,7 +464,7 @@ __device__ __forceinline__ void block_pv(const BlockRegs<VB>& R, const uint8_t* 
 
     float sv[NG][16];
 #pragma unroll
-    for (int g = 0; g < NG; g++) read16f(lds + META_VS + (G == 8 ? g : (c >> 3)) * 256 + 64 * q, sv[g]);
+    for (int g = 0; g < NG; g++) read16f(lds + META_VS + g * 256 + 64 * q, sv[g]);
     uint32_t zv[2][4];
 #pragma unroll
     for (int g = 0; g < 2; g++) read16b(lds + META_VZ + g * 64 + 16 * q, zv[g]);
@@ -506,11 +515,263 @@ __device__ __forceinline__ void block_pv(const BlockRegs<VB>& R, const uint8_t* 
                 bv[3] = pair6<84>(R.vr[T], mk);
             }
             const int gT = T >> 2;
-            const int ga = G == 8 ? gT : 0;
             // sum_t p'(t) (-(OFF + z(t))), then + sum_t p'(t) (OFF + c(t)): the
             // offset never accumulates beyond 32 tokens
-            S.acc[T] = mfma_16x16x32(pa[ga], bz[gT], S.acc[T]);
-            S.acc[T] = mfma_16x16x32(pa[ga], bv, S.acc[T]);
+            S.acc[T] = mfma_16x16x32(pa[gT], bz[gT], S.acc[T]);
+            S.acc[T] = mfma_16x16x32(pa[gT], bv, S.acc[T]);
+        }
+    }
+}
+
+// ---- 4 query heads per KV head: two token sets per product
+// With 4 heads the 16 QK columns would hold only 8 (head, group) pairs, and
+// every lane would score 16 tokens of which half belong to idle columns.
+// Instead the K dimension of each QK product carries two 16-token sets: lane
+// groups q = 0, 1 hold set 0 and q = 2, 3 set 1, q & 1 selecting the channel
+// group; a product then covers 32 tokens x 16 channels, the columns are
+// (set s, head h, group g) = 8 s + 2 h + g, and each lane scores 8 tokens of
+// a block.  In the P.V products the rows are (set, head, part): a set's rows
+// take the A operand of that set's tokens and zero elsewhere, so the two
+// sets' rows add up to the head's sum.  The token of K index j in lane group
+// q is unchanged (16 q + 8 u + tok_of(2 u, j) for tile pair u), so the V
+// operands are those of the 8-head layout.
+
+// Token (0..63) of the lane's score (u, i): lane group q, token set s.
+template <int VB>
+__device__ __forceinline__ int set_tok(int q, int s, int u, int i)
+{
+    return 16 * q + tok_of<VB>(2 * u, i) + (VB == 4 ? 2 : 4) * s;
+}
+
+// fp32 values of the lane's 8 tokens from a 64-slot LDS section.
+template <int VB>
+__device__ __forceinline__ void set_floats(const uint8_t* sec, int q, int s, float (&v)[8])
+{
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+        const int t = set_tok<VB>(q, s, u, 0);
+        if constexpr (VB == 4) {  // tokens t, t + 4, t + 1, t + 5
+            const float2 a = *(const float2*)(sec + 4 * t), b = *(const float2*)(sec + 4 * (t + 4));
+            v[4 * u] = a.x; v[4 * u + 1] = b.x; v[4 * u + 2] = a.y; v[4 * u + 3] = b.y;
+        } else {  // tokens t .. t + 3
+            const float4 a = *(const float4*)(sec + 4 * t);
+            v[4 * u] = a.x; v[4 * u + 1] = a.y; v[4 * u + 2] = a.z; v[4 * u + 3] = a.w;
+        }
+    }
+}
+
+// Zero points (uint8) of the lane's 8 tokens from a 64-slot LDS section, as fp32.
+template <int VB>
+__device__ __forceinline__ void set_bytes(const uint8_t* sec, int q, int s, float (&v)[8])
+{
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+        const int t = set_tok<VB>(q, s, u, 0);
+        if constexpr (VB == 4) {
+            const uint32_t a = *(const uint16_t*)(sec + t), b = *(const uint16_t*)(sec + t + 4);
+            v[4 * u] = (float)(a & 0xFFu); v[4 * u + 1] = (float)(b & 0xFFu);
+            v[4 * u + 2] = (float)(a >> 8); v[4 * u + 3] = (float)(b >> 8);
+        } else {
+            const uint32_t a = *(const uint32_t*)(sec + t);
+#pragma unroll
+            for (int i = 0; i < 4; i++) v[4 * u + i] = (float)((a >> (8 * i)) & 0xFFu);
+        }
+    }
+}
+
+// K codes: for tile pair u, lane (q, c) holds channel group q & 1 (48
+// contiguous bytes) of the token of QK row c in set q >> 1; words 0..11 go
+// to kr[2u][0..5], kr[2u + 1][0..5].
+template <int VB>
+__device__ __forceinline__ void load_k_sets(BlockRegs<VB>& R, const uint8_t* ch, uint32_t off_kc, int c, int q)
+{
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+        const uint32_t tok = 16 * (c >> 2) + set_tok<VB>(0, q >> 1, u, c & 3);
+        const uint4* p = (const uint4*)(ch + (off_kc + tok * 96 + 48 * (q & 1)));
+        const uint4 x0 = p[0], x1 = p[1], x2 = p[2];
+        R.kr[2 * u][0] = x0.x; R.kr[2 * u][1] = x0.y; R.kr[2 * u][2] = x0.z;
+        R.kr[2 * u][3] = x0.w; R.kr[2 * u][4] = x1.x; R.kr[2 * u][5] = x1.y;
+        R.kr[2 * u + 1][0] = x1.z; R.kr[2 * u + 1][1] = x1.w; R.kr[2 * u + 1][2] = x2.x;
+        R.kr[2 * u + 1][3] = x2.y; R.kr[2 * u + 1][4] = x2.z; R.kr[2 * u + 1][5] = x2.w;
+    }
+}
+
+// Q.K of both tile pairs: 8 products each, product m taking pairs
+// 4 (m & 1) .. 4 (m & 1) + 3 of the lane's 16-channel run m >> 1.
+template <int VB>
+__device__ __forceinline__ void block_qk_sets(const BlockRegs<VB>& R, const uint32_t (&qb)[8][4], float q128,
+                                              const Magic& mk, f32x4_t (&dot)[2])
+{
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+        uint32_t pr[4][8];
+        k16_pairs(R.kr[2 * u][0], R.kr[2 * u][1], R.kr[2 * u][2], mk, pr[0]);
+        k16_pairs(R.kr[2 * u][3], R.kr[2 * u][4], R.kr[2 * u][5], mk, pr[1]);
+        k16_pairs(R.kr[2 * u + 1][0], R.kr[2 * u + 1][1], R.kr[2 * u + 1][2], mk, pr[2]);
+        k16_pairs(R.kr[2 * u + 1][3], R.kr[2 * u + 1][4], R.kr[2 * u + 1][5], mk, pr[3]);
+        f32x4_t d4 = {-q128, -q128, -q128, -q128};  // removes the 128 offset of the codes
+#pragma unroll
+        for (int m = 0; m < 8; m++) {
+            const uint32_t ka[4] = {pr[m >> 1][4 * (m & 1)], pr[m >> 1][4 * (m & 1) + 1],
+                                    pr[m >> 1][4 * (m & 1) + 2], pr[m >> 1][4 * (m & 1) + 3]};
+            d4 = mfma_16x16x32(ka, qb[m], d4);
+        }
+        dot[u] = d4;
+    }
+}
+
+// block_softmax for the two-set layout: the lane's 8 scores are tokens
+// set_tok(q, c >> 3, u, i) of head (c >> 1) & 3; the running (m, L) of a head
+// is reduced over both sets, so every lane of a head holds the same values.
+template <int VB, bool PARTIAL, bool KN>
+__device__ __forceinline__ float block_softmax_sets(const f32x4_t (&dot)[2], const uint8_t* lds, SplitState& S,
+                                                    float qsum, float score_scale, float tau_low, int nlive, int q,
+                                                    int c, float (&p)[8], uint32_t& keep, float* srow)
+{
+    const int gc = c & 1, s = c >> 3;
+    float sk[8], zk[8];
+    set_floats<VB>(lds + gc * 256, q, s, sk);
+    set_bytes<VB>(lds + META_KZ + gc * 64, q, s, zk);
+    float rk[8];  // direction-preserving K: the norm factors of the lane's 8 tokens
+    if constexpr (KN) set_floats<VB>(lds + META_BYTES, q, s, rk);
+    float sc[8];
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int x = 4 * u + i;
+            // the group share rounded before the exchange, as in block_softmax
+            const float pg = mul_rounded(sk[x], dot[u][i] - zk[x] * qsum);
+            float s2 = pg + xor1(pg);
+            if constexpr (KN) s2 *= rk[x];
+            if constexpr (PARTIAL) s2 = set_tok<VB>(q, s, u, i) < nlive ? s2 : -INFINITY;
+            sc[x] = s2;
+            bmax = fmaxf(bmax, s2);
+        }
+    }
+    if (srow != nullptr && gc == 0) {
+        float v[8];
+#pragma unroll
+        for (int x = 0; x < 8; x++) v[x] = sc[x] * score_scale;
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            const int t = set_tok<VB>(q, s, u, 0);
+            if constexpr (PARTIAL) {
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int ti = set_tok<VB>(q, s, u, i);
+                    if (ti < nlive) srow[ti] = v[4 * u + i];
+                }
+            } else if constexpr (VB == 4) {
+                *(float2*)(srow + t) = make_float2(v[4 * u], v[4 * u + 2]);
+                *(float2*)(srow + t + 4) = make_float2(v[4 * u + 1], v[4 * u + 3]);
+            } else {
+                *(float4*)(srow + t) = make_float4(v[4 * u], v[4 * u + 1], v[4 * u + 2], v[4 * u + 3]);
+            }
+        }
+    }
+    bmax = rows_max(fmaxf(bmax, xor8(bmax))) * score_scale;  // both sets, base 2
+    const float m_new = bmax > S.m_run + 8.0f ? bmax : S.m_run;
+    const float m_ref = PARTIAL && m_new == -INFINITY ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(S.m_run - m_ref);
+    float bsum = 0.0f;
+#pragma unroll
+    for (int x = 0; x < 8; x++) {
+        p[x] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[x], score_scale, -m_ref));
+        bsum += p[x];
+    }
+    S.l_run = S.l_run * alpha + rows_sum(bsum + xor8(bsum));
+    S.m_run = m_new;
+    keep = 3u;
+    if (tau_low > 0.0f) {
+        const float thr = tau_low * S.l_run;
+        bool k0 = false, k1 = false;
+#pragma unroll
+        for (int x = 0; x < 8; x++) {
+            p[x] = p[x] < thr ? 0.0f : p[x];
+            if (x < 4) k0 |= p[x] > 0.0f;  // tile pair 0
+            else k1 |= p[x] > 0.0f;
+        }
+        keep = (__builtin_amdgcn_ballot_w64(k0) ? 1u : 0u) | (__builtin_amdgcn_ballot_w64(k1) ? 2u : 0u);
+    }
+    return alpha;
+}
+
+// block_pv for the two-set layout: row c = (set c >> 3, head, part c & 1);
+// K indices 4 s .. 4 s + 3 of the lane's 8 carry its own tokens, the others
+// zero.  Both V groups have an A operand of their own.
+template <int VB, bool PARTIAL>
+__device__ __forceinline__ void block_pv_sets(const BlockRegs<VB>& R, const uint8_t* lds, SplitState& S,
+                                              const float (&p)[8], float alpha, uint32_t keep, int q, int c,
+                                              int hA, const Magic& mk)
+{
+    const int part = c & 1, s = c >> 3;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+        const float alA = __shfl(alpha, 2 * hA, 64), alB = __shfl(alpha, 2 * hA + 2, 64);
+#pragma unroll
+        for (int T = 0; T < 8; T++) {
+            S.acc[T][0] *= alA;
+            S.acc[T][1] *= alA;
+            S.acc[T][2] *= alB;
+            S.acc[T][3] *= alB;
+        }
+    }
+    float sv[2][8];
+    set_floats<VB>(lds + META_VS, q, s, sv[0]);
+    set_floats<VB>(lds + META_VS + 256, q, s, sv[1]);
+    uint32_t zv[2][4];
+#pragma unroll
+    for (int g = 0; g < 2; g++) read16b(lds + META_VZ + g * 64 + 16 * q, zv[g]);
+
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+        if (!(keep & (1u << u))) continue;
+        uint32_t pa[2][4];
+#pragma unroll
+        for (int g = 0; g < 2; g++) {
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const float pj = p[4 * u + i];
+                float pp = pj * sv[g][4 * u + i];
+                if constexpr (PARTIAL) pp = pj > 0.0f ? pp : 0.0f;  // dead token: its scale bytes may be stale
+                const float hi = __uint_as_float(__float_as_uint(pp) & 0xFFFF0000u);
+                v[i] = part ? pp - hi : hi;
+            }
+            const uint32_t d0 = pack_bf16(v[0], v[1]), d1 = pack_bf16(v[2], v[3]);
+            pa[g][0] = s ? 0u : d0;
+            pa[g][1] = s ? 0u : d1;
+            pa[g][2] = s ? d0 : 0u;
+            pa[g][3] = s ? d1 : 0u;
+        }
+        uint32_t bz[2][4];
+        neg_off_pairs<VB>(zv[0], u, bz[0]);
+        neg_off_pairs<VB>(zv[1], u, bz[1]);
+#pragma unroll
+        for (int T = 0; T < 8; T++) {
+            uint32_t bv[4];
+            if constexpr (VB == 4) {
+                const uint32_t w = R.vr[T][u];
+                bv[0] = pair4<0>(w, mk);
+                bv[1] = pair4<1>(w, mk);
+                bv[2] = pair4<2>(w, mk);
+                bv[3] = pair4<3>(w, mk);
+            } else if (u == 0) {
+                bv[0] = pair6<0>(R.vr[T], mk);
+                bv[1] = pair6<12>(R.vr[T], mk);
+                bv[2] = pair6<24>(R.vr[T], mk);
+                bv[3] = pair6<36>(R.vr[T], mk);
+            } else {
+                bv[0] = pair6<48>(R.vr[T], mk);
+                bv[1] = pair6<60>(R.vr[T], mk);
+                bv[2] = pair6<72>(R.vr[T], mk);
+                bv[3] = pair6<84>(R.vr[T], mk);
+            }
+            const int gT = T >> 2;
+            S.acc[T] = mfma_16x16x32(pa[gT], bz[gT], S.acc[T]);
+            S.acc[T] = mfma_16x16x32(pa[gT], bv, S.acc[T]);
         }
     }
 }
@@ -528,6 +789,7 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
 {
     static_assert(G == 4 || G == 8, "4 or 8 query heads per KV head");
     static_assert(!PAIR || G == 8, "a pair fills the 8-head layout");
+    constexpr bool SETS = G == 4;  // the two-set layout
     constexpr int D = 128;
     const SegArgs& sg = a.seg;
     const Fmt& f = sg.f;
@@ -579,9 +841,10 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
     }
 
     // ---- roles of this lane
-    // QK column c -> (head hc, group gc); P.V row c -> (head hc, part c&1,
-    // and for G = 4 the group c>>3, the two groups sharing one A operand).
-    const int hc = G == 8 ? (c >> 1) : ((c & 7) >> 1);
+    // 8-head layout: QK column c -> (head hc, group gc), P.V row c -> (head
+    // hc, part c & 1).  Two-set layout: QK column c -> (set c >> 3, head hc,
+    // group gc), P.V row c -> (set c >> 3, head hc, part c & 1).
+    const int hc = G == 8 ? (c >> 1) : ((c >> 1) & 3);
     const int gc = c & 1;
     const int part = c & 1;
     const int head = kvh * G + hc;
@@ -590,11 +853,38 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
     // this lane's head's score row, at the split's first token
     const int64_t srow0 = ((int64_t)b * a.num_q_heads + head) * sg.score_stride + sg.tok_base + t0;
 
-    // ---- Q as the QK B operand: this lane group (q) holds channels
-    // [32q, 32q + 32), in group q >> 1; zero unless that is the column's group.
-    uint32_t qb[4][4];
+    // ---- Q as the QK B operand.  8-head layout: this lane group (q) holds
+    // channels [32q, 32q + 32), in group q >> 1; zero unless that is the
+    // column's group.  Two-set layout: lane group q holds all 64 channels of
+    // group q & 1 for set q >> 1; zero unless both are the column's.
+    uint32_t qb[SETS ? 8 : 4][4];
     float qpart = 0.0f;
-    {
+    if constexpr (SETS) {
+        const uint4* src = (const uint4*)(a.q + ((int64_t)b * a.num_q_heads + head) * D + 64 * gc);
+        const bool live = q == 2 * (c >> 3) + gc;
+        uint32_t qw[32];  // channels 2i, 2i+1 of the group
+#pragma unroll
+        for (int s8 = 0; s8 < 8; s8++) {
+            const uint4 v = src[s8];
+            qw[4 * s8] = live ? v.x : 0u;
+            qw[4 * s8 + 1] = live ? v.y : 0u;
+            qw[4 * s8 + 2] = live ? v.z : 0u;
+            qw[4 * s8 + 3] = live ? v.w : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < 32; i++) qpart += __uint_as_float(qw[i] << 16) + __uint_as_float(qw[i] & 0xFFFF0000u);
+        // product m: pairs 4(m&1) .. 4(m&1)+3 of channel run m>>1, the pairing the K codes use
+#pragma unroll
+        for (int m = 0; m < 8; m++) {
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int pj = 4 * (m & 1) + j;
+                const int ca = 16 * (m >> 1) + kpair_ch(pj, 0), cb = 16 * (m >> 1) + kpair_ch(pj, 1);
+                const uint32_t sel = ((ca & 1) ? 0x0302u : 0x0100u) | (((cb & 1) ? 0x0706u : 0x0504u) << 16);
+                qb[m][j] = __builtin_amdgcn_perm(qw[cb >> 1], qw[ca >> 1], sel);
+            }
+        }
+    } else {
         const uint4* src = (const uint4*)(a.q + (PAIR ? prow(hc) : (int64_t)b * a.num_q_heads + head) * D + 32 * q);
         const bool live = (q >> 1) == gc;
         uint32_t qw[16];  // channels 2i, 2i+1 of this lane group's 32
@@ -661,7 +951,8 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
         const uint8_t* c0 = chunk_of(0);
         load_meta<VB, KN>(R, c0, off_ks, lane);
         asm volatile("" ::: "memory");
-        load_k<VB>(R, c0, off_kc, c, q);
+        if constexpr (SETS) load_k_sets<VB>(R, c0, off_kc, c, q);
+        else load_k<VB>(R, c0, off_kc, c, q);
         asm volatile("" ::: "memory");
         load_v<VB>(R, c0, off_vc, c, q);
         asm volatile("" ::: "memory");
@@ -675,17 +966,27 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
         stage_meta<KN>(R.meta, meta_lds, lane);
         if constexpr (MORE) load_meta<VB, KN>(R, cn, off_ks, lane);
         asm volatile("" ::: "memory");
-        f32x4_t dot[4];
-        block_qk<VB>(R, qb, q128, mk, dot);
-        if constexpr (MORE) load_k<VB>(R, cn, off_kc, c, q);
+        f32x4_t dot[SETS ? 2 : 4];
+        if constexpr (SETS) block_qk_sets<VB>(R, qb, q128, mk, dot);
+        else block_qk<VB>(R, qb, q128, mk, dot);
+        if constexpr (MORE) {
+            if constexpr (SETS) load_k_sets<VB>(R, cn, off_kc, c, q);
+            else load_k<VB>(R, cn, off_kc, c, q);
+        }
         asm volatile("" ::: "memory");
         const int nlive = min(BT, tl - t0 - k * BT);  // PAIR: this lane's column's (may be <= 0)
-        float p[16];
+        float p[SETS ? 8 : 16];
         uint32_t keep;
         float* srow = !PAIR && sg.scores != nullptr ? sg.scores + srow0 + (int64_t)k * BT : nullptr;
-        const float alpha =
-            block_softmax<VB, G, PARTIAL, KN>(dot, lds, S, qsum, a.score_scale, a.tau_low, nlive, q, c, p, keep, srow);
-        block_pv<VB, G, PARTIAL>(R, lds, S, p, alpha, keep, q, c, hA, mk);
+        if constexpr (SETS) {
+            const float alpha = block_softmax_sets<VB, PARTIAL, KN>(dot, lds, S, qsum, a.score_scale, a.tau_low,
+                                                                    nlive, q, c, p, keep, srow);
+            block_pv_sets<VB, PARTIAL>(R, lds, S, p, alpha, keep, q, c, hA, mk);
+        } else {
+            const float alpha = block_softmax<VB, PARTIAL, KN>(dot, lds, S, qsum, a.score_scale, a.tau_low, nlive, q,
+                                                               c, p, keep, srow);
+            block_pv<VB, PARTIAL>(R, lds, S, p, alpha, keep, q, c, hA, mk);
+        }
         if constexpr (MORE) load_v<VB>(R, cn, off_vc, c, q);
         asm volatile("" ::: "memory");
     };
@@ -729,10 +1030,16 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
     const int64_t soff = (int64_t)(sg.split_base + sp) * (D + 2);
 #pragma unroll
     for (int T = 0; T < 8; T++) {
-        // G = 8: both groups valid in every lane; G = 4: rows of group q >> 1
-        if (G == 4 && (q >> 1) != (T >> 2)) continue;
-        base[hA * hstride + soff + 16 * T + c] = S.acc[T][0] + S.acc[T][1];
-        base[(hA + 1) * hstride + soff + 16 * T + c] = S.acc[T][2] + S.acc[T][3];
+        float o0 = S.acc[T][0] + S.acc[T][1], o1 = S.acc[T][2] + S.acc[T][3];
+        if constexpr (SETS) {
+            // rows of set 1 (lane groups 2, 3) add to those of set 0; the
+            // lane groups of V group T >> 2 write the sum
+            o0 = halves_sum(o0);
+            o1 = halves_sum(o1);
+            if ((q >> 1) != (T >> 2)) continue;
+        }
+        base[hA * hstride + soff + 16 * T + c] = o0;
+        base[(hA + 1) * hstride + soff + 16 * T + c] = o1;
     }
     if (q == 0 && part == 0 && (G == 8 || c < 8)) {
         base[hc * hstride + soff + D] = S.m_run;

@@ -34,10 +34,25 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32_f16(const uint32_t (&a)[4], con
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, c, 0, 0, 0);
 }
 
-// Value of the neighbouring lane (lane ^ 1) -- DPP quad permutation.
+// Value of the neighbouring lane (lane ^ 1) -- DPP quad permutation.  Every
+// lane is active where it is called; with bound_ctrl set the compiler folds
+// the move into the instruction that consumes it (v_add_f32_dpp).
 __device__ __forceinline__ float xor1(float v)
 {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+
+// Value of lane ^ 8 within each 16-lane row -- DPP row rotation by 8.
+__device__ __forceinline__ float xor8(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, true));
+}
+
+// v + the value of lane ^ 32 (both halves end with the same sum).
+__device__ __forceinline__ float halves_sum(float v)
+{
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(a[0]) + __uint_as_float(a[1]);
 }
 
 // Reductions over the four 16-lane rows (lanes l, l^16, l^32, l^48).
