@@ -856,70 +856,20 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
     // ---- Q as the QK B operand.  8-head layout: this lane group (q) holds
     // channels [32q, 32q + 32), in group q >> 1; zero unless that is the
     // column's group.  Two-set layout: lane group q holds all 64 channels of
-    // group q & 1 for set q >> 1; zero unless both are the column's.
-    uint32_t qb[SETS ? 8 : 4][4];
-    float qpart = 0.0f;
-    if constexpr (SETS) {
-        const uint4* src = (const uint4*)(a.q + ((int64_t)b * a.num_q_heads + head) * D + 64 * gc);
-        const bool live = q == 2 * (c >> 3) + gc;
-        uint32_t qw[32];  // channels 2i, 2i+1 of the group
+    // group q & 1 for set q >> 1; zero unless both are the column's.  Q is
+    // loaded before the first block's loads are issued and turned into the
+    // operand while that block is in flight.  (Every lane loads: the lanes of
+    // one column read the same bytes, so the idle ones add no lines.)
+    constexpr int NQ = SETS ? 8 : 4;  // 16-byte pieces per lane
+    const bool qlive = SETS ? q == 2 * (c >> 3) + gc : (q >> 1) == gc;
+    uint4 qraw[NQ];
+    {
+        const int64_t qrow = PAIR ? prow(hc) : (int64_t)b * a.num_q_heads + head;
+        const uint4* src = (const uint4*)(a.q + qrow * D + (SETS ? 64 * gc : 32 * q));
 #pragma unroll
-        for (int s8 = 0; s8 < 8; s8++) {
-            const uint4 v = src[s8];
-            qw[4 * s8] = live ? v.x : 0u;
-            qw[4 * s8 + 1] = live ? v.y : 0u;
-            qw[4 * s8 + 2] = live ? v.z : 0u;
-            qw[4 * s8 + 3] = live ? v.w : 0u;
-        }
-#pragma unroll
-        for (int i = 0; i < 32; i++) qpart += __uint_as_float(qw[i] << 16) + __uint_as_float(qw[i] & 0xFFFF0000u);
-        // product m: pairs 4(m&1) .. 4(m&1)+3 of channel run m>>1, the pairing the K codes use
-#pragma unroll
-        for (int m = 0; m < 8; m++) {
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const int pj = 4 * (m & 1) + j;
-                const int ca = 16 * (m >> 1) + kpair_ch(pj, 0), cb = 16 * (m >> 1) + kpair_ch(pj, 1);
-                const uint32_t sel = ((ca & 1) ? 0x0302u : 0x0100u) | (((cb & 1) ? 0x0706u : 0x0504u) << 16);
-                qb[m][j] = __builtin_amdgcn_perm(qw[cb >> 1], qw[ca >> 1], sel);
-            }
-        }
-    } else {
-        const uint4* src = (const uint4*)(a.q + (PAIR ? prow(hc) : (int64_t)b * a.num_q_heads + head) * D + 32 * q);
-        const bool live = (q >> 1) == gc;
-        uint32_t qw[16];  // channels 2i, 2i+1 of this lane group's 32
-#pragma unroll
-        for (int s4 = 0; s4 < 4; s4++) {
-            const uint4 v = src[s4];
-            qw[4 * s4] = live ? v.x : 0u;
-            qw[4 * s4 + 1] = live ? v.y : 0u;
-            qw[4 * s4 + 2] = live ? v.z : 0u;
-            qw[4 * s4 + 3] = live ? v.w : 0u;
-        }
-#pragma unroll
-        for (int i = 0; i < 16; i++) qpart += __uint_as_float(qw[i] << 16) + __uint_as_float(qw[i] & 0xFFFF0000u);
-        // K-step s: pairs 4(s&1) .. 4(s&1)+3 of channel group s>>1, the pairing the K codes use
-#pragma unroll
-        for (int st = 0; st < 4; st++) {
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const int pj = 4 * (st & 1) + j;
-                const int ca = 16 * (st >> 1) + kpair_ch(pj, 0), cb = 16 * (st >> 1) + kpair_ch(pj, 1);
-                // bytes of channel ca (low half) and cb (high half)
-                const uint32_t sel = ((ca & 1) ? 0x0302u : 0x0100u) | (((cb & 1) ? 0x0706u : 0x0504u) << 16);
-                qb[st][j] = __builtin_amdgcn_perm(qw[cb >> 1], qw[ca >> 1], sel);
-            }
-        }
+        for (int i = 0; i < NQ; i++) qraw[i] = src[i];
     }
-    const float qsum = rows_sum(qpart);
-    const float q128 = 128.0f * qsum;
-
-    const Magic mk = make_magic();
-    SplitState S;
-    S.m_run = -INFINITY;
-    S.l_run = 0.0f;
-#pragma unroll
-    for (int T = 0; T < 8; T++) S.acc[T] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    asm volatile("" ::: "memory");
 
     const uint8_t* lds = (const uint8_t*)meta_lds;
 
@@ -957,6 +907,46 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
         load_v<VB>(R, c0, off_vc, c, q);
         asm volatile("" ::: "memory");
     }
+    // Q is used from here on (not earlier: the first block's loads go first)
+#pragma unroll
+    for (int i = 0; i < NQ; i++) asm volatile("" : "+v"(qraw[i].x), "+v"(qraw[i].y), "+v"(qraw[i].z), "+v"(qraw[i].w));
+
+    uint32_t qb[SETS ? 8 : 4][4];
+    float qpart = 0.0f;
+    {
+        uint32_t qw[4 * NQ];  // channels 2i, 2i+1 of the lane's run
+#pragma unroll
+        for (int i = 0; i < NQ; i++) {
+            qw[4 * i] = qlive ? qraw[i].x : 0u;
+            qw[4 * i + 1] = qlive ? qraw[i].y : 0u;
+            qw[4 * i + 2] = qlive ? qraw[i].z : 0u;
+            qw[4 * i + 3] = qlive ? qraw[i].w : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < 4 * NQ; i++) qpart += __uint_as_float(qw[i] << 16) + __uint_as_float(qw[i] & 0xFFFF0000u);
+        // product m (two-set layout) or K-step m (8-head layout): pairs
+        // 4(m&1) .. 4(m&1)+3 of the 16-channel run m>>1, the pairing the K
+        // codes use; bytes of channel ca (low half) and cb (high half)
+#pragma unroll
+        for (int m = 0; m < (SETS ? 8 : 4); m++) {
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int pj = 4 * (m & 1) + j;
+                const int ca = 16 * (m >> 1) + kpair_ch(pj, 0), cb = 16 * (m >> 1) + kpair_ch(pj, 1);
+                const uint32_t sel = ((ca & 1) ? 0x0302u : 0x0100u) | (((cb & 1) ? 0x0706u : 0x0504u) << 16);
+                qb[m][j] = __builtin_amdgcn_perm(qw[cb >> 1], qw[ca >> 1], sel);
+            }
+        }
+    }
+    const float qsum = rows_sum(qpart);
+    const float q128 = 128.0f * qsum;
+
+    const Magic mk = make_magic();
+    SplitState S;
+    S.m_run = -INFINITY;
+    S.l_run = 0.0f;
+#pragma unroll
+    for (int T = 0; T < 8; T++) S.acc[T] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     // (the empty asm statements keep the compiler from moving the loads to
     // their first use)
     auto block = [&](int k, auto partial, auto prefetch) {
