@@ -995,7 +995,8 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
 
     // ---- write the partial (o, m, L) of every head of the group
     // P.V output: lane (column c, row group q) holds rows 4q .. 4q+3 of each
-    // channel tile T; rows 4q, 4q+1 are head hA (hi, lo), 4q+2, 4q+3 head hA+1.
+    // channel tile T; rows 4q, 4q+1 are head hA (hi, lo), 4q+2, 4q+3 head hA+1
+    // (two-set layout: of token set q >> 1).
     if constexpr (PAIR) {
         // rows hA, hA + 1 belong to one token (hA even)
         const int64_t soff = (int64_t)(sg.split_base + sp) * (D + 2);
@@ -1031,7 +1032,7 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
         base[hA * hstride + soff + 16 * T + c] = o0;
         base[(hA + 1) * hstride + soff + 16 * T + c] = o1;
     }
-    if (q == 0 && part == 0 && (G == 8 || c < 8)) {
+    if (q == 0 && part == 0 && (G == 8 || c < 8)) {  // two-set layout: set 0's lane of the head
         base[hc * hstride + soff + D] = S.m_run;
         base[hc * hstride + soff + D + 1] = S.l_run;
     }
