@@ -43,11 +43,15 @@ def _append(pair, lens, Hkv, D, seed, bt, dtype="bf16"):
     O.append(pair.ref, to_f32_host(k), to_f32_host(v), cu, np.zeros(len(lens), np.int32), bt)
 
 
-@pytest.mark.parametrize("fmt", [(128, 64, 6, 4), (128, 32, 4, 6), (64, 16, 6, 6)], ids=lambda f: "D{}g{}k{}v{}".format(*f))
+# (128, 64, 6, x) with bf16 queries run the matrix-core kernels: at 4 query
+# heads per KV head the two-set layout, at 8 the 8-head one
+@pytest.mark.parametrize("fmt", [(128, 64, 6, 4), (128, 64, 6, 6), (128, 32, 4, 6), (64, 16, 6, 6)],
+                         ids=lambda f: "D{}g{}k{}v{}".format(*f))
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_knorm_append_then_decode(fmt, dtype):
+@pytest.mark.parametrize("G", [4, 8])
+def test_knorm_append_then_decode(fmt, dtype, G):
     D, g, kb, vb = fmt
-    Hkv, G = 2, 4
+    Hkv = 2
     lens = [1, 65, 300]
     rng = np.random.default_rng(120)
     bt, nblk = block_tables([n + 2 for n in lens], rng)
@@ -74,7 +78,7 @@ def test_knorm_append_then_decode(fmt, dtype):
             from tests import np_reference as R
             _, Vh = R.dequant_sequence(pair.ref.pool, pair.ref.chunk_bytes, Hkv, D, g, kb, vb, bt[b], n)
             vmax = max(vmax, float(np.abs(Vh).max()))
-        assert_attention_close(got, want, vmax, f"knorm {fmt} tau {tau}")
+        assert_attention_close(got, want, vmax, f"knorm {fmt} G {G} tau {tau}")
 
 
 def test_knorm_rejects_unaligned_inputs_and_tiers():
