@@ -953,6 +953,10 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
         constexpr bool PARTIAL = decltype(partial)::value;
         constexpr bool MORE = decltype(prefetch)::value;  // load block k + 1 (false: the split's last block)
         const uint8_t* cn = MORE ? chunk_of(k + 1) : nullptr;
+        // raised wave priority from the block's start until the next block's
+        // K loads are issued: a wave whose data has arrived gets to its next
+        // loads ahead of the other wave's softmax and P.V
+        __builtin_amdgcn_s_setprio(1);
         stage_meta<KN>(R.meta, meta_lds, lane);
         if constexpr (MORE) load_meta<VB, KN>(R, cn, off_ks, lane);
         asm volatile("" ::: "memory");
@@ -964,6 +968,7 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
             else load_k<VB>(R, cn, off_kc, c, q);
         }
         asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_setprio(0);
         const int nlive = min(BT, tl - t0 - k * BT);  // PAIR: this lane's column's (may be <= 0)
         float p[SETS ? 8 : 16];
         uint32_t keep;
