@@ -400,10 +400,11 @@ static double deq_v(const uint8_t* ch, const fmt_t* f, int slot, int d)
  * segment s, summed over the query heads h of the sequence, is added to
  * score_acc[s][b][j].  Skipped tokens keep their weight (they stay in the
  * softmax); the sum over heads runs in head order. */
-int orc_decode(const orc_cache* segs, const orc_view* views, int32_t nseg,
-               const float* q, int32_t batch, int32_t num_q_heads,
-               float sm_scale, float tau_low, int32_t split_tokens,
-               double* out, uint8_t* skip, double* score_acc, int32_t acc_stride)
+static int decode_impl(const orc_cache* segs, const orc_view* views, int32_t nseg,
+                       const float* q, int32_t batch, int32_t num_q_heads,
+                       float sm_scale, float tau_low, int32_t split_tokens,
+                       double* out, uint8_t* skip, double* score_acc, int32_t acc_stride,
+                       const uint8_t* given, double band, uint8_t* ambiguous, double* margin)
 {
     if (nseg < 1 || nseg > 8 || batch < 0 || num_q_heads <= 0) return -1;
     if (split_tokens < 0 || split_tokens % BT != 0) return -1;
@@ -481,7 +482,16 @@ int orc_decode(const orc_cache* segs, const orc_view* views, int32_t nseg,
                             m_run = m_new;
                             l_run = l_new;
                             for (int32_t j = b0; j < b1; j++) {
-                                int sk = tau_low > 0.0f && exp(sc[n + j] - m_run) < (double)tau_low * l_run;
+                                const double e = exp(sc[n + j] - m_run), t = (double)tau_low * l_run;
+                                int sk = tau_low > 0.0f && e < t;
+                                /* a margin within band * t of the bound: either
+                                 * decision is correct; take the given one */
+                                const int64_t at = (((int64_t)b * num_q_heads + h) * nseg + s) * max_tok + j;
+                                if (margin && tau_low > 0.0f) margin[at] = (e - t) / t;
+                                if (tau_low > 0.0f && fabs(e - t) <= band * t) {
+                                    if (ambiguous) ambiguous[at] = 1;
+                                    if (given) sk = given[at] != 0;
+                                }
                                 kept[n + j] = (uint8_t)!sk;
                             }
                         }
@@ -543,6 +553,37 @@ int orc_decode(const orc_cache* segs, const orc_view* views, int32_t nseg,
     }
     free(wts);
     return fail ? -1 : 0;
+}
+
+int orc_decode(const orc_cache* segs, const orc_view* views, int32_t nseg,
+               const float* q, int32_t batch, int32_t num_q_heads,
+               float sm_scale, float tau_low, int32_t split_tokens,
+               double* out, uint8_t* skip, double* score_acc, int32_t acc_stride)
+{
+    return decode_impl(segs, views, nseg, q, batch, num_q_heads, sm_scale, tau_low, split_tokens, out, skip,
+                       score_acc, acc_stride, NULL, 0.0, NULL, NULL);
+}
+
+/* Several skip sets are correct.  The rule compares exp(s - m) with
+ * tau_low * L, and an evaluation in finite precision (fp32 on the GPU) can
+ * take either side when the two are closer than its rounding error.  A pair
+ * (token, head) whose exact margin |exp(s - m) - tau_low * L| is at most
+ * band * tau_low * L is therefore ambiguous: the decision given for it is
+ * taken (given may be NULL: the exact decision stays), and it is flagged in
+ * ambiguous.  Every other decision is the exact one.  A flipped decision
+ * moves the output by at most that token's weight, which is below
+ * tau_low * (1 + band), times max |v_hat|.  margin (may be NULL) receives
+ * the relative margin (exp(s - m) - tau_low * L) / (tau_low * L) of every
+ * live pair when tau_low > 0. */
+int orc_decode_resolved(const orc_cache* segs, const orc_view* views, int32_t nseg,
+                        const float* q, int32_t batch, int32_t num_q_heads,
+                        float sm_scale, float tau_low, int32_t split_tokens,
+                        double* out, uint8_t* skip, const uint8_t* given, double band, uint8_t* ambiguous,
+                        double* margin)
+{
+    if (!(band >= 0.0)) return -1;
+    return decode_impl(segs, views, nseg, q, batch, num_q_heads, sm_scale, tau_low, split_tokens, out, skip,
+                       NULL, 0, given, band, ambiguous, margin);
 }
 
 /* --------------------------------------------------------- tier update */

@@ -93,6 +93,20 @@ int orc_decode(const orc_cache* segs, const orc_view* views, int32_t nseg,
                float sm_scale, float tau_low, int32_t split_tokens,
                double* out, uint8_t* skip, double* score_acc, int32_t acc_stride);
 
+/* orc_decode with the near-threshold skip decisions resolved: a pair whose
+ * exact margin |exp(s - m) - tau_low * L| is at most band * tau_low * L can
+ * go either way in finite precision; for it the decision in given (layout of
+ * skip; NULL keeps the exact one) is taken and ambiguous (same layout, may
+ * be NULL, filled with 1 where a pair is ambiguous and left alone elsewhere)
+ * records it.  margin (may be NULL, layout of skip, fp64) receives each live
+ * pair's relative margin (exp(s - m) - tau_low * L) / (tau_low * L) when
+ * tau_low > 0.  band >= 0. */
+int orc_decode_resolved(const orc_cache* segs, const orc_view* views, int32_t nseg,
+                        const float* q, int32_t batch, int32_t num_q_heads,
+                        float sm_scale, float tau_low, int32_t split_tokens,
+                        double* out, uint8_t* skip, const uint8_t* given, double band, uint8_t* ambiguous,
+                        double* margin);
+
 /* Tier update.  src: K6V6 cache + view.  scores fp32 [batch][scores_stride].
  * Writes tiers uint8 [batch][scores_stride] (0 low, 1 mid, 2 high; entries
  * past the sequence length are left untouched), compacts HIGH tokens into

@@ -66,6 +66,10 @@ def lib():
                                  C.c_int32, C.c_int32, C.c_float, C.c_float, C.c_int32,
                                  C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32]
         L.orc_decode.restype = C.c_int
+        L.orc_decode_resolved.argtypes = [C.POINTER(_Cache), C.POINTER(_View), C.c_int32, C.c_void_p,
+                                          C.c_int32, C.c_int32, C.c_float, C.c_float, C.c_int32,
+                                          C.c_void_p, C.c_void_p, C.c_void_p, C.c_double, C.c_void_p, C.c_void_p]
+        L.orc_decode_resolved.restype = C.c_int
         L.orc_tier_update.argtypes = [C.POINTER(_Cache), C.POINTER(_View), C.c_void_p, C.c_int32,
                                       C.c_float, C.c_float,
                                       C.POINTER(_Cache), C.c_void_p, C.c_int32,
@@ -222,6 +226,57 @@ def decode(caches, block_tables, seq_lens, q: np.ndarray, sm_scale: float,
     return (out, skip) if want_skip else out
 
 
+def decode_resolved(caches, block_tables, seq_lens, q: np.ndarray, sm_scale: float, tau_low: float,
+                    split_tokens: int, given: np.ndarray | None, band: float):
+    """decode() with the skip decisions near the threshold resolved.
+
+    A (token, head) pair whose exact margin |exp(s - m) - tau_low L| is at
+    most band * tau_low * L can take either decision in finite precision; for
+    it the decision in `given` (uint8 [B][Hq][nseg][max_tok], 1 = skipped; None
+    keeps the exact one) is taken.  Returns (out fp64 [B][Hq][D], skip,
+    ambiguous, margin): skip and ambiguous uint8 in the layout of given, margin
+    fp64 the relative margin (exp(s - m) - tau_low L) / (tau_low L) of every
+    live pair (0 elsewhere)."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    B, Hq, D = q.shape
+    nseg = len(caches)
+    bts = [_i32(t) for t in block_tables]
+    lens = [_i32(n) for n in seq_lens]
+    ccs = (_Cache * nseg)(*[c.c() for c in caches])
+    views = (_View * nseg)(*[_View(bt.ctypes.data, ln.ctypes.data, bt.shape[1]) for bt, ln in zip(bts, lens)])
+    max_tok = max(bt.shape[1] for bt in bts) * BLOCK_TOKENS
+    shape = (B, Hq, nseg, max_tok)
+    out = np.zeros((B, Hq, D), np.float64)
+    skip = np.zeros(shape, np.uint8)
+    amb = np.zeros(shape, np.uint8)
+    margin = np.zeros(shape, np.float64)
+    if given is not None:
+        given = np.ascontiguousarray(given, dtype=np.uint8)
+        if given.shape != shape:
+            raise ValueError(f"given must be {shape}")
+    rc = lib().orc_decode_resolved(ccs, views, nseg, _p(q), B, Hq, sm_scale, tau_low, split_tokens, _p(out),
+                                   _p(skip), _p(given) if given is not None else None, float(band), _p(amb),
+                                   _p(margin))
+    if rc != 0:
+        raise ValueError("oracle decode rejected its arguments")
+    return out, skip, amb, margin
+
+
+def multi_entries(block_tables, seq_lens, T: int):
+    """The decode entries of T query tokens per sequence: entry (b, i) reads
+    sequence b's tables, with segment 0 cut to its causal prefix
+    0 .. L - T + i.  Returns (tables, lens) per segment."""
+    bts = [_i32(t) for t in block_tables]
+    lens = [_i32(n) for n in seq_lens]
+    if T < 1 or np.any(lens[0] < T):
+        raise ValueError("every sequence must hold its T query tokens")
+    B = len(lens[0])
+    ebts = [np.repeat(bt, T, axis=0) for bt in bts]                  # entry (b, i): sequence b's table
+    elens = [np.repeat(ln, T) for ln in lens]
+    elens[0] = elens[0] - (T - 1) + np.tile(np.arange(T, dtype=np.int32), B)  # causal prefix in segment 0
+    return ebts, elens
+
+
 def decode_multi(caches, block_tables, seq_lens, q: np.ndarray, sm_scale: float,
                  tau_low: float = 0.0, split_tokens: int = 0):
     """Attention of T query tokens per sequence over the packed cache, with a
@@ -236,13 +291,7 @@ def decode_multi(caches, block_tables, seq_lens, q: np.ndarray, sm_scale: float,
     rule.  Returns fp64 [B][T][Hq][D]."""
     q = np.ascontiguousarray(q, dtype=np.float32)
     B, T, Hq, D = q.shape
-    bts = [_i32(t) for t in block_tables]
-    lens = [_i32(n) for n in seq_lens]
-    if T < 1 or np.any(lens[0] < T):
-        raise ValueError("every sequence must hold its T query tokens")
-    ebts = [np.repeat(bt, T, axis=0) for bt in bts]                  # entry (b, i): sequence b's table
-    elens = [np.repeat(ln, T) for ln in lens]
-    elens[0] = elens[0] - (T - 1) + np.tile(np.arange(T, dtype=np.int32), B)  # causal prefix in segment 0
+    ebts, elens = multi_entries(block_tables, seq_lens, T)
     out = decode(caches, ebts, elens, q.reshape(B * T, Hq, D), sm_scale, tau_low, split_tokens)
     return out.reshape(B, T, Hq, D)
 
