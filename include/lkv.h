@@ -52,8 +52,11 @@
  * 1 for a zero k_hat), and every call reads the key as r * k_hat: the
  * direction of the group codes with the norm of the original key.  The
  * codes, scales and zeros are those of the plain format.  lkv_quant_append
- * needs K and V aligned to head_dim / 64 elements for it; decode runs the
- * generic kernel; the tier calls return LKV_EUNSUPPORTED.
+ * needs K and V aligned to head_dim / 64 elements for it.  Decode reads the
+ * factors in the matrix-core kernels (bf16 Q, head_dim 128, group 64, K6 with
+ * V4 or V6, 4 or 8 query heads per KV head, a 16-byte aligned Q, splits of at
+ * most 4096 tokens) and in the generic kernel otherwise; the tier calls
+ * return LKV_EUNSUPPORTED.
  */
 #ifndef LKV_H
 #define LKV_H
@@ -97,7 +100,9 @@ typedef struct lkv_view {
     const int32_t* block_table; /* [batch][max_blocks] int32 */
     const int32_t* seq_lens;    /* [batch] int32, live tokens per sequence */
     int32_t max_blocks;
-    int32_t max_len;            /* (host) upper bound of seq_lens, sizes the grid */
+    int32_t max_len;            /* (host) upper bound of seq_lens, sizes the grid; a
+                                   length above it is out of contract and is read
+                                   as max_len */
     int64_t sum_len;            /* (host) hint: total of seq_lens over the batch,
                                    or 0 if unknown; only lkv_decode_plan reads it,
                                    to size splits for ragged batches */
@@ -196,6 +201,28 @@ int lkv_decode_attn_multi(const lkv_cache* segs, const lkv_view* views, int32_t 
                           int32_t q_dtype, int32_t batch, int32_t q_per_seq, int32_t num_q_heads, float sm_scale,
                           float tau_low, int32_t split_tokens, float* out, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/* lkv_decode_attn_multi (q_per_seq = T; 1 is lkv_decode_attn) that also
+ * reports every sparse-V skip decision, for tests that compare skip sets
+ * bit for bit (Super KV Compression page, third layer: the V term of a
+ * token under the threshold is not dequantised).  The rule compares
+ * exp(s - m) with tau_low * L in fp32; near the bound a test takes this
+ * call's decision as one of the correct ones.  The kernels, split plan and
+ * output are those of lkv_decode_attn_multi; only the mask is added.
+ * skip_mask  uint32 [batch * q_per_seq][num_q_heads][mask_words]; bit c of
+ *            a row (word c / 32, bit c % 32) is set when the V term of score
+ *            column c was skipped for that query head.  Column c is token
+ *            c of the first segment, or token c - C0 of the second, where
+ *            C0 = views[0].max_len rounded up to 64.  Bits of columns
+ *            without a live token are 0.  The call clears the mask first.
+ * mask_words >= (sum over segments of max_len rounded up to 64) / 32
+ * Other arguments as lkv_decode_attn_multi (split_tokens 0 =
+ * lkv_decode_plan_multi()).  Not for production use: the skip decisions
+ * cost one atomic per skipped pair. */
+int lkv_decode_attn_debug(const lkv_cache* segs, const lkv_view* views, int32_t nseg, const void* q,
+                          int32_t q_dtype, int32_t batch, int32_t q_per_seq, int32_t num_q_heads, float sm_scale,
+                          float tau_low, int32_t split_tokens, float* out, uint32_t* skip_mask, int32_t mask_words,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* The two stages of lkv_decode_attn, for callers that schedule them apart
  * (lkv_decode_attn is exactly lkv_decode_split followed by

@@ -89,12 +89,30 @@ static int32_t score_cols(const lkv_view* views, int32_t nseg)
     return n;
 }
 
+// Host checks of the split stage (every one of them runs before a launch);
+// fills one Fmt per segment.  batch counts grid entries.
+static int check_split(const lkv_cache* segs, const lkv_view* views, int32_t nseg, const void* q, int32_t q_dtype,
+                       int32_t batch, int32_t num_q_heads, float sm_scale, float tau_low, int32_t split_tokens,
+                       const void* workspace, size_t workspace_bytes, Fmt* f)
+{
+    const int st = check_decode(segs, views, nseg, batch, num_q_heads, f);
+    if (st != LKV_OK) return st;
+    if (q_dtype != LKV_F32 && q_dtype != LKV_BF16) return LKV_EINVAL;
+    if (split_tokens <= 0 || split_tokens % BT != 0) return LKV_EINVAL;
+    if (!std::isfinite(sm_scale) || std::isnan(tau_low)) return LKV_EINVAL;
+    const int64_t need = (int64_t)batch * num_q_heads * total_splits(views, nseg, split_tokens) * (f[0].D + 2) * 4;
+    if ((int64_t)workspace_bytes < need) return LKV_EINVAL;
+    if (batch == 0) return LKV_OK;
+    if (!q || (need > 0 && !workspace) || (uintptr_t)workspace % 16 != 0) return LKV_EINVAL;
+    return LKV_OK;
+}
+
 // Split stage; scores (optional) receives the base-2 score rows.  batch
 // counts grid entries: sequences times q_per_seq query tokens.
 static int split_impl(const lkv_cache* segs, const lkv_view* views, int32_t nseg, const void* q, int32_t q_dtype,
                       int32_t batch, int32_t num_q_heads, float sm_scale, float tau_low, int32_t split_tokens,
                       void* workspace, size_t workspace_bytes, void* stream, float* scores, int32_t score_stride,
-                      int32_t q_per_seq = 1);
+                      int32_t q_per_seq = 1, uint32_t* skip_mask = nullptr, int32_t mask_stride = 0);
 
 // Merge stage; ml (optional) receives (M, 1 / L) per (sequence, head).
 static int combine_impl(const lkv_cache* segs, const lkv_view* views, int32_t nseg, int32_t batch,
@@ -216,18 +234,12 @@ namespace lkv {
 static int split_impl(const lkv_cache* segs, const lkv_view* views, int32_t nseg, const void* q, int32_t q_dtype,
                       int32_t batch, int32_t num_q_heads, float sm_scale, float tau_low, int32_t split_tokens,
                       void* workspace, size_t workspace_bytes, void* stream, float* scores, int32_t score_stride,
-                      int32_t q_per_seq)
+                      int32_t q_per_seq, uint32_t* skip_mask, int32_t mask_stride)
 {
     Fmt f[2];
-    const int st = check_decode(segs, views, nseg, batch, num_q_heads, f);
-    if (st != LKV_OK) return st;
-    if (q_dtype != LKV_F32 && q_dtype != LKV_BF16) return LKV_EINVAL;
-    if (split_tokens <= 0 || split_tokens % BT != 0) return LKV_EINVAL;
-    if (!std::isfinite(sm_scale) || std::isnan(tau_low)) return LKV_EINVAL;
-    const int64_t need = (int64_t)batch * num_q_heads * total_splits(views, nseg, split_tokens) * (f[0].D + 2) * 4;
-    if ((int64_t)workspace_bytes < need) return LKV_EINVAL;
-    if (batch == 0) return LKV_OK;
-    if (!q || (need > 0 && !workspace) || (uintptr_t)workspace % 16 != 0) return LKV_EINVAL;
+    const int st = check_split(segs, views, nseg, q, q_dtype, batch, num_q_heads, sm_scale, tau_low, split_tokens,
+                               workspace, workspace_bytes, f);
+    if (st != LKV_OK || batch == 0) return st;
     const int32_t tot = (int32_t)total_splits(views, nseg, split_tokens);
     SegArgs a[2];
     int32_t base = 0;
@@ -237,6 +249,7 @@ static int split_impl(const lkv_cache* segs, const lkv_view* views, int32_t nseg
         a[s].block_table = views[s].block_table;
         a[s].seq_lens = views[s].seq_lens;
         a[s].max_blocks = views[s].max_blocks;
+        a[s].len_cap = views[s].max_len;
         a[s].n_splits = splits_of(views[s].max_len, split_tokens);
         a[s].split_base = base;
         base += a[s].n_splits;
@@ -245,6 +258,8 @@ static int split_impl(const lkv_cache* segs, const lkv_view* views, int32_t nseg
         a[s].tok_base = s == 0 ? 0 : (views[0].max_len + BT - 1) / BT * BT;
         a[s].q_per_seq = q_per_seq;
         a[s].causal = q_per_seq > 1 && s == 0;  // the new tokens are the first segment's tail
+        a[s].skip_mask = skip_mask;
+        a[s].mask_stride = mask_stride;
     }
     hipError_t e;
     if (nseg == 2 && launch_decode_split_mfma_tiered(a[0], a[1], q, q_dtype, batch, num_q_heads, sm_scale, tau_low,
@@ -345,7 +360,7 @@ int lkv_decode_attn_scores(const lkv_cache* segs, const lkv_view* views, int32_t
     for (int s = 0; s < 2; s++) {
         const bool on = s < nseg;
         sa.lens[s] = on ? views[s].seq_lens : nullptr;
-        sa.len_cap[s] = on ? views[s].max_blocks * BT : 0;
+        sa.len_cap[s] = on ? views[s].max_len : 0;
         sa.tok_base[s] = s == 0 ? 0 : (views[0].max_len + BT - 1) / BT * BT;
     }
     sa.acc = score_acc;
@@ -397,6 +412,38 @@ int lkv_decode_attn_multi(const lkv_cache* segs, const lkv_view* views, int32_t 
     if (batch > 0 && !out) return LKV_EINVAL;
     const int st = split_impl(segs, views, nseg, q, q_dtype, entries, num_q_heads, sm_scale, tau_low, split_tokens,
                               workspace, workspace_bytes, stream, nullptr, 0, q_per_seq);
+    if (st != LKV_OK) return st;
+    return lkv_decode_combine(segs, views, nseg, entries, num_q_heads, split_tokens, out, workspace, workspace_bytes,
+                              stream);
+}
+
+int lkv_decode_attn_debug(const lkv_cache* segs, const lkv_view* views, int32_t nseg, const void* q,
+                          int32_t q_dtype, int32_t batch, int32_t q_per_seq, int32_t num_q_heads, float sm_scale,
+                          float tau_low, int32_t split_tokens, float* out, uint32_t* skip_mask, int32_t mask_words,
+                          void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (q_per_seq < 1 || (int64_t)batch * q_per_seq > INT32_MAX) return LKV_EINVAL;
+    if (!segs || !views || nseg < 1 || nseg > 2) return LKV_EINVAL;
+    for (int s = 0; s < nseg; s++)
+        if (views[s].max_len < (s == 0 ? q_per_seq : 0) && batch > 0) return LKV_EINVAL;
+    if (split_tokens == 0) {
+        const int st = lkv_decode_plan_multi(segs, views, nseg, batch, q_per_seq, num_q_heads, &split_tokens);
+        if (st != LKV_OK) return st;
+    }
+    const int32_t entries = batch * q_per_seq;
+    Fmt f[2];
+    const int st0 = check_split(segs, views, nseg, q, q_dtype, entries, num_q_heads, sm_scale, tau_low, split_tokens,
+                                workspace, workspace_bytes, f);
+    if (st0 != LKV_OK) return st0;
+    const int64_t cols = score_cols(views, nseg);
+    if (mask_words < cols / 32) return LKV_EINVAL;
+    if (batch == 0) return LKV_OK;
+    if (!out || !skip_mask) return LKV_EINVAL;
+    const hipError_t e = launch_fill_u32(skip_mask, (int64_t)entries * num_q_heads * mask_words, 0u,
+                                         (hipStream_t)stream);
+    if (e != hipSuccess) return LKV_EHIP;
+    const int st = split_impl(segs, views, nseg, q, q_dtype, entries, num_q_heads, sm_scale, tau_low, split_tokens,
+                              workspace, workspace_bytes, stream, nullptr, 0, q_per_seq, skip_mask, mask_words);
     if (st != LKV_OK) return st;
     return lkv_decode_combine(segs, views, nseg, entries, num_q_heads, split_tokens, out, workspace, workspace_bytes,
                               stream);

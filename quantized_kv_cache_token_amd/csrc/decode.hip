@@ -12,6 +12,8 @@
 // combine kernel merges them.
 #include <hip/hip_fp16.h>
 
+#include <algorithm>
+
 #include "lkv_internal.h"
 #include "quant_device.h"
 
@@ -68,7 +70,7 @@ __global__ __launch_bounds__(64) void split_valu_kernel(SplitArgs a)
     const Fmt& f = sg.f;
     const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x;
-    const int len = max(0, min(entry_len(sg, b), sg.max_blocks * BT));  // out-of-contract lengths are clamped
+    const int len = max(0, min(entry_len(sg, b), sg.len_cap));  // out-of-contract lengths are clamped
     const int t0 = sp * a.split_tokens;
     const int t1 = min(t0 + a.split_tokens, len);
     if (t1 <= t0) {  // a split past the end: only (m, L) = (-inf, 0), its o row is never read
@@ -130,6 +132,9 @@ __global__ __launch_bounds__(64) void split_valu_kernel(SplitArgs a)
             m[h] = m_new;
             const bool skip = a.tau_low > 0.0f && e < a.tau_low * L[h];
             ps[h][lane] = skip ? 0.0f : e;
+            if (sg.skip_mask != nullptr && skip && live)
+                mark_skipped(sg.skip_mask + ((int64_t)b * a.num_q_heads + kvh * G + h) * sg.mask_stride,
+                             sg.tok_base + bs + lane);
 #pragma unroll
             for (int i = 0; i < VPL; i++) o[h][i] *= alpha;
         }
@@ -332,6 +337,19 @@ __global__ __launch_bounds__(256) void score_accumulate_kernel(ScoreAccArgs a)
     }
     for (; h < a.num_q_heads; h++) part[0] += exp2f(srow[(int64_t)h * a.score_stride] - ml[2 * h]) * ml[2 * h + 1];
     a.acc[((int64_t)seg * a.batch + b) * a.acc_stride + j] += (part[0] + part[1]) + (part[2] + part[3]);
+}
+
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v)
+{
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
+}
+
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t stream)
+{
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n, v);
+    return hipGetLastError();
 }
 
 hipError_t launch_score_accumulate(const ScoreAccArgs& a, hipStream_t stream)

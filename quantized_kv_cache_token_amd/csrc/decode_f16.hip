@@ -106,7 +106,9 @@ __device__ __forceinline__ void as_words(const uint4& x, uint32_t (&w)[4])
     w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
 }
 
-template <int G>
+// DBG: the same kernel that also records its skip decisions (the test entry
+// point's skip mask); production launches take DBG = false.
+template <int G, bool DBG>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void split_f16_kernel(F16Args a)
 {
     static_assert(G == 4 || G == 8, "4 or 8 query heads per KV head");
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
     // (the sequence and length are uniform: computed before the lane-dependent
     // load, so that they stay in scalar registers)
     const int seq = entry_seq(sg, b);
-    const int len = max(0, min(entry_len(sg, b), sg.max_blocks * BT));
+    const int len = max(0, min(entry_len(sg, b), sg.len_cap));
     const int32_t* bt = sg.block_table + (int64_t)seq * sg.max_blocks + t0 / BT;
     const int bt_lane = lane < min(64, sg.max_blocks - t0 / BT) ? bt[lane] : 0;
     asm volatile("" ::: "memory");  // both loads are issued before either is waited for
@@ -149,6 +151,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
     float* const srow = sg.scores != nullptr && part == 0 && c < 2 * G
                             ? sg.scores + ((int64_t)b * a.num_q_heads + head) * sg.score_stride + sg.tok_base + t0
                             : nullptr;
+    // the same lane's skip-mask row (test entry point only)
+    uint32_t* const mrow = DBG && sg.skip_mask != nullptr && part == 0 && c < 2 * G
+                               ? sg.skip_mask + ((int64_t)b * a.num_q_heads + head) * sg.mask_stride
+                               : nullptr;
 
     // ---- Q as the QK B operand: K-step s, K index 8q + i <-> channel 32s + 8q + i
     float x[4][8];
@@ -294,6 +300,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
                 else k1 |= p[i] > 0.0f;
             }
             keep = (__builtin_amdgcn_ballot_w64(k0) ? 1u : 0u) | (__builtin_amdgcn_ballot_w64(k1) ? 2u : 0u);
+            if (mrow != nullptr) {  // a live token's weight is 0 here exactly when it was below thr
+#pragma unroll
+                for (int t = 0; t < 4; t++) {
+#pragma unroll
+                    for (int r = 0; r < 4; r++) {
+                        const int x = f16_tok(t, 4 * q + r);
+                        if (x < nlive && p[4 * t + r] == 0.0f) mark_skipped(mrow, sg.tok_base + t0 + k * BT + x);
+                    }
+                }
+            }
         }
 
         // ---- P.V
@@ -384,8 +400,11 @@ bool launch_decode_split_f16(const SegArgs& s, const void* q, int q_dtype, int32
     a.tau_low = tau_low;
     a.partials = partials;
     dim3 grid((unsigned)s.n_splits, (unsigned)f.H, (unsigned)batch);
-    if (G == 4) hipLaunchKernelGGL((split_f16_kernel<4>), grid, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL((split_f16_kernel<8>), grid, dim3(64), 0, stream, a);
+    const bool dbg = s.skip_mask != nullptr;
+    if (G == 4 && dbg) hipLaunchKernelGGL((split_f16_kernel<4, true>), grid, dim3(64), 0, stream, a);
+    else if (G == 4) hipLaunchKernelGGL((split_f16_kernel<4, false>), grid, dim3(64), 0, stream, a);
+    else if (dbg) hipLaunchKernelGGL((split_f16_kernel<8, true>), grid, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL((split_f16_kernel<8, false>), grid, dim3(64), 0, stream, a);
     *err = hipGetLastError();
     return true;
 }

@@ -340,7 +340,8 @@ __device__ __forceinline__ void block_qk(const BlockRegs<VB>& R, const uint32_t 
 template <int VB, bool PARTIAL, bool KN>
 __device__ __forceinline__ float block_softmax(const f32x4_t (&dot)[4], const uint8_t* lds, SplitState& S, float qsum,
                                                float score_scale, float tau_low, int nlive, int q, int c,
-                                               float (&p)[16], uint32_t& keep, float* srow)
+                                               float (&p)[16], uint32_t& keep, float* srow, uint32_t* mrow,
+                                               int mcol)
 {
     const int gc = c & 1;
     float sk[16];
@@ -414,6 +415,16 @@ __device__ __forceinline__ float block_softmax(const f32x4_t (&dot)[4], const ui
             else k1 |= p[i] > 0.0f;
         }
         keep = (__builtin_amdgcn_ballot_w64(k0) ? 1u : 0u) | (__builtin_amdgcn_ballot_w64(k1) ? 2u : 0u);
+        if (mrow != nullptr && (c & 1) == 0) {  // a live token's weight is 0 here exactly when it was below thr
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int tok = 16 * q + tok_of<VB>(t, r);
+                    if ((!PARTIAL || tok < nlive) && p[4 * t + r] == 0.0f) mark_skipped(mrow, mcol + tok);
+                }
+            }
+        }
     }
     return alpha;
 }
@@ -627,7 +638,8 @@ __device__ __forceinline__ void block_qk_sets(const BlockRegs<VB>& R, const uint
 template <int VB, bool PARTIAL, bool KN>
 __device__ __forceinline__ float block_softmax_sets(const f32x4_t (&dot)[2], const uint8_t* lds, SplitState& S,
                                                     float qsum, float score_scale, float tau_low, int nlive, int q,
-                                                    int c, float (&p)[8], uint32_t& keep, float* srow)
+                                                    int c, float (&p)[8], uint32_t& keep, float* srow,
+                                                    uint32_t* mrow, int mcol)
 {
     const int gc = c & 1, s = c >> 3;
     float sk[8], zk[8];
@@ -695,6 +707,16 @@ __device__ __forceinline__ float block_softmax_sets(const f32x4_t (&dot)[2], con
             else k1 |= p[x] > 0.0f;
         }
         keep = (__builtin_amdgcn_ballot_w64(k0) ? 1u : 0u) | (__builtin_amdgcn_ballot_w64(k1) ? 2u : 0u);
+        if (mrow != nullptr && gc == 0) {  // a live token's weight is 0 here exactly when it was below thr
+#pragma unroll
+            for (int u = 0; u < 2; u++) {
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int tok = set_tok<VB>(q, s, u, i);
+                    if ((!PARTIAL || tok < nlive) && p[4 * u + i] == 0.0f) mark_skipped(mrow, mcol + tok);
+                }
+            }
+        }
     }
     return alpha;
 }
@@ -784,7 +806,7 @@ __device__ __forceinline__ void block_pv_sets(const BlockRegs<VB>& R, const uint
 // for both.  The earlier token's causal prefix is one token shorter: its
 // columns are masked in the split's last blocks.  An odd T's last token is
 // paired with itself and its second copy is not written.
-template <int VB, int G, bool KN, bool PAIR = false>
+template <int VB, int G, bool KN, bool PAIR = false, bool DBG = false>
 __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint4* meta_lds)
 {
     static_assert(G == 4 || G == 8, "4 or 8 query heads per KV head");
@@ -808,11 +830,11 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
         e0 = b / np * T + tk;
         e1 = tk + 1 < T ? e0 + 1 : e0;
         seq = entry_seq(sg, e0);
-        len0 = max(0, min(entry_len(sg, e0), sg.max_blocks * BT));
-        len = max(0, min(entry_len(sg, e1), sg.max_blocks * BT));
+        len0 = max(0, min(entry_len(sg, e0), sg.len_cap));
+        len = max(0, min(entry_len(sg, e1), sg.len_cap));
     } else {
         seq = entry_seq(sg, b);
-        len = max(0, min(entry_len(sg, b), sg.max_blocks * BT));
+        len = max(0, min(entry_len(sg, b), sg.len_cap));
     }
     // partial row (entry, query head) of layout head hh, and whether it is written
     auto prow = [&](int hh) -> int64_t {
@@ -852,6 +874,10 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
     const int hA = G == 8 ? 2 * q : 2 * (q & 1);
     // this lane's head's score row, at the split's first token
     const int64_t srow0 = ((int64_t)b * a.num_q_heads + head) * sg.score_stride + sg.tok_base + t0;
+    // this lane's head's skip-mask row (test entry point only)
+    uint32_t* const mrow = DBG && sg.skip_mask != nullptr && pwrite(hc)
+                               ? sg.skip_mask + (PAIR ? prow(hc) : (int64_t)b * a.num_q_heads + head) * sg.mask_stride
+                               : nullptr;
 
     // ---- Q as the QK B operand.  8-head layout: this lane group (q) holds
     // channels [32q, 32q + 32), in group q >> 1; zero unless that is the
@@ -973,13 +999,14 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
         float p[SETS ? 8 : 16];
         uint32_t keep;
         float* srow = !PAIR && sg.scores != nullptr ? sg.scores + srow0 + (int64_t)k * BT : nullptr;
+        const int mcol = sg.tok_base + t0 + k * BT;
         if constexpr (SETS) {
             const float alpha = block_softmax_sets<VB, PARTIAL, KN>(dot, lds, S, qsum, a.score_scale, a.tau_low,
-                                                                    nlive, q, c, p, keep, srow);
+                                                                    nlive, q, c, p, keep, srow, mrow, mcol);
             block_pv_sets<VB, PARTIAL>(R, lds, S, p, alpha, keep, q, c, hA, mk);
         } else {
             const float alpha = block_softmax<VB, PARTIAL, KN>(dot, lds, S, qsum, a.score_scale, a.tau_low, nlive, q,
-                                                               c, p, keep, srow);
+                                                               c, p, keep, srow, mrow, mcol);
             block_pv<VB, PARTIAL>(R, lds, S, p, alpha, keep, q, c, hA, mk);
         }
         if constexpr (MORE) load_v<VB>(R, cn, off_vc, c, q);
@@ -1043,33 +1070,36 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
     }
 }
 
-template <int VB, int G, bool KN>
+// DBG: the same kernel that also records its skip decisions (the test entry
+// point's skip mask); production launches take DBG = false, where the mask
+// code is compiled out.
+template <int VB, int G, bool KN, bool DBG>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void split_mfma_kernel(MfmaArgs a)
 {
     __shared__ uint4 meta_lds[meta_bytes<KN>() / 16];
-    split_body<VB, G, KN>(a, blockIdx.x, meta_lds);
+    split_body<VB, G, KN, false, DBG>(a, blockIdx.x, meta_lds);
 }
 
 // Query-token pairs of a multi-token call with 4 query heads per KV head
 // (split_body's PAIR): grid z = sequence x ceil(T / 2) pairs.
-template <int VB, bool KN>
+template <int VB, bool KN, bool DBG>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void split_mfma_pair_kernel(MfmaArgs a)
 {
     __shared__ uint4 meta_lds[meta_bytes<KN>() / 16];
-    split_body<VB, 8, KN, true>(a, blockIdx.x, meta_lds);
+    split_body<VB, 8, KN, true, DBG>(a, blockIdx.x, meta_lds);
 }
 
 // Both segments of a tiered cache in one launch: workgroups [0, n0) run the
 // HIGH (V6) segment's splits, the rest the MID (V4) segment's, so the two
 // share the machine instead of running one after the other.
-template <int G>
+template <int G, bool DBG>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void split_mfma_tiered_kernel(MfmaArgs a0,
                                                                                                        MfmaArgs a1)
 {
     __shared__ uint4 meta_lds[META_BYTES / 16];
     const int sp = blockIdx.x;
-    if (sp < a0.seg.n_splits) split_body<6, G, false>(a0, sp, meta_lds);
-    else split_body<4, G, false>(a1, sp - a0.seg.n_splits, meta_lds);
+    if (sp < a0.seg.n_splits) split_body<6, G, false, false, DBG>(a0, sp, meta_lds);
+    else split_body<4, G, false, false, DBG>(a1, sp - a0.seg.n_splits, meta_lds);
 }
 
 // Whether a segment has a matrix-core kernel.
@@ -1115,10 +1145,36 @@ bool launch_decode_split_mfma_tiered(const SegArgs& high, const SegArgs& mid, co
     const MfmaArgs a1 = mfma_args(mid, q, num_q_heads, sm_scale, tau_low, split_tokens, total_splits, partials);
     const int G = num_q_heads / high.f.H;
     dim3 grid((unsigned)(high.n_splits + mid.n_splits), (unsigned)high.f.H, (unsigned)batch);
-    if (G == 4) hipLaunchKernelGGL(split_mfma_tiered_kernel<4>, grid, dim3(64), 0, stream, a0, a1);
-    else hipLaunchKernelGGL(split_mfma_tiered_kernel<8>, grid, dim3(64), 0, stream, a0, a1);
+    const bool dbg = high.skip_mask != nullptr;
+    if (G == 4 && dbg) hipLaunchKernelGGL((split_mfma_tiered_kernel<4, true>), grid, dim3(64), 0, stream, a0, a1);
+    else if (G == 4) hipLaunchKernelGGL((split_mfma_tiered_kernel<4, false>), grid, dim3(64), 0, stream, a0, a1);
+    else if (dbg) hipLaunchKernelGGL((split_mfma_tiered_kernel<8, true>), grid, dim3(64), 0, stream, a0, a1);
+    else hipLaunchKernelGGL((split_mfma_tiered_kernel<8, false>), grid, dim3(64), 0, stream, a0, a1);
     *err = hipGetLastError();
     return true;
+}
+
+template <bool DBG>
+static void launch_pair(const MfmaArgs& a, int vb, bool kn, dim3 grid, hipStream_t st)
+{
+    if (vb == 4 && kn) hipLaunchKernelGGL((split_mfma_pair_kernel<4, true, DBG>), grid, dim3(64), 0, st, a);
+    else if (vb == 4) hipLaunchKernelGGL((split_mfma_pair_kernel<4, false, DBG>), grid, dim3(64), 0, st, a);
+    else if (kn) hipLaunchKernelGGL((split_mfma_pair_kernel<6, true, DBG>), grid, dim3(64), 0, st, a);
+    else hipLaunchKernelGGL((split_mfma_pair_kernel<6, false, DBG>), grid, dim3(64), 0, st, a);
+}
+
+template <bool DBG>
+static void launch_plain(const MfmaArgs& a, int vb, int G, bool kn, dim3 grid, hipStream_t st)
+{
+    if (kn) {  // direction-preserving K
+        if (vb == 4 && G == 4) hipLaunchKernelGGL((split_mfma_kernel<4, 4, true, DBG>), grid, dim3(64), 0, st, a);
+        else if (vb == 4) hipLaunchKernelGGL((split_mfma_kernel<4, 8, true, DBG>), grid, dim3(64), 0, st, a);
+        else if (G == 4) hipLaunchKernelGGL((split_mfma_kernel<6, 4, true, DBG>), grid, dim3(64), 0, st, a);
+        else hipLaunchKernelGGL((split_mfma_kernel<6, 8, true, DBG>), grid, dim3(64), 0, st, a);
+    } else if (vb == 4 && G == 4) hipLaunchKernelGGL((split_mfma_kernel<4, 4, false, DBG>), grid, dim3(64), 0, st, a);
+    else if (vb == 4) hipLaunchKernelGGL((split_mfma_kernel<4, 8, false, DBG>), grid, dim3(64), 0, st, a);
+    else if (G == 4) hipLaunchKernelGGL((split_mfma_kernel<6, 4, false, DBG>), grid, dim3(64), 0, st, a);
+    else hipLaunchKernelGGL((split_mfma_kernel<6, 8, false, DBG>), grid, dim3(64), 0, st, a);
 }
 
 // Returns true and launches when the format and shape have a matrix-core
@@ -1134,23 +1190,13 @@ bool launch_decode_split_mfma(const SegArgs& s, const void* q, int q_dtype, int3
     const int T = s.q_per_seq;
     if (T > 1 && G == 4) {  // batch counts B * T entries: B * ceil(T / 2) pairs
         dim3 grid((unsigned)s.n_splits, (unsigned)f.H, (unsigned)(batch / T * ((T + 1) / 2)));
-        if (f.vb == 4 && f.k_norm) hipLaunchKernelGGL((split_mfma_pair_kernel<4, true>), grid, dim3(64), 0, stream, a);
-        else if (f.vb == 4) hipLaunchKernelGGL((split_mfma_pair_kernel<4, false>), grid, dim3(64), 0, stream, a);
-        else if (f.k_norm) hipLaunchKernelGGL((split_mfma_pair_kernel<6, true>), grid, dim3(64), 0, stream, a);
-        else hipLaunchKernelGGL((split_mfma_pair_kernel<6, false>), grid, dim3(64), 0, stream, a);
-        *err = hipGetLastError();
-        return true;
+        if (s.skip_mask != nullptr) launch_pair<true>(a, f.vb, f.k_norm, grid, stream);
+        else launch_pair<false>(a, f.vb, f.k_norm, grid, stream);
+    } else {
+        dim3 grid((unsigned)s.n_splits, (unsigned)f.H, (unsigned)batch);
+        if (s.skip_mask != nullptr) launch_plain<true>(a, f.vb, G, f.k_norm, grid, stream);
+        else launch_plain<false>(a, f.vb, G, f.k_norm, grid, stream);
     }
-    dim3 grid((unsigned)s.n_splits, (unsigned)f.H, (unsigned)batch);
-    if (f.k_norm) {  // direction-preserving K
-        if (f.vb == 4 && G == 4) hipLaunchKernelGGL((split_mfma_kernel<4, 4, true>), grid, dim3(64), 0, stream, a);
-        else if (f.vb == 4) hipLaunchKernelGGL((split_mfma_kernel<4, 8, true>), grid, dim3(64), 0, stream, a);
-        else if (G == 4) hipLaunchKernelGGL((split_mfma_kernel<6, 4, true>), grid, dim3(64), 0, stream, a);
-        else hipLaunchKernelGGL((split_mfma_kernel<6, 8, true>), grid, dim3(64), 0, stream, a);
-    } else if (f.vb == 4 && G == 4) hipLaunchKernelGGL((split_mfma_kernel<4, 4, false>), grid, dim3(64), 0, stream, a);
-    else if (f.vb == 4) hipLaunchKernelGGL((split_mfma_kernel<4, 8, false>), grid, dim3(64), 0, stream, a);
-    else if (G == 4) hipLaunchKernelGGL((split_mfma_kernel<6, 4, false>), grid, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL((split_mfma_kernel<6, 8, false>), grid, dim3(64), 0, stream, a);
     *err = hipGetLastError();
     return true;
 }

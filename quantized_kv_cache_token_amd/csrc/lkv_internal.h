@@ -33,6 +33,8 @@ struct SegArgs {
     const int32_t* block_table;
     const int32_t* seq_lens;
     int32_t max_blocks;
+    int32_t len_cap;       // the view's max_len (<= max_blocks * 64): lengths are clamped to it, so
+                           // an out-of-contract length never reaches past the grid or the score rows
     int32_t n_splits;      // splits of this segment in the grid
     int32_t split_base;    // index of its first split in the partials
     // optional: every live token's base-2 score per query head, into rows
@@ -47,7 +49,18 @@ struct SegArgs {
     // newest tokens
     int32_t q_per_seq;
     int32_t causal;
+    // optional (test entry point only): one bit per (grid entry, query
+    // head, score column), set when the token's V term is skipped; rows of
+    // mask_stride words, cleared by the caller; null otherwise
+    uint32_t* skip_mask;
+    int32_t mask_stride;
 };
+
+// Records a skipped (token, head) pair in a skip-mask row (bit col).
+__device__ __forceinline__ void mark_skipped(uint32_t* row, int col)
+{
+    atomicOr(row + (col >> 5), 1u << (col & 31));
+}
 
 // Block-table row and length that grid entry e reads in segment s (the
 // length before clamping to the table).
@@ -116,6 +129,9 @@ struct ScoreAccArgs {
 hipError_t launch_score_accumulate(const ScoreAccArgs& a, hipStream_t stream);
 
 hipError_t launch_decode_combine(const CombineArgs& a, int32_t batch, int32_t D, hipStream_t stream);
+
+// p[0 .. n) = v on the stream (a kernel, not a memset node).
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t stream);
 
 // A source segment of a tier scan and a destination segment.
 struct TierSource {

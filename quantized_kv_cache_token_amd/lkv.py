@@ -7,6 +7,7 @@ library is missing, loading it raises -- there is no fallback.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes as C
 import os
 from dataclasses import dataclass
@@ -45,7 +46,8 @@ EXPORTS = ["lkv_status_string", "lkv_chunk_layout", "lkv_quant_append", "lkv_dec
            "lkv_decode_workspace_bytes", "lkv_decode_attn", "lkv_decode_split", "lkv_decode_combine",
            "lkv_decode_scores_workspace_bytes", "lkv_decode_attn_scores",
            "lkv_default_thresholds", "lkv_tier_workspace_bytes", "lkv_tier_update",
-           "lkv_retier_workspace_bytes", "lkv_retier", "lkv_decode_attn_multi", "lkv_decode_plan_multi"]
+           "lkv_retier_workspace_bytes", "lkv_retier", "lkv_decode_attn_multi", "lkv_decode_plan_multi",
+           "lkv_decode_attn_debug"]
 
 
 def lib():
@@ -77,6 +79,8 @@ def lib():
         "lkv_retier_workspace_bytes": ([I32, I32, I32], I64),
         "lkv_decode_attn_multi": ([PC, PV, I32, P, I32, I32, I32, I32, F, F, I32, P, P, C.c_size_t, V], C.c_int),
         "lkv_decode_plan_multi": ([PC, PV, I32, I32, I32, I32, C.POINTER(I32)], C.c_int),
+        "lkv_decode_attn_debug": ([PC, PV, I32, P, I32, I32, I32, I32, F, F, I32, P, P, I32, P, C.c_size_t, V],
+                                  C.c_int),
         "lkv_retier": ([PC, PV, P, I32, PC, PV, P, I32, F, F, PC, P, I32, PC, P, I32, P, P, P, P, I32, P,
                         C.c_size_t, V], C.c_int),
     }
@@ -106,6 +110,13 @@ def _require(cond: bool, what: str) -> None:
 def _stream(stream=None):
     s = stream if stream is not None else torch.cuda.current_stream()
     return C.c_void_p(s.cuda_stream)
+
+
+def _on(stream=None):
+    """Context for the binding's own allocations (outputs, workspaces): on the
+    stream the call's kernels run on, so that the caching allocator does not
+    hand that memory to other work while they are queued."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
 
 
 def _ptr(t):
@@ -216,10 +227,11 @@ def decode_attn(caches, views, q: torch.Tensor, sm_scale: float, tau_low: float 
     _require(q.is_contiguous(), "q must be contiguous")
     if split_tokens == 0:
         split_tokens = decode_plan(caches, views, B, Hq)
-    if workspace is None:
-        workspace = decode_workspace(caches, views, B, Hq, split_tokens, q.device)
-    if out is None:
-        out = torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
+    with _on(stream):
+        if workspace is None:
+            workspace = decode_workspace(caches, views, B, Hq, split_tokens, q.device)
+        if out is None:
+            out = torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
     cs, vs, n = _segs(caches, views)
     _check("lkv_decode_attn", lib().lkv_decode_attn(
         cs, vs, n, _ptr(q), _DTYPE[q.dtype], B, Hq, sm_scale, tau_low, split_tokens, _ptr(out), _ptr(workspace),
@@ -236,15 +248,49 @@ def decode_attn_multi(caches, views, q: torch.Tensor, sm_scale: float, tau_low: 
     _require(q.is_contiguous(), "q must be contiguous")
     if split_tokens == 0:
         split_tokens = decode_plan_multi(caches, views, B, T, Hq)
-    if workspace is None:
-        workspace = decode_workspace(caches, views, B * T, Hq, split_tokens, q.device)
-    if out is None:
-        out = torch.empty(B, T, Hq, D, dtype=torch.float32, device=q.device)
+    with _on(stream):
+        if workspace is None:
+            workspace = decode_workspace(caches, views, B * T, Hq, split_tokens, q.device)
+        if out is None:
+            out = torch.empty(B, T, Hq, D, dtype=torch.float32, device=q.device)
     cs, vs, n = _segs(caches, views)
     _check("lkv_decode_attn_multi", lib().lkv_decode_attn_multi(
         cs, vs, n, _ptr(q), _DTYPE[q.dtype], B, T, Hq, sm_scale, tau_low, split_tokens, _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
+
+
+def skip_mask_words(views) -> int:
+    """Words per row of the skip mask of decode_attn_debug: every segment's
+    max_len rounded up to 64 tokens, one bit per token."""
+    return sum(-(-int(v.max_len) // BLOCK_TOKENS) * BLOCK_TOKENS for v in views) // 32
+
+
+def decode_attn_debug(caches, views, q: torch.Tensor, sm_scale: float, tau_low: float = 0.0,
+                      split_tokens: int = 0, stream=None):
+    """lkv_decode_attn_debug: decode_attn (q [B][Hq][D]) or decode_attn_multi
+    (q [B][T][Hq][D]) that also returns the sparse-V skip decisions.  Returns
+    (out, mask): mask int32 [B*T][Hq][words], bit c set when score column c
+    (the first segment's tokens, then the second's from its max_len rounded
+    up to 64) had its V term skipped.  For tests."""
+    if q.dim() == 3:
+        B, Hq, D = q.shape
+        T = 1
+    else:
+        B, T, Hq, D = q.shape
+    _require(q.is_contiguous(), "q must be contiguous")
+    if split_tokens == 0:
+        split_tokens = decode_plan_multi(caches, views, B, T, Hq)
+    words = max(skip_mask_words(views), 1)
+    with _on(stream):
+        workspace = decode_workspace(caches, views, B * T, Hq, split_tokens, q.device)
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        mask = torch.empty(B * T, Hq, words, dtype=torch.int32, device=q.device)
+    cs, vs, n = _segs(caches, views)
+    _check("lkv_decode_attn_debug", lib().lkv_decode_attn_debug(
+        cs, vs, n, _ptr(q), _DTYPE[q.dtype], B, T, Hq, sm_scale, tau_low, split_tokens, _ptr(out), _ptr(mask),
+        words, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, mask
 
 
 def decode_scores_workspace(caches, views, batch, num_q_heads, split_tokens, device="cuda") -> torch.Tensor:
@@ -267,10 +313,11 @@ def decode_attn_scores(caches, views, q: torch.Tensor, score_acc: torch.Tensor, 
     _require(score_acc.dim() == 3 and score_acc.shape[:2] == (len(caches), B), "score_acc must be [nseg][B][stride]")
     if split_tokens == 0:
         split_tokens = decode_plan(caches, views, B, Hq)
-    if workspace is None:
-        workspace = decode_scores_workspace(caches, views, B, Hq, split_tokens, q.device)
-    if out is None:
-        out = torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
+    with _on(stream):
+        if workspace is None:
+            workspace = decode_scores_workspace(caches, views, B, Hq, split_tokens, q.device)
+        if out is None:
+            out = torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
     cs, vs, n = _segs(caches, views)
     _check("lkv_decode_attn_scores", lib().lkv_decode_attn_scores(
         cs, vs, n, _ptr(q), _DTYPE[q.dtype], B, Hq, sm_scale, tau_low, split_tokens, _ptr(out), _ptr(score_acc),
@@ -315,7 +362,9 @@ def tier_update(src: Cache, src_view: View, scores: torch.Tensor, tau_low: float
     _require(scores.dtype == torch.float32 and tiers.dtype == torch.uint8 and tiers.shape == scores.shape,
              "scores fp32 and tiers uint8, both [B][stride]")
     if workspace is None:
-        workspace = torch.empty(max(tier_workspace_bytes(B, stride), 4), dtype=torch.uint8, device=scores.device)
+        with _on(stream):
+            workspace = torch.empty(max(tier_workspace_bytes(B, stride), 4), dtype=torch.uint8,
+                                    device=scores.device)
     cs, ch, cm, sv = src.c(), dst_h.c(), dst_m.c(), src_view.c()
     _check("lkv_tier_update", lib().lkv_tier_update(
         C.byref(cs), C.byref(sv), _ptr(scores), stride, tau_low, tau_high, C.byref(ch), _ptr(h_block_table),
@@ -344,8 +393,9 @@ def retier(h: Cache, h_view: View, h_scores: torch.Tensor, m: Cache, m_view: Vie
     _require(h_tiers.dtype == torch.uint8 and h_tiers.shape == h_scores.shape, "h_tiers uint8, shape of h_scores")
     _require(m_tiers.dtype == torch.uint8 and m_tiers.shape == m_scores.shape, "m_tiers uint8, shape of m_scores")
     if workspace is None:
-        workspace = torch.empty(max(retier_workspace_bytes(B, hs, ms), 8), dtype=torch.uint8,
-                                device=h_scores.device)
+        with _on(stream):
+            workspace = torch.empty(max(retier_workspace_bytes(B, hs, ms), 8), dtype=torch.uint8,
+                                    device=h_scores.device)
     ch, cm, cdh, cdm, hv, mv = h.c(), m.c(), dst_h.c(), dst_m.c(), h_view.c(), m_view.c()
     _check("lkv_retier", lib().lkv_retier(
         C.byref(ch), C.byref(hv), _ptr(h_scores), hs, C.byref(cm), C.byref(mv), _ptr(m_scores), ms, tau_low,

@@ -97,3 +97,54 @@ class Pair:
 
 def sm_scale(D: int) -> float:
     return float(np.float32(1.0 / math.sqrt(D)))
+
+
+# Relative band of the sparse-V skip decisions that may go either way: the
+# GPU evaluates exp(s - m) and tau_low * L in fp32, where a score carries a
+# relative error of order 1e-5 of its terms (bf16-exact products, fp32
+# accumulation over 128 channels against an offset of 128 per code) and L
+# one of order n * 2^-24; pairs whose exact margin is within 2^-10 of the
+# bound are taken as the GPU decides.
+SKIP_BAND = 2.0 ** -10
+
+
+def mask_to_given(mask: torch.Tensor, max_lens, max_tok: int) -> np.ndarray:
+    """GPU skip mask int32 [E][Hq][words] -> the oracle's layout uint8
+    [E][Hq][nseg][max_tok] (segment s's columns start at the sum of the
+    earlier segments' max_len rounded up to 64)."""
+    m = mask.cpu().numpy()
+    bits = np.unpackbits(m.view(np.uint8), axis=-1, bitorder="little")
+    E, Hq = m.shape[:2]
+    given = np.zeros((E, Hq, len(max_lens), max_tok), np.uint8)
+    col = 0
+    for s, ml in enumerate(max_lens):
+        given[:, :, s, :ml] = bits[:, :, col:col + ml]
+        assert not bits[:, :, col + ml:col + -(-ml // BT) * BT].any(), "mask bits past max_len"
+        col += -(-ml // BT) * BT
+    return given
+
+
+def resolved_reference(ref_caches, ref_bts, ref_lens, q_host: np.ndarray, sm: float, tau: float, split: int,
+                       mask: torch.Tensor, max_lens, what: str = ""):
+    """The oracle's decode with the GPU's skip decisions taken inside
+    SKIP_BAND; every decision outside the band must equal the exact one, bit
+    for bit, and no column without a live token may be marked.  Returns the
+    oracle output and (live pairs, pairs whose GPU decision differs from the
+    exact one, the largest relative margin among those)."""
+    max_tok = max(np.asarray(bt).shape[1] for bt in ref_bts) * BT
+    given = mask_to_given(mask, max_lens, max_tok)
+    out, skip, amb, margin = O.decode_resolved(ref_caches, ref_bts, ref_lens, q_host, sm, tau, split, given,
+                                               SKIP_BAND)
+    E, Hq = given.shape[:2]
+    live = np.zeros(given.shape, bool)
+    for s, ln in enumerate(ref_lens):
+        ln = np.asarray(ln)
+        for e in range(E):
+            live[e, :, s, :int(ln[e])] = True
+    assert not (given.astype(bool) & ~live).any(), f"{what}: skip bits on columns without a live token"
+    bad = (given != skip) & live
+    assert not bad.any(), (f"{what}: {int(bad.sum())} skip decisions differ outside the band; relative margins "
+                           f"{margin[bad][:8]}")
+    flips = live & (given.astype(bool) != (margin < 0)) if tau > 0 else np.zeros_like(live)
+    worst = float(np.abs(margin[flips]).max()) if flips.any() else 0.0
+    return out, (int(live.sum()), int(flips.sum()), worst)

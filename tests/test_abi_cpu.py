@@ -188,6 +188,32 @@ def test_decode_multi_rejects_bad_arguments():
     assert L.lkv_decode_workspace_bytes(cs, vs, 1, 8 * 4, 32, 256) == 8 * 4 * 32 * 4 * 130 * 4
 
 
+def test_decode_debug_rejects_bad_arguments_before_any_launch():
+    """Every check of the skip-mask entry point runs before it clears the
+    mask: a rejected call queues nothing (without a GPU, a queued kernel
+    would report LKV_EHIP instead)."""
+    L = lkv.lib()
+    p = C.c_void_p(0x90000)
+    cs = (lkv._Cache * 2)(_cache(v_bits=6), _cache())
+
+    def call(T=1, nseg=1, words=None, q_dtype=lkv.BF16, ws=1 << 30, sm=0.088, tau=1e-3, mask=p, out=p):
+        v = (lkv._View * 2)(_view(max_len=1000), _view(max_len=300))
+        if words is None:
+            words = (1024 + (320 if nseg == 2 else 0)) // 32
+        return L.lkv_decode_attn_debug(cs, v, nseg, p, q_dtype, 8, T, 32, sm, tau, 256, out, mask, words, p, ws,
+                                       None)
+
+    assert call(words=31) == lkv.EINVAL              # 1000 tokens round up to 1024 columns: 32 words
+    assert call(nseg=2, words=32) == lkv.EINVAL      # + 300 rounded up to 320: 42 words
+    assert call(q_dtype=7) == lkv.EINVAL
+    assert call(ws=100) == lkv.EINVAL
+    assert call(sm=float("inf")) == lkv.EINVAL
+    assert call(tau=float("nan")) == lkv.EINVAL
+    assert call(T=0) == lkv.EINVAL
+    assert call(mask=None) == lkv.EINVAL
+    assert call(out=None) == lkv.EINVAL
+
+
 def test_multi_token_plan_counts_query_pairs_at_four_heads_per_kv_head():
     L = lkv.lib()
     out = C.c_int32()

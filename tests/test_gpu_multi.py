@@ -8,7 +8,8 @@ import torch
 
 from oracle import oracle as O
 from quantized_kv_cache_token_amd import inputs, lkv
-from tests.gpu_common import Pair, assert_attention_close, max_abs_vhat, say, sm_scale, to_f32_host
+from tests.gpu_common import (Pair, assert_attention_close, max_abs_vhat, resolved_reference, say, sm_scale,
+                              to_f32_host)
 from tests.oracle_cases import block_tables
 from tests.test_gpu_parity import _prefill
 
@@ -29,9 +30,22 @@ def _multi_case(fmt, G, qdtype, lens, T, tau, split, seed=40, Hkv=2):
     q = _queries(seed + 1, len(lens), T, Hkv * G, D, qdtype)
     view = lkv.View(torch.tensor(bt).cuda(), torch.tensor(lens, dtype=torch.int32).cuda(), max(lens))
     say("multi", fmt, "G", G, qdtype, "T", T, "lens", lens, "tau", tau, "split", split)
-    got = lkv.decode_attn_multi([pair.gpu], [view], q.cuda(), sm_scale(D), tau, split).cpu().numpy()
-    want = O.decode_multi([pair.ref], [bt], [np.array(lens, np.int32)], to_f32_host(q.reshape(-1, Hkv * G, D))
-                          .reshape(q.shape), sm_scale(D), tau, split)
+    got_t = lkv.decode_attn_multi([pair.gpu], [view], q.cuda(), sm_scale(D), tau, split)
+    got = got_t.cpu().numpy()
+    if tau > 0:
+        # the skip decisions too: the oracle takes the GPU's near the bound
+        dbg, mask = lkv.decode_attn_debug([pair.gpu], [view], q.cuda(), sm_scale(D), tau, split)
+        torch.cuda.synchronize()
+        assert torch.equal(dbg, got_t), "the debug entry point must give the production output bit for bit"
+        ebts, elens = O.multi_entries([bt], [np.array(lens, np.int32)], T)
+        sp = split or lkv.decode_plan_multi([pair.gpu], [view], len(lens), T, Hkv * G)
+        want, stats = resolved_reference([pair.ref], ebts, elens, to_f32_host(q.reshape(-1, Hkv * G, D)),
+                                         sm_scale(D), tau, sp, mask, [view.max_len])
+        want = want.reshape(q.shape)
+        say("  skip pairs live / flipped near the bound / largest flipped margin:", *stats)
+    else:
+        want = O.decode_multi([pair.ref], [bt], [np.array(lens, np.int32)],
+                              to_f32_host(q.reshape(-1, Hkv * G, D)).reshape(q.shape), sm_scale(D), tau, split)
     return got, want, max_abs_vhat(pair.ref), (pair, view, q, bt)
 
 

@@ -8,7 +8,8 @@ import torch
 
 from oracle import oracle as O
 from quantized_kv_cache_token_amd import inputs, lkv
-from tests.gpu_common import Pair, assert_attention_close, max_abs_vhat, say, sm_scale, to_f32_host
+from tests.gpu_common import (Pair, assert_attention_close, max_abs_vhat, resolved_reference, say, sm_scale,
+                              to_f32_host)
 from tests.oracle_cases import block_tables
 
 pytestmark = pytest.mark.gpu
@@ -143,10 +144,14 @@ def test_append_unaligned_inputs_bit_exact():
 
 
 def _decode_case(fmt, G, qdtype, lens, tau, split, seed=5, Hkv=2, nseg=1):
-    D, g, kb, vb = fmt
+    """fmt: one format for every segment, or a list with one per segment."""
+    fmts = list(fmt) if isinstance(fmt, list) else [fmt] * nseg
+    nseg = len(fmts)
+    D = fmts[0][0]
     rng = np.random.default_rng(seed)
     pairs, views, ref_views = [], [], []
     for s in range(nseg):
+        _, g, kb, vb = fmts[s]
         seg_lens = [max(0, n - 37 * s) for n in lens]
         bt, nblk = block_tables([max(n, 1) for n in seg_lens], rng)
         pair = Pair(D, g, kb, vb, Hkv, nblk)
@@ -160,8 +165,20 @@ def _decode_case(fmt, G, qdtype, lens, tau, split, seed=5, Hkv=2, nseg=1):
     say("decode", fmt, "G", G, qdtype, "lens", lens, "tau", tau, "split", split, "nseg", nseg)
     out = lkv.decode_attn([p.gpu for p in pairs], views, q.cuda(), sm, tau, split)
     torch.cuda.synchronize()
-    want = O.decode([p.ref for p in pairs], [v[0] for v in ref_views], [v[1] for v in ref_views],
-                    to_f32_host(q), sm, tau, split)
+    if tau > 0:
+        # the skip decisions too: the oracle takes the GPU's near the bound
+        dbg, mask = lkv.decode_attn_debug([p.gpu for p in pairs], views, q.cuda(), sm, tau, split)
+        torch.cuda.synchronize()
+        assert torch.equal(dbg, out), "the debug entry point must give the production output bit for bit"
+        want, stats = resolved_reference([p.ref for p in pairs], [v[0] for v in ref_views],
+                                         [v[1] for v in ref_views], to_f32_host(q), sm, tau,
+                                         split or lkv.decode_plan([p.gpu for p in pairs], views, len(lens),
+                                                                  Hkv * G),
+                                         mask, [v.max_len for v in views])
+        say("  skip pairs live / flipped near the bound / largest flipped margin:", *stats)
+    else:
+        want = O.decode([p.ref for p in pairs], [v[0] for v in ref_views], [v[1] for v in ref_views],
+                        to_f32_host(q), sm, tau, split)
     vmax = max(max_abs_vhat(p.ref) for p in pairs)
     return out.cpu().numpy(), want, vmax
 
@@ -179,6 +196,51 @@ def test_decode_parity_formats(fmt, G):
 def test_decode_parity_splits_and_skip(qdtype, split, tau):
     got, want, vmax = _decode_case((128, 64, 6, 4), 4, qdtype, [5, 700, 1500, 2048], tau, split)
     assert_attention_close(got, want, vmax, f"split {split} tau {tau}")
+
+
+SKIP_KERNELS = [  # (formats, G, q dtype): every split kernel that applies the skip
+    ((128, 64, 6, 4), 4, "bf16"),                        # matrix cores, two-set layout
+    ((128, 64, 6, 4), 8, "bf16"),                        # matrix cores, 8-head layout
+    ((128, 64, 6, 6), 4, "bf16"),
+    ([(128, 64, 6, 6), (128, 64, 6, 4)], 4, "bf16"),     # tiered {HIGH, MID} in one launch
+    ([(128, 64, 6, 6), (128, 64, 6, 4)], 8, "bf16"),
+    ((128, 64, 16, 16), 8, "bf16"),                      # fp16 layer
+    ((128, 64, 16, 16), 4, "f32"),
+    ((64, 32, 6, 4), 2, "bf16"),                         # generic kernel
+    ((128, 64, 6, 4), 4, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", SKIP_KERNELS, ids=lambda c: f"{c[0]}G{c[1]}{c[2]}".replace(" ", ""))
+@pytest.mark.parametrize("tau", [1e-3, 5e-3, 3e-2])
+def test_skip_decisions_bit_exact_outside_the_band(case, tau):
+    """The skip mask of the debug entry point: every decision outside the
+    band fp32 can take either way equals the exact one; with the GPU's
+    decisions inside it, the oracle's output matches within tolerance."""
+    fmts, G, qd = case
+    got, want, vmax = _decode_case(fmts, G, qd, [5, 300, 1500, 2048], tau, 256)
+    assert_attention_close(got, want, vmax, f"{case} tau {tau}")
+
+
+def test_debug_mask_is_empty_without_a_threshold_and_clears_stale_bits():
+    """tau_low = 0 skips nothing: the mask comes back all zero (the call
+    clears it first), and the output is the production call's."""
+    D, g, Hkv, G = 128, 64, 2, 4
+    lens = [70, 1000]
+    rng = np.random.default_rng(8)
+    bt, nblk = block_tables(lens, rng)
+    pair = Pair(D, g, 6, 4, Hkv, nblk)
+    _prefill(pair, lens, Hkv, D, "bf16", 8, bt)
+    q = inputs.queries(8, len(lens), Hkv * G, D).cuda()
+    view = lkv.View(torch.tensor(bt).cuda(), torch.tensor(lens, dtype=torch.int32).cuda(), max(lens))
+    say("debug mask at tau 0")
+    _, m1 = lkv.decode_attn_debug([pair.gpu], [view], q, sm_scale(D), 0.05, 128)
+    out0, m0 = lkv.decode_attn_debug([pair.gpu], [view], q, sm_scale(D), 0.0, 128)
+    ref = lkv.decode_attn([pair.gpu], [view], q, sm_scale(D), 0.0, 128)
+    torch.cuda.synchronize()
+    assert int((m1 != 0).sum()) > 0          # at 0.05 most tokens are skipped
+    assert int((m0 != 0).sum()) == 0
+    assert torch.equal(out0, ref)
 
 
 @pytest.mark.parametrize("G", [4, 8])
