@@ -74,7 +74,9 @@ typedef enum {
     LKV_OK = 0,
     LKV_EINVAL = -1,       /* null pointer, bad size or inconsistent arguments */
     LKV_EUNSUPPORTED = -2, /* a format or shape the library has no kernel for */
-    LKV_EHIP = -3          /* the HIP runtime refused a launch */
+    LKV_EHIP = -3,         /* the HIP runtime refused a launch */
+    LKV_ESCRATCH = -4      /* lkv_decode_attn_noalloc: the call's partials exceed
+                              LKV_NOALLOC_SCRATCH_BYTES */
 } lkv_status;
 
 typedef enum { LKV_F32 = 0, LKV_BF16 = 1, LKV_F16 = 2 } lkv_dtype;
@@ -173,6 +175,22 @@ int lkv_decode_attn(const lkv_cache* segs, const lkv_view* views, int32_t nseg,
                     const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
                     float sm_scale, float tau_low, int32_t split_tokens,
                     float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* lkv_decode_attn for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It takes no workspace and allocates nothing: the split
+ * partials go to a static device array of LKV_NOALLOC_SCRATCH_BYTES that
+ * the library holds on every GPU it runs on until the process ends.  Same
+ * arguments, kernels, split plan and output as lkv_decode_attn.
+ * The array is shared by every call on one GPU and keeps the last call's
+ * contents (the partials need no initialisation): calls that overlap on one
+ * GPU -- on different streams, or from several threads -- race, so the
+ * caller orders them.  Returns LKV_ESCRATCH when the call's partials,
+ * lkv_decode_workspace_bytes(), exceed LKV_NOALLOC_SCRATCH_BYTES. */
+#define LKV_NOALLOC_SCRATCH_BYTES (16u << 20)
+int lkv_decode_attn_noalloc(const lkv_cache* segs, const lkv_view* views, int32_t nseg, const void* q,
+                            int32_t q_dtype, int32_t batch, int32_t num_q_heads, float sm_scale, float tau_low,
+                            int32_t split_tokens, float* out, void* stream);
 
 /* Split size for lkv_decode_attn_multi (host): lkv_decode_plan over the
  * work items the call launches, batch * T query tokens, or batch * ceil(T/2)

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "lkv_internal.h"
 
@@ -132,6 +133,7 @@ const char* lkv_status_string(int status)
     case LKV_EINVAL: return "invalid argument";
     case LKV_EUNSUPPORTED: return "unsupported format or shape";
     case LKV_EHIP: return "HIP launch failed";
+    case LKV_ESCRATCH: return "the call needs more than the library's static decode scratch";
     default: return "unknown status";
     }
 }
@@ -564,6 +566,62 @@ int lkv_retier(const lkv_cache* h, const lkv_view* h_view, const float* h_scores
     const hipError_t e = launch_tiering(s, 2, tau_low, tau_high, dh, dm, n_high, n_mid, batch, workspace,
                                         (hipStream_t)stream);
     return e == hipSuccess ? LKV_OK : LKV_EHIP;
+}
+
+}  // extern "C"
+
+// ---- decode without a caller-provided workspace
+//
+// The split partials of lkv_decode_attn_noalloc live in this file-scope
+// device array.  Every GPU the library runs on holds its own copy, at its
+// own address, until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device memory: kernels receive the address
+// that hipGetSymbolAddress returns for the current device.
+
+namespace {
+
+static __device__ __align__(256) uint8_t scratch[LKV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[MAX_DEVICES] = {};
+
+// Address of the current device's scratch, looked up once per device.
+int scratch_of_current_device(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return LKV_EHIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LKV_EHIP;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return LKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lkv_decode_attn_noalloc(const lkv_cache* segs, const lkv_view* views, int32_t nseg, const void* q,
+                            int32_t q_dtype, int32_t batch, int32_t num_q_heads, float sm_scale, float tau_low,
+                            int32_t split_tokens, float* out, void* stream)
+{
+    if (split_tokens == 0) {
+        const int st = lkv_decode_plan(segs, views, nseg, batch, num_q_heads, &split_tokens);
+        if (st != LKV_OK) return st;
+    }
+    const int64_t need = lkv_decode_workspace_bytes(segs, views, nseg, batch, num_q_heads, split_tokens);
+    if (need < 0) return (int)need;
+    if (need > (int64_t)LKV_NOALLOC_SCRATCH_BYTES) return LKV_ESCRATCH;
+    if (batch == 0) return LKV_OK;
+    void* ws = nullptr;
+    const int st = scratch_of_current_device(&ws);
+    if (st != LKV_OK) return st;
+    return lkv_decode_attn(segs, views, nseg, q, q_dtype, batch, num_q_heads, sm_scale, tau_low, split_tokens, out,
+                           ws, (size_t)LKV_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

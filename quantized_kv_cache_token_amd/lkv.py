@@ -18,7 +18,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblkv.so")
 BLOCK_TOKENS = 64
 
-OK, EINVAL, EUNSUPPORTED, EHIP = 0, -1, -2, -3
+OK, EINVAL, EUNSUPPORTED, EHIP, ESCRATCH = 0, -1, -2, -3, -4
+NOALLOC_SCRATCH_BYTES = 16 << 20  # LKV_NOALLOC_SCRATCH_BYTES
 F32, BF16, F16 = 0, 1, 2
 _DTYPE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
 
@@ -47,7 +48,7 @@ EXPORTS = ["lkv_status_string", "lkv_chunk_layout", "lkv_quant_append", "lkv_dec
            "lkv_decode_scores_workspace_bytes", "lkv_decode_attn_scores",
            "lkv_default_thresholds", "lkv_tier_workspace_bytes", "lkv_tier_update",
            "lkv_retier_workspace_bytes", "lkv_retier", "lkv_decode_attn_multi", "lkv_decode_plan_multi",
-           "lkv_decode_attn_debug"]
+           "lkv_decode_attn_debug", "lkv_decode_attn_noalloc"]
 
 
 def lib():
@@ -79,6 +80,7 @@ def lib():
         "lkv_retier_workspace_bytes": ([I32, I32, I32], I64),
         "lkv_decode_attn_multi": ([PC, PV, I32, P, I32, I32, I32, I32, F, F, I32, P, P, C.c_size_t, V], C.c_int),
         "lkv_decode_plan_multi": ([PC, PV, I32, I32, I32, I32, C.POINTER(I32)], C.c_int),
+        "lkv_decode_attn_noalloc": ([PC, PV, I32, P, I32, I32, I32, F, F, I32, P, V], C.c_int),
         "lkv_decode_attn_debug": ([PC, PV, I32, P, I32, I32, I32, I32, F, F, I32, P, P, I32, P, C.c_size_t, V],
                                   C.c_int),
         "lkv_retier": ([PC, PV, P, I32, PC, PV, P, I32, F, F, PC, P, I32, PC, P, I32, P, P, P, P, I32, P,
@@ -236,6 +238,22 @@ def decode_attn(caches, views, q: torch.Tensor, sm_scale: float, tau_low: float 
     _check("lkv_decode_attn", lib().lkv_decode_attn(
         cs, vs, n, _ptr(q), _DTYPE[q.dtype], B, Hq, sm_scale, tau_low, split_tokens, _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def decode_attn_noalloc(caches, views, q: torch.Tensor, sm_scale: float, tau_low: float = 0.0,
+                        split_tokens: int = 0, out: torch.Tensor | None = None, stream=None):
+    """lkv_decode_attn_noalloc: decode_attn with the split partials in the
+    library's static device scratch (no workspace).  With `out` given, the
+    call allocates nothing at all."""
+    B, Hq, D = q.shape
+    _require(q.is_contiguous(), "q must be contiguous")
+    if out is None:
+        with _on(stream):
+            out = torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
+    cs, vs, n = _segs(caches, views)
+    _check("lkv_decode_attn_noalloc", lib().lkv_decode_attn_noalloc(
+        cs, vs, n, _ptr(q), _DTYPE[q.dtype], B, Hq, sm_scale, tau_low, split_tokens, _ptr(out), _stream(stream)))
     return out
 
 
