@@ -3,11 +3,14 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2|3|4|5]
 
 A step is one pass of the hot path for one layer: quantise-and-append the
-new token of every sequence (lkv_quant_append), then split-K decode
-attention of one query per sequence over the whole packed cache
-(lkv_decode_split + lkv_decode_combine, i.e. lkv_decode_attn).  Steps rotate
-over several layer caches so that consecutive steps stream from HBM, not
-from the 256 MB last-level cache.
+new token of every sequence, then split-K decode attention of one query per
+sequence over the whole packed cache, then the merge of the split partials.
+With one segment (workloads 2, 4, 5) that is lkv_append_decode: the split
+kernel writes each sequence's new row itself (lkv_append_split), then
+lkv_decode_combine -- two launches.  The tiered workload 3 (two segments),
+and every workload with --unfused, runs lkv_quant_append, lkv_decode_split
+and lkv_decode_combine.  Steps rotate over several layer caches so that
+consecutive steps stream from HBM, not from the 256 MB last-level cache.
 
   workload 2 (default) and 4: every step re-appends the row of the last
     position and attends over all N positions, the same work as the step
@@ -60,33 +63,42 @@ def parse():
     p.add_argument("--no-tier", action="store_true", help="skip the tier-update and re-tiering secondary figures")
     p.add_argument("--no-secondary", action="store_true",
                    help="skip every secondary figure but the prefill append (counter passes: only the step's kernels run)")
+    p.add_argument("--graph", action="store_true",
+                   help="replay each step as a captured HIP graph instead of launching its kernels from the host")
+    p.add_argument("--unfused", action="store_true",
+                   help="three launches per step: the append kernel, the split kernel, the merge")
     return p.parse_args()
 
 
-def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed counter summary, if it was
-    taken on the current kernel source; else None."""
+def measured_traffic(kernel: str, workload: str, fused: bool):
+    """HBM bytes of the split kernel and the merge per step, from the
+    committed counter summary, if it was taken on the current kernel sources
+    with the same step; else None."""
     path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     from quantized_kv_cache_token_amd.profsum import kernel_source_hash
 
-    if rec.get("source_hash") != kernel_source_hash():
+    if rec.get("source_hash") != kernel_source_hash() or bool(rec.get("fused")) != fused:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get("hbm_bytes_per_step")
 
 
 class Setup:
-    """What the timing loop needs from a workload: the prepared calls of each
-    step (append, split, combine), the counted bytes of step i, the split
+    """What the timing loop needs from a workload: the prepared stages of
+    each step ((append, split, combine), or (append + split, combine) when
+    the split kernel appends), the counted bytes of step i, the split
     kernel's algorithmic bytes, and the JSON config."""
 
     def __init__(self):
-        self.calls = []          # (append, split, combine) per rotation slot
+        self.calls = []          # stages per rotation slot
+        self.fused = False       # the split stage also appends the new rows
         self.keep = []           # tensors the prepared calls point at
         self.step_bytes = None   # i -> counted bytes of step i
-        self.split_alg = None    # i -> algorithmic bytes of the split launch of step i
+        self.split_alg = None    # i -> algorithmic bytes of the split launch of step i (KV + Q)
+        self.append_bytes = 0    # counted bytes of a step's append (rows in, packed rows out)
+        self.out_bytes = 0       # bytes of O the merge writes
         self.sequences = 0
         self.config = {}
         self.secondary = {}
@@ -140,13 +152,17 @@ def setup_uniform(args, wl, dev) -> Setup:
     split = args.split_tokens or lkv.decode_plan([caches[0]], [view], B, Hq)
     ws = lkv.decode_workspace([caches[0]], [view], B, Hq, split, dev)
     out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
+    S.fused = not args.unfused
     for layer in range(args.layers):
         k, v = inputs.kv_rows(wl.seed, 1000, B, Hkv, D, dtype=wl.dtype, outliers=outl, layer=layer, step=1,
                               device=dev)
         q = inputs.queries(wl.seed, B, Hq, D, dtype=wl.dtype, layer=layer, device=dev)
-        app = lkv.prepare_append(caches[layer], k, v, cu1, last, bt, 1)
-        spl, comb = lkv.prepare_decode([caches[layer]], [view], q, sm, 0.0, split, out, ws)
-        S.calls.append((app, spl, comb))
+        if S.fused:  # the new row of each sequence is position N - 1: lengths are N
+            S.calls.append(lkv.prepare_append_decode(caches[layer], view, k, v, q, sm, 0.0, split, out, ws))
+        else:
+            app = lkv.prepare_append(caches[layer], k, v, cu1, last, bt, 1)
+            spl, comb = lkv.prepare_decode([caches[layer]], [view], q, sm, 0.0, split, out, ws)
+            S.calls.append((app, spl, comb))
         S.keep += [k, v, q]
     S.keep += [caches, bt, lens, view, cu1, last, ws, out]
     ptk = caches[0].chunk_bytes // 64
@@ -159,11 +175,12 @@ def setup_uniform(args, wl, dev) -> Setup:
     S.per_token_head, S.q_bytes = ptk, qb
     S.step_bytes = lambda i: kv + B * Hq * D * (qb + 4) + B * Hkv * (2 * D * qb + ptk)
     S.split_alg = lambda i: kv + B * Hq * D * qb
+    S.append_bytes, S.out_bytes = B * Hkv * (2 * D * qb + ptk), B * Hq * D * 4
     S.sequences = B
     S.config = {"workload": wl.name if not args.fp16_layer else wl.name.replace("k6v4", "fp16"), "batch": B,
                 "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "ctx_tokens": N,
                 "group_size": wl.group_size, "k_bits": kb, "v_bits": vb, "q_dtype": wl.dtype,
-                "split_tokens": split, "layers_rotated": args.layers}
+                "split_tokens": split, "layers_rotated": args.layers, "append_in_split_kernel": S.fused}
     pre_bytes = (N - 1) * Hkv * (2 * D * qb + ptk)
     pre_s = float(np.median(prefill_ms)) / 1e3
     S.secondary["append_prefill"] = {"GB/s": round(pre_bytes / pre_s / 1e9, 1),
@@ -359,11 +376,12 @@ def setup_tiered(args, wl, dev) -> Setup:
     S.per_token_head, S.q_bytes = 212, qb
     S.step_bytes = lambda i: kv + B * Hq * D * (qb + 4) + B * Hkv * (2 * D * qb + 212)
     S.split_alg = lambda i: kv + B * Hq * D * qb
+    S.append_bytes, S.out_bytes = B * Hkv * (2 * D * qb + 212), B * Hq * D * 4
     S.sequences = B
     S.config = {"workload": wl.name, "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
                 "ctx_tokens": N, "high_tokens": int(nh_h[0]), "mid_tokens": int(nm_h[0]),
                 "group_size": wl.group_size, "segments": "K6V6 + K6V4", "tau_low": tl, "q_dtype": wl.dtype,
-                "split_tokens": split, "layers_rotated": args.layers}
+                "split_tokens": split, "layers_rotated": args.layers, "append_in_split_kernel": False}
     return S
 
 
@@ -423,12 +441,17 @@ def setup_ragged(args, wl, dev) -> Setup:
     qs = [inputs.queries(wl.seed, B, Hq, D, dtype=wl.dtype, layer=layer, device=dev) for layer in range(args.layers)]
     views = [lkv.View(bt, after[s], max_len, live[s]) for s in range(n_steps)]
     # rotation slot i = s * layers + layer: decode step s of that layer
+    S.fused = not args.unfused
     for s in range(n_steps):
         for layer in range(args.layers):
             k, v = kvs[layer]
-            app = lkv.prepare_append(caches[layer], k, v, cu1, pos[s], bt, 1)
-            spl, comb = lkv.prepare_decode([caches[layer]], [views[s]], qs[layer], sm, 0.0, split, out, ws)
-            S.calls.append((app, spl, comb))
+            if S.fused:  # the new row of sequence b is position len_b + s: the step's lengths count it
+                S.calls.append(lkv.prepare_append_decode(caches[layer], views[s], k, v, qs[layer], sm, 0.0, split,
+                                                         out, ws))
+            else:
+                app = lkv.prepare_append(caches[layer], k, v, cu1, pos[s], bt, 1)
+                spl, comb = lkv.prepare_decode([caches[layer]], [views[s]], qs[layer], sm, 0.0, split, out, ws)
+                S.calls.append((app, spl, comb))
     S.keep += [caches, bt, pos, after, views, ws, out, cu1, kvs, qs]
     qb = 2 if wl.dtype == "bf16" else 4
     L = args.layers
@@ -436,12 +459,14 @@ def setup_ragged(args, wl, dev) -> Setup:
     S.step_bytes = lambda i: live[(i // L) % n_steps] * Hkv * 180 + B * Hq * D * (qb + 4) + B * Hkv * (
         2 * D * qb + 180)
     S.split_alg = lambda i: live[(i // L) % n_steps] * Hkv * 180 + B * Hq * D * qb
+    S.append_bytes, S.out_bytes = B * Hkv * (2 * D * qb + 180), B * Hq * D * 4
     S.sequences = B
     S.config = {"workload": wl.name, "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
                 "ctx_tokens_min": int(lens.min()), "ctx_tokens_max": int(cap.max()),
                 "ctx_tokens_mean": round(float(lens.mean()), 1), "decode_steps": n_steps,
                 "group_size": wl.group_size, "k_bits": wl.k_bits, "v_bits": wl.v_bits, "q_dtype": wl.dtype,
-                "split_tokens": split, "layers_rotated": L, "paged": "seeded permutation of pool blocks"}
+                "split_tokens": split, "layers_rotated": L, "paged": "seeded permutation of pool blocks",
+                "append_in_split_kernel": S.fused}
     return S
 
 
@@ -460,41 +485,76 @@ def main():
     wl = workloads.BY_INDEX[args.workload]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    if args.workload == 3:
-        S = setup_tiered(args, wl, dev)
-    elif args.workload == 5:
-        S = setup_ragged(args, wl, dev)
-        args.steps = min(args.steps, len(S.calls))
-    else:
-        S = setup_uniform(args, wl, dev)
+    # one stream (default priority) for every prepared call and graph
+    run_stream = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(run_stream):
+        if args.workload == 3:
+            S = setup_tiered(args, wl, dev)
+        elif args.workload == 5:
+            S = setup_ragged(args, wl, dev)
+            args.steps = min(args.steps, len(S.calls))
+        else:
+            S = setup_uniform(args, wl, dev)
+    torch.cuda.synchronize()
     n_calls = len(S.calls)
 
     def step(i, ev=None):
-        app, spl, comb = S.calls[i % n_calls]
-        app()
+        stages = S.calls[i % n_calls]
         if ev is not None:
-            ev[0].record()
-        spl()
-        if ev is not None:
-            ev[1].record()
-        comb()
+            ev[0].record(run_stream)
+        for j, fn in enumerate(stages):
+            fn()
+            if ev is not None:
+                ev[j + 1].record(run_stream)
 
     # warmup, then the timed steps; workload 5 times its decode steps from
     # the first (its warmup replays the first slots, appending the same rows)
     first = 0 if args.workload == 5 else args.warmup
-    for i in range(args.warmup):
-        step(i)
+    with torch.cuda.stream(run_stream):
+        for i in range(args.warmup):
+            step(i)
     torch.cuda.synchronize()
-    # HIP events bracket the split kernel on one step of every rotation
-    # cycle (an event between kernels adds a small gap to that step only)
-    timed = [i for i in range(args.steps) if i % args.layers == 0]
-    evs = {i: (_event(), _event()) for i in timed}
+    n_stages = len(S.calls[0])
+    # the step of each rotation slot as a HIP graph (its launches replayed
+    # without host work in between, as a serving loop runs a decode step)
+    graphs = None
+    if args.graph:
+        graphs = []
+        for i in range(n_calls):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=run_stream):
+                step(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(run_stream):
+            for i in range(args.warmup):
+                graphs[i % n_calls].replay()
+        torch.cuda.synchronize()
+    # timed region: K steps between synchronisations; HIP events on the
+    # run stream bracket all of them (the steps' GPU time)
+    g0, g1 = _event(), _event()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(first + i, evs.get(i))
+    with torch.cuda.stream(run_stream):
+        g0.record(run_stream)
+        for i in range(args.steps):
+            if graphs is not None:
+                graphs[(first + i) % n_calls].replay()
+            else:
+                step(first + i)
+        g1.record(run_stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    gpu_step_s = g0.elapsed_time(g1) / 1e3 / args.steps
+    # then, outside the timed region, HIP events before and after each stage
+    # of one step in every rotation cycle, replaying the same steps launch by
+    # launch: the split kernel's and the merge's own durations
+    timed = [i for i in range(args.steps) if i % args.layers == 0]
+    evs = {i: tuple(_event() for _ in range(n_stages + 1)) for i in timed}
+    with torch.cuda.stream(run_stream):
+        for i in timed:
+            step(first + i, evs[i])
+    torch.cuda.synchronize()
     if args.copy_probe:
         # a plain streaming kernel of known traffic: reads 1 GiB, writes 1 GiB
         src = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
@@ -507,12 +567,30 @@ def main():
     step_s = (t1 - t0) / args.steps
     total_bytes = sum(S.step_bytes(first + i) for i in range(args.steps))
     value = total_bytes / (t1 - t0) / 1e9
-    split_ms = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in timed])
+    # stage times: the split stage (K2; with the fused append it also writes
+    # the new rows) and the merge (K3), from the events around them
+    si = n_stages - 2  # the split stage is the one before the merge
+    split_ms = np.array([evs[i][si].elapsed_time(evs[i][si + 1]) for i in timed])
+    comb_ms = np.array([evs[i][si + 1].elapsed_time(evs[i][si + 2]) for i in timed])
     split_alg = np.array([S.split_alg(first + i) for i in timed], dtype=np.float64)
+    if S.fused:
+        split_alg = split_alg + S.append_bytes
+    k23_alg = split_alg + S.out_bytes
     split_s = float(split_ms.mean()) / 1e3
-    achieved = float(split_alg.sum() / (split_ms.sum() / 1e3)) / 1e9
-    kname = "decode_split"
-    traffic = measured_traffic(kname, S.config["workload"])
+    split_achieved = float(split_alg.sum() / (split_ms.sum() / 1e3)) / 1e9
+    if S.fused:
+        # a step is the split kernel and the merge: its GPU time over the
+        # timed region is K2 + K3 (with the gap between them)
+        k23_alg = np.array([S.split_alg(first + i) + S.append_bytes + S.out_bytes for i in range(args.steps)],
+                           dtype=np.float64)
+        k23_s = gpu_step_s
+        k23_src = "hip events around the timed steps (a step is the split kernel and the merge)"
+    else:
+        k23_s = float((split_ms + comb_ms).mean()) / 1e3
+        k23_src = "hip events around each kernel, one step in every rotation cycle"
+    achieved = float(k23_alg.mean() / k23_s) / 1e9
+    kname = "append_split+combine" if S.fused else "decode_split+combine"
+    traffic = measured_traffic("decode_step", S.config["workload"], S.fused)
 
     rec = {
         "metric": METRIC,
@@ -522,10 +600,13 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(step_s * 1e3, 4),
+        "gpu_ms_per_step": round(gpu_step_s * 1e3, 4),
+        "graph_replay": graphs is not None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": ("f16x2-mfma/f32-acc" if S.config.get("k_bits") == 16 else "bf16x2-mfma/f32-acc")
+        if S.config.get("q_dtype") == "bf16" else "f32",
         "data": "synthetic",
         "config": S.config,
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
@@ -533,8 +614,14 @@ def main():
         "bytes_per_step": int(round(total_bytes / args.steps)),
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "alg_bytes_per_launch": int(round(split_alg.mean())),
-                     "avg_launch_us": round(split_s * 1e6, 2)},
+                     "traffic": traffic, "alg_bytes_per_launch": int(round(k23_alg.mean())),
+                     "avg_launch_us": round(k23_s * 1e6, 2), "timing": k23_src,
+                     "split_only": {"kernel": "append_split" if S.fused else "decode_split",
+                                    "achieved": round(split_achieved, 2),
+                                    "frac": round(split_achieved / HBM_PEAK_GBS, 4),
+                                    "alg_bytes_per_launch": int(round(split_alg.mean())),
+                                    "avg_launch_us": round(split_s * 1e6, 2)},
+                     "combine_us": round(float(comb_ms.mean()) * 1e3, 2)},
     }
     secondary = dict(S.secondary)
     ptk, qb = S.per_token_head, S.q_bytes
@@ -655,8 +742,14 @@ def cpu_baseline(wl, kb, vb, nseq, per_token_head, q_bytes, min_seconds):
         if dt >= min_seconds:
             break
     nbytes = B * Hkv * N * per_token_head + B * Hq * D * (q_bytes + 4) + B * Hkv * (2 * D * q_bytes + per_token_head)
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": round(steps * nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": O.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
             "sample": f"{B} of {wl.batch} sequences, all {Hq} query heads; {steps} steps of (append 1 row per "
                       f"sequence + fp64 decode over {N} tokens) in {dt:.2f} s"}
 

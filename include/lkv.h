@@ -176,6 +176,40 @@ int lkv_decode_attn(const lkv_cache* segs, const lkv_view* views, int32_t nseg,
                     float sm_scale, float tau_low, int32_t split_tokens,
                     float* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* One decode step of a layer in one call: lkv_quant_append of each
+ * sequence's new K and V row, then lkv_decode_attn over the cache that
+ * holds it (the pages' two operations in sequence: quantise and pack the new
+ * token, TurboQuant page core innovation and Super KV Compression page first
+ * layer; then attention over the packed cache, which includes the token
+ * appended in the same step).  One segment.
+ * view.seq_lens[b] already counts the new token: its row goes to position
+ * seq_lens[b] - 1 (through view.block_table, which must map that block) and
+ * attention reads seq_lens[b] tokens.  A sequence of length 0 appends
+ * nothing and gives a zero row.
+ * k_new, v_new  [batch][num_kv_heads][head_dim] in kv_dtype (LKV_F32, BF16
+ *               or F16); with k_norm, aligned as lkv_quant_append requires
+ * Other arguments, the workspace and out as lkv_decode_attn (split_tokens
+ * 0 = lkv_decode_plan()).  The pool and out are exactly those of
+ * lkv_quant_append (cu_new = 0, 1, .., batch; start_pos = seq_lens - 1)
+ * followed by lkv_decode_attn.  For bf16 Q, head_dim 128, group 64, K6
+ * with V4 or V6, 4 or 8 query heads per KV head and new rows aligned to two
+ * channels, the split kernel writes the rows itself (the wave whose split
+ * holds a sequence's newest token), so the step is two launches; other
+ * formats run the append kernel first. */
+int lkv_append_decode(const lkv_cache* cache, const lkv_view* view, const void* k_new, const void* v_new,
+                      int32_t kv_dtype, const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+                      float sm_scale, float tau_low, int32_t split_tokens, float* out, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* The first stage of lkv_append_decode, for callers that schedule the two
+ * apart (lkv_append_decode is exactly lkv_append_split followed by
+ * lkv_decode_combine on the same stream): the new rows and the split
+ * partials.  split_tokens must be the resolved (non-zero) split size. */
+int lkv_append_split(const lkv_cache* cache, const lkv_view* view, const void* k_new, const void* v_new,
+                     int32_t kv_dtype, const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+                     float sm_scale, float tau_low, int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
 /* lkv_decode_attn for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  It takes no workspace and allocates nothing: the split

@@ -108,6 +108,11 @@ static int check_split(const lkv_cache* segs, const lkv_view* views, int32_t nse
     return LKV_OK;
 }
 
+// The kernels' view of the segments; returns the total split count.
+static int32_t seg_args(const lkv_cache* segs, const lkv_view* views, int32_t nseg, const Fmt* f,
+                        int32_t split_tokens, float* scores, int32_t score_stride, int32_t q_per_seq,
+                        uint32_t* skip_mask, int32_t mask_stride, SegArgs* a);
+
 // Split stage; scores (optional) receives the base-2 score rows.  batch
 // counts grid entries: sequences times q_per_seq query tokens.
 static int split_impl(const lkv_cache* segs, const lkv_view* views, int32_t nseg, const void* q, int32_t q_dtype,
@@ -242,8 +247,25 @@ static int split_impl(const lkv_cache* segs, const lkv_view* views, int32_t nseg
     const int st = check_split(segs, views, nseg, q, q_dtype, batch, num_q_heads, sm_scale, tau_low, split_tokens,
                                workspace, workspace_bytes, f);
     if (st != LKV_OK || batch == 0) return st;
-    const int32_t tot = (int32_t)total_splits(views, nseg, split_tokens);
     SegArgs a[2];
+    const int32_t tot = seg_args(segs, views, nseg, f, split_tokens, scores, score_stride, q_per_seq, skip_mask,
+                                 mask_stride, a);
+    hipError_t e;
+    if (nseg == 2 && launch_decode_split_mfma_tiered(a[0], a[1], q, q_dtype, batch, num_q_heads, sm_scale, tau_low,
+                                                     split_tokens, tot, (float*)workspace, (hipStream_t)stream, &e))
+        return e == hipSuccess ? LKV_OK : LKV_EHIP;
+    for (int s = 0; s < nseg; s++) {
+        e = launch_decode_split(a[s], q, q_dtype, batch, num_q_heads, sm_scale, tau_low, split_tokens, tot,
+                                (float*)workspace, (hipStream_t)stream);
+        if (e != hipSuccess) return LKV_EHIP;
+    }
+    return LKV_OK;
+}
+
+static int32_t seg_args(const lkv_cache* segs, const lkv_view* views, int32_t nseg, const Fmt* f,
+                        int32_t split_tokens, float* scores, int32_t score_stride, int32_t q_per_seq,
+                        uint32_t* skip_mask, int32_t mask_stride, SegArgs* a)
+{
     int32_t base = 0;
     for (int s = 0; s < nseg; s++) {
         a[s].f = f[s];
@@ -263,16 +285,7 @@ static int split_impl(const lkv_cache* segs, const lkv_view* views, int32_t nseg
         a[s].skip_mask = skip_mask;
         a[s].mask_stride = mask_stride;
     }
-    hipError_t e;
-    if (nseg == 2 && launch_decode_split_mfma_tiered(a[0], a[1], q, q_dtype, batch, num_q_heads, sm_scale, tau_low,
-                                                     split_tokens, tot, (float*)workspace, (hipStream_t)stream, &e))
-        return e == hipSuccess ? LKV_OK : LKV_EHIP;
-    for (int s = 0; s < nseg; s++) {
-        e = launch_decode_split(a[s], q, q_dtype, batch, num_q_heads, sm_scale, tau_low, split_tokens, tot,
-                                (float*)workspace, (hipStream_t)stream);
-        if (e != hipSuccess) return LKV_EHIP;
-    }
-    return LKV_OK;
+    return base;
 }
 
 static int combine_impl(const lkv_cache* segs, const lkv_view* views, int32_t nseg, int32_t batch,
@@ -383,6 +396,55 @@ int lkv_decode_attn(const lkv_cache* segs, const lkv_view* views, int32_t nseg, 
                               workspace, workspace_bytes, stream);
     if (st != LKV_OK) return st;
     return lkv_decode_combine(segs, views, nseg, batch, num_q_heads, split_tokens, out, workspace, workspace_bytes,
+                              stream);
+}
+
+int lkv_append_split(const lkv_cache* cache, const lkv_view* view, const void* k_new, const void* v_new,
+                     int32_t kv_dtype, const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+                     float sm_scale, float tau_low, int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                     void* stream)
+{
+    Fmt f[2];
+    int st = check_split(cache, view, 1, q, q_dtype, batch, num_q_heads, sm_scale, tau_low, split_tokens, workspace,
+                         workspace_bytes, f);
+    if (st != LKV_OK) return st;
+    if (kv_dtype != LKV_F32 && kv_dtype != LKV_BF16 && kv_dtype != LKV_F16) return LKV_EINVAL;
+    if (batch == 0) return LKV_OK;
+    if (!k_new || !v_new) return LKV_EINVAL;
+    if (f[0].k_norm) {  // as lkv_quant_append: the norm factors need P-element alignment
+        const uintptr_t need = (uintptr_t)(f[0].D / 64) * (kv_dtype == LKV_F32 ? 4 : 2);
+        if ((uintptr_t)k_new % need != 0 || (uintptr_t)v_new % need != 0) return LKV_EUNSUPPORTED;
+    }
+    SegArgs a[2];
+    const int32_t tot = seg_args(cache, view, 1, f, split_tokens, nullptr, 0, 1, nullptr, 0, a);
+    hipError_t e;
+    if (!launch_append_decode_mfma(a[0], q, q_dtype, batch, num_q_heads, sm_scale, tau_low, split_tokens, tot,
+                                   (float*)workspace, k_new, v_new, kv_dtype, (hipStream_t)stream, &e)) {
+        // no fused kernel for this format: the append kernel (one row per
+        // sequence at its last position), then the split kernel
+        e = launch_append(f[0], (uint8_t*)cache->pool, k_new, v_new, kv_dtype, nullptr, view->seq_lens,
+                          view->block_table, view->max_blocks, batch, 1, (hipStream_t)stream, view->max_len);
+        if (e != hipSuccess) return LKV_EHIP;
+        e = launch_decode_split(a[0], q, q_dtype, batch, num_q_heads, sm_scale, tau_low, split_tokens, tot,
+                                (float*)workspace, (hipStream_t)stream);
+    }
+    return e == hipSuccess ? LKV_OK : LKV_EHIP;
+}
+
+int lkv_append_decode(const lkv_cache* cache, const lkv_view* view, const void* k_new, const void* v_new,
+                      int32_t kv_dtype, const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+                      float sm_scale, float tau_low, int32_t split_tokens, float* out, void* workspace,
+                      size_t workspace_bytes, void* stream)
+{
+    if (split_tokens == 0) {
+        const int st = lkv_decode_plan(cache, view, 1, batch, num_q_heads, &split_tokens);
+        if (st != LKV_OK) return st;
+    }
+    if (batch > 0 && !out) return LKV_EINVAL;
+    const int st = lkv_append_split(cache, view, k_new, v_new, kv_dtype, q, q_dtype, batch, num_q_heads, sm_scale,
+                                    tau_low, split_tokens, workspace, workspace_bytes, stream);
+    if (st != LKV_OK) return st;
+    return lkv_decode_combine(cache, view, 1, batch, num_q_heads, split_tokens, out, workspace, workspace_bytes,
                               stream);
 }
 

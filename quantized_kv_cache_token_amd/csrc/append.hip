@@ -32,7 +32,24 @@ struct AppendArgs {
     const int32_t* block_table;
     int32_t max_blocks;
     int32_t nblk;    // logical blocks a sequence's new rows can touch
+    int32_t len_cap; // cu_new null: start_pos holds lengths, clamped to this
 };
+
+// Input rows [row0, row0 + n) of sequence b go to positions sp, sp + 1, ...
+// Without cu_new, each sequence appends one row (row b) at its last
+// position: start_pos then holds the lengths, which count that row.
+__device__ __forceinline__ void rows_of(const AppendArgs& a, int b, int& row0, int& n, int& sp)
+{
+    if (a.cu_new != nullptr) {
+        row0 = a.cu_new[b];
+        n = a.cu_new[b + 1] - row0;
+        sp = a.start_pos[b];
+    } else {
+        row0 = b;
+        sp = min(a.start_pos[b], a.len_cap) - 1;
+        n = sp >= 0 ? 1 : 0;
+    }
+}
 
 // Raw bits of input element i (fp32, or a 16-bit pattern), and their value.
 template <int DT>
@@ -61,11 +78,9 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
     const int b = blockIdx.x / a.nblk;
     const int i = blockIdx.x % a.nblk;
     const int kvh = blockIdx.y;
-    // the three index loads are independent: issue them together
-    const int row0 = a.cu_new[b];
-    const int row1 = a.cu_new[b + 1];
-    const int sp = a.start_pos[b];
-    const int n = row1 - row0;
+    // the index loads are independent: issued together
+    int row0, n, sp;
+    rows_of(a, b, row0, n, sp);
     const int lb = sp / BT + i;
     const int p0 = max(sp, lb * BT);
     const int p1 = min(sp + n, lb * BT + BT);
@@ -310,10 +325,8 @@ __global__ __launch_bounds__(256) void append_quant_kernel(AppendArgs a)
     const int b = blockIdx.x / a.nblk;
     const int i = blockIdx.x % a.nblk;
     const int kvh = blockIdx.y;
-    const int row0 = a.cu_new[b];
-    const int row1 = a.cu_new[b + 1];
-    const int sp = a.start_pos[b];
-    const int n = row1 - row0;
+    int row0, n, sp;
+    rows_of(a, b, row0, n, sp);
     const int lb = sp / BT + i;
     const int p0 = max(sp, lb * BT);
     const int p1 = min(sp + n, lb * BT + BT);
@@ -378,7 +391,7 @@ static void launch_d(const AppendArgs& a, int dtype, dim3 grid, hipStream_t stre
 
 hipError_t launch_append(const Fmt& f, uint8_t* pool, const void* k, const void* v, int dtype,
                          const int32_t* cu_new, const int32_t* start_pos, const int32_t* block_table,
-                         int32_t max_blocks, int32_t batch, int32_t max_new, hipStream_t stream)
+                         int32_t max_blocks, int32_t batch, int32_t max_new, hipStream_t stream, int32_t len_cap)
 {
     if (batch == 0 || max_new == 0) return hipSuccess;
     AppendArgs a;
@@ -391,6 +404,7 @@ hipError_t launch_append(const Fmt& f, uint8_t* pool, const void* k, const void*
     a.block_table = block_table;
     a.max_blocks = max_blocks;
     a.nblk = (max_new + BT - 1) / BT + 1;
+    a.len_cap = len_cap;
     dim3 grid((unsigned)batch * (unsigned)a.nblk, (unsigned)f.H);
     if (f.D == 64) launch_d<64>(a, dtype, grid, stream);
     else launch_d<128>(a, dtype, grid, stream);

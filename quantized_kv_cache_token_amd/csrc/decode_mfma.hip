@@ -42,6 +42,7 @@
 #include <type_traits>
 
 #include "lkv_internal.h"
+#include "quant_device.h"
 #include "wave_util.h"
 
 namespace lkv {
@@ -55,6 +56,10 @@ struct MfmaArgs {
     float score_scale;   // sm_scale * log2(e)
     float tau_low;
     float* partials;
+    // the step's new K and V rows [B][Hkv][128] (lkv_append_decode), in kv_dtype
+    const void* k_new;
+    const void* v_new;
+    int32_t kv_dtype;
 };
 
 // The bit manipulations below are plain C, never inline asm: a matrix-core
@@ -798,6 +803,170 @@ __device__ __forceinline__ void block_pv_sets(const BlockRegs<VB>& R, const uint
     }
 }
 
+// ---- the decode step's own append (lkv_append_decode)
+// The wave whose split holds a sequence's newest token (position len - 1,
+// in the split's last block) quantises that token's K and V row with the
+// append kernel's quantiser (the same codes, scales and zero points:
+// group-wise asymmetric quantisation of the TurboQuant page, K6 and 4- or
+// 6-bit V of the Super KV Compression page, first layer).  It writes the row
+// into the pool for later steps and places it in its own registers for the
+// block it reads, whose loads may precede those writes: nothing is read back,
+// and no store is waited for.  Lane l holds channels 2l and 2l + 1 of the
+// row, so a 64-channel group is 32 lanes.
+
+// Channels 2 lane and 2 lane + 1 of row `row` of a [rows][128] input, as fp32.
+__device__ __forceinline__ void load_pair(const void* p, int64_t row, int dt, int lane, float (&x)[2])
+{
+    if (dt == LKV_F32) {
+        const float2 t = ((const float2*)p)[row * 64 + lane];
+        x[0] = t.x;
+        x[1] = t.y;
+    } else {
+        const uint32_t t = ((const uint32_t*)p)[row * 64 + lane];
+        if (dt == LKV_BF16) {
+            x[0] = __uint_as_float(t << 16);
+            x[1] = __uint_as_float(t & 0xFFFF0000u);
+        } else {
+            x[0] = __half2float(__ushort_as_half((uint16_t)(t & 0xFFFFu)));
+            x[1] = __half2float(__ushort_as_half((uint16_t)(t >> 16)));
+        }
+    }
+}
+
+// The quantised new row as the wave holds it.
+struct NewRow {
+    uint32_t kw;         // K row word 3 (lane >> 3) + (lane & 7) (lanes with lane & 7 < 3; 24 words)
+    uint32_t vq;         // V codes of channels 2 lane (bits 0..7) and 2 lane + 1 (bits 8..15)
+    float ks0, ks1, vs0, vs1;  // scales of groups 0 and 1 (uniform)
+    int kz0, kz1, vz0, vz1;    // zero points (uniform)
+};
+
+template <int VB>
+__device__ __forceinline__ void quantize_new_row(const float (&xk)[2], const float (&xv)[2], int lane, NewRow& r)
+{
+    QRow<2> k, v;
+    quantize_fast<2, 64>(xk, 6, k);
+    quantize_fast<2, 64>(xv, VB, v);
+    if (k.slow) quantize_exact<2>(xk, 6, k);
+    if (v.slow) quantize_exact<2>(xv, VB, v);
+    // K: the lane's two codes are 12 bits at bit 12 lane of the 96-byte row;
+    // 8 lanes fill 3 words, held by the first three of them
+    const uint32_t k12 = (uint32_t)k.q[0] | ((uint32_t)k.q[1] << 6);
+    const int m = lane >> 3, j = lane & 7;
+    uint32_t vals[8], w[3];
+#pragma unroll
+    for (int i = 0; i < 8; i++) vals[i] = (uint32_t)__shfl((int)k12, 8 * m + i, 64);
+    pack_values<12, 8, 3>(vals, w);
+    r.kw = j == 0 ? w[0] : (j == 1 ? w[1] : w[2]);
+    r.vq = (uint32_t)v.q[0] | ((uint32_t)v.q[1] << 8);
+    auto from = [](float x, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l)); };
+    r.ks0 = from(k.s, 0);
+    r.ks1 = from(k.s, 32);
+    r.vs0 = from(v.s, 0);
+    r.vs1 = from(v.s, 32);
+    r.kz0 = __builtin_amdgcn_readlane(k.z, 0);
+    r.kz1 = __builtin_amdgcn_readlane(k.z, 32);
+    r.vz0 = __builtin_amdgcn_readlane(v.z, 0);
+    r.vz1 = __builtin_amdgcn_readlane(v.z, 32);
+}
+
+// The K codes, scales and zero points of the new row into slot `slot` of
+// chunk ch (the V codes are written by patch_v, merged with the words'
+// other slots).
+__device__ __forceinline__ void store_new_row(const NewRow& r, uint8_t* ch, const Fmt& f, int slot, int lane)
+{
+    if ((lane & 7) < 3) ((uint32_t*)(ch + f.off_kc + slot * 96))[3 * (lane >> 3) + (lane & 7)] = r.kw;
+    if (lane < 2) {  // lane g: group g
+        ((float*)(ch + f.off_ks))[lane * BT + slot] = lane ? r.ks1 : r.ks0;
+        ((float*)(ch + f.off_vs))[lane * BT + slot] = lane ? r.vs1 : r.vs0;
+        ch[f.off_kz + lane * BT + slot] = (uint8_t)(lane ? r.kz1 : r.kz0);
+        ch[f.off_vz + lane * BT + slot] = (uint8_t)(lane ? r.vz1 : r.vz0);
+    }
+}
+
+// The new row's scales and zero points into the block's staged metadata.
+__device__ __forceinline__ void patch_meta(const NewRow& r, uint8_t* lds, int slot, int lane)
+{
+    if (lane < 2) {
+        *(float*)(lds + lane * 256 + 4 * slot) = lane ? r.ks1 : r.ks0;
+        *(float*)(lds + META_VS + lane * 256 + 4 * slot) = lane ? r.vs1 : r.vs0;
+        lds[META_KZ + lane * 64 + slot] = (uint8_t)(lane ? r.kz1 : r.kz0);
+        lds[META_VZ + lane * 64 + slot] = (uint8_t)(lane ? r.vz1 : r.vz0);
+    }
+}
+
+// K row word w of the new row, from the lane that holds it.
+__device__ __forceinline__ uint32_t new_k_word(const NewRow& r, int w)
+{
+    return (uint32_t)__shfl((int)r.kw, 8 * (w / 3) + w % 3, 64);
+}
+
+// The new row's K codes into the block's K registers: the lanes whose
+// tiles hold token `slot` (load_k_sets / load_k layouts).
+template <int VB, bool SETS>
+__device__ __forceinline__ void patch_k(BlockRegs<VB>& R, const NewRow& r, int slot, int q, int c)
+{
+    if constexpr (SETS) {
+        uint32_t w[12];
+#pragma unroll
+        for (int i = 0; i < 12; i++) w[i] = new_k_word(r, 12 * (q & 1) + i);
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            const bool hit = 16 * (c >> 2) + set_tok<VB>(0, q >> 1, u, c & 3) == slot;
+#pragma unroll
+            for (int i = 0; i < 6; i++) {
+                R.kr[2 * u][i] = hit ? w[i] : R.kr[2 * u][i];
+                R.kr[2 * u + 1][i] = hit ? w[6 + i] : R.kr[2 * u + 1][i];
+            }
+        }
+    } else {
+        uint32_t w[6];
+#pragma unroll
+        for (int i = 0; i < 6; i++) w[i] = new_k_word(r, 6 * q + i);
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            const bool hit = 16 * (c >> 2) + tok_of<VB>(t, c & 3) == slot;
+#pragma unroll
+            for (int i = 0; i < 6; i++) R.kr[t][i] = hit ? w[i] : R.kr[t][i];
+        }
+    }
+}
+
+// The new row's V codes into the block's V registers (lane group q holds
+// tokens 16 q .. 16 q + 15 of channels 16 T + c), and the merged words, the
+// pool's new contents, into chunk ch.
+template <int VB>
+__device__ __forceinline__ void patch_v(BlockRegs<VB>& R, const NewRow& r, int slot, int q, int c, uint8_t* ch,
+                                        uint32_t off_vc)
+{
+    constexpr int NW = VB == 4 ? 2 : 3;
+    const int bit = VB * (slot & 15), wi = bit >> 5, sh = bit & 31;
+    const bool spill = sh + VB > 32;  // a 6-bit field across two words
+    const uint32_t fm = (1u << VB) - 1u;
+    const bool mine = q == (slot >> 4);
+#pragma unroll
+    for (int T = 0; T < 8; T++) {
+        const uint32_t x = (uint32_t)__shfl((int)r.vq, 8 * T + (c >> 1), 64);
+        const uint32_t code = (c & 1) ? (x >> 8) & 0xFFu : x & 0xFFu;
+        uint32_t* row = (uint32_t*)(ch + off_vc + (16 * T + c) * (8 * VB)) + (VB * q) / 2;
+#pragma unroll
+        for (int w = 0; w < NW; w++) {
+            uint32_t m = 0u, v = 0u;
+            if (w == wi) {
+                m = fm << sh;
+                v = code << sh;
+            } else if (w == wi + 1 && spill) {
+                m = fm >> (32 - sh);
+                v = code >> (32 - sh);
+            }
+            if (mine && m != 0u) {
+                R.vr[T][w] = (R.vr[T][w] & ~m) | v;
+                row[w] = R.vr[T][w];
+            }
+        }
+    }
+}
+
 // One wave's split: split sp of KV head blockIdx.y of grid entry blockIdx.z.
 // PAIR (the 8-head layout over 4 query heads per KV head): grid entry
 // blockIdx.z is a pair of consecutive query tokens (2i, 2i + 1) of one
@@ -806,8 +975,9 @@ __device__ __forceinline__ void block_pv_sets(const BlockRegs<VB>& R, const uint
 // for both.  The earlier token's causal prefix is one token shorter: its
 // columns are masked in the split's last blocks.  An odd T's last token is
 // paired with itself and its second copy is not written.
-template <int VB, int G, bool KN, bool PAIR = false, bool DBG = false>
-__device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint4* meta_lds)
+template <int VB, int G, bool KN, bool PAIR = false, bool DBG = false, bool APP = false>
+__device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, const int kvh, const int b, const int lane,
+                                           uint4* meta_lds)
 {
     static_assert(G == 4 || G == 8, "4 or 8 query heads per KV head");
     static_assert(!PAIR || G == 8, "a pair fills the 8-head layout");
@@ -815,8 +985,6 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
     constexpr int D = 128;
     const SegArgs& sg = a.seg;
     const Fmt& f = sg.f;
-    const int kvh = blockIdx.y, b = blockIdx.z;
-    const int lane = threadIdx.x;
     const int c = lane & 15, q = lane >> 4;
     const int t0 = sp * a.split_tokens;
     // the split's block-table entries (at most 64, one per lane) do not
@@ -853,8 +1021,8 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
                 p[D] = -INFINITY;
                 p[D + 1] = 0.0f;
             }
-        } else if (threadIdx.x < G) {
-            float* p = a.partials + (((int64_t)b * a.num_q_heads + kvh * G + threadIdx.x) * a.total_splits +
+        } else if (lane < G) {
+            float* p = a.partials + (((int64_t)b * a.num_q_heads + kvh * G + lane) * a.total_splits +
                                      sg.split_base + sp) * (D + 2);
             p[D] = -INFINITY;
             p[D + 1] = 0.0f;
@@ -895,13 +1063,24 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
 #pragma unroll
         for (int i = 0; i < NQ; i++) qraw[i] = src[i];
     }
+    const int nblk = (t1 - t0 + BT - 1) / BT;
+    // APP: this wave appends the newest token (position len - 1, in its last
+    // block) when the token falls in its split; the row's inputs are
+    // requested together with Q
+    const bool app = APP && (len - 1) / a.split_tokens == sp;
+    float xk[2] = {0.0f, 0.0f}, xv[2] = {0.0f, 0.0f};
+    if constexpr (APP) {
+        if (app) {
+            load_pair(a.k_new, (int64_t)seq * f.H + kvh, a.kv_dtype, lane, xk);
+            load_pair(a.v_new, (int64_t)seq * f.H + kvh, a.kv_dtype, lane, xv);
+        }
+    }
     asm volatile("" ::: "memory");
 
     const uint8_t* lds = (const uint8_t*)meta_lds;
 
     // the split's block-table entries (at most 64), one per lane, so that
     // every chunk address is a register read instead of a memory round trip
-    const int nblk = (t1 - t0 + BT - 1) / BT;
     // end of this lane's column's tokens in the split, and of the tokens
     // every column has (they differ only for a pair: t1 belongs to the later
     // token, the earlier one ends a token sooner)
@@ -966,6 +1145,18 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
     }
     const float qsum = rows_sum(qpart);
     const float q128 = 128.0f * qsum;
+    // APP: quantise the new row while the first block is in flight (its
+    // inputs are not waited for before the block's loads are issued), and
+    // write its K codes and metadata for later steps
+    NewRow nr{};
+    const int app_slot = (len - 1) & (BT - 1);
+    if constexpr (APP) {
+        asm volatile("" : "+v"(xk[0]), "+v"(xk[1]), "+v"(xv[0]), "+v"(xv[1]));
+        if (app) {
+            quantize_new_row<VB>(xk, xv, lane, nr);
+            store_new_row(nr, (uint8_t*)chunk_of(nblk - 1), f, app_slot, lane);
+        }
+    }
 
     const Magic mk = make_magic();
     SplitState S;
@@ -984,6 +1175,13 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
         // loads ahead of the other wave's softmax and P.V
         __builtin_amdgcn_s_setprio(1);
         stage_meta<KN>(R.meta, meta_lds, lane);
+        if constexpr (APP && !MORE) {
+            // the split's last block holds the appended token
+            if (app) {
+                patch_meta(nr, (uint8_t*)meta_lds, app_slot, lane);
+                patch_k<VB, SETS>(R, nr, app_slot, q, c);
+            }
+        }
         if constexpr (MORE) load_meta<VB, KN>(R, cn, off_ks, lane);
         asm volatile("" ::: "memory");
         f32x4_t dot[SETS ? 2 : 4];
@@ -1003,10 +1201,16 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
         if constexpr (SETS) {
             const float alpha = block_softmax_sets<VB, PARTIAL, KN>(dot, lds, S, qsum, a.score_scale, a.tau_low,
                                                                     nlive, q, c, p, keep, srow, mrow, mcol);
+            if constexpr (APP && !MORE) {
+                if (app) patch_v<VB>(R, nr, app_slot, q, c, (uint8_t*)chunk_of(k), off_vc);
+            }
             block_pv_sets<VB, PARTIAL>(R, lds, S, p, alpha, keep, q, c, hA, mk);
         } else {
             const float alpha = block_softmax<VB, PARTIAL, KN>(dot, lds, S, qsum, a.score_scale, a.tau_low, nlive, q,
                                                                c, p, keep, srow, mrow, mcol);
+            if constexpr (APP && !MORE) {
+                if (app) patch_v<VB>(R, nr, app_slot, q, c, (uint8_t*)chunk_of(k), off_vc);
+            }
             block_pv<VB, PARTIAL>(R, lds, S, p, alpha, keep, q, c, hA, mk);
         }
         if constexpr (MORE) load_v<VB>(R, cn, off_vc, c, q);
@@ -1073,11 +1277,14 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, uint
 // DBG: the same kernel that also records its skip decisions (the test entry
 // point's skip mask); production launches take DBG = false, where the mask
 // code is compiled out.
+// DBG: the same kernel that also records its skip decisions (the test entry
+// point's skip mask); production launches take DBG = false, where the mask
+// code is compiled out.
 template <int VB, int G, bool KN, bool DBG>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void split_mfma_kernel(MfmaArgs a)
 {
     __shared__ uint4 meta_lds[meta_bytes<KN>() / 16];
-    split_body<VB, G, KN, false, DBG>(a, blockIdx.x, meta_lds);
+    split_body<VB, G, KN, false, DBG>(a, blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x, meta_lds);
 }
 
 // Query-token pairs of a multi-token call with 4 query heads per KV head
@@ -1086,7 +1293,7 @@ template <int VB, bool KN, bool DBG>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void split_mfma_pair_kernel(MfmaArgs a)
 {
     __shared__ uint4 meta_lds[meta_bytes<KN>() / 16];
-    split_body<VB, 8, KN, true, DBG>(a, blockIdx.x, meta_lds);
+    split_body<VB, 8, KN, true, DBG>(a, blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x, meta_lds);
 }
 
 // Both segments of a tiered cache in one launch: workgroups [0, n0) run the
@@ -1098,8 +1305,39 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
 {
     __shared__ uint4 meta_lds[META_BYTES / 16];
     const int sp = blockIdx.x;
-    if (sp < a0.seg.n_splits) split_body<6, G, false, false, DBG>(a0, sp, meta_lds);
-    else split_body<4, G, false, false, DBG>(a1, sp - a0.seg.n_splits, meta_lds);
+    if (sp < a0.seg.n_splits) split_body<6, G, false, false, DBG>(a0, sp, blockIdx.y, blockIdx.z, threadIdx.x, meta_lds);
+    else split_body<4, G, false, false, DBG>(a1, sp - a0.seg.n_splits, blockIdx.y, blockIdx.z, threadIdx.x, meta_lds);
+}
+
+// Decode with the step's own append (lkv_append_decode): the split holding
+// each sequence's newest token writes that token's K and V row first.
+//
+// Dispatch order.  Workgroups start in linear order, one wave per SIMD
+// first; on every SIMD the wave that started first finishes well ahead of
+// the one that started second (about 15 us in a 60 us call), so the second
+// half of the grid sets the call's time.  The splits holding a sequence's
+// newest token, which carry the append, are therefore started first: the
+// first half of the grid takes the last ceil(n/2) splits of every row (KV
+// head, entry), newest first, the second half the rest.  Inside each half
+// the split index runs fastest, so consecutive workgroups (which go to the
+// XCDs in turn) still take different splits of one row.
+template <int VB, int G>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void split_append_kernel(MfmaArgs a)
+{
+    __shared__ uint4 meta_lds[META_BYTES / 16];
+    const int ns = a.seg.n_splits, H = a.seg.f.H;
+    const int P = (ns + 1) / 2;  // splits per row in the first half
+    const int rows = (int)gridDim.x / ns;  // (KV head, entry) rows
+    int lin = blockIdx.x, rev, row;
+    if (lin < P * rows) {
+        rev = lin % P;
+        row = lin / P;
+    } else {
+        lin -= P * rows;
+        rev = P + lin % (ns - P);
+        row = lin / (ns - P);
+    }
+    split_body<VB, G, false, false, false, true>(a, ns - 1 - rev, row % H, row / H, threadIdx.x, meta_lds);
 }
 
 // Whether a segment has a matrix-core kernel.
@@ -1127,6 +1365,9 @@ static MfmaArgs mfma_args(const SegArgs& s, const void* q, int32_t num_q_heads, 
     a.score_scale = sm_scale * 1.4426950408889634f;
     a.tau_low = tau_low;
     a.partials = partials;
+    a.k_new = nullptr;
+    a.v_new = nullptr;
+    a.kv_dtype = 0;
     return a;
 }
 
@@ -1175,6 +1416,30 @@ static void launch_plain(const MfmaArgs& a, int vb, int G, bool kn, dim3 grid, h
     else if (vb == 4) hipLaunchKernelGGL((split_mfma_kernel<4, 8, false, DBG>), grid, dim3(64), 0, st, a);
     else if (G == 4) hipLaunchKernelGGL((split_mfma_kernel<6, 4, false, DBG>), grid, dim3(64), 0, st, a);
     else hipLaunchKernelGGL((split_mfma_kernel<6, 8, false, DBG>), grid, dim3(64), 0, st, a);
+}
+
+bool launch_append_decode_mfma(const SegArgs& s, const void* q, int q_dtype, int32_t batch, int32_t num_q_heads,
+                               float sm_scale, float tau_low, int32_t split_tokens, int32_t total_splits,
+                               float* partials, const void* k_new, const void* v_new, int kv_dtype,
+                               hipStream_t stream, hipError_t* err)
+{
+    const uintptr_t align = kv_dtype == LKV_F32 ? 8 : 4;  // a lane reads its two channels at once
+    if (!mfma_ok(s, q, q_dtype, num_q_heads, sm_scale, split_tokens) || s.f.k_norm || s.q_per_seq != 1 ||
+        s.skip_mask != nullptr || s.scores != nullptr || (uintptr_t)k_new % align != 0 ||
+        (uintptr_t)v_new % align != 0)
+        return false;
+    const int G = num_q_heads / s.f.H;
+    MfmaArgs a = mfma_args(s, q, num_q_heads, sm_scale, tau_low, split_tokens, total_splits, partials);
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.kv_dtype = kv_dtype;
+    const dim3 grid((unsigned)(s.n_splits * s.f.H * batch));  // every (split, KV head, entry), in the order above
+    if (s.f.vb == 4 && G == 4) hipLaunchKernelGGL((split_append_kernel<4, 4>), grid, dim3(64), 0, stream, a);
+    else if (s.f.vb == 4) hipLaunchKernelGGL((split_append_kernel<4, 8>), grid, dim3(64), 0, stream, a);
+    else if (G == 4) hipLaunchKernelGGL((split_append_kernel<6, 4>), grid, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL((split_append_kernel<6, 8>), grid, dim3(64), 0, stream, a);
+    *err = hipGetLastError();
+    return true;
 }
 
 // Returns true and launches when the format and shape have a matrix-core

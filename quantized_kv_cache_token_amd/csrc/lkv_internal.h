@@ -71,9 +71,20 @@ __device__ __forceinline__ int entry_len(const SegArgs& s, int e)
     return s.causal ? len - (s.q_per_seq - 1 - e % s.q_per_seq) : len;
 }
 
+// cu_new null: one row per sequence (row b) at position min(start_pos[b],
+// len_cap) - 1, start_pos holding lengths that count the row.
 hipError_t launch_append(const Fmt& f, uint8_t* pool, const void* k, const void* v, int dtype,
                          const int32_t* cu_new, const int32_t* start_pos, const int32_t* block_table,
-                         int32_t max_blocks, int32_t batch, int32_t max_new, hipStream_t stream);
+                         int32_t max_blocks, int32_t batch, int32_t max_new, hipStream_t stream,
+                         int32_t len_cap = 0);
+
+// The matrix-core split kernel that also appends each sequence's newest row
+// (lkv_append_decode); false when the format, shape or input alignment has
+// no such kernel.
+bool launch_append_decode_mfma(const SegArgs& s, const void* q, int q_dtype, int32_t batch, int32_t num_q_heads,
+                               float sm_scale, float tau_low, int32_t split_tokens, int32_t total_splits,
+                               float* partials, const void* k_new, const void* v_new, int kv_dtype,
+                               hipStream_t stream, hipError_t* err);
 
 // Partials: fp32 [batch][Hq][total_splits][D + 2] = (o[D], m, L).
 hipError_t launch_decode_split(const SegArgs& s, const void* q, int q_dtype, int32_t batch,

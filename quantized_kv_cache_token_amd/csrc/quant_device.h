@@ -3,9 +3,11 @@
 // Group-wise asymmetric integer quantisation with an fp32 scale and an integer
 // zero point (TurboQuant page, core innovation; K at 6 bits and V at 4 bits,
 // Super KV Compression page, first layer).  Files that include this header
-// are compiled with -ffp-contract=off: the scale, zero point and codes are
-// computed in IEEE fp32 with correctly rounded division and round-half-even
-// rint, in a fixed order, so they are reproducible bit for bit.
+// are compiled with -ffp-contract=off, and the quantiser functions also turn
+// contraction off themselves (for the decode kernel that appends a row): the
+// scale, zero point and codes are computed in IEEE fp32 with correctly
+// rounded division and round-half-even rint, in a fixed order, so they are
+// reproducible bit for bit.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -53,6 +55,7 @@ __device__ __forceinline__ float seg_max(float x, int seg) { return seg_extreme<
 // The sign of a zero minimum or maximum never changes the result.
 __device__ __forceinline__ int quantize_lane(float x, int g, int bits, float* s_out, int* z_out)
 {
+#pragma clang fp contract(off)
     const int qmax = (1 << bits) - 1;
     const float mn = seg_min(x, g);
     const float mx = seg_max(x, g);
@@ -127,6 +130,7 @@ __device__ __forceinline__ int lanes_extreme(int k)
 // within two ulps of 1 / s; sets `slow` when the result is not certain.
 __device__ __forceinline__ float rint_quot(float x, float s, float rc, bool& slow)
 {
+#pragma clang fp contract(off)
     const float q0 = x * rc;
     const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, s, x), rc, q0);
     const float r = rintf(q1);
@@ -149,6 +153,7 @@ struct QRow {
 template <int P, int GS>
 __device__ __forceinline__ void quantize_fast(const float (&x)[P], int bits, QRow<P>& o)
 {
+#pragma clang fp contract(off)
     const int qmax = (1 << bits) - 1;
     const float fq = (float)qmax;
     const float C = bits == 6 ? 0x1.041042p-6f : 0x1.111112p-4f;  // RN(1/63), RN(1/15)
@@ -193,6 +198,7 @@ __device__ __forceinline__ void quantize_fast(const float (&x)[P], int bits, QRo
 template <int P>
 __device__ __forceinline__ void quantize_exact(const float (&x)[P], int bits, QRow<P>& o)
 {
+#pragma clang fp contract(off)
     const int qmax = (1 << bits) - 1;
     const float lo = o.mn < 0.0f ? o.mn : 0.0f;
     const float hi = o.mx > 0.0f ? o.mx : 0.0f;

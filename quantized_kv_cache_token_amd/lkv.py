@@ -48,7 +48,7 @@ EXPORTS = ["lkv_status_string", "lkv_chunk_layout", "lkv_quant_append", "lkv_dec
            "lkv_decode_scores_workspace_bytes", "lkv_decode_attn_scores",
            "lkv_default_thresholds", "lkv_tier_workspace_bytes", "lkv_tier_update",
            "lkv_retier_workspace_bytes", "lkv_retier", "lkv_decode_attn_multi", "lkv_decode_plan_multi",
-           "lkv_decode_attn_debug", "lkv_decode_attn_noalloc"]
+           "lkv_decode_attn_debug", "lkv_decode_attn_noalloc", "lkv_append_decode", "lkv_append_split"]
 
 
 def lib():
@@ -80,6 +80,8 @@ def lib():
         "lkv_retier_workspace_bytes": ([I32, I32, I32], I64),
         "lkv_decode_attn_multi": ([PC, PV, I32, P, I32, I32, I32, I32, F, F, I32, P, P, C.c_size_t, V], C.c_int),
         "lkv_decode_plan_multi": ([PC, PV, I32, I32, I32, I32, C.POINTER(I32)], C.c_int),
+        "lkv_append_decode": ([PC, PV, P, P, I32, P, I32, I32, I32, F, F, I32, P, P, C.c_size_t, V], C.c_int),
+        "lkv_append_split": ([PC, PV, P, P, I32, P, I32, I32, I32, F, F, I32, P, C.c_size_t, V], C.c_int),
         "lkv_decode_attn_noalloc": ([PC, PV, I32, P, I32, I32, I32, F, F, I32, P, V], C.c_int),
         "lkv_decode_attn_debug": ([PC, PV, I32, P, I32, I32, I32, I32, F, F, I32, P, P, I32, P, C.c_size_t, V],
                                   C.c_int),
@@ -238,6 +240,31 @@ def decode_attn(caches, views, q: torch.Tensor, sm_scale: float, tau_low: float 
     _check("lkv_decode_attn", lib().lkv_decode_attn(
         cs, vs, n, _ptr(q), _DTYPE[q.dtype], B, Hq, sm_scale, tau_low, split_tokens, _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def append_decode(cache: Cache, view: View, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                  sm_scale: float, tau_low: float = 0.0, split_tokens: int = 0, out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None, stream=None):
+    """lkv_append_decode: append each sequence's new row (k_new, v_new
+    [B][Hkv][D]) at position seq_lens[b] - 1, then decode q [B][Hq][D] over
+    seq_lens[b] tokens -> out fp32 [B][Hq][D]."""
+    B, Hq, D = q.shape
+    _require(q.is_contiguous() and k_new.is_contiguous() and v_new.is_contiguous(), "q, k_new, v_new contiguous")
+    _require(k_new.dtype == v_new.dtype and k_new.shape == v_new.shape == (B, cache.num_kv_heads, cache.head_dim),
+             "k_new and v_new must be [B][Hkv][D] of one dtype")
+    if split_tokens == 0:
+        split_tokens = decode_plan([cache], [view], B, Hq)
+    with _on(stream):
+        if workspace is None:
+            workspace = decode_workspace([cache], [view], B, Hq, split_tokens, q.device)
+        if out is None:
+            out = torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
+    cc, vc = cache.c(), view.c()
+    _check("lkv_append_decode", lib().lkv_append_decode(
+        C.byref(cc), C.byref(vc), _ptr(k_new), _ptr(v_new), _DTYPE[k_new.dtype], _ptr(q), _DTYPE[q.dtype], B, Hq,
+        sm_scale, tau_low, split_tokens, _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
     return out
 
 
@@ -455,6 +482,20 @@ def prepare_decode_scores(caches, views, q, sm_scale: float, tau_low: float, spl
                     workspace.numel() * workspace.element_size(), _stream(stream))
     call._keep = (cs, vs)
     return call
+
+
+def prepare_append_decode(cache: Cache, view: View, k_new, v_new, q, sm_scale: float, tau_low: float,
+                          split_tokens: int, out, workspace, stream=None) -> tuple[Prepared, Prepared]:
+    """(append + split, combine) stages of lkv_append_decode as prepared calls."""
+    B, Hq, _ = q.shape
+    cs, vs, n = _segs([cache], [view])
+    nbytes = workspace.numel() * workspace.element_size()
+    st = _stream(stream)
+    split = Prepared("lkv_append_split", cs, vs, _ptr(k_new), _ptr(v_new), _DTYPE[k_new.dtype], _ptr(q),
+                     _DTYPE[q.dtype], B, Hq, sm_scale, tau_low, split_tokens, _ptr(workspace), nbytes, st)
+    comb = Prepared("lkv_decode_combine", cs, vs, n, B, Hq, split_tokens, _ptr(out), _ptr(workspace), nbytes, st)
+    split._keep = comb._keep = (cs, vs)
+    return split, comb
 
 
 def prepare_decode(caches, views, q, sm_scale: float, tau_low: float, split_tokens: int, out, workspace,

@@ -3,7 +3,8 @@
     python -m quantized_kv_cache_token_amd.profsum stats <dir> [--match REGEX]
     python -m quantized_kv_cache_token_amd.profsum dispatches <dir> [--match REGEX]
     python -m quantized_kv_cache_token_amd.profsum traffic --fetch <dir> --write <dir>
-        --kernel REGEX --workload NAME --alg-bytes N --out FILE [--command TEXT]
+        --kernel REGEX [--kernel REGEX ...] --workload NAME --alg-bytes N [--fused]
+        --out FILE [--command TEXT]
 
 `stats` prints per-kernel call counts and durations from a
 `rocprofv3 --kernel-trace --stats --output-format csv` run.
@@ -13,7 +14,8 @@ separates, say, the one-row appends of decode steps from prefill appends.
 
 `traffic` turns two counter runs (`--pmc FETCH_SIZE`, then `--pmc
 WRITE_SIZE`, both of `bench.py --copy-probe`) into HBM bytes per launch of
-one kernel.  Both counters read in KiB per dispatch.  Each is scaled by what
+each named kernel (the split kernel and the merge), and their sum: the bytes
+of one decode step's attention.  Both counters read in KiB per dispatch.  Each is scaled by what
 the same counter reads for the streaming probe, which reads exactly 1 GiB and
 writes exactly 1 GiB, so that the figure is in true bytes.  The
 result goes to a JSON file keyed by the hash of the decode kernel sources:
@@ -34,8 +36,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 PROBE_BYTES = 1 << 30          # the streaming probe reads and writes 1 GiB
 PROBE_REGEX = r"neg_kernel"    # its kernel: an elementwise negation over fp32
-# the sources of the split kernel the traffic record describes
-DECODE_SOURCES = ("decode_mfma.hip", "wave_util.h", "lkv_internal.h")
+# the sources of the split kernel and the merge the traffic record describes
+DECODE_SOURCES = ("decode_mfma.hip", "decode.hip", "quant_device.h", "wave_util.h", "lkv_internal.h")
 
 
 def kernel_source_hash() -> str:
@@ -105,27 +107,30 @@ def _mean_of(vals: dict[str, list[float]], regex: str) -> tuple[str, float, int]
     return names[0], sum(v) / len(v), len(v)
 
 
-def traffic(fetch_dir: str, write_dir: str, kernel: str, workload: str, alg_bytes: int, command: str) -> dict:
+def traffic(fetch_dir: str, write_dir: str, kernels: list[str], workload: str, alg_bytes: int, fused: bool,
+            command: str) -> dict:
     f = _per_dispatch(fetch_dir, "FETCH_SIZE")
     w = _per_dispatch(write_dir, "WRITE_SIZE")
-    kname, kf, nf = _mean_of(f, kernel)
-    _, kw, nw = _mean_of(w, kernel)
     _, pf, _ = _mean_of(f, PROBE_REGEX)
     _, pw, _ = _mean_of(w, PROBE_REGEX)
     sf = PROBE_BYTES / (pf * 1024.0)
     sw = PROBE_BYTES / (pw * 1024.0)
-    fetch_b = kf * 1024.0 * sf
-    write_b = kw * 1024.0 * sw
+    per, total = [], 0.0
+    for kernel in kernels:
+        kname, kf, nf = _mean_of(f, kernel)
+        _, kw, nw = _mean_of(w, kernel)
+        fetch_b = kf * 1024.0 * sf
+        write_b = kw * 1024.0 * sw
+        total += fetch_b + write_b
+        per.append({"kernel": _short(kname), "dispatches": [nf, nw], "fetch_kib_raw": round(kf, 2),
+                    "write_kib_raw": round(kw, 2), "hbm_fetch_bytes_per_launch": int(fetch_b),
+                    "hbm_write_bytes_per_launch": int(write_b)})
     return {
-        "kernel": _short(kname), "workload": workload, "source_hash": kernel_source_hash(),
-        "dispatches": [nf, nw],
-        "fetch_kib_raw": round(kf, 2), "write_kib_raw": round(kw, 2),
+        "workload": workload, "fused": fused, "source_hash": kernel_source_hash(), "kernels": per,
         "probe_fetch_kib_raw": round(pf, 2), "probe_write_kib_raw": round(pw, 2),
         "scale_fetch": round(sf, 5), "scale_write": round(sw, 5),
-        "hbm_fetch_bytes_per_launch": int(fetch_b), "hbm_write_bytes_per_launch": int(write_b),
-        "hbm_bytes_per_launch": int(fetch_b + write_b),
-        "alg_bytes_per_launch": alg_bytes,
-        "traffic_over_alg": round((fetch_b + write_b) / alg_bytes, 4),
+        "hbm_bytes_per_step": int(total), "alg_bytes_per_step": alg_bytes,
+        "traffic_over_alg": round(total / alg_bytes, 4),
         "command": command,
     }
 
@@ -142,7 +147,8 @@ def main(argv=None):
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
-    t.add_argument("--kernel", required=True)
+    t.add_argument("--kernel", required=True, action="append")
+    t.add_argument("--fused", action="store_true")
     t.add_argument("--workload", required=True)
     t.add_argument("--alg-bytes", type=int, required=True)
     t.add_argument("--out", required=True)
@@ -153,7 +159,7 @@ def main(argv=None):
     elif a.cmd == "dispatches":
         print(dispatches(a.dir, a.match))
     else:
-        rec = traffic(a.fetch, a.write, a.kernel, a.workload, a.alg_bytes, a.command)
+        rec = traffic(a.fetch, a.write, a.kernel, a.workload, a.alg_bytes, a.fused, a.command)
         with open(a.out, "w") as fh:
             json.dump(rec, fh, indent=1)
             fh.write("\n")

@@ -214,6 +214,40 @@ def test_decode_debug_rejects_bad_arguments_before_any_launch():
     assert call(out=None) == lkv.EINVAL
 
 
+def test_append_decode_rejects_bad_arguments_before_any_launch():
+    L = lkv.lib()
+    p = C.c_void_p(0x90000)
+    vs = (lkv._View * 1)(_view(max_len=1000))
+
+    def call(fn="lkv_append_decode", kvd=lkv.BF16, k=p, v=p, split=256, ws=1 << 30, q_dtype=lkv.BF16, knorm=0,
+             out=p):
+        cs = (lkv._Cache * 1)(_cache(k_norm=knorm))
+        if fn == "lkv_append_decode":
+            return L.lkv_append_decode(cs, vs, k, v, kvd, p, q_dtype, 8, 32, 0.088, 0.0, split, out, p, ws, None)
+        return L.lkv_append_split(cs, vs, k, v, kvd, p, q_dtype, 8, 32, 0.088, 0.0, split, p, ws, None)
+
+    for fn in ("lkv_append_decode", "lkv_append_split"):
+        assert call(fn, kvd=7) == lkv.EINVAL
+        assert call(fn, k=None) == lkv.EINVAL
+        assert call(fn, v=None) == lkv.EINVAL
+        assert call(fn, ws=100) == lkv.EINVAL
+        assert call(fn, q_dtype=lkv.F16) == lkv.EINVAL
+        assert call(fn, knorm=1, k=C.c_void_p(0x90002)) == lkv.EUNSUPPORTED  # k_norm: two-element alignment
+    assert call("lkv_append_split", split=0) == lkv.EINVAL       # the split stage takes a resolved size
+    assert call("lkv_append_decode", out=None) == lkv.EINVAL
+
+
+def test_noalloc_rejects_partials_beyond_its_scratch_before_any_launch():
+    L = lkv.lib()
+    p = C.c_void_p(0x90000)
+    cs = (lkv._Cache * 1)(_cache(num_blocks=1 << 20))
+    vs = (lkv._View * 1)(_view(max_len=64, max_blocks=1))
+    # 65536 sequences x 32 heads x 1 split x 130 floats = 1.09 GB of partials
+    assert L.lkv_decode_attn_noalloc(cs, vs, 1, p, lkv.BF16, 65536, 32, 0.088, 0.0, 64, p, None) == lkv.ESCRATCH
+    assert "scratch" in lkv.status_string(lkv.ESCRATCH)
+    assert L.lkv_decode_attn_noalloc(cs, vs, 1, p, lkv.BF16, 8, 32, 0.088, 0.0, 48, p, None) == lkv.EINVAL
+
+
 def test_multi_token_plan_counts_query_pairs_at_four_heads_per_kv_head():
     L = lkv.lib()
     out = C.c_int32()
