@@ -295,6 +295,45 @@ __global__ __launch_bounds__(64 * NW) void combine_kernel(CombineArgs a)
     }
 }
 
+// The merge for head_dim 128 and at most 32 splits, the shape of the
+// matrix-core decode: one wave per (sequence, query head) whose lane l holds
+// channels 2l and 2l + 1 of every split's row (one 8-byte load per split,
+// all issued at once), with the splits' weights taken from their lanes by
+// readlane.  Same arithmetic, in the same order, as combine_kernel<128, 1>.
+__global__ __launch_bounds__(64) void combine128_kernel(CombineArgs a)
+{
+    constexpr int D = 128, CH = 32;
+    const int64_t bh = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int n = a.total_splits;
+    const float* p = a.part + bh * n * (D + 2);
+    float2 ov[CH];
+#pragma unroll
+    for (int i = 0; i < CH; i++) ov[i] = i < n ? *(const float2*)(p + (int64_t)i * (D + 2) + 2 * lane) : float2{};
+    const float mi = lane < n ? p[(int64_t)lane * (D + 2) + D] : -INFINITY;
+    const float li = lane < n ? p[(int64_t)lane * (D + 2) + D + 1] : 0.0f;
+    const float M = wave_max(mi);
+    float2 acc = {0.0f, 0.0f};
+    float L = 0.0f;
+    if (M != -INFINITY) {
+        const float wi = mi == -INFINITY ? 0.0f : exp2f(mi - M);
+        L = wave_sum(li * wi);
+#pragma unroll
+        for (int i = 0; i < CH; i++) {
+            // splits past n have weight 0 (their lanes hold mi = -inf)
+            const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wi), i));
+            acc.x += w != 0.0f ? ov[i].x * w : 0.0f;
+            acc.y += w != 0.0f ? ov[i].y * w : 0.0f;
+        }
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    *(float2*)(a.out + bh * D + 2 * lane) = float2{acc.x * inv, acc.y * inv};
+    if (a.ml != nullptr && lane == 0) {
+        a.ml[2 * bh] = M;
+        a.ml[2 * bh + 1] = inv;
+    }
+}
+
 hipError_t launch_decode_combine(const CombineArgs& a, int32_t batch, int32_t D, hipStream_t stream)
 {
     if (batch == 0) return hipSuccess;
@@ -304,7 +343,7 @@ hipError_t launch_decode_combine(const CombineArgs& a, int32_t batch, int32_t D,
     const bool one = a.total_splits <= 32;
     if (D == 64 && one) hipLaunchKernelGGL((combine_kernel<64, 1>), grid, dim3(64), 0, stream, a);
     else if (D == 64) hipLaunchKernelGGL((combine_kernel<64, 4>), grid, dim3(256), 0, stream, a);
-    else if (one) hipLaunchKernelGGL((combine_kernel<128, 1>), grid, dim3(64), 0, stream, a);
+    else if (one) hipLaunchKernelGGL(combine128_kernel, grid, dim3(64), 0, stream, a);
     else hipLaunchKernelGGL((combine_kernel<128, 4>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
