@@ -9,6 +9,7 @@ device code.
 """
 from __future__ import annotations
 
+import glob
 import os
 import shutil
 import subprocess
@@ -65,6 +66,45 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("link failed")
     os.replace(tmp, LIB)
     return LIB
+
+
+ASAN_LIB = os.path.join(BUILD, "liblkv_asan.so")
+
+
+def asan_runtime() -> str | None:
+    """The compiler's shared AddressSanitizer runtime, if present."""
+    root = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(hipcc()))), "llvm", "lib", "clang")
+    for cand in sorted(glob.glob(os.path.join(root, "*", "lib", "linux", "libclang_rt.asan-x86_64.so"))):
+        return cand
+    return None
+
+
+def build_asan(verbose: bool = False) -> str:
+    """The library with its host code (the C ABI's validation, planning and
+    launch set-up in api.cpp) built with AddressSanitizer; device code as in
+    build().  Written to _build/liblkv_asan.so, for CPU tests that load it
+    with the sanitizer runtime preloaded."""
+    cc = hipcc()
+    objs = []
+    for src, _ in SOURCES:
+        if src == "api.cpp":
+            continue
+        obj = os.path.join(BUILD, src.replace(".", "_") + ".o")
+        if not os.path.exists(obj):
+            build(verbose)
+        objs.append(obj)
+    api = os.path.join(BUILD, "api_cpp_asan.o")
+    cmd = [cc, *COMMON, "-x", "hip", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",
+           "-c", os.path.join(CSRC, "api.cpp"), "-o", api]
+    for c in (cmd, [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, api, "-Xarch_host",
+                    "-fsanitize=address", "-shared-libsan", "-o", ASAN_LIB]):
+        if verbose:
+            print(" ".join(c), flush=True)
+        r = subprocess.run(c, capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError("ASan build failed")
+    return ASAN_LIB
 
 
 if __name__ == "__main__":

@@ -86,12 +86,14 @@ __device__ __forceinline__ int quantize_lane(float x, int g, int bits, float* s_
 //    over the g / P lanes of the group;
 //  - s = RN(r / qmax) as r * RN(1 / qmax) plus one fma correction, which is
 //    the correctly rounded quotient for every finite r >= 0 when qmax is 15
-//    or 63 (checked exhaustively over all fp32 values);
+//    or 63 (tests/native/quant_exact.c checks every finite fp32 r);
 //  - rint(RN(x / s)) from an approximate reciprocal and one fma correction,
 //    which gives the quotient to within an ulp: rint can differ only when
 //    that quotient lies within a few ulps of a half-integer.  Such lanes
 //    (and any scale that is not a finite normal number) are flagged and
-//    recomputed with correctly rounded division (quantize_exact).
+//    recomputed with correctly rounded division (quantize_exact); the same
+//    file checks the flagged bound on random and near-tie quotients with
+//    reciprocals up to two ulps off.
 
 // Order-preserving integer key of a finite float (the map is its own
 // inverse): min / max of keys are single integer instructions, with no NaN
