@@ -344,7 +344,13 @@ int64_t lkv_tier_workspace_bytes(int32_t batch, int32_t scores_stride);
  * a destination has fewer than the count's slots (max_blocks * 64), the
  * count is returned negated and nothing is written to either destination for
  * that sequence.  scores, tiers: [batch][scores_stride]; workspace:
- * lkv_tier_workspace_bytes() bytes.  src is only read. */
+ * lkv_tier_workspace_bytes() bytes.  src is only read, unless dst_h is src
+ * compacted in place: the same pool and the same block table (pointer and
+ * h_max_blocks equal to the view's max_blocks).  Then the HIGH tokens end
+ * at positions 0 .. n_high-1 of src's own blocks, the blocks of a row past
+ * ceil(n_high / 64) hold no live token and may be reused, and the slots past
+ * n_high keep stale codes.  Otherwise no destination block may be one src
+ * uses; dst_m never shares src's block table (LKV_EINVAL). */
 int lkv_tier_update(const lkv_cache* src, const lkv_view* src_view,
                     const float* scores, int32_t scores_stride, float tau_low, float tau_high,
                     const lkv_cache* dst_h, const int32_t* h_block_table, int32_t h_max_blocks,
@@ -377,9 +383,22 @@ int64_t lkv_retier_workspace_bytes(int32_t batch, int32_t h_stride, int32_t m_st
  * and m_tiers[b][j] receive each live token's new tier (2, 1 or 0); n_high
  * and n_mid the new lengths.  If a destination has fewer than the count's
  * slots, both counts are returned negated and nothing is written to either
- * destination for that sequence.  The destination blocks must not be blocks
- * that the sources use (the pools may be the same), and n_high, n_mid must
- * not be the sources' seq_lens.  Workspace: lkv_retier_workspace_bytes(). */
+ * destination for that sequence.  n_high, n_mid must not be the sources'
+ * seq_lens.  Workspace: lkv_retier_workspace_bytes().
+ *
+ * In place: dst_h may be h and dst_m may be m, each the same pool and the
+ * same block table (pointer and max_blocks equal to its view's), so that a
+ * re-tier needs no second set of blocks.  A segment is then compacted
+ * within its own blocks (MID first, then HIGH, one launch after the other;
+ * within a segment a token never moves to a later position).  The MID row
+ * must hold valid blocks for n_mid positions, at most m_len + h_len: the
+ * demoted tokens follow the kept MID ones.  Afterwards the blocks of a row
+ * past ceil(n / 64) hold no live token and may go back to a free list; the
+ * slots past n keep stale codes.  In-place compaction walks each (sequence,
+ * KV head) in one workgroup, so it trades speed for memory.  Any other
+ * overlap between destination blocks and the blocks a source uses is not
+ * allowed; dst_h sharing m's block table or dst_m sharing h's is
+ * LKV_EINVAL. */
 int lkv_retier(const lkv_cache* h, const lkv_view* h_view, const float* h_scores, int32_t h_stride,
                const lkv_cache* m, const lkv_view* m_view, const float* m_scores, int32_t m_stride,
                float tau_low, float tau_high,

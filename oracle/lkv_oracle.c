@@ -574,16 +574,17 @@ int orc_decode(const orc_cache* segs, const orc_view* views, int32_t nseg,
  * moves the output by at most that token's weight, which is below
  * tau_low * (1 + band), times max |v_hat|.  margin (may be NULL) receives
  * the relative margin (exp(s - m) - tau_low * L) / (tau_low * L) of every
- * live pair when tau_low > 0. */
+ * live pair when tau_low > 0.  score_acc (may be NULL) accumulates the
+ * softmax weights as orc_decode does: they do not depend on the skip. */
 int orc_decode_resolved(const orc_cache* segs, const orc_view* views, int32_t nseg,
                         const float* q, int32_t batch, int32_t num_q_heads,
                         float sm_scale, float tau_low, int32_t split_tokens,
                         double* out, uint8_t* skip, const uint8_t* given, double band, uint8_t* ambiguous,
-                        double* margin)
+                        double* margin, double* score_acc, int32_t acc_stride)
 {
     if (!(band >= 0.0)) return -1;
     return decode_impl(segs, views, nseg, q, batch, num_q_heads, sm_scale, tau_low, split_tokens, out, skip,
-                       NULL, 0, given, band, ambiguous, margin);
+                       score_acc, acc_stride, given, band, ambiguous, margin);
 }
 
 /* --------------------------------------------------------- tier update */

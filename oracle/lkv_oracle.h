@@ -105,7 +105,7 @@ int orc_decode_resolved(const orc_cache* segs, const orc_view* views, int32_t ns
                         const float* q, int32_t batch, int32_t num_q_heads,
                         float sm_scale, float tau_low, int32_t split_tokens,
                         double* out, uint8_t* skip, const uint8_t* given, double band, uint8_t* ambiguous,
-                        double* margin);
+                        double* margin, double* score_acc, int32_t acc_stride);
 
 /* Tier update.  src: K6V6 cache + view.  scores fp32 [batch][scores_stride].
  * Writes tiers uint8 [batch][scores_stride] (0 low, 1 mid, 2 high; entries

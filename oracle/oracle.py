@@ -68,7 +68,8 @@ def lib():
         L.orc_decode.restype = C.c_int
         L.orc_decode_resolved.argtypes = [C.POINTER(_Cache), C.POINTER(_View), C.c_int32, C.c_void_p,
                                           C.c_int32, C.c_int32, C.c_float, C.c_float, C.c_int32,
-                                          C.c_void_p, C.c_void_p, C.c_void_p, C.c_double, C.c_void_p, C.c_void_p]
+                                          C.c_void_p, C.c_void_p, C.c_void_p, C.c_double, C.c_void_p, C.c_void_p,
+                                          C.c_void_p, C.c_int32]
         L.orc_decode_resolved.restype = C.c_int
         L.orc_tier_update.argtypes = [C.POINTER(_Cache), C.POINTER(_View), C.c_void_p, C.c_int32,
                                       C.c_float, C.c_float,
@@ -227,7 +228,7 @@ def decode(caches, block_tables, seq_lens, q: np.ndarray, sm_scale: float,
 
 
 def decode_resolved(caches, block_tables, seq_lens, q: np.ndarray, sm_scale: float, tau_low: float,
-                    split_tokens: int, given: np.ndarray | None, band: float):
+                    split_tokens: int, given: np.ndarray | None, band: float, score_acc: np.ndarray | None = None):
     """decode() with the skip decisions near the threshold resolved.
 
     A (token, head) pair whose exact margin |exp(s - m) - tau_low L| is at
@@ -236,7 +237,8 @@ def decode_resolved(caches, block_tables, seq_lens, q: np.ndarray, sm_scale: flo
     keeps the exact one) is taken.  Returns (out fp64 [B][Hq][D], skip,
     ambiguous, margin): skip and ambiguous uint8 in the layout of given, margin
     fp64 the relative margin (exp(s - m) - tau_low L) / (tau_low L) of every
-    live pair (0 elsewhere)."""
+    live pair (0 elsewhere).  score_acc: as in decode() (the weights do not
+    depend on the skip)."""
     q = np.ascontiguousarray(q, dtype=np.float32)
     B, Hq, D = q.shape
     nseg = len(caches)
@@ -254,9 +256,13 @@ def decode_resolved(caches, block_tables, seq_lens, q: np.ndarray, sm_scale: flo
         given = np.ascontiguousarray(given, dtype=np.uint8)
         if given.shape != shape:
             raise ValueError(f"given must be {shape}")
+    if score_acc is not None:
+        assert score_acc.dtype == np.float64 and score_acc.flags.c_contiguous
+        assert score_acc.ndim == 3 and score_acc.shape[:2] == (nseg, B)
     rc = lib().orc_decode_resolved(ccs, views, nseg, _p(q), B, Hq, sm_scale, tau_low, split_tokens, _p(out),
                                    _p(skip), _p(given) if given is not None else None, float(band), _p(amb),
-                                   _p(margin))
+                                   _p(margin), _p(score_acc) if score_acc is not None else None,
+                                   score_acc.shape[2] if score_acc is not None else 0)
     if rc != 0:
         raise ValueError("oracle decode rejected its arguments")
     return out, skip, amb, margin

@@ -14,7 +14,15 @@
 //    counts (negative when a destination has no room).
 //  tier_move: one workgroup per (8 consecutive source chunks, KV head,
 //    sequence, source).  Each source chunk is read once, whole and
-//    coalesced; its survivors go to consecutive destination positions.  K
+//    coalesced; its survivors go to consecutive destination positions.
+//    A destination that is its source segment itself (the same pool and
+//    block table) is compacted in place: then one workgroup walks a
+//    sequence's chunks of one KV head in order.  A survivor never moves to
+//    a later position and a chunk is read whole before anything is written
+//    into its block, so every chunk is read before it is overwritten; and
+//    the sources run one launch after the other, in destination order, so
+//    that the MID source's chunks are read before demoted tokens land in
+//    them.  K
 //    rows, scales and zeros are stored straight from the loaded pieces; V
 //    codes are copied (same width) or dequantised in fp32 and requantised
 //    at 4 bits (V6 -> V4) into an LDS block of destination codes, which is
@@ -202,6 +210,7 @@ struct MoveArgs {
     const int32_t* n_high;
     const int32_t* n_mid;
     int32_t nsrc;
+    int32_t per_wg;  // source chunks per workgroup (all of a sequence's when compacting in place)
 };
 
 __device__ __forceinline__ uint8_t* dst_chunk(const MoveDst& d, int b, int pos, int kvh)
@@ -328,9 +337,9 @@ __global__ __launch_bounds__(256) void tier_move_kernel(MoveArgs a)
     const Fmt& fs = S.f;
     const int len = max(0, min(S.lens[b], S.len_cap));
     const int nblocks = (len + BT - 1) / BT;
-    const int c0 = blockIdx.x * MOVE_CHUNKS;
+    const int c0 = blockIdx.x * a.per_wg;
     if (c0 >= nblocks) return;
-    const int c1 = min(nblocks, c0 + MOVE_CHUNKS);
+    const int c1 = min(nblocks, c0 + a.per_wg);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int2 base = S.blk_base[(int64_t)b * S.base_stride + c0];
     // next destination position of each segment, and the first position this
@@ -349,33 +358,49 @@ __global__ __launch_bounds__(256) void tier_move_kernel(MoveArgs a)
     const Fmt& fm = a.dst[1].f;
     const bool copy_m = fm.vb == fs.vb;  // MID survivors keep their V codes (a MID source)
 
-    // a chunk's tiers and its pieces are requested together (the tiers and
-    // block of the next chunk one iteration ahead)
+    // The pieces of the next chunk are in flight while a chunk is written
+    // out; its tiers come with them and the block of the one after.  The
+    // next chunk's loads are issued after the barrier that precedes this
+    // chunk's stores, which never touch the next chunk's block, and they
+    // complete before the barrier that precedes its own stores: in place,
+    // every chunk is read before it is overwritten.
     auto tiers_of = [&](int c) __attribute__((always_inline)) {
         return lane < min(BT, len - c * BT) ? (int)S.tiers[(int64_t)b * S.tier_stride + c * BT + lane] : 0;
     };
-    int t_next = tiers_of(c0);
-    int blk_next = S.bt[(int64_t)b * S.max_blocks + c0];
-    for (int c = c0; c < c1; c++) {
-        const uint8_t* sch = S.pool + ((int64_t)blk_next * fs.H + kvh) * fs.chunk;
-        uint4 pc[MOVE_PIECES];
+    auto load_pieces = [&](uint4 (&pc)[MOVE_PIECES], int blk) __attribute__((always_inline)) {
+        const uint4* sch = (const uint4*)(S.pool + ((int64_t)blk * fs.H + kvh) * fs.chunk);
 #pragma unroll
         for (int k = 0; k < MOVE_PIECES; k++) {
             const int p = tid + 256 * k;
-            pc[k] = p < npieces ? ((const uint4*)sch)[p] : make_uint4(0u, 0u, 0u, 0u);
+            pc[k] = p < npieces ? sch[p] : make_uint4(0u, 0u, 0u, 0u);
         }
+    };
+    const int32_t* brow = S.bt + (int64_t)b * S.max_blocks;
+    uint4 pn[MOVE_PIECES];
+    load_pieces(pn, brow[c0]);
+    int t_next = tiers_of(c0);
+    int blk_after = c0 + 1 < c1 ? brow[c0 + 1] : 0;
+    for (int c = c0; c < c1; c++) {
+        uint4 pc[MOVE_PIECES];
+#pragma unroll
+        for (int k = 0; k < MOVE_PIECES; k++) pc[k] = pn[k];
         // tiers of the chunk's 64 slots; every wave derives the same masks
         const int t = t_next;
-        if (c + 1 < c1) {
+        const int blk_next = blk_after;
+        const bool more = c + 1 < c1;
+        if (more) {
             t_next = tiers_of(c + 1);
-            blk_next = S.bt[(int64_t)b * S.max_blocks + c + 1];
+            blk_after = c + 2 < c1 ? brow[c + 2] : 0;
         }
         const uint64_t mk0 = __ballot(t == 2), mk1 = __ballot(t == 1);
         const uint64_t below = (1ull << lane) - 1ull;
         if (t == 2) src_of[wave][0][__popcll(mk0 & below)] = (uint8_t)lane;
         else if (t == 1) src_of[wave][1][__popcll(mk1 & below)] = (uint8_t)lane;
         const int n0 = __popcll(mk0), n1 = __popcll(mk1);
-        if (n0 + n1 == 0) continue;
+        if (n0 + n1 == 0) {
+            if (more) load_pieces(pn, blk_next);
+            continue;
+        }
         // destination chunks: the block of each segment's next position and
         // the one after it
         uint8_t *dA0 = nullptr, *dB0 = nullptr, *dA1 = nullptr, *dB1 = nullptr;
@@ -388,6 +413,7 @@ __global__ __launch_bounds__(256) void tier_move_kernel(MoveArgs a)
             dB1 = pos1 % BT + n1 > BT ? dst_chunk(a.dst[1], b, pos1 + BT, kvh) : dA1;
         }
         __syncthreads();  // the previous chunk's readers of vsrc and meta are done
+        if (more) load_pieces(pn, blk_next);
 #pragma unroll
         for (int k = 0; k < MOVE_PIECES; k++) {
             const int off = 16 * (tid + 256 * k);
@@ -534,11 +560,31 @@ hipError_t launch_tiering(const TierSource* src, int nsrc, float tau_low, float 
     a.n_high = n_high;
     a.n_mid = n_mid;
     a.nsrc = nsrc;
-    const dim3 grid((unsigned)((max_blocks + MOVE_CHUNKS - 1) / MOVE_CHUNKS), (unsigned)h.f.H,
-                    (unsigned)(batch * nsrc));
-    if (h.f.D == 64) hipLaunchKernelGGL(tier_move_kernel<64>, grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(tier_move_kernel<128>, grid, dim3(256), 0, stream, a);
-    return hipGetLastError();
+    a.per_wg = MOVE_CHUNKS;
+    bool in_place = false;
+    for (int i = 0; i < nsrc; i++)
+        for (const TierDest* d : {&h, &m})
+            in_place |= d->pool == src[i].pool && d->block_table == src[i].block_table;
+    auto launch = [&](const MoveArgs& x, int nz) {
+        const dim3 grid((unsigned)((max_blocks + x.per_wg - 1) / x.per_wg), (unsigned)h.f.H, (unsigned)(batch * nz));
+        if (h.f.D == 64) hipLaunchKernelGGL(tier_move_kernel<64>, grid, dim3(256), 0, stream, x);
+        else hipLaunchKernelGGL(tier_move_kernel<128>, grid, dim3(256), 0, stream, x);
+    };
+    if (!in_place) {
+        launch(a, nsrc);
+        return hipGetLastError();
+    }
+    // in place: a sequence's chunks of one KV head in order, one source per
+    // launch in destination order
+    for (int i = 0; i < nsrc; i++) {
+        MoveArgs one = a;
+        one.src[0] = a.src[i];
+        one.nsrc = 1;
+        one.per_wg = max(max_blocks, 1);
+        launch(one, 1);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace lkv

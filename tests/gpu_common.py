@@ -46,6 +46,21 @@ def max_abs_vhat(cache: O.Cache, batch: int = 256) -> float:
     return best
 
 
+def max_abs_vhat_live(cache: O.Cache, block_table, lens) -> float:
+    """max |v_hat| over the live tokens of a host pool only (pools that hold
+    stale bytes in other slots), read with the independent numpy unpacking."""
+    from tests import np_reference as R
+
+    best = 0.0
+    for b, n in enumerate(np.asarray(lens)):
+        if int(n) <= 0:
+            continue
+        _, V = R.dequant_sequence(cache.pool, cache.chunk_bytes, cache.num_kv_heads, cache.head_dim,
+                                  cache.group_size, cache.k_bits, cache.v_bits, np.asarray(block_table)[b], int(n))
+        best = max(best, float(np.abs(V).max()))
+    return best
+
+
 def assert_attention_close(got: np.ndarray, want: np.ndarray, vmax: float, what: str = ""):
     """max|d| <= 1e-3 max|v_hat| and ||d||_2 / ||want||_2 <= 1e-4."""
     got = np.asarray(got, np.float64)

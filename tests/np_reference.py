@@ -75,6 +75,28 @@ def dequant_sequence(pool: np.ndarray, chunk_bytes: int, Hkv: int, D: int, g: in
     return K, V
 
 
+def token_fields(pool: np.ndarray, chunk_bytes: int, Hkv: int, D: int, g: int, kb: int, vb: int,
+                 block_row: np.ndarray, n: int) -> dict:
+    """Raw fields of positions 0 .. n-1 of one sequence, every KV head:
+    codes kc, vc [Hkv][n][D]; scales ks, vs as fp32 bit patterns and zero
+    points kz, vz [Hkv][n][D/g] (quantised formats)."""
+    out = {k: [] for k in ("kc", "vc", "ks", "vs", "kz", "vz")}
+    for h in range(Hkv):
+        rows = {k: [] for k in out}
+        for lb in range(-(-n // BT)):
+            o = (int(block_row[lb]) * Hkv + h) * chunk_bytes
+            _, _, f = dequant_chunk(pool[o:o + chunk_bytes], D, g, kb, vb)
+            m = min(BT, n - lb * BT)
+            rows["kc"].append(f["kc"][:m])
+            rows["vc"].append(f["vc"][:m])
+            for k in ("ks", "vs", "kz", "vz"):
+                a = f[k].view(np.uint32) if k in ("ks", "vs") else f[k]
+                rows[k].append(a[:, :m].T)
+        for k in out:
+            out[k].append(np.concatenate(rows[k]) if rows[k] else np.zeros((0,), np.uint32))
+    return {k: np.stack(v) for k, v in out.items()}
+
+
 def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float, keep=None) -> np.ndarray:
     """Brute-force softmax attention, float64.
 

@@ -111,7 +111,7 @@ def test_seeded_random_appends_and_tiers_bit_exact():
                 r = TR._retier_both(h, hbt, nh, m, mbt, nm, tl, th, seed + 7 * it + 1, rng, frac=frac,
                                     boundaries=bool(rng.random() < 0.5))
                 TR._check_bit_exact(r)
-                h, hbt, nh, m, mbt, nm = r["dh"], r["dhb"], r["nh"], r["dm"], r["dmb"], r["nm"]
+                h, hbt, nh, m, mbt, nm = r["dh"], r["dhb"], r["ref"][2], r["dm"], r["dmb"], r["ref"][3]
 
 
 N_SCORES_KNORM = 120

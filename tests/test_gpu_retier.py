@@ -7,7 +7,8 @@ import torch
 
 from oracle import oracle as O
 from quantized_kv_cache_token_amd import inputs, lkv
-from tests.gpu_common import Pair, assert_attention_close, max_abs_vhat, say, sm_scale, to_f32_host
+from tests.gpu_common import (Pair, assert_attention_close, max_abs_vhat, max_abs_vhat_live, say, sm_scale,
+                              to_f32_host)
 from tests.oracle_cases import block_tables
 
 pytestmark = pytest.mark.gpu
@@ -108,7 +109,7 @@ def test_retier_bit_exact_then_decode(lens):
         say("retier", it, "counts", nh.tolist(), nm.tolist())
         r = _retier_both(h, hbt, nh, m, mbt, nm, tl, th, 92 + 10 * it, rng)
         _check_bit_exact(r)
-        h, hbt, nh, m, mbt, nm = r["dh"], r["dhb"], r["nh"], r["dm"], r["dmb"], r["nm"]
+        h, hbt, nh, m, mbt, nm = r["dh"], r["dhb"], r["ref"][2], r["dm"], r["dmb"], r["ref"][3]
     q = inputs.queries(95, len(lens), Hkv * G, D)
     views = [lkv.View(_dev(hbt), _dev(nh), int(max(nh.max(), 0))), lkv.View(_dev(mbt), _dev(nm), int(nm.max()))]
     say("decode the re-tiered segments")
@@ -215,3 +216,109 @@ def test_tier_and_retier_into_stale_pools():
     assert np.array_equal(ht.cpu().numpy(), ht_ref) and np.array_equal(mt.cpu().numpy(), mt_ref)
     assert dh.pool_equal(), dh.first_pool_mismatch()
     assert dm.pool_equal(), dm.first_pool_mismatch()
+
+
+def _grown(pair: Pair, bt, lens_now, lens_need, rng):
+    """A pair whose rows hold blocks for lens_need positions: the old blocks
+    (same bytes), then fresh blocks of stale random bytes (same on both
+    sides)."""
+    from tests.test_oracle_retier import grow_rows
+
+    big, bt2 = grow_rows(pair.ref, bt, lens_now, lens_need, rng)
+    p = Pair(D, g, pair.ref.k_bits, pair.ref.v_bits, pair.ref.num_kv_heads, big.num_blocks)
+    p.ref.pool[:] = big.pool
+    p.gpu.pool.copy_(torch.from_numpy(big.pool).cuda())
+    return p, bt2
+
+
+@pytest.mark.parametrize("lens", [[300, 65, 1, 0, 130], [5000, 2600]], ids=str)
+def test_retier_in_place_bit_exact(lens):
+    """Each segment compacted within its own blocks (the MID rows grown for
+    the demoted tokens), twice in a row: tiers, counts and whole pools
+    bit-exact with the oracle's in-place re-tier, then decode."""
+    Hkv, G = 2, 4
+    rng = np.random.default_rng(120)
+    say("in-place retier: first tiering", lens)
+    h, hbt, nh, m, mbt, nm, tl, th = _tiered(lens, Hkv, 121, rng)
+    for it in range(2):
+        m, mbt = _grown(m, mbt, nm, nm + nh, rng)
+        B = len(nh)
+        hs_stride, ms_stride = int(max(nh.max(), 1)) + 3, int(max(nm.max(), 1)) + 7
+        hs = _segment_scores(122 + it, nh, hs_stride, tl, th, 0.3, 0.4)
+        ms = _segment_scores(132 + it, nm, ms_stride, tl, th, 0.3, 0.4)
+        n_high = torch.zeros(B, dtype=torch.int32, device="cuda")
+        n_mid = torch.zeros_like(n_high)
+        ht = torch.full((B, hs_stride), 255, dtype=torch.uint8, device="cuda")
+        mt = torch.full((B, ms_stride), 255, dtype=torch.uint8, device="cuda")
+        hb, mb = _dev(hbt), _dev(mbt)
+        hv = lkv.View(hb, _dev(nh), int(nh.max()))
+        mv = lkv.View(mb, _dev(nm), int(nm.max()))
+        say("in-place retier", it, "counts", nh.tolist(), nm.tolist())
+        lkv.retier(h.gpu, hv, hs.cuda(), m.gpu, mv, ms.cuda(), tl, th, h.gpu, hb, m.gpu, mb, n_high, n_mid, ht, mt)
+        torch.cuda.synchronize()
+        t_h, t_m, nh_ref, nm_ref = O.retier(h.ref, hbt, nh, hs.numpy(), m.ref, mbt, nm, ms.numpy(), tl, th, h.ref,
+                                            hbt, m.ref, mbt)
+        assert np.array_equal(n_high.cpu().numpy(), nh_ref) and np.array_equal(n_mid.cpu().numpy(), nm_ref)
+        assert np.array_equal(ht.cpu().numpy(), t_h) and np.array_equal(mt.cpu().numpy(), t_m)
+        assert h.pool_equal(), h.first_pool_mismatch()
+        assert m.pool_equal(), m.first_pool_mismatch()
+        nh, nm = nh_ref, nm_ref
+    q = inputs.queries(125, len(lens), Hkv * G, D)
+    views = [lkv.View(_dev(hbt), _dev(nh), int(max(nh.max(), 0))), lkv.View(_dev(mbt), _dev(nm), int(nm.max()))]
+    say("decode the segments re-tiered in place")
+    got = lkv.decode_attn([h.gpu, m.gpu], views, q.cuda(), sm_scale(D), tl, 128).cpu().numpy()
+    want = O.decode([h.ref, m.ref], [hbt, mbt], [nh, nm], to_f32_host(q), sm_scale(D), tl, 128)
+    vmax = max(max_abs_vhat_live(h.ref, hbt, nh), max_abs_vhat_live(m.ref, mbt, nm))  # the pools hold stale bytes
+    assert_attention_close(got, want, vmax, f"in place {lens}")
+
+
+def test_tier_update_in_place_bit_exact():
+    """HIGH compacted within the K6V6 source's blocks, MID into new ones."""
+    Hkv, lens = 2, [900, 70, 4100]
+    rng = np.random.default_rng(140)
+    bt, nblk = block_tables(lens, rng)
+    src = Pair(D, g, 6, 6, Hkv, nblk)
+    K, V = zip(*[inputs.kv_rows(141, b, n, Hkv, D, dtype="bf16") for b, n in enumerate(lens)])
+    src.append(torch.cat(K), torch.cat(V), np.concatenate([[0], np.cumsum(lens)]).astype(np.int32),
+               np.zeros(len(lens), np.int32), bt)
+    stride = max(lens) + 1
+    tl, th = O.default_thresholds(stride)
+    scores = _segment_scores(142, lens, stride, tl, th, 0.2, 0.3)
+    mbt, mn = block_tables(lens, rng)
+    m = Pair(D, g, 6, 4, Hkv, mn)
+    _stale(m, 143)
+    nh = torch.zeros(len(lens), dtype=torch.int32, device="cuda")
+    nm = torch.zeros_like(nh)
+    tiers = torch.full((len(lens), stride), 255, dtype=torch.uint8, device="cuda")
+    sb = _dev(bt)
+    say("tier update in place")
+    lkv.tier_update(src.gpu, lkv.View(sb, _dev(lens), max(lens)), scores.cuda(), tl, th, src.gpu, sb, m.gpu,
+                    _dev(mbt), nh, nm, tiers)
+    torch.cuda.synchronize()
+    t_ref, nh_ref, nm_ref = O.tier_update(src.ref, bt, np.array(lens, np.int32), scores.numpy(), tl, th, src.ref, bt,
+                                          m.ref, mbt)
+    assert np.array_equal(tiers.cpu().numpy()[:, :max(lens)], t_ref[:, :max(lens)])
+    assert np.array_equal(nh.cpu().numpy(), nh_ref) and np.array_equal(nm.cpu().numpy(), nm_ref)
+    assert src.pool_equal(), src.first_pool_mismatch()
+    assert m.pool_equal(), m.first_pool_mismatch()
+
+
+def test_in_place_rejects_a_mismatched_row_width():
+    """A destination sharing a source's block table must also share its pool
+    and row width."""
+    Hkv = 1
+    rng = np.random.default_rng(150)
+    h, hbt, nh, m, mbt, nm, tl, th = _tiered([300, 100], Hkv, 151, rng)
+    hb, mb = _dev(hbt), _dev(mbt)
+    hs = torch.zeros((2, int(nh.max())), device="cuda")
+    ms = torch.zeros((2, int(nm.max())), device="cuda")
+    n_high = torch.zeros(2, dtype=torch.int32, device="cuda")
+    n_mid = torch.zeros_like(n_high)
+    ht = torch.zeros((2, int(nh.max())), dtype=torch.uint8, device="cuda")
+    mt = torch.zeros((2, int(nm.max())), dtype=torch.uint8, device="cuda")
+    hv = lkv.View(hb, _dev(nh), int(nh.max()))
+    mv = lkv.View(mb, _dev(nm), int(nm.max()))
+    with pytest.raises(lkv.LkvError):  # MID destination on HIGH's table
+        lkv.retier(h.gpu, hv, hs, m.gpu, mv, ms, tl, th, h.gpu, hb, m.gpu, hb, n_high, n_mid, ht, mt)
+    with pytest.raises(lkv.LkvError):  # HIGH's table with a narrower row width
+        lkv.retier(h.gpu, hv, hs, m.gpu, mv, ms, tl, th, h.gpu, hb[:, :1], m.gpu, mb, n_high, n_mid, ht, mt)

@@ -142,8 +142,10 @@ def test_scores_drive_the_tier_update():
     torch.cuda.synchronize()
     assert_scores_close(acc.cpu().numpy(), want_acc, "three steps")
     # the thresholds bound one head's weight at one step: tier on the mean
-    # weight per head and step (both sides read these same fp32 values)
-    scores = (acc[0] / (3 * Hkv * G)).contiguous()
+    # weight per head and step.  Both sides read the oracle's scores,
+    # rounded to fp32: no oracle input comes from the GPU
+    scores_h = np.ascontiguousarray(want_acc[0] / (3 * Hkv * G), np.float32)
+    scores = torch.from_numpy(scores_h).cuda()
     tl, th = lkv.default_thresholds(max(lens))
     hbt, hn = block_tables(lens, rng)
     mbt, mn = block_tables(lens, rng)
@@ -155,7 +157,7 @@ def test_scores_drive_the_tier_update():
     lkv.tier_update(src.gpu, view, scores, tl, th, h.gpu, torch.tensor(hbt).cuda(), m.gpu, torch.tensor(mbt).cuda(),
                     nh, nm, tiers)
     torch.cuda.synchronize()
-    t_ref, nh_ref, nm_ref = O.tier_update(src.ref, bt, np.array(lens, np.int32), scores.cpu().numpy(), tl, th,
+    t_ref, nh_ref, nm_ref = O.tier_update(src.ref, bt, np.array(lens, np.int32), scores_h, tl, th,
                                           h.ref, hbt, m.ref, mbt)
     assert np.array_equal(tiers.cpu().numpy(), t_ref)
     assert np.array_equal(nh.cpu().numpy(), nh_ref) and np.array_equal(nm.cpu().numpy(), nm_ref)

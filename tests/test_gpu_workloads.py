@@ -161,8 +161,11 @@ def test_workload3_tiered_sampled():
         assert_attention_close(out[b:b + 1], want, max(max_abs_vhat(rh), max_abs_vhat(rm)), f"workload 3 seq {b}")
         say("workload 3 oracle retier, sequence", b)
         rh2, rm2 = O.Cache(D, wl.group_size, 6, 6, Hkv, nb), O.Cache(D, wl.group_size, 6, 4, Hkv, nb)
-        ht_ref, mt_ref, nh2_ref, nm2_ref = O.retier(rh, rbt, nh_ref, hs[b:b + 1, :nh_ref[0]].numpy(), rm, rbt, nm_ref,
-                                                    ms[b:b + 1, :nm_ref[0]].numpy(), tl, th, rh2, rbt, rm2, rbt)
+        # the oracle's scores drawn from its own counts (the GPU's drew the same from equal counts)
+        hs_ref = inputs.tier_scores(wl.seed + 1, b, int(nh_ref[0]), tl, th).numpy()[None]
+        ms_ref = inputs.tier_scores(wl.seed + 2, b, int(nm_ref[0]), tl, th).numpy()[None]
+        ht_ref, mt_ref, nh2_ref, nm2_ref = O.retier(rh, rbt, nh_ref, hs_ref, rm, rbt, nm_ref, ms_ref, tl, th, rh2, rbt,
+                                                    rm2, rbt)
         assert nh2_h[b] == nh2_ref[0] and nm2_h[b] == nm2_ref[0]
         assert np.array_equal(ht2_h[b, :nh_ref[0]], ht_ref[0]) and np.array_equal(mt2_h[b, :nm_ref[0]], mt_ref[0])
         _chunks_equal(h2.pool, hbt[b].numpy(), rh2, rbt[0], int(nh2_h[b]), Hkv)

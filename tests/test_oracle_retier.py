@@ -118,3 +118,68 @@ def test_retier_rejects_a_destination_without_room():
     with pytest.raises(ValueError):
         O.retier(h, hbt, nh, hs, m, mbt, nm, ms, tl, th, small, np.zeros((1, 1), np.int32),
                  O.Cache(D, g, 6, 4, HKV, 8), np.arange(8, dtype=np.int32)[None])
+
+
+def grow_rows(cache, bt, lens_now, lens_need, rng):
+    """A copy of `cache` whose rows hold blocks for lens_need positions: the
+    row's blocks for lens_now positions, then fresh blocks appended to the
+    pool (filled with random bytes: stale data)."""
+    have = [-(-int(n) // 64) for n in lens_now]
+    need = [max(-(-int(n) // 64), h) for n, h in zip(lens_need, have)]
+    extra = sum(n - h for n, h in zip(need, have))
+    big = O.Cache(cache.head_dim, cache.group_size, cache.k_bits, cache.v_bits, cache.num_kv_heads,
+                  cache.num_blocks + extra)
+    big.pool[:cache.pool.size] = cache.pool
+    big.pool[cache.pool.size:] = rng.integers(0, 256, big.pool.size - cache.pool.size, dtype=np.uint8)
+    width = max(max(need), bt.shape[1], 1)
+    out = np.zeros((len(have), width), np.int32)
+    fresh = cache.num_blocks
+    for b, (h, n) in enumerate(zip(have, need)):
+        out[b, :h] = bt[b, :h]
+        out[b, h:n] = np.arange(fresh, fresh + n - h)
+        fresh += n - h
+    return big, out
+
+
+def _same_live(a, abt, b, bbt, lens, vb):
+    for r, n in enumerate(lens):
+        fa = R.token_fields(a.pool, a.chunk_bytes, HKV, D, g, 6, vb, abt[r], int(n))
+        fb = R.token_fields(b.pool, b.chunk_bytes, HKV, D, g, 6, vb, bbt[r], int(n))
+        for k in fa:
+            assert np.array_equal(fa[k], fb[k]), (r, k)
+
+
+def test_retier_in_place_equals_the_retier_into_new_blocks():
+    """Destinations that are the sources themselves (same pools, same block
+    tables; MID rows grown for the demoted tokens): tiers, counts and every
+    live token's codes, scales and zeros as the re-tier into fresh blocks."""
+    rng, h, hbt, nh, m, mbt, nm, tl, th = _tiered(5, [300, 1000, 65, 2100])
+    r = _retier(rng, h, hbt, nh, m, mbt, nm, tl, th)
+    h2 = O.Cache(D, g, 6, 6, HKV, h.num_blocks, pool=h.pool.copy())
+    m2, mbt2 = grow_rows(m, mbt, nm, nm + nh, rng)
+    ht, mt, n_h, n_m = O.retier(h2, hbt, nh, r["hs"], m2, mbt2, nm, r["ms"], tl, th, h2, hbt, m2, mbt2)
+    assert np.array_equal(n_h, r["nh"]) and np.array_equal(n_m, r["nm"])
+    assert np.array_equal(ht, r["ht"]) and np.array_equal(mt, r["mt"])
+    assert 0 < int(n_h.sum()) and int(n_m.sum()) > int(nm.sum()) // 2  # kept, demoted and evicted tokens
+    _same_live(h2, hbt, r["dh"], r["dhb"], n_h, 6)
+    _same_live(m2, mbt2, r["dm"], r["dmb"], n_m, 4)
+
+
+def test_tier_update_in_place_equals_the_update_into_new_blocks():
+    """HIGH compacted within the K6V6 source's own blocks."""
+    rng = np.random.default_rng(6)
+    lens = [500, 64, 1300]
+    K = [rng.standard_normal((n, HKV, D)).astype(np.float32) for n in lens]
+    V = [rng.standard_normal((n, HKV, D)).astype(np.float32) for n in lens]
+    src, sbt, lens = build_cache(K, V, D, g, 6, 6, rng=rng)
+    tl, th = O.default_thresholds(int(max(lens)))
+    sc = _scores(rng, lens, tl, th)
+    hbt, hn = block_tables(lens, rng)
+    mbt, mn = block_tables(lens, rng)
+    h, m = O.Cache(D, g, 6, 6, HKV, hn), O.Cache(D, g, 6, 4, HKV, mn)
+    t, nh, nm = O.tier_update(src, sbt, lens, sc, tl, th, h, hbt, m, mbt)
+    m2 = O.Cache(D, g, 6, 4, HKV, mn)
+    t2, nh2, nm2 = O.tier_update(src, sbt, lens, sc, tl, th, src, sbt, m2, mbt)
+    assert np.array_equal(t, t2) and np.array_equal(nh, nh2) and np.array_equal(nm, nm2)
+    assert np.array_equal(m.pool, m2.pool)
+    _same_live(src, sbt, h, hbt, nh, 6)

@@ -118,3 +118,20 @@ def test_margin_of_a_one_block_split():
     want = w / (tau * w.sum()) - 1.0
     assert np.allclose(margin[0, 0, 0, :50], want, rtol=1e-12, atol=1e-12)
     assert np.all(margin[0, 0, 0, 50:] == 0.0)
+
+
+def test_resolved_decode_accumulates_the_same_scores():
+    """The weights a resolved decode adds to score_acc are decode()'s: they
+    do not depend on the skip decisions."""
+    rng = np.random.default_rng(31)
+    lens = [300, 70]
+    K = [rng.standard_normal((n, 1, 64)).astype(np.float32) for n in lens]
+    V = [rng.standard_normal((n, 1, 64)).astype(np.float32) for n in lens]
+    cache, bt, lens = build_cache(K, V, 64, 32, 6, 4, rng=rng)
+    q = rng.standard_normal((2, 2, 64)).astype(np.float32)
+    a = np.zeros((1, 2, 320))
+    b = np.zeros((1, 2, 320))
+    O.decode([cache], [bt], [lens], q, 0.125, 0.02, 64, score_acc=a)
+    given = np.ones((2, 2, 1, bt.shape[1] * 64), np.uint8)  # every ambiguous pair skipped
+    O.decode_resolved([cache], [bt], [lens], q, 0.125, 0.02, 64, given, 0.5, score_acc=b)
+    assert np.array_equal(a, b) and a.sum() > 0
