@@ -630,6 +630,10 @@ def main():
         del S
         torch.cuda.empty_cache()
         secondary["tier_update"], secondary["retier"] = tier_figure(workloads.BY_INDEX[3], dev)
+    if args.workload in (2, 5) and not args.fp16_layer and not args.no_tier and not args.no_secondary:
+        S = None
+        torch.cuda.empty_cache()
+        secondary["serving_tiered"] = serving_figure(workloads.BY_INDEX[5], dev)
     if secondary:
         rec["secondary"] = secondary
     if not args.no_cpu_baseline and args.workload in (2, 4):
@@ -706,7 +710,154 @@ def tier_figure(wl, dev):
     retier = {"GB/s": round(nbytes / t / 1e9, 1), "us_per_call": round(t * 1e6, 1), "high": n_h2, "mid": n_m2,
               "evicted": n_h + n_m - n_h2 - n_m2,
               "counted": "HIGH/MID rows and their scores in, new HIGH/MID rows and tiers out"}
+    # the same re-tier in place, each segment compacted within its own
+    # blocks (one call: it consumes its input)
+    e0.record()
+    lkv.retier(hdst, hv, hs, mdst, mv, ms, tl, th, hdst, bt, mdst, bt, nh2, nm2, ht, mt, ws2)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3
+    retier["in_place_us_per_call"] = round(t * 1e6, 1)
+    retier["in_place_GB/s"] = round(nbytes / t / 1e9, 1)
+    assert int(nh2.sum()) == n_h2 and int(nm2.sum()) == n_m2
     return tier, retier
+
+
+def serving_figure(wl, dev, every=32, tl_rel=0.35, th_rel=1.9):
+    """The tiered serving loop at the ragged workload's shape: the cache is
+    prefilled at K6V6 (all HIGH); each step appends one row per sequence to
+    HIGH and decodes over HIGH + MID with the sparse-V skip, accumulating
+    every token's weight (lkv_decode_attn_scores); every `every` steps the
+    segments are re-tiered in place (lkv_retier with each destination its
+    own source) on the weights scaled per sequence to weight x live tokens
+    (1 = the uniform weight; tl_rel, th_rel on that scale).  Blocks come from
+    host free lists: HIGH blocks for the epoch's appends beforehand, MID rows
+    grown for every HIGH token before a re-tier, and the blocks past each new
+    length returned after it.  GPU time from HIP events around each epoch's
+    steps and around each re-tier; the wall time includes the host's block
+    bookkeeping and the synchronisation that reads the new counts."""
+    import numpy as np
+    import torch
+
+    from quantized_kv_cache_token_amd import inputs, lkv
+
+    B, Hq, Hkv, D = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    steps = wl.steps
+    blocks = lambda n: -(-int(n) // 64)
+    lens = inputs.ragged_lengths(wl.seed, B, *wl.ragged).numpy().astype(np.int64)
+    width = blocks(lens.max() + steps) + 1
+    nh_pool = int(sum(blocks(n) for n in lens)) + B * (blocks(steps) + 1)
+    nm_pool = int(sum(blocks(n + steps) for n in lens)) + B
+    h = lkv.Cache(D, wl.group_size, 6, 6, Hkv, nh_pool, device=dev)
+    m = lkv.Cache(D, wl.group_size, 6, 4, Hkv, nm_pool, device=dev)
+    free_h, free_m = list(range(nh_pool - 1, -1, -1)), list(range(nm_pool - 1, -1, -1))
+    hbt = np.zeros((B, width), np.int32)
+    mbt = np.zeros((B, width), np.int32)
+    for b in range(B):
+        for i in range(blocks(lens[b])):
+            hbt[b, i] = free_h.pop()
+    hb, mb = torch.tensor(hbt, device=dev), torch.tensor(mbt, device=dev)
+    outl = inputs.outlier_channels(wl.seed, Hkv, D)
+    for b in range(B):
+        k, v = inputs.kv_rows(wl.seed, b, int(lens[b]), Hkv, D, dtype=wl.dtype, outliers=outl, device=dev)
+        lkv.quant_append(h, k, v, torch.tensor([0, int(lens[b])], dtype=torch.int32, device=dev),
+                         torch.zeros(1, dtype=torch.int32, device=dev), hb[b:b + 1].contiguous(), int(lens[b]))
+        del k, v
+    hl, ml = lens.astype(np.int32), np.zeros(B, np.int32)
+    stride = int(lens.max()) + steps + 64
+    acc = torch.zeros((2, B, stride), dtype=torch.float32, device=dev)
+    out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
+    cu1 = torch.arange(B + 1, dtype=torch.int32, device=dev)
+    sm = float(np.float32(1.0 / np.sqrt(D)))
+    tau = lkv.default_thresholds(int(lens.max()))[0]
+    rows = [inputs.kv_rows(wl.seed, 7000, B, Hkv, D, dtype=wl.dtype, outliers=outl, step=s + 1, device=dev)
+            for s in range(every)]
+    qs = [inputs.queries(wl.seed, B, Hq, D, dtype=wl.dtype, step=s, device=dev) for s in range(every)]
+    n_high = torch.zeros(B, dtype=torch.int32, device=dev)
+    n_mid = torch.zeros_like(n_high)
+    torch.cuda.synchronize()
+    step_ms, retier_ms, live, growth, recycled = [], [], [], [], 0
+    freed_h, freed_m = set(), set()
+    t0 = time.perf_counter()
+    done = 0
+    while done < steps:
+        n = min(every, steps - done)
+        for b in range(B):  # HIGH blocks for this epoch's rows
+            for i in range(blocks(hl[b]), blocks(hl[b] + n)):
+                hbt[b, i] = free_h.pop()
+                recycled += int(hbt[b, i]) in freed_h
+        hb.copy_(torch.from_numpy(hbt))
+        pos = [torch.tensor(hl + s, device=dev) for s in range(n)]
+        hlen = [torch.tensor(hl + s + 1, device=dev) for s in range(n)]
+        mlen = torch.tensor(ml, device=dev)
+        views = [[lkv.View(hb, hlen[s], int(hl.max()) + s + 1, int(hl.sum()) + B * (s + 1)),
+                  lkv.View(mb, mlen, max(int(ml.max()), 1), int(ml.sum()))] for s in range(n)]
+        split = lkv.decode_plan([h, m], views[-1], B, Hq)
+        ws = lkv.decode_scores_workspace([h, m], views[-1], B, Hq, split, dev)
+        calls = []
+        for s in range(n):
+            k, v = rows[s]
+            calls.append(lkv.prepare_append(h, k, v, cu1, pos[s], hb, 1))
+            calls.append(lkv.prepare_decode_scores([h, m], views[s], qs[s], sm, tau, split, out, acc, ws))
+        e0, e1, e2 = _event(), _event(), _event()
+        e0.record()
+        for c in calls:
+            c()
+        e1.record()
+        hl = hl + n
+        done += n
+        # re-tier in place on the epoch's weights
+        scale = torch.tensor((hl + ml).astype(np.float64) / (n * Hq), dtype=torch.float32, device=dev)
+        rel = acc * scale[None, :, None]
+        hs = rel[0, :, :max(int(hl.max()), 1)].contiguous()
+        ms = rel[1, :, :max(int(ml.max()), 1)].contiguous()
+        grown = 0
+        for b in range(B):
+            for i in range(blocks(ml[b]), blocks(ml[b] + hl[b])):
+                mbt[b, i] = free_m.pop()
+                recycled += int(mbt[b, i]) in freed_m
+                grown += 1
+        mb.copy_(torch.from_numpy(mbt))
+        ht = torch.empty(hs.shape, dtype=torch.uint8, device=dev)
+        mt = torch.empty(ms.shape, dtype=torch.uint8, device=dev)
+        hv = lkv.View(hb, torch.tensor(hl, device=dev), int(hl.max()))
+        mv = lkv.View(mb, torch.tensor(ml, device=dev), max(int(ml.max()), 1))
+        ws2 = torch.empty(lkv.retier_workspace_bytes(B, hs.shape[1], ms.shape[1]), dtype=torch.uint8, device=dev)
+        e1b = _event()
+        e1b.record()
+        lkv.retier(h, hv, hs, m, mv, ms, tl_rel, th_rel, h, hb, m, mb, n_high, n_mid, ht, mt, ws2)
+        e2.record()
+        nh, nm = n_high.cpu().numpy(), n_mid.cpu().numpy()  # synchronises
+        if (nh < 0).any() or (nm < 0).any():
+            raise RuntimeError("serving loop: a re-tier found no room")
+        step_ms.append(e0.elapsed_time(e1) / n)
+        retier_ms.append(e1b.elapsed_time(e2))
+        live.append(int(hl.sum() + ml.sum()))
+        growth.append(grown)
+        for b in range(B):
+            for blk in hbt[b, blocks(nh[b]):blocks(hl[b])]:
+                free_h.append(int(blk))
+                freed_h.add(int(blk))
+            for blk in mbt[b, blocks(nm[b]):blocks(ml[b] + hl[b])]:
+                free_m.append(int(blk))
+                freed_m.add(int(blk))
+        hl, ml = nh.astype(np.int32), nm.astype(np.int32)
+        acc.zero_()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_s = (sum(x * every for x in step_ms[:-1]) + step_ms[-1] * (steps - every * (len(step_ms) - 1)) +
+             sum(retier_ms)) / 1e3
+    return {"workload": wl.name + "_tiered", "steps": steps, "retier_every": every, "retier_in_place": True,
+            "tau_rel": [tl_rel, th_rel], "tau_skip": tau,
+            "decode_step_us": [round(x * 1e3, 1) for x in step_ms],
+            "retier_us": [round(x * 1e3, 1) for x in retier_ms],
+            "tokens_per_s_gpu": round(B * steps / gpu_s, 1), "tokens_per_s_wall": round(B * steps / wall, 1),
+            "live_tokens_at_retier": live, "final_high_mid": [int(hl.sum()), int(ml.sum())],
+            "mid_blocks_grown_per_retier": growth, "recycled_blocks_taken": recycled,
+            "blocks_in_use_after": [nh_pool - len(free_h), nm_pool - len(free_m)],
+            "pool_blocks": [nh_pool, nm_pool],
+            "timing": "hip events around each epoch's append+decode launches and each re-tier; wall includes "
+                      "host block bookkeeping and the count read-back"}
 
 
 def cpu_baseline(wl, kb, vb, nseq, per_token_head, q_bytes, min_seconds):

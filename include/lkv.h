@@ -324,10 +324,11 @@ void lkv_default_thresholds(int32_t n_tokens, float* tau_low, float* tau_high);
 
 /* Workspace bytes of lkv_tier_update (host): (HIGH, MID) int32 counts per
  * 2048-token scan chunk of each sequence, then the (HIGH, MID) destination
- * positions of every 64-token block of each sequence:
- * batch * (ceil(scores_stride / 2048) + ceil(scores_stride / 64)) * 8 bytes
- * (each ceil at least 1).  The workspace must be 8-byte aligned; its contents
- * need no initialisation. */
+ * positions of every 64-token block of each sequence, then 8 bytes and a
+ * uint32 per 64-token block of each sequence for in-place compaction:
+ * batch * (ceil(scores_stride / 2048) + ceil(scores_stride / 64)) * 8 + 8
+ * + batch * ceil(scores_stride / 64) * 4 bytes (each ceil at least 1).  The
+ * workspace must be 8-byte aligned; its contents need no initialisation. */
 int64_t lkv_tier_workspace_bytes(int32_t batch, int32_t scores_stride);
 
 /* Attention-aware tier update (Super KV Compression page, second layer).
@@ -350,7 +351,7 @@ int64_t lkv_tier_workspace_bytes(int32_t batch, int32_t scores_stride);
  * at positions 0 .. n_high-1 of src's own blocks, the blocks of a row past
  * ceil(n_high / 64) hold no live token and may be reused, and the slots past
  * n_high keep stale codes.  Otherwise no destination block may be one src
- * uses; dst_m never shares src's block table (LKV_EINVAL). */
+ * uses; dst_m with src's pool and block table is LKV_EINVAL. */
 int lkv_tier_update(const lkv_cache* src, const lkv_view* src_view,
                     const float* scores, int32_t scores_stride, float tau_low, float tau_high,
                     const lkv_cache* dst_h, const int32_t* h_block_table, int32_t h_max_blocks,
@@ -360,9 +361,11 @@ int lkv_tier_update(const lkv_cache* src, const lkv_view* src_view,
 
 /* Workspace bytes of lkv_retier (host): the (HIGH, MID) int32 counts of
  * every 2048-token scan chunk and the (HIGH, MID) destination positions of
- * every 64-token block, of both segments:
+ * every 64-token block, of both segments, then the in-place compaction's
+ * 8 bytes and uint32 per 64-token block of the longer segment:
  * batch * (ceil(h_stride / 2048) + ceil(m_stride / 2048) + ceil(h_stride / 64)
- * + ceil(m_stride / 64)) * 8 bytes (each ceil at least 1).  8-byte aligned;
+ * + ceil(m_stride / 64)) * 8 + 8 + batch * max(ceil(h_stride / 64),
+ * ceil(m_stride / 64)) * 4 bytes (each ceil at least 1).  8-byte aligned;
  * its contents need no initialisation. */
 int64_t lkv_retier_workspace_bytes(int32_t batch, int32_t h_stride, int32_t m_stride);
 
@@ -394,11 +397,11 @@ int64_t lkv_retier_workspace_bytes(int32_t batch, int32_t h_stride, int32_t m_st
  * must hold valid blocks for n_mid positions, at most m_len + h_len: the
  * demoted tokens follow the kept MID ones.  Afterwards the blocks of a row
  * past ceil(n / 64) hold no live token and may go back to a free list; the
- * slots past n keep stale codes.  In-place compaction walks each (sequence,
- * KV head) in one workgroup, so it trades speed for memory.  Any other
+ * slots past n keep stale codes.  Any other
  * overlap between destination blocks and the blocks a source uses is not
- * allowed; dst_h sharing m's block table or dst_m sharing h's is
- * LKV_EINVAL. */
+ * allowed; dst_h with m's pool and block table, or dst_m with h's, is
+ * LKV_EINVAL.  (A block table shared between different pools names
+ * different blocks and is no overlap.) */
 int lkv_retier(const lkv_cache* h, const lkv_view* h_view, const float* h_scores, int32_t h_stride,
                const lkv_cache* m, const lkv_view* m_view, const float* m_scores, int32_t m_stride,
                float tau_low, float tau_high,

@@ -577,20 +577,13 @@ bool sources_ready(const TierSource* s, int n)
     return true;
 }
 
-}  // namespace
-
-extern "C" {
-
-}  // extern "C"
-
-namespace {
-
-// A destination that shares its source's block table is that segment
-// compacted in place: the same pool and the same row width.
-bool aliasing_ok(const TierSource* s, int nsrc, const TierDest& d)
+// A destination with a source's pool and block table is that segment
+// compacted in place: only source `own` may be (-1: none), with the same
+// row width.  A table shared between different pools names different blocks.
+bool aliasing_ok(const TierSource* s, int nsrc, const TierDest& d, int own)
 {
     for (int i = 0; i < nsrc; i++)
-        if (d.block_table == s[i].block_table && (d.pool != s[i].pool || d.max_blocks != s[i].max_blocks))
+        if (d.pool == s[i].pool && d.block_table == s[i].block_table && (i != own || d.max_blocks != s[i].max_blocks))
             return false;
     return true;
 }
@@ -615,8 +608,7 @@ int lkv_tier_update(const lkv_cache* src, const lkv_view* src_view, const float*
     if ((int64_t)workspace_bytes < lkv_tier_workspace_bytes(batch, scores_stride)) return LKV_EINVAL;
     if (batch == 0) return LKV_OK;
     if (!sources_ready(&s, 1) || !h_block_table || !m_block_table || !n_high || !n_mid || !workspace ||
-        (uintptr_t)workspace % 8 != 0 || !aliasing_ok(&s, 1, h) || !aliasing_ok(&s, 1, m) ||
-        m.block_table == s.block_table)
+        (uintptr_t)workspace % 8 != 0 || !aliasing_ok(&s, 1, h, 0) || !aliasing_ok(&s, 1, m, -1))
         return LKV_EINVAL;
     const hipError_t e = launch_tiering(&s, 1, tau_low, tau_high, h, m, n_high, n_mid, batch, workspace,
                                         (hipStream_t)stream);
@@ -642,8 +634,7 @@ int lkv_retier(const lkv_cache* h, const lkv_view* h_view, const float* h_scores
     if (need < 0 || (int64_t)workspace_bytes < need) return LKV_EINVAL;
     if (batch == 0) return LKV_OK;
     if (!sources_ready(s, 2) || !dh_block_table || !dm_block_table || !n_high || !n_mid || !workspace ||
-        (uintptr_t)workspace % 8 != 0 || !aliasing_ok(s, 2, dh) || !aliasing_ok(s, 2, dm) ||
-        dh.block_table == s[0].block_table || dm.block_table == s[1].block_table)
+        (uintptr_t)workspace % 8 != 0 || !aliasing_ok(s, 2, dh, 1) || !aliasing_ok(s, 2, dm, 0))
         return LKV_EINVAL;
     const hipError_t e = launch_tiering(s, 2, tau_low, tau_high, dh, dm, n_high, n_mid, batch, workspace,
                                         (hipStream_t)stream);

@@ -178,15 +178,17 @@ inline int32_t tier_blocks(int32_t stride) { return stride > 0 ? (stride + BT - 
 
 // The (HIGH, MID) int32 counts of every scan chunk of every source, then
 // the (HIGH, MID) destination positions of every 64-token block of every
-// source.
+// source, then (in-place compaction) a ticket counter padded to 8 bytes and
+// a uint32 read count per 64-token block of the longest source.
 inline int64_t tiering_workspace_bytes(int32_t batch, const int32_t* strides, int nsrc)
 {
-    int64_t chunks = 0, blocks = 0;
+    int64_t chunks = 0, blocks = 0, widest = 0;
     for (int i = 0; i < nsrc; i++) {
         chunks += tier_chunks(strides[i]);
         blocks += tier_blocks(strides[i]);
+        widest = tier_blocks(strides[i]) > widest ? tier_blocks(strides[i]) : widest;
     }
-    return (int64_t)batch * (chunks + blocks) * 8;
+    return (int64_t)batch * (chunks + blocks) * 8 + 8 + (int64_t)batch * widest * 4;
 }
 
 }  // namespace lkv

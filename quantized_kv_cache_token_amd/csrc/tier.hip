@@ -16,13 +16,16 @@
 //    sequence, source).  Each source chunk is read once, whole and
 //    coalesced; its survivors go to consecutive destination positions.
 //    A destination that is its source segment itself (the same pool and
-//    block table) is compacted in place: then one workgroup walks a
-//    sequence's chunks of one KV head in order.  A survivor never moves to
-//    a later position and a chunk is read whole before anything is written
-//    into its block, so every chunk is read before it is overwritten; and
-//    the sources run one launch after the other, in destination order, so
-//    that the MID source's chunks are read before demoted tokens land in
-//    them.  K
+//    block table) is compacted in place.  A survivor never moves to a later
+//    position, so a chunk's survivors land in its own block or earlier
+//    ones.  Then each workgroup moves one chunk: it takes the chunk from a
+//    ticket counter (chunks of a sequence in order, its KV heads together),
+//    reads it whole, marks it read, and waits until every chunk whose block
+//    it writes into has been marked read by all KV heads.  Those chunks hold
+//    earlier tickets, taken by workgroups that are running or done and that
+//    mark their chunk before they wait for anything, so the wait ends.  The
+//    sources run one launch after the other, in destination order, so that
+//    the MID source's chunks are read before demoted tokens land in them.  K
 //    rows, scales and zeros are stored straight from the loaded pieces; V
 //    codes are copied (same width) or dequantised in fp32 and requantised
 //    at 4 bits (V6 -> V4) into an LDS block of destination codes, which is
@@ -210,7 +213,15 @@ struct MoveArgs {
     const int32_t* n_high;
     const int32_t* n_mid;
     int32_t nsrc;
-    int32_t per_wg;  // source chunks per workgroup (all of a sequence's when compacting in place)
+    int32_t per_wg;  // source chunks per workgroup
+    // in place (flags != nullptr): one source, one chunk per workgroup taken
+    // from *ticket; flags[b][c] counts the KV heads that have read chunk c;
+    // inplace_seg is the destination (0 HIGH, 1 MID) that is the source
+    uint32_t* ticket;
+    uint32_t* flags;
+    int32_t flag_stride;
+    int32_t inplace_seg;
+    int32_t gx;      // chunks per sequence in the ticket order
 };
 
 __device__ __forceinline__ uint8_t* dst_chunk(const MoveDst& d, int b, int pos, int kvh)
@@ -331,13 +342,29 @@ __global__ __launch_bounds__(256) void tier_move_kernel(MoveArgs a)
     __shared__ uint8_t stage[2][D][VPITCH];      // destination codes of the current HIGH / MID block
     __shared__ uint8_t src_of[4][2][BT];         // per wave: source slot of each survivor rank
 
-    const int si = blockIdx.z % a.nsrc, b = blockIdx.z / a.nsrc, kvh = blockIdx.y;
+    __shared__ int ticket_of;
+    const bool in_place = a.flags != nullptr;
+    int si, b, kvh, bx;
+    if (in_place) {  // every workgroup takes a ticket before anything else
+        if (threadIdx.x == 0) ticket_of = (int)atomicAdd(a.ticket, 1u);
+        __syncthreads();
+        const int t = ticket_of, H = a.src[0].f.H;
+        si = 0;
+        kvh = t % H;
+        bx = t / H % a.gx;
+        b = t / H / a.gx;
+    } else {
+        si = blockIdx.z % a.nsrc;
+        b = blockIdx.z / a.nsrc;
+        kvh = blockIdx.y;
+        bx = blockIdx.x;
+    }
     if (a.n_high[b] < 0 || a.n_mid[b] < 0) return;  // no room: nothing is written
     const MoveSrc& S = si == 0 ? a.src[0] : a.src[1];
     const Fmt& fs = S.f;
     const int len = max(0, min(S.lens[b], S.len_cap));
     const int nblocks = (len + BT - 1) / BT;
-    const int c0 = blockIdx.x * a.per_wg;
+    const int c0 = bx * a.per_wg;
     if (c0 >= nblocks) return;
     const int c1 = min(nblocks, c0 + a.per_wg);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -380,6 +407,27 @@ __global__ __launch_bounds__(256) void tier_move_kernel(MoveArgs a)
     load_pieces(pn, brow[c0]);
     int t_next = tiers_of(c0);
     int blk_after = c0 + 1 < c1 ? brow[c0 + 1] : 0;
+    if (in_place) {
+        // The chunk (per_wg is 1) is read once every thread's loads have
+        // returned their data: an empty statement that takes each loaded
+        // register makes the compiler wait for them.  Only then is it marked
+        // read.  The order needed is a load's return before another
+        // workgroup's store to the same bytes, so no cache writeback or
+        // invalidation is involved: the mark and its polling are relaxed
+        // device-scope atomics.  Then wait for the chunks of the blocks this
+        // one writes into, first / 64 .. c0 - 1, read by every KV head.
+#pragma unroll
+        for (int k = 0; k < MOVE_PIECES; k++)
+            asm volatile("" ::"v"(pn[k].x), "v"(pn[k].y), "v"(pn[k].z), "v"(pn[k].w) : "memory");
+        __syncthreads();
+        uint32_t* frow = a.flags + (int64_t)b * a.flag_stride;
+        if (tid == 0) __hip_atomic_fetch_add(frow + c0, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t heads = (uint32_t)fs.H;
+        for (int j = (a.inplace_seg == 0 ? base.x : base.y) / BT + tid; j < c0; j += 256)
+            while (__hip_atomic_load(frow + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < heads)
+                __builtin_amdgcn_s_sleep(2);
+        __syncthreads();
+    }
     for (int c = c0; c < c1; c++) {
         uint4 pc[MOVE_PIECES];
 #pragma unroll
@@ -516,7 +564,7 @@ hipError_t launch_tiering(const TierSource* src, int nsrc, float tau_low, float 
         TierSrc& s = t.src[i];
         s.scores = src[i].scores;
         s.stride = src[i].stride;
-        s.len_cap = min(src[i].stride, src[i].max_blocks * BT);
+        s.len_cap = src[i].max_len;  // lengths above max_len read as max_len (max_len <= stride, validated)
         s.lens = src[i].view_lens;
         s.tiers = src[i].tiers;
         s.max_tier = src[i].max_tier;
@@ -561,27 +609,45 @@ hipError_t launch_tiering(const TierSource* src, int nsrc, float tau_low, float 
     a.n_mid = n_mid;
     a.nsrc = nsrc;
     a.per_wg = MOVE_CHUNKS;
+    // the destination segment (0 HIGH, 1 MID) that is source i itself, or -1
+    int own[2] = {-1, -1};
     bool in_place = false;
-    for (int i = 0; i < nsrc; i++)
-        for (const TierDest* d : {&h, &m})
-            in_place |= d->pool == src[i].pool && d->block_table == src[i].block_table;
-    auto launch = [&](const MoveArgs& x, int nz) {
-        const dim3 grid((unsigned)((max_blocks + x.per_wg - 1) / x.per_wg), (unsigned)h.f.H, (unsigned)(batch * nz));
+    for (int i = 0; i < nsrc; i++) {
+        if (h.pool == src[i].pool && h.block_table == src[i].block_table) own[i] = 0;
+        if (m.pool == src[i].pool && m.block_table == src[i].block_table) own[i] = 1;
+        in_place |= own[i] >= 0;
+    }
+    auto launch = [&](const MoveArgs& x, dim3 grid) {
         if (h.f.D == 64) hipLaunchKernelGGL(tier_move_kernel<64>, grid, dim3(256), 0, stream, x);
         else hipLaunchKernelGGL(tier_move_kernel<128>, grid, dim3(256), 0, stream, x);
     };
     if (!in_place) {
-        launch(a, nsrc);
+        launch(a, dim3((unsigned)((max_blocks + MOVE_CHUNKS - 1) / MOVE_CHUNKS), (unsigned)h.f.H,
+                       (unsigned)(batch * nsrc)));
         return hipGetLastError();
     }
-    // in place: a sequence's chunks of one KV head in order, one source per
-    // launch in destination order
+    // one source per launch, in destination order; a source compacted in
+    // place moves one chunk per workgroup in ticket order
+    uint32_t* ticket = (uint32_t*)(bases + (int64_t)batch * base_total);
+    uint32_t* flags = ticket + 2;
     for (int i = 0; i < nsrc; i++) {
         MoveArgs one = a;
         one.src[0] = a.src[i];
         one.nsrc = 1;
-        one.per_wg = max(max_blocks, 1);
-        launch(one, 1);
+        if (own[i] < 0) {
+            launch(one, dim3((unsigned)((max_blocks + MOVE_CHUNKS - 1) / MOVE_CHUNKS), (unsigned)h.f.H,
+                             (unsigned)batch));
+        } else {
+            const int32_t gx = max(1, (src[i].max_len + BT - 1) / BT);
+            if ((e = launch_fill_u32(ticket, 2 + (int64_t)batch * gx, 0u, stream)) != hipSuccess) return e;
+            one.per_wg = 1;
+            one.ticket = ticket;
+            one.flags = flags;
+            one.flag_stride = gx;
+            one.inplace_seg = own[i];
+            one.gx = gx;
+            launch(one, dim3((unsigned)((int64_t)gx * h.f.H * batch)));
+        }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;

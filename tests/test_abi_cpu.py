@@ -140,10 +140,39 @@ def test_tier_update_rejects_bad_formats():
     assert call(stride=512) == lkv.EINVAL                      # scores shorter than max_len
     assert call(ws=100) == lkv.EINVAL
     # (HIGH, MID) int32 counts per 2048-token scan chunk, then (HIGH, MID)
-    # destination positions per 64-token block
-    assert L.lkv_tier_workspace_bytes(8, 32768) == 8 * (16 + 512) * 8
-    assert L.lkv_tier_workspace_bytes(2, 300) == 2 * (1 + 5) * 8
-    assert L.lkv_tier_workspace_bytes(1, 0) == 1 * (1 + 1) * 8
+    # destination positions per 64-token block, then a ticket (8 bytes) and a
+    # uint32 read count per 64-token block for in-place compaction
+    assert L.lkv_tier_workspace_bytes(8, 32768) == 8 * (16 + 512) * 8 + 8 + 8 * 512 * 4
+    assert L.lkv_tier_workspace_bytes(2, 300) == 2 * (1 + 5) * 8 + 8 + 2 * 5 * 4
+    assert L.lkv_tier_workspace_bytes(1, 0) == 1 * (1 + 1) * 8 + 8 + 1 * 1 * 4
+
+
+def test_in_place_tiering_needs_its_own_segment_and_row_width():
+    """A destination with a source's pool and block table compacts that
+    source in place: only its own segment, read with the source's row
+    width; anything else is rejected before a launch."""
+    L = lkv.lib()
+    p = C.c_void_p(0x90000)
+    h, m = _cache(v_bits=6, pool=0x11000), _cache(v_bits=4, pool=0x12000)
+    hv = lkv._View(0x20000, 0x30000, 16, 1024, 0)
+    mv = lkv._View(0x21000, 0x31000, 16, 1024, 0)
+
+    def retier(dh=h, dh_bt=0x90000, dh_w=16, dm=m, dm_bt=0x91000, dm_w=16):
+        return L.lkv_retier(C.byref(h), C.byref(hv), p, 1024, C.byref(m), C.byref(mv), p, 1024, 1e-6, 1e-4,
+                            C.byref(dh), C.c_void_p(dh_bt), dh_w, C.byref(dm), C.c_void_p(dm_bt), dm_w, p, p, p, p,
+                            8, p, 1 << 22, None)
+
+    assert retier(dh_bt=0x20000, dh_w=8) == lkv.EINVAL                         # HIGH in place, narrower rows
+    assert retier(dm_bt=0x21000, dm_w=32) == lkv.EINVAL                        # MID in place, wider rows
+    assert retier(dh=_cache(v_bits=6, pool=0x12000), dh_bt=0x21000) == lkv.EINVAL  # HIGH onto MID's blocks
+    assert retier(dm=_cache(v_bits=4, pool=0x11000), dm_bt=0x20000) == lkv.EINVAL  # MID onto HIGH's blocks
+
+    def tier(dh=h, dh_bt=0x90000, dh_w=16, dm=m, dm_bt=0x91000):
+        return L.lkv_tier_update(C.byref(h), C.byref(hv), p, 1024, 1e-6, 1e-4, C.byref(dh), C.c_void_p(dh_bt),
+                                 dh_w, C.byref(dm), C.c_void_p(dm_bt), 16, p, p, p, 8, p, 1 << 20, None)
+
+    assert tier(dh_bt=0x20000, dh_w=4) == lkv.EINVAL
+    assert tier(dm=_cache(v_bits=4, pool=0x11000), dm_bt=0x20000) == lkv.EINVAL  # MID onto the source's blocks
 
 
 def test_retier_rejects_bad_formats():
@@ -165,8 +194,8 @@ def test_retier_rejects_bad_formats():
     assert call(ws=100) == lkv.EINVAL
     # (HIGH, MID) counts per 2048-token chunk and destination positions per
     # 64-token block, of each segment
-    assert L.lkv_retier_workspace_bytes(8, 32768, 4096) == 8 * (16 + 2 + 512 + 64) * 8
-    assert L.lkv_retier_workspace_bytes(2, 300, 0) == 2 * (1 + 1 + 5 + 1) * 8
+    assert L.lkv_retier_workspace_bytes(8, 32768, 4096) == 8 * (16 + 2 + 512 + 64) * 8 + 8 + 8 * 512 * 4
+    assert L.lkv_retier_workspace_bytes(2, 300, 0) == 2 * (1 + 1 + 5 + 1) * 8 + 8 + 2 * 5 * 4
     assert L.lkv_retier_workspace_bytes(-1, 1, 1) == lkv.EINVAL
 
 

@@ -304,8 +304,8 @@ def test_tier_update_in_place_bit_exact():
 
 
 def test_in_place_rejects_a_mismatched_row_width():
-    """A destination sharing a source's block table must also share its pool
-    and row width."""
+    """A destination with a source's pool and block table (in place) must
+    read the table with the source's row width."""
     Hkv = 1
     rng = np.random.default_rng(150)
     h, hbt, nh, m, mbt, nm, tl, th = _tiered([300, 100], Hkv, 151, rng)
@@ -318,7 +318,9 @@ def test_in_place_rejects_a_mismatched_row_width():
     mt = torch.zeros((2, int(nm.max())), dtype=torch.uint8, device="cuda")
     hv = lkv.View(hb, _dev(nh), int(nh.max()))
     mv = lkv.View(mb, _dev(nm), int(nm.max()))
-    with pytest.raises(lkv.LkvError):  # MID destination on HIGH's table
-        lkv.retier(h.gpu, hv, hs, m.gpu, mv, ms, tl, th, h.gpu, hb, m.gpu, hb, n_high, n_mid, ht, mt)
-    with pytest.raises(lkv.LkvError):  # HIGH's table with a narrower row width
+    # each source's own table (same address) read with a narrower row width:
+    # rejected before any launch
+    with pytest.raises(lkv.LkvError):
         lkv.retier(h.gpu, hv, hs, m.gpu, mv, ms, tl, th, h.gpu, hb[:, :1], m.gpu, mb, n_high, n_mid, ht, mt)
+    with pytest.raises(lkv.LkvError):
+        lkv.retier(h.gpu, hv, hs, m.gpu, mv, ms, tl, th, h.gpu, hb, m.gpu, mb[:, :1], n_high, n_mid, ht, mt)
