@@ -65,6 +65,8 @@ def parse():
                    help="skip every secondary figure but the prefill append (counter passes: only the step's kernels run)")
     p.add_argument("--graph", action="store_true",
                    help="replay each step as a captured HIP graph instead of launching its kernels from the host")
+    p.add_argument("--tier-only", action="store_true",
+                   help="only the tier-update and re-tier figures at the tiered workload's shape (profiling)")
     p.add_argument("--unfused", action="store_true",
                    help="three launches per step: the append kernel, the split kernel, the merge")
     return p.parse_args()
@@ -485,6 +487,10 @@ def main():
     wl = workloads.BY_INDEX[args.workload]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.tier_only:
+        tier, retier = tier_figure(workloads.BY_INDEX[3], dev)
+        print(json.dumps({"tier_update": tier, "retier": retier}), flush=True)
+        return
     # one stream (default priority) for every prepared call and graph
     run_stream = torch.cuda.Stream(device=dev)
     with torch.cuda.stream(run_stream):
