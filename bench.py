@@ -65,6 +65,8 @@ def parse():
                    help="skip every secondary figure but the prefill append (counter passes: only the step's kernels run)")
     p.add_argument("--graph", action="store_true",
                    help="replay each step as a captured HIP graph instead of launching its kernels from the host")
+    p.add_argument("--probe-only", action="store_true",
+                   help="only the HBM read probe (a streaming read of 4 GiB; profiling)")
     p.add_argument("--tier-only", action="store_true",
                    help="only the tier-update and re-tier figures at the tiered workload's shape (profiling)")
     p.add_argument("--unfused", action="store_true",
@@ -491,6 +493,9 @@ def main():
         tier, retier = tier_figure(workloads.BY_INDEX[3], dev)
         print(json.dumps({"tier_update": tier, "retier": retier}), flush=True)
         return
+    if args.probe_only:
+        print(json.dumps({"hbm_read_probe": probe_figure(dev)}), flush=True)
+        return
     # one stream (default priority) for every prepared call and graph
     run_stream = torch.cuda.Stream(device=dev)
     with torch.cuda.stream(run_stream):
@@ -640,6 +645,8 @@ def main():
         S = None
         torch.cuda.empty_cache()
         secondary["serving_tiered"] = serving_figure(workloads.BY_INDEX[5], dev)
+    if not args.no_secondary:
+        secondary["hbm_read_probe"] = probe_figure(dev)
     if secondary:
         rec["secondary"] = secondary
     if not args.no_cpu_baseline and args.workload in (2, 4):
@@ -727,6 +734,33 @@ def tier_figure(wl, dev):
     retier["in_place_GB/s"] = round(nbytes / t / 1e9, 1)
     assert int(nh2.sum()) == n_h2 and int(nm2.sum()) == n_m2
     return tier, retier
+
+
+def probe_figure(dev, gib=4, reps=20):
+    """lkv_hbm_read_probe over a zero-filled buffer of `gib` GiB, plain and
+    non-temporal loads, each timed with HIP events over `reps` launches after
+    two untimed ones: the read bandwidth a streaming kernel reaches."""
+    import torch
+
+    from quantized_kv_cache_token_amd import lkv
+
+    buf = torch.zeros(gib << 28, dtype=torch.float32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    res = {"bytes": buf.numel() * 4, "launches": reps}
+    for nt in (False, True):
+        for _ in range(2):
+            lkv.hbm_read_probe(buf, sink, nt)
+        e0, e1 = _event(), _event()
+        e0.record()
+        for _ in range(reps):
+            lkv.hbm_read_probe(buf, sink, nt)
+        e1.record()
+        torch.cuda.synchronize()
+        res["nt_GB/s" if nt else "GB/s"] = round(buf.numel() * 4 * reps / (e0.elapsed_time(e1) / 1e3) / 1e9, 1)
+    assert int(sink.item()) == 0
+    del buf
+    torch.cuda.empty_cache()
+    return res
 
 
 def serving_figure(wl, dev, every=32, tl_rel=0.35, th_rel=1.9):

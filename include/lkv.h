@@ -226,6 +226,17 @@ int lkv_decode_attn_noalloc(const lkv_cache* segs, const lkv_view* views, int32_
                             int32_t q_dtype, int32_t batch, int32_t num_q_heads, float sm_scale, float tau_low,
                             int32_t split_tokens, float* out, void* stream);
 
+/* Measurement helper, not a step of the method: a streaming read of
+ * `bytes` of the device buffer buf, the bandwidth a read-only kernel
+ * reaches on this part, against which the decode kernels' fractions of the
+ * HBM peak are read.  One launch of (compute units x 8) workgroups of 256
+ * threads, each thread keeping four 16-byte loads in flight over a
+ * grid-stride loop; nontemporal != 0 loads with the non-temporal hint.
+ * sink: one device uint32, written only if the buffer's words xor-fold to
+ * 0x9E3779B9 (never for a zero-filled buffer).  buf 16-byte aligned, bytes
+ * a positive multiple of 16, else LKV_EINVAL. */
+int lkv_hbm_read_probe(const void* buf, int64_t bytes, int32_t nontemporal, uint32_t* sink, void* stream);
+
 /* Split size for lkv_decode_attn_multi (host): lkv_decode_plan over the
  * work items the call launches, batch * T query tokens, or batch * ceil(T/2)
  * query-token pairs at 4 query heads per KV head (the matrix-core kernel

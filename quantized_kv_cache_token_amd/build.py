@@ -30,6 +30,7 @@ SOURCES = [
     ("decode.hip", []),
     ("decode_mfma.hip", []),
     ("decode_f16.hip", []),
+    ("probe.hip", []),
     ("api.cpp", ["-x", "hip"]),
 ]
 

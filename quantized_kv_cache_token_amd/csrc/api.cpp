@@ -678,6 +678,13 @@ int scratch_of_current_device(void** out)
 
 extern "C" {
 
+int lkv_hbm_read_probe(const void* buf, int64_t bytes, int32_t nontemporal, uint32_t* sink, void* stream)
+{
+    if (!buf || !sink || bytes <= 0 || bytes % 16 != 0 || (uintptr_t)buf % 16 != 0) return LKV_EINVAL;
+    return launch_hbm_read_probe(buf, bytes, nontemporal != 0, sink, (hipStream_t)stream) == hipSuccess ? LKV_OK
+                                                                                                       : LKV_EHIP;
+}
+
 int lkv_decode_attn_noalloc(const lkv_cache* segs, const lkv_view* views, int32_t nseg, const void* q,
                             int32_t q_dtype, int32_t batch, int32_t num_q_heads, float sm_scale, float tau_low,
                             int32_t split_tokens, float* out, void* stream)

@@ -144,6 +144,10 @@ hipError_t launch_decode_combine(const CombineArgs& a, int32_t batch, int32_t D,
 // p[0 .. n) = v on the stream (a kernel, not a memset node).
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t stream);
 
+// Streaming read of `bytes` (a multiple of 16, 16-byte aligned) of a device
+// buffer; writes sink[0] only if the buffer's words fold to a fixed value.
+hipError_t launch_hbm_read_probe(const void* buf, int64_t bytes, bool nontemporal, uint32_t* sink, hipStream_t stream);
+
 // A source segment of a tier scan and a destination segment.
 struct TierSource {
     Fmt f;

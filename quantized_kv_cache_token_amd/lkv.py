@@ -48,7 +48,8 @@ EXPORTS = ["lkv_status_string", "lkv_chunk_layout", "lkv_quant_append", "lkv_dec
            "lkv_decode_scores_workspace_bytes", "lkv_decode_attn_scores",
            "lkv_default_thresholds", "lkv_tier_workspace_bytes", "lkv_tier_update",
            "lkv_retier_workspace_bytes", "lkv_retier", "lkv_decode_attn_multi", "lkv_decode_plan_multi",
-           "lkv_decode_attn_debug", "lkv_decode_attn_noalloc", "lkv_append_decode", "lkv_append_split"]
+           "lkv_decode_attn_debug", "lkv_decode_attn_noalloc", "lkv_append_decode", "lkv_append_split",
+           "lkv_hbm_read_probe"]
 
 
 def lib():
@@ -83,6 +84,7 @@ def lib():
         "lkv_append_decode": ([PC, PV, P, P, I32, P, I32, I32, I32, F, F, I32, P, P, C.c_size_t, V], C.c_int),
         "lkv_append_split": ([PC, PV, P, P, I32, P, I32, I32, I32, F, F, I32, P, C.c_size_t, V], C.c_int),
         "lkv_decode_attn_noalloc": ([PC, PV, I32, P, I32, I32, I32, F, F, I32, P, V], C.c_int),
+        "lkv_hbm_read_probe": ([P, I64, I32, P, V], C.c_int),
         "lkv_decode_attn_debug": ([PC, PV, I32, P, I32, I32, I32, I32, F, F, I32, P, P, I32, P, C.c_size_t, V],
                                   C.c_int),
         "lkv_retier": ([PC, PV, P, I32, PC, PV, P, I32, F, F, PC, P, I32, PC, P, I32, P, P, P, P, I32, P,
@@ -266,6 +268,14 @@ def append_decode(cache: Cache, view: View, k_new: torch.Tensor, v_new: torch.Te
         sm_scale, tau_low, split_tokens, _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
     return out
+
+
+def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor, nontemporal: bool = False, stream=None) -> None:
+    """lkv_hbm_read_probe: a streaming read of buf (a device tensor)."""
+    _require(buf.is_cuda and buf.is_contiguous() and sink.dtype in (torch.int32, torch.uint32) and sink.is_cuda,
+             "buf: contiguous device tensor; sink: one device int32")
+    _check("lkv_hbm_read_probe", lib().lkv_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(),
+                                                          int(nontemporal), _ptr(sink), _stream(stream)))
 
 
 def decode_attn_noalloc(caches, views, q: torch.Tensor, sm_scale: float, tau_low: float = 0.0,

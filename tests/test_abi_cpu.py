@@ -175,6 +175,16 @@ def test_in_place_tiering_needs_its_own_segment_and_row_width():
     assert tier(dm=_cache(v_bits=4, pool=0x11000), dm_bt=0x20000) == lkv.EINVAL  # MID onto the source's blocks
 
 
+def test_hbm_read_probe_rejects_bad_buffers():
+    L = lkv.lib()
+    p = C.c_void_p(0x90000)
+    assert L.lkv_hbm_read_probe(None, 1 << 20, 0, p, None) == lkv.EINVAL
+    assert L.lkv_hbm_read_probe(p, 0, 0, p, None) == lkv.EINVAL
+    assert L.lkv_hbm_read_probe(p, 1000, 0, p, None) == lkv.EINVAL          # not a multiple of 16
+    assert L.lkv_hbm_read_probe(C.c_void_p(0x90004), 1 << 20, 1, p, None) == lkv.EINVAL  # misaligned
+    assert L.lkv_hbm_read_probe(p, 1 << 20, 0, None, None) == lkv.EINVAL
+
+
 def test_retier_rejects_bad_formats():
     L = lkv.lib()
     p = C.c_void_p(0x90000)
