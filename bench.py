@@ -65,16 +65,23 @@ def parse():
                    help="skip every secondary figure but the prefill append (counter passes: only the step's kernels run)")
     p.add_argument("--graph", action="store_true",
                    help="replay each step as a captured HIP graph instead of launching its kernels from the host")
+    p.add_argument("--kv-heads", type=int, default=0,
+                   help="workloads 2 and 4: this many KV heads (query heads scaled to keep the GQA group), e.g. 1 "
+                        "for one GPU's share of a cache sharded by KV head over 8 GPUs")
     p.add_argument("--probe-only", action="store_true",
                    help="only the HBM read probe (a streaming read of 4 GiB; profiling)")
     p.add_argument("--tier-only", action="store_true",
                    help="only the tier-update and re-tier figures at the tiered workload's shape (profiling)")
+    p.add_argument("--merged", action="store_true",
+                   help="one launch per step where the library takes it: the split kernel also merges its own "
+                        "splits (lkv_append_decode_merged); by default the merge is its own kernel, which "
+                        "measured faster")
     p.add_argument("--unfused", action="store_true",
                    help="three launches per step: the append kernel, the split kernel, the merge")
     return p.parse_args()
 
 
-def measured_traffic(kernel: str, workload: str, fused: bool):
+def measured_traffic(kernel: str, workload: str, fused: bool, merged: bool = False):
     """HBM bytes of the split kernel and the merge per step, from the
     committed counter summary, if it was taken on the current kernel sources
     with the same step; else None."""
@@ -84,7 +91,8 @@ def measured_traffic(kernel: str, workload: str, fused: bool):
     rec = json.load(open(path))
     from quantized_kv_cache_token_amd.profsum import kernel_source_hash
 
-    if rec.get("source_hash") != kernel_source_hash() or bool(rec.get("fused")) != fused:
+    if (rec.get("source_hash") != kernel_source_hash() or bool(rec.get("fused")) != fused or
+            bool(rec.get("merged")) != merged):
         return None
     return rec.get("hbm_bytes_per_step")
 
@@ -98,6 +106,7 @@ class Setup:
     def __init__(self):
         self.calls = []          # stages per rotation slot
         self.fused = False       # the split stage also appends the new rows
+        self.merged = None       # ... and merges its own splits (one launch per step)
         self.keep = []           # tensors the prepared calls point at
         self.step_bytes = None   # i -> counted bytes of step i
         self.split_alg = None    # i -> algorithmic bytes of the split launch of step i (KV + Q)
@@ -116,6 +125,26 @@ def _event():
     return torch.cuda.Event(enable_timing=True)
 
 
+def fused_step(args, S, cache, view, k, v, q, sm, split, out, ws, counters):
+    """The stages of one fused step: lkv_append_decode_merged (one launch)
+    where the split kernel can merge its own splits, else the split kernel
+    with the append and the merge kernel (lkv_append_decode's two stages)."""
+    from quantized_kv_cache_token_amd import lkv
+
+    if S.merged is None:  # decided once, by whether the library takes the merged form
+        S.merged = False
+        if args.merged:
+            try:
+                lkv.append_decode_merged(cache, view, k, v, q, sm, 0.0, split, counters, out, ws)
+                S.merged = True
+            except lkv.LkvError as e:
+                if e.status != lkv.EUNSUPPORTED:
+                    raise
+    if S.merged:
+        return (lkv.prepare_append_decode_merged(cache, view, k, v, q, sm, 0.0, split, out, counters, ws),)
+    return lkv.prepare_append_decode(cache, view, k, v, q, sm, 0.0, split, out, ws)
+
+
 def setup_uniform(args, wl, dev) -> Setup:
     """Workloads 2 and 4: every sequence at N tokens, identity block tables."""
     import numpy as np
@@ -125,6 +154,10 @@ def setup_uniform(args, wl, dev) -> Setup:
 
     kb, vb = (16, 16) if args.fp16_layer else (wl.k_bits, wl.v_bits)
     B, Hq, Hkv, D, N = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.n_ctx
+    name = wl.name if not args.fp16_layer else wl.name.replace("k6v4", "fp16")
+    if args.kv_heads:  # one GPU's share of a cache sharded by KV head: the same GQA group
+        Hq, Hkv = Hq // Hkv * args.kv_heads, args.kv_heads
+        name = name.replace(f"hq{wl.num_q_heads}_hkv{wl.num_kv_heads}", f"hq{Hq}_hkv{Hkv}")
     nblk = (N + 63) // 64
     bt = torch.arange(B * nblk, dtype=torch.int32, device=dev).view(B, nblk)
     lens = torch.full((B,), N, dtype=torch.int32, device=dev)
@@ -157,18 +190,19 @@ def setup_uniform(args, wl, dev) -> Setup:
     ws = lkv.decode_workspace([caches[0]], [view], B, Hq, split, dev)
     out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
     S.fused = not args.unfused
+    counters = lkv.merge_counters(caches[0], B, dev)
     for layer in range(args.layers):
         k, v = inputs.kv_rows(wl.seed, 1000, B, Hkv, D, dtype=wl.dtype, outliers=outl, layer=layer, step=1,
                               device=dev)
         q = inputs.queries(wl.seed, B, Hq, D, dtype=wl.dtype, layer=layer, device=dev)
         if S.fused:  # the new row of each sequence is position N - 1: lengths are N
-            S.calls.append(lkv.prepare_append_decode(caches[layer], view, k, v, q, sm, 0.0, split, out, ws))
+            S.calls.append(fused_step(args, S, caches[layer], view, k, v, q, sm, split, out, ws, counters))
         else:
             app = lkv.prepare_append(caches[layer], k, v, cu1, last, bt, 1)
             spl, comb = lkv.prepare_decode([caches[layer]], [view], q, sm, 0.0, split, out, ws)
             S.calls.append((app, spl, comb))
         S.keep += [k, v, q]
-    S.keep += [caches, bt, lens, view, cu1, last, ws, out]
+    S.keep += [caches, bt, lens, view, cu1, last, ws, out, counters]
     ptk = caches[0].chunk_bytes // 64
     if not args.fp16_layer and not args.no_secondary:
         S.secondary["decode_with_scores"] = scores_figure(caches, view, S.keep, B, Hq, Hkv, D, N, sm, split, dev)
@@ -181,10 +215,11 @@ def setup_uniform(args, wl, dev) -> Setup:
     S.split_alg = lambda i: kv + B * Hq * D * qb
     S.append_bytes, S.out_bytes = B * Hkv * (2 * D * qb + ptk), B * Hq * D * 4
     S.sequences = B
-    S.config = {"workload": wl.name if not args.fp16_layer else wl.name.replace("k6v4", "fp16"), "batch": B,
+    S.config = {"workload": name, "batch": B,
                 "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "ctx_tokens": N,
                 "group_size": wl.group_size, "k_bits": kb, "v_bits": vb, "q_dtype": wl.dtype,
-                "split_tokens": split, "layers_rotated": args.layers, "append_in_split_kernel": S.fused}
+                "split_tokens": split, "layers_rotated": args.layers, "append_in_split_kernel": S.fused,
+                "merge_in_split_kernel": bool(S.merged)}
     pre_bytes = (N - 1) * Hkv * (2 * D * qb + ptk)
     pre_s = float(np.median(prefill_ms)) / 1e3
     S.secondary["append_prefill"] = {"GB/s": round(pre_bytes / pre_s / 1e9, 1),
@@ -446,17 +481,18 @@ def setup_ragged(args, wl, dev) -> Setup:
     views = [lkv.View(bt, after[s], max_len, live[s]) for s in range(n_steps)]
     # rotation slot i = s * layers + layer: decode step s of that layer
     S.fused = not args.unfused
+    counters = lkv.merge_counters(caches[0], B, dev)
     for s in range(n_steps):
         for layer in range(args.layers):
             k, v = kvs[layer]
             if S.fused:  # the new row of sequence b is position len_b + s: the step's lengths count it
-                S.calls.append(lkv.prepare_append_decode(caches[layer], views[s], k, v, qs[layer], sm, 0.0, split,
-                                                         out, ws))
+                S.calls.append(fused_step(args, S, caches[layer], views[s], k, v, qs[layer], sm, split, out, ws,
+                                          counters))
             else:
                 app = lkv.prepare_append(caches[layer], k, v, cu1, pos[s], bt, 1)
                 spl, comb = lkv.prepare_decode([caches[layer]], [views[s]], qs[layer], sm, 0.0, split, out, ws)
                 S.calls.append((app, spl, comb))
-    S.keep += [caches, bt, pos, after, views, ws, out, cu1, kvs, qs]
+    S.keep += [caches, bt, pos, after, views, ws, out, cu1, kvs, qs, counters]
     qb = 2 if wl.dtype == "bf16" else 4
     L = args.layers
     S.per_token_head, S.q_bytes = 180, qb
@@ -470,7 +506,7 @@ def setup_ragged(args, wl, dev) -> Setup:
                 "ctx_tokens_mean": round(float(lens.mean()), 1), "decode_steps": n_steps,
                 "group_size": wl.group_size, "k_bits": wl.k_bits, "v_bits": wl.v_bits, "q_dtype": wl.dtype,
                 "split_tokens": split, "layers_rotated": L, "paged": "seeded permutation of pool blocks",
-                "append_in_split_kernel": S.fused}
+                "append_in_split_kernel": S.fused, "merge_in_split_kernel": bool(S.merged)}
     return S
 
 
@@ -580,9 +616,13 @@ def main():
     value = total_bytes / (t1 - t0) / 1e9
     # stage times: the split stage (K2; with the fused append it also writes
     # the new rows) and the merge (K3), from the events around them
-    si = n_stages - 2  # the split stage is the one before the merge
-    split_ms = np.array([evs[i][si].elapsed_time(evs[i][si + 1]) for i in timed])
-    comb_ms = np.array([evs[i][si + 1].elapsed_time(evs[i][si + 2]) for i in timed])
+    if n_stages == 1:  # one launch: the split kernel appends and merges
+        split_ms = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in timed])
+        comb_ms = np.zeros_like(split_ms)
+    else:
+        si = n_stages - 2  # the split stage is the one before the merge
+        split_ms = np.array([evs[i][si].elapsed_time(evs[i][si + 1]) for i in timed])
+        comb_ms = np.array([evs[i][si + 1].elapsed_time(evs[i][si + 2]) for i in timed])
     split_alg = np.array([S.split_alg(first + i) for i in timed], dtype=np.float64)
     if S.fused:
         split_alg = split_alg + S.append_bytes
@@ -590,18 +630,20 @@ def main():
     split_s = float(split_ms.mean()) / 1e3
     split_achieved = float(split_alg.sum() / (split_ms.sum() / 1e3)) / 1e9
     if S.fused:
-        # a step is the split kernel and the merge: its GPU time over the
-        # timed region is K2 + K3 (with the gap between them)
+        # a step is the split kernel and the merge (one kernel when it merges
+        # its own splits): its GPU time over the timed region is K2 + K3
+        # (with any gap between them)
         k23_alg = np.array([S.split_alg(first + i) + S.append_bytes + S.out_bytes for i in range(args.steps)],
                            dtype=np.float64)
         k23_s = gpu_step_s
-        k23_src = "hip events around the timed steps (a step is the split kernel and the merge)"
+        k23_src = ("hip events around the timed steps (a step is one kernel that appends, splits and merges)"
+                   if S.merged else "hip events around the timed steps (a step is the split kernel and the merge)")
     else:
         k23_s = float((split_ms + comb_ms).mean()) / 1e3
         k23_src = "hip events around each kernel, one step in every rotation cycle"
     achieved = float(k23_alg.mean() / k23_s) / 1e9
-    kname = "append_split+combine" if S.fused else "decode_split+combine"
-    traffic = measured_traffic("decode_step", S.config["workload"], S.fused)
+    kname = ("append_split_merged" if S.merged else "append_split+combine") if S.fused else "decode_split+combine"
+    traffic = measured_traffic("decode_step", S.config["workload"], S.fused, bool(S.merged))
 
     rec = {
         "metric": METRIC,
@@ -627,7 +669,8 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "alg_bytes_per_launch": int(round(k23_alg.mean())),
                      "avg_launch_us": round(k23_s * 1e6, 2), "timing": k23_src,
-                     "split_only": {"kernel": "append_split" if S.fused else "decode_split",
+                     "split_only": {"kernel": ("append_split_merged" if S.merged else "append_split") if S.fused
+                                    else "decode_split",
                                     "achieved": round(split_achieved, 2),
                                     "frac": round(split_achieved / HBM_PEAK_GBS, 4),
                                     "alg_bytes_per_launch": int(round(split_alg.mean())),

@@ -201,6 +201,22 @@ int lkv_append_decode(const lkv_cache* cache, const lkv_view* view, const void* 
                       float sm_scale, float tau_low, int32_t split_tokens, float* out, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* lkv_append_decode in one launch: the split kernel also merges the split
+ * partials (the combine step of the split decode), the last wave to finish
+ * a (sequence, KV head) merging that row's splits.  The output and the pool
+ * are exactly lkv_append_decode's.  counters: uint32 [batch][number of KV
+ * heads], caller-owned, all zero before the first call (a zero-filled
+ * allocation); every completed call leaves them zero.  Calls that share
+ * counters or a workspace must not overlap.  Formats and shapes: those for
+ * which lkv_append_decode writes the new rows in the split kernel, with at
+ * most 32 splits per sequence (max_len <= 32 * split_tokens); otherwise
+ * LKV_EUNSUPPORTED and nothing is launched (lkv_append_decode serves every
+ * case).  Workspace: lkv_decode_workspace_bytes(). */
+int lkv_append_decode_merged(const lkv_cache* cache, const lkv_view* view, const void* k_new, const void* v_new,
+                             int32_t kv_dtype, const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+                             float sm_scale, float tau_low, int32_t split_tokens, float* out, uint32_t* counters,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* The first stage of lkv_append_decode, for callers that schedule the two
  * apart (lkv_append_decode is exactly lkv_append_split followed by
  * lkv_decode_combine on the same stream): the new rows and the split

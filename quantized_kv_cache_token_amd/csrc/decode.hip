@@ -15,6 +15,7 @@
 #include <algorithm>
 
 #include "lkv_internal.h"
+#include "merge128.h"
 #include "quant_device.h"
 
 namespace lkv {
@@ -298,8 +299,8 @@ __global__ __launch_bounds__(64 * NW) void combine_kernel(CombineArgs a)
 // The merge for head_dim 128 and at most 32 splits, the shape of the
 // matrix-core decode: one wave per (sequence, query head) whose lane l holds
 // channels 2l and 2l + 1 of every split's row (one 8-byte load per split,
-// all issued at once), with the splits' weights taken from their lanes by
-// readlane.  Same arithmetic, in the same order, as combine_kernel<128, 1>.
+// all issued at once); merge128 does the arithmetic, as the split kernel
+// that merges its own splits does.
 __global__ __launch_bounds__(64) void combine128_kernel(CombineArgs a)
 {
     constexpr int D = 128, CH = 32;
@@ -312,12 +313,44 @@ __global__ __launch_bounds__(64) void combine128_kernel(CombineArgs a)
     for (int i = 0; i < CH; i++) ov[i] = i < n ? *(const float2*)(p + (int64_t)i * (D + 2) + 2 * lane) : float2{};
     const float mi = lane < n ? p[(int64_t)lane * (D + 2) + D] : -INFINITY;
     const float li = lane < n ? p[(int64_t)lane * (D + 2) + D + 1] : 0.0f;
-    const float M = wave_max(mi);
+    float M, inv;
+    *(float2*)(a.out + bh * D + 2 * lane) = merge128(ov, mi, li, &M, &inv);
+    if (a.ml != nullptr && lane == 0) {
+        a.ml[2 * bh] = M;
+        a.ml[2 * bh + 1] = inv;
+    }
+}
+
+// The merge for head_dim 128 with more than 32 splits: NW waves per
+// (sequence, query head), each taking chunks of 32 splits in the layout of
+// combine128_kernel (lane l: channels 2l and 2l + 1, one 8-byte load per
+// split, weights by readlane), then the waves' (M, L, o) merged through
+// LDS.  Per channel the same arithmetic, in the same order, as
+// combine_kernel<128, NW>.
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void combine128w_kernel(CombineArgs a)
+{
+    constexpr int D = 128, CH = 32;
+    const int64_t bh = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const float* p = a.part + bh * a.total_splits * (D + 2);
     float2 acc = {0.0f, 0.0f};
-    float L = 0.0f;
-    if (M != -INFINITY) {
-        const float wi = mi == -INFINITY ? 0.0f : exp2f(mi - M);
-        L = wave_sum(li * wi);
+    float M = -INFINITY, L = 0.0f;
+    for (int i0 = CH * wave; i0 < a.total_splits; i0 += CH * NW) {
+        const int n = min(CH, a.total_splits - i0);
+        float2 ov[CH];
+#pragma unroll
+        for (int i = 0; i < CH; i++)
+            ov[i] = i < n ? *(const float2*)(p + (int64_t)(i0 + i) * (D + 2) + 2 * lane) : float2{};
+        const float mi = lane < n ? p[(int64_t)(i0 + lane) * (D + 2) + D] : -INFINITY;
+        const float li = lane < n ? p[(int64_t)(i0 + lane) * (D + 2) + D + 1] : 0.0f;
+        const float m_new = fmaxf(M, wave_max(mi));
+        if (m_new == -INFINITY) continue;  // no token so far
+        const float alpha = exp2f(M - m_new);
+        const float wi = mi == -INFINITY ? 0.0f : exp2f(mi - m_new);
+        L = L * alpha + wave_sum(li * wi);
+        acc.x *= alpha;
+        acc.y *= alpha;
 #pragma unroll
         for (int i = 0; i < CH; i++) {
             // splits past n have weight 0 (their lanes hold mi = -inf)
@@ -325,11 +358,35 @@ __global__ __launch_bounds__(64) void combine128_kernel(CombineArgs a)
             acc.x += w != 0.0f ? ov[i].x * w : 0.0f;
             acc.y += w != 0.0f ? ov[i].y * w : 0.0f;
         }
+        M = m_new;
     }
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    *(float2*)(a.out + bh * D + 2 * lane) = float2{acc.x * inv, acc.y * inv};
+    __shared__ float sm_m[NW], sm_l[NW];
+    __shared__ float2 sm_o[NW][D / 2];
+    if (lane == 0) {
+        sm_m[wave] = M;
+        sm_l[wave] = L;
+    }
+    sm_o[wave][lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; w++) Mt = fmaxf(Mt, sm_m[w]);
+    float Lt = 0.0f;
+    float2 o = {0.0f, 0.0f};
+    if (Mt != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < NW; w++) {
+            const float ww = sm_m[w] == -INFINITY ? 0.0f : exp2f(sm_m[w] - Mt);
+            Lt += sm_l[w] * ww;
+            o.x += sm_o[w][lane].x * ww;
+            o.y += sm_o[w][lane].y * ww;
+        }
+    }
+    const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
+    *(float2*)(a.out + bh * D + 2 * lane) = float2{o.x * inv, o.y * inv};
     if (a.ml != nullptr && lane == 0) {
-        a.ml[2 * bh] = M;
+        a.ml[2 * bh] = Mt;
         a.ml[2 * bh + 1] = inv;
     }
 }
@@ -339,12 +396,13 @@ hipError_t launch_decode_combine(const CombineArgs& a, int32_t batch, int32_t D,
     if (batch == 0) return hipSuccess;
     const dim3 grid((unsigned)(batch * a.num_q_heads));
     // one wave takes up to 32 splits in one memory latency; more splits are
-    // spread over four waves
+    // spread over four waves (sixteen past 128 splits at head_dim 128)
     const bool one = a.total_splits <= 32;
     if (D == 64 && one) hipLaunchKernelGGL((combine_kernel<64, 1>), grid, dim3(64), 0, stream, a);
     else if (D == 64) hipLaunchKernelGGL((combine_kernel<64, 4>), grid, dim3(256), 0, stream, a);
     else if (one) hipLaunchKernelGGL(combine128_kernel, grid, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL((combine_kernel<128, 4>), grid, dim3(256), 0, stream, a);
+    else if (a.total_splits <= 4 * 32) hipLaunchKernelGGL(combine128w_kernel<4>, grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(combine128w_kernel<16>, grid, dim3(1024), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -42,6 +42,7 @@
 #include <type_traits>
 
 #include "lkv_internal.h"
+#include "merge128.h"
 #include "quant_device.h"
 #include "wave_util.h"
 
@@ -60,7 +61,21 @@ struct MfmaArgs {
     const void* k_new;
     const void* v_new;
     int32_t kv_dtype;
+    // the split kernel that merges its own splits: one counter per (entry, KV
+    // head) row, zero between calls, and the output [B][Hq][128]
+    uint32_t* counters;
+    float* out;
 };
+
+// A partial's value, stored plainly, or (WT) as a device-scope relaxed
+// atomic store, which writes through to where every compute unit reads it:
+// the splits a wave merges were written by waves on other L2 caches.
+template <bool WT>
+__device__ __forceinline__ void pstore(float* p, float v)
+{
+    if constexpr (WT) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *p = v;
+}
 
 // The bit manipulations below are plain C, never inline asm: a matrix-core
 // instruction that reads a VGPR just written by a vector instruction needs
@@ -975,7 +990,7 @@ __device__ __forceinline__ void patch_v(BlockRegs<VB>& R, const NewRow& r, int s
 // for both.  The earlier token's causal prefix is one token shorter: its
 // columns are masked in the split's last blocks.  An odd T's last token is
 // paired with itself and its second copy is not written.
-template <int VB, int G, bool KN, bool PAIR = false, bool DBG = false, bool APP = false>
+template <int VB, int G, bool KN, bool PAIR = false, bool DBG = false, bool APP = false, bool WT = false>
 __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, const int kvh, const int b, const int lane,
                                            uint4* meta_lds)
 {
@@ -1024,8 +1039,8 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, cons
         } else if (lane < G) {
             float* p = a.partials + (((int64_t)b * a.num_q_heads + kvh * G + lane) * a.total_splits +
                                      sg.split_base + sp) * (D + 2);
-            p[D] = -INFINITY;
-            p[D + 1] = 0.0f;
+            pstore<WT>(p + D, -INFINITY);
+            pstore<WT>(p + D + 1, 0.0f);
         }
         return;
     }
@@ -1265,18 +1280,15 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, cons
             o1 = halves_sum(o1);
             if ((q >> 1) != (T >> 2)) continue;
         }
-        base[hA * hstride + soff + 16 * T + c] = o0;
-        base[(hA + 1) * hstride + soff + 16 * T + c] = o1;
+        pstore<WT>(base + hA * hstride + soff + 16 * T + c, o0);
+        pstore<WT>(base + (hA + 1) * hstride + soff + 16 * T + c, o1);
     }
     if (q == 0 && part == 0 && (G == 8 || c < 8)) {  // two-set layout: set 0's lane of the head
-        base[hc * hstride + soff + D] = S.m_run;
-        base[hc * hstride + soff + D + 1] = S.l_run;
+        pstore<WT>(base + hc * hstride + soff + D, S.m_run);
+        pstore<WT>(base + hc * hstride + soff + D + 1, S.l_run);
     }
 }
 
-// DBG: the same kernel that also records its skip decisions (the test entry
-// point's skip mask); production launches take DBG = false, where the mask
-// code is compiled out.
 // DBG: the same kernel that also records its skip decisions (the test entry
 // point's skip mask); production launches take DBG = false, where the mask
 // code is compiled out.
@@ -1321,7 +1333,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
 // head, entry), newest first, the second half the rest.  Inside each half
 // the split index runs fastest, so consecutive workgroups (which go to the
 // XCDs in turn) still take different splits of one row.
-template <int VB, int G>
+template <int VB, int G, bool MERGE>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void split_append_kernel(MfmaArgs a)
 {
     __shared__ uint4 meta_lds[META_BYTES / 16];
@@ -1337,7 +1349,47 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
         rev = P + lin % (ns - P);
         row = lin / (ns - P);
     }
-    split_body<VB, G, false, false, false, true>(a, ns - 1 - rev, row % H, row / H, threadIdx.x, meta_lds);
+    split_body<VB, G, false, false, false, true, MERGE>(a, ns - 1 - rev, row % H, row / H, threadIdx.x, meta_lds);
+    if constexpr (MERGE) {
+        // The row's last wave to finish merges its ns (<= 32) splits.  The
+        // partial's stores went through to the shared level; once they are
+        // complete the wave counts itself in (the counter wraps to 0 at ns),
+        // and the wave that counts last reads every split of the row back
+        // with device-scope loads.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        uint32_t old = 0;
+        if (threadIdx.x == 0) old = atomicInc(a.counters + row, (unsigned)(ns - 1));
+        if (__builtin_amdgcn_readfirstlane(old) != (uint32_t)(ns - 1)) return;
+        constexpr int D = 128;
+        const int lane = threadIdx.x, b = row / H, kvh = row % H;
+        float2 ov[2][32];
+        float mi[2], li[2];
+        auto fetch = [&](int g, int k) __attribute__((always_inline)) {
+            float* p = a.partials + ((int64_t)b * a.num_q_heads + kvh * G + g) * a.total_splits * (D + 2);
+#pragma unroll
+            for (int i = 0; i < 32; i++) {
+                const uint64_t v = i < ns ? __hip_atomic_load((uint64_t*)(p + (int64_t)i * (D + 2) + 2 * lane),
+                                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                          : 0ull;
+                ov[k][i] = float2{__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32))};
+            }
+            mi[k] = lane < ns ? __hip_atomic_load(p + (int64_t)lane * (D + 2) + D, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT)
+                              : -INFINITY;
+            li[k] = lane < ns ? __hip_atomic_load(p + (int64_t)lane * (D + 2) + D + 1, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT)
+                              : 0.0f;
+        };
+        // head g + 1's loads are in flight while head g is merged
+        fetch(0, 0);
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+            if (g + 1 < G) fetch(g + 1, (g + 1) & 1);
+            float M, inv;
+            *(float2*)(a.out + ((int64_t)b * a.num_q_heads + kvh * G + g) * D + 2 * lane) =
+                merge128(ov[g & 1], mi[g & 1], li[g & 1], &M, &inv);
+        }
+    }
 }
 
 // Whether a segment has a matrix-core kernel.
@@ -1421,23 +1473,35 @@ static void launch_plain(const MfmaArgs& a, int vb, int G, bool kn, dim3 grid, h
 bool launch_append_decode_mfma(const SegArgs& s, const void* q, int q_dtype, int32_t batch, int32_t num_q_heads,
                                float sm_scale, float tau_low, int32_t split_tokens, int32_t total_splits,
                                float* partials, const void* k_new, const void* v_new, int kv_dtype,
-                               hipStream_t stream, hipError_t* err)
+                               hipStream_t stream, hipError_t* err, float* out, uint32_t* counters)
 {
     const uintptr_t align = kv_dtype == LKV_F32 ? 8 : 4;  // a lane reads its two channels at once
     if (!mfma_ok(s, q, q_dtype, num_q_heads, sm_scale, split_tokens) || s.f.k_norm || s.q_per_seq != 1 ||
         s.skip_mask != nullptr || s.scores != nullptr || (uintptr_t)k_new % align != 0 ||
         (uintptr_t)v_new % align != 0)
         return false;
+    const bool merge = counters != nullptr;
+    if (merge && (s.n_splits > 32 || total_splits != s.n_splits || !out)) return false;
     const int G = num_q_heads / s.f.H;
     MfmaArgs a = mfma_args(s, q, num_q_heads, sm_scale, tau_low, split_tokens, total_splits, partials);
     a.k_new = k_new;
     a.v_new = v_new;
     a.kv_dtype = kv_dtype;
+    a.counters = counters;
+    a.out = out;
     const dim3 grid((unsigned)(s.n_splits * s.f.H * batch));  // every (split, KV head, entry), in the order above
-    if (s.f.vb == 4 && G == 4) hipLaunchKernelGGL((split_append_kernel<4, 4>), grid, dim3(64), 0, stream, a);
-    else if (s.f.vb == 4) hipLaunchKernelGGL((split_append_kernel<4, 8>), grid, dim3(64), 0, stream, a);
-    else if (G == 4) hipLaunchKernelGGL((split_append_kernel<6, 4>), grid, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL((split_append_kernel<6, 8>), grid, dim3(64), 0, stream, a);
+    auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(64), 0, stream, a); };
+    if (merge) {
+        if (s.f.vb == 4 && G == 4) go(split_append_kernel<4, 4, true>);
+        else if (s.f.vb == 4) go(split_append_kernel<4, 8, true>);
+        else if (G == 4) go(split_append_kernel<6, 4, true>);
+        else go(split_append_kernel<6, 8, true>);
+    } else {
+        if (s.f.vb == 4 && G == 4) go(split_append_kernel<4, 4, false>);
+        else if (s.f.vb == 4) go(split_append_kernel<4, 8, false>);
+        else if (G == 4) go(split_append_kernel<6, 4, false>);
+        else go(split_append_kernel<6, 8, false>);
+    }
     *err = hipGetLastError();
     return true;
 }

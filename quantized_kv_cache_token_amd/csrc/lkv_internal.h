@@ -84,7 +84,8 @@ hipError_t launch_append(const Fmt& f, uint8_t* pool, const void* k, const void*
 bool launch_append_decode_mfma(const SegArgs& s, const void* q, int q_dtype, int32_t batch, int32_t num_q_heads,
                                float sm_scale, float tau_low, int32_t split_tokens, int32_t total_splits,
                                float* partials, const void* k_new, const void* v_new, int kv_dtype,
-                               hipStream_t stream, hipError_t* err);
+                               hipStream_t stream, hipError_t* err, float* out = nullptr,
+                               uint32_t* counters = nullptr);
 
 // Partials: fp32 [batch][Hq][total_splits][D + 2] = (o[D], m, L).
 hipError_t launch_decode_split(const SegArgs& s, const void* q, int q_dtype, int32_t batch,

@@ -1,0 +1,52 @@
+// merge128.h -- the merge of up to 32 split partials (o, m, L) of one
+// (sequence, query head) at head_dim 128, in one wave (the split step of the
+// pages' decode: per-split running maximum and sum, then one rescaled sum).
+// Lane l holds channels 2l and 2l + 1 of every split's o row and split l's
+// (m, L); splits past the count hold m = -inf.  Both the merge kernel and the
+// split kernel that merges its own splits call this one function, built
+// without fp contraction, so the two give the same output bit for bit.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace lkv {
+
+__device__ __forceinline__ float merge_wave_max(float x)
+{
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+    return x;
+}
+
+__device__ __forceinline__ float merge_wave_sum(float x)
+{
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+// M = max_i m_i, L = sum_i L_i 2^(m_i - M), o = sum_i o_i 2^(m_i - M) / L
+// (splits in order; base 2).  Returns the lane's two output channels; M and
+// 1 / L (0 when no split has a token) go to *M_out and *inv_out.
+__device__ __forceinline__ float2 merge128(const float2 (&ov)[32], float mi, float li, float* M_out, float* inv_out)
+{
+#pragma clang fp contract(off)
+    const float M = merge_wave_max(mi);
+    float2 acc = {0.0f, 0.0f};
+    float L = 0.0f;
+    if (M != -INFINITY) {
+        const float wi = mi == -INFINITY ? 0.0f : exp2f(mi - M);
+        L = merge_wave_sum(li * wi);
+#pragma unroll
+        for (int i = 0; i < 32; i++) {
+            // splits past the count have weight 0 (their lanes hold mi = -inf)
+            const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wi), i));
+            acc.x += w != 0.0f ? ov[i].x * w : 0.0f;
+            acc.y += w != 0.0f ? ov[i].y * w : 0.0f;
+        }
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    *M_out = M;
+    *inv_out = inv;
+    return float2{acc.x * inv, acc.y * inv};
+}
+
+}  // namespace lkv

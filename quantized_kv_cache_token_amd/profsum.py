@@ -3,7 +3,7 @@
     python -m quantized_kv_cache_token_amd.profsum stats <dir> [--match REGEX]
     python -m quantized_kv_cache_token_amd.profsum dispatches <dir> [--match REGEX]
     python -m quantized_kv_cache_token_amd.profsum traffic --fetch <dir> --write <dir>
-        --kernel REGEX [--kernel REGEX ...] --workload NAME --alg-bytes N [--fused]
+        --kernel REGEX [--kernel REGEX ...] --workload NAME --alg-bytes N [--fused] [--merged]
         --out FILE [--command TEXT]
 
 `stats` prints per-kernel call counts and durations from a
@@ -37,7 +37,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 PROBE_BYTES = 1 << 30          # the streaming probe reads and writes 1 GiB
 PROBE_REGEX = r"neg_kernel"    # its kernel: an elementwise negation over fp32
 # the sources of the split kernel and the merge the traffic record describes
-DECODE_SOURCES = ("decode_mfma.hip", "decode.hip", "quant_device.h", "wave_util.h", "lkv_internal.h")
+DECODE_SOURCES = ("decode_mfma.hip", "decode.hip", "merge128.h", "quant_device.h", "wave_util.h",
+                  "lkv_internal.h")
 
 
 def kernel_source_hash() -> str:
@@ -108,6 +109,7 @@ def _mean_of(vals: dict[str, list[float]], regex: str) -> tuple[str, float, int]
 
 
 def traffic(fetch_dir: str, write_dir: str, kernels: list[str], workload: str, alg_bytes: int, fused: bool,
+            merged: bool,
             command: str) -> dict:
     f = _per_dispatch(fetch_dir, "FETCH_SIZE")
     w = _per_dispatch(write_dir, "WRITE_SIZE")
@@ -126,7 +128,7 @@ def traffic(fetch_dir: str, write_dir: str, kernels: list[str], workload: str, a
                     "write_kib_raw": round(kw, 2), "hbm_fetch_bytes_per_launch": int(fetch_b),
                     "hbm_write_bytes_per_launch": int(write_b)})
     return {
-        "workload": workload, "fused": fused, "source_hash": kernel_source_hash(), "kernels": per,
+        "workload": workload, "fused": fused, "merged": merged, "source_hash": kernel_source_hash(), "kernels": per,
         "probe_fetch_kib_raw": round(pf, 2), "probe_write_kib_raw": round(pw, 2),
         "scale_fetch": round(sf, 5), "scale_write": round(sw, 5),
         "hbm_bytes_per_step": int(total), "alg_bytes_per_step": alg_bytes,
@@ -149,6 +151,7 @@ def main(argv=None):
     t.add_argument("--write", required=True)
     t.add_argument("--kernel", required=True, action="append")
     t.add_argument("--fused", action="store_true")
+    t.add_argument("--merged", action="store_true", help="the split kernel also merges (one kernel per step)")
     t.add_argument("--workload", required=True)
     t.add_argument("--alg-bytes", type=int, required=True)
     t.add_argument("--out", required=True)
@@ -159,7 +162,7 @@ def main(argv=None):
     elif a.cmd == "dispatches":
         print(dispatches(a.dir, a.match))
     else:
-        rec = traffic(a.fetch, a.write, a.kernel, a.workload, a.alg_bytes, a.fused, a.command)
+        rec = traffic(a.fetch, a.write, a.kernel, a.workload, a.alg_bytes, a.fused, a.merged, a.command)
         with open(a.out, "w") as fh:
             json.dump(rec, fh, indent=1)
             fh.write("\n")

@@ -106,3 +106,55 @@ def test_append_decode_steps_with_skip_against_the_oracle():
         want, _ = resolved_reference([pair.ref], [bt], [np.array(lens, np.int32)], to_f32_host(q), sm_scale(D),
                                      tau, split, mask, [view.max_len], f"step {s}")
         assert_attention_close(out.cpu().numpy(), want, max_abs_vhat(pair.ref), f"step {s}")
+
+
+MERGED = [c for c in CASES if c[0][:3] == (128, 64, 6) and c[0][3] in (4, 6) and c[2] == "bf16"]
+
+
+@pytest.mark.parametrize("case", MERGED, ids=lambda c: "D{}g{}k{}v{}".format(*c[0]) + f"G{c[1]}{c[2]}{c[3]}")
+@pytest.mark.parametrize("split", [64, 1024])
+def test_append_decode_merged_equals_append_decode(case, split):
+    """The split kernel that merges its own splits: three steps in a row, each
+    with the pool and the output bit for bit those of lkv_append_decode, and
+    the counters back at zero after every call."""
+    fmt, G, qd, kvd = case
+    Hkv = 2
+    lens0 = [max(n - 3, 0) for n in LENS]
+    B = len(lens0)
+    rng = np.random.default_rng(47)
+    bt, nblk = block_tables([n + 3 for n in lens0], rng)
+    a = Pair(*fmt, Hkv, nblk)
+    _prefill(a, lens0, Hkv, fmt[0], "bf16", 47, bt, outliers=True)
+    b = lkv.Cache(*fmt, Hkv, nblk, pool=a.gpu.pool.clone())
+    counters = lkv.merge_counters(b, B)
+    btd = torch.tensor(bt).cuda()
+    for s in range(3):
+        lens = [n + s + 1 if n > 0 else 0 for n in lens0]
+        view = lkv.View(btd, torch.tensor(lens, dtype=torch.int32).cuda(), max(lens))
+        k_new, v_new = inputs.kv_rows(48, 0, B, Hkv, fmt[0], dtype=kvd, step=s)
+        q = inputs.queries(49 + s, B, Hkv * G, fmt[0], dtype=qd).cuda()
+        tau = 0.0 if s == 0 else 1e-4
+        say("append_decode_merged", case, "split", split, "step", s)
+        want = lkv.append_decode(a.gpu, view, k_new.cuda(), v_new.cuda(), q, sm_scale(fmt[0]), tau, split)
+        got = lkv.append_decode_merged(b, view, k_new.cuda(), v_new.cuda(), q, sm_scale(fmt[0]), tau, split,
+                                       counters)
+        torch.cuda.synchronize()
+        assert torch.equal(b.pool, a.gpu.pool), f"step {s}: pool differs from lkv_append_decode"
+        assert torch.equal(got, want), f"step {s}: output differs: max |d| {float((got - want).abs().max())}"
+        assert int(counters.abs().sum()) == 0, f"step {s}: counters not back at zero"
+
+
+def test_append_decode_merged_rejects_more_than_32_splits():
+    fmt, G, Hkv = (128, 64, 6, 4), 4, 2
+    lens = [2049, 100]  # 33 splits of 64 tokens
+    bt, nblk = block_tables(lens, np.random.default_rng(50))
+    c = lkv.Cache(*fmt, Hkv, nblk)
+    view = lkv.View(torch.tensor(bt).cuda(), torch.tensor(lens, dtype=torch.int32).cuda(), max(lens))
+    k_new, v_new = inputs.kv_rows(51, 0, 2, Hkv, 128)
+    q = inputs.queries(52, 2, Hkv * G, 128).cuda()
+    counters = lkv.merge_counters(c, 2)
+    with pytest.raises(lkv.LkvError) as e:
+        lkv.append_decode_merged(c, view, k_new.cuda(), v_new.cuda(), q, sm_scale(128), 0.0, 64, counters)
+    assert e.value.status == lkv.EUNSUPPORTED
+    torch.cuda.synchronize()
+    assert int(counters.abs().sum()) == 0 and not c.pool.any()  # nothing was launched
