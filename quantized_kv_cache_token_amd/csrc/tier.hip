@@ -543,6 +543,519 @@ __global__ __launch_bounds__(256) void tier_move_kernel(MoveArgs a)
     }
 }
 
+// ---- Out-of-place compaction: tier_compact_kernel<D> ----
+//
+// One workgroup per run of CMP_R consecutive source chunks of one
+// (sequence, KV head, source); wave w owns chunk w of the run.
+//  1. The run's V sections are loaded (coalesced, 16 B per thread) while
+//     each wave moves its chunk's K rows, K scales and zeros, and the V
+//     scales and zeros of survivors whose V codes are copied: lane = slot,
+//     every survivor's row goes straight from its source slot to its
+//     destination slot.  Nothing of an evicted token is read.
+//  2. The V sections go to LDS and the survivors of the run are listed per
+//     destination segment, in slot order (ranks).
+//  3. V codes are written per window of TPW destination slots (aligned, so
+//     a window's words hold no slot of another window): lane = (slot of the
+//     window, half of the channels).  Each lane takes its survivor's codes
+//     from LDS, copies them or requantises them at 4 bits (the group's
+//     extremes from the extreme codes, since the dequantised value is
+//     monotone in the code; every lane holds whole groups, so no lane
+//     exchange), and puts them in a small per-wave stage from which whole
+//     words are packed and stored.  Words that also hold slots of a
+//     neighbouring run are merged with atomics.
+constexpr int CMP_R = 4;  // source chunks per run (one per wave)
+constexpr int CMP_S = 8;  // most runs per workgroup, one after the other (MoveArgs::per_wg)
+typedef uint32_t cmp_u32x4 __attribute__((ext_vector_type(4)));
+
+// Orders one wave's LDS stores before its later LDS loads (other lanes).
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Step 1 for one survivor (lane) of segment SEG (0 HIGH, 1 MID); P its
+// destination position.  KR 16-byte pieces per K row, NG quantisation
+// groups.  Every load is issued before the first store.
+template <int KR, int NG, int SEG>
+__device__ __forceinline__ void compact_row(const MoveArgs& a, const Fmt& fs, const uint8_t* sch, int P, int b,
+                                            int kvh, int lane, bool vcopy)
+{
+    const MoveDst& d = a.dst[SEG];
+    const int32_t blk = d.bt[(int64_t)b * d.max_blocks + P / BT];
+    const cmp_u32x4* ks = (const cmp_u32x4*)(sch + fs.off_kc + lane * (16 * KR));
+    cmp_u32x4 kv[KR];
+#pragma unroll
+    for (int i = 0; i < KR; i++) kv[i] = ks[i];
+    float k_s[NG], v_s[NG];
+    uint32_t k_z[NG], v_z[NG];
+#pragma unroll
+    for (int gi = 0; gi < NG; gi++) {
+        k_s[gi] = ((const float*)(sch + fs.off_ks))[gi * BT + lane];
+        k_z[gi] = sch[fs.off_kz + gi * BT + lane];
+        if (vcopy) {
+            v_s[gi] = ((const float*)(sch + fs.off_vs))[gi * BT + lane];
+            v_z[gi] = sch[fs.off_vz + gi * BT + lane];
+        }
+    }
+    uint8_t* dch = d.pool + ((int64_t)blk * fs.H + kvh) * d.f.chunk;
+    const int ds = P % BT;
+    cmp_u32x4* kd = (cmp_u32x4*)(dch + d.f.off_kc + ds * (16 * KR));
+#pragma unroll
+    for (int i = 0; i < KR; i++) kd[i] = kv[i];
+#pragma unroll
+    for (int gi = 0; gi < NG; gi++) {
+        ((float*)(dch + d.f.off_ks))[gi * BT + ds] = k_s[gi];
+        dch[d.f.off_kz + gi * BT + ds] = (uint8_t)k_z[gi];
+        if (vcopy) {
+            ((float*)(dch + d.f.off_vs))[gi * BT + ds] = v_s[gi];
+            dch[d.f.off_vz + gi * BT + ds] = (uint8_t)v_z[gi];
+        }
+    }
+}
+
+template <int D, int NG, int SEG>
+__device__ __forceinline__ void compact_row_any(const MoveArgs& a, const Fmt& fs, const uint8_t* sch, int P, int b,
+                                                int kvh, int lane, bool vcopy)
+{
+    constexpr int K4 = D / 32, K6 = D * 6 / 128;  // 16-byte pieces of a 4- or 6-bit K row
+    if (fs.kb == 6) compact_row<K6, NG, SEG>(a, fs, sch, P, b, kvh, lane, vcopy);
+    else compact_row<K4, NG, SEG>(a, fs, sch, P, b, kvh, lane, vcopy);
+}
+
+template <int D, int NG>
+struct alignas(16) CmpShared {
+    static constexpr int NH = D / 64;          // channel halves: lanes per survivor
+    static constexpr int TPW = 64 / NH;        // destination slots per window
+    static constexpr int CW = D * 12 + 4;      // words per staged V section (6-bit rows; 4-bit use less)
+    static constexpr int SP = TPW + 16;        // stage row pitch (bytes, a multiple of 16)
+    uint32_t vsec[CMP_R][CW];
+    float vs[CMP_R][NG * BT];                  // source V scales and zeros (requantised MID)
+    uint8_t vz[CMP_R][NG * BT];
+    uint8_t stage[4][16 * NH][SP];             // per wave: 16 channels of each half x TPW slots
+    uint16_t lst[2][CMP_R * BT];               // survivors per segment: (chunk of the run << 6) | slot
+    int32_t cnt[2][CMP_R];
+    int32_t dblk[2][8];                        // destination blocks from the run's first position
+    // a segment's last word when the run ends inside it, carried into the
+    // workgroup's next run: [run parity][segment], and {valid, low bit,
+    // high bit, word, destination block}
+    uint32_t carry[2][2][D];
+    int32_t cmeta[2][2][8];
+};
+
+// Where a window's words go: the destination chunk, the run's slots [lo, hi)
+// relative to that chunk's block, and the carries in and out.
+struct WordSink {
+    uint8_t* dch;
+    int off_vc, vrow, lo, hi, blk;
+    const uint32_t* cin;    // the word the previous run ended inside, or null
+    int cin_lo;
+    uint32_t* cout;
+    int32_t* cmeta_out;
+};
+
+// Word W of channel row d holds this run's bits [a, e) (e > a).  A word the
+// run completes is stored whole (with the carried bits of the previous run
+// when it starts inside the word); one the run ends inside is carried; one
+// that starts with another workgroup's bits is merged with atomics.
+template <int NB>
+__device__ __forceinline__ void sink_word(const WordSink& k, int d, int W, uint32_t w)
+{
+    const int a = min(32, max(0, NB * k.lo - 32 * W)), e = min(32, max(0, NB * k.hi - 32 * W));
+    if (e <= a) return;
+    const uint32_t top = e == 32 ? 0xFFFFFFFFu : ((1u << e) - 1u);
+    uint32_t val = w & (top & ~((1u << a) - 1u));
+    int low = a;
+    if (a > 0 && k.cin) {
+        val |= k.cin[d];
+        low = k.cin_lo;
+    }
+    if (e < 32) {
+        k.cout[d] = val;
+        if (d == 0) {
+            k.cmeta_out[0] = 1;
+            k.cmeta_out[1] = low;
+            k.cmeta_out[2] = e;
+            k.cmeta_out[3] = W;
+            k.cmeta_out[4] = k.blk;
+        }
+        return;
+    }
+    uint32_t* p = (uint32_t*)(k.dch + k.off_vc + d * k.vrow) + W;
+    if (low == 0) {
+        *p = val;
+    } else {
+        atomicAnd(p, (1u << low) - 1u);
+        atomicOr(p, val);
+    }
+}
+
+// Code of channel row dl (of the lane's half) at slot s of a staged section.
+template <int VB>
+__device__ __forceinline__ uint32_t staged_code(const uint32_t* row, int dl, int ws, int sh)
+{
+    constexpr int VW = 2 * VB;  // words per row: 64 slots x VB bits
+    if constexpr (VB == 6) {
+        return __builtin_amdgcn_alignbit(row[dl * VW + ws + 1], row[dl * VW + ws], sh) & 63u;
+    } else {
+        return (row[dl * VW + ws] >> sh) & 15u;
+    }
+}
+
+// Packs the wave's stage (16 channels of each half, block jb of the
+// channel loop) into NB-bit words of destination chunk dch, window k; only
+// fields of slots [lo, hi) (relative to the window's block) are written.
+template <int D, int NB>
+__device__ __forceinline__ void pack_stage(const uint8_t (*st)[CmpShared<D, 1>::SP], const WordSink& sink, int k,
+                                           int jb, int lane)
+{
+    constexpr int NH = CmpShared<D, 1>::NH, TPW = CmpShared<D, 1>::TPW;
+    constexpr int FPG = NB == 4 ? 8 : 16;  // fields per packed group
+    constexpr int GPR = TPW / FPG;
+    constexpr int ITEMS = 16 * NH * GPR;
+    const int s0 = (k * TPW) % BT;  // the window's first slot in its block
+#pragma unroll
+    for (int it = 0; it < (ITEMS + 63) / 64; it++) {
+        const int idx = lane + 64 * it;
+        if (ITEMS % 64 != 0 && idx >= ITEMS) break;
+        const int i = idx / GPR, gq = idx % GPR;
+        const int d = 64 * (i / 16) + 16 * jb + (i % 16);
+        const int slot = s0 + gq * FPG;
+        if constexpr (NB == 4) {
+            const uint2 x = *(const uint2*)(st[i] + gq * FPG);
+            const uint32_t yl = x.x | (x.x >> 4), yh = x.y | (x.y >> 4);
+            const uint32_t w = (yl & 0xFFu) | ((yl >> 8) & 0xFF00u) | ((yh & 0xFFu) << 16) | ((yh << 8) & 0xFF000000u);
+            sink_word<4>(sink, d, slot / 8, w);
+        } else {
+            const uint4 x = *(const uint4*)(st[i] + gq * FPG);
+            uint32_t v[16], w[3];
+            const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                v[4 * q] = xs[q] & 0xFFu;
+                v[4 * q + 1] = (xs[q] >> 8) & 0xFFu;
+                v[4 * q + 2] = (xs[q] >> 16) & 0xFFu;
+                v[4 * q + 3] = xs[q] >> 24;
+            }
+            pack_values<6, 16, 3>(v, w);
+            const int W0 = slot / 16 * 3;
+#pragma unroll
+            for (int q = 0; q < 3; q++) sink_word<6>(sink, d, W0 + q, w[q]);
+        }
+    }
+}
+
+// One window of copied codes (VB bits at the source and the destination).
+template <int D, int NG, int VB>
+__device__ __forceinline__ void compact_copy(CmpShared<D, NG>& sh, const MoveDst& dst, int kvh, int seg, int k,
+                                             int plo, int n, int wave, int lane, WordSink sink)
+{
+    constexpr int NH = CmpShared<D, NG>::NH, TPW = CmpShared<D, NG>::TPW;
+    const int t = lane % TPW, h = lane / TPW;
+    const int p = k * TPW + t, r = p - plo;
+    const bool valid = r >= 0 && r < n;
+    const int e = sh.lst[seg][valid ? r : 0];
+    const int cl = e >> 6, s = e & 63;
+    const uint32_t* row = sh.vsec[cl] + 64 * h * (2 * VB);
+    const int bit = s * VB, ws = bit >> 5, bsh = bit & 31;
+    const int blk0 = k * TPW / BT * BT;
+    sink.blk = sh.dblk[seg][blk0 / BT - plo / BT];
+    sink.dch = dst.pool + ((int64_t)sink.blk * dst.f.H + kvh) * dst.f.chunk;
+    sink.off_vc = dst.f.off_vc;
+    sink.vrow = dst.f.vrow;
+    sink.lo = plo - blk0;
+    sink.hi = plo + n - blk0;
+    auto st = sh.stage[wave];
+    for (int jb = 0; jb < 4; jb++) {
+        // all 16 loads first: the stage stores could alias them for the compiler
+        uint32_t code[16];
+#pragma unroll
+        for (int j = 0; j < 16; j++) code[j] = staged_code<VB>(row, 16 * jb + j, ws, bsh);
+#pragma unroll
+        for (int j = 0; j < 16; j++) st[h * 16 + j][t] = (uint8_t)code[j];
+        wave_lds_sync();
+        pack_stage<D, VB>(st, sink, k, jb, lane);
+        wave_lds_sync();
+    }
+    (void)NH;
+}
+
+// One window of MID codes requantised from 6 to 4 bits, with their V scales
+// and zeros; groups of GS channels.  The same codes, scales and zero points
+// as quantize_fast / quantize_exact over the dequantised row: the group's
+// min / max are the dequantised extreme codes; a quotient that the fast
+// division leaves uncertain is recomputed with correctly rounded division.
+template <int D, int GS>
+__device__ __forceinline__ void compact_requant(CmpShared<D, D / GS>& sh, const MoveArgs& a, int kvh, int k, int plo,
+                                                int n, int wave, int lane, WordSink sink)
+{
+    constexpr int TPW = CmpShared<D, D / GS>::TPW, GL = 64 / GS;
+    const MoveDst& dst = a.dst[1];
+    const Fmt& fm = dst.f;
+    const int t = lane % TPW, h = lane / TPW;
+    const int p = k * TPW + t, r = p - plo;
+    const bool valid = r >= 0 && r < n;
+    const int e = sh.lst[1][valid ? r : 0];
+    const int cl = e >> 6, s = e & 63;
+    float sv[GL];
+    int zv[GL];
+#pragma unroll
+    for (int gl = 0; gl < GL; gl++) {
+        const int gi = h * GL + gl;
+        sv[gl] = sh.vs[cl][gi * BT + s];
+        zv[gl] = sh.vz[cl][gi * BT + s];
+    }
+    const uint32_t* row = sh.vsec[cl] + 64 * h * 12;
+    const int bit = s * 6, ws = bit >> 5, bsh = bit & 31;
+    int cmn[GL], cmx[GL];
+#pragma unroll
+    for (int gl = 0; gl < GL; gl++) { cmn[gl] = 63; cmx[gl] = 0; }
+#pragma unroll
+    for (int j = 0; j < 64; j++) {
+        const int c = (int)staged_code<6>(row, j, ws, bsh);
+        cmn[j / GS] = min(cmn[j / GS], c);
+        cmx[j / GS] = max(cmx[j / GS], c);
+    }
+    float qs[GL], qrc[GL];
+    int qz[GL], cq[GL];
+    bool gslow[GL], cst[GL];
+    {
+#pragma clang fp contract(off)
+#pragma unroll
+        for (int gl = 0; gl < GL; gl++) {
+            const float xa = (float)(cmn[gl] - zv[gl]) * sv[gl];
+            const float xb = (float)(cmx[gl] - zv[gl]) * sv[gl];
+            const int ka = fkey(xa), kb = fkey(xb);
+            const float mn = fkey_value(min(ka, kb)), mx = fkey_value(max(ka, kb));
+            const float lo = mn < 0.0f ? mn : 0.0f;
+            const float hi = mx > 0.0f ? mx : 0.0f;
+            const float rr = hi - lo;
+            const float s0 = rr * 0x1.111112p-4f;  // RN(1/15)
+            const float sc = __builtin_fmaf(__builtin_fmaf(-s0, 15.0f, rr), 0x1.111112p-4f, s0);
+            const float rc = __builtin_amdgcn_rcpf(sc);
+            bool slow = !(sc >= 0x1p-126f && sc <= 0x1.fffffep127f);
+            float zf = slow ? 0.0f : rint_quot(-lo, sc, rc, slow);
+            if (slow) zf = rintf(-lo / sc);
+            int z = (int)zf;
+            z = z < 0 ? 0 : (z > 15 ? 15 : z);
+            qs[gl] = sc;
+            qrc[gl] = rc;
+            qz[gl] = z;
+            gslow[gl] = !(sc >= 0x1p-126f && sc <= 0x1.fffffep127f);
+            cst[gl] = mn == mx;
+            cq[gl] = mn > 0.0f ? 1 : 0;
+            if (cst[gl]) {
+                qs[gl] = mn > 0.0f ? mn : (mn < 0.0f ? -mn : 0.0f);
+                qz[gl] = mn < 0.0f ? 1 : 0;
+            }
+        }
+    }
+    const int blk0 = k * TPW / BT * BT;
+    sink.blk = sh.dblk[1][blk0 / BT - plo / BT];
+    uint8_t* dch = dst.pool + ((int64_t)sink.blk * fm.H + kvh) * fm.chunk;
+    sink.dch = dch;
+    sink.off_vc = fm.off_vc;
+    sink.vrow = fm.vrow;
+    sink.lo = plo - blk0;
+    sink.hi = plo + n - blk0;
+    if (valid) {
+        const int ds = p % BT;
+#pragma unroll
+        for (int gl = 0; gl < GL; gl++) {
+            const int gi = h * GL + gl;
+            ((float*)(dch + fm.off_vs))[gi * BT + ds] = qs[gl];
+            dch[fm.off_vz + gi * BT + ds] = (uint8_t)qz[gl];
+        }
+    }
+    auto st = sh.stage[wave];
+    for (int jb = 0; jb < 4; jb++) {
+        int code[16];
+#pragma unroll
+        for (int j = 0; j < 16; j++) code[j] = (int)staged_code<6>(row, 16 * jb + j, ws, bsh);
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+#pragma clang fp contract(off)
+            const int jj = 16 * jb + j, gl = jj / GS;
+            const int c = code[j];
+            const float x = (float)(c - zv[gl]) * sv[gl];
+            bool slow = gslow[gl];
+            float qf = rint_quot(x, qs[gl], qrc[gl], slow);
+            if (slow) qf = rintf(x / qs[gl]);
+            int q = (int)qf + qz[gl];
+            q = q < 0 ? 0 : (q > 15 ? 15 : q);
+            st[h * 16 + j][t] = (uint8_t)(cst[gl] ? cq[gl] : q);
+        }
+        wave_lds_sync();
+        pack_stage<D, 4>(st, sink, k, jb, lane);
+        wave_lds_sync();
+    }
+}
+
+template <int D, int GS, int VS>
+__device__ __forceinline__ void tier_compact_body(CmpShared<D, D / GS>& sh, const MoveArgs& a, const MoveSrc& S,
+                                                  int b, int kvh, int len, int c0, int nc, int par)
+{
+    constexpr int NG = D / GS;
+    const Fmt& fs = S.f;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int32_t* brow = S.bt + (int64_t)b * S.max_blocks;
+    const bool copy_m = a.dst[1].f.vb == VS;
+    const bool requant = VS == 6 && !copy_m;
+
+    // 1. each wave's chunk: its V section (and, when MID survivors are
+    //    requantised, its V scales and zeros) copied into LDS by the memory
+    //    unit, its rows moved by the lanes.  Everything the windows read
+    //    from memory is staged here, before the barrier.
+    constexpr int NPC = D * VS * 64 / 8 / 16;  // 16-byte pieces of a V section
+    static_assert(NPC % 64 == 0, "whole wave copies");
+    const bool live = wave < nc;
+    const int c = c0 + min(wave, nc - 1);
+    const int tok = c * BT + lane;
+    const int traw = S.tiers[(int64_t)b * S.tier_stride + min(tok, len - 1)];
+    const int2 base_c = S.blk_base[(int64_t)b * S.base_stride + c];
+    const int2 base = S.blk_base[(int64_t)b * S.base_stride + c0];
+    const int32_t blk_c = brow[c];
+    if (tid < 16) {  // destination blocks of each segment from the run's first position on
+        const int seg = tid / 8;
+        const MoveDst& d = seg == 0 ? a.dst[0] : a.dst[1];
+        const int first = (seg == 0 ? base.x : base.y) / BT;
+        sh.dblk[seg][tid % 8] = d.bt[(int64_t)b * d.max_blocks + min(first + tid % 8, d.max_blocks - 1)];
+    }
+    const uint8_t* sch = S.pool + ((int64_t)blk_c * fs.H + kvh) * fs.chunk;
+    if (live) {
+        typedef __attribute__((address_space(1))) void gvoid;
+        typedef __attribute__((address_space(3))) void lvoid;
+#pragma unroll
+        for (int i = 0; i < NPC / 64; i++)
+            __builtin_amdgcn_global_load_lds((gvoid*)(sch + fs.off_vc + 16 * (64 * i + lane)),
+                                             (lvoid*)((uint8_t*)sh.vsec[wave] + 1024 * i), 16, 0, 0);
+        if (requant) {
+            if (lane < NG * 16)
+                __builtin_amdgcn_global_load_lds((gvoid*)(sch + fs.off_vs + 16 * lane), (lvoid*)sh.vs[wave], 16, 0,
+                                                 0);
+            if (lane < NG * 4)
+                __builtin_amdgcn_global_load_lds((gvoid*)(sch + fs.off_vz + 16 * lane), (lvoid*)sh.vz[wave], 16, 0,
+                                                 0);
+        }
+    }
+    const int tw = live && tok < len ? traw : 0;
+    const uint64_t mk0 = __ballot(tw == 2), mk1 = __ballot(tw == 1);
+    const uint64_t below = (1ull << lane) - 1ull;
+    const int r0 = __popcll(mk0 & below), r1 = __popcll(mk1 & below);
+    if (lane == 0) {
+        sh.cnt[0][wave] = __popcll(mk0);
+        sh.cnt[1][wave] = __popcll(mk1);
+    }
+    if (tid < 2) sh.cmeta[par][tid][0] = 0;  // nothing carried out yet (this parity was read by the run before last)
+    if (mk0 && tw == 2) compact_row_any<D, NG, 0>(a, fs, sch, base_c.x + r0, b, kvh, lane, true);
+    if (mk1 && tw == 1) compact_row_any<D, NG, 1>(a, fs, sch, base_c.y + r1, b, kvh, lane, copy_m);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the V sections are in LDS
+    __syncthreads();
+
+    // 2. survivors of the run per segment, in slot order
+    int pre0 = 0, pre1 = 0, n0 = 0, n1 = 0;
+#pragma unroll
+    for (int w = 0; w < CMP_R; w++) {
+        const int x0 = sh.cnt[0][w], x1 = sh.cnt[1][w];
+        if (w < wave) { pre0 += x0; pre1 += x1; }
+        n0 += x0;
+        n1 += x1;
+    }
+    if (tw == 2) sh.lst[0][pre0 + r0] = (uint16_t)((wave << 6) | lane);
+    else if (tw == 1) sh.lst[1][pre1 + r1] = (uint16_t)((wave << 6) | lane);
+    __syncthreads();
+
+    // 3. windows of destination slots: MID first (the costlier ones), then HIGH
+    constexpr int TPW = CmpShared<D, NG>::TPW;
+    const int win0 = n0 ? (base.x + n0 - 1) / TPW - base.x / TPW + 1 : 0;
+    const int win1 = n1 ? (base.y + n1 - 1) / TPW - base.y / TPW + 1 : 0;
+    WordSink sk[2];
+#pragma unroll
+    for (int seg = 0; seg < 2; seg++) {
+        sk[seg].cin = sh.cmeta[par ^ 1][seg][0] ? sh.carry[par ^ 1][seg] : nullptr;
+        sk[seg].cin_lo = sh.cmeta[par ^ 1][seg][1];
+        sk[seg].cout = sh.carry[par][seg];
+        sk[seg].cmeta_out = sh.cmeta[par][seg];
+    }
+    for (int q = wave; q < win0 + win1; q += 4) {
+        if (q < win1) {
+            const int k = base.y / TPW + q;
+            if (VS == 4) compact_copy<D, NG, 4>(sh, a.dst[1], kvh, 1, k, base.y, n1, wave, lane, sk[1]);
+            else compact_requant<D, GS>(sh, a, kvh, k, base.y, n1, wave, lane, sk[1]);
+        } else if (VS == 6) {
+            const int k = base.x / TPW + q - win1;
+            compact_copy<D, NG, 6>(sh, a.dst[0], kvh, 0, k, base.x, n0, wave, lane, sk[0]);
+        }
+    }
+    __syncthreads();
+    // a segment without survivors in this run passes its carry on
+#pragma unroll
+    for (int seg = 0; seg < 2; seg++) {
+        if ((seg == 0 ? n0 : n1) != 0) continue;
+        for (int d = tid; d < D; d += 256) sh.carry[par][seg][d] = sh.carry[par ^ 1][seg][d];
+        if (tid < 8) sh.cmeta[par][seg][tid] = sh.cmeta[par ^ 1][seg][tid];
+    }
+}
+
+// grid (groups of per_wg runs of CMP_R chunks, KV heads, batch x sources);
+// 256 threads; GS channels per quantisation group.  Sources are 6-bit (HIGH copied, MID
+// requantised) or 4-bit (MID copied).
+template <int D, int GS>
+__device__ __forceinline__ void tier_compact(const MoveArgs& a)
+{
+    __shared__ CmpShared<D, D / GS> sh;
+    const int si = blockIdx.z % a.nsrc, b = blockIdx.z / a.nsrc, kvh = blockIdx.y;
+    if (a.n_high[b] < 0 || a.n_mid[b] < 0) return;  // no room: nothing is written
+    const MoveSrc& S = si == 0 ? a.src[0] : a.src[1];
+    const int len = max(0, min(S.lens[b], S.len_cap));
+    const int nblocks = (len + BT - 1) / BT;
+    const int S_ = a.per_wg;
+    if (blockIdx.x * S_ * CMP_R >= nblocks) return;
+    if (threadIdx.x < 4) sh.cmeta[threadIdx.x / 2][threadIdx.x % 2][0] = 0;
+    const int runs = min(S_, (nblocks - blockIdx.x * S_ * CMP_R + CMP_R - 1) / CMP_R);
+    auto each_run = [&](auto vs) __attribute__((always_inline)) {
+#pragma nounroll
+        for (int r = 0; r < runs; r++) {
+            const int c0 = (blockIdx.x * S_ + r) * CMP_R;
+            tier_compact_body<D, GS, decltype(vs)::value>(sh, a, S, b, kvh, len, c0, min(CMP_R, nblocks - c0), r & 1);
+            __syncthreads();
+        }
+    };
+    if (S.f.vb == 6) each_run(std::integral_constant<int, 6>());
+    else each_run(std::integral_constant<int, 4>());
+    const int r = runs;
+    // the words the last runs ended inside: merged with the neighbours' bits
+    const int par = (r - 1) & 1;
+#pragma unroll
+    for (int seg = 0; seg < 2; seg++) {
+        const int32_t* m = sh.cmeta[par][seg];
+        if (!m[0]) continue;
+        const MoveDst& d = seg == 0 ? a.dst[0] : a.dst[1];
+        const uint32_t mask = (m[2] == 32 ? 0xFFFFFFFFu : ((1u << m[2]) - 1u)) & ~((1u << m[1]) - 1u);
+        uint8_t* dch = d.pool + ((int64_t)m[4] * d.f.H + kvh) * d.f.chunk + d.f.off_vc;
+        for (int ch = threadIdx.x; ch < D; ch += 256) {
+            uint32_t* p = (uint32_t*)(dch + ch * d.f.vrow) + m[3];
+            atomicAnd(p, ~mask);
+            atomicOr(p, sh.carry[par][seg][ch] & mask);
+        }
+    }
+}
+
+// Four waves per SIMD for groups of 32 or 64 channels (at most 128
+// registers); groups of 16 need more registers than that.
+template <int D, int GS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void tier_compact_kernel(MoveArgs a)
+{
+    tier_compact<D, GS>(a);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void tier_compact16_kernel(MoveArgs a)
+{
+    tier_compact<D, 16>(a);
+}
+
 hipError_t launch_tiering(const TierSource* src, int nsrc, float tau_low, float tau_high, const TierDest& h,
                           const TierDest& m, int32_t* n_high, int32_t* n_mid, int32_t batch, void* workspace,
                           hipStream_t stream)
@@ -622,8 +1135,27 @@ hipError_t launch_tiering(const TierSource* src, int nsrc, float tau_low, float 
         else hipLaunchKernelGGL(tier_move_kernel<128>, grid, dim3(256), 0, stream, x);
     };
     if (!in_place) {
-        launch(a, dim3((unsigned)((max_blocks + MOVE_CHUNKS - 1) / MOVE_CHUNKS), (unsigned)h.f.H,
-                       (unsigned)(batch * nsrc)));
+        // V codes: 6-bit sources (HIGH copied, MID requantised) or 4-bit ones (MID copied)
+        for (int i = 0; i < nsrc; i++)
+            if (!(src[i].f.vb == 6 || (src[i].f.vb == 4 && m.f.vb == 4))) return hipErrorInvalidValue;
+        if (h.f.vb != 6 || m.f.vb != 4) return hipErrorInvalidValue;
+        // runs per workgroup: as many as keep about 1024 workgroups in the
+        // grid (fewer workgroup edges, whose words take atomics), at most CMP_S
+        int64_t runs = 0;
+        for (int i = 0; i < nsrc; i++) runs += (int64_t)batch * h.f.H * ((src[i].max_len + BT * CMP_R - 1) / (BT * CMP_R));
+        a.per_wg = (int32_t)std::max<int64_t>(1, std::min<int64_t>(CMP_S, runs / 1024));
+        const int span = CMP_R * a.per_wg;
+        const dim3 grid((unsigned)((max_blocks + span - 1) / span), (unsigned)h.f.H, (unsigned)(batch * nsrc));
+        auto go = [&](auto k) { hipLaunchKernelGGL(k, grid, dim3(256), 0, stream, a); };
+        if (h.f.D == 64) {
+            if (h.f.g == 64) go(tier_compact_kernel<64, 64>);
+            else if (h.f.g == 32) go(tier_compact_kernel<64, 32>);
+            else go(tier_compact16_kernel<64>);
+        } else {
+            if (h.f.g == 64) go(tier_compact_kernel<128, 64>);
+            else if (h.f.g == 32) go(tier_compact_kernel<128, 32>);
+            else go(tier_compact16_kernel<128>);
+        }
         return hipGetLastError();
     }
     // one source per launch, in destination order; a source compacted in
