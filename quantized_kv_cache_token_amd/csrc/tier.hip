@@ -12,26 +12,17 @@
 //    writes their tiers and the destination positions of every 64-token
 //    block's first HIGH and MID survivor.  The first chunk writes the two
 //    counts (negative when a destination has no room).
-//  tier_move: one workgroup per (8 consecutive source chunks, KV head,
-//    sequence, source).  Each source chunk is read once, whole and
-//    coalesced; its survivors go to consecutive destination positions.
-//    A destination that is its source segment itself (the same pool and
-//    block table) is compacted in place.  A survivor never moves to a later
-//    position, so a chunk's survivors land in its own block or earlier
-//    ones.  Then each workgroup moves one chunk: it takes the chunk from a
-//    ticket counter (chunks of a sequence in order, its KV heads together),
-//    reads it whole, marks it read, and waits until every chunk whose block
-//    it writes into has been marked read by all KV heads.  Those chunks hold
-//    earlier tickets, taken by workgroups that are running or done and that
-//    mark their chunk before they wait for anything, so the wait ends.  The
-//    sources run one launch after the other, in destination order, so that
-//    the MID source's chunks are read before demoted tokens land in them.  K
-//    rows, scales and zeros are stored straight from the loaded pieces; V
-//    codes are copied (same width) or dequantised in fp32 and requantised
-//    at 4 bits (V6 -> V4) into an LDS block of destination codes, which is
-//    packed into the channel-major rows when it fills or the workgroup ends.
-//    Only the words a neighbouring workgroup also writes are merged with
-//    atomics.
+//  tier_compact: the survivors' rows, scales and zeros and V codes, run by
+//    run (4 source chunks of one sequence, KV head and source) in
+//    destination order; see the section of that name below.  A
+//    destination that is its source segment itself (the same pool and
+//    block table) is compacted in place: a survivor never moves to a later
+//    position, so a run writes only into its own blocks or earlier ones;
+//    workgroups then take their runs from a ticket counter and wait, before
+//    writing into blocks that earlier workgroups own, until those blocks
+//    have been read.  The sources run one launch after the other, in
+//    destination order, so that the MID source's chunks are read before
+//    demoted tokens land in them.
 #include <hip/hip_fp16.h>
 
 #include "lkv_internal.h"
@@ -183,10 +174,6 @@ __global__ __launch_bounds__(256) void tier_write_kernel(TierScanArgs a)
     if ((tid & 7) == 0 && j0 < len) src.blk_base[(int64_t)b * src.base_stride + j0 / BT] = make_int2(ph, pm);
 }
 
-constexpr int MOVE_CHUNKS = 8;   // source chunks per workgroup, in token order
-constexpr int MOVE_PIECES = 5;   // 16-byte pieces per thread of one chunk (chunks up to 20 KiB)
-constexpr int MOVE_META = 5120;  // bytes of the scale and zero sections (D / g = 8 groups)
-
 struct MoveSrc {
     Fmt f;
     const uint8_t* pool;
@@ -213,337 +200,19 @@ struct MoveArgs {
     const int32_t* n_high;
     const int32_t* n_mid;
     int32_t nsrc;
-    int32_t per_wg;  // source chunks per workgroup
-    // in place (flags != nullptr): one source, one chunk per workgroup taken
-    // from *ticket; flags[b][c] counts the KV heads that have read chunk c;
-    // inplace_seg is the destination (0 HIGH, 1 MID) that is the source
+    int32_t per_wg;  // runs per workgroup
+    // in place: one source; a workgroup's (sequence, group of runs, KV head)
+    // comes from *ticket; flags[b][run] counts the KV heads that have read
+    // a run's chunks; inplace_seg is the destination (0 HIGH, 1 MID) that
+    // is the source
     uint32_t* ticket;
     uint32_t* flags;
     int32_t flag_stride;
     int32_t inplace_seg;
-    int32_t gx;      // chunks per sequence in the ticket order
+    int32_t gx;      // groups of runs per sequence in the ticket order
 };
 
-__device__ __forceinline__ uint8_t* dst_chunk(const MoveDst& d, int b, int pos, int kvh)
-{
-    return d.pool + ((int64_t)d.bt[(int64_t)b * d.max_blocks + pos / BT] * d.f.H + kvh) * d.f.chunk;
-}
-
-// Packs destination slots [slo, shi) of every channel row from the staged
-// codes into chunk dch; words shared with slots outside the range are
-// merged with atomics.
-template <int D>
-__device__ __forceinline__ void flush_block(const Fmt& fd, uint8_t* dch, const uint8_t (*st)[VPITCH], int slo, int shi)
-{
-    if (fd.vb == 6) pack_v_rows<6, 16, 3, D>(st, dch, fd.off_vc, fd.vrow, slo, shi);
-    else pack_v_rows<4, 8, 1, D>(st, dch, fd.off_vc, fd.vrow, slo, shi);
-}
-
-// Where slot s of a source chunk goes: its segment (0 HIGH, 1 MID, -1
-// evicted), destination chunk and slot.  The survivors of segment i (mask
-// mk_i) take consecutive positions from pos_i in slot order; a chunk's
-// survivors span at most two destination blocks (dA_i: pos_i's block, dB_i:
-// the next one).
-__device__ __forceinline__ int slot_dest(int s, uint64_t mk0, uint64_t mk1, int pos0, int pos1, uint8_t* dA0,
-                                         uint8_t* dB0, uint8_t* dA1, uint8_t* dB1, uint8_t** dch, int* ds)
-{
-    const uint64_t bit = 1ull << s, lt = bit - 1ull;
-    if (mk0 & bit) {
-        const int P = pos0 + __popcll(mk0 & lt);
-        *dch = P / BT == pos0 / BT ? dA0 : dB0;
-        *ds = P % BT;
-        return 0;
-    }
-    if (mk1 & bit) {
-        const int P = pos1 + __popcll(mk1 & lt);
-        *dch = P / BT == pos1 / BT ? dA1 : dB1;
-        *ds = P % BT;
-        return 1;
-    }
-    return -1;
-}
-
-// V codes of survivor ranks [r0, r1) of one segment, copied at the source
-// width into staged slots r + sh of the channel-major stage.
-template <int D>
-__device__ __forceinline__ void copy_codes(uint8_t (*st)[VPITCH], const uint8_t* src_of, const uint32_t* vsrc,
-                                           int vrow_w, int vb, int r0, int r1, int sh)
-{
-    const int cnt = (r1 - r0) * D;
-    for (int i = threadIdx.x; i < cnt; i += 256) {
-        const int r = r0 + i / D, d = i % D;
-        st[d][r + sh] = (uint8_t)get_field(vsrc + d * vrow_w, src_of[r], vb);
-    }
-}
-
-// MID survivor ranks [r0, r1) from 6-bit V: dequantised in fp32 and
-// requantised at the destination width, four tokens per wave at a time
-// (lane: channels P * lane + p); codes into staged slots r + sh, scales and
-// zeros straight to the destination.
-template <int D, int GS>
-__device__ __forceinline__ void requant_codes_g(uint8_t (*st)[VPITCH], const uint8_t* src_of, const uint32_t* vsrc,
-                                              int vrow_w, const Fmt& fs, const Fmt& fm, const float* m_vs,
-                                              const uint8_t* m_vz, int pos, uint8_t* dA, uint8_t* dB, int r0, int r1,
-                                              int sh)
-{
-    constexpr int P = D / 64, T = 4;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int rb = r0 + T * wave; rb < r1; rb += 4 * T) {
-        float x[T][P];
-        QRow<P> q[T];
-#pragma unroll
-        for (int t = 0; t < T; t++) {
-            const int s = src_of[min(rb + t, r1 - 1)];
-#pragma unroll
-            for (int p = 0; p < P; p++) {
-                const int d = P * lane + p, gi = d / fs.g;
-                const uint32_t code = get_field(vsrc + d * vrow_w, s, fs.vb);
-                x[t][p] = (float)((int)code - (int)m_vz[gi * BT + s]) * m_vs[gi * BT + s];  // one fp32 rounding
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < T; t++) quantize_fast<P, GS>(x[t], fm.vb, q[t]);
-#pragma unroll
-        for (int t = 0; t < T; t++)
-            if (q[t].slow) quantize_exact<P>(x[t], fm.vb, q[t]);
-#pragma unroll
-        for (int t = 0; t < T; t++) {
-            const int r = rb + t;
-            if (r >= r1) break;
-            const int P_ = pos + r;
-            uint8_t* dch = P_ / BT == pos / BT ? dA : dB;
-#pragma unroll
-            for (int p = 0; p < P; p++) st[P * lane + p][r + sh] = (uint8_t)q[t].q[p];
-            if ((P * lane) % GS == 0) {
-                const int gi = P * lane / GS;
-                ((float*)(dch + fm.off_vs))[gi * BT + P_ % BT] = q[t].s;
-                dch[fm.off_vz + gi * BT + P_ % BT] = (uint8_t)q[t].z;
-            }
-        }
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void requant_codes(uint8_t (*st)[VPITCH], const uint8_t* src_of, const uint32_t* vsrc,
-                                              int vrow_w, const Fmt& fs, const Fmt& fm, const float* m_vs,
-                                              const uint8_t* m_vz, int pos, uint8_t* dA, uint8_t* dB, int r0, int r1,
-                                              int sh)
-{
-    if (fm.g == 64) requant_codes_g<D, 64>(st, src_of, vsrc, vrow_w, fs, fm, m_vs, m_vz, pos, dA, dB, r0, r1, sh);
-    else if (fm.g == 32) requant_codes_g<D, 32>(st, src_of, vsrc, vrow_w, fs, fm, m_vs, m_vz, pos, dA, dB, r0, r1, sh);
-    else requant_codes_g<D, 16>(st, src_of, vsrc, vrow_w, fs, fm, m_vs, m_vz, pos, dA, dB, r0, r1, sh);
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void tier_move_kernel(MoveArgs a)
-{
-    __shared__ uint32_t vsrc[D * 12 + 4];        // the V section (up to 6-bit), plus slack for straddling reads
-    __shared__ uint32_t meta[MOVE_META / 4];     // K scales, V scales, K zeros, V zeros
-    __shared__ uint8_t stage[2][D][VPITCH];      // destination codes of the current HIGH / MID block
-    __shared__ uint8_t src_of[4][2][BT];         // per wave: source slot of each survivor rank
-
-    __shared__ int ticket_of;
-    const bool in_place = a.flags != nullptr;
-    int si, b, kvh, bx;
-    if (in_place) {  // every workgroup takes a ticket before anything else
-        if (threadIdx.x == 0) ticket_of = (int)atomicAdd(a.ticket, 1u);
-        __syncthreads();
-        const int t = ticket_of, H = a.src[0].f.H;
-        si = 0;
-        kvh = t % H;
-        bx = t / H % a.gx;
-        b = t / H / a.gx;
-    } else {
-        si = blockIdx.z % a.nsrc;
-        b = blockIdx.z / a.nsrc;
-        kvh = blockIdx.y;
-        bx = blockIdx.x;
-    }
-    if (a.n_high[b] < 0 || a.n_mid[b] < 0) return;  // no room: nothing is written
-    const MoveSrc& S = si == 0 ? a.src[0] : a.src[1];
-    const Fmt& fs = S.f;
-    const int len = max(0, min(S.lens[b], S.len_cap));
-    const int nblocks = (len + BT - 1) / BT;
-    const int c0 = bx * a.per_wg;
-    if (c0 >= nblocks) return;
-    const int c1 = min(nblocks, c0 + a.per_wg);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int2 base = S.blk_base[(int64_t)b * S.base_stride + c0];
-    // next destination position of each segment, and the first position this
-    // workgroup staged in the segment's current block
-    int pos0 = base.x, pos1 = base.y, lo0 = base.x, lo1 = base.y;
-    const int krows = BT * fs.krow, vbytes = D * fs.vrow;
-    const int npieces = (int)(fs.chunk / 16);
-    const int vrow_w = fs.vrow / 4;
-    const float* m_ks = (const float*)meta;
-    const float* m_vs = (const float*)((const uint8_t*)meta + (fs.off_vs - fs.off_ks));
-    const uint8_t* m_kz = (const uint8_t*)meta + (fs.off_kz - fs.off_ks);
-    const uint8_t* m_vz = (const uint8_t*)meta + (fs.off_vz - fs.off_ks);
-    // destination layouts: both hold the source's K format, so K rows sit at
-    // the same offsets; the scale and zero sections differ with the V width
-    const Fmt& fh = a.dst[0].f;
-    const Fmt& fm = a.dst[1].f;
-    const bool copy_m = fm.vb == fs.vb;  // MID survivors keep their V codes (a MID source)
-
-    // The pieces of the next chunk are in flight while a chunk is written
-    // out; its tiers come with them and the block of the one after.  The
-    // next chunk's loads are issued after the barrier that precedes this
-    // chunk's stores, which never touch the next chunk's block, and they
-    // complete before the barrier that precedes its own stores: in place,
-    // every chunk is read before it is overwritten.
-    auto tiers_of = [&](int c) __attribute__((always_inline)) {
-        return lane < min(BT, len - c * BT) ? (int)S.tiers[(int64_t)b * S.tier_stride + c * BT + lane] : 0;
-    };
-    auto load_pieces = [&](uint4 (&pc)[MOVE_PIECES], int blk) __attribute__((always_inline)) {
-        const uint4* sch = (const uint4*)(S.pool + ((int64_t)blk * fs.H + kvh) * fs.chunk);
-#pragma unroll
-        for (int k = 0; k < MOVE_PIECES; k++) {
-            const int p = tid + 256 * k;
-            pc[k] = p < npieces ? sch[p] : make_uint4(0u, 0u, 0u, 0u);
-        }
-    };
-    const int32_t* brow = S.bt + (int64_t)b * S.max_blocks;
-    uint4 pn[MOVE_PIECES];
-    load_pieces(pn, brow[c0]);
-    int t_next = tiers_of(c0);
-    int blk_after = c0 + 1 < c1 ? brow[c0 + 1] : 0;
-    if (in_place) {
-        // The chunk (per_wg is 1) is read once every thread's loads have
-        // returned their data: an empty statement that takes each loaded
-        // register makes the compiler wait for them.  Only then is it marked
-        // read.  The order needed is a load's return before another
-        // workgroup's store to the same bytes, so no cache writeback or
-        // invalidation is involved: the mark and its polling are relaxed
-        // device-scope atomics.  Then wait for the chunks of the blocks this
-        // one writes into, first / 64 .. c0 - 1, read by every KV head.
-#pragma unroll
-        for (int k = 0; k < MOVE_PIECES; k++)
-            asm volatile("" ::"v"(pn[k].x), "v"(pn[k].y), "v"(pn[k].z), "v"(pn[k].w) : "memory");
-        __syncthreads();
-        uint32_t* frow = a.flags + (int64_t)b * a.flag_stride;
-        if (tid == 0) __hip_atomic_fetch_add(frow + c0, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t heads = (uint32_t)fs.H;
-        for (int j = (a.inplace_seg == 0 ? base.x : base.y) / BT + tid; j < c0; j += 256)
-            while (__hip_atomic_load(frow + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < heads)
-                __builtin_amdgcn_s_sleep(2);
-        __syncthreads();
-    }
-    for (int c = c0; c < c1; c++) {
-        uint4 pc[MOVE_PIECES];
-#pragma unroll
-        for (int k = 0; k < MOVE_PIECES; k++) pc[k] = pn[k];
-        // tiers of the chunk's 64 slots; every wave derives the same masks
-        const int t = t_next;
-        const int blk_next = blk_after;
-        const bool more = c + 1 < c1;
-        if (more) {
-            t_next = tiers_of(c + 1);
-            blk_after = c + 2 < c1 ? brow[c + 2] : 0;
-        }
-        const uint64_t mk0 = __ballot(t == 2), mk1 = __ballot(t == 1);
-        const uint64_t below = (1ull << lane) - 1ull;
-        if (t == 2) src_of[wave][0][__popcll(mk0 & below)] = (uint8_t)lane;
-        else if (t == 1) src_of[wave][1][__popcll(mk1 & below)] = (uint8_t)lane;
-        const int n0 = __popcll(mk0), n1 = __popcll(mk1);
-        if (n0 + n1 == 0) {
-            if (more) load_pieces(pn, blk_next);
-            continue;
-        }
-        // destination chunks: the block of each segment's next position and
-        // the one after it
-        uint8_t *dA0 = nullptr, *dB0 = nullptr, *dA1 = nullptr, *dB1 = nullptr;
-        if (n0) {
-            dA0 = dst_chunk(a.dst[0], b, pos0, kvh);
-            dB0 = pos0 % BT + n0 > BT ? dst_chunk(a.dst[0], b, pos0 + BT, kvh) : dA0;
-        }
-        if (n1) {
-            dA1 = dst_chunk(a.dst[1], b, pos1, kvh);
-            dB1 = pos1 % BT + n1 > BT ? dst_chunk(a.dst[1], b, pos1 + BT, kvh) : dA1;
-        }
-        __syncthreads();  // the previous chunk's readers of vsrc and meta are done
-        if (more) load_pieces(pn, blk_next);
-#pragma unroll
-        for (int k = 0; k < MOVE_PIECES; k++) {
-            const int off = 16 * (tid + 256 * k);
-            if (off >= 16 * npieces) continue;
-            if (off >= fs.off_ks) {
-                *(uint4*)((uint8_t*)meta + (off - fs.off_ks)) = pc[k];
-            } else if (off >= fs.off_vc) {
-                if (off < fs.off_vc + vbytes) *(uint4*)((uint8_t*)vsrc + (off - fs.off_vc)) = pc[k];
-            } else if (off < krows) {  // a K row piece: stored straight to its survivor's row
-                uint8_t* dch;
-                int ds;
-                if (slot_dest(off / fs.krow, mk0, mk1, pos0, pos1, dA0, dB0, dA1, dB1, &dch, &ds) >= 0)
-                    *(uint4*)(dch + fh.off_kc + ds * fh.krow + off % fs.krow) = pc[k];
-            }
-        }
-        __syncthreads();
-        // K scales and zeros of every survivor; V scales and zeros where V is copied
-        for (int i = tid; i < fs.ngroups * BT; i += 256) {
-            uint8_t* dch;
-            int ds;
-            const int seg = slot_dest(i % BT, mk0, mk1, pos0, pos1, dA0, dB0, dA1, dB1, &dch, &ds);
-            if (seg < 0) continue;
-            ds += i / BT * BT;
-            ((float*)(dch + (seg == 0 ? fh.off_ks : fm.off_ks)))[ds] = m_ks[i];
-            dch[(seg == 0 ? fh.off_kz : fm.off_kz) + ds] = m_kz[i];
-            if (seg == 0 || copy_m) {
-                ((float*)(dch + (seg == 0 ? fh.off_vs : fm.off_vs)))[ds] = m_vs[i];
-                dch[(seg == 0 ? fh.off_vz : fm.off_vz) + ds] = m_vz[i];
-            }
-        }
-        // V codes of each segment into its staged block; a block that fills
-        // is packed out and the rest of the chunk's survivors start the next
-        // one.  HIGH codes are always copied (6-bit to 6-bit).
-        if (n0) {
-            const int first = min(n0, BT - pos0 % BT);
-            copy_codes<D>(stage[0], src_of[wave][0], vsrc, vrow_w, fs.vb, 0, first, pos0 % BT);
-            if (pos0 % BT + n0 >= BT) {  // the block is complete
-                __syncthreads();
-                flush_block<D>(fh, dA0, stage[0], lo0 - pos0 / BT * BT, BT);
-                __syncthreads();
-                lo0 = (pos0 / BT + 1) * BT;
-                if (first < n0) copy_codes<D>(stage[0], src_of[wave][0], vsrc, vrow_w, fs.vb, first, n0, -first);
-            }
-            pos0 += n0;
-        }
-        if (n1) {
-            const int first = min(n1, BT - pos1 % BT);
-            if (copy_m)
-                copy_codes<D>(stage[1], src_of[wave][1], vsrc, vrow_w, fs.vb, 0, first, pos1 % BT);
-            else
-                requant_codes<D>(stage[1], src_of[wave][1], vsrc, vrow_w, fs, fm, m_vs, m_vz, pos1, dA1, dB1,
-                                 0, first, pos1 % BT);
-            if (pos1 % BT + n1 >= BT) {
-                __syncthreads();
-                flush_block<D>(fm, dA1, stage[1], lo1 - pos1 / BT * BT, BT);
-                __syncthreads();
-                lo1 = (pos1 / BT + 1) * BT;
-                if (first < n1) {
-                    if (copy_m)
-                        copy_codes<D>(stage[1], src_of[wave][1], vsrc, vrow_w, fs.vb, first, n1, -first);
-                    else
-                        requant_codes<D>(stage[1], src_of[wave][1], vsrc, vrow_w, fs, fm, m_vs, m_vz, pos1, dA1,
-                                         dB1, first, n1, -first);
-                }
-            }
-            pos1 += n1;
-        }
-    }
-    // the partly filled last block of each segment
-    if (pos0 > lo0) {
-        __syncthreads();
-        const int blk0 = lo0 / BT * BT;
-        flush_block<D>(fh, dst_chunk(a.dst[0], b, lo0, kvh), stage[0], lo0 - blk0, pos0 - blk0);
-    }
-    if (pos1 > lo1) {
-        __syncthreads();
-        const int blk0 = lo1 / BT * BT;
-        flush_block<D>(fm, dst_chunk(a.dst[1], b, lo1, kvh), stage[1], lo1 - blk0, pos1 - blk0);
-    }
-}
-
-// ---- Out-of-place compaction: tier_compact_kernel<D> ----
+// ---- Compaction: tier_compact_kernel<D, g, in place> ----
 //
 // One workgroup per run of CMP_R consecutive source chunks of one
 // (sequence, KV head, source); wave w owns chunk w of the run.
@@ -624,15 +293,20 @@ __device__ __forceinline__ void compact_row_any(const MoveArgs& a, const Fmt& fs
     else compact_row<K4, NG, SEG>(a, fs, sch, P, b, kvh, lane, vcopy);
 }
 
-template <int D, int NG>
+template <int D, int NG, bool IP = false>
 struct alignas(16) CmpShared {
     static constexpr int NH = D / 64;          // channel halves: lanes per survivor
     static constexpr int TPW = 64 / NH;        // destination slots per window
     static constexpr int CW = D * 12 + 4;      // words per staged V section (6-bit rows; 4-bit use less)
     static constexpr int SP = TPW + 16;        // stage row pitch (bytes, a multiple of 16)
-    uint32_t vsec[CMP_R][CW];
-    float vs[CMP_R][NG * BT];                  // source V scales and zeros (requantised MID)
-    uint8_t vz[CMP_R][NG * BT];
+    // in place (IP) whole source chunks, so that a run has read everything
+    // before it marks its chunks read; otherwise only the V sections and,
+    // for requantised MID survivors, the V scales and zeros
+    static constexpr int IMG = (96 * D + 10 * NG * BT + 15) / 16 * 16;  // the largest chunk (K6V6)
+    uint8_t img[IP ? CMP_R : 1][IP ? IMG : 16];
+    uint32_t vsec[IP ? 1 : CMP_R][IP ? 1 : CW];
+    float vs[IP ? 1 : CMP_R][IP ? 1 : NG * BT];
+    uint8_t vz[IP ? 1 : CMP_R][IP ? 1 : NG * BT];
     uint8_t stage[4][16 * NH][SP];             // per wave: 16 channels of each half x TPW slots
     uint16_t lst[2][CMP_R * BT];               // survivors per segment: (chunk of the run << 6) | slot
     int32_t cnt[2][CMP_R];
@@ -642,6 +316,22 @@ struct alignas(16) CmpShared {
     // high bit, word, destination block}
     uint32_t carry[2][2][D];
     int32_t cmeta[2][2][8];
+
+    __device__ __forceinline__ const uint32_t* vrows(int cl, const Fmt& fs) const
+    {
+        if constexpr (IP) return (const uint32_t*)(img[cl] + fs.off_vc);
+        else return vsec[cl];
+    }
+    __device__ __forceinline__ float vscale(int cl, const Fmt& fs, int i) const
+    {
+        if constexpr (IP) return ((const float*)(img[cl] + fs.off_vs))[i];
+        else return vs[cl][i];
+    }
+    __device__ __forceinline__ int vzero(int cl, const Fmt& fs, int i) const
+    {
+        if constexpr (IP) return img[cl][fs.off_vz + i];
+        else return vz[cl][i];
+    }
 };
 
 // Where a window's words go: the destination chunk, the run's slots [lo, hi)
@@ -747,9 +437,9 @@ __device__ __forceinline__ void pack_stage(const uint8_t (*st)[CmpShared<D, 1>::
 }
 
 // One window of copied codes (VB bits at the source and the destination).
-template <int D, int NG, int VB>
-__device__ __forceinline__ void compact_copy(CmpShared<D, NG>& sh, const MoveDst& dst, int kvh, int seg, int k,
-                                             int plo, int n, int wave, int lane, WordSink sink)
+template <int D, int NG, int VB, bool IP>
+__device__ __forceinline__ void compact_copy(CmpShared<D, NG, IP>& sh, const Fmt& fs, const MoveDst& dst, int kvh,
+                                             int seg, int k, int plo, int n, int wave, int lane, WordSink sink)
 {
     constexpr int NH = CmpShared<D, NG>::NH, TPW = CmpShared<D, NG>::TPW;
     const int t = lane % TPW, h = lane / TPW;
@@ -757,7 +447,7 @@ __device__ __forceinline__ void compact_copy(CmpShared<D, NG>& sh, const MoveDst
     const bool valid = r >= 0 && r < n;
     const int e = sh.lst[seg][valid ? r : 0];
     const int cl = e >> 6, s = e & 63;
-    const uint32_t* row = sh.vsec[cl] + 64 * h * (2 * VB);
+    const uint32_t* row = sh.vrows(cl, fs) + 64 * h * (2 * VB);
     const int bit = s * VB, ws = bit >> 5, bsh = bit & 31;
     const int blk0 = k * TPW / BT * BT;
     sink.blk = sh.dblk[seg][blk0 / BT - plo / BT];
@@ -786,9 +476,9 @@ __device__ __forceinline__ void compact_copy(CmpShared<D, NG>& sh, const MoveDst
 // as quantize_fast / quantize_exact over the dequantised row: the group's
 // min / max are the dequantised extreme codes; a quotient that the fast
 // division leaves uncertain is recomputed with correctly rounded division.
-template <int D, int GS>
-__device__ __forceinline__ void compact_requant(CmpShared<D, D / GS>& sh, const MoveArgs& a, int kvh, int k, int plo,
-                                                int n, int wave, int lane, WordSink sink)
+template <int D, int GS, bool IP>
+__device__ __forceinline__ void compact_requant(CmpShared<D, D / GS, IP>& sh, const Fmt& fs, const MoveArgs& a, int kvh,
+                                                int k, int plo, int n, int wave, int lane, WordSink sink)
 {
     constexpr int TPW = CmpShared<D, D / GS>::TPW, GL = 64 / GS;
     const MoveDst& dst = a.dst[1];
@@ -803,10 +493,10 @@ __device__ __forceinline__ void compact_requant(CmpShared<D, D / GS>& sh, const 
 #pragma unroll
     for (int gl = 0; gl < GL; gl++) {
         const int gi = h * GL + gl;
-        sv[gl] = sh.vs[cl][gi * BT + s];
-        zv[gl] = sh.vz[cl][gi * BT + s];
+        sv[gl] = sh.vscale(cl, fs, gi * BT + s);
+        zv[gl] = sh.vzero(cl, fs, gi * BT + s);
     }
-    const uint32_t* row = sh.vsec[cl] + 64 * h * 12;
+    const uint32_t* row = sh.vrows(cl, fs) + 64 * h * 12;
     const int bit = s * 6, ws = bit >> 5, bsh = bit & 31;
     int cmn[GL], cmx[GL];
 #pragma unroll
@@ -892,9 +582,9 @@ __device__ __forceinline__ void compact_requant(CmpShared<D, D / GS>& sh, const 
     }
 }
 
-template <int D, int GS, int VS>
-__device__ __forceinline__ void tier_compact_body(CmpShared<D, D / GS>& sh, const MoveArgs& a, const MoveSrc& S,
-                                                  int b, int kvh, int len, int c0, int nc, int par)
+template <int D, int GS, int VS, bool IP>
+__device__ __forceinline__ void tier_compact_body(CmpShared<D, D / GS, IP>& sh, const MoveArgs& a, const MoveSrc& S,
+                                                  int b, int kvh, int len, int c0, int nc, int par, int cwg)
 {
     constexpr int NG = D / GS;
     const Fmt& fs = S.f;
@@ -902,11 +592,14 @@ __device__ __forceinline__ void tier_compact_body(CmpShared<D, D / GS>& sh, cons
     const int32_t* brow = S.bt + (int64_t)b * S.max_blocks;
     const bool copy_m = a.dst[1].f.vb == VS;
     const bool requant = VS == 6 && !copy_m;
+    typedef __attribute__((address_space(1))) void gvoid;
+    typedef __attribute__((address_space(3))) void lvoid;
 
     // 1. each wave's chunk: its V section (and, when MID survivors are
-    //    requantised, its V scales and zeros) copied into LDS by the memory
-    //    unit, its rows moved by the lanes.  Everything the windows read
-    //    from memory is staged here, before the barrier.
+    //    requantised, its V scales and zeros; in place the whole chunk)
+    //    copied into LDS by the memory unit, its rows moved by the lanes
+    //    (in place only after step 2).  Everything the windows read from
+    //    memory is staged here, before the barrier.
     constexpr int NPC = D * VS * 64 / 8 / 16;  // 16-byte pieces of a V section
     static_assert(NPC % 64 == 0, "whole wave copies");
     const bool live = wave < nc;
@@ -924,19 +617,26 @@ __device__ __forceinline__ void tier_compact_body(CmpShared<D, D / GS>& sh, cons
     }
     const uint8_t* sch = S.pool + ((int64_t)blk_c * fs.H + kvh) * fs.chunk;
     if (live) {
-        typedef __attribute__((address_space(1))) void gvoid;
-        typedef __attribute__((address_space(3))) void lvoid;
+        if constexpr (IP) {
+            constexpr int NI = (CmpShared<D, NG, IP>::IMG + 1023) / 1024;
 #pragma unroll
-        for (int i = 0; i < NPC / 64; i++)
-            __builtin_amdgcn_global_load_lds((gvoid*)(sch + fs.off_vc + 16 * (64 * i + lane)),
-                                             (lvoid*)((uint8_t*)sh.vsec[wave] + 1024 * i), 16, 0, 0);
-        if (requant) {
-            if (lane < NG * 16)
-                __builtin_amdgcn_global_load_lds((gvoid*)(sch + fs.off_vs + 16 * lane), (lvoid*)sh.vs[wave], 16, 0,
-                                                 0);
-            if (lane < NG * 4)
-                __builtin_amdgcn_global_load_lds((gvoid*)(sch + fs.off_vz + 16 * lane), (lvoid*)sh.vz[wave], 16, 0,
-                                                 0);
+            for (int i = 0; i < NI; i++)
+                if (16 * (64 * i + lane) < fs.chunk)
+                    __builtin_amdgcn_global_load_lds((gvoid*)(sch + 16 * (64 * i + lane)),
+                                                     (lvoid*)(sh.img[wave] + 1024 * i), 16, 0, 0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NPC / 64; i++)
+                __builtin_amdgcn_global_load_lds((gvoid*)(sch + fs.off_vc + 16 * (64 * i + lane)),
+                                                 (lvoid*)((uint8_t*)sh.vsec[wave] + 1024 * i), 16, 0, 0);
+            if (requant) {
+                if (lane < NG * 16)
+                    __builtin_amdgcn_global_load_lds((gvoid*)(sch + fs.off_vs + 16 * lane), (lvoid*)sh.vs[wave], 16,
+                                                     0, 0);
+                if (lane < NG * 4)
+                    __builtin_amdgcn_global_load_lds((gvoid*)(sch + fs.off_vz + 16 * lane), (lvoid*)sh.vz[wave], 16,
+                                                     0, 0);
+            }
         }
     }
     const int tw = live && tok < len ? traw : 0;
@@ -948,9 +648,11 @@ __device__ __forceinline__ void tier_compact_body(CmpShared<D, D / GS>& sh, cons
         sh.cnt[1][wave] = __popcll(mk1);
     }
     if (tid < 2) sh.cmeta[par][tid][0] = 0;  // nothing carried out yet (this parity was read by the run before last)
-    if (mk0 && tw == 2) compact_row_any<D, NG, 0>(a, fs, sch, base_c.x + r0, b, kvh, lane, true);
-    if (mk1 && tw == 1) compact_row_any<D, NG, 1>(a, fs, sch, base_c.y + r1, b, kvh, lane, copy_m);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the V sections are in LDS
+    if constexpr (!IP) {
+        if (mk0 && tw == 2) compact_row_any<D, NG, 0>(a, fs, sch, base_c.x + r0, b, kvh, lane, true);
+        if (mk1 && tw == 1) compact_row_any<D, NG, 1>(a, fs, sch, base_c.y + r1, b, kvh, lane, copy_m);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the sections are in LDS
     __syncthreads();
 
     // 2. survivors of the run per segment, in slot order
@@ -964,7 +666,35 @@ __device__ __forceinline__ void tier_compact_body(CmpShared<D, D / GS>& sh, cons
     }
     if (tw == 2) sh.lst[0][pre0 + r0] = (uint16_t)((wave << 6) | lane);
     else if (tw == 1) sh.lst[1][pre1 + r1] = (uint16_t)((wave << 6) | lane);
+    if constexpr (IP) {
+        // The run's chunks are read (every load has returned): mark them for
+        // this KV head.  Then wait until the blocks the run writes into that
+        // belong to earlier workgroups (below cwg, the workgroup's first
+        // chunk) have been read by every KV head: those workgroups hold
+        // earlier tickets and mark each run before they wait for anything.
+        // Relaxed device-scope atomics: the order needed is a load's return
+        // before another workgroup's store to the same bytes.
+        uint32_t* frow = a.flags + (int64_t)b * a.flag_stride;
+        if (tid == 0) __hip_atomic_fetch_add(frow + c0 / CMP_R, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int own = a.inplace_seg;
+        const int n_own = own == 0 ? n0 : n1, p_own = own == 0 ? base.x : base.y;
+        if (n_own > 0) {
+            const int jlo = p_own / BT / CMP_R, jhi = min((p_own + n_own - 1) / BT, cwg - 1) / CMP_R;
+            const uint32_t heads = (uint32_t)fs.H;
+            if (p_own / BT < cwg)
+                for (int j = jlo + tid; j <= jhi; j += 256)
+                    for (uint32_t spin = 0; spin < (1u << 20); spin++) {
+                        if (__hip_atomic_load(frow + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= heads) break;
+                        __builtin_amdgcn_s_sleep(2);
+                    }
+        }
+    }
     __syncthreads();
+    if constexpr (IP) {
+        const uint8_t* img = (const uint8_t*)sh.img[wave];
+        if (mk0 && tw == 2) compact_row_any<D, NG, 0>(a, fs, img, base_c.x + r0, b, kvh, lane, true);
+        if (mk1 && tw == 1) compact_row_any<D, NG, 1>(a, fs, img, base_c.y + r1, b, kvh, lane, copy_m);
+    }
 
     // 3. windows of destination slots: MID first (the costlier ones), then HIGH
     constexpr int TPW = CmpShared<D, NG>::TPW;
@@ -981,11 +711,11 @@ __device__ __forceinline__ void tier_compact_body(CmpShared<D, D / GS>& sh, cons
     for (int q = wave; q < win0 + win1; q += 4) {
         if (q < win1) {
             const int k = base.y / TPW + q;
-            if (VS == 4) compact_copy<D, NG, 4>(sh, a.dst[1], kvh, 1, k, base.y, n1, wave, lane, sk[1]);
-            else compact_requant<D, GS>(sh, a, kvh, k, base.y, n1, wave, lane, sk[1]);
+            if (VS == 4) compact_copy<D, NG, 4, IP>(sh, fs, a.dst[1], kvh, 1, k, base.y, n1, wave, lane, sk[1]);
+            else compact_requant<D, GS, IP>(sh, fs, a, kvh, k, base.y, n1, wave, lane, sk[1]);
         } else if (VS == 6) {
             const int k = base.x / TPW + q - win1;
-            compact_copy<D, NG, 6>(sh, a.dst[0], kvh, 0, k, base.x, n0, wave, lane, sk[0]);
+            compact_copy<D, NG, 6, IP>(sh, fs, a.dst[0], kvh, 0, k, base.x, n0, wave, lane, sk[0]);
         }
     }
     __syncthreads();
@@ -998,35 +728,55 @@ __device__ __forceinline__ void tier_compact_body(CmpShared<D, D / GS>& sh, cons
     }
 }
 
-// grid (groups of per_wg runs of CMP_R chunks, KV heads, batch x sources);
-// 256 threads; GS channels per quantisation group.  Sources are 6-bit (HIGH copied, MID
-// requantised) or 4-bit (MID copied).
-template <int D, int GS>
+// Out of place: grid (groups of per_wg runs of CMP_R chunks, KV heads,
+// batch x sources).  In place (IP, one source per launch): a 1-D grid whose
+// workgroups take their (sequence, group, KV head) from a ticket counter,
+// a sequence's groups in order and their KV heads together; flags[b][run]
+// counts the KV heads that have read a run.  256 threads; GS channels per
+// quantisation group.  Sources are 6-bit (HIGH copied, MID requantised) or
+// 4-bit (MID copied).
+template <int D, int GS, bool IP>
 __device__ __forceinline__ void tier_compact(const MoveArgs& a)
 {
-    __shared__ CmpShared<D, D / GS> sh;
-    const int si = blockIdx.z % a.nsrc, b = blockIdx.z / a.nsrc, kvh = blockIdx.y;
+    __shared__ CmpShared<D, D / GS, IP> sh;
+    __shared__ int ticket_of;
+    int si, b, kvh, g;
+    if constexpr (IP) {  // every workgroup takes a ticket before anything else
+        if (threadIdx.x == 0) ticket_of = (int)atomicAdd(a.ticket, 1u);
+        __syncthreads();
+        const int t = ticket_of, H = a.src[0].f.H;
+        si = 0;
+        kvh = t % H;
+        g = t / H % a.gx;
+        b = t / H / a.gx;
+    } else {
+        si = blockIdx.z % a.nsrc;
+        b = blockIdx.z / a.nsrc;
+        kvh = blockIdx.y;
+        g = blockIdx.x;
+    }
     if (a.n_high[b] < 0 || a.n_mid[b] < 0) return;  // no room: nothing is written
     const MoveSrc& S = si == 0 ? a.src[0] : a.src[1];
     const int len = max(0, min(S.lens[b], S.len_cap));
     const int nblocks = (len + BT - 1) / BT;
     const int S_ = a.per_wg;
-    if (blockIdx.x * S_ * CMP_R >= nblocks) return;
+    const int cwg = g * S_ * CMP_R;
+    if (cwg >= nblocks) return;
     if (threadIdx.x < 4) sh.cmeta[threadIdx.x / 2][threadIdx.x % 2][0] = 0;
-    const int runs = min(S_, (nblocks - blockIdx.x * S_ * CMP_R + CMP_R - 1) / CMP_R);
+    const int runs = min(S_, (nblocks - cwg + CMP_R - 1) / CMP_R);
     auto each_run = [&](auto vs) __attribute__((always_inline)) {
 #pragma nounroll
         for (int r = 0; r < runs; r++) {
-            const int c0 = (blockIdx.x * S_ + r) * CMP_R;
-            tier_compact_body<D, GS, decltype(vs)::value>(sh, a, S, b, kvh, len, c0, min(CMP_R, nblocks - c0), r & 1);
+            const int c0 = cwg + r * CMP_R;
+            tier_compact_body<D, GS, decltype(vs)::value, IP>(sh, a, S, b, kvh, len, c0, min(CMP_R, nblocks - c0),
+                                                              r & 1, cwg);
             __syncthreads();
         }
     };
     if (S.f.vb == 6) each_run(std::integral_constant<int, 6>());
     else each_run(std::integral_constant<int, 4>());
-    const int r = runs;
     // the words the last runs ended inside: merged with the neighbours' bits
-    const int par = (r - 1) & 1;
+    const int par = (runs - 1) & 1;
 #pragma unroll
     for (int seg = 0; seg < 2; seg++) {
         const int32_t* m = sh.cmeta[par][seg];
@@ -1044,16 +794,24 @@ __device__ __forceinline__ void tier_compact(const MoveArgs& a)
 
 // Four waves per SIMD for groups of 32 or 64 channels (at most 128
 // registers); groups of 16 need more registers than that.
-template <int D, int GS>
+template <int D, int GS, bool IP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void tier_compact_kernel(MoveArgs a)
 {
-    tier_compact<D, GS>(a);
+    tier_compact<D, GS, IP>(a);
+}
+
+// In place: whole chunks in LDS allow two workgroups per compute unit, so
+// no register cap.
+template <int D, int GS>
+__global__ __launch_bounds__(256) void tier_compact_ip_kernel(MoveArgs a)
+{
+    tier_compact<D, GS, true>(a);
 }
 
 template <int D>
 __global__ __launch_bounds__(256) void tier_compact16_kernel(MoveArgs a)
 {
-    tier_compact<D, 16>(a);
+    tier_compact<D, 16, false>(a);
 }
 
 hipError_t launch_tiering(const TierSource* src, int nsrc, float tau_low, float tau_high, const TierDest& h,
@@ -1061,9 +819,8 @@ hipError_t launch_tiering(const TierSource* src, int nsrc, float tau_low, float 
                           hipStream_t stream)
 {
     if (batch == 0) return hipSuccess;
-    for (int i = 0; i < nsrc; i++)  // every quantised format fits the move kernel's staging
-        if (src[i].f.chunk > 16 * 256 * MOVE_PIECES || src[i].f.chunk - src[i].f.off_ks > MOVE_META ||
-            src[i].f.vb > 6 || src[i].f.D != h.f.D)
+    for (int i = 0; i < nsrc; i++)  // every quantised format (K and V at 4 or 6 bits) fits the staging
+        if (src[i].f.kb > 6 || src[i].f.vb > 6 || src[i].f.D != h.f.D || src[i].f.g != h.f.g)
             return hipErrorInvalidValue;
     TierScanArgs t = {};
     int2* counts = (int2*)workspace;
@@ -1121,7 +878,10 @@ hipError_t launch_tiering(const TierSource* src, int nsrc, float tau_low, float 
     a.n_high = n_high;
     a.n_mid = n_mid;
     a.nsrc = nsrc;
-    a.per_wg = MOVE_CHUNKS;
+    // V codes: 6-bit sources (HIGH copied, MID requantised) or 4-bit ones (MID copied)
+    for (int i = 0; i < nsrc; i++)
+        if (!(src[i].f.vb == 6 || (src[i].f.vb == 4 && m.f.vb == 4))) return hipErrorInvalidValue;
+    if (h.f.vb != 6 || m.f.vb != 4) return hipErrorInvalidValue;
     // the destination segment (0 HIGH, 1 MID) that is source i itself, or -1
     int own[2] = {-1, -1};
     bool in_place = false;
@@ -1130,55 +890,53 @@ hipError_t launch_tiering(const TierSource* src, int nsrc, float tau_low, float 
         if (m.pool == src[i].pool && m.block_table == src[i].block_table) own[i] = 1;
         in_place |= own[i] >= 0;
     }
-    auto launch = [&](const MoveArgs& x, dim3 grid) {
-        if (h.f.D == 64) hipLaunchKernelGGL(tier_move_kernel<64>, grid, dim3(256), 0, stream, x);
-        else hipLaunchKernelGGL(tier_move_kernel<128>, grid, dim3(256), 0, stream, x);
+    // runs per workgroup: as many as keep about 1024 workgroups in the grid
+    // (fewer workgroup edges, whose words take atomics), at most CMP_S
+    auto per_wg = [&](const TierSource* ss, int n) {
+        int64_t runs = 0;
+        for (int i = 0; i < n; i++) runs += (int64_t)batch * h.f.H * ((ss[i].max_len + BT * CMP_R - 1) / (BT * CMP_R));
+        return (int32_t)std::max<int64_t>(1, std::min<int64_t>(CMP_S, runs / 1024));
+    };
+    auto go = [&](const MoveArgs& x, dim3 grid, bool ip) {
+        auto run = [&](auto k) { hipLaunchKernelGGL(k, grid, dim3(256), 0, stream, x); };
+        if (h.f.D == 64) {
+            if (h.f.g == 64) ip ? run(tier_compact_ip_kernel<64, 64>) : run(tier_compact_kernel<64, 64, false>);
+            else if (h.f.g == 32) ip ? run(tier_compact_ip_kernel<64, 32>) : run(tier_compact_kernel<64, 32, false>);
+            else ip ? run(tier_compact_ip_kernel<64, 16>) : run(tier_compact16_kernel<64>);
+        } else {
+            if (h.f.g == 64) ip ? run(tier_compact_ip_kernel<128, 64>) : run(tier_compact_kernel<128, 64, false>);
+            else if (h.f.g == 32) ip ? run(tier_compact_ip_kernel<128, 32>) : run(tier_compact_kernel<128, 32, false>);
+            else ip ? run(tier_compact_ip_kernel<128, 16>) : run(tier_compact16_kernel<128>);
+        }
     };
     if (!in_place) {
-        // V codes: 6-bit sources (HIGH copied, MID requantised) or 4-bit ones (MID copied)
-        for (int i = 0; i < nsrc; i++)
-            if (!(src[i].f.vb == 6 || (src[i].f.vb == 4 && m.f.vb == 4))) return hipErrorInvalidValue;
-        if (h.f.vb != 6 || m.f.vb != 4) return hipErrorInvalidValue;
-        // runs per workgroup: as many as keep about 1024 workgroups in the
-        // grid (fewer workgroup edges, whose words take atomics), at most CMP_S
-        int64_t runs = 0;
-        for (int i = 0; i < nsrc; i++) runs += (int64_t)batch * h.f.H * ((src[i].max_len + BT * CMP_R - 1) / (BT * CMP_R));
-        a.per_wg = (int32_t)std::max<int64_t>(1, std::min<int64_t>(CMP_S, runs / 1024));
+        a.per_wg = per_wg(src, nsrc);
         const int span = CMP_R * a.per_wg;
-        const dim3 grid((unsigned)((max_blocks + span - 1) / span), (unsigned)h.f.H, (unsigned)(batch * nsrc));
-        auto go = [&](auto k) { hipLaunchKernelGGL(k, grid, dim3(256), 0, stream, a); };
-        if (h.f.D == 64) {
-            if (h.f.g == 64) go(tier_compact_kernel<64, 64>);
-            else if (h.f.g == 32) go(tier_compact_kernel<64, 32>);
-            else go(tier_compact16_kernel<64>);
-        } else {
-            if (h.f.g == 64) go(tier_compact_kernel<128, 64>);
-            else if (h.f.g == 32) go(tier_compact_kernel<128, 32>);
-            else go(tier_compact16_kernel<128>);
-        }
+        go(a, dim3((unsigned)((max_blocks + span - 1) / span), (unsigned)h.f.H, (unsigned)(batch * nsrc)), false);
         return hipGetLastError();
     }
-    // one source per launch, in destination order; a source compacted in
-    // place moves one chunk per workgroup in ticket order
+    // one source per launch, in destination order (MID first: the demoted
+    // HIGH tokens land in MID blocks after the kept MID tokens); a source
+    // compacted in place takes its workgroups' work from a ticket counter
     uint32_t* ticket = (uint32_t*)(bases + (int64_t)batch * base_total);
     uint32_t* flags = ticket + 2;
     for (int i = 0; i < nsrc; i++) {
         MoveArgs one = a;
         one.src[0] = a.src[i];
         one.nsrc = 1;
+        one.per_wg = per_wg(&src[i], 1);
+        const int32_t nruns = max(1, (src[i].max_len + BT * CMP_R - 1) / (BT * CMP_R));
+        const int32_t groups = (nruns + one.per_wg - 1) / one.per_wg;
         if (own[i] < 0) {
-            launch(one, dim3((unsigned)((max_blocks + MOVE_CHUNKS - 1) / MOVE_CHUNKS), (unsigned)h.f.H,
-                             (unsigned)batch));
+            go(one, dim3((unsigned)groups, (unsigned)h.f.H, (unsigned)batch), false);
         } else {
-            const int32_t gx = max(1, (src[i].max_len + BT - 1) / BT);
-            if ((e = launch_fill_u32(ticket, 2 + (int64_t)batch * gx, 0u, stream)) != hipSuccess) return e;
-            one.per_wg = 1;
+            if ((e = launch_fill_u32(ticket, 2 + (int64_t)batch * nruns, 0u, stream)) != hipSuccess) return e;
             one.ticket = ticket;
             one.flags = flags;
-            one.flag_stride = gx;
+            one.flag_stride = nruns;
             one.inplace_seg = own[i];
-            one.gx = gx;
-            launch(one, dim3((unsigned)((int64_t)gx * h.f.H * batch)));
+            one.gx = groups;
+            go(one, dim3((unsigned)((int64_t)groups * h.f.H * batch)), true);
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
