@@ -65,6 +65,9 @@ struct MfmaArgs {
     // head) row, zero between calls, and the output [B][Hq][128]
     uint32_t* counters;
     float* out;
+    // multi-token calls with 8 query heads per KV head: (split, KV head,
+    // sequence) items, each run for the call's T query tokens
+    int32_t items;
 };
 
 // A partial's value, stored plainly, or (WT) as a device-scope relaxed
@@ -1299,6 +1302,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
     split_body<VB, G, KN, false, DBG>(a, blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x, meta_lds);
 }
 
+// Multi-token calls with 8 query heads per KV head: the T query tokens of
+// one (split, KV head, sequence) item run in workgroups 8 apart, which the
+// dispatcher sends to the same XCD one after another, so that the later
+// tokens find the split's chunks in that XCD's L2 rather than read them
+// from memory again.  1-D grid: ceil(items / 8) * 8 * T workgroups.
+template <int VB, bool KN, bool DBG>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void split_mfma_multi8_kernel(MfmaArgs a)
+{
+    __shared__ uint4 meta_lds[meta_bytes<KN>() / 16];
+    const int T = a.seg.q_per_seq, ns = a.seg.n_splits, H = a.seg.f.H;
+    const int j = blockIdx.x / 8;
+    const int t = j % T, item = j / T * 8 + blockIdx.x % 8;
+    if (item >= a.items) return;
+    split_body<VB, 8, KN, false, DBG>(a, item % ns, item / ns % H, item / ns / H * T + t, threadIdx.x, meta_lds);
+}
+
 // Query-token pairs of a multi-token call with 4 query heads per KV head
 // (split_body's PAIR): grid z = sequence x ceil(T / 2) pairs.
 template <int VB, bool KN, bool DBG>
@@ -1420,6 +1439,9 @@ static MfmaArgs mfma_args(const SegArgs& s, const void* q, int32_t num_q_heads, 
     a.k_new = nullptr;
     a.v_new = nullptr;
     a.kv_dtype = 0;
+    a.counters = nullptr;
+    a.out = nullptr;
+    a.items = 0;
     return a;
 }
 
@@ -1454,6 +1476,15 @@ static void launch_pair(const MfmaArgs& a, int vb, bool kn, dim3 grid, hipStream
     else if (vb == 4) hipLaunchKernelGGL((split_mfma_pair_kernel<4, false, DBG>), grid, dim3(64), 0, st, a);
     else if (kn) hipLaunchKernelGGL((split_mfma_pair_kernel<6, true, DBG>), grid, dim3(64), 0, st, a);
     else hipLaunchKernelGGL((split_mfma_pair_kernel<6, false, DBG>), grid, dim3(64), 0, st, a);
+}
+
+template <bool DBG>
+static void launch_multi8(const MfmaArgs& a, int vb, bool kn, dim3 grid, hipStream_t st)
+{
+    if (vb == 4 && kn) hipLaunchKernelGGL((split_mfma_multi8_kernel<4, true, DBG>), grid, dim3(64), 0, st, a);
+    else if (vb == 4) hipLaunchKernelGGL((split_mfma_multi8_kernel<4, false, DBG>), grid, dim3(64), 0, st, a);
+    else if (kn) hipLaunchKernelGGL((split_mfma_multi8_kernel<6, true, DBG>), grid, dim3(64), 0, st, a);
+    else hipLaunchKernelGGL((split_mfma_multi8_kernel<6, false, DBG>), grid, dim3(64), 0, st, a);
 }
 
 template <bool DBG>
@@ -1515,12 +1546,18 @@ bool launch_decode_split_mfma(const SegArgs& s, const void* q, int q_dtype, int3
     if (!mfma_ok(s, q, q_dtype, num_q_heads, sm_scale, split_tokens)) return false;
     const Fmt& f = s.f;
     const int G = num_q_heads / f.H;
-    const MfmaArgs a = mfma_args(s, q, num_q_heads, sm_scale, tau_low, split_tokens, total_splits, partials);
+    MfmaArgs a = mfma_args(s, q, num_q_heads, sm_scale, tau_low, split_tokens, total_splits, partials);
     const int T = s.q_per_seq;
     if (T > 1 && G == 4) {  // batch counts B * T entries: B * ceil(T / 2) pairs
         dim3 grid((unsigned)s.n_splits, (unsigned)f.H, (unsigned)(batch / T * ((T + 1) / 2)));
         if (s.skip_mask != nullptr) launch_pair<true>(a, f.vb, f.k_norm, grid, stream);
         else launch_pair<false>(a, f.vb, f.k_norm, grid, stream);
+    } else if (T > 1) {  // 8 heads: a token's layout is full; the tokens of an item share its L2
+        const int64_t items = (int64_t)s.n_splits * f.H * (batch / T);
+        a.items = (int32_t)items;
+        const dim3 grid((unsigned)((items + 7) / 8 * 8 * T));
+        if (s.skip_mask != nullptr) launch_multi8<true>(a, f.vb, f.k_norm, grid, stream);
+        else launch_multi8<false>(a, f.vb, f.k_norm, grid, stream);
     } else {
         dim3 grid((unsigned)s.n_splits, (unsigned)f.H, (unsigned)batch);
         if (s.skip_mask != nullptr) launch_plain<true>(a, f.vb, G, f.k_norm, grid, stream);

@@ -53,6 +53,7 @@ CASES = [  # (format, G, q dtype): the matrix-core, fp16 and generic kernels
     ((128, 64, 6, 4), 4, "bf16"),
     ((128, 64, 6, 4), 8, "bf16"),
     ((128, 64, 6, 6), 4, "bf16"),
+    ((128, 64, 6, 6), 8, "bf16"),
     ((128, 64, 16, 16), 8, "bf16"),
     ((64, 32, 6, 4), 2, "bf16"),
     ((128, 64, 6, 4), 4, "f32"),
