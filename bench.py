@@ -114,6 +114,7 @@ class Setup:
         self.out_bytes = 0       # bytes of O the merge writes
         self.sequences = 0
         self.config = {}
+        self.later = []          # (name, figure) secondary figures run after the timed steps
         self.secondary = {}
         self.per_token_head = 0
         self.q_bytes = 2
@@ -205,9 +206,12 @@ def setup_uniform(args, wl, dev) -> Setup:
     S.keep += [caches, bt, lens, view, cu1, last, ws, out, counters]
     ptk = caches[0].chunk_bytes // 64
     if not args.fp16_layer and not args.no_secondary:
-        S.secondary["decode_with_scores"] = scores_figure(caches, view, S.keep, B, Hq, Hkv, D, N, sm, split, dev)
-        S.secondary["multi_token"] = multi_figure(caches, view, S.keep, B, Hq, Hkv, D, N, sm, ptk, dev)
-        S.secondary["k_norm"] = knorm_figure(args, wl, bt, view, S.keep, sm, dev)
+        # measured after the timed steps, so that their buffers and launches
+        # are not around while the steps run
+        keep = S.keep
+        S.later += [("decode_with_scores", lambda: scores_figure(caches, view, keep, B, Hq, Hkv, D, N, sm, split, dev)),
+                    ("multi_token", lambda: multi_figure(caches, view, keep, B, Hq, Hkv, D, N, sm, ptk, dev)),
+                    ("k_norm", lambda: knorm_figure(args, wl, bt, view, keep, sm, dev))]
     qb = 2 if wl.dtype == "bf16" else 4
     kv = B * Hkv * N * ptk
     S.per_token_head, S.q_bytes = ptk, qb
@@ -582,6 +586,9 @@ def main():
     # timed region: K steps between synchronisations; HIP events on the
     # run stream bracket all of them (the steps' GPU time)
     g0, g1 = _event(), _event()
+    import gc
+    gc.collect()
+    gc.disable()  # no cycle-collector pause inside the timed steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     with torch.cuda.stream(run_stream):
@@ -594,6 +601,7 @@ def main():
         g1.record(run_stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    gc.enable()
     gpu_step_s = g0.elapsed_time(g1) / 1e3 / args.steps
     # then, outside the timed region, HIP events before and after each stage
     # of one step in every rotation cycle, replaying the same steps launch by
@@ -674,8 +682,14 @@ def main():
                      "combine_us": round(float(comb_ms.mean()) * 1e3, 2)},
     }
     secondary = dict(S.secondary)
+    with torch.cuda.stream(run_stream):
+        for name, fig in S.later:
+            secondary[name] = fig()
+    torch.cuda.synchronize()
     ptk, qb = S.per_token_head, S.q_bytes
     kb, vb = S.config.get("k_bits"), S.config.get("v_bits")
+    if args.workload == 4 and not args.fp16_layer and not args.kv_heads and not args.no_secondary:
+        secondary["stack_32_layers"] = stack_figure(args, wl, dev, gpu_step_s)
     if args.workload == 2 and not args.fp16_layer and not args.no_tier and not args.no_secondary:
         del S
         torch.cuda.empty_cache()
@@ -691,6 +705,50 @@ def main():
     if not args.no_cpu_baseline and args.workload in (2, 4):
         rec["cpu_baseline"] = cpu_baseline(wl, kb, vb, min(args.cpu_seqs, wl.batch), ptk, qb, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
+
+
+def stack_figure(args, wl, dev, quant_step_s):
+    """The whole decode stack of workload 4 (2 of every 32 layers held in
+    fp16): the fp16 layer's step (append + decode at the same shape, two
+    layer caches rotated, 64 steps between one event pair after 8 untimed
+    ones), then per token step 30 quantised layers at the timed step's GPU
+    time and 2 fp16 layers."""
+    import copy
+
+    import torch
+
+    a16 = copy.copy(args)
+    a16.fp16_layer, a16.no_secondary, a16.layers, a16.kv_heads = True, True, 2, 0
+    run_stream = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(run_stream):
+        S16 = setup_uniform(a16, wl, dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        for fn in S16.calls[i % len(S16.calls)]:
+            fn()
+
+    with torch.cuda.stream(run_stream):
+        for i in range(8):
+            step(i)
+    torch.cuda.synchronize()
+    e0, e1 = _event(), _event()
+    with torch.cuda.stream(run_stream):
+        e0.record(run_stream)
+        for i in range(64):
+            step(i)
+        e1.record(run_stream)
+    torch.cuda.synchronize()
+    f16_s = e0.elapsed_time(e1) / 64 / 1e3
+    nf = wl.fp16_layers
+    nq = wl.layers_per_stack - nf
+    stack_s = nq * quant_step_s + nf * f16_s
+    del S16
+    torch.cuda.empty_cache()
+    return {"layers": wl.layers_per_stack, "fp16_layers": nf, "quantised_layer_us": round(quant_step_s * 1e6, 2),
+            "fp16_layer_us": round(f16_s * 1e6, 2), "stack_us_per_token_step": round(stack_s * 1e6, 1),
+            "decode_tokens_per_s": round(wl.batch / stack_s, 1),
+            "counted": "attention of every layer (append + decode), nothing else of the model"}
 
 
 def copy_probe(dev):
@@ -824,6 +882,20 @@ def probe_figure(dev, gib=4, reps=20):
 
 
 def serving_figure(wl, dev, every=32, tl_rel=0.35, th_rel=1.9):
+    """The loop below, with Python's cycle collector off: a collection that
+    falls between a re-tier's opening event and its launches would count as
+    GPU time (such a pause once added 40 ms to one re-tier)."""
+    import gc
+
+    gc.collect()
+    gc.disable()
+    try:
+        return _serving_loop(wl, dev, every, tl_rel, th_rel)
+    finally:
+        gc.enable()
+
+
+def _serving_loop(wl, dev, every, tl_rel, th_rel):
     """The tiered serving loop at the ragged workload's shape: the cache is
     prefilled at K6V6 (all HIGH); each step appends one row per sequence to
     HIGH and decodes over HIGH + MID with the sparse-V skip, accumulating

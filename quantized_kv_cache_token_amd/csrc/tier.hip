@@ -892,10 +892,12 @@ hipError_t launch_tiering(const TierSource* src, int nsrc, float tau_low, float 
     }
     // runs per workgroup: as many as keep about 1024 workgroups in the grid
     // (fewer workgroup edges, whose words take atomics), at most CMP_S
-    auto per_wg = [&](const TierSource* ss, int n) {
+    // (in place about 4096: its workgroups wait on earlier ones, and the
+    // run count assumes every sequence at max_len)
+    auto per_wg = [&](const TierSource* ss, int n, int64_t target) {
         int64_t runs = 0;
         for (int i = 0; i < n; i++) runs += (int64_t)batch * h.f.H * ((ss[i].max_len + BT * CMP_R - 1) / (BT * CMP_R));
-        return (int32_t)std::max<int64_t>(1, std::min<int64_t>(CMP_S, runs / 1024));
+        return (int32_t)std::max<int64_t>(1, std::min<int64_t>(CMP_S, runs / target));
     };
     auto go = [&](const MoveArgs& x, dim3 grid, bool ip) {
         auto run = [&](auto k) { hipLaunchKernelGGL(k, grid, dim3(256), 0, stream, x); };
@@ -910,7 +912,7 @@ hipError_t launch_tiering(const TierSource* src, int nsrc, float tau_low, float 
         }
     };
     if (!in_place) {
-        a.per_wg = per_wg(src, nsrc);
+        a.per_wg = per_wg(src, nsrc, 1024);
         const int span = CMP_R * a.per_wg;
         go(a, dim3((unsigned)((max_blocks + span - 1) / span), (unsigned)h.f.H, (unsigned)(batch * nsrc)), false);
         return hipGetLastError();
@@ -924,7 +926,7 @@ hipError_t launch_tiering(const TierSource* src, int nsrc, float tau_low, float 
         MoveArgs one = a;
         one.src[0] = a.src[i];
         one.nsrc = 1;
-        one.per_wg = per_wg(&src[i], 1);
+        one.per_wg = per_wg(&src[i], 1, own[i] < 0 ? 1024 : 4096);
         const int32_t nruns = max(1, (src[i].max_len + BT * CMP_R - 1) / (BT * CMP_R));
         const int32_t groups = (nruns + one.per_wg - 1) / one.per_wg;
         if (own[i] < 0) {
