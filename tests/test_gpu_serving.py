@@ -34,7 +34,7 @@ pytestmark = pytest.mark.gpu
 B, HQ, HKV, D, GS = 64, 16, 2, 128, 64
 BT = 64
 SEED = 160
-STEPS, EVERY = 72, 32
+STEPS, EVERY = 136, 32
 # relative-score thresholds: tokens under 0.35 of the uniform weight are
 # evicted, tokens over 1.9 times it stay HIGH (each re-tier then evicts,
 # demotes and keeps a share of the tokens)
