@@ -1,10 +1,14 @@
 """Parity on the five workloads at their full sizes, in the launch
-configuration the benchmark uses (the library's own split plan).
+configuration the benchmark uses: the library's own split plan, and the
+decode step as lkv_append_decode (workloads 2, 4 and 5, each also through
+lkv_decode_attn).
 
-The oracle cannot afford every output at these sizes, so each test checks
-sampled sequences in full: their packed cache chunks bit for bit (the
-oracle appends the same rows into its own pool) and every query head's
-attention output, against max|d| <= 1e-3 max|v_hat| and rel L2 <= 1e-4.
+Workloads 2 to 4 check every sequence in full: its packed cache chunks bit
+for bit (the oracle appends the same rows into its own pool) and every query
+head's attention output, against max|d| <= 1e-3 max|v_hat| and rel L2 <=
+1e-4.  Workload 5 checks every sequence's appended rows at every step, every
+sequence's output at every third step, and two sequences' outputs at the
+other steps.
 """
 import numpy as np
 import pytest
@@ -62,9 +66,9 @@ def test_workload1_tiny_exhaustive():
 
 
 @pytest.mark.timeout(900)
-def test_workload2_llama8b_32k_sampled():
-    """Prefill 32767 tokens, append the 32768th, decode; sequences 0 and 5
-    are checked in full."""
+def test_workload2_llama8b_32k():
+    """Prefill 32767 tokens, then the benchmark's step: lkv_append_decode
+    appends the 32768th and decodes; every sequence is checked in full."""
     wl = workloads.LLAMA8B_32K
     B, Hq, Hkv, D, N = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.n_ctx
     nb = N // BT
@@ -76,15 +80,14 @@ def test_workload2_llama8b_32k_sampled():
         rows[b] = _prefill_gpu(gpu, wl, b, N - 1, bt[b:b + 1])
     outl = inputs.outlier_channels(wl.seed, Hkv, D)
     kn, vn = inputs.kv_rows(wl.seed, 1000, B, Hkv, D, outliers=outl, step=1)
-    lkv.quant_append(gpu, kn.cuda(), vn.cuda(), torch.arange(B + 1, dtype=torch.int32).cuda(),
-                     torch.full((B,), N - 1, dtype=torch.int32).cuda(), bt.cuda(), 1)
     q = inputs.queries(wl.seed, B, Hq, D)
     view = lkv.View(bt.cuda(), torch.full((B,), N, dtype=torch.int32).cuda(), N)
     split = lkv.decode_plan([gpu], [view], B, Hq)
-    say("workload 2 decode split", split)
-    out = lkv.decode_attn([gpu], [view], q.cuda(), sm_scale(D), 0.0, split).cpu().numpy()
+    say("workload 2 append + decode, split", split)
+    out = lkv.append_decode(gpu, view, kn.cuda(), vn.cuda(), q.cuda(), sm_scale(D), 0.0, split).cpu().numpy()
+    again = lkv.decode_attn([gpu], [view], q.cuda(), sm_scale(D), 0.0, split).cpu().numpy()
     torch.cuda.synchronize()
-    for b in (0, 5):
+    for b in range(B):
         say("workload 2 oracle, sequence", b)
         ref = O.Cache(D, wl.group_size, 6, 4, Hkv, nb)
         rbt = np.arange(nb, dtype=np.int32)[None]
@@ -95,10 +98,11 @@ def test_workload2_llama8b_32k_sampled():
         want = O.decode([ref], [rbt], [np.array([N], np.int32)], q[b:b + 1].float().numpy(), sm_scale(D), 0.0,
                         split)
         assert_attention_close(out[b:b + 1], want, max_abs_vhat(ref), f"workload 2 sequence {b}")
+        assert_attention_close(again[b:b + 1], want, max_abs_vhat(ref), f"workload 2 sequence {b}, decode only")
 
 
 @pytest.mark.timeout(900)
-def test_workload3_tiered_sampled():
+def test_workload3_tiered():
     """K6V6 cache, tier update with the error-bound thresholds, decode over
     the HIGH (K6V6) and MID (K6V4) segments with the sparse-V skip, then a
     re-tiering of those segments with fresh scores."""
@@ -145,7 +149,7 @@ def test_workload3_tiered_sampled():
                ht2, mt2)
     torch.cuda.synchronize()
     nh2_h, nm2_h, ht2_h, mt2_h = nh2.cpu().numpy(), nm2.cpu().numpy(), ht2.cpu().numpy(), mt2.cpu().numpy()
-    for b in (1, 6):
+    for b in range(B):
         say("workload 3 oracle, sequence", b)
         ref = O.Cache(D, wl.group_size, 6, 6, Hkv, nb)
         rbt = np.arange(nb, dtype=np.int32)[None]
@@ -174,7 +178,7 @@ def test_workload3_tiered_sampled():
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("fp16", [False, True], ids=["k6v4", "fp16_layer"])
-def test_workload4_llama70b_128k_sampled(fp16):
+def test_workload4_llama70b_128k(fp16):
     wl = workloads.LLAMA70B_128K
     B, Hq, Hkv, D, N = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.n_ctx
     kb, vb = (16, 16) if fp16 else (6, 4)
@@ -182,29 +186,39 @@ def test_workload4_llama70b_128k_sampled(fp16):
     bt = torch.arange(B * nb, dtype=torch.int32).view(B, nb)
     gpu = lkv.Cache(D, wl.group_size, kb, vb, Hkv, B * nb)
     say("workload 4 prefill", wl.name, "fp16" if fp16 else "k6v4")
-    rows = {b: _prefill_gpu(gpu, wl, b, N, bt[b:b + 1]) for b in range(B)}
+    rows = {b: _prefill_gpu(gpu, wl, b, N - 1, bt[b:b + 1]) for b in range(B)}
+    outl = inputs.outlier_channels(wl.seed, Hkv, D)
+    kn, vn = inputs.kv_rows(wl.seed, 1000, B, Hkv, D, outliers=outl, step=1)
     q = inputs.queries(wl.seed, B, Hq, D)
     view = lkv.View(bt.cuda(), torch.full((B,), N, dtype=torch.int32).cuda(), N)
     split = lkv.decode_plan([gpu], [view], B, Hq)
-    say("workload 4 decode split", split)
-    out = lkv.decode_attn([gpu], [view], q.cuda(), sm_scale(D), 0.0, split).cpu().numpy()
+    say("workload 4 append + decode, split", split)
+    out = lkv.append_decode(gpu, view, kn.cuda(), vn.cuda(), q.cuda(), sm_scale(D), 0.0, split).cpu().numpy()
+    again = lkv.decode_attn([gpu], [view], q.cuda(), sm_scale(D), 0.0, split).cpu().numpy()
     torch.cuda.synchronize()
-    b = 1
-    say("workload 4 oracle, sequence", b)
-    ref = O.Cache(D, wl.group_size, kb, vb, Hkv, nb)
-    rbt = np.arange(nb, dtype=np.int32)[None]
-    k, v = rows[b]
-    O.append(ref, k.float().numpy(), v.float().numpy(), [0, N], [0], rbt)
-    _chunks_equal(gpu.pool, bt[b].numpy(), ref, rbt[0], N, Hkv)
-    want = O.decode([ref], [rbt], [np.array([N], np.int32)], q[b:b + 1].float().numpy(), sm_scale(D), 0.0, split)
-    assert_attention_close(out[b:b + 1], want, max_abs_vhat(ref), "workload 4")
+    for b in range(B):
+        say("workload 4 oracle, sequence", b)
+        ref = O.Cache(D, wl.group_size, kb, vb, Hkv, nb)
+        rbt = np.arange(nb, dtype=np.int32)[None]
+        k, v = rows[b]
+        O.append(ref, k.float().numpy(), v.float().numpy(), [0, N - 1], [0], rbt)
+        O.append(ref, kn[b:b + 1].float().numpy(), vn[b:b + 1].float().numpy(), [0, 1], [N - 1], rbt)
+        _chunks_equal(gpu.pool, bt[b].numpy(), ref, rbt[0], N, Hkv)
+        want = O.decode([ref], [rbt], [np.array([N], np.int32)], q[b:b + 1].float().numpy(), sm_scale(D), 0.0,
+                        split)
+        assert_attention_close(out[b:b + 1], want, max_abs_vhat(ref), f"workload 4 sequence {b}")
+        assert_attention_close(again[b:b + 1], want, max_abs_vhat(ref), f"workload 4 sequence {b}, decode only")
 
 
 @pytest.mark.timeout(1200)
 def test_workload5_ragged_paged_every_step():
     """64 ragged sequences (1K-16K) in a randomly permuted paged pool; 128
-    steps of (append one token per sequence, decode).  Every step: the new
-    rows of every sequence bit for bit and two sequences' outputs in full."""
+    steps of (append one token per sequence, decode): even steps as the
+    benchmark runs them (lkv_append_decode, the grid and split of the last
+    step), odd ones as lkv_quant_append then lkv_decode_attn sized for the
+    step.  Every step: the new rows of every sequence bit for bit; the
+    outputs of every sequence at every third step, of two sequences at the
+    others."""
     wl = workloads.QWEN3B_RAGGED
     B, Hq, Hkv, D = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
     lens = inputs.ragged_lengths(wl.seed, B, *wl.ragged).numpy().astype(np.int64)
@@ -239,16 +253,26 @@ def test_workload5_ragged_paged_every_step():
     cu1 = torch.arange(B + 1, dtype=torch.int32).cuda()
     sm = sm_scale(D)
     vmax = max_abs_vhat(ref)
+    # the benchmark's launch configuration: the grid sized by the last step's
+    # max_len, the split by its total length
+    max_len = int(cap.max())
+    split_bench = lkv.decode_plan([gpu], [lkv.View(bt_gpu, torch.tensor(cap, dtype=torch.int32).cuda(), max_len,
+                                                   int(cap.sum()))], B, Hq)
     for step in range(wl.steps):
         k, v = inputs.kv_rows(wl.seed, 2000, B, Hkv, D, step=step + 1)
-        sp = torch.tensor(cur, dtype=torch.int32)
-        lkv.quant_append(gpu, k.cuda(), v.cuda(), cu1, sp.cuda(), bt_gpu, 1)
         O.append(ref, k.float().numpy(), v.float().numpy(), np.arange(B + 1), cur.astype(np.int32), bt)
-        cur = cur + 1
+        lt = torch.tensor(cur + 1, dtype=torch.int32).cuda()
         q = inputs.queries(wl.seed, B, Hq, D, step=step + 1)
-        view = lkv.View(bt_gpu, torch.tensor(cur, dtype=torch.int32).cuda(), int(cur.max()))
-        split = lkv.decode_plan([gpu], [view], B, Hq)
-        out = lkv.decode_attn([gpu], [view], q.cuda(), sm, 0.0, split).cpu().numpy()
+        if step % 2 == 0:  # the benchmark's step: lkv_append_decode (the split kernel appends)
+            view = lkv.View(bt_gpu, lt, max_len, int((cur + 1).sum()))
+            split = split_bench
+            out = lkv.append_decode(gpu, view, k.cuda(), v.cuda(), q.cuda(), sm, 0.0, split).cpu().numpy()
+        else:  # the two calls, the grid and the split sized for this step
+            lkv.quant_append(gpu, k.cuda(), v.cuda(), cu1, torch.tensor(cur, dtype=torch.int32).cuda(), bt_gpu, 1)
+            view = lkv.View(bt_gpu, lt, int(cur.max()) + 1)
+            split = lkv.decode_plan([gpu], [view], B, Hq)
+            out = lkv.decode_attn([gpu], [view], q.cuda(), sm, 0.0, split).cpu().numpy()
+        cur = cur + 1
         torch.cuda.synchronize()
         # the new row of every sequence: the chunk that holds it, bit for bit
         gp = gpu.pool.view(-1, Hkv, ref.chunk_bytes)
@@ -256,7 +280,7 @@ def test_workload5_ragged_paged_every_step():
         g = gp[torch.tensor(blocks, device="cuda")].cpu().numpy()
         r = ref.pool.reshape(-1, Hkv, ref.chunk_bytes)[blocks]
         assert np.array_equal(g, r), f"step {step}: appended rows differ"
-        sample = [step % B, (7 * step + 13) % B]
+        sample = list(range(B)) if step % 3 == 0 else [step % B, (7 * step + 13) % B]
         want = O.decode([ref], [bt[sample]], [cur[sample].astype(np.int32)], q[sample].float().numpy(), sm, 0.0, split)
         assert_attention_close(out[sample], want, vmax, f"workload 5 step {step} sequences {sample}")
         if step % 32 == 0:
