@@ -106,8 +106,11 @@ typedef struct lkv_view {
                                    length above it is out of contract and is read
                                    as max_len */
     int64_t sum_len;            /* (host) hint: total of seq_lens over the batch,
-                                   or 0 if unknown; only lkv_decode_plan reads it,
-                                   to size splits for ragged batches */
+                                   or 0 if unknown; lkv_decode_plan sizes splits
+                                   for ragged batches by it, and the merge of a
+                                   one-segment call whose sum_len is below
+                                   batch * max_len reads only the splits that
+                                   hold tokens (the result is the same) */
 } lkv_view;
 
 /* Human-readable name of a status. */
@@ -308,8 +311,8 @@ int lkv_decode_attn_debug(const lkv_cache* segs, const lkv_view* views, int32_t 
  * lkv_decode_combine on the same stream).  split_tokens must be the
  * resolved (non-zero) split size.  lkv_decode_split writes the partial
  * (o[head_dim], m, L) of every split; a split past its sequence's end writes
- * only m = -inf and L = 0, and lkv_decode_combine gives it weight 0 without
- * reading its o row, so the workspace needs no initialisation. */
+ * only m = -inf and L = 0, and lkv_decode_combine gives it weight 0 and
+ * never uses its o row, so the workspace needs no initialisation. */
 int lkv_decode_split(const lkv_cache* segs, const lkv_view* views, int32_t nseg,
                      const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
                      float sm_scale, float tau_low, int32_t split_tokens,

@@ -121,9 +121,12 @@ static int split_impl(const lkv_cache* segs, const lkv_view* views, int32_t nseg
                       int32_t q_per_seq = 1, uint32_t* skip_mask = nullptr, int32_t mask_stride = 0);
 
 // Merge stage; ml (optional) receives (M, 1 / L) per (sequence, head).
+// per_seq: the rows are the views' sequences (not multi-token entries), so a
+// one-segment merge of a ragged batch can skip the splits past each
+// sequence's end.
 static int combine_impl(const lkv_cache* segs, const lkv_view* views, int32_t nseg, int32_t batch,
                         int32_t num_q_heads, int32_t split_tokens, float* out, const void* workspace,
-                        size_t workspace_bytes, void* stream, float* ml);
+                        size_t workspace_bytes, void* stream, float* ml, bool per_seq = true);
 
 }  // namespace lkv
 
@@ -290,7 +293,7 @@ static int32_t seg_args(const lkv_cache* segs, const lkv_view* views, int32_t ns
 
 static int combine_impl(const lkv_cache* segs, const lkv_view* views, int32_t nseg, int32_t batch,
                         int32_t num_q_heads, int32_t split_tokens, float* out, const void* workspace,
-                        size_t workspace_bytes, void* stream, float* ml)
+                        size_t workspace_bytes, void* stream, float* ml, bool per_seq)
 {
     Fmt f[2];
     const int st = check_decode(segs, views, nseg, batch, num_q_heads, f);
@@ -307,6 +310,14 @@ static int combine_impl(const lkv_cache* segs, const lkv_view* views, int32_t ns
     ca.num_q_heads = num_q_heads;
     ca.total_splits = (int32_t)tot;
     ca.ml = ml;
+    // a ragged batch (the host's total length below batch x max_len): its
+    // merge reads only the splits that hold tokens (one length load per row
+    // first, which a uniform batch would pay for nothing)
+    const bool skip = per_seq && nseg == 1 && views[0].sum_len > 0 &&
+                      views[0].sum_len < (int64_t)batch * views[0].max_len;
+    ca.lens = skip ? views[0].seq_lens : nullptr;
+    ca.len_cap = skip ? views[0].max_len : 0;
+    ca.split_tokens = split_tokens;
     const hipError_t e = launch_decode_combine(ca, batch, f[0].D, (hipStream_t)stream);
     return e == hipSuccess ? LKV_OK : LKV_EHIP;
 }
@@ -502,8 +513,8 @@ int lkv_decode_attn_multi(const lkv_cache* segs, const lkv_view* views, int32_t 
     const int st = split_impl(segs, views, nseg, q, q_dtype, entries, num_q_heads, sm_scale, tau_low, split_tokens,
                               workspace, workspace_bytes, stream, nullptr, 0, q_per_seq);
     if (st != LKV_OK) return st;
-    return lkv_decode_combine(segs, views, nseg, entries, num_q_heads, split_tokens, out, workspace, workspace_bytes,
-                              stream);
+    return combine_impl(segs, views, nseg, entries, num_q_heads, split_tokens, out, workspace, workspace_bytes, stream,
+                        nullptr, false);
 }
 
 int lkv_decode_attn_debug(const lkv_cache* segs, const lkv_view* views, int32_t nseg, const void* q,
@@ -534,8 +545,8 @@ int lkv_decode_attn_debug(const lkv_cache* segs, const lkv_view* views, int32_t 
     const int st = split_impl(segs, views, nseg, q, q_dtype, entries, num_q_heads, sm_scale, tau_low, split_tokens,
                               workspace, workspace_bytes, stream, nullptr, 0, q_per_seq, skip_mask, mask_words);
     if (st != LKV_OK) return st;
-    return lkv_decode_combine(segs, views, nseg, entries, num_q_heads, split_tokens, out, workspace, workspace_bytes,
-                              stream);
+    return combine_impl(segs, views, nseg, entries, num_q_heads, split_tokens, out, workspace, workspace_bytes, stream,
+                        nullptr, false);
 }
 
 void lkv_default_thresholds(int32_t n_tokens, float* tau_low, float* tau_high)

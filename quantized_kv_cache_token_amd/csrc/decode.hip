@@ -300,14 +300,20 @@ __global__ __launch_bounds__(64 * NW) void combine_kernel(CombineArgs a)
 // matrix-core decode: one wave per (sequence, query head) whose lane l holds
 // channels 2l and 2l + 1 of every split's row (one 8-byte load per split,
 // all issued at once); merge128 does the arithmetic, as the split kernel
-// that merges its own splits does.
+// that merges its own splits does.  Given the lengths, only the splits that
+// hold tokens are read: the others' (m, L) are (-inf, 0), which is what the
+// lanes past them take.
 __global__ __launch_bounds__(64) void combine128_kernel(CombineArgs a)
 {
     constexpr int D = 128, CH = 32;
     const int64_t bh = blockIdx.x;
     const int lane = threadIdx.x;
-    const int n = a.total_splits;
-    const float* p = a.part + bh * n * (D + 2);
+    const float* p = a.part + bh * a.total_splits * (D + 2);
+    int n = a.total_splits;
+    if (a.lens != nullptr) {
+        const int len = max(0, min(a.lens[bh / a.num_q_heads], a.len_cap));
+        n = min(n, (len + a.split_tokens - 1) / a.split_tokens);
+    }
     float2 ov[CH];
 #pragma unroll
     for (int i = 0; i < CH; i++) ov[i] = i < n ? *(const float2*)(p + (int64_t)i * (D + 2) + 2 * lane) : float2{};

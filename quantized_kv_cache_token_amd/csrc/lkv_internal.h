@@ -120,6 +120,12 @@ struct CombineArgs {
     int32_t num_q_heads;
     int32_t total_splits;
     float* ml;             // optional: (M, 1 / L) of every (sequence, head), base 2
+    // optional (one segment, a row per sequence): the sequences' lengths, so
+    // that splits past a sequence's end, whose (m, L) = (-inf, 0), are not
+    // read at all; null: every split is read
+    const int32_t* lens;
+    int32_t len_cap;
+    int32_t split_tokens;
 };
 
 // Accumulated attention scores: for every live token j of segment s of

@@ -158,3 +158,34 @@ def test_append_decode_merged_rejects_more_than_32_splits():
     assert e.value.status == lkv.EUNSUPPORTED
     torch.cuda.synchronize()
     assert int(counters.abs().sum()) == 0 and not c.pool.any()  # nothing was launched
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "D{}g{}k{}v{}".format(*c[0]) + f"G{c[1]}{c[2]}{c[3]}")
+@pytest.mark.parametrize("split", [64, 1024])
+def test_ragged_hint_merge_equals_full_merge(case, split):
+    """With a view's sum_len hint on a ragged batch the merge reads only the
+    splits that hold tokens; the decode step's output and pool, and a decode
+    over the same cache, are bit-equal to the calls without the hint, which
+    read every split (an empty sequence, lengths on block and split edges)."""
+    fmt, G, qd, kvd = case
+    D = fmt[0]
+    Hkv = 2
+    lens = LENS
+    B = len(lens)
+    pair, hinted_cache, bt = _caches(fmt, lens, Hkv, 61)
+    q = inputs.queries(62, B, Hkv * G, D, dtype=qd).cuda()
+    btd, lt = torch.tensor(bt).cuda(), torch.tensor(lens, dtype=torch.int32).cuda()
+    plain = lkv.View(btd, lt, max(lens))
+    hinted = lkv.View(btd, lt, max(lens), sum(lens))
+    sm = sm_scale(D)
+    k_new, v_new = inputs.kv_rows(63, 0, B, Hkv, D, dtype=kvd)
+    say("ragged hint", case, "split", split)
+    got = lkv.append_decode(hinted_cache, hinted, k_new.cuda(), v_new.cuda(), q, sm, 0.0, split)
+    want = lkv.append_decode(pair.gpu, plain, k_new.cuda(), v_new.cuda(), q, sm, 0.0, split)
+    again = lkv.decode_attn([hinted_cache], [hinted], q, sm, 0.0, split)
+    base = lkv.decode_attn([hinted_cache], [plain], q, sm, 0.0, split)
+    torch.cuda.synchronize()
+    assert torch.equal(hinted_cache.pool, pair.gpu.pool)
+    assert torch.equal(got, want), f"decode step: max |d| {float((got - want).abs().max())}"
+    assert torch.equal(again, base), f"decode: max |d| {float((again - base).abs().max())}"
+    assert torch.equal(again, got)
