@@ -473,9 +473,10 @@ def setup_ragged(args, wl, dev) -> Setup:
     torch.cuda.synchronize()
     sm = float(np.float32(1.0 / np.sqrt(D)))
     live = [int((lens + s + 1).sum()) for s in range(n_steps)]
-    # the host knows the batch's total length: it sizes the splits (sum_len)
+    # the host knows the batch's lengths: they size the splits (sum_len hint,
+    # and the last step's lengths, which every step's work items fit)
     view_last = lkv.View(bt, after[-1], max_len, live[-1])
-    split = args.split_tokens or lkv.decode_plan([caches[0]], [view_last], B, Hq)
+    split = args.split_tokens or lkv.decode_plan_lens(caches[0], view_last, cap, Hq)
     ws = lkv.decode_workspace([caches[0]], [view_last], B, Hq, split, dev)
     out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
     cu1 = torch.arange(B + 1, dtype=torch.int32, device=dev)

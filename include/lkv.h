@@ -152,6 +152,19 @@ int lkv_quant_append(const lkv_cache* cache, const void* k, const void* v, int32
 int lkv_decode_plan(const lkv_cache* segs, const lkv_view* views, int32_t nseg,
                     int32_t batch, int32_t num_q_heads, int32_t* split_tokens);
 
+/* Split plan of a one-segment decode step (lkv_append_decode,
+ * lkv_append_split) for a host that also knows every sequence's length.  A
+ * ragged batch (view->sum_len below batch * max_len) of at most 64 sequences
+ * in a format with the fused matrix-core step (head_dim 128, K6, V4 or V6,
+ * plain K, 4 or 8 query heads per KV head) runs only its splits with tokens,
+ * each in its own wave: the smallest split whose count of such splits over
+ * the KV heads (an empty sequence counts one) is at most 2048.  Otherwise
+ * lkv_decode_plan's choice.  host_lens [batch] int32, host memory: the
+ * lengths the call will see (the new token counted).  Lengths that differ
+ * from the device's change only the speed.  (host) */
+int lkv_decode_plan_lens(const lkv_cache* cache, const lkv_view* view, const int32_t* host_lens,
+                         int32_t batch, int32_t num_q_heads, int32_t* split_tokens);
+
 /* Bytes of workspace lkv_decode_attn needs for a split size (host):
  * fp32 partials [batch][num_q_heads][total_splits][head_dim + 2]. */
 int64_t lkv_decode_workspace_bytes(const lkv_cache* segs, const lkv_view* views, int32_t nseg,

@@ -128,6 +128,13 @@ static int combine_impl(const lkv_cache* segs, const lkv_view* views, int32_t ns
                         int32_t num_q_heads, int32_t split_tokens, float* out, const void* workspace,
                         size_t workspace_bytes, void* stream, float* ml, bool per_seq = true);
 
+// The view's host hint says the batch is ragged: its total length is known
+// and below batch x max_len.
+static bool ragged_hint(const lkv_view* view, int32_t batch)
+{
+    return view->sum_len > 0 && view->sum_len < (int64_t)batch * view->max_len;
+}
+
 }  // namespace lkv
 
 using namespace lkv;
@@ -227,6 +234,34 @@ int lkv_decode_plan(const lkv_cache* segs, const lkv_view* views, int32_t nseg, 
     return LKV_OK;
 }
 
+int lkv_decode_plan_lens(const lkv_cache* cache, const lkv_view* view, const int32_t* host_lens, int32_t batch,
+                         int32_t num_q_heads, int32_t* split_tokens)
+{
+    const int st = lkv_decode_plan(cache, view, 1, batch, num_q_heads, split_tokens);
+    if (st != LKV_OK) return st;
+    if (batch > 0 && !host_lens) return LKV_EINVAL;
+    // the decode step's compact order runs only the splits with tokens (an
+    // empty sequence counts one): a ragged batch of at most 64 sequences in
+    // a format with the fused matrix-core step
+    const int G = num_q_heads / cache->num_kv_heads;
+    const bool compact = batch <= 64 && ragged_hint(view, batch) && cache->head_dim == 128 && cache->k_bits == 6 &&
+                         (cache->v_bits == 4 || cache->v_bits == 6) && !cache->k_norm && (G == 4 || G == 8);
+    if (!compact) return LKV_OK;
+    // the smallest split whose items fit in one round of 2048, counted exactly
+    constexpr int64_t ITEMS = 2048;
+    int64_t per = 1;
+    for (; per < 64; per++) {
+        int64_t items = 0;
+        for (int b = 0; b < batch; b++) {
+            const int64_t len = std::max<int64_t>(0, std::min<int64_t>(host_lens[b], view->max_len));
+            items += cache->num_kv_heads * std::max<int64_t>(1, (len + per * BT - 1) / (per * BT));
+        }
+        if (items <= ITEMS) break;
+    }
+    *split_tokens = (int32_t)(per * BT);
+    return LKV_OK;
+}
+
 int64_t lkv_decode_workspace_bytes(const lkv_cache* segs, const lkv_view* views, int32_t nseg, int32_t batch,
                                    int32_t num_q_heads, int32_t split_tokens)
 {
@@ -313,8 +348,7 @@ static int combine_impl(const lkv_cache* segs, const lkv_view* views, int32_t ns
     // a ragged batch (the host's total length below batch x max_len): its
     // merge reads only the splits that hold tokens (one length load per row
     // first, which a uniform batch would pay for nothing)
-    const bool skip = per_seq && nseg == 1 && views[0].sum_len > 0 &&
-                      views[0].sum_len < (int64_t)batch * views[0].max_len;
+    const bool skip = per_seq && nseg == 1 && ragged_hint(&views[0], batch);
     ca.lens = skip ? views[0].seq_lens : nullptr;
     ca.len_cap = skip ? views[0].max_len : 0;
     ca.split_tokens = split_tokens;
@@ -430,7 +464,8 @@ int lkv_append_split(const lkv_cache* cache, const lkv_view* view, const void* k
     const int32_t tot = seg_args(cache, view, 1, f, split_tokens, nullptr, 0, 1, nullptr, 0, a);
     hipError_t e;
     if (!launch_append_decode_mfma(a[0], q, q_dtype, batch, num_q_heads, sm_scale, tau_low, split_tokens, tot,
-                                   (float*)workspace, k_new, v_new, kv_dtype, (hipStream_t)stream, &e)) {
+                                   (float*)workspace, k_new, v_new, kv_dtype, (hipStream_t)stream, &e, nullptr,
+                                   nullptr, ragged_hint(view, batch))) {
         // no fused kernel for this format: the append kernel (one row per
         // sequence at its last position), then the split kernel
         e = launch_append(f[0], (uint8_t*)cache->pool, k_new, v_new, kv_dtype, nullptr, view->seq_lens,

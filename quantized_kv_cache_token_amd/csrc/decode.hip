@@ -296,22 +296,26 @@ __global__ __launch_bounds__(64 * NW) void combine_kernel(CombineArgs a)
     }
 }
 
-// The merge for head_dim 128 and at most 32 splits, the shape of the
-// matrix-core decode: one wave per (sequence, query head) whose lane l holds
-// channels 2l and 2l + 1 of every split's row (one 8-byte load per split,
-// all issued at once); merge128 does the arithmetic, as the split kernel
-// that merges its own splits does.  Given the lengths, only the splits that
-// hold tokens are read: the others' (m, L) are (-inf, 0), which is what the
-// lanes past them take.
+// The merge for head_dim 128 and at most CH (32 or 64) splits, the shape of
+// the matrix-core decode: one wave per (sequence, query head) whose lane l
+// holds channels 2l and 2l + 1 of every split's row (one 8-byte load per
+// split) and split l's (m, L); merge128 does the arithmetic, as the split
+// kernel that merges its own splits does.  Given the lengths, only the
+// splits that hold tokens are read: the others' (m, L) are (-inf, 0), which
+// is what the lanes past them take.  (Loads clamped to the last counted
+// split and issued without branches measured no faster: at 32 splits the
+// same, at 33 slower by the cache re-reads.)
+template <int CH>
 __global__ __launch_bounds__(64) void combine128_kernel(CombineArgs a)
 {
-    constexpr int D = 128, CH = 32;
+    constexpr int D = 128;
     const int64_t bh = blockIdx.x;
     const int lane = threadIdx.x;
     const float* p = a.part + bh * a.total_splits * (D + 2);
     int n = a.total_splits;
     if (a.lens != nullptr) {
-        const int len = max(0, min(a.lens[bh / a.num_q_heads], a.len_cap));
+        const int b = (int)(blockIdx.x / (unsigned)a.num_q_heads);
+        const int len = max(0, min(a.lens[b], a.len_cap));
         n = min(n, (len + a.split_tokens - 1) / a.split_tokens);
     }
     float2 ov[CH];
@@ -401,12 +405,14 @@ hipError_t launch_decode_combine(const CombineArgs& a, int32_t batch, int32_t D,
 {
     if (batch == 0) return hipSuccess;
     const dim3 grid((unsigned)(batch * a.num_q_heads));
-    // one wave takes up to 32 splits in one memory latency; more splits are
-    // spread over four waves (sixteen past 128 splits at head_dim 128)
+    // one wave takes up to 32 splits in one memory latency (at head_dim 128
+    // up to 64, a split per lane); more splits are spread over four waves
+    // (sixteen past 128 splits at head_dim 128)
     const bool one = a.total_splits <= 32;
     if (D == 64 && one) hipLaunchKernelGGL((combine_kernel<64, 1>), grid, dim3(64), 0, stream, a);
     else if (D == 64) hipLaunchKernelGGL((combine_kernel<64, 4>), grid, dim3(256), 0, stream, a);
-    else if (one) hipLaunchKernelGGL(combine128_kernel, grid, dim3(64), 0, stream, a);
+    else if (one) hipLaunchKernelGGL(combine128_kernel<32>, grid, dim3(64), 0, stream, a);
+    else if (a.total_splits <= 64) hipLaunchKernelGGL(combine128_kernel<64>, grid, dim3(64), 0, stream, a);
     else if (a.total_splits <= 4 * 32) hipLaunchKernelGGL(combine128w_kernel<4>, grid, dim3(256), 0, stream, a);
     else hipLaunchKernelGGL(combine128w_kernel<16>, grid, dim3(1024), 0, stream, a);
     return hipGetLastError();

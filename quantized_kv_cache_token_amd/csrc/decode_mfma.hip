@@ -68,6 +68,9 @@ struct MfmaArgs {
     // multi-token calls with 8 query heads per KV head: (split, KV head,
     // sequence) items, each run for the call's T query tokens
     int32_t items;
+    // the decode step of a ragged batch of at most 64 sequences: its entry
+    // count, and the grid in compact order (split_append_kernel); 0 otherwise
+    int32_t compact;
 };
 
 // A partial's value, stored plainly, or (WT) as a device-scope relaxed
@@ -1352,23 +1355,71 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
 // head, entry), newest first, the second half the rest.  Inside each half
 // the split index runs fastest, so consecutive workgroups (which go to the
 // XCDs in turn) still take different splits of one row.
+//
+// Compact order (a.compact entries, at most 64: a ragged batch).  Workgroup
+// i takes the i-th (entry, KV head, split) that holds tokens, entries in
+// turn, an entry's KV heads in turn, splits fastest; an empty sequence
+// counts one split, which writes its (m, L) = (-inf, 0).  Every wave finds
+// its item from the entries' lengths (a prefix sum over the lanes), so no
+// slot goes to a split past a sequence's end and the items are spread over
+// the XCDs evenly; workgroups past the last item return at once.  The wave
+// with an entry's newest split also writes (-inf, 0) for the row's splits
+// that have no workgroup, so the partials are complete for any merge.
+__device__ __forceinline__ bool compact_item(const MfmaArgs& a, int lin, int& sp, int& row, int& nsp)
+{
+    const SegArgs& sg = a.seg;
+    const int lane = threadIdx.x, H = sg.f.H, st = a.split_tokens;
+    int c = 0;
+    if (lane < a.compact) c = max(1, min(sg.n_splits, (max(0, min(sg.seq_lens[lane], sg.len_cap)) + st - 1) / st));
+    int x = H * c;  // inclusive prefix sum of the entries' items
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    const uint64_t past = __ballot(x > lin);
+    if (past == 0) return false;
+    const int e = __builtin_ctzll(past);
+    const int ce = __builtin_amdgcn_readlane(c, e);
+    const int k = lin - (__builtin_amdgcn_readlane(x, e) - H * ce);
+    row = e * H + k / ce;
+    sp = k % ce;
+    nsp = ce;
+    return true;
+}
+
 template <int VB, int G, bool MERGE>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void split_append_kernel(MfmaArgs a)
 {
     __shared__ uint4 meta_lds[META_BYTES / 16];
     const int ns = a.seg.n_splits, H = a.seg.f.H;
-    const int P = (ns + 1) / 2;  // splits per row in the first half
-    const int rows = (int)gridDim.x / ns;  // (KV head, entry) rows
-    int lin = blockIdx.x, rev, row;
-    if (lin < P * rows) {
-        rev = lin % P;
-        row = lin / P;
+    int sp, row, nsp = 0;
+    if (!MERGE && a.compact > 0) {
+        if (!compact_item(a, blockIdx.x, sp, row, nsp)) return;
     } else {
-        lin -= P * rows;
-        rev = P + lin % (ns - P);
-        row = lin / (ns - P);
+        const int P = (ns + 1) / 2;  // splits per row in the first half
+        const int rows = (int)gridDim.x / ns;  // (KV head, entry) rows
+        int lin = blockIdx.x, rev;
+        if (lin < P * rows) {
+            rev = lin % P;
+            row = lin / P;
+        } else {
+            lin -= P * rows;
+            rev = P + lin % (ns - P);
+            row = lin / (ns - P);
+        }
+        sp = ns - 1 - rev;
     }
-    split_body<VB, G, false, false, false, true, MERGE>(a, ns - 1 - rev, row % H, row / H, threadIdx.x, meta_lds);
+    split_body<VB, G, false, false, false, true, MERGE>(a, sp, row % H, row / H, threadIdx.x, meta_lds);
+    if (!MERGE && nsp > 0 && sp == nsp - 1) {  // the row's splits without a workgroup: (m, L) = (-inf, 0)
+        const int b = row / H, kvh = row % H;
+        for (int i = threadIdx.x; i < (ns - nsp) * G; i += 64) {
+            float* p = a.partials + (((int64_t)b * a.num_q_heads + kvh * G + i % G) * a.total_splits +
+                                     a.seg.split_base + nsp + i / G) * (128 + 2);
+            p[128] = -INFINITY;
+            p[129] = 0.0f;
+        }
+    }
     if constexpr (MERGE) {
         // The row's last wave to finish merges its ns (<= 32) splits.  The
         // partial's stores went through to the shared level; once they are
@@ -1442,6 +1493,7 @@ static MfmaArgs mfma_args(const SegArgs& s, const void* q, int32_t num_q_heads, 
     a.counters = nullptr;
     a.out = nullptr;
     a.items = 0;
+    a.compact = 0;
     return a;
 }
 
@@ -1504,7 +1556,7 @@ static void launch_plain(const MfmaArgs& a, int vb, int G, bool kn, dim3 grid, h
 bool launch_append_decode_mfma(const SegArgs& s, const void* q, int q_dtype, int32_t batch, int32_t num_q_heads,
                                float sm_scale, float tau_low, int32_t split_tokens, int32_t total_splits,
                                float* partials, const void* k_new, const void* v_new, int kv_dtype,
-                               hipStream_t stream, hipError_t* err, float* out, uint32_t* counters)
+                               hipStream_t stream, hipError_t* err, float* out, uint32_t* counters, bool ragged)
 {
     const uintptr_t align = kv_dtype == LKV_F32 ? 8 : 4;  // a lane reads its two channels at once
     if (!mfma_ok(s, q, q_dtype, num_q_heads, sm_scale, split_tokens) || s.f.k_norm || s.q_per_seq != 1 ||
@@ -1520,7 +1572,10 @@ bool launch_append_decode_mfma(const SegArgs& s, const void* q, int q_dtype, int
     a.kv_dtype = kv_dtype;
     a.counters = counters;
     a.out = out;
-    const dim3 grid((unsigned)(s.n_splits * s.f.H * batch));  // every (split, KV head, entry), in the order above
+    a.compact = !merge && ragged && batch <= 64 ? batch : 0;
+    // every (split, KV head, entry), in the order above (compact: every item
+    // fits, whatever the lengths)
+    const dim3 grid((unsigned)(s.n_splits * s.f.H * batch));
     auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(64), 0, stream, a); };
     if (merge) {
         if (s.f.vb == 4 && G == 4) go(split_append_kernel<4, 4, true>);

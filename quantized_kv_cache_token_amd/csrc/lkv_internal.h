@@ -85,7 +85,7 @@ bool launch_append_decode_mfma(const SegArgs& s, const void* q, int q_dtype, int
                                float sm_scale, float tau_low, int32_t split_tokens, int32_t total_splits,
                                float* partials, const void* k_new, const void* v_new, int kv_dtype,
                                hipStream_t stream, hipError_t* err, float* out = nullptr,
-                               uint32_t* counters = nullptr);
+                               uint32_t* counters = nullptr, bool ragged = false);
 
 // Partials: fp32 [batch][Hq][total_splits][D + 2] = (o[D], m, L).
 hipError_t launch_decode_split(const SegArgs& s, const void* q, int q_dtype, int32_t batch,

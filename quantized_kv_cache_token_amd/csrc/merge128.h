@@ -1,8 +1,8 @@
-// merge128.h -- the merge of up to 32 split partials (o, m, L) of one
-// (sequence, query head) at head_dim 128, in one wave (the split step of the
-// pages' decode: per-split running maximum and sum, then one rescaled sum).
-// Lane l holds channels 2l and 2l + 1 of every split's o row and split l's
-// (m, L); splits past the count hold m = -inf.  Both the merge kernel and the
+// merge128.h -- the merge of up to CH (32 or 64) split partials (o, m, L) of
+// one (sequence, query head) at head_dim 128, in one wave (the split step of
+// the pages' decode: per-split running maximum and sum, then one rescaled
+// sum).  Lane l holds channels 2l and 2l + 1 of every split's o row and
+// split l's (m, L); splits past the count hold m = -inf.  Both the merge kernel and the
 // split kernel that merges its own splits call this one function, built
 // without fp contraction, so the two give the same output bit for bit.
 #pragma once
@@ -26,7 +26,8 @@ __device__ __forceinline__ float merge_wave_sum(float x)
 // M = max_i m_i, L = sum_i L_i 2^(m_i - M), o = sum_i o_i 2^(m_i - M) / L
 // (splits in order; base 2).  Returns the lane's two output channels; M and
 // 1 / L (0 when no split has a token) go to *M_out and *inv_out.
-__device__ __forceinline__ float2 merge128(const float2 (&ov)[32], float mi, float li, float* M_out, float* inv_out)
+template <int CH>
+__device__ __forceinline__ float2 merge128(const float2 (&ov)[CH], float mi, float li, float* M_out, float* inv_out)
 {
 #pragma clang fp contract(off)
     const float M = merge_wave_max(mi);
@@ -36,7 +37,7 @@ __device__ __forceinline__ float2 merge128(const float2 (&ov)[32], float mi, flo
         const float wi = mi == -INFINITY ? 0.0f : exp2f(mi - M);
         L = merge_wave_sum(li * wi);
 #pragma unroll
-        for (int i = 0; i < 32; i++) {
+        for (int i = 0; i < CH; i++) {
             // splits past the count have weight 0 (their lanes hold mi = -inf)
             const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wi), i));
             acc.x += w != 0.0f ? ov[i].x * w : 0.0f;

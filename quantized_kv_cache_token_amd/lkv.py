@@ -49,7 +49,7 @@ EXPORTS = ["lkv_status_string", "lkv_chunk_layout", "lkv_quant_append", "lkv_dec
            "lkv_default_thresholds", "lkv_tier_workspace_bytes", "lkv_tier_update",
            "lkv_retier_workspace_bytes", "lkv_retier", "lkv_decode_attn_multi", "lkv_decode_plan_multi",
            "lkv_decode_attn_debug", "lkv_decode_attn_noalloc", "lkv_append_decode", "lkv_append_split",
-           "lkv_hbm_read_probe", "lkv_append_decode_merged"]
+           "lkv_hbm_read_probe", "lkv_append_decode_merged", "lkv_decode_plan_lens"]
 
 
 def lib():
@@ -67,6 +67,7 @@ def lib():
         "lkv_chunk_layout": ([I32, I32, I32, I32, C.POINTER(I64)], C.c_int),
         "lkv_quant_append": ([PC, P, P, I32, P, P, P, I32, I32, I32, V], C.c_int),
         "lkv_decode_plan": ([PC, PV, I32, I32, I32, C.POINTER(I32)], C.c_int),
+        "lkv_decode_plan_lens": ([PC, PV, P, I32, I32, C.POINTER(I32)], C.c_int),
         "lkv_decode_workspace_bytes": ([PC, PV, I32, I32, I32, I32], I64),
         "lkv_decode_attn": ([PC, PV, I32, P, I32, I32, I32, F, F, I32, P, P, C.c_size_t, V], C.c_int),
         "lkv_decode_split": ([PC, PV, I32, P, I32, I32, I32, F, F, I32, P, C.c_size_t, V], C.c_int),
@@ -170,7 +171,7 @@ class View:
     block_table: torch.Tensor   # int32 [B][max_blocks], device
     seq_lens: torch.Tensor      # int32 [B], device
     max_len: int                # host upper bound of seq_lens
-    sum_len: int = 0            # host hint: total of seq_lens (0 = unknown), read by the split plan only
+    sum_len: int = 0            # host hint: total of seq_lens (0 = unknown); sizes splits, marks a batch ragged
 
     def c(self) -> _View:
         _require(self.block_table.dtype == torch.int32 and self.seq_lens.dtype == torch.int32,
@@ -203,6 +204,19 @@ def decode_plan(caches, views, batch: int, num_q_heads: int) -> int:
     cs, vs, n = _segs(caches, views)
     out = C.c_int32()
     _check("lkv_decode_plan", lib().lkv_decode_plan(cs, vs, n, batch, num_q_heads, C.byref(out)))
+    return out.value
+
+
+def decode_plan_lens(cache: Cache, view: View, host_lens, num_q_heads: int) -> int:
+    """lkv_decode_plan_lens: the decode step's split size from the host's
+    lengths (a sequence of ints, the new token counted)."""
+    import numpy as np
+
+    lens = np.ascontiguousarray(np.asarray(host_lens, dtype=np.int32))
+    out = C.c_int32()
+    cc, vc = cache.c(), view.c()
+    _check("lkv_decode_plan_lens", lib().lkv_decode_plan_lens(C.byref(cc), C.byref(vc), lens.ctypes.data, lens.size,
+                                                              num_q_heads, C.byref(out)))
     return out.value
 
 

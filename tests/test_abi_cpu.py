@@ -123,6 +123,58 @@ def test_plan_uses_the_total_length_hint_of_a_ragged_batch():
         assert out.value == want, (hint, out.value)
 
 
+def _items(lens, H, per, cap):
+    """Splits with tokens of the decode step's compact order (an empty
+    sequence counts one), written out."""
+    return sum(H * max(1, -(-min(max(n, 0), cap) // (64 * per))) for n in lens)
+
+
+def test_exact_length_plan_fits_the_compact_order_in_one_round():
+    """lkv_decode_plan_lens: for a ragged batch of at most 64 sequences in a
+    fused format, the smallest split (in 64-token blocks) whose splits with
+    tokens over the KV heads number at most 2048, by brute force over the
+    lengths; otherwise exactly lkv_decode_plan's choice."""
+    L = lkv.lib()
+    out, ref = C.c_int32(), C.c_int32()
+    rng = np.random.default_rng(7)
+    for trial in range(40):
+        B = int(rng.integers(1, 65))
+        H = int(rng.choice([1, 2, 4, 8]))
+        cap = int(rng.integers(64, 40000))
+        lens = rng.integers(0, cap + 1, B).astype(np.int32)
+        lens[0] = cap
+        total = int(lens.sum())
+        cache = _cache(num_kv_heads=H, num_blocks=100000)
+        view = _view(max_len=cap, max_blocks=-(-cap // 64), sum_len=total)
+        st = L.lkv_decode_plan_lens(C.byref(cache), C.byref(view), lens.ctypes.data, B, 4 * H, C.byref(out))
+        assert st == lkv.OK
+        if total < B * cap:
+            want = next((p for p in range(1, 64) if _items(lens, H, p, cap) <= 2048), 64)
+        else:  # not ragged: the plan of lkv_decode_plan
+            assert L.lkv_decode_plan(C.byref(cache), C.byref(view), 1, B, 4 * H, C.byref(ref)) == lkv.OK
+            want = ref.value // 64
+        assert out.value == 64 * want, (trial, B, H, cap, out.value, want)
+    # the workload shape: 64 sequences of 1K to 16K (+128 steps), 2 KV heads
+    lens = np.arange(64, dtype=np.int32) * 240 + 1152
+    view = _view(max_len=int(lens.max()), max_blocks=-(-int(lens.max()) // 64), sum_len=int(lens.sum()))
+    cache = _cache(num_kv_heads=2, num_blocks=100000)
+    assert L.lkv_decode_plan_lens(C.byref(cache), C.byref(view), lens.ctypes.data, 64, 16, C.byref(out)) == lkv.OK
+    assert _items(lens, 2, out.value // 64, int(lens.max())) <= 2048 < _items(lens, 2, out.value // 64 - 1,
+                                                                              int(lens.max()))
+    # no compact order: more than 64 sequences, the fp16 format, direction-preserving K, 2 query heads per KV head
+    lens = np.full(65, 100, np.int32)
+    lens[0] = 5000
+    for cache, B, Hq in [(_cache(num_kv_heads=2, num_blocks=100000), 65, 8),
+                         (_cache(num_kv_heads=2, num_blocks=100000, k_bits=16, v_bits=16), 64, 8),
+                         (_cache(num_kv_heads=2, num_blocks=100000, k_norm=1), 64, 8),
+                         (_cache(num_kv_heads=2, num_blocks=100000), 64, 4)]:
+        view = _view(max_len=5000, max_blocks=79, sum_len=int(lens[:B].sum()))
+        assert L.lkv_decode_plan_lens(C.byref(cache), C.byref(view), lens.ctypes.data, B, Hq, C.byref(out)) == lkv.OK
+        assert L.lkv_decode_plan(C.byref(cache), C.byref(view), 1, B, Hq, C.byref(ref)) == lkv.OK
+        assert out.value == ref.value
+    assert L.lkv_decode_plan_lens(C.byref(cache), C.byref(view), None, 4, 8, C.byref(out)) == lkv.EINVAL
+
+
 def test_tier_update_rejects_bad_formats():
     L = lkv.lib()
     p = C.c_void_p(0x90000)

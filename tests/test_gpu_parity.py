@@ -183,11 +183,12 @@ def _decode_case(fmt, G, qdtype, lens, tau, split, seed=5, Hkv=2, nseg=1):
     return out.cpu().numpy(), want, vmax
 
 
-@pytest.mark.parametrize("lens", [[4100, 64, 9], [5, 2700, 9000]], ids=["65_splits", "141_splits"])
+@pytest.mark.parametrize("lens", [[2100, 64, 9], [4096, 1, 3000], [4100, 64, 9], [5, 2700, 9000]],
+                         ids=["33_splits", "64_splits", "65_splits", "141_splits"])
 @pytest.mark.parametrize("tau", [0.0, 1e-4])
 def test_decode_parity_many_splits(lens, tau):
-    """More than 32 splits of a sequence: at head_dim 128 the merge spreads
-    them over four waves (up to 128 splits) or sixteen."""
+    """More than 32 splits of a sequence: at head_dim 128 one wave merges up
+    to 64 (a split per lane), four waves up to 128, sixteen beyond."""
     got, want, vmax = _decode_case((128, 64, 6, 4), 4, "bf16", lens, tau, 64)
     assert_attention_close(got, want, vmax, f"{max(lens) // 64 + 1} splits tau {tau}")
 

@@ -254,10 +254,10 @@ def test_workload5_ragged_paged_every_step():
     sm = sm_scale(D)
     vmax = max_abs_vhat(ref)
     # the benchmark's launch configuration: the grid sized by the last step's
-    # max_len, the split by its total length
+    # max_len, the split by its lengths
     max_len = int(cap.max())
-    split_bench = lkv.decode_plan([gpu], [lkv.View(bt_gpu, torch.tensor(cap, dtype=torch.int32).cuda(), max_len,
-                                                   int(cap.sum()))], B, Hq)
+    split_bench = lkv.decode_plan_lens(gpu, lkv.View(bt_gpu, torch.tensor(cap, dtype=torch.int32).cuda(), max_len,
+                                                     int(cap.sum())), cap, Hq)
     for step in range(wl.steps):
         k, v = inputs.kv_rows(wl.seed, 2000, B, Hkv, D, step=step + 1)
         O.append(ref, k.float().numpy(), v.float().numpy(), np.arange(B + 1), cur.astype(np.int32), bt)
