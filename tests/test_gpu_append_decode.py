@@ -189,3 +189,54 @@ def test_ragged_hint_merge_equals_full_merge(case, split):
     assert torch.equal(got, want), f"decode step: max |d| {float((got - want).abs().max())}"
     assert torch.equal(again, base), f"decode: max |d| {float((again - base).abs().max())}"
     assert torch.equal(again, got)
+
+
+N_RAGGED = 120
+
+
+def test_seeded_random_ragged_steps():
+    """Seeded random decode steps of ragged batches (up to 64 sequences,
+    empty ones and block and split edges among them) in the fused formats:
+    with the sum_len hint (the compact order and the merge over the splits
+    with tokens) the pool and the output are bit-equal to the calls without
+    it (the full grid), with and without the skip; without the skip the
+    output is within tolerance of the oracle.  Split sizes are drawn, or
+    taken from lkv_decode_plan_lens."""
+    rng = np.random.default_rng(4077)
+    edge = [0, 1, 63, 64, 65, 127, 128, 129, 511, 512, 513, 1024, 1025]
+    for i in range(N_RAGGED):
+        fmt = ((128, 64, 6, 4), (128, 64, 6, 6), (128, 32, 6, 4))[rng.integers(3)]
+        G = int(rng.choice([4, 8]))
+        Hkv = int(rng.choice([1, 2, 4]))
+        B = int(rng.choice([2, 5, 17, 64])) if rng.random() < 0.5 else int(rng.integers(1, 65))
+        lens = [int(rng.choice(edge)) if rng.random() < 0.4 else int(rng.integers(1, 3000)) for _ in range(B)]
+        lens[0] = max(lens[0], 1)
+        tau = float(rng.choice([0.0, 0.0, 1e-4, 2e-3]))
+        seed = int(rng.integers(1, 10**6))
+        pair, hinted_cache, bt = _caches(fmt, lens, Hkv, seed)
+        D = fmt[0]
+        q = inputs.queries(seed + 1, B, Hkv * G, D).cuda()
+        btd, lt = torch.tensor(bt).cuda(), torch.tensor(lens, dtype=torch.int32).cuda()
+        plain = lkv.View(btd, lt, max(lens))
+        hinted = lkv.View(btd, lt, max(lens), sum(lens))
+        if rng.random() < 0.4:
+            split = lkv.decode_plan_lens(hinted_cache, hinted, lens, Hkv * G)
+        else:
+            split = int(rng.choice([64, 128, 256, 512, 1024]))
+        what = f"case {i}: {fmt} G{G} Hkv{Hkv} B{B} lens {lens} split {split} tau {tau} seed {seed}"
+        say(what)
+        k_new, v_new = inputs.kv_rows(seed + 2, 0, B, Hkv, D)
+        sm = sm_scale(D)
+        got = lkv.append_decode(hinted_cache, hinted, k_new.cuda(), v_new.cuda(), q, sm, tau, split)
+        want = lkv.append_decode(pair.gpu, plain, k_new.cuda(), v_new.cuda(), q, sm, tau, split)
+        torch.cuda.synchronize()
+        assert torch.equal(hinted_cache.pool, pair.gpu.pool), what
+        assert torch.equal(got, want), f"{what}: max |d| {float((got - want).abs().max())}"
+        if tau == 0.0:
+            live = [b for b, n in enumerate(lens) if n > 0]
+            O.append(pair.ref, to_f32_host(k_new[live]), to_f32_host(v_new[live]),
+                     np.arange(len(live) + 1, dtype=np.int32), np.array([lens[b] - 1 for b in live], np.int32),
+                     bt[live])
+            assert pair.pool_equal(), (what, pair.first_pool_mismatch())
+            ref = O.decode([pair.ref], [bt], [np.array(lens, np.int32)], to_f32_host(q), sm, 0.0, split)
+            assert_attention_close(got.cpu().numpy(), ref, max_abs_vhat(pair.ref), what)
