@@ -5,11 +5,14 @@
 A step is one pass of the hot path for one layer: quantise-and-append the
 new token of every sequence, then split-K decode attention of one query per
 sequence over the whole packed cache, then the merge of the split partials.
-With one segment (workloads 2, 4, 5) that is lkv_append_decode: the split
-kernel writes each sequence's new row itself (lkv_append_split), then
-lkv_decode_combine -- two launches.  The tiered workload 3 (two segments),
-and every workload with --unfused, runs lkv_quant_append, lkv_decode_split
-and lkv_decode_combine.  Steps rotate over several layer caches so that
+With one segment and a uniform batch (workloads 2, 4) that is
+lkv_append_decode_merged, one launch: the split kernel writes each
+sequence's new row itself and merges the splits (--two-launch:
+lkv_append_decode, the split kernel then lkv_decode_combine).  The ragged
+workload 5 runs lkv_append_decode (its split kernel in compact order, then
+the merge kernel; --merged: one launch).  The tiered workload 3 (two
+segments), and every workload with --unfused, runs lkv_quant_append,
+lkv_decode_split and lkv_decode_combine.  Steps rotate over several layer caches so that
 consecutive steps stream from HBM, not from the 256 MB last-level cache.
 
   workload 2 (default) and 4: every step re-appends the row of the last
@@ -73,9 +76,12 @@ def parse():
     p.add_argument("--tier-only", action="store_true",
                    help="only the tier-update and re-tier figures at the tiered workload's shape (profiling)")
     p.add_argument("--merged", action="store_true",
-                   help="one launch per step where the library takes it: the split kernel also merges its own "
-                        "splits (lkv_append_decode_merged); by default the merge is its own kernel, which "
-                        "measured faster")
+                   help="ragged workload: one launch per step (lkv_append_decode_merged, the split kernel also "
+                        "merges its own splits) instead of the split kernel in compact order and the merge kernel, "
+                        "which measured faster there; uniform batches (workloads 2 and 4) take one launch by default")
+    p.add_argument("--two-launch", action="store_true",
+                   help="uniform batches: the split kernel, then the merge kernel (lkv_append_decode) instead of "
+                        "one launch that merges in the split kernel")
     p.add_argument("--unfused", action="store_true",
                    help="three launches per step: the append kernel, the split kernel, the merge")
     return p.parse_args()
@@ -126,15 +132,16 @@ def _event():
     return torch.cuda.Event(enable_timing=True)
 
 
-def fused_step(args, S, cache, view, k, v, q, sm, split, out, ws, counters):
+def fused_step(args, S, cache, view, k, v, q, sm, split, out, ws, counters, merged: bool):
     """The stages of one fused step: lkv_append_decode_merged (one launch)
-    where the split kernel can merge its own splits, else the split kernel
-    with the append and the merge kernel (lkv_append_decode's two stages)."""
+    when asked for (merged) and the library takes that form, else the split
+    kernel with the append and the merge kernel (lkv_append_decode's two
+    stages)."""
     from quantized_kv_cache_token_amd import lkv
 
     if S.merged is None:  # decided once, by whether the library takes the merged form
         S.merged = False
-        if args.merged:
+        if merged:
             try:
                 lkv.append_decode_merged(cache, view, k, v, q, sm, 0.0, split, counters, out, ws)
                 S.merged = True
@@ -197,7 +204,8 @@ def setup_uniform(args, wl, dev) -> Setup:
                               device=dev)
         q = inputs.queries(wl.seed, B, Hq, D, dtype=wl.dtype, layer=layer, device=dev)
         if S.fused:  # the new row of each sequence is position N - 1: lengths are N
-            S.calls.append(fused_step(args, S, caches[layer], view, k, v, q, sm, split, out, ws, counters))
+            S.calls.append(fused_step(args, S, caches[layer], view, k, v, q, sm, split, out, ws, counters,
+                                      not args.two_launch))
         else:
             app = lkv.prepare_append(caches[layer], k, v, cu1, last, bt, 1)
             spl, comb = lkv.prepare_decode([caches[layer]], [view], q, sm, 0.0, split, out, ws)
@@ -492,7 +500,7 @@ def setup_ragged(args, wl, dev) -> Setup:
             k, v = kvs[layer]
             if S.fused:  # the new row of sequence b is position len_b + s: the step's lengths count it
                 S.calls.append(fused_step(args, S, caches[layer], views[s], k, v, qs[layer], sm, split, out, ws,
-                                          counters))
+                                          counters, args.merged))
             else:
                 app = lkv.prepare_append(caches[layer], k, v, cu1, pos[s], bt, 1)
                 spl, comb = lkv.prepare_decode([caches[layer]], [views[s]], qs[layer], sm, 0.0, split, out, ws)

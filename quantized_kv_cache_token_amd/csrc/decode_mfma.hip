@@ -73,16 +73,6 @@ struct MfmaArgs {
     int32_t compact;
 };
 
-// A partial's value, stored plainly, or (WT) as a device-scope relaxed
-// atomic store, which writes through to where every compute unit reads it:
-// the splits a wave merges were written by waves on other L2 caches.
-template <bool WT>
-__device__ __forceinline__ void pstore(float* p, float v)
-{
-    if constexpr (WT) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else *p = v;
-}
-
 // The bit manipulations below are plain C, never inline asm: a matrix-core
 // instruction that reads a VGPR just written by a vector instruction needs
 // wait states, which the compiler inserts only for instructions it can see.
@@ -996,9 +986,12 @@ __device__ __forceinline__ void patch_v(BlockRegs<VB>& R, const NewRow& r, int s
 // for both.  The earlier token's causal prefix is one token shorter: its
 // columns are masked in the split's last blocks.  An odd T's last token is
 // paired with itself and its second copy is not written.
-template <int VB, int G, bool KN, bool PAIR = false, bool DBG = false, bool APP = false, bool WT = false>
+//
+// LO: the partial goes to lo (LDS, [G][D + 2]) instead of the workspace, for
+// a workgroup that merges its waves' splits before anything leaves the CU.
+template <int VB, int G, bool KN, bool PAIR = false, bool DBG = false, bool APP = false, bool LO = false>
 __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, const int kvh, const int b, const int lane,
-                                           uint4* meta_lds)
+                                           uint4* meta_lds, float* lo = nullptr)
 {
     static_assert(G == 4 || G == 8, "4 or 8 query heads per KV head");
     static_assert(!PAIR || G == 8, "a pair fills the 8-head layout");
@@ -1042,11 +1035,14 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, cons
                 p[D] = -INFINITY;
                 p[D + 1] = 0.0f;
             }
+        } else if (LO && lane < G) {
+            lo[lane * (D + 2) + D] = -INFINITY;
+            lo[lane * (D + 2) + D + 1] = 0.0f;
         } else if (lane < G) {
             float* p = a.partials + (((int64_t)b * a.num_q_heads + kvh * G + lane) * a.total_splits +
                                      sg.split_base + sp) * (D + 2);
-            pstore<WT>(p + D, -INFINITY);
-            pstore<WT>(p + D + 1, 0.0f);
+            p[D] = -INFINITY;
+            p[D + 1] = 0.0f;
         }
         return;
     }
@@ -1286,12 +1282,22 @@ __device__ __forceinline__ void split_body(const MfmaArgs& a, const int sp, cons
             o1 = halves_sum(o1);
             if ((q >> 1) != (T >> 2)) continue;
         }
-        pstore<WT>(base + hA * hstride + soff + 16 * T + c, o0);
-        pstore<WT>(base + (hA + 1) * hstride + soff + 16 * T + c, o1);
+        if constexpr (LO) {
+            lo[hA * (D + 2) + 16 * T + c] = o0;
+            lo[(hA + 1) * (D + 2) + 16 * T + c] = o1;
+        } else {
+            base[hA * hstride + soff + 16 * T + c] = o0;
+            base[(hA + 1) * hstride + soff + 16 * T + c] = o1;
+        }
     }
     if (q == 0 && part == 0 && (G == 8 || c < 8)) {  // two-set layout: set 0's lane of the head
-        pstore<WT>(base + hc * hstride + soff + D, S.m_run);
-        pstore<WT>(base + hc * hstride + soff + D + 1, S.l_run);
+        if constexpr (LO) {
+            lo[hc * (D + 2) + D] = S.m_run;
+            lo[hc * (D + 2) + D + 1] = S.l_run;
+        } else {
+            base[hc * hstride + soff + D] = S.m_run;
+            base[hc * hstride + soff + D + 1] = S.l_run;
+        }
     }
 }
 
@@ -1388,13 +1394,13 @@ __device__ __forceinline__ bool compact_item(const MfmaArgs& a, int lin, int& sp
     return true;
 }
 
-template <int VB, int G, bool MERGE>
+template <int VB, int G>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void split_append_kernel(MfmaArgs a)
 {
     __shared__ uint4 meta_lds[META_BYTES / 16];
     const int ns = a.seg.n_splits, H = a.seg.f.H;
     int sp, row, nsp = 0;
-    if (!MERGE && a.compact > 0) {
+    if (a.compact > 0) {
         if (!compact_item(a, blockIdx.x, sp, row, nsp)) return;
     } else {
         const int P = (ns + 1) / 2;  // splits per row in the first half
@@ -1410,8 +1416,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
         }
         sp = ns - 1 - rev;
     }
-    split_body<VB, G, false, false, false, true, MERGE>(a, sp, row % H, row / H, threadIdx.x, meta_lds);
-    if (!MERGE && nsp > 0 && sp == nsp - 1) {  // the row's splits without a workgroup: (m, L) = (-inf, 0)
+    split_body<VB, G, false, false, false, true>(a, sp, row % H, row / H, threadIdx.x, meta_lds);
+    if (nsp > 0 && sp == nsp - 1) {  // the row's splits without a workgroup: (m, L) = (-inf, 0)
         const int b = row / H, kvh = row % H;
         for (int i = threadIdx.x; i < (ns - nsp) * G; i += 64) {
             float* p = a.partials + (((int64_t)b * a.num_q_heads + kvh * G + i % G) * a.total_splits +
@@ -1420,46 +1426,106 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
             p[129] = 0.0f;
         }
     }
-    if constexpr (MERGE) {
-        // The row's last wave to finish merges its ns (<= 32) splits.  The
-        // partial's stores went through to the shared level; once they are
-        // complete the wave counts itself in (the counter wraps to 0 at ns),
-        // and the wave that counts last reads every split of the row back
-        // with device-scope loads.
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        uint32_t old = 0;
-        if (threadIdx.x == 0) old = atomicInc(a.counters + row, (unsigned)(ns - 1));
-        if (__builtin_amdgcn_readfirstlane(old) != (uint32_t)(ns - 1)) return;
-        constexpr int D = 128;
-        const int lane = threadIdx.x, b = row / H, kvh = row % H;
-        float2 ov[2][32];
-        float mi[2], li[2];
-        auto fetch = [&](int g, int k) __attribute__((always_inline)) {
-            float* p = a.partials + ((int64_t)b * a.num_q_heads + kvh * G + g) * a.total_splits * (D + 2);
+}
+
+// The decode step in one launch (lkv_append_decode_merged): the split kernel
+// with the step's append also merges the splits.  A workgroup of MW waves
+// takes MW consecutive splits of one (KV head, entry) row, one per wave, and
+// each wave leaves its partial in LDS.  The workgroup merges those into one
+// partial (wave w: heads w, w + MW, ..), writes it through to the workspace
+// as the row's partial j (device-scope stores, which reach the level every
+// compute unit reads: the row's other workgroups run on other L2 caches),
+// waits for the stores and counts itself in the row's counter (atomicInc,
+// wrapping to 0 at the row's workgroup count nw).  The workgroup that counts
+// last reads the row's nw partials back with device-scope loads and merges
+// them into the output.  Only nw partials per head leave a compute unit, and
+// the last workgroup's MW waves merge the heads side by side.
+//
+// Dispatch order as in split_append_kernel, by workgroup: the first half of
+// the grid takes the last ceil(nw / 2) workgroups of every row (which hold
+// the newest splits and the append), newest first, the second half the rest.
+constexpr int MW = 4;
+
+template <int VB, int G>
+__global__ __launch_bounds__(64 * MW) __attribute__((amdgpu_waves_per_eu(2))) void split_append_merged_kernel(
+    MfmaArgs a)
+{
+    constexpr int D = 128;
+    __shared__ uint4 meta_lds[MW][META_BYTES / 16];
+    __shared__ float part[MW][G][D + 2];
+    __shared__ uint32_t ticket;
+    // the wave index is uniform: read it into a scalar register, so that the
+    // split and everything addressed from it stay scalar in split_body
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int ns = a.seg.n_splits, H = a.seg.f.H;
+    const int nw = (ns + MW - 1) / MW;  // workgroups (merged partials) per row
+    const int P = (nw + 1) / 2;         // workgroups per row in the first half
+    const int rows = (int)gridDim.x / nw;
+    int lin = blockIdx.x, rev, row;
+    if (lin < P * rows) {
+        rev = lin % P;
+        row = lin / P;
+    } else {
+        lin -= P * rows;
+        rev = P + lin % (nw - P);
+        row = lin / (nw - P);
+    }
+    const int j = nw - 1 - rev;
+    const int sp = j * MW + w, b = row / H, kvh = row % H;
+    if (sp < ns) {
+        split_body<VB, G, false, false, false, true, true>(a, sp, kvh, b, lane, meta_lds[w], &part[w][0][0]);
+    } else if (lane < G) {  // past the row's last split: no token
+        part[w][lane][D] = -INFINITY;
+        part[w][lane][D + 1] = 0.0f;
+    }
+    __syncthreads();
+    float* const prow0 = a.partials + ((int64_t)b * a.num_q_heads + kvh * G) * a.total_splits * (D + 2);
+    for (int h = w; h < G; h += MW) {
+        float2 ov[MW];
 #pragma unroll
-            for (int i = 0; i < 32; i++) {
-                const uint64_t v = i < ns ? __hip_atomic_load((uint64_t*)(p + (int64_t)i * (D + 2) + 2 * lane),
-                                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                          : 0ull;
-                ov[k][i] = float2{__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32))};
-            }
-            mi[k] = lane < ns ? __hip_atomic_load(p + (int64_t)lane * (D + 2) + D, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT)
-                              : -INFINITY;
-            li[k] = lane < ns ? __hip_atomic_load(p + (int64_t)lane * (D + 2) + D + 1, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT)
-                              : 0.0f;
-        };
-        // head g + 1's loads are in flight while head g is merged
-        fetch(0, 0);
-#pragma unroll
-        for (int g = 0; g < G; g++) {
-            if (g + 1 < G) fetch(g + 1, (g + 1) & 1);
-            float M, inv;
-            *(float2*)(a.out + ((int64_t)b * a.num_q_heads + kvh * G + g) * D + 2 * lane) =
-                merge128(ov[g & 1], mi[g & 1], li[g & 1], &M, &inv);
+        for (int i = 0; i < MW; i++) ov[i] = *(const float2*)&part[i][h][2 * lane];
+        const float mi = lane < MW ? part[lane][h][D] : -INFINITY;
+        const float li = lane < MW ? part[lane][h][D + 1] : 0.0f;
+        float M, L;
+        const float2 o = merge128_partial(ov, mi, li, &M, &L);
+        float* p = prow0 + ((int64_t)h * a.total_splits + j) * (D + 2);
+        const uint64_t ob = (uint64_t)__float_as_uint(o.x) | ((uint64_t)__float_as_uint(o.y) << 32);
+        __hip_atomic_store((uint64_t*)(p + 2 * lane), ob, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) {
+            const uint64_t ml = (uint64_t)__float_as_uint(M) | ((uint64_t)__float_as_uint(L) << 32);
+            __hip_atomic_store((uint64_t*)(p + D), ml, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are complete
+    __syncthreads();                                  // ... and every wave's
+    if (threadIdx.x == 0) ticket = atomicInc(a.counters + row, (unsigned)(nw - 1));
+    __syncthreads();
+    if (ticket != (uint32_t)(nw - 1)) return;
+    // the row's last workgroup: wave w merges heads w, w + MW, .. over the nw partials
+    auto merge_row = [&](auto ch) __attribute__((always_inline)) {
+        constexpr int CH = decltype(ch)::value;
+        for (int h = w; h < G; h += MW) {
+            const float* p = prow0 + (int64_t)h * a.total_splits * (D + 2);
+            float2 ov[CH];
+#pragma unroll
+            for (int i = 0; i < CH; i++) {  // past the count: a counted row again, at weight 0
+                const uint64_t v = __hip_atomic_load((const uint64_t*)(p + (int64_t)min(i, nw - 1) * (D + 2) + 2 * lane),
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ov[i] = float2{__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32))};
+            }
+            uint64_t ml = 0xFF800000ull;  // (m, L) = (-inf, 0) past the count
+            if (lane < nw)
+                ml = __hip_atomic_load((const uint64_t*)(p + (int64_t)lane * (D + 2) + D), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            float M, inv;
+            *(float2*)(a.out + ((int64_t)b * a.num_q_heads + kvh * G + h) * D + 2 * lane) =
+                merge128(ov, __uint_as_float((uint32_t)ml), __uint_as_float((uint32_t)(ml >> 32)), &M, &inv);
+        }
+    };
+    if (nw <= 8) merge_row(std::integral_constant<int, 8>{});
+    else if (nw <= 16) merge_row(std::integral_constant<int, 16>{});
+    else if (nw <= 32) merge_row(std::integral_constant<int, 32>{});
+    else merge_row(std::integral_constant<int, 64>{});
 }
 
 // Whether a segment has a matrix-core kernel.
@@ -1564,7 +1630,7 @@ bool launch_append_decode_mfma(const SegArgs& s, const void* q, int q_dtype, int
         (uintptr_t)v_new % align != 0)
         return false;
     const bool merge = counters != nullptr;
-    if (merge && (s.n_splits > 32 || total_splits != s.n_splits || !out)) return false;
+    if (merge && ((s.n_splits + MW - 1) / MW > 64 || total_splits != s.n_splits || !out)) return false;
     const int G = num_q_heads / s.f.H;
     MfmaArgs a = mfma_args(s, q, num_q_heads, sm_scale, tau_low, split_tokens, total_splits, partials);
     a.k_new = k_new;
@@ -1573,20 +1639,20 @@ bool launch_append_decode_mfma(const SegArgs& s, const void* q, int q_dtype, int
     a.counters = counters;
     a.out = out;
     a.compact = !merge && ragged && batch <= 64 ? batch : 0;
-    // every (split, KV head, entry), in the order above (compact: every item
-    // fits, whatever the lengths)
-    const dim3 grid((unsigned)(s.n_splits * s.f.H * batch));
-    auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(64), 0, stream, a); };
-    if (merge) {
-        if (s.f.vb == 4 && G == 4) go(split_append_kernel<4, 4, true>);
-        else if (s.f.vb == 4) go(split_append_kernel<4, 8, true>);
-        else if (G == 4) go(split_append_kernel<6, 4, true>);
-        else go(split_append_kernel<6, 8, true>);
-    } else {
-        if (s.f.vb == 4 && G == 4) go(split_append_kernel<4, 4, false>);
-        else if (s.f.vb == 4) go(split_append_kernel<4, 8, false>);
-        else if (G == 4) go(split_append_kernel<6, 4, false>);
-        else go(split_append_kernel<6, 8, false>);
+    if (merge) {  // every (workgroup of MW splits, KV head, entry), in the order above
+        const dim3 grid((unsigned)((s.n_splits + MW - 1) / MW * s.f.H * batch));
+        auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(64 * MW), 0, stream, a); };
+        if (s.f.vb == 4 && G == 4) go(split_append_merged_kernel<4, 4>);
+        else if (s.f.vb == 4) go(split_append_merged_kernel<4, 8>);
+        else if (G == 4) go(split_append_merged_kernel<6, 4>);
+        else go(split_append_merged_kernel<6, 8>);
+    } else {  // every (split, KV head, entry), in the order above (compact: every item fits, whatever the lengths)
+        const dim3 grid((unsigned)(s.n_splits * s.f.H * batch));
+        auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(64), 0, stream, a); };
+        if (s.f.vb == 4 && G == 4) go(split_append_kernel<4, 4>);
+        else if (s.f.vb == 4) go(split_append_kernel<4, 8>);
+        else if (G == 4) go(split_append_kernel<6, 4>);
+        else go(split_append_kernel<6, 8>);
     }
     *err = hipGetLastError();
     return true;

@@ -1,10 +1,11 @@
-// merge128.h -- the merge of up to CH (32 or 64) split partials (o, m, L) of
+// merge128.h -- the merge of up to CH (at most 64) split partials (o, m, L) of
 // one (sequence, query head) at head_dim 128, in one wave (the split step of
 // the pages' decode: per-split running maximum and sum, then one rescaled
 // sum).  Lane l holds channels 2l and 2l + 1 of every split's o row and
-// split l's (m, L); splits past the count hold m = -inf.  Both the merge kernel and the
-// split kernel that merges its own splits call this one function, built
-// without fp contraction, so the two give the same output bit for bit.
+// split l's (m, L); splits past the count hold m = -inf.  The merge kernel
+// and the split kernel that merges its own splits (a workgroup's splits
+// first, then the workgroups' partials) use these functions, built without
+// fp contraction.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -48,6 +49,33 @@ __device__ __forceinline__ float2 merge128(const float2 (&ov)[CH], float mi, flo
     *M_out = M;
     *inv_out = inv;
     return float2{acc.x * inv, acc.y * inv};
+}
+
+// The same merge without the final division: the partial (o, M, L) of the
+// union of the splits, o = sum_i o_i 2^(m_i - M) and L = sum_i L_i 2^(m_i -
+// M), to be merged again with other such partials.  M = -inf and L = 0 when
+// no split has a token.
+template <int CH>
+__device__ __forceinline__ float2 merge128_partial(const float2 (&ov)[CH], float mi, float li, float* M_out,
+                                                   float* L_out)
+{
+#pragma clang fp contract(off)
+    const float M = merge_wave_max(mi);
+    float2 acc = {0.0f, 0.0f};
+    float L = 0.0f;
+    if (M != -INFINITY) {
+        const float wi = mi == -INFINITY ? 0.0f : exp2f(mi - M);
+        L = merge_wave_sum(li * wi);
+#pragma unroll
+        for (int i = 0; i < CH; i++) {
+            const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wi), i));
+            acc.x += w != 0.0f ? ov[i].x * w : 0.0f;
+            acc.y += w != 0.0f ? ov[i].y * w : 0.0f;
+        }
+    }
+    *M_out = M;
+    *L_out = L;
+    return acc;
 }
 
 }  // namespace lkv
