@@ -52,8 +52,11 @@ PROFILES = os.path.join(ROOT, "profiles")
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=400)
-    p.add_argument("--warmup", type=int, default=40)
+    # by default the timed steps start after the GPU's step time has settled:
+    # from a start the first ~30 steps of workload 2 ran fast, the next few
+    # hundred up to 40% slower, and from there on the step time was steady
+    p.add_argument("--steps", type=int, default=2000)
+    p.add_argument("--warmup", type=int, default=1000)
     p.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5])
     p.add_argument("--layers", type=int, default=4, help="layer caches rotated over (HBM, not cache)")
     p.add_argument("--split-tokens", type=int, default=0)
@@ -600,9 +603,14 @@ def main():
     gc.disable()  # no cycle-collector pause inside the timed steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    # (and an event at each tenth of them: the step time by window)
+    nwin = min(10, args.steps)
+    wev = [_event() for _ in range(nwin - 1)]
     with torch.cuda.stream(run_stream):
         g0.record(run_stream)
         for i in range(args.steps):
+            if i * nwin % args.steps < nwin and 0 < i * nwin // args.steps:
+                wev[i * nwin // args.steps - 1].record(run_stream)
             if graphs is not None:
                 graphs[(first + i) % n_calls].replay()
             else:
@@ -612,10 +620,13 @@ def main():
     t1 = time.perf_counter()
     gc.enable()
     gpu_step_s = g0.elapsed_time(g1) / 1e3 / args.steps
+    bounds = [g0] + wev + [g1]
+    edges = [0] + [next(i for i in range(args.steps) if i * nwin // args.steps == w) for w in range(1, nwin)] + [args.steps]
+    window_us = [round(bounds[w].elapsed_time(bounds[w + 1]) * 1e3 / (edges[w + 1] - edges[w]), 1) for w in range(nwin)]
     # then, outside the timed region, HIP events before and after each stage
     # of one step in every rotation cycle, replaying the same steps launch by
     # launch: the split kernel's and the merge's own durations
-    timed = [i for i in range(args.steps) if i % args.layers == 0]
+    timed = list(range(args.steps))
     evs = {i: tuple(_event() for _ in range(n_stages + 1)) for i in timed}
     with torch.cuda.stream(run_stream):
         for i in timed:
@@ -667,6 +678,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(step_s * 1e3, 4),
         "gpu_ms_per_step": round(gpu_step_s * 1e3, 4),
+        "step_us_by_tenth": window_us,
         "graph_replay": graphs is not None,
         "higher_is_better": True,
         "scaling": "weak",
