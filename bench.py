@@ -52,11 +52,12 @@ PROFILES = os.path.join(ROOT, "profiles")
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    # by default the timed steps start after the GPU's step time has settled:
-    # from a start the first ~30 steps of workload 2 ran fast, the next few
-    # hundred up to 40% slower, and from there on the step time was steady
-    p.add_argument("--steps", type=int, default=2000)
-    p.add_argument("--warmup", type=int, default=1000)
+    # after every synchronisation (the GPU idle) the step time of workload 2
+    # ran fast for ~30 steps, then up to 40% slower for a few hundred, then
+    # steady: the default run times enough steps for the steady part to
+    # dominate
+    p.add_argument("--steps", type=int, default=10000)
+    p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5])
     p.add_argument("--layers", type=int, default=4, help="layer caches rotated over (HBM, not cache)")
     p.add_argument("--split-tokens", type=int, default=0)
@@ -624,9 +625,9 @@ def main():
     edges = [0] + [next(i for i in range(args.steps) if i * nwin // args.steps == w) for w in range(1, nwin)] + [args.steps]
     window_us = [round(bounds[w].elapsed_time(bounds[w + 1]) * 1e3 / (edges[w + 1] - edges[w]), 1) for w in range(nwin)]
     # then, outside the timed region, HIP events before and after each stage
-    # of one step in every rotation cycle, replaying the same steps launch by
-    # launch: the split kernel's and the merge's own durations
-    timed = list(range(args.steps))
+    # of the first (at most 2000) timed steps, replayed launch by launch over
+    # the same rotation: the split kernel's and the merge's own durations
+    timed = list(range(min(args.steps, 2000)))
     evs = {i: tuple(_event() for _ in range(n_stages + 1)) for i in timed}
     with torch.cuda.stream(run_stream):
         for i in timed:

@@ -218,18 +218,19 @@ int lkv_append_decode(const lkv_cache* cache, const lkv_view* view, const void* 
                       size_t workspace_bytes, void* stream);
 
 /* lkv_append_decode in one launch: the split kernel also merges the split
- * partials (the combine step of the split decode).  A workgroup of four
- * waves runs four consecutive splits of a (sequence, KV head) and merges
- * them in LDS; the last of a row's workgroups to finish merges the row's
- * workgroup partials into the output.  The pool is exactly
- * lkv_append_decode's; the output is the same attention merged in another
- * order (four splits at a time, then the groups), so it may differ from
+ * partials (the combine step of the split decode).  A workgroup of G waves
+ * (G = query heads per KV head, 4 or 8) runs G consecutive splits of a
+ * (sequence, KV head) and merges them in LDS; the last of a row's
+ * workgroups to finish merges the row's workgroup partials into the output.
+ * The pool is exactly lkv_append_decode's; the output is the same attention
+ * merged in another order (G splits at a time, then the groups), so it may
+ * differ from
  * lkv_append_decode's in the last bits.  counters: uint32 [batch][number of
  * KV heads], caller-owned, all zero before the first call (a zero-filled
  * allocation); every completed call leaves them zero.  Calls that share
  * counters or a workspace must not overlap.  Formats and shapes: those for
  * which lkv_append_decode writes the new rows in the split kernel, with at
- * most 256 splits per sequence (max_len <= 256 * split_tokens); otherwise
+ * most 64 G splits per sequence (max_len <= 64 * G * split_tokens); otherwise
  * LKV_EUNSUPPORTED and nothing is launched (lkv_append_decode serves every
  * case).  Workspace: lkv_decode_workspace_bytes(). */
 int lkv_append_decode_merged(const lkv_cache* cache, const lkv_view* view, const void* k_new, const void* v_new,

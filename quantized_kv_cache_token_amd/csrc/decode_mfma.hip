@@ -1429,28 +1429,27 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
 }
 
 // The decode step in one launch (lkv_append_decode_merged): the split kernel
-// with the step's append also merges the splits.  A workgroup of MW waves
-// takes MW consecutive splits of one (KV head, entry) row, one per wave, and
+// with the step's append also merges the splits.  A workgroup of MW = G
+// waves (as many as query heads per KV head) takes MW consecutive splits of
+// one (KV head, entry) row, one per wave, and
 // each wave leaves its partial in LDS.  The workgroup merges those into one
-// partial (wave w: heads w, w + MW, ..), writes it through to the workspace
+// partial (wave w: head w), writes it through to the workspace
 // as the row's partial j (device-scope stores, which reach the level every
 // compute unit reads: the row's other workgroups run on other L2 caches),
 // waits for the stores and counts itself in the row's counter (atomicInc,
 // wrapping to 0 at the row's workgroup count nw).  The workgroup that counts
 // last reads the row's nw partials back with device-scope loads and merges
 // them into the output.  Only nw partials per head leave a compute unit, and
-// the last workgroup's MW waves merge the heads side by side.
+// the last workgroup's waves merge the heads side by side, one head each.
 //
 // Dispatch order as in split_append_kernel, by workgroup: the first half of
 // the grid takes the last ceil(nw / 2) workgroups of every row (which hold
 // the newest splits and the append), newest first, the second half the rest.
-constexpr int MW = 4;
-
 template <int VB, int G>
-__global__ __launch_bounds__(64 * MW) __attribute__((amdgpu_waves_per_eu(2))) void split_append_merged_kernel(
+__global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2))) void split_append_merged_kernel(
     MfmaArgs a)
 {
-    constexpr int D = 128;
+    constexpr int D = 128, MW = G;
     __shared__ uint4 meta_lds[MW][META_BYTES / 16];
     __shared__ float part[MW][G][D + 2];
     __shared__ uint32_t ticket;
@@ -1480,7 +1479,8 @@ __global__ __launch_bounds__(64 * MW) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
     __syncthreads();
     float* const prow0 = a.partials + ((int64_t)b * a.num_q_heads + kvh * G) * a.total_splits * (D + 2);
-    for (int h = w; h < G; h += MW) {
+    {
+        const int h = w;
         float2 ov[MW];
 #pragma unroll
         for (int i = 0; i < MW; i++) ov[i] = *(const float2*)&part[i][h][2 * lane];
@@ -1501,10 +1501,11 @@ __global__ __launch_bounds__(64 * MW) __attribute__((amdgpu_waves_per_eu(2))) vo
     if (threadIdx.x == 0) ticket = atomicInc(a.counters + row, (unsigned)(nw - 1));
     __syncthreads();
     if (ticket != (uint32_t)(nw - 1)) return;
-    // the row's last workgroup: wave w merges heads w, w + MW, .. over the nw partials
+    // the row's last workgroup: wave w merges head w over the nw partials
     auto merge_row = [&](auto ch) __attribute__((always_inline)) {
         constexpr int CH = decltype(ch)::value;
-        for (int h = w; h < G; h += MW) {
+        {
+            const int h = w;
             const float* p = prow0 + (int64_t)h * a.total_splits * (D + 2);
             float2 ov[CH];
 #pragma unroll
@@ -1630,8 +1631,8 @@ bool launch_append_decode_mfma(const SegArgs& s, const void* q, int q_dtype, int
         (uintptr_t)v_new % align != 0)
         return false;
     const bool merge = counters != nullptr;
-    if (merge && ((s.n_splits + MW - 1) / MW > 64 || total_splits != s.n_splits || !out)) return false;
     const int G = num_q_heads / s.f.H;
+    if (merge && ((s.n_splits + G - 1) / G > 64 || total_splits != s.n_splits || !out)) return false;
     MfmaArgs a = mfma_args(s, q, num_q_heads, sm_scale, tau_low, split_tokens, total_splits, partials);
     a.k_new = k_new;
     a.v_new = v_new;
@@ -1639,9 +1640,9 @@ bool launch_append_decode_mfma(const SegArgs& s, const void* q, int q_dtype, int
     a.counters = counters;
     a.out = out;
     a.compact = !merge && ragged && batch <= 64 ? batch : 0;
-    if (merge) {  // every (workgroup of MW splits, KV head, entry), in the order above
-        const dim3 grid((unsigned)((s.n_splits + MW - 1) / MW * s.f.H * batch));
-        auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(64 * MW), 0, stream, a); };
+    if (merge) {  // every (workgroup of G splits, KV head, entry), in the order above
+        const dim3 grid((unsigned)((s.n_splits + G - 1) / G * s.f.H * batch));
+        auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(64 * G), 0, stream, a); };
         if (s.f.vb == 4 && G == 4) go(split_append_merged_kernel<4, 4>);
         else if (s.f.vb == 4) go(split_append_merged_kernel<4, 8>);
         else if (G == 4) go(split_append_merged_kernel<6, 4>);

@@ -117,12 +117,12 @@ MERGED = [c for c in CASES if c[0][:3] == (128, 64, 6) and c[0][3] in (4, 6) and
 def test_append_decode_merged_equals_append_decode(case, split):
     """The split kernel that merges its own splits: three steps in a row, each
     with the pool bit for bit that of lkv_append_decode, the output within
-    tolerance of the oracle (the splits are merged four at a time, then the
+    tolerance of the oracle (the splits are merged G at a time, then the
     groups, so the rounding differs from the merge kernel's within a few fp32
     ulps), and the counters back at zero after every call."""
     fmt, G, qd, kvd = case
     Hkv = 2
-    # and one long sequence: 129 splits of 64 tokens, 33 workgroup partials
+    # and one long sequence: 129 splits of 64 tokens, 33 (G 4) or 17 (G 8) workgroup partials
     lens0 = [max(n - 3, 0) for n in LENS] + [8197]
     B = len(lens0)
     rng = np.random.default_rng(47)
