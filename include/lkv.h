@@ -230,7 +230,7 @@ int lkv_append_decode(const lkv_cache* cache, const lkv_view* view, const void* 
  * allocation); every completed call leaves them zero.  Calls that share
  * counters or a workspace must not overlap.  Formats and shapes: those for
  * which lkv_append_decode writes the new rows in the split kernel, with at
- * most 64 G splits per sequence (max_len <= 64 * G * split_tokens); otherwise
+ * most 256 G splits per sequence (max_len <= 256 * G * split_tokens); otherwise
  * LKV_EUNSUPPORTED and nothing is launched (lkv_append_decode serves every
  * case).  Workspace: lkv_decode_workspace_bytes(). */
 int lkv_append_decode_merged(const lkv_cache* cache, const lkv_view* view, const void* k_new, const void* v_new,

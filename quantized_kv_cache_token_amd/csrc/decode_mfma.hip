@@ -1445,6 +1445,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
 // Dispatch order as in split_append_kernel, by workgroup: the first half of
 // the grid takes the last ceil(nw / 2) workgroups of every row (which hold
 // the newest splits and the append), newest first, the second half the rest.
+constexpr int MERGED_MAX_PARTIALS = 256;  // workgroup partials per row the last workgroup merges
+
 template <int VB, int G>
 __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2))) void split_append_merged_kernel(
     MfmaArgs a)
@@ -1526,7 +1528,34 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2))) voi
     if (nw <= 8) merge_row(std::integral_constant<int, 8>{});
     else if (nw <= 16) merge_row(std::integral_constant<int, 16>{});
     else if (nw <= 32) merge_row(std::integral_constant<int, 32>{});
-    else merge_row(std::integral_constant<int, 64>{});
+    else if (nw <= 64) merge_row(std::integral_constant<int, 64>{});
+    else {  // more than 64 partials: chunks of 64, each merged unnormalised, folded into a running partial
+        const int h = w;
+        const float* p = prow0 + (int64_t)h * a.total_splits * (D + 2);
+        float Mr = -INFINITY, Lr = 0.0f;
+        float2 ar = {0.0f, 0.0f};
+        for (int c0 = 0; c0 < nw; c0 += 64) {
+            const int nc = min(64, nw - c0);
+            float2 ov[64];
+#pragma unroll
+            for (int i = 0; i < 64; i++) {  // past the chunk's count: a counted row again, at weight 0
+                const uint64_t v = __hip_atomic_load(
+                    (const uint64_t*)(p + (int64_t)(c0 + min(i, nc - 1)) * (D + 2) + 2 * lane), __ATOMIC_RELAXED,
+                    __HIP_MEMORY_SCOPE_AGENT);
+                ov[i] = float2{__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32))};
+            }
+            uint64_t ml = 0xFF800000ull;
+            if (lane < nc)
+                ml = __hip_atomic_load((const uint64_t*)(p + (int64_t)(c0 + lane) * (D + 2) + D), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            float Mc, Lc;
+            const float2 oc =
+                merge128_partial(ov, __uint_as_float((uint32_t)ml), __uint_as_float((uint32_t)(ml >> 32)), &Mc, &Lc);
+            fold_partial(Mr, Lr, ar, Mc, Lc, oc);
+        }
+        const float inv = Lr > 0.0f ? 1.0f / Lr : 0.0f;
+        *(float2*)(a.out + ((int64_t)b * a.num_q_heads + kvh * G + h) * D + 2 * lane) = float2{ar.x * inv, ar.y * inv};
+    }
 }
 
 // Whether a segment has a matrix-core kernel.
@@ -1632,7 +1661,8 @@ bool launch_append_decode_mfma(const SegArgs& s, const void* q, int q_dtype, int
         return false;
     const bool merge = counters != nullptr;
     const int G = num_q_heads / s.f.H;
-    if (merge && ((s.n_splits + G - 1) / G > 64 || total_splits != s.n_splits || !out)) return false;
+    if (merge && ((s.n_splits + G - 1) / G > MERGED_MAX_PARTIALS || total_splits != s.n_splits || !out))
+        return false;
     MfmaArgs a = mfma_args(s, q, num_q_heads, sm_scale, tau_low, split_tokens, total_splits, partials);
     a.k_new = k_new;
     a.v_new = v_new;

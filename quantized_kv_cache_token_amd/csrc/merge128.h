@@ -78,4 +78,20 @@ __device__ __forceinline__ float2 merge128_partial(const float2 (&ov)[CH], float
     return acc;
 }
 
+// Folds the partial (Mc, Lc, oc) into the running partial (Mr, Lr, ar) of
+// the same rows: M = max(Mr, Mc), each side weighted by 2^(its M - M).  A
+// side with M = -inf (no token) has weight 0.
+__device__ __forceinline__ void fold_partial(float& Mr, float& Lr, float2& ar, float Mc, float Lc, float2 oc)
+{
+#pragma clang fp contract(off)
+    const float M = fmaxf(Mr, Mc);
+    if (M == -INFINITY) return;
+    const float wr = Mr == -INFINITY ? 0.0f : exp2f(Mr - M);
+    const float wc = Mc == -INFINITY ? 0.0f : exp2f(Mc - M);
+    Lr = Lr * wr + Lc * wc;
+    ar.x = ar.x * wr + oc.x * wc;
+    ar.y = ar.y * wr + oc.y * wc;
+    Mr = M;
+}
+
 }  // namespace lkv

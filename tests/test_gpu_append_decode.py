@@ -158,9 +158,38 @@ def test_append_decode_merged_equals_append_decode(case, split):
         assert_attention_close(got.cpu().numpy(), ref, max_abs_vhat(a.ref), f"{case} split {split} step {s}")
 
 
-def test_append_decode_merged_rejects_more_than_256_splits():
+@pytest.mark.parametrize("G", [4, 8])
+def test_append_decode_merged_many_workgroup_partials(G):
+    """Rows with more than 64 workgroup partials (the last workgroup merges
+    them in chunks of 64): one step, pool bit-exact, output within tolerance
+    of the oracle, counters back at zero."""
+    fmt, Hkv, split = (128, 64, 6, 4), 2, 64
+    # 64 G + 1 and 130 G splits of 64 tokens (65 and 130 partials), and a short row
+    lens0 = [64 * G * 64 + 63, 130 * G * 64 - 1, 300]
+    B = len(lens0)
+    rng = np.random.default_rng(53)
+    bt, nblk = block_tables([n + 1 for n in lens0], rng)
+    a = Pair(*fmt, Hkv, nblk)
+    _prefill(a, lens0, Hkv, fmt[0], "bf16", 53, bt, outliers=True)
+    counters = lkv.merge_counters(a.gpu, B)
+    lens = [n + 1 for n in lens0]
+    view = lkv.View(torch.tensor(bt).cuda(), torch.tensor(lens, dtype=torch.int32).cuda(), max(lens))
+    k_new, v_new = inputs.kv_rows(54, 0, B, Hkv, fmt[0])
+    q = inputs.queries(55, B, Hkv * G, fmt[0]).cuda()
+    say("append_decode_merged many partials G", G, "lens", lens)
+    got = lkv.append_decode_merged(a.gpu, view, k_new.cuda(), v_new.cuda(), q, sm_scale(fmt[0]), 0.0, split, counters)
+    O.append(a.ref, to_f32_host(k_new), to_f32_host(v_new), np.arange(B + 1, dtype=np.int32), np.array(lens0, np.int32),
+             bt)
+    torch.cuda.synchronize()
+    assert a.pool_equal(), a.first_pool_mismatch()
+    assert int(counters.abs().sum()) == 0
+    ref = O.decode([a.ref], [bt], [np.array(lens, np.int32)], to_f32_host(q), sm_scale(fmt[0]), 0.0, split)
+    assert_attention_close(got.cpu().numpy(), ref, max_abs_vhat(a.ref), f"G {G}")
+
+
+def test_append_decode_merged_rejects_more_than_256_workgroup_partials():
     fmt, G, Hkv = (128, 64, 6, 4), 4, 2
-    lens = [256 * 64 + 1, 100]  # 257 splits of 64 tokens: 65 workgroups of 4
+    lens = [1024 * 64 + 1, 100]  # 1025 splits of 64 tokens: 257 workgroups of 4
     bt, nblk = block_tables(lens, np.random.default_rng(50))
     c = lkv.Cache(*fmt, Hkv, nblk)
     view = lkv.View(torch.tensor(bt).cuda(), torch.tensor(lens, dtype=torch.int32).cuda(), max(lens))

@@ -84,3 +84,37 @@ def test_noalloc_decode_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(other, want[:1])
         assert torch.equal(out, want), f"replay {r}"
+
+
+@pytest.mark.parametrize("G", [4, 8])
+def test_append_decode_merged_graph_replays_match_eager(G):
+    """The one-launch step (lkv_append_decode_merged) under capture: its
+    counters come back to zero at the end of every launch, so the graph needs
+    no clearing node; every replay equals the eager call bit for bit."""
+    fmt, D = (128, 64, 6, 4), 128
+    cache, view, k_new, v_new, q = _setup(fmt, G, [70, 1000, 2049, 64], 72)
+    B, Hq = q.shape[0], q.shape[1]
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        split = lkv.decode_plan([cache], [view], B, Hq)
+        ws = lkv.decode_workspace([cache], [view], B, Hq, split, q.device)
+        out = torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
+        counters = lkv.merge_counters(cache, B)
+        say("graph: eager append_decode_merged", G)
+        lkv.append_decode_merged(cache, view, k_new, v_new, q, sm_scale(D), 1e-4, split, counters, out, ws, stream)
+    torch.cuda.synchronize()
+    want_out, want_pool = out.clone(), cache.pool.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        lkv.append_decode_merged(cache, view, k_new, v_new, q, sm_scale(D), 1e-4, split, counters, out, ws, stream)
+    for r in range(4):
+        out.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device="cuda").sum()  # the program's own eager work between replays
+        torch.cuda.synchronize()
+        say("graph replay", r)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        assert torch.equal(out, want_out), f"replay {r}: output differs from the eager call"
+        assert torch.equal(cache.pool, want_pool), f"replay {r}: pool differs from the eager call"
+        assert int(counters.abs().sum()) == 0, f"replay {r}: counters not back at zero"
