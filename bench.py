@@ -8,11 +8,13 @@ sequence over the whole packed cache, then the merge of the split partials.
 With one segment and a uniform batch (workloads 2, 4) that is
 lkv_append_decode_merged, one launch: the split kernel writes each
 sequence's new row itself and merges the splits (--two-launch:
-lkv_append_decode, the split kernel then lkv_decode_combine).  The ragged
-workload 5 runs lkv_append_decode (its split kernel in compact order, then
-the merge kernel; --merged: one launch).  The tiered workload 3 (two
-segments), and every workload with --unfused, runs lkv_quant_append,
-lkv_decode_split and lkv_decode_combine.  Steps rotate over several layer caches so that
+lkv_append_decode, the split kernel then lkv_decode_combine).  The tiered
+workload 3 (two segments) is one launch too: lkv_append_decode_merged over
+both segments, the new row going to HIGH (--two-launch: lkv_quant_append,
+then lkv_decode_split and lkv_decode_combine).  The ragged workload 5 runs
+lkv_append_decode (its split kernel in compact order, then the merge
+kernel; --merged: one launch).  Every workload with --unfused runs
+lkv_quant_append, lkv_decode_split and lkv_decode_combine.  Steps rotate over several layer caches so that
 consecutive steps stream from HBM, not from the 256 MB last-level cache.
 
   workload 2 (default) and 4: every step re-appends the row of the last
@@ -84,8 +86,8 @@ def parse():
                         "merges its own splits) instead of the split kernel in compact order and the merge kernel, "
                         "which measured faster there; uniform batches (workloads 2 and 4) take one launch by default")
     p.add_argument("--two-launch", action="store_true",
-                   help="uniform batches: the split kernel, then the merge kernel (lkv_append_decode) instead of "
-                        "one launch that merges in the split kernel")
+                   help="uniform batches and the tiered workload: the split kernel, then the merge kernel "
+                        "instead of one launch that merges in the split kernel")
     p.add_argument("--unfused", action="store_true",
                    help="three launches per step: the append kernel, the split kernel, the merge")
     return p.parse_args()
@@ -415,17 +417,23 @@ def setup_tiered(args, wl, dev) -> Setup:
     ws = lkv.decode_workspace([segs[0][0], segs[0][1]], views0, B, Hq, split, dev)
     out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
     cu1 = torch.arange(B + 1, dtype=torch.int32, device=dev)
+    counters = lkv.merge_counters(segs[0][0], B, dev)
+    S.fused = S.merged = not args.two_launch and not args.unfused
     for layer, (h, m, nh, nm) in enumerate(segs):
         lv = [lkv.View(bt, nh, max_h), lkv.View(bt, nm, max_m)]
         last = (nh - 1).contiguous()
         k, v = inputs.kv_rows(wl.seed, 1000, B, Hkv, D, dtype=wl.dtype, outliers=outl, layer=layer, step=1,
                               device=dev)
         q = inputs.queries(wl.seed, B, Hq, D, dtype=wl.dtype, layer=layer, device=dev)
-        app = lkv.prepare_append(h, k, v, cu1, last, bt, 1)
-        spl, comb = lkv.prepare_decode([h, m], lv, q, sm, tl, split, out, ws)
-        S.calls.append((app, spl, comb))
+        if S.merged:  # one launch: append into HIGH, split over both segments, merge
+            S.calls.append((lkv.prepare_append_decode_merged([h, m], lv, k, v, q, sm, tl, split, out, counters,
+                                                             ws),))
+        else:
+            app = lkv.prepare_append(h, k, v, cu1, last, bt, 1)
+            spl, comb = lkv.prepare_decode([h, m], lv, q, sm, tl, split, out, ws)
+            S.calls.append((app, spl, comb))
         S.keep += [k, v, q, last, lv]
-    S.keep += [segs, bt, scores, views0, ws, out, cu1]
+    S.keep += [segs, bt, scores, views0, ws, out, cu1, counters]
     qb = 2 if wl.dtype == "bf16" else 4
     kv = int(Hkv * (int(nh_h.sum()) * 212 + int(nm_h.sum()) * 180))
     S.per_token_head, S.q_bytes = 212, qb
@@ -436,7 +444,8 @@ def setup_tiered(args, wl, dev) -> Setup:
     S.config = {"workload": wl.name, "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
                 "ctx_tokens": N, "high_tokens": int(nh_h[0]), "mid_tokens": int(nm_h[0]),
                 "group_size": wl.group_size, "segments": "K6V6 + K6V4", "tau_low": tl, "q_dtype": wl.dtype,
-                "split_tokens": split, "layers_rotated": args.layers, "append_in_split_kernel": False}
+                "split_tokens": split, "layers_rotated": args.layers, "append_in_split_kernel": S.fused,
+                "merge_in_split_kernel": S.merged}
     return S
 
 

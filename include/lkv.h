@@ -217,26 +217,34 @@ int lkv_append_decode(const lkv_cache* cache, const lkv_view* view, const void* 
                       float sm_scale, float tau_low, int32_t split_tokens, float* out, void* workspace,
                       size_t workspace_bytes, void* stream);
 
-/* lkv_append_decode in one launch: the split kernel also merges the split
+/* The decode step of a layer in one launch: the split kernel appends each
+ * sequence's new row, as lkv_append_decode does, and also merges the split
  * partials (the combine step of the split decode).  A workgroup of G waves
  * (G = query heads per KV head, 4 or 8) runs G consecutive splits of a
  * (sequence, KV head) and merges them in LDS; the last of a row's
  * workgroups to finish merges the row's workgroup partials into the output.
- * The pool is exactly lkv_append_decode's; the output is the same attention
- * merged in another order (G splits at a time, then the groups), so it may
- * differ from
- * lkv_append_decode's in the last bits.  counters: uint32 [batch][number of
- * KV heads], caller-owned, all zero before the first call (a zero-filled
- * allocation); every completed call leaves them zero.  Calls that share
- * counters or a workspace must not overlap.  Formats and shapes: those for
- * which lkv_append_decode writes the new rows in the split kernel, with at
- * most 256 G splits per sequence (max_len <= 256 * G * split_tokens); otherwise
- * LKV_EUNSUPPORTED and nothing is launched (lkv_append_decode serves every
- * case).  Workspace: lkv_decode_workspace_bytes(). */
-int lkv_append_decode_merged(const lkv_cache* cache, const lkv_view* view, const void* k_new, const void* v_new,
-                             int32_t kv_dtype, const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
-                             float sm_scale, float tau_low, int32_t split_tokens, float* out, uint32_t* counters,
-                             void* workspace, size_t workspace_bytes, void* stream);
+ * segs, views, nseg: one segment (the formats for which lkv_append_decode
+ * writes the new rows in the split kernel), or a tiered cache's two
+ * segments (Super KV Compression page, second layer): segs[0] HIGH (K6V6)
+ * and segs[1] MID (K6V4), head_dim 128, group 64, bf16 Q, 4 or 8 query
+ * heads per KV head, no direction-preserving K.  The new rows go to
+ * segs[0] at views[0].seq_lens[b] - 1, as lkv_quant_append would write
+ * them; attention reads every segment, with the sparse-V skip at tau_low.
+ * The pool is exactly that of lkv_quant_append then lkv_decode_attn; the
+ * output is the same attention merged in another order (G splits at a
+ * time, then the groups), so it may differ from theirs in the last bits.
+ * counters: uint32 [batch][number of KV heads], caller-owned, all zero
+ * before the first call (a zero-filled allocation); every completed call
+ * leaves them zero.  Calls that share counters or a workspace must not
+ * overlap.  At most 256 G splits per sequence over all segments; otherwise,
+ * or for another format or shape, LKV_EUNSUPPORTED and nothing is launched
+ * (lkv_append_decode, or lkv_quant_append then lkv_decode_attn, serves
+ * every case).  nseg other than 1 or 2: LKV_EINVAL.  Workspace:
+ * lkv_decode_workspace_bytes() of the same segments. */
+int lkv_append_decode_merged(const lkv_cache* segs, const lkv_view* views, int32_t nseg, const void* k_new,
+                             const void* v_new, int32_t kv_dtype, const void* q, int32_t q_dtype, int32_t batch,
+                             int32_t num_q_heads, float sm_scale, float tau_low, int32_t split_tokens, float* out,
+                             uint32_t* counters, void* workspace, size_t workspace_bytes, void* stream);
 
 /* The first stage of lkv_append_decode, for callers that schedule the two
  * apart (lkv_append_decode is exactly lkv_append_split followed by

@@ -494,28 +494,35 @@ int lkv_append_decode(const lkv_cache* cache, const lkv_view* view, const void* 
                               stream);
 }
 
-int lkv_append_decode_merged(const lkv_cache* cache, const lkv_view* view, const void* k_new, const void* v_new,
-                             int32_t kv_dtype, const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
-                             float sm_scale, float tau_low, int32_t split_tokens, float* out, uint32_t* counters,
-                             void* workspace, size_t workspace_bytes, void* stream)
+int lkv_append_decode_merged(const lkv_cache* segs, const lkv_view* views, int32_t nseg, const void* k_new,
+                             const void* v_new, int32_t kv_dtype, const void* q, int32_t q_dtype, int32_t batch,
+                             int32_t num_q_heads, float sm_scale, float tau_low, int32_t split_tokens, float* out,
+                             uint32_t* counters, void* workspace, size_t workspace_bytes, void* stream)
 {
+    if (nseg != 1 && nseg != 2) return LKV_EINVAL;
     if (split_tokens == 0) {
-        const int st = lkv_decode_plan(cache, view, 1, batch, num_q_heads, &split_tokens);
+        const int st = lkv_decode_plan(segs, views, nseg, batch, num_q_heads, &split_tokens);
         if (st != LKV_OK) return st;
     }
     Fmt f[2];
-    const int st = check_split(cache, view, 1, q, q_dtype, batch, num_q_heads, sm_scale, tau_low, split_tokens,
+    const int st = check_split(segs, views, nseg, q, q_dtype, batch, num_q_heads, sm_scale, tau_low, split_tokens,
                                workspace, workspace_bytes, f);
     if (st != LKV_OK) return st;
     if (kv_dtype != LKV_F32 && kv_dtype != LKV_BF16 && kv_dtype != LKV_F16) return LKV_EINVAL;
     if (batch == 0) return LKV_OK;
     if (!k_new || !v_new || !out || !counters || (uintptr_t)counters % 4 != 0) return LKV_EINVAL;
     SegArgs a[2];
-    const int32_t tot = seg_args(cache, view, 1, f, split_tokens, nullptr, 0, 1, nullptr, 0, a);
+    const int32_t tot = seg_args(segs, views, nseg, f, split_tokens, nullptr, 0, 1, nullptr, 0, a);
     hipError_t e;
-    if (!launch_append_decode_mfma(a[0], q, q_dtype, batch, num_q_heads, sm_scale, tau_low, split_tokens, tot,
-                                   (float*)workspace, k_new, v_new, kv_dtype, (hipStream_t)stream, &e, out, counters))
-        return LKV_EUNSUPPORTED;
+    const bool ok = nseg == 1
+                        ? launch_append_decode_mfma(a[0], q, q_dtype, batch, num_q_heads, sm_scale, tau_low,
+                                                    split_tokens, tot, (float*)workspace, k_new, v_new, kv_dtype,
+                                                    (hipStream_t)stream, &e, out, counters)
+                        : launch_append_decode_tiered_merged(a[0], a[1], q, q_dtype, batch, num_q_heads, sm_scale,
+                                                             tau_low, split_tokens, tot, (float*)workspace, k_new,
+                                                             v_new, kv_dtype, (hipStream_t)stream, &e, out,
+                                                             counters);
+    if (!ok) return LKV_EUNSUPPORTED;
     return e == hipSuccess ? LKV_OK : LKV_EHIP;
 }
 

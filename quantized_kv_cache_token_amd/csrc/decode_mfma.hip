@@ -1447,9 +1447,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
 // the newest splits and the append), newest first, the second half the rest.
 constexpr int MERGED_MAX_PARTIALS = 256;  // workgroup partials per row the last workgroup merges
 
-template <int VB, int G>
+//
+// TIER: a tiered cache's two segments, HIGH (a, K6V6, which takes the new
+// rows) and MID (a1, K6V4): a row's splits are HIGH's then MID's, so a
+// workgroup may hold splits of both.
+template <int VB, int G, bool TIER>
 __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2))) void split_append_merged_kernel(
-    MfmaArgs a)
+    MfmaArgs a, MfmaArgs a1)
 {
     constexpr int D = 128, MW = G;
     __shared__ uint4 meta_lds[MW][META_BYTES / 16];
@@ -1458,7 +1462,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2))) voi
     // the wave index is uniform: read it into a scalar register, so that the
     // split and everything addressed from it stay scalar in split_body
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int ns = a.seg.n_splits, H = a.seg.f.H;
+    const int ns0 = a.seg.n_splits, ns = ns0 + (TIER ? a1.seg.n_splits : 0), H = a.seg.f.H;
     const int nw = (ns + MW - 1) / MW;  // workgroups (merged partials) per row
     const int P = (nw + 1) / 2;         // workgroups per row in the first half
     const int rows = (int)gridDim.x / nw;
@@ -1473,8 +1477,10 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2))) voi
     }
     const int j = nw - 1 - rev;
     const int sp = j * MW + w, b = row / H, kvh = row % H;
-    if (sp < ns) {
+    if (sp < ns0) {
         split_body<VB, G, false, false, false, true, true>(a, sp, kvh, b, lane, meta_lds[w], &part[w][0][0]);
+    } else if (TIER && sp < ns) {
+        split_body<4, G, false, false, false, false, true>(a1, sp - ns0, kvh, b, lane, meta_lds[w], &part[w][0][0]);
     } else if (lane < G) {  // past the row's last split: no token
         part[w][lane][D] = -INFINITY;
         part[w][lane][D + 1] = 0.0f;
@@ -1672,11 +1678,11 @@ bool launch_append_decode_mfma(const SegArgs& s, const void* q, int q_dtype, int
     a.compact = !merge && ragged && batch <= 64 ? batch : 0;
     if (merge) {  // every (workgroup of G splits, KV head, entry), in the order above
         const dim3 grid((unsigned)((s.n_splits + G - 1) / G * s.f.H * batch));
-        auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(64 * G), 0, stream, a); };
-        if (s.f.vb == 4 && G == 4) go(split_append_merged_kernel<4, 4>);
-        else if (s.f.vb == 4) go(split_append_merged_kernel<4, 8>);
-        else if (G == 4) go(split_append_merged_kernel<6, 4>);
-        else go(split_append_merged_kernel<6, 8>);
+        auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(64 * G), 0, stream, a, a); };
+        if (s.f.vb == 4 && G == 4) go(split_append_merged_kernel<4, 4, false>);
+        else if (s.f.vb == 4) go(split_append_merged_kernel<4, 8, false>);
+        else if (G == 4) go(split_append_merged_kernel<6, 4, false>);
+        else go(split_append_merged_kernel<6, 8, false>);
     } else {  // every (split, KV head, entry), in the order above (compact: every item fits, whatever the lengths)
         const dim3 grid((unsigned)(s.n_splits * s.f.H * batch));
         auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(64), 0, stream, a); };
@@ -1685,6 +1691,41 @@ bool launch_append_decode_mfma(const SegArgs& s, const void* q, int q_dtype, int
         else if (G == 4) go(split_append_kernel<6, 4>);
         else go(split_append_kernel<6, 8>);
     }
+    *err = hipGetLastError();
+    return true;
+}
+
+// The decode step of a tiered cache in one launch: HIGH (K6V6) takes the
+// new rows, HIGH and MID (K6V4) are read, the splits are merged in the
+// kernel.  false when the pair or the shape has no such kernel.
+bool launch_append_decode_tiered_merged(const SegArgs& high, const SegArgs& mid, const void* q, int q_dtype,
+                                        int32_t batch, int32_t num_q_heads, float sm_scale, float tau_low,
+                                        int32_t split_tokens, int32_t total_splits, float* partials,
+                                        const void* k_new, const void* v_new, int kv_dtype, hipStream_t stream,
+                                        hipError_t* err, float* out, uint32_t* counters)
+{
+    const uintptr_t align = kv_dtype == LKV_F32 ? 8 : 4;  // a lane reads its two channels at once
+    const int G = num_q_heads / high.f.H;
+    if (high.f.vb != 6 || mid.f.vb != 4 || high.f.H != mid.f.H || high.f.k_norm || mid.f.k_norm ||
+        !mfma_ok(high, q, q_dtype, num_q_heads, sm_scale, split_tokens) ||
+        !mfma_ok(mid, q, q_dtype, num_q_heads, sm_scale, split_tokens) || high.q_per_seq != 1 ||
+        mid.q_per_seq != 1 || high.skip_mask != nullptr || high.scores != nullptr || mid.skip_mask != nullptr ||
+        mid.scores != nullptr || (uintptr_t)k_new % align != 0 || (uintptr_t)v_new % align != 0 || !out ||
+        !counters || total_splits != high.n_splits + mid.n_splits ||
+        (total_splits + G - 1) / G > MERGED_MAX_PARTIALS)
+        return false;
+    *err = hipSuccess;
+    if (batch == 0) return true;
+    MfmaArgs a0 = mfma_args(high, q, num_q_heads, sm_scale, tau_low, split_tokens, total_splits, partials);
+    MfmaArgs a1 = mfma_args(mid, q, num_q_heads, sm_scale, tau_low, split_tokens, total_splits, partials);
+    a0.k_new = k_new;
+    a0.v_new = v_new;
+    a0.kv_dtype = kv_dtype;
+    a0.counters = a1.counters = counters;
+    a0.out = a1.out = out;
+    const dim3 grid((unsigned)((total_splits + G - 1) / G * high.f.H * batch));
+    if (G == 4) hipLaunchKernelGGL((split_append_merged_kernel<6, 4, true>), grid, dim3(256), 0, stream, a0, a1);
+    else hipLaunchKernelGGL((split_append_merged_kernel<6, 8, true>), grid, dim3(512), 0, stream, a0, a1);
     *err = hipGetLastError();
     return true;
 }

@@ -87,6 +87,15 @@ bool launch_append_decode_mfma(const SegArgs& s, const void* q, int q_dtype, int
                                hipStream_t stream, hipError_t* err, float* out = nullptr,
                                uint32_t* counters = nullptr, bool ragged = false);
 
+// The one-launch decode step of a tiered cache: HIGH (K6V6) takes the new
+// rows, both segments are read and the splits merged in the kernel; false
+// when the pair or the shape has no such kernel.
+bool launch_append_decode_tiered_merged(const SegArgs& high, const SegArgs& mid, const void* q, int q_dtype,
+                                        int32_t batch, int32_t num_q_heads, float sm_scale, float tau_low,
+                                        int32_t split_tokens, int32_t total_splits, float* partials,
+                                        const void* k_new, const void* v_new, int kv_dtype, hipStream_t stream,
+                                        hipError_t* err, float* out, uint32_t* counters);
+
 // Partials: fp32 [batch][Hq][total_splits][D + 2] = (o[D], m, L).
 hipError_t launch_decode_split(const SegArgs& s, const void* q, int q_dtype, int32_t batch,
                                int32_t num_q_heads, float sm_scale, float tau_low,

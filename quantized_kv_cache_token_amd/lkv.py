@@ -84,8 +84,8 @@ def lib():
         "lkv_decode_plan_multi": ([PC, PV, I32, I32, I32, I32, C.POINTER(I32)], C.c_int),
         "lkv_append_decode": ([PC, PV, P, P, I32, P, I32, I32, I32, F, F, I32, P, P, C.c_size_t, V], C.c_int),
         "lkv_append_split": ([PC, PV, P, P, I32, P, I32, I32, I32, F, F, I32, P, C.c_size_t, V], C.c_int),
-        "lkv_append_decode_merged": ([PC, PV, P, P, I32, P, I32, I32, I32, F, F, I32, P, P, P, C.c_size_t, V],
-                                     C.c_int),
+        "lkv_append_decode_merged": ([PC, PV, I32, P, P, I32, P, I32, I32, I32, F, F, I32, P, P, P, C.c_size_t,
+                                      V], C.c_int),
         "lkv_decode_attn_noalloc": ([PC, PV, I32, P, I32, I32, I32, F, F, I32, P, V], C.c_int),
         "lkv_hbm_read_probe": ([P, I64, I32, P, V], C.c_int),
         "lkv_decode_attn_debug": ([PC, PV, I32, P, I32, I32, I32, I32, F, F, I32, P, P, I32, P, C.c_size_t, V],
@@ -529,35 +529,47 @@ def merge_counters(cache: Cache, batch: int, device="cuda") -> torch.Tensor:
     return torch.zeros(batch * cache.num_kv_heads, dtype=torch.int32, device=device)
 
 
-def append_decode_merged(cache: Cache, view: View, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+def _seg_list(cache, view):
+    """A cache and its view, or lists of them (a tiered cache's segments)."""
+    caches = list(cache) if isinstance(cache, (list, tuple)) else [cache]
+    views = list(view) if isinstance(view, (list, tuple)) else [view]
+    return caches, views
+
+
+def append_decode_merged(cache, view, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
                          sm_scale: float, tau_low: float, split_tokens: int, counters: torch.Tensor,
                          out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
-    """lkv_append_decode_merged: lkv_append_decode in one launch (the split
-    kernel merges its own splits); counters from merge_counters()."""
+    """lkv_append_decode_merged: the decode step in one launch (the split
+    kernel appends the new rows and merges its own splits); counters from
+    merge_counters().  cache and view: one segment, or the lists [HIGH, MID]
+    of a tiered cache (the new rows go to HIGH)."""
+    caches, views = _seg_list(cache, view)
     B, Hq, D = q.shape
     _require(q.is_contiguous() and k_new.is_contiguous() and v_new.is_contiguous() and k_new.dtype == v_new.dtype,
              "q, k_new, v_new contiguous; k_new and v_new of one dtype")
-    _require(counters.dtype == torch.int32 and counters.numel() >= B * cache.num_kv_heads and counters.is_cuda,
+    _require(counters.dtype == torch.int32 and counters.numel() >= B * caches[0].num_kv_heads and counters.is_cuda,
              "counters: int32 [batch * KV heads] on the device")
     with _on(stream):
         if workspace is None:
-            workspace = decode_workspace([cache], [view], B, Hq, split_tokens, q.device)
+            workspace = decode_workspace(caches, views, B, Hq, split_tokens, q.device)
         if out is None:
             out = torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
-    cs, vs, _ = _segs([cache], [view])
+    cs, vs, n = _segs(caches, views)
     _check("lkv_append_decode_merged", lib().lkv_append_decode_merged(
-        cs, vs, _ptr(k_new), _ptr(v_new), _DTYPE[k_new.dtype], _ptr(q), _DTYPE[q.dtype], B, Hq, sm_scale, tau_low,
-        split_tokens, _ptr(out), _ptr(counters), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        cs, vs, n, _ptr(k_new), _ptr(v_new), _DTYPE[k_new.dtype], _ptr(q), _DTYPE[q.dtype], B, Hq, sm_scale,
+        tau_low, split_tokens, _ptr(out), _ptr(counters), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
     return out
 
 
-def prepare_append_decode_merged(cache: Cache, view: View, k_new, v_new, q, sm_scale: float, tau_low: float,
+def prepare_append_decode_merged(cache, view, k_new, v_new, q, sm_scale: float, tau_low: float,
                                  split_tokens: int, out, counters, workspace, stream=None) -> Prepared:
-    """lkv_append_decode_merged as a prepared call."""
+    """lkv_append_decode_merged as a prepared call (cache and view as in
+    append_decode_merged)."""
+    caches, views = _seg_list(cache, view)
     B, Hq, _ = q.shape
-    cs, vs, _ = _segs([cache], [view])
-    call = Prepared("lkv_append_decode_merged", cs, vs, _ptr(k_new), _ptr(v_new), _DTYPE[k_new.dtype], _ptr(q),
+    cs, vs, n = _segs(caches, views)
+    call = Prepared("lkv_append_decode_merged", cs, vs, n, _ptr(k_new), _ptr(v_new), _DTYPE[k_new.dtype], _ptr(q),
                     _DTYPE[q.dtype], B, Hq, sm_scale, tau_low, split_tokens, _ptr(out), _ptr(counters),
                     _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     call._keep = (cs, vs)

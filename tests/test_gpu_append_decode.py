@@ -283,3 +283,73 @@ def test_seeded_random_ragged_steps():
             assert pair.pool_equal(), (what, pair.first_pool_mismatch())
             ref = O.decode([pair.ref], [bt], [np.array(lens, np.int32)], to_f32_host(q), sm, 0.0, split)
             assert_attention_close(got.cpu().numpy(), ref, max_abs_vhat(pair.ref), what)
+
+
+@pytest.mark.parametrize("G", [4, 8])
+@pytest.mark.parametrize("tau,split", [(0.0, 64), (1e-4, 256)])
+def test_append_decode_merged_tiered_segments(G, tau, split):
+    """The one-launch step over a tiered cache: HIGH (K6V6) takes the new
+    rows, HIGH and MID (K6V4) are read, the splits merged in the kernel.
+    Ragged lengths, a sequence with no HIGH token (nothing appended), one
+    whose only HIGH token is the new one and whose MID is empty.  Both pools
+    bit-exact with the oracle's append, the output within tolerance of the
+    oracle's decode over both segments (skip decisions resolved through the
+    debug entry point) and within 1e-5 max|v_hat| of lkv_decode_attn over
+    the same pools, the counters back at zero."""
+    from tests.gpu_common import resolved_reference
+
+    D, g, Hkv = 128, 64, 2
+    rng = np.random.default_rng(61)
+    lens_h = [0, 131, 701, 65, 1]  # after the new row
+    lens_m = [900, 1, 2100, 65, 0]
+    B = len(lens_h)
+    pairs, views, bts = [], [], []
+    for vb, lens, pre, seed in ((6, lens_h, [max(n - 1, 0) for n in lens_h], 62), (4, lens_m, lens_m, 63)):
+        bt, nblk = block_tables([max(n, 1) for n in lens], rng)
+        pair = Pair(D, g, 6, vb, Hkv, nblk)
+        _prefill(pair, pre, Hkv, D, "bf16", seed, bt, outliers=True)
+        pairs.append(pair)
+        bts.append(bt)
+        views.append(lkv.View(torch.tensor(bt).cuda(), torch.tensor(lens, dtype=torch.int32).cuda(), max(max(lens), 1)))
+    k_new, v_new = inputs.kv_rows(64, 0, B, Hkv, D)
+    q = inputs.queries(65, B, Hkv * G, D).cuda()
+    counters = lkv.merge_counters(pairs[0].gpu, B)
+    say("append_decode_merged tiered G", G, "tau", tau, "split", split)
+    got = lkv.append_decode_merged([p.gpu for p in pairs], views, k_new.cuda(), v_new.cuda(), q, sm_scale(D), tau,
+                                   split, counters)
+    again, mask = lkv.decode_attn_debug([p.gpu for p in pairs], views, q, sm_scale(D), tau, split)
+    live = [b for b in range(B) if lens_h[b] > 0]
+    O.append(pairs[0].ref, to_f32_host(k_new[live]), to_f32_host(v_new[live]), np.arange(len(live) + 1, dtype=np.int32),
+             np.array([lens_h[b] - 1 for b in live], np.int32), bts[0][live])
+    torch.cuda.synchronize()
+    assert pairs[0].pool_equal(), pairs[0].first_pool_mismatch()
+    assert pairs[1].pool_equal(), pairs[1].first_pool_mismatch()
+    assert int(counters.abs().sum()) == 0
+    vmax = max(max_abs_vhat(p.ref) for p in pairs)
+    assert float((got - again).abs().max()) <= 1e-5 * vmax
+    want, _ = resolved_reference([p.ref for p in pairs], bts, [np.array(lens_h, np.int32), np.array(lens_m, np.int32)],
+                                 to_f32_host(q), sm_scale(D), tau, split, mask, [v.max_len for v in views],
+                                 f"tiered G {G}")
+    assert_attention_close(got.cpu().numpy(), want, vmax, f"tiered G {G} tau {tau}")
+
+
+def test_append_decode_merged_rejects_other_segment_pairs():
+    """Two segments must be {K6V6, K6V4}: another pair is LKV_EUNSUPPORTED
+    with nothing launched; three segments are LKV_EINVAL."""
+    D, g, Hkv, G = 128, 64, 2, 4
+    lens = [100, 300]
+    bt, nblk = block_tables(lens, np.random.default_rng(66))
+    a, b = lkv.Cache(D, g, 6, 4, Hkv, nblk), lkv.Cache(D, g, 6, 4, Hkv, nblk)
+    view = lkv.View(torch.tensor(bt).cuda(), torch.tensor(lens, dtype=torch.int32).cuda(), max(lens))
+    k_new, v_new = inputs.kv_rows(67, 0, 2, Hkv, D)
+    q = inputs.queries(68, 2, Hkv * G, D).cuda()
+    counters = lkv.merge_counters(a, 2)
+    with pytest.raises(lkv.LkvError) as e:
+        lkv.append_decode_merged([a, b], [view, view], k_new.cuda(), v_new.cuda(), q, sm_scale(D), 0.0, 64, counters)
+    assert e.value.status == lkv.EUNSUPPORTED
+    with pytest.raises(lkv.LkvError) as e:
+        lkv.append_decode_merged([a, b, a], [view, view, view], k_new.cuda(), v_new.cuda(), q, sm_scale(D), 0.0, 64,
+                                 counters)
+    assert e.value.status == lkv.EINVAL
+    torch.cuda.synchronize()
+    assert int(counters.abs().sum()) == 0 and not a.pool.any() and not b.pool.any()
