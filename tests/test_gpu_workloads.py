@@ -156,6 +156,15 @@ def test_workload3_tiered():
                ht2, mt2)
     torch.cuda.synchronize()
     nh2_h, nm2_h, ht2_h, mt2_h = nh2.cpu().numpy(), nm2.cpu().numpy(), ht2.cpu().numpy(), mt2.cpu().numpy()
+    # the benchmark's step: one launch that appends a row into HIGH (here a copy) and decodes both segments
+    hcopy = lkv.Cache(D, wl.group_size, 6, 6, Hkv, B * nb, pool=hdst.pool.clone())
+    views1 = [lkv.View(hbt.cuda(), (nh + 1).contiguous(), int(nh_h.max()) + 1), views[1]]
+    split1 = lkv.decode_plan([hcopy, mdst], views1, B, Hq)
+    kn, vn = inputs.kv_rows(wl.seed, 1000, B, Hkv, D, outliers=inputs.outlier_channels(wl.seed, Hkv, D), step=1)
+    say("workload 3 one-launch step, split", split1)
+    out1 = lkv.append_decode_merged([hcopy, mdst], views1, kn.cuda(), vn.cuda(), q.cuda(), sm_scale(D), tl, split1,
+                                    lkv.merge_counters(hcopy, B)).cpu().numpy()
+    torch.cuda.synchronize()
     for b in range(B):
         say("workload 3 oracle, sequence", b)
         ref = O.Cache(D, wl.group_size, 6, 6, Hkv, nb)
@@ -170,6 +179,13 @@ def test_workload3_tiered():
         _chunks_equal(mdst.pool, hbt[b].numpy(), rm, rbt[0], int(nm_h[b]), Hkv)
         want = O.decode([rh, rm], [rbt, rbt], [nh_ref, nm_ref], q[b:b + 1].float().numpy(), sm_scale(D), tl, split)
         assert_attention_close(out[b:b + 1], want, max(max_abs_vhat(rh), max_abs_vhat(rm)), f"workload 3 seq {b}")
+        rh1 = O.Cache(D, wl.group_size, 6, 6, Hkv, nb, pool=rh.pool.copy())
+        O.append(rh1, kn[b:b + 1].float().numpy(), vn[b:b + 1].float().numpy(), [0, 1], [int(nh_ref[0])], rbt)
+        _chunks_equal(hcopy.pool, hbt[b].numpy(), rh1, rbt[0], int(nh_h[b]) + 1, Hkv)
+        want1 = O.decode([rh1, rm], [rbt, rbt], [nh_ref + 1, nm_ref], q[b:b + 1].float().numpy(), sm_scale(D), tl,
+                         split1)
+        assert_attention_close(out1[b:b + 1], want1, max(max_abs_vhat(rh1), max_abs_vhat(rm)),
+                               f"workload 3 seq {b}, one-launch step")
         say("workload 3 oracle retier, sequence", b)
         rh2, rm2 = O.Cache(D, wl.group_size, 6, 6, Hkv, nb), O.Cache(D, wl.group_size, 6, 4, Hkv, nb)
         # the oracle's scores drawn from its own counts (the GPU's drew the same from equal counts)
