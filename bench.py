@@ -12,9 +12,10 @@ lkv_append_decode, the split kernel then lkv_decode_combine).  The tiered
 workload 3 (two segments) is one launch too: lkv_append_decode_merged over
 both segments, the new row going to HIGH (--two-launch: lkv_quant_append,
 then lkv_decode_split and lkv_decode_combine).  The ragged workload 5 runs
-lkv_append_decode (its split kernel in compact order, then the merge
-kernel; --merged: one launch).  Every workload with --unfused runs
-lkv_quant_append, lkv_decode_split and lkv_decode_combine.  Steps rotate over several layer caches so that
+lkv_append_decode_merged in compact order (--two-launch: lkv_append_decode,
+its split kernel in compact order, then the merge kernel).  Every workload
+with --unfused runs lkv_quant_append, lkv_decode_split and
+lkv_decode_combine.  Steps rotate over several layer caches so that
 consecutive steps stream from HBM, not from the 256 MB last-level cache.
 
   workload 2 (default) and 4: every step re-appends the row of the last
@@ -81,13 +82,9 @@ def parse():
                    help="only the HBM read probe (a streaming read of 4 GiB; profiling)")
     p.add_argument("--tier-only", action="store_true",
                    help="only the tier-update and re-tier figures at the tiered workload's shape (profiling)")
-    p.add_argument("--merged", action="store_true",
-                   help="ragged workload: one launch per step (lkv_append_decode_merged, the split kernel also "
-                        "merges its own splits) instead of the split kernel in compact order and the merge kernel, "
-                        "which measured faster there; uniform batches (workloads 2 and 4) take one launch by default")
     p.add_argument("--two-launch", action="store_true",
-                   help="uniform batches and the tiered workload: the split kernel, then the merge kernel "
-                        "instead of one launch that merges in the split kernel")
+                   help="the split kernel, then the merge kernel, instead of one launch that merges in the split "
+                        "kernel (workloads 2 to 5)")
     p.add_argument("--unfused", action="store_true",
                    help="three launches per step: the append kernel, the split kernel, the merge")
     return p.parse_args()
@@ -513,7 +510,7 @@ def setup_ragged(args, wl, dev) -> Setup:
             k, v = kvs[layer]
             if S.fused:  # the new row of sequence b is position len_b + s: the step's lengths count it
                 S.calls.append(fused_step(args, S, caches[layer], views[s], k, v, qs[layer], sm, split, out, ws,
-                                          counters, args.merged))
+                                          counters, not args.two_launch))
             else:
                 app = lkv.prepare_append(caches[layer], k, v, cu1, pos[s], bt, 1)
                 spl, comb = lkv.prepare_decode([caches[layer]], [views[s]], qs[layer], sm, 0.0, split, out, ws)

@@ -230,7 +230,11 @@ int lkv_append_decode(const lkv_cache* cache, const lkv_view* view, const void* 
  * heads per KV head, no direction-preserving K.  The new rows go to
  * segs[0] at views[0].seq_lens[b] - 1, as lkv_quant_append would write
  * them; attention reads every segment, with the sparse-V skip at tau_low.
- * The pool is exactly that of lkv_quant_append then lkv_decode_attn; the
+ * One segment whose view marks a ragged batch (sum_len below batch x
+ * max_len) of at most 64 sequences runs in the compact order of
+ * lkv_append_decode (every wave a split with tokens; lkv_decode_plan_lens
+ * sizes the splits), its workgroups merging the runs of consecutive splits
+ * they hold.  The pool is exactly that of lkv_quant_append then lkv_decode_attn; the
  * output is the same attention merged in another order (G splits at a
  * time, then the groups), so it may differ from theirs in the last bits.
  * counters: uint32 [batch][number of KV heads], caller-owned, all zero

@@ -517,7 +517,8 @@ int lkv_append_decode_merged(const lkv_cache* segs, const lkv_view* views, int32
     const bool ok = nseg == 1
                         ? launch_append_decode_mfma(a[0], q, q_dtype, batch, num_q_heads, sm_scale, tau_low,
                                                     split_tokens, tot, (float*)workspace, k_new, v_new, kv_dtype,
-                                                    (hipStream_t)stream, &e, out, counters)
+                                                    (hipStream_t)stream, &e, out, counters,
+                                                    ragged_hint(&views[0], batch))
                         : launch_append_decode_tiered_merged(a[0], a[1], q, q_dtype, batch, num_q_heads, sm_scale,
                                                              tau_low, split_tokens, tot, (float*)workspace, k_new,
                                                              v_new, kv_dtype, (hipStream_t)stream, &e, out,

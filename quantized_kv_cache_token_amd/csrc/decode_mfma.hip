@@ -1374,7 +1374,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
 __device__ __forceinline__ bool compact_item(const MfmaArgs& a, int lin, int& sp, int& row, int& nsp)
 {
     const SegArgs& sg = a.seg;
-    const int lane = threadIdx.x, H = sg.f.H, st = a.split_tokens;
+    const int lane = threadIdx.x & 63, H = sg.f.H, st = a.split_tokens;
     int c = 0;
     if (lane < a.compact) c = max(1, min(sg.n_splits, (max(0, min(sg.seq_lens[lane], sg.len_cap)) + st - 1) / st));
     int x = H * c;  // inclusive prefix sum of the entries' items
@@ -1564,6 +1564,130 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2))) voi
     }
 }
 
+// The one-launch step of a ragged batch (at most 64 sequences) in compact
+// order: workgroup i's G waves take items G i .. G i + G - 1 of the compact
+// order of split_append_kernel, so every wave slot holds a split with
+// tokens.  The waves of a workgroup that share a row (KV head, entry) form
+// a run of consecutive splits; each run is merged in LDS into one partial,
+// written through to the workspace at the slot of its first split, and
+// counted in the row's counter.  A row's runs are known from where its items
+// start: a run begins at its split 0 and wherever an item index is a
+// multiple of G.  The workgroup that counts a row's last run merges that
+// row's run partials into the output.
+template <int VB, int G>
+__global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2))) void split_append_merged_compact_kernel(
+    MfmaArgs a)
+{
+    constexpr int D = 128;
+    __shared__ uint4 meta_lds[G][META_BYTES / 16];
+    __shared__ float part[G][G][D + 2];
+    __shared__ int wrow[G], wsp[G], wnsp[G], wbase[G];
+    __shared__ uint32_t ticket[G];
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int H = a.seg.f.H;
+    // a row's runs: split 0, then every split whose item index is a multiple of G
+    auto first_split = [](int base) { return G - base % G; };  // the second run's first split
+    auto runs_of = [&](int base, int ns) {
+        const int s1 = first_split(base);
+        return s1 >= ns ? 1 : 2 + (ns - 1 - s1) / G;
+    };
+    {
+        int sp, row, nsp;
+        if (!compact_item(a, blockIdx.x * G, sp, row, nsp)) return;  // the whole group is past the last item
+        const int lin = blockIdx.x * G + w;
+        const bool has = compact_item(a, lin, sp, row, nsp);
+        if (has) {
+            split_body<VB, G, false, false, false, true, true>(a, sp, row % H, row / H, lane, meta_lds[w],
+                                                                 &part[w][0][0]);
+        } else if (lane < G) {  // past the last item
+            part[w][lane][D] = -INFINITY;
+            part[w][lane][D + 1] = 0.0f;
+        }
+        if (lane == 0) {
+            wrow[w] = has ? row : -1;
+            wsp[w] = sp;
+            wnsp[w] = nsp;
+            wbase[w] = lin - sp;  // the row's first item
+        }
+        __syncthreads();
+        // runs: wave r starts one when its row differs from wave r - 1's; wave
+        // w merges head w of every run
+        for (int r = 0; r < G; r++) {
+            const int rr = wrow[r];
+            if (rr < 0 || (r > 0 && wrow[r - 1] == rr)) continue;
+            int e = r + 1;
+            while (e < G && wrow[e] == rr) e++;
+            const int n = e - r, h = w;
+            float2 ov[G];
+#pragma unroll
+            for (int i = 0; i < G; i++) ov[i] = *(const float2*)&part[min(r + i, e - 1)][h][2 * lane];
+            const float mi = lane < n ? part[r + lane][h][D] : -INFINITY;
+            const float li = lane < n ? part[r + lane][h][D + 1] : 0.0f;
+            float M, L;
+            const float2 o = merge128_partial(ov, mi, li, &M, &L);
+            float* p = a.partials +
+                       (((int64_t)(rr / H) * a.num_q_heads + (rr % H) * G + h) * a.total_splits + wsp[r]) * (D + 2);
+            const uint64_t ob = (uint64_t)__float_as_uint(o.x) | ((uint64_t)__float_as_uint(o.y) << 32);
+            __hip_atomic_store((uint64_t*)(p + 2 * lane), ob, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane == 0) {
+                const uint64_t ml = (uint64_t)__float_as_uint(M) | ((uint64_t)__float_as_uint(L) << 32);
+                __hip_atomic_store((uint64_t*)(p + D), ml, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are complete
+        __syncthreads();                                  // ... and every wave's
+        if (lane == 0) {
+            const int rr = wrow[w];
+            uint32_t t = 0xFFFFFFFFu;
+            if (rr >= 0 && (w == 0 || wrow[w - 1] != rr)) {
+                const unsigned last = (unsigned)(runs_of(wbase[w], wnsp[w]) - 1);
+                t = atomicInc(a.counters + rr, last) == last ? 1u : 0u;
+            }
+            ticket[w] = t;
+        }
+        __syncthreads();
+        // rows whose last run this workgroup counted: wave w merges head w of
+        // the row's run partials
+        for (int r = 0; r < G; r++) {
+            if (ticket[r] != 1u) continue;
+            const int rr = wrow[r], nr = runs_of(wbase[r], wnsp[r]), s1 = first_split(wbase[r]), h = w;
+            const float* p =
+                a.partials + ((int64_t)(rr / H) * a.num_q_heads + (rr % H) * G + h) * a.total_splits * (D + 2);
+            auto slot = [&](int j) { return j == 0 ? 0 : s1 + (j - 1) * G; };
+            float Mr = -INFINITY, Lr = 0.0f;
+            float2 ar = {0.0f, 0.0f};
+            auto merge_runs = [&](auto ch) __attribute__((always_inline)) {
+                constexpr int CH = decltype(ch)::value;
+                for (int c0 = 0; c0 < nr; c0 += CH) {
+                    const int nc = min(CH, nr - c0);
+                    float2 ov[CH];
+#pragma unroll
+                    for (int i = 0; i < CH; i++) {  // past the count: a counted partial again, at weight 0
+                        const uint64_t v = __hip_atomic_load(
+                            (const uint64_t*)(p + (int64_t)slot(c0 + min(i, nc - 1)) * (D + 2) + 2 * lane),
+                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        ov[i] = float2{__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32))};
+                    }
+                    uint64_t ml = 0xFF800000ull;
+                    if (lane < nc)
+                        ml = __hip_atomic_load((const uint64_t*)(p + (int64_t)slot(c0 + lane) * (D + 2) + D),
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    float Mc, Lc;
+                    const float2 oc = merge128_partial(ov, __uint_as_float((uint32_t)ml),
+                                                       __uint_as_float((uint32_t)(ml >> 32)), &Mc, &Lc);
+                    fold_partial(Mr, Lr, ar, Mc, Lc, oc);
+                }
+            };
+            if (nr <= 8) merge_runs(std::integral_constant<int, 8>{});
+            else if (nr <= 16) merge_runs(std::integral_constant<int, 16>{});
+            else merge_runs(std::integral_constant<int, 64>{});
+            const float inv = Lr > 0.0f ? 1.0f / Lr : 0.0f;
+            *(float2*)(a.out + ((int64_t)(rr / H) * a.num_q_heads + (rr % H) * G + h) * D + 2 * lane) =
+                float2{ar.x * inv, ar.y * inv};
+        }
+    }
+}
+
 // Whether a segment has a matrix-core kernel.
 static bool mfma_ok(const SegArgs& s, const void* q, int q_dtype, int32_t num_q_heads, float sm_scale,
                     int32_t split_tokens)
@@ -1675,8 +1799,15 @@ bool launch_append_decode_mfma(const SegArgs& s, const void* q, int q_dtype, int
     a.kv_dtype = kv_dtype;
     a.counters = counters;
     a.out = out;
-    a.compact = !merge && ragged && batch <= 64 ? batch : 0;
-    if (merge) {  // every (workgroup of G splits, KV head, entry), in the order above
+    a.compact = ragged && batch <= 64 ? batch : 0;
+    if (merge && a.compact > 0) {  // compact order: one workgroup per G items (those past the last item return)
+        const dim3 grid((unsigned)((s.n_splits * s.f.H * batch + G - 1) / G));
+        auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(64 * G), 0, stream, a); };
+        if (s.f.vb == 4 && G == 4) go(split_append_merged_compact_kernel<4, 4>);
+        else if (s.f.vb == 4) go(split_append_merged_compact_kernel<4, 8>);
+        else if (G == 4) go(split_append_merged_compact_kernel<6, 4>);
+        else go(split_append_merged_compact_kernel<6, 8>);
+    } else if (merge) {  // every (workgroup of G splits, KV head, entry), in the order above
         const dim3 grid((unsigned)((s.n_splits + G - 1) / G * s.f.H * batch));
         auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(64 * G), 0, stream, a, a); };
         if (s.f.vb == 4 && G == 4) go(split_append_merged_kernel<4, 4, false>);

@@ -353,3 +353,59 @@ def test_append_decode_merged_rejects_other_segment_pairs():
     assert e.value.status == lkv.EINVAL
     torch.cuda.synchronize()
     assert int(counters.abs().sum()) == 0 and not a.pool.any() and not b.pool.any()
+
+
+N_RAGGED_MERGED = 40
+
+
+def test_seeded_random_ragged_steps_one_launch():
+    """Seeded random decode steps of ragged batches (up to 64 sequences,
+    empty ones and block and split edges among them) through the one-launch
+    step in compact order (the sum_len hint): pool bit-equal to the two-launch
+    step's, output within 1e-5 max|v_hat| of it (the same skip decisions, the
+    splits merged in another order) and, without the skip, within tolerance
+    of the oracle; counters back at zero.  Split sizes are drawn, or taken
+    from lkv_decode_plan_lens."""
+    rng = np.random.default_rng(4099)
+    edge = [0, 1, 63, 64, 65, 127, 128, 129, 511, 512, 513, 1024, 1025]
+    for i in range(N_RAGGED_MERGED):
+        fmt = ((128, 64, 6, 4), (128, 64, 6, 6))[rng.integers(2)]
+        G = int(rng.choice([4, 8]))
+        Hkv = int(rng.choice([1, 2, 4]))
+        B = int(rng.choice([2, 5, 17, 64])) if rng.random() < 0.5 else int(rng.integers(1, 65))
+        lens = [int(rng.choice(edge)) if rng.random() < 0.4 else int(rng.integers(1, 3000)) for _ in range(B)]
+        lens[0] = max(lens[0], 1)
+        tau = float(rng.choice([0.0, 0.0, 1e-4, 2e-3]))
+        seed = int(rng.integers(1, 10**6))
+        pair, cache, bt = _caches(fmt, lens, Hkv, seed)
+        D = fmt[0]
+        q = inputs.queries(seed + 1, B, Hkv * G, D).cuda()
+        btd, lt = torch.tensor(bt).cuda(), torch.tensor(lens, dtype=torch.int32).cuda()
+        hinted = lkv.View(btd, lt, max(lens), sum(lens))
+        if rng.random() < 0.5:
+            split = lkv.decode_plan_lens(cache, hinted, lens, Hkv * G)
+        else:
+            split = int(rng.choice([64, 128, 256, 512, 1024]))
+        what = f"case {i}: {fmt} G{G} Hkv{Hkv} B{B} lens {lens} split {split} tau {tau} seed {seed}"
+        say(what)
+        k_new, v_new = inputs.kv_rows(seed + 2, 0, B, Hkv, D)
+        sm = sm_scale(D)
+        counters = lkv.merge_counters(cache, B)
+        want = lkv.append_decode(cache, hinted, k_new.cuda(), v_new.cuda(), q, sm, tau, split)
+        pool = cache.pool.clone()
+        got = lkv.append_decode_merged(cache, hinted, k_new.cuda(), v_new.cuda(), q, sm, tau, split, counters)
+        live = [b for b, n in enumerate(lens) if n > 0]
+        O.append(pair.ref, to_f32_host(k_new[live]), to_f32_host(v_new[live]), np.arange(len(live) + 1, dtype=np.int32),
+                 np.array([lens[b] - 1 for b in live], np.int32), bt[live])
+        torch.cuda.synchronize()
+        assert torch.equal(cache.pool, pool), f"{what}: the re-appended rows changed the pool"
+        assert int(counters.abs().sum()) == 0, f"{what}: counters not back at zero"
+        vmax = max_abs_vhat(pair.ref)
+        d = float((got - want).abs().max())
+        assert d <= 1e-5 * vmax, f"{what}: max |d| {d} against the two-launch step"
+        assert np.all(got.cpu().numpy()[[b for b, n in enumerate(lens) if n == 0]] == 0.0), what
+        if tau == 0.0:
+            pair.gpu.pool.copy_(cache.pool)
+            assert pair.pool_equal(), (what, pair.first_pool_mismatch())
+            ref = O.decode([pair.ref], [bt], [np.array(lens, np.int32)], to_f32_host(q), sm, 0.0, split)
+            assert_attention_close(got.cpu().numpy(), ref, vmax, what)

@@ -247,8 +247,10 @@ def test_workload4_llama70b_128k(fp16):
 def test_workload5_ragged_paged_every_step():
     """64 ragged sequences (1K-16K) in a randomly permuted paged pool; 128
     steps of (append one token per sequence, decode): even steps as the
-    benchmark runs them (lkv_append_decode, the grid and split of the last
-    step), odd ones as lkv_quant_append then lkv_decode_attn sized for the
+    benchmark runs them, with the grid and split of the last step (every
+    fourth step lkv_append_decode_merged, the one launch in compact order;
+    the others lkv_append_decode, the split kernel in compact order then the
+    merge), odd ones as lkv_quant_append then lkv_decode_attn sized for the
     step.  Every step: the new rows of every sequence bit for bit; the
     outputs of every sequence at every third step, of two sequences at the
     others."""
@@ -291,12 +293,19 @@ def test_workload5_ragged_paged_every_step():
     max_len = int(cap.max())
     split_bench = lkv.decode_plan_lens(gpu, lkv.View(bt_gpu, torch.tensor(cap, dtype=torch.int32).cuda(), max_len,
                                                      int(cap.sum())), cap, Hq)
+    counters = lkv.merge_counters(gpu, B)
     for step in range(wl.steps):
         k, v = inputs.kv_rows(wl.seed, 2000, B, Hkv, D, step=step + 1)
         O.append(ref, k.float().numpy(), v.float().numpy(), np.arange(B + 1), cur.astype(np.int32), bt)
         lt = torch.tensor(cur + 1, dtype=torch.int32).cuda()
         q = inputs.queries(wl.seed, B, Hq, D, step=step + 1)
-        if step % 2 == 0:  # the benchmark's step: lkv_append_decode (the split kernel appends)
+        if step % 4 == 0:  # the benchmark's step: one launch (append, split in compact order, merge)
+            view = lkv.View(bt_gpu, lt, max_len, int((cur + 1).sum()))
+            split = split_bench
+            out = lkv.append_decode_merged(gpu, view, k.cuda(), v.cuda(), q.cuda(), sm, 0.0, split,
+                                           counters).cpu().numpy()
+            assert int(counters.abs().sum()) == 0
+        elif step % 2 == 0:  # the benchmark's --two-launch step: lkv_append_decode (the split kernel appends)
             view = lkv.View(bt_gpu, lt, max_len, int((cur + 1).sum()))
             split = split_bench
             out = lkv.append_decode(gpu, view, k.cuda(), v.cuda(), q.cuda(), sm, 0.0, split).cpu().numpy()
