@@ -388,3 +388,25 @@ def test_binding_checks_raise_value_errors_before_any_call():
     from quantized_kv_cache_token_amd import inputs
     with pytest.raises(ValueError):
         inputs.tier_scores(1, 0, 10, 1e-4, 1e-3, frac_high=0.8, frac_mid=0.5)
+
+
+def test_append_decode_merged_rejects_bad_arguments_before_any_launch():
+    """lkv_append_decode_merged: one or two segments, counters, out and the
+    new rows are checked on the host; nothing is launched when they fail."""
+    L = lkv.lib()
+    p = C.c_void_p(0x90000)
+
+    def call(nseg=1, counters=p, out=p, k=p, kvd=lkv.BF16, ws=1 << 30):
+        cs = (lkv._Cache * 3)(_cache(), _cache(), _cache())
+        vs = (lkv._View * 3)(_view(max_len=1000), _view(max_len=1000), _view(max_len=1000))
+        return L.lkv_append_decode_merged(cs, vs, nseg, k, p, kvd, p, lkv.BF16, 8, 32, 0.088, 0.0, 256, out,
+                                          counters, p, ws, None)
+
+    assert call(nseg=0) == lkv.EINVAL
+    assert call(nseg=3) == lkv.EINVAL
+    assert call(counters=None) == lkv.EINVAL
+    assert call(counters=C.c_void_p(0x90002)) == lkv.EINVAL  # counters are 4-byte aligned
+    assert call(out=None) == lkv.EINVAL
+    assert call(k=None) == lkv.EINVAL
+    assert call(kvd=7) == lkv.EINVAL
+    assert call(ws=100) == lkv.EINVAL
