@@ -582,9 +582,19 @@ def main():
     # warmup, then the timed steps; workload 5 times its decode steps from
     # the first (its warmup replays the first slots, appending the same rows)
     first = 0 if args.workload == 5 else args.warmup
+    import gc
     with torch.cuda.stream(run_stream):
         for i in range(args.warmup):
             step(i)
+    if not args.graph:
+        # the host's own preparation of the timed region runs while the
+        # warmup steps do, so that the GPU does not idle before the timed
+        # steps: the cycle collector, and the timed region's events
+        gc.collect()
+        gc.disable()  # no cycle-collector pause inside the timed steps
+    g0, g1 = _event(), _event()
+    nwin = min(10, args.steps)  # an event at each tenth of the timed steps: the step time by window
+    wev = [_event() for _ in range(nwin - 1)]
     torch.cuda.synchronize()
     n_stages = len(S.calls[0])
     # the step of each rotation slot as a HIP graph (its launches replayed
@@ -604,15 +614,11 @@ def main():
         torch.cuda.synchronize()
     # timed region: K steps between synchronisations; HIP events on the
     # run stream bracket all of them (the steps' GPU time)
-    g0, g1 = _event(), _event()
-    import gc
-    gc.collect()
-    gc.disable()  # no cycle-collector pause inside the timed steps
-    torch.cuda.synchronize()
+    if args.graph:
+        gc.collect()
+        gc.disable()  # no cycle-collector pause inside the timed steps
+        torch.cuda.synchronize()
     t0 = time.perf_counter()
-    # (and an event at each tenth of them: the step time by window)
-    nwin = min(10, args.steps)
-    wev = [_event() for _ in range(nwin - 1)]
     with torch.cuda.stream(run_stream):
         g0.record(run_stream)
         for i in range(args.steps):
